@@ -1,0 +1,183 @@
+"""Oracle for the fused indexer-Q preparation: block-scaled FP8 Q projection,
+RoPE on each head's rope slice, 128-point Hadamard rotation, FP4 quantization.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+The chain follows TensorRT-LLM PR "Fuse DeepSeek-V4 Indexer Q projection with
+CuTe DSL" (sequence diagram: FP8 input and UE8M0 scales go into a GEMM whose
+epilogue applies RoPE and writes packed FP4 Q and scales; Description / Paths
+compared: the unfused chain is the Q GEMM, an in-place RoPE kernel and an FP4
+quantization kernel with scale copies) and tokenspeed PR "perf(deepseek-v4):
+accelerate indexer Q and packed FP8 quantization" (Summary: RoPE, FP4
+quantization and a Hadamard transform make up indexer-Q preparation).
+
+The pages name these steps without formulas. The readings taken here:
+
+* weights are E4M3 with one UE8M0 scale per 128x128 tile (the pages only say
+  the GEMM is block-scaled FP8);
+* RoPE rotates pairs (i, i + rope_dim/2) of the first rope_dim dims of each
+  head ("half-split" layout), angle pos * theta^(-2i/rope_dim);
+* the Hadamard matrix is the Sylvester one, H[r][c] = (-1)^popcount(r & c),
+  normalised by 1/sqrt(128) so that it is orthonormal, and it is applied after
+  RoPE to all 128 dims of a head;
+* FP4 blocks are 32 consecutive dims with a UE8M0 scale 2^e,
+  e = ceil(log2(amax / 6)) with amax floored at 1e-4, codes rounded to nearest
+  even; two codes per byte, the even element in the low nibble.
+"""
+import numpy as np
+
+from .formats import (E2M1_MAX, ceil_log2_ratio, e2m1_encode_rne, e2m1_pack,
+                      e4m3_decode)
+
+KBLOCK = 128          # K extent of one activation / weight scale block
+WBLOCK_N = 128        # N extent of one weight scale block
+FP4_BLOCK = 32        # elements per FP4 scale block
+FP4_AMAX_FLOOR = 1e-4
+HADAMARD_N = 128
+
+
+# ----------------------------------------------------------------------------
+# Block-scaled FP8 GEMM
+# ----------------------------------------------------------------------------
+
+
+def block_scaled_gemm(a_codes, a_scale_bytes, w_codes, w_scale_bytes) -> np.ndarray:
+    """Q[m, n] = sum_j 2^(ea[m,j] + ew[n/128, j]) * sum_{k in block j} A[m,k] W[n,k].
+
+    a_codes [M, K] and w_codes [N, K] are E4M3 codes; a_scale_bytes [M, K/128]
+    and w_scale_bytes [N/128, K/128] are UE8M0 bytes.
+
+    Each E4M3 value is an integer multiple of 2^-9 below 2^9, so every product
+    is a multiple of 2^-18 and every partial sum of one 128-block stays below
+    2^43 such units: the per-block dot products are exact in float64 whatever
+    order the matrix product uses. Only the sum over blocks (ascending j)
+    rounds.
+    """
+    A = e4m3_decode(a_codes)
+    W = e4m3_decode(w_codes)
+    M, K = A.shape
+    N = W.shape[0]
+    if K % KBLOCK or N % WBLOCK_N or W.shape[1] != K:
+        raise ValueError("block_scaled_gemm: bad shapes")
+    nb = K // KBLOCK
+    sa = np.ldexp(1.0, np.asarray(a_scale_bytes, dtype=np.int64) - 127)      # [M, nb]
+    sw = np.ldexp(1.0, np.asarray(w_scale_bytes, dtype=np.int64) - 127)      # [N/128, nb]
+    sw_n = np.repeat(sw, WBLOCK_N, axis=0)                                   # [N, nb]
+    Q = np.zeros((M, N), dtype=np.float64)
+    for j in range(nb):
+        ks = slice(j * KBLOCK, (j + 1) * KBLOCK)
+        P = A[:, ks] @ W[:, ks].T
+        Q += P * sa[:, j:j + 1] * sw_n[None, :, j]
+    return Q
+
+
+# ----------------------------------------------------------------------------
+# RoPE
+# ----------------------------------------------------------------------------
+
+
+def rope_angles(positions, theta: float, rope_dim: int) -> np.ndarray:
+    """Angles [M, rope_dim/2]: pos * theta^(-2i/rope_dim), in float64."""
+    half = rope_dim // 2
+    i = np.arange(half, dtype=np.float64)
+    inv_freq = np.power(float(theta), -2.0 * i / rope_dim)
+    return np.asarray(positions, dtype=np.float64)[:, None] * inv_freq[None, :]
+
+
+def rope_cos_sin_table(theta: float, max_pos: int, rope_dim: int) -> np.ndarray:
+    """[max_pos, rope_dim] table: cos of the angles in the first half of each
+    row, sin in the second half (float64)."""
+    ang = rope_angles(np.arange(max_pos), theta, rope_dim)
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1)
+
+
+def rope_half_split(q, positions, theta: float = 10000.0, rope_dim: int = 64) -> np.ndarray:
+    """Rotate each head's first rope_dim dims; q is [M, H, D] float64.
+
+    For i < rope_dim/2: (x_i, x_{i+half}) -> (x_i c - x_{i+half} s,
+    x_{i+half} c + x_i s); dims rope_dim..D-1 are unchanged.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    half = rope_dim // 2
+    ang = rope_angles(positions, theta, rope_dim)
+    c = np.cos(ang)[:, None, :]
+    s = np.sin(ang)[:, None, :]
+    out = q.copy()
+    x1 = q[..., :half]
+    x2 = q[..., half:rope_dim]
+    out[..., :half] = x1 * c - x2 * s
+    out[..., half:rope_dim] = x2 * c + x1 * s
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Hadamard
+# ----------------------------------------------------------------------------
+
+
+def hadamard_matrix(n: int = HADAMARD_N) -> np.ndarray:
+    """Unnormalised Sylvester Hadamard matrix, H[r][c] = (-1)^popcount(r & c)."""
+    r = np.arange(n)[:, None]
+    c = np.arange(n)[None, :]
+    bits = r & c
+    pop = np.zeros_like(bits)
+    for b in range(int(n).bit_length()):
+        pop += (bits >> b) & 1
+    return np.where(pop % 2 == 0, 1.0, -1.0)
+
+
+def hadamard_rotate(y) -> np.ndarray:
+    """z = (H / sqrt(128)) y along the last axis, as a dense matrix product."""
+    y = np.asarray(y, dtype=np.float64)
+    H = hadamard_matrix(y.shape[-1])
+    return (y @ H.T) / np.sqrt(float(y.shape[-1]))
+
+
+# ----------------------------------------------------------------------------
+# FP4 e2m1 with UE8M0 block scales
+# ----------------------------------------------------------------------------
+
+
+def fp4_quantize(z, decide_dtype=np.float32) -> tuple:
+    """Quantize the last axis (a multiple of 32) in 32-element blocks.
+
+    The scale and code decisions are taken on z rounded to ``decide_dtype``
+    (float32 by default: the precision the device path holds z in); the
+    decision itself is exact. Returns ``(packed, scale_bytes)``: packed codes
+    [..., n/2] uint8 and scale bytes [..., n/32] uint8.
+    """
+    z = np.asarray(z, dtype=np.float64)
+    if decide_dtype is not None:
+        z = z.astype(decide_dtype).astype(np.float64)
+    n = z.shape[-1]
+    if n % FP4_BLOCK:
+        raise ValueError("fp4_quantize: last axis must be a multiple of 32")
+    blocks = z.reshape(z.shape[:-1] + (n // FP4_BLOCK, FP4_BLOCK))
+    amax = np.maximum(np.abs(blocks).max(axis=-1), FP4_AMAX_FLOOR)
+    e = ceil_log2_ratio(amax, E2M1_MAX)
+    scaled = blocks * np.ldexp(1.0, -e)[..., None]
+    codes = e2m1_encode_rne(scaled).reshape(z.shape)
+    return e2m1_pack(codes), (e + 127).astype(np.uint8)
+
+
+# ----------------------------------------------------------------------------
+# Whole chain
+# ----------------------------------------------------------------------------
+
+
+def indexer_q_chain(a_codes, a_scale_bytes, w_codes, w_scale_bytes, positions,
+                    n_heads: int = 64, head_dim: int = 128, rope_dim: int = 64,
+                    theta: float = 10000.0) -> dict:
+    """The whole indexer-Q preparation for one batch of tokens.
+
+    Returns a dict with ``q_fp4`` [M, H, D/2] uint8, ``q_scales`` [M, H, D/32]
+    uint8, and the float64 intermediates ``q`` (GEMM output, [M, H, D]),
+    ``q_rope`` and ``z`` (the Hadamard-rotated values that were quantized).
+    """
+    M = np.asarray(a_codes).shape[0]
+    q = block_scaled_gemm(a_codes, a_scale_bytes, w_codes, w_scale_bytes)
+    q = q.reshape(M, n_heads, head_dim)
+    q_rope = rope_half_split(q, positions, theta, rope_dim)
+    z = hadamard_rotate(q_rope)
+    packed, scales = fp4_quantize(z)
+    return {"q": q, "q_rope": q_rope, "z": z, "q_fp4": packed, "q_scales": scales}

@@ -1,0 +1,23 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: takes more than a few seconds on the CPU")
+
+
+@pytest.fixture(scope="session")
+def gpu_lib():
+    """The product binding, with the HIP library loaded on a GPU device."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import fp4_quantized_prep_amd as iqp
+    return iqp

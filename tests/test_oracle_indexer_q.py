@@ -1,0 +1,280 @@
+"""Pins for the indexer-Q oracle: block-scaled FP8 GEMM, RoPE, Hadamard-128 and
+FP4 e2m1 quantization (TensorRT-LLM PR "Fuse DeepSeek-V4 Indexer Q projection
+with CuTe DSL", sequence diagram; tokenspeed PR "perf(deepseek-v4): accelerate
+indexer Q and packed FP8 quantization", Summary)."""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import formats as F
+from oracle import indexer_q as IQ
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+E4M3_FINITE = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+
+
+def rand_codes(g, shape):
+    return g.choice(E4M3_FINITE, size=shape)
+
+
+# ---------------------------------------------------------------- GEMM
+
+
+def test_gemm_one_hot_weights_give_dequantized_activations():
+    g = np.random.default_rng(0)
+    M, K, N = 5, 256, 128
+    a = rand_codes(g, (M, K))
+    sa = g.integers(110, 140, size=(M, K // 128)).astype(np.uint8)
+    w = np.zeros((N, K), dtype=np.uint8)
+    cols = g.integers(0, K, size=N)
+    w[np.arange(N), cols] = 0x38          # 1.0
+    sw = np.full((1, K // 128), 127, dtype=np.uint8)
+    Qm = IQ.block_scaled_gemm(a, sa, w, sw)
+    deq = F.e4m3_decode(a) * np.ldexp(1.0, np.repeat(sa.astype(np.int64) - 127, 128, axis=1))
+    assert np.array_equal(Qm, deq[:, cols])
+
+
+def _exact_gemm(a, sa, w, sw):
+    """Pure-Python exact rational GEMM: integer block dots times powers of two."""
+    M, K = a.shape
+    N = w.shape[0]
+    A = [[Fraction(float(v)) for v in F.e4m3_decode(r)] for r in a]
+    W = [[Fraction(float(v)) for v in F.e4m3_decode(r)] for r in w]
+    out = [[Fraction(0)] * N for _ in range(M)]
+    for m in range(M):
+        for n in range(N):
+            tot = Fraction(0)
+            for j in range(K // 128):
+                dot = sum(A[m][k] * W[n][k] for k in range(128 * j, 128 * j + 128))
+                tot += dot * Fraction(2) ** (int(sa[m, j]) - 127) * Fraction(2) ** (int(sw[n // 128, j]) - 127)
+            out[m][n] = tot
+    return out
+
+
+def test_gemm_vs_exact_rationals():
+    g = np.random.default_rng(1)
+    M, K, N = 3, 384, 256
+    a = rand_codes(g, (M, K))
+    w = rand_codes(g, (N, K))
+    sa = g.integers(100, 150, size=(M, K // 128)).astype(np.uint8)
+    sw = g.integers(100, 150, size=(N // 128, K // 128)).astype(np.uint8)
+    got = IQ.block_scaled_gemm(a, sa, w, sw)
+    want = _exact_gemm(a, sa, w, sw)
+    for m in range(M):
+        for n in range(0, N, 7):
+            exact = want[m][n]
+            # only the 3-term sum over blocks rounds: relative error <= 3 * 2^-53
+            assert abs(Fraction(float(got[m, n])) - exact) <= abs(exact) * Fraction(3, 2 ** 53) + Fraction(1, 2 ** 200)
+
+
+def test_gemm_k128_is_one_scaled_integer_dot():
+    g = np.random.default_rng(2)
+    a = rand_codes(g, (4, 128))
+    w = rand_codes(g, (128, 128))
+    sa = np.array([[120], [127], [130], [140]], dtype=np.uint8)
+    sw = np.array([[125]], dtype=np.uint8)
+    got = IQ.block_scaled_gemm(a, sa, w, sw)
+    ai = np.round(F.e4m3_decode(a) * 512).astype(np.int64)     # integers (units of 2^-9)
+    wi = np.round(F.e4m3_decode(w) * 512).astype(np.int64)
+    dots = ai @ wi.T                                             # exact int64
+    want = np.ldexp(dots.astype(np.float64), (sa.astype(np.int64) - 127 + 125 - 127 - 18))
+    assert np.array_equal(got, want)
+
+
+def test_gemm_matches_numpy_float64_on_small_shape():
+    g = np.random.default_rng(3)
+    a = rand_codes(g, (6, 256))
+    w = rand_codes(g, (128, 256))
+    sa = np.full((6, 2), 127, np.uint8)
+    sw = np.full((1, 2), 127, np.uint8)
+    got = IQ.block_scaled_gemm(a, sa, w, sw)
+    want = np.matmul(F.e4m3_decode(a), F.e4m3_decode(w).T)
+    assert np.allclose(got, want, rtol=1e-15, atol=0)
+
+
+def test_gemm_weight_scale_applies_per_128_rows():
+    g = np.random.default_rng(4)
+    a = rand_codes(g, (2, 128))
+    w = rand_codes(g, (256, 128))
+    sa = np.full((2, 1), 127, np.uint8)
+    base = IQ.block_scaled_gemm(a, sa, w, np.array([[127], [127]], np.uint8))
+    moved = IQ.block_scaled_gemm(a, sa, w, np.array([[127], [130]], np.uint8))
+    assert np.array_equal(moved[:, :128], base[:, :128])
+    assert np.array_equal(moved[:, 128:], base[:, 128:] * 8)
+
+
+# ---------------------------------------------------------------- RoPE
+
+
+def test_rope_golden_unit_vectors():
+    gd = json.load(open(os.path.join(GOLDEN, "rope_hadamard_closed_forms.json")))["rope"]
+    for case in gd["cases"]:
+        x = np.zeros((1, 1, 128))
+        x[0, 0, case["unit"]] = 1.0
+        y = IQ.rope_half_split(x, np.array([gd["position"]]), gd["theta"], gd["rope_dim"])[0, 0]
+        want = np.zeros(128)
+        for i, v in case["out"]:
+            want[i] = v
+        assert np.allclose(y, want, rtol=0, atol=1e-15), case["note"]
+
+
+def test_rope_position_zero_is_identity():
+    x = np.random.default_rng(5).standard_normal((3, 4, 128))
+    assert np.array_equal(IQ.rope_half_split(x, np.zeros(3, np.int64)), x)
+
+
+def test_rope_preserves_pair_norms_and_composes():
+    g = np.random.default_rng(6)
+    x = g.standard_normal((8, 2, 128))
+    p1 = g.integers(0, 131072, 8)
+    p2 = g.integers(0, 131072, 8)
+    y = IQ.rope_half_split(x, p1)
+    n_in = x[..., :32] ** 2 + x[..., 32:64] ** 2
+    n_out = y[..., :32] ** 2 + y[..., 32:64] ** 2
+    assert np.allclose(n_in, n_out, rtol=1e-13, atol=0)
+    assert np.array_equal(y[..., 64:], x[..., 64:])
+    z = IQ.rope_half_split(y, p2)
+    direct = IQ.rope_half_split(x, p1 + p2)
+    assert np.allclose(z, direct, rtol=0, atol=1e-9)
+
+
+def test_rope_pairs_are_half_split_not_interleaved():
+    x = np.zeros((1, 1, 128))
+    x[0, 0, 0] = 1.0
+    y = IQ.rope_half_split(x, np.array([1]))[0, 0]
+    assert y[1] == 0.0 and y[32] != 0.0
+
+
+def test_rope_table_closed_form():
+    t = IQ.rope_cos_sin_table(10000.0, 5, 64)
+    assert t.shape == (5, 64)
+    for p in range(5):
+        for i in (0, 1, 16, 31):
+            ang = p * 10000.0 ** (-2 * i / 64)
+            assert abs(t[p, i] - math.cos(ang)) < 1e-15 and abs(t[p, 32 + i] - math.sin(ang)) < 1e-15
+
+
+# ---------------------------------------------------------------- Hadamard
+
+
+def test_hadamard_orthogonality_and_symmetry():
+    H = IQ.hadamard_matrix(128)
+    assert np.array_equal(H @ H.T, 128 * np.eye(128))
+    assert np.array_equal(H, H.T)
+    Hn = H / np.sqrt(128)
+    assert np.allclose(Hn @ Hn, np.eye(128), atol=1e-14)
+
+
+def test_hadamard_matches_sylvester_recursion_and_butterflies():
+    S = np.array([[1.0]])
+    while S.shape[0] < 128:
+        S = np.block([[S, S], [S, -S]])
+    assert np.array_equal(IQ.hadamard_matrix(128), S)
+    # brute-force radix-2 butterflies on a small random vector
+    y = np.random.default_rng(7).standard_normal(128)
+    v = y.copy()
+    h = 1
+    while h < 128:
+        for i in range(0, 128, 2 * h):
+            for j in range(i, i + h):
+                v[j], v[j + h] = v[j] + v[j + h], v[j] - v[j + h]
+        h *= 2
+    assert np.allclose(IQ.hadamard_rotate(y), v / np.sqrt(128), rtol=0, atol=1e-13)
+
+
+def test_hadamard_golden_and_norm():
+    gd = json.load(open(os.path.join(GOLDEN, "rope_hadamard_closed_forms.json")))["hadamard"]
+    c = gd["inv_sqrt_n"]
+    r = np.arange(128)
+    pop = np.array([bin(i).count("1") for i in r])
+    rules = [np.full(128, c), np.where(r % 2 == 0, 2 * c, 0.0), np.where(pop % 2 == 0, c, -c)]
+    for case, want in zip(gd["cases"], rules):
+        x = np.zeros(128)
+        for i, v in case["input_nonzero"]:
+            x[i] = v
+        assert np.allclose(IQ.hadamard_rotate(x), want, rtol=0, atol=1e-15), case["rule"]
+    y = np.random.default_rng(8).standard_normal((10, 128))
+    assert np.allclose(np.linalg.norm(IQ.hadamard_rotate(y), axis=1), np.linalg.norm(y, axis=1), rtol=1e-14)
+
+
+# ---------------------------------------------------------------- FP4
+
+
+def test_fp4_golden_worked_example():
+    gd = json.load(open(os.path.join(GOLDEN, "fp4_worked_example.json")))
+    z = np.zeros(128)
+    for base, entries in gd["z"].items():
+        for i, v in entries:
+            z[int(base) + i] = v
+    packed, sb = IQ.fp4_quantize(z[None, :], decide_dtype=None)
+    assert sb[0].tolist() == gd["scale_bytes"]
+    for base, vals in gd["packed"].items():
+        b = int(base)
+        assert packed[0, b:b + len(vals)].tolist() == vals
+
+
+@pytest.mark.parametrize("k", [-15, -7, 0, 5, 20])
+def test_fp4_scale_closed_form(k):
+    z = np.zeros((2, 32))
+    z[0, 3] = 6.0 * 2.0 ** k
+    z[1, 3] = np.nextafter(np.float32(6.0 * 2.0 ** k), np.float32(np.inf))
+    _, sb = IQ.fp4_quantize(z)
+    assert sb[0, 0] == 127 + k and sb[1, 0] == 128 + k
+
+
+def test_fp4_floor():
+    z = np.zeros((3, 32))
+    z[1, 0] = 1e-9
+    z[2, 0] = -6.0 * 2.0 ** -15
+    _, sb = IQ.fp4_quantize(z)
+    assert sb[:, 0].tolist() == [112, 112, 112]
+
+
+def test_fp4_dequant_error_bound():
+    g = np.random.default_rng(9)
+    z = g.standard_normal((50, 128)) * np.exp(g.uniform(-10, 10, (50, 1)))
+    packed, sb = IQ.fp4_quantize(z)
+    codes = F.e2m1_unpack(packed)
+    scale = np.repeat(np.ldexp(1.0, sb.astype(np.int64) - 127), 32, axis=1)
+    deq = F.e2m1_decode(codes) * scale
+    z32 = z.astype(np.float32).astype(np.float64)
+    t = np.abs(z32) / scale
+    step = np.where(t < 2, 0.5, np.where(t < 4, 1.0, 2.0))
+    assert np.all(np.abs(deq - z32) <= step / 2 * scale)
+
+
+def test_fp4_decision_uses_float32_value():
+    """A float64 value a hair above a midpoint that rounds to the midpoint in
+    float32 is decided on the float32 value (tie -> even code)."""
+    z = np.zeros((1, 32))
+    z[0, 0] = 6.0
+    z[0, 1] = 0.25 + 2.0 ** -40
+    packed, _ = IQ.fp4_quantize(z)
+    assert F.e2m1_unpack(packed)[0, 1] == 0
+    packed64, _ = IQ.fp4_quantize(z, decide_dtype=None)
+    assert F.e2m1_unpack(packed64)[0, 1] == 1
+
+
+# ---------------------------------------------------------------- chain
+
+
+def test_chain_composes_the_stages():
+    g = np.random.default_rng(10)
+    M, K, H = 4, 256, 2
+    a = rand_codes(g, (M, K))
+    w = rand_codes(g, (H * 128, K))
+    sa = g.integers(115, 130, size=(M, 2)).astype(np.uint8)
+    sw = g.integers(110, 120, size=(H, 2)).astype(np.uint8)
+    pos = g.integers(0, 4096, M)
+    out = IQ.indexer_q_chain(a, sa, w, sw, pos, n_heads=H)
+    q = IQ.block_scaled_gemm(a, sa, w, sw).reshape(M, H, 128)
+    assert np.array_equal(out["q"], q)
+    z = IQ.hadamard_rotate(IQ.rope_half_split(q, pos))
+    assert np.array_equal(out["z"], z)
+    p, s = IQ.fp4_quantize(z)
+    assert np.array_equal(out["q_fp4"], p) and np.array_equal(out["q_scales"], s)
+    assert out["q_fp4"].shape == (M, H, 64) and out["q_scales"].shape == (M, H, 4)
