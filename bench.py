@@ -1,0 +1,240 @@
+"""Benchmark of the indexer-Q preparation hot path on one MI355X.
+
+One step = the whole path over one batch of 4,632 tokens (X bf16 [4632, 1536]):
+packed-UE8M0 FP8 quantization, then the fused block-scaled FP8 Q projection +
+RoPE + Hadamard-128 + FP4 kernel (64 heads x 128). Inputs are synthetic and
+already resident in HBM when timing starts; outputs are preallocated.
+
+Prints ONE JSON line with whole-job tokens/s, the fused kernel's MFMA roofline
+(algorithmic FLOPs / measured average kernel time, against the dense FP8 peak),
+the standalone quantizer's HBM roofline on a [4632, 7168] matrix (rotated over
+enough buffer sets to defeat the 256 MiB Infinity Cache), and the CPU oracle
+timed on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA, TFLOP/s
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
+M_TOKENS, K_PROJ, N_HEADS, HEAD_DIM = 4632, 1536, 64, 128
+QUANT_M, QUANT_K = 4632, 7168
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0: calibrate to ~15 s)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain device copy of 256 MiB (for HBM byte-counter scaling)")
+    return ap.parse_args()
+
+
+def fused_bytes(M):
+    """Algorithmic HBM bytes of one fused launch: A + its scale words, W + its
+    scales, positions, the table rows read, and the FP4 codes + scales written."""
+    nkb = K_PROJ // 128
+    return (M * K_PROJ + M * 4 * ((nkb + 3) // 4) + N_HEADS * HEAD_DIM * K_PROJ + N_HEADS * nkb
+            + M * 8 + M * 64 * 4 + M * N_HEADS * (HEAD_DIM // 2 + HEAD_DIM // 32))
+
+
+def quant_bytes(M, K):
+    """Algorithmic HBM bytes of one quantizer launch: bf16 in, E4M3 + words out."""
+    return M * K * 2 + M * K + M * 4 * ((K // 128 + 3) // 4)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this path has no cross-GPU step); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import fp4_quantized_prep_amd as iqp
+    import synthetic as S
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    print(f"[bench] device {torch.cuda.get_device_name(dev)}; preparing inputs", file=sys.stderr, flush=True)
+
+    inp = S.indexer_q_inputs("indexer_q_m4632")
+    x = inp["x"].to(dev)
+    pos = inp["positions"].to(dev)
+    w_cpu, wsb_cpu = S.weights()
+    w, wsb = w_cpu.to(dev), wsb_cpu.to(dev)
+    cs = iqp.rope_cos_sin_table(S.ROPE_THETA, inp["max_pos"], 64, device=dev)
+    M = x.shape[0]
+    a = torch.empty((M, K_PROJ), dtype=torch.uint8, device=dev)
+    a_s = torch.empty((M, (K_PROJ // 128 + 3) // 4), dtype=torch.int32, device=dev)
+    q = torch.empty((M, N_HEADS, HEAD_DIM // 2), dtype=torch.uint8, device=dev)
+    qs = torch.empty((M, N_HEADS, HEAD_DIM // 32), dtype=torch.uint8, device=dev)
+
+    def step():
+        iqp.fp8_quant_1x128_ue8m0(x, q=a, scales=a_s)
+        iqp.indexer_q_gemm_rope_fp4(a, a_s, w, wsb, pos, cs, n_heads=N_HEADS, q_fp4=q, q_scales=qs)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K whole steps, events around each kernel on its stream
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(K):
+        ev[i][0].record(stream)
+        iqp.fp8_quant_1x128_ue8m0(x, q=a, scales=a_s)
+        ev[i][1].record(stream)
+        iqp.indexer_q_gemm_rope_fp4(a, a_s, w, wsb, pos, cs, n_heads=N_HEADS, q_fp4=q, q_scales=qs)
+        ev[i][2].record(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(stop)
+    t_quant = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3       # s
+    t_fused = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e-3
+    ms_per_step = total_ms / K
+    tokens_per_s = M * K / (total_ms * 1e-3)
+    flops = 2.0 * M * (N_HEADS * HEAD_DIM) * K_PROJ
+    fused_tflops = flops / t_fused / 1e12
+    print(f"[bench] chain: {ms_per_step * 1e3:.1f} us/step (wall {wall * 1e6 / K:.1f} us); "
+          f"quant {t_quant * 1e6:.1f} us, fused {t_fused * 1e6:.1f} us = {fused_tflops:.0f} TFLOP/s",
+          file=sys.stderr, flush=True)
+
+    # ---- standalone quantizer on [4632, 7168], rotating buffer sets (> 256 MiB)
+    xq_cpu = S.quant_input("quant_4632x7168")
+    n_sets = 5
+    xs = [xq_cpu.to(dev) for _ in range(n_sets)]
+    qq = [torch.empty((QUANT_M, QUANT_K), dtype=torch.uint8, device=dev) for _ in range(n_sets)]
+    ss = [torch.empty((QUANT_M, (QUANT_K // 128 + 3) // 4), dtype=torch.int32, device=dev) for _ in range(n_sets)]
+    for i in range(10):
+        iqp.fp8_quant_1x128_ue8m0(xs[i % n_sets], q=qq[i % n_sets], scales=ss[i % n_sets])
+    torch.cuda.synchronize()
+    n_q = max(50, K)
+    qev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_q)]
+    for i in range(n_q):
+        k = i % n_sets
+        qev[i][0].record(stream)
+        iqp.fp8_quant_1x128_ue8m0(xs[k], q=qq[k], scales=ss[k])
+        qev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t_q_big = float(np.mean([b.elapsed_time(e) for b, e in qev])) * 1e-3
+    qbytes = quant_bytes(QUANT_M, QUANT_K)
+    q_gbs = qbytes / t_q_big / 1e9
+    print(f"[bench] quantizer [4632,7168]: {t_q_big * 1e6:.1f} us = {q_gbs:.0f} GB/s", file=sys.stderr, flush=True)
+    del xs, qq, ss
+
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # ---- CPU baseline: the oracle on a bounded sample of the same workload
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.cpu_tokens, inp, w_cpu, wsb_cpu)
+
+    result = {
+        "metric": "tokens/sec & % roofline: FP8 quant (HBM GB/s) + fused indexer-Q (MFMA util)",
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-e4m3 (fp32 accumulate), bf16 in, fp4-e2m1 out",
+        "data": "synthetic",
+        "config": {
+            "workload": "indexer-Q chain, 4632 tokens: X bf16 [4632,1536] -> FP8 1x128 UE8M0 -> "
+                        "Q = A W^T (W [8192,1536] E4M3, 128x128 UE8M0) -> RoPE(64 of 128) -> "
+                        "Hadamard-128 -> FP4 e2m1 [4632,64,64] + UE8M0 [4632,64,4]",
+            "tokens": M, "K": K_PROJ, "heads": N_HEADS, "head_dim": HEAD_DIM, "rope_dim": 64,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "kernel": "indexer_q_kernel (fused GEMM + RoPE + Hadamard + FP4)",
+            "bound": "mfma",
+            "achieved": fused_tflops,
+            "peak": PEAK_FP8_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": fused_tflops / PEAK_FP8_TFLOPS,
+            "traffic": None,
+            "algorithmic_flops_per_launch": flops,
+            "avg_launch_us": t_fused * 1e6,
+        },
+        "quant_roofline": {
+            "kernel": "fp8_quant_1x128_kernel on [4632,7168] (5 rotating buffer sets)",
+            "bound": "hbm",
+            "achieved": q_gbs,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": q_gbs / PEAK_HBM_GBS,
+            "algorithmic_bytes_per_launch": qbytes,
+            "avg_launch_us": t_q_big * 1e6,
+            "in_chain_avg_launch_us": t_quant * 1e6,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(n_tokens, inp, w_cpu, wsb_cpu):
+    """Time the oracle (as it stands) on the first n tokens of the workload:
+    its FP8 quantization and its whole fused chain."""
+    import numpy as np
+
+    from oracle import indexer_q as IQ
+    from oracle import quant_fp8 as QO
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    except Exception:  # threadpoolctl missing: report the affinity set
+        threads = len(os.sched_getaffinity(0))
+
+    x = inp["x"].float().numpy()
+    pos = inp["positions"].numpy()
+    w = w_cpu.numpy()
+    wsb = wsb_cpu.numpy()
+
+    def run(n):
+        t0 = time.perf_counter()
+        a, words = QO.fp8_quant_1x128_ue8m0(x[:n])
+        IQ.indexer_q_chain(a, QO.unpack_scale_words(words, K_PROJ // 128), w, wsb, pos[:n], n_heads=N_HEADS)
+        return time.perf_counter() - t0
+
+    if n_tokens <= 0:
+        t_probe = run(128)
+        n_tokens = int(min(M_TOKENS, max(128, 128 * 15.0 / max(t_probe, 1e-3))))
+    dt = run(n_tokens)
+    print(f"[bench] oracle: {n_tokens} tokens in {dt:.2f} s on {threads} threads", file=sys.stderr, flush=True)
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n_tokens} of the 4632 tokens, whole chain (quantize + GEMM + RoPE + "
+                      f"Hadamard + FP4), numpy float64, {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,231 @@
+"""DeepSeek-V4 indexer-Q preparation on AMD Instinct MI355X (gfx950).
+
+Thin Python binding over ``libiqprep.so`` (C ABI in ``include/iqprep.h``).
+This module only checks and marshals arguments: every step of the path runs
+in the library's HIP kernels, on torch's current stream. Torch provides device
+memory and streams, nothing else.
+
+If the library has not been built, importing this package raises ImportError
+(build it with ``python fp4_quantized_prep_amd/build.py``); there is no
+fallback implementation.
+"""
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libiqprep.so")
+
+__all__ = [
+    "IqpError", "fp8_quant_1x128_ue8m0", "indexer_q_gemm_rope_fp4", "rope_cos_sin_table",
+    "debug_indexer_q_f32", "indexer_q_prep", "abi_version", "library_path",
+    "IQP_OK", "IQP_ERR_INVALID", "IQP_ERR_UNSUPPORTED", "IQP_ERR_HIP",
+]
+
+IQP_OK = 0
+IQP_ERR_INVALID = 1
+IQP_ERR_UNSUPPORTED = 2
+IQP_ERR_HIP = 3
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python fp4_quantized_prep_amd/build.py`")
+    lib = ctypes.CDLL(LIB_PATH)
+    c_i64, c_i32, c_p, c_dbl = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_double
+    lib.fp8_quant_1x128_ue8m0.argtypes = [c_p, c_i64, c_i64, c_i64, c_p, c_i64, c_p, c_i64, c_i64, c_p]
+    lib.fp8_quant_1x128_ue8m0.restype = ctypes.c_int
+    iq_args = [c_p, c_i64, c_p, c_i64, c_i64, c_p, c_i64, c_p, c_i64, c_i64, c_i32, c_i32, c_i32,
+               c_p, c_p, c_i64]
+    lib.indexer_q_gemm_rope_fp4.argtypes = iq_args + [c_p, c_p, c_p]
+    lib.indexer_q_gemm_rope_fp4.restype = ctypes.c_int
+    lib.iqp_debug_indexer_q_f32.argtypes = iq_args + [c_p, c_i32, c_p]
+    lib.iqp_debug_indexer_q_f32.restype = ctypes.c_int
+    lib.iqp_rope_cos_sin_table.argtypes = [c_dbl, c_i64, c_i32, c_p, c_p]
+    lib.iqp_rope_cos_sin_table.restype = ctypes.c_int
+    lib.iqp_status_string.argtypes = [ctypes.c_int]
+    lib.iqp_status_string.restype = ctypes.c_char_p
+    lib.iqp_abi_version.argtypes = []
+    lib.iqp_abi_version.restype = ctypes.c_int
+    return lib
+
+
+_lib = _load()
+
+
+class IqpError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {_lib.iqp_status_string(status).decode()} (status {status})")
+
+
+def _check(status: int, where: str):
+    if status != IQP_OK:
+        raise IqpError(status, where)
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def abi_version() -> int:
+    return _lib.iqp_abi_version()
+
+
+def _stream(t: torch.Tensor, stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _require(t: torch.Tensor, name: str, dtype, device: torch.device, ndim: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D, got shape {tuple(t.shape)}")
+
+
+def _bytes_u8(t: torch.Tensor) -> torch.Tensor:
+    return t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t
+
+
+def fp8_quant_1x128_ue8m0(x: torch.Tensor, scale_layout: str = "k", q: torch.Tensor = None,
+                          scales: torch.Tensor = None, stream=None):
+    """Packed-UE8M0 FP8 1x128 quantization of a bf16 [M, K] matrix.
+
+    Returns ``(q, scales)``: q is uint8 [M, K] holding E4M3 codes and scales is
+    an int32 [M, ceil(K/512)] view of the packed UE8M0 words. With
+    ``scale_layout="k"`` the words are row-major (K-major); with ``"mn"`` the
+    storage is [ceil(K/512), M rounded up to 4] and the returned view has
+    strides (1, M_pad). Pre-allocated ``q`` / ``scales`` may be passed in.
+    """
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    dev = x.device
+    _require(x, "x", torch.bfloat16, dev, 2)
+    if x.stride(1) != 1:
+        raise ValueError("x rows must be contiguous")
+    M, K = x.shape
+    nw = (K // 128 + 3) // 4
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    q = _bytes_u8(q)
+    _require(q, "q", torch.uint8, dev, 2)
+    if scales is None:
+        if scale_layout == "k":
+            scales = torch.empty((M, nw), dtype=torch.int32, device=dev)
+        elif scale_layout == "mn":
+            m_pad = max(4, (M + 3) // 4 * 4)
+            scales = torch.empty((nw, m_pad), dtype=torch.int32, device=dev).t()[:M]
+        else:
+            raise ValueError("scale_layout must be 'k' or 'mn'")
+    _require(scales, "scales", torch.int32, dev, 2)
+    st = _lib.fp8_quant_1x128_ue8m0(_ptr(x), M, K, x.stride(0), _ptr(q), q.stride(0), _ptr(scales),
+                                    scales.stride(0), scales.stride(1), _stream(x, stream))
+    _check(st, "fp8_quant_1x128_ue8m0")
+    return q, scales
+
+
+def _indexer_q_common(a, a_scales, w, w_scales, positions, cos_sin, n_heads, head_dim, rope_dim):
+    a = _bytes_u8(a)
+    w = _bytes_u8(w)
+    dev = a.device
+    _require(a, "a", torch.uint8, dev, 2)
+    _require(a_scales, "a_scales", torch.int32, dev, 2)
+    _require(w, "w", torch.uint8, dev, 2)
+    _require(w_scales, "w_scales", torch.uint8, dev, 2)
+    _require(positions, "positions", torch.int64, dev, 1)
+    _require(cos_sin, "cos_sin", torch.float32, dev, 2)
+    if a.stride(1) != 1 or w.stride(1) != 1 or not w_scales.is_contiguous() or not positions.is_contiguous() \
+            or not cos_sin.is_contiguous():
+        raise ValueError("a, w need contiguous rows; w_scales, positions, cos_sin must be contiguous")
+    M, K = a.shape
+    if w.shape[1] != K or w.shape[0] != n_heads * head_dim:
+        raise ValueError(f"w must be [{n_heads * head_dim}, {K}], got {tuple(w.shape)}")
+    if tuple(w_scales.shape) != (n_heads * head_dim // 128, K // 128):
+        raise ValueError(f"w_scales must be [{n_heads * head_dim // 128}, {K // 128}]")
+    if positions.shape[0] != M or a_scales.shape[0] != M:
+        raise ValueError("positions and a_scales need one row per token")
+    if cos_sin.shape[1] != rope_dim:
+        raise ValueError(f"cos_sin must have {rope_dim} columns")
+    args = [_ptr(a), a.stride(0), _ptr(a_scales), a_scales.stride(0), a_scales.stride(1),
+            _ptr(w), w.stride(0), _ptr(w_scales), M, K, n_heads, head_dim, rope_dim,
+            _ptr(positions), _ptr(cos_sin), cos_sin.shape[0]]
+    return a, args
+
+
+def indexer_q_gemm_rope_fp4(a, a_scales, w, w_scales, positions, cos_sin, n_heads: int = 64,
+                            head_dim: int = 128, rope_dim: int = 64, q_fp4=None, q_scales=None,
+                            stream=None):
+    """Fused block-scaled FP8 Q projection + RoPE + Hadamard-128 + FP4 e2m1.
+
+    a: E4M3 [M, K] (uint8 or float8_e4m3fn) and a_scales: the packed words from
+    :func:`fp8_quant_1x128_ue8m0`; w: E4M3 [H*128, K]; w_scales: uint8
+    [H, K/128]; positions: int64 [M]; cos_sin: float32 [max_pos, 64].
+    Returns ``(q_fp4, q_scales)``: uint8 [M, H, 64] packed codes and uint8
+    [M, H, 4] UE8M0 scale bytes.
+    """
+    a, args = _indexer_q_common(a, a_scales, w, w_scales, positions, cos_sin, n_heads, head_dim, rope_dim)
+    M = a.shape[0]
+    dev = a.device
+    if q_fp4 is None:
+        q_fp4 = torch.empty((M, n_heads, head_dim // 2), dtype=torch.uint8, device=dev)
+    if q_scales is None:
+        q_scales = torch.empty((M, n_heads, head_dim // 32), dtype=torch.uint8, device=dev)
+    _require(q_fp4, "q_fp4", torch.uint8, dev, 3)
+    _require(q_scales, "q_scales", torch.uint8, dev, 3)
+    if not (q_fp4.is_contiguous() and q_scales.is_contiguous()):
+        raise ValueError("q_fp4 and q_scales must be contiguous")
+    if tuple(q_fp4.shape) != (M, n_heads, head_dim // 2) or tuple(q_scales.shape) != (M, n_heads, head_dim // 32):
+        raise ValueError("q_fp4 / q_scales have the wrong shape")
+    st = _lib.indexer_q_gemm_rope_fp4(*args, _ptr(q_fp4), _ptr(q_scales), _stream(a, stream))
+    _check(st, "indexer_q_gemm_rope_fp4")
+    return q_fp4, q_scales
+
+
+def debug_indexer_q_f32(a, a_scales, w, w_scales, positions, cos_sin, stage: int, n_heads: int = 64,
+                        head_dim: int = 128, rope_dim: int = 64, out=None, stream=None):
+    """float32 [M, H*128] after stage 0 (GEMM), 1 (RoPE) or 2 (Hadamard) of the
+    fused kernel, for stage-wise parity checks."""
+    a, args = _indexer_q_common(a, a_scales, w, w_scales, positions, cos_sin, n_heads, head_dim, rope_dim)
+    M = a.shape[0]
+    if out is None:
+        out = torch.empty((M, n_heads * head_dim), dtype=torch.float32, device=a.device)
+    _require(out, "out", torch.float32, a.device, 2)
+    if not out.is_contiguous() or tuple(out.shape) != (M, n_heads * head_dim):
+        raise ValueError("out must be a contiguous [M, H*128] float32 tensor")
+    st = _lib.iqp_debug_indexer_q_f32(*args, _ptr(out), stage, _stream(a, stream))
+    _check(st, "iqp_debug_indexer_q_f32")
+    return out
+
+
+def rope_cos_sin_table(theta: float, max_pos: int, rope_dim: int = 64, device=None, out=None, stream=None):
+    """float32 [max_pos, rope_dim] table of cos (first half) and sin (second
+    half) of pos * theta^(-2i/rope_dim), computed on the device in float64."""
+    if out is None:
+        out = torch.empty((max_pos, rope_dim), dtype=torch.float32,
+                          device=device if device is not None else "cuda")
+    _require(out, "out", torch.float32, out.device, 2)
+    if not out.is_contiguous() or tuple(out.shape) != (max_pos, rope_dim):
+        raise ValueError("out must be a contiguous [max_pos, rope_dim] float32 tensor")
+    st = _lib.iqp_rope_cos_sin_table(float(theta), max_pos, rope_dim, _ptr(out), _stream(out, stream))
+    _check(st, "iqp_rope_cos_sin_table")
+    return out
+
+
+def indexer_q_prep(x, w, w_scales, positions, cos_sin, n_heads: int = 64, stream=None):
+    """The whole indexer-Q preparation for a bf16 [M, 1536] activation batch:
+    FP8 quantization, then the fused projection / RoPE / Hadamard / FP4 call,
+    both on one stream. Returns ``(q_fp4, q_scales)``."""
+    a, a_scales = fp8_quant_1x128_ue8m0(x, stream=stream)
+    return indexer_q_gemm_rope_fp4(a, a_scales, w, w_scales, positions, cos_sin, n_heads=n_heads,
+                                   stream=stream)

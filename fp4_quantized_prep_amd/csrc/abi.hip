@@ -1,0 +1,173 @@
+// C ABI of libiqprep.so (declared and documented in include/iqprep.h).
+//
+// Every entry point validates its arguments on the host first; nothing that
+// fails validation touches the device. Then it checks, once per device, that
+// the current device is gfx950, and enqueues its kernel on the caller's stream.
+#include <atomic>
+#include <cstring>
+
+#include "iqp_internal.h"
+#include "iqprep.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// 0 = not yet queried, 1 = gfx950, 2 = other architecture, 3 = query failed
+std::atomic<int> g_arch_state[kMaxDevices];
+
+int device_status() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return IQP_ERR_HIP;
+  if (dev >= kMaxDevices) return IQP_ERR_UNSUPPORTED;
+  int st = g_arch_state[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      st = 3;
+    } else {
+      st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    }
+    g_arch_state[dev].store(st, std::memory_order_release);
+  }
+  return st == 1 ? IQP_OK : (st == 2 ? IQP_ERR_UNSUPPORTED : IQP_ERR_HIP);
+}
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Packed scale words: [M, nw] logically; K-major or MN-major strides only.
+int check_scale_strides(int64_t M, int64_t nw, int64_t sm, int64_t sw) {
+  if (sw == 1 && sm >= nw && sm >= 1) return IQP_OK;
+  if (sm == 1 && sw >= M && sw >= 1) return IQP_OK;
+  return IQP_ERR_INVALID;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? IQP_OK : IQP_ERR_HIP; }
+
+// Shared argument checks of the fused call and its diagnostic twin.
+int check_indexer_q_args(const void* a, int64_t lda, const int32_t* a_scales, int64_t as_sm,
+                         int64_t as_sw, const void* w, int64_t ldw, const uint8_t* w_scales,
+                         int64_t M, int64_t K, int32_t H, int32_t D, int32_t rope_dim,
+                         const int64_t* positions, const float* cos_sin, int64_t max_pos,
+                         const void* out0, const void* out1) {
+  if (M < 0 || K < 0 || H < 0 || D < 0 || rope_dim < 0 || max_pos < 0) return IQP_ERR_INVALID;
+  if (M == 0) return IQP_OK;
+  if (!a || !a_scales || !w || !w_scales || !positions || !cos_sin || !out0 || !out1)
+    return IQP_ERR_INVALID;
+  if (K == 0 || H == 0 || max_pos == 0) return IQP_ERR_INVALID;
+  if (lda < K || ldw < K) return IQP_ERR_INVALID;
+  const int64_t nw = (K / 128 + 3) / 4;
+  if (K % 128) return IQP_ERR_UNSUPPORTED;
+  if (check_scale_strides(M, nw, as_sm, as_sw) != IQP_OK) return IQP_ERR_INVALID;
+  if (D != 128 || rope_dim != 64) return IQP_ERR_UNSUPPORTED;
+  if (!aligned(a, 16) || lda % 16 || !aligned(w, 16) || ldw % 16 || !aligned(a_scales, 4) ||
+      !aligned(positions, 8) || !aligned(cos_sin, 16))
+    return IQP_ERR_UNSUPPORTED;
+  if ((int64_t)H * 128 > ((int64_t)1 << 31)) return IQP_ERR_UNSUPPORTED;
+  return IQP_OK;
+}
+
+iqp::IndexerQArgs make_args(const void* a, int64_t lda, const int32_t* a_scales, int64_t as_sm,
+                            int64_t as_sw, const void* w, int64_t ldw, const uint8_t* w_scales,
+                            int64_t M, int64_t K, int32_t H, const int64_t* positions,
+                            const float* cos_sin, int64_t max_pos) {
+  iqp::IndexerQArgs p{};
+  p.a = static_cast<const uint8_t*>(a);
+  p.lda = lda;
+  p.a_scale_bytes = reinterpret_cast<const uint8_t*>(a_scales);
+  p.as_sm = as_sm;
+  p.as_sw = as_sw;
+  p.w = static_cast<const uint8_t*>(w);
+  p.ldw = ldw;
+  p.w_scales = w_scales;
+  p.M = M;
+  p.nkb = (int32_t)(K / 128);
+  p.H = H;
+  p.positions = positions;
+  p.cos_sin = cos_sin;
+  p.max_pos = max_pos;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8_quant_1x128_ue8m0(const void* x, int64_t M, int64_t K, int64_t ldx, void* q, int64_t ldq,
+                          int32_t* scales, int64_t s_stride_m, int64_t s_stride_w, void* stream) {
+  if (M < 0 || K < 0) return IQP_ERR_INVALID;
+  if (M == 0 || K == 0) return IQP_OK;
+  if (!x || !q || !scales) return IQP_ERR_INVALID;
+  if (ldx < K || ldq < K) return IQP_ERR_INVALID;
+  if (K % 128) return IQP_ERR_UNSUPPORTED;
+  if (check_scale_strides(M, (K / 128 + 3) / 4, s_stride_m, s_stride_w) != IQP_OK) return IQP_ERR_INVALID;
+  if (!aligned(x, 16) || ldx % 8 || !aligned(q, 8) || ldq % 8 || !aligned(scales, 4))
+    return IQP_ERR_UNSUPPORTED;
+  if (K / 128 > 0x7FFFFFFF) return IQP_ERR_UNSUPPORTED;
+  const int ds = device_status();
+  if (ds != IQP_OK) return ds;
+  return from_hip(iqp::launch_fp8_quant(static_cast<const uint16_t*>(x), M, K, ldx,
+                                        static_cast<uint8_t*>(q), ldq, scales, s_stride_m,
+                                        s_stride_w, static_cast<hipStream_t>(stream)));
+}
+
+int indexer_q_gemm_rope_fp4(const void* a, int64_t lda, const int32_t* a_scales, int64_t as_stride_m,
+                            int64_t as_stride_w, const void* w, int64_t ldw, const uint8_t* w_scales,
+                            int64_t M, int64_t K, int32_t H, int32_t D, int32_t rope_dim,
+                            const int64_t* positions, const float* cos_sin, int64_t max_pos,
+                            uint8_t* q_fp4, uint8_t* q_scales, void* stream) {
+  int st = check_indexer_q_args(a, lda, a_scales, as_stride_m, as_stride_w, w, ldw, w_scales, M, K,
+                                H, D, rope_dim, positions, cos_sin, max_pos, q_fp4, q_scales);
+  if (st != IQP_OK || M == 0) return st;
+  if (!aligned(q_fp4, 16) || !aligned(q_scales, 4)) return IQP_ERR_UNSUPPORTED;
+  st = device_status();
+  if (st != IQP_OK) return st;
+  iqp::IndexerQArgs p = make_args(a, lda, a_scales, as_stride_m, as_stride_w, w, ldw, w_scales, M,
+                                  K, H, positions, cos_sin, max_pos);
+  p.q_fp4 = q_fp4;
+  p.q_scales = q_scales;
+  return from_hip(iqp::launch_indexer_q(p, -1, static_cast<hipStream_t>(stream)));
+}
+
+int iqp_debug_indexer_q_f32(const void* a, int64_t lda, const int32_t* a_scales, int64_t as_stride_m,
+                            int64_t as_stride_w, const void* w, int64_t ldw, const uint8_t* w_scales,
+                            int64_t M, int64_t K, int32_t H, int32_t D, int32_t rope_dim,
+                            const int64_t* positions, const float* cos_sin, int64_t max_pos,
+                            float* out, int32_t stage, void* stream) {
+  if (stage < 0 || stage > 2) return IQP_ERR_INVALID;
+  int st = check_indexer_q_args(a, lda, a_scales, as_stride_m, as_stride_w, w, ldw, w_scales, M, K,
+                                H, D, rope_dim, positions, cos_sin, max_pos, out, out);
+  if (st != IQP_OK || M == 0) return st;
+  if (!aligned(out, 16)) return IQP_ERR_UNSUPPORTED;
+  st = device_status();
+  if (st != IQP_OK) return st;
+  iqp::IndexerQArgs p = make_args(a, lda, a_scales, as_stride_m, as_stride_w, w, ldw, w_scales, M,
+                                  K, H, positions, cos_sin, max_pos);
+  p.dbg = out;
+  return from_hip(iqp::launch_indexer_q(p, stage, static_cast<hipStream_t>(stream)));
+}
+
+int iqp_rope_cos_sin_table(double theta, int64_t max_pos, int32_t rope_dim, float* cos_sin,
+                           void* stream) {
+  if (max_pos < 0 || rope_dim <= 0 || rope_dim % 2 || !(theta > 0.0)) return IQP_ERR_INVALID;
+  if (max_pos == 0) return IQP_OK;
+  if (!cos_sin) return IQP_ERR_INVALID;
+  if (!aligned(cos_sin, 4)) return IQP_ERR_UNSUPPORTED;
+  const int st = device_status();
+  if (st != IQP_OK) return st;
+  return from_hip(iqp::launch_rope_table(theta, max_pos, rope_dim, cos_sin,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+const char* iqp_status_string(int status) {
+  switch (status) {
+    case IQP_OK: return "IQP_OK";
+    case IQP_ERR_INVALID: return "IQP_ERR_INVALID: invalid argument";
+    case IQP_ERR_UNSUPPORTED: return "IQP_ERR_UNSUPPORTED: outside the kernel's contract";
+    case IQP_ERR_HIP: return "IQP_ERR_HIP: HIP runtime or launch failure";
+    default: return "unknown iqprep status";
+  }
+}
+
+int iqp_abi_version(void) { return IQP_ABI_VERSION; }
+
+}  // extern "C"

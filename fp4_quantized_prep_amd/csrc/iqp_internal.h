@@ -1,0 +1,39 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace iqp {
+
+// Arguments of the fused indexer-Q kernel (validated on the host).
+struct IndexerQArgs {
+  const uint8_t* a;              // E4M3 activations [M, K], row stride lda bytes
+  int64_t lda;
+  const uint8_t* a_scale_bytes;  // packed UE8M0 words viewed as bytes
+  int64_t as_sm, as_sw;          // word strides (int32 units)
+  const uint8_t* w;              // E4M3 weights [H*128, K], row stride ldw bytes
+  int64_t ldw;
+  const uint8_t* w_scales;       // UE8M0 [H, K/128]
+  int64_t M;
+  int32_t nkb;                   // K / 128
+  int32_t H;
+  const int64_t* positions;      // [M]
+  const float* cos_sin;          // [max_pos, 64]
+  int64_t max_pos;
+  uint8_t* q_fp4;                // [M, H, 64]
+  uint8_t* q_scales;             // [M, H, 4]
+  float* dbg;                    // [M, H*128] for the diagnostic stages
+};
+
+hipError_t launch_fp8_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                            uint8_t* q, int64_t ldq, int32_t* scales,
+                            int64_t s_stride_m, int64_t s_stride_w, hipStream_t stream);
+
+// stage -1: FP4 output; 0, 1, 2: float32 diagnostics (see iqprep.h)
+hipError_t launch_indexer_q(const IndexerQArgs& args, int stage, hipStream_t stream);
+
+hipError_t launch_rope_table(double theta, int64_t max_pos, int32_t rope_dim,
+                             float* cos_sin, hipStream_t stream);
+
+}  // namespace iqp

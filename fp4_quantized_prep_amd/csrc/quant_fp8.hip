@@ -1,0 +1,135 @@
+// Packed-UE8M0 FP8 1x128 activation quantizer for gfx950.
+//
+// tokenspeed PR "perf(deepseek-v4): accelerate indexer Q and packed FP8
+// quantization", Summary (online FP8 activation quantization whose UE8M0 scale
+// exponents are packed four to an int32) and Risk and fallback (BF16 input with
+// K divisible by 128; the tiny-scale floor is kept).
+//
+// The work is HBM-bound (2 bytes in, 1 + 1/128 bytes out per element), so the
+// kernel is organised around wide, coalesced memory operations:
+//   * one wave64 owns one packed scale word = 4 blocks = 512 contiguous bf16 of
+//     a row (1 KiB); lane l loads 16 B (8 bf16), so the 16 lanes of a DPP row
+//     hold exactly one 128-element block;
+//   * the block amax is reduced with four DPP max steps inside the row, on the
+//     bf16 magnitude bits as integers (order-free and exact), with no LDS;
+//   * the scale exponent comes from the amax bits with integer arithmetic;
+//   * v_cvt_pk_fp8_f32 rounds x * 2^-e to E4M3 (OCP "fn", round to nearest
+//     even, subnormals kept); lanes store 8 B each, 512 B per wave contiguous;
+//   * the four block bytes are gathered with readlane and stored as one word;
+//   * each wave keeps QUNROLL words' loads in flight before converting.
+#include "iqp_internal.h"
+
+namespace iqp {
+namespace {
+
+constexpr int QWAVES = 4;   // waves per workgroup
+constexpr int QUNROLL = 4;  // scale words (1 KiB of input each) per wave
+
+// DPP controls (gfx9 encoding)
+constexpr int DPP_QUAD_XOR1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_ROW_MIRROR = 0x140;
+
+__device__ __forceinline__ uint32_t row16_max(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, DPP_QUAD_XOR1, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, DPP_QUAD_XOR2, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, DPP_ROW_HALF_MIRROR, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, DPP_ROW_MIRROR, 0xF, 0xF, false));
+  return v;
+}
+
+// Largest |bf16| of the two halves of a dword, as 15-bit magnitude codes.
+__device__ __forceinline__ uint32_t mag2(uint32_t d) {
+  return max(d & 0x7FFFu, (d >> 16) & 0x7FFFu);
+}
+
+// Scale exponent from the bf16 magnitude code of the block amax:
+// e = max(ceil(log2(amax / 448)), -22). With amax = (1 + f/128) 2^(E-127) and
+// 448 = (1 + 96/128) 2^8, amax/448 <= 2^(E-135) exactly when f <= 96. E = 0
+// (zero or subnormal amax) lands on the floor.
+__device__ __forceinline__ int block_exponent(uint32_t amag) {
+  const int E = (int)(amag >> 7);
+  const int f = (int)(amag & 0x7F);
+  const int e = E - 135 + (f > 96 ? 1 : 0);
+  return max(e, -22);
+}
+
+__device__ __forceinline__ uint32_t cvt4(uint32_t d0, uint32_t d1, float mul) {
+  // bf16 -> f32 is a 16-bit shift; element 2k is the low half of dword k
+  const float f0 = __uint_as_float(d0 << 16) * mul;
+  const float f1 = __uint_as_float(d0 & 0xFFFF0000u) * mul;
+  const float f2 = __uint_as_float(d1 << 16) * mul;
+  const float f3 = __uint_as_float(d1 & 0xFFFF0000u) * mul;
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, r, true);
+  return (uint32_t)r;
+}
+
+__global__ __launch_bounds__(QWAVES * 64)
+void fp8_quant_1x128_kernel(const uint16_t* __restrict__ x, int64_t ldx,
+                            uint8_t* __restrict__ q, int64_t ldq,
+                            int32_t* __restrict__ scales, int64_t sm, int64_t sw,
+                            int32_t nw, int32_t nkb, int64_t units) {
+  const int lane = threadIdx.x & 63;
+  const int blk = lane >> 4;  // block of this lane within the word
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t u0 = ((int64_t)blockIdx.x * QWAVES + wave) * QUNROLL;
+
+  uint4 d[QUNROLL];
+#pragma unroll
+  for (int i = 0; i < QUNROLL; ++i) {
+    const int64_t u = u0 + i;
+    d[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (u < units) {
+      const int64_t row = u / nw;
+      const int w = (int)(u - row * nw);
+      if (4 * w + blk < nkb)
+        d[i] = *reinterpret_cast<const uint4*>(x + row * ldx + (int64_t)w * 512 + lane * 8);
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < QUNROLL; ++i) {
+    const int64_t u = u0 + i;
+    if (u >= units) break;  // uniform across the wave
+    const int64_t row = u / nw;
+    const int w = (int)(u - row * nw);
+    const bool valid = 4 * w + blk < nkb;
+
+    uint32_t m = max(max(mag2(d[i].x), mag2(d[i].y)), max(mag2(d[i].z), mag2(d[i].w)));
+    m = row16_max(m);
+    const int e = block_exponent(m);
+    const float mul = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, a normal float
+
+    const uint32_t lo = cvt4(d[i].x, d[i].y, mul);
+    const uint32_t hi = cvt4(d[i].z, d[i].w, mul);
+    if (valid)
+      *reinterpret_cast<uint2*>(q + row * ldq + (int64_t)w * 512 + lane * 8) = make_uint2(lo, hi);
+
+    const uint32_t byte = valid ? (uint32_t)(e + 127) : 0u;
+    const uint32_t word = (uint32_t)__builtin_amdgcn_readlane((int)byte, 0) |
+                          ((uint32_t)__builtin_amdgcn_readlane((int)byte, 16) << 8) |
+                          ((uint32_t)__builtin_amdgcn_readlane((int)byte, 32) << 16) |
+                          ((uint32_t)__builtin_amdgcn_readlane((int)byte, 48) << 24);
+    if (lane == 0) scales[row * sm + (int64_t)w * sw] = (int32_t)word;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fp8_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                            uint8_t* q, int64_t ldq, int32_t* scales,
+                            int64_t s_stride_m, int64_t s_stride_w, hipStream_t stream) {
+  const int32_t nkb = (int32_t)(K / 128);
+  const int32_t nw = (nkb + 3) / 4;
+  const int64_t units = M * nw;
+  const int64_t per_block = (int64_t)QWAVES * QUNROLL;
+  const int64_t blocks = (units + per_block - 1) / per_block;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(fp8_quant_1x128_kernel, dim3((unsigned)blocks), dim3(QWAVES * 64), 0, stream,
+                     x, ldx, q, ldq, scales, s_stride_m, s_stride_w, nw, nkb, units);
+  return hipGetLastError();
+}
+
+}  // namespace iqp

@@ -1,0 +1,194 @@
+/*
+ * iqprep.h — C ABI of libiqprep.so: DeepSeek-V4 indexer-Q preparation on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The library computes, on the GPU, the two calls of indexer-Q preparation:
+ *
+ *   1. fp8_quant_1x128_ue8m0     packed-UE8M0 FP8 1x128 activation quantization
+ *      (tokenspeed PR "perf(deepseek-v4): accelerate indexer Q and packed FP8
+ *      quantization", Summary; input contract in Risk and fallback).
+ *   2. indexer_q_gemm_rope_fp4   block-scaled FP8 Q projection whose epilogue
+ *      applies RoPE, a 128-point Hadamard rotation and FP4 e2m1 quantization
+ *      (TensorRT-LLM PR "Fuse DeepSeek-V4 Indexer Q projection with CuTe DSL",
+ *      sequence diagram: FP8 input + UE8M0 scales in, packed FP4 Q and scales
+ *      out; the same tokenspeed PR, Summary: RoPE, Hadamard and FP4 make up
+ *      the Q preparation).
+ *
+ * Conventions shared by every entry point:
+ *
+ *   - Every data pointer is a caller-owned DEVICE pointer on the current HIP
+ *     device. The library never allocates, frees, copies or synchronizes; it
+ *     enqueues kernels on `stream` (a hipStream_t; NULL = the null stream) and
+ *     returns. Calls are therefore safe to capture into a HIP graph.
+ *   - Inputs are never modified.
+ *   - Sizes and leading dimensions are in elements of the named type unless
+ *     stated otherwise; all offsets are computed in 64-bit.
+ *   - Return value: IQP_OK, or an IQP_ERR_* code. Argument checks happen on
+ *     the host before anything is enqueued; on any error nothing is enqueued
+ *     (IQP_ERR_HIP: the launch itself failed). IQP_ERR_UNSUPPORTED means the
+ *     arguments are well formed but outside the fast path's contract, and the
+ *     caller should use another implementation: the library never falls back
+ *     silently.
+ *   - M == 0 is a successful no-op.
+ *   - Entry points are reentrant and thread-safe; the only global state is a
+ *     per-device cache of the device architecture, filled on first use.
+ *
+ * Number formats: E4M3 is the OCP OFP8 "fn" variant (bias 7, max 448, no
+ * infinities); E2M1 is OCP MX FP4 (magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6);
+ * a UE8M0 byte b means 2^(b-127).
+ */
+#ifndef IQPREP_H
+#define IQPREP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define IQP_OK              0
+#define IQP_ERR_INVALID     1  /* null pointer, negative size, leading dimension smaller than a row, overlapping scale strides */
+#define IQP_ERR_UNSUPPORTED 2  /* well formed but outside the contract (K % 128, alignment, head shape, device): use another path */
+#define IQP_ERR_HIP         3  /* a HIP runtime call or kernel launch failed */
+
+#define IQP_ABI_VERSION     1
+
+/*
+ * fp8_quant_1x128_ue8m0 — packed-UE8M0 FP8 activation quantization.
+ *
+ * tokenspeed PR "perf(deepseek-v4): accelerate indexer Q and packed FP8
+ * quantization", Summary (an online FP8 quantizer for DeepGEMM activations
+ * with UE8M0 scale exponents packed into int32 words) and Risk and fallback
+ * (a contiguous, aligned BF16 matrix with K divisible by 128; the existing
+ * tiny-scale floor is kept).
+ *
+ * For every row m and 128-element block j of x:
+ *   amax = max(max_k |x[m, 128j+k]|, 1e-4)          (1e-4: the tiny-scale floor)
+ *   e    = ceil(log2(amax / 448))                     exact; -22 <= e <= 120
+ *   q[m, 128j+k] = E4M3 round-to-nearest-even of x * 2^-e   (never saturates)
+ *   byte(m, j) = e + 127
+ * Four consecutive block bytes form one int32 word, block 4w+t in byte t
+ * (little-endian): word (m, w) = scales[m * s_stride_m + w * s_stride_w], for
+ * 0 <= w < ceil(K/512). Bytes for blocks past K/128 are written as zero.
+ *
+ *   x        bf16 [M, K], row stride ldx (elements, >= K); 16-byte aligned and
+ *            ldx a multiple of 8, else IQP_ERR_UNSUPPORTED.
+ *   q        E4M3 bytes [M, K], row stride ldq (bytes, >= K); 8-byte aligned
+ *            and ldq a multiple of 8, else IQP_ERR_UNSUPPORTED.
+ *   scales   int32 words, 4-byte aligned. Strides in int32 units; the two
+ *            supported layouts are K-major (s_stride_w == 1, s_stride_m >=
+ *            ceil(K/512)) and MN-major (s_stride_m == 1, s_stride_w >= M);
+ *            anything else is IQP_ERR_INVALID.
+ *   K        multiple of 128, else IQP_ERR_UNSUPPORTED.
+ *
+ * Inputs must be finite (NaN / Inf are outside the contract).
+ */
+int fp8_quant_1x128_ue8m0(const void* x, int64_t M, int64_t K, int64_t ldx,
+                          void* q, int64_t ldq,
+                          int32_t* scales, int64_t s_stride_m, int64_t s_stride_w,
+                          void* stream);
+
+/*
+ * indexer_q_gemm_rope_fp4 — fused block-scaled FP8 Q projection + RoPE +
+ * Hadamard-128 + FP4 e2m1 quantization, one launch.
+ *
+ * TensorRT-LLM PR "Fuse DeepSeek-V4 Indexer Q projection with CuTe DSL",
+ * sequence diagram (FP8 input and UE8M0 scales from the quantizer feed a GEMM
+ * with a RoPE and FP4 epilogue that returns packed FP4 Q and scales) and
+ * Description / Paths compared (the unfused chain: Q GEMM, RoPE kernel, FP4
+ * quantization kernel, scale copies); tokenspeed PR "perf(deepseek-v4):
+ * accelerate indexer Q and packed FP8 quantization", Summary (the Hadamard
+ * transform belongs to the optimized Q preparation).
+ *
+ * For every token m and head h (n = 128h + d, 0 <= d < 128):
+ *   Q[m, n]  = sum_j 2^(ea(m,j) + ew(h,j)) * sum_{k in block j} A[m,k] W[n,k]
+ *              (float32 accumulation)
+ *   RoPE     for i < 32, p = positions[m], c = cos_sin[p, i], s = cos_sin[p, 32+i]:
+ *              y_i = Q_i c - Q_{i+32} s,  y_{i+32} = Q_{i+32} c + Q_i s;  y_d = Q_d for d >= 64
+ *   Hadamard z = (H_128 / sqrt(128)) y,  H[r][c] = (-1)^popcount(r & c)
+ *   FP4      per 32-element block b: amax = max(max |z|, 1e-4),
+ *              e = ceil(log2(amax / 6)) (so e >= -15), q_scales[m, h, b] = e + 127,
+ *              codes = E2M1 round-to-nearest-even of z * 2^-e; two codes per
+ *              byte, element 2t in the low nibble.
+ * Q is never written to memory in any precision.
+ *
+ *   a          E4M3 [M, K] from fp8_quant_1x128_ue8m0, row stride lda (bytes);
+ *              16-byte aligned, lda a multiple of 16.
+ *   a_scales   the packed scale words that call wrote, with its strides
+ *              (as_stride_m, as_stride_w), same layout rules.
+ *   w          E4M3 weights [H*D, K], K contiguous, row stride ldw (bytes);
+ *              16-byte aligned, ldw a multiple of 16.
+ *   w_scales   UE8M0 bytes [H*D/128, K/128], row-major (one per 128x128 tile).
+ *   M          tokens (>= 0); K: multiple of 128; H >= 1; D must be 128 and
+ *              rope_dim 64 (else IQP_ERR_UNSUPPORTED).
+ *   positions  int64 [M]. A position outside [0, max_pos) is a precondition
+ *              violation: it is clamped into range (the row's output is then
+ *              meaningless, but no memory outside the table is read).
+ *   cos_sin    float32 [max_pos, rope_dim]: cos of the rotation angles in
+ *              columns [0, rope_dim/2), sin in [rope_dim/2, rope_dim); any
+ *              frequencies may be used (iqp_rope_cos_sin_table builds the
+ *              standard ones). 16-byte aligned; max_pos >= 1.
+ *   q_fp4      uint8 [M, H, D/2] packed E2M1 codes, 16-byte aligned.
+ *   q_scales   uint8 [M, H, D/32] UE8M0 bytes, 4-byte aligned.
+ *
+ * Q must fit float32: the output is undefined if |Q| would overflow, which
+ * needs an exponent sum ea + ew near 99 or above (|A W| <= 448^2 per term);
+ * activations from fp8_quant_1x128_ue8m0 and weights of ordinary magnitude
+ * are far inside that range.
+ */
+int indexer_q_gemm_rope_fp4(const void* a, int64_t lda,
+                            const int32_t* a_scales, int64_t as_stride_m, int64_t as_stride_w,
+                            const void* w, int64_t ldw,
+                            const uint8_t* w_scales,
+                            int64_t M, int64_t K, int32_t H, int32_t D, int32_t rope_dim,
+                            const int64_t* positions,
+                            const float* cos_sin, int64_t max_pos,
+                            uint8_t* q_fp4, uint8_t* q_scales,
+                            void* stream);
+
+/*
+ * iqp_rope_cos_sin_table — builds the standard RoPE table that
+ * indexer_q_gemm_rope_fp4 reads: for 0 <= p < max_pos and i < rope_dim/2,
+ *   cos_sin[p, i] = cos(p * theta^(-2i/rope_dim)),
+ *   cos_sin[p, rope_dim/2 + i] = sin(p * theta^(-2i/rope_dim)),
+ * evaluated in float64 on the device and rounded to float32 once.
+ * (tokenspeed PR "perf(deepseek-v4): accelerate indexer Q and packed FP8
+ * quantization", Summary: RoPE on the indexer Q; the base and layout are not
+ * on the page, theta = 10000 is the usual base.)
+ *
+ *   cos_sin   float32 [max_pos, rope_dim], 4-byte aligned. rope_dim even, > 0;
+ *             theta > 0; max_pos >= 0 (0: no-op).
+ */
+int iqp_rope_cos_sin_table(double theta, int64_t max_pos, int32_t rope_dim,
+                           float* cos_sin, void* stream);
+
+/*
+ * iqp_debug_indexer_q_f32 — diagnostic twin of indexer_q_gemm_rope_fp4 for
+ * parity testing of its stages: same inputs and same kernel, but instead of
+ * FP4 codes it writes float32 out[M, H*D] holding
+ *   stage 0: Q (the GEMM output),
+ *   stage 1: Q after RoPE,
+ *   stage 2: z (after RoPE and the normalized Hadamard rotation).
+ * out is 16-byte aligned; any other stage is IQP_ERR_INVALID.
+ */
+int iqp_debug_indexer_q_f32(const void* a, int64_t lda,
+                            const int32_t* a_scales, int64_t as_stride_m, int64_t as_stride_w,
+                            const void* w, int64_t ldw,
+                            const uint8_t* w_scales,
+                            int64_t M, int64_t K, int32_t H, int32_t D, int32_t rope_dim,
+                            const int64_t* positions,
+                            const float* cos_sin, int64_t max_pos,
+                            float* out, int32_t stage,
+                            void* stream);
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* iqp_status_string(int status);
+
+/* IQP_ABI_VERSION of the built library. */
+int iqp_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IQPREP_H */

@@ -1,0 +1,56 @@
+"""Helpers shared by the GPU parity tests: run the oracle on the same seeded
+inputs the device path gets, and build inputs with exact properties."""
+import numpy as np
+import torch
+
+from oracle import indexer_q as IQ
+from oracle import quant_fp8 as QO
+
+import synthetic as S
+
+
+def bf16_to_np(x: torch.Tensor) -> np.ndarray:
+    return x.float().cpu().numpy()
+
+
+def oracle_chain_from_x(x_bf16: torch.Tensor, w_codes: torch.Tensor, w_sb: torch.Tensor,
+                        positions: torch.Tensor, n_heads: int) -> dict:
+    """The oracle's whole chain (its own FP8 quantization, then the fused stages)."""
+    xn = bf16_to_np(x_bf16)
+    a_codes, a_words = QO.fp8_quant_1x128_ue8m0(xn)
+    a_sb = QO.unpack_scale_words(a_words, xn.shape[1] // 128)
+    out = IQ.indexer_q_chain(a_codes, a_sb, w_codes.numpy(), w_sb.numpy(), positions.numpy(),
+                             n_heads=n_heads)
+    out["a_codes"] = a_codes
+    out["a_words"] = a_words
+    return out
+
+
+def weights_for_heads(n_heads: int):
+    """The standard synthetic weights, cut to the first n_heads heads."""
+    codes, sb = S.weights()
+    return codes[: n_heads * 128].contiguous(), sb[:n_heads].contiguous()
+
+
+def exhaustive_quant_rows() -> np.ndarray:
+    """Rows of 128 bf16 values covering every (bf16 pattern, exponent e) pair
+    whose scaled value stays within E4M3 range: each row has one anchor element
+    whose magnitude fixes the block exponent to e, and 127 payload values with
+    |x| <= anchor. Returns float32 [rows, 128] holding bf16 values."""
+    bits = (np.arange(65536, dtype=np.uint32) << 16).view(np.float32)
+    finite = bits[np.isfinite(bits)]
+    rows = []
+    for e in range(-22, 121):
+        if e <= 119:
+            anchor = np.float32(448.0 * 2.0 ** e)
+        else:
+            anchor = np.uint32(0x7F7F0000).view(np.float32)    # largest bf16, exponent 120
+        payload = finite[np.abs(finite) <= anchor]
+        n = -(-len(payload) // 127)
+        padded = np.zeros(n * 127, dtype=np.float32)
+        padded[: len(payload)] = payload
+        blk = np.empty((n, 128), dtype=np.float32)
+        blk[:, 0] = anchor
+        blk[:, 1:] = padded.reshape(n, 127)
+        rows.append(blk)
+    return np.concatenate(rows)

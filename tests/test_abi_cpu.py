@@ -1,0 +1,106 @@
+"""The C-ABI library on the host: it loads without a GPU, exports every entry
+point include/iqprep.h declares, and rejects malformed arguments before it
+would touch a device (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "iqprep.h")
+
+
+@pytest.fixture(scope="module")
+def iqp():
+    import fp4_quantized_prep_amd as m
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    assert {"fp8_quant_1x128_ue8m0", "indexer_q_gemm_rope_fp4", "iqp_status_string",
+            "iqp_abi_version"} <= set(names)
+
+
+def test_library_exports_every_declared_symbol(iqp):
+    lib = ctypes.CDLL(iqp.library_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(iqp):
+    assert iqp.abi_version() == 1
+    for st in range(4):
+        assert iqp._lib.iqp_status_string(st)
+    assert b"unknown" in iqp._lib.iqp_status_string(99)
+
+
+P = ctypes.c_void_p
+
+
+def quant(iqp, x=16, M=4, K=128, ldx=128, q=16, ldq=128, s=16, sm=1, sw=1):
+    return iqp._lib.fp8_quant_1x128_ue8m0(P(x), M, K, ldx, P(q), ldq, P(s), sm, sw, None)
+
+
+def test_quant_argument_checks(iqp):
+    # fake, never-dereferenced addresses: every case fails before any device call
+    assert quant(iqp, M=-1) == iqp.IQP_ERR_INVALID
+    assert quant(iqp, x=0) == iqp.IQP_ERR_INVALID
+    assert quant(iqp, q=0) == iqp.IQP_ERR_INVALID
+    assert quant(iqp, s=0) == iqp.IQP_ERR_INVALID
+    assert quant(iqp, ldx=64) == iqp.IQP_ERR_INVALID
+    assert quant(iqp, K=100, ldx=128, ldq=128) == iqp.IQP_ERR_UNSUPPORTED
+    assert quant(iqp, x=24) == iqp.IQP_ERR_UNSUPPORTED        # not 16-byte aligned
+    assert quant(iqp, ldx=132) == iqp.IQP_ERR_UNSUPPORTED     # row pitch not a multiple of 16 B
+    assert quant(iqp, q=20) == iqp.IQP_ERR_UNSUPPORTED
+    assert quant(iqp, sm=1, sw=2) == iqp.IQP_ERR_INVALID      # MN-major with stride < M
+    assert quant(iqp, sm=2, sw=2) == iqp.IQP_ERR_INVALID      # neither layout
+    assert quant(iqp, M=0) == iqp.IQP_OK                      # empty: no-op
+    assert quant(iqp, x=0, q=0, s=0, M=0) == iqp.IQP_OK
+
+
+def fused(iqp, M=4, K=256, H=2, D=128, rd=64, a=16, lda=256, s=16, sm=1, sw=1, w=16, ldw=256,
+          ws=16, pos=16, cs=16, mp=10, q=16, qs=16):
+    return iqp._lib.indexer_q_gemm_rope_fp4(P(a), lda, P(s), sm, sw, P(w), ldw, P(ws), M, K, H, D, rd,
+                                            P(pos), P(cs), mp, P(q), P(qs), None)
+
+
+def test_fused_argument_checks(iqp):
+    assert fused(iqp, M=-3) == iqp.IQP_ERR_INVALID
+    assert fused(iqp, a=0) == iqp.IQP_ERR_INVALID
+    assert fused(iqp, pos=0) == iqp.IQP_ERR_INVALID
+    assert fused(iqp, q=0) == iqp.IQP_ERR_INVALID
+    assert fused(iqp, mp=0) == iqp.IQP_ERR_INVALID
+    assert fused(iqp, lda=128) == iqp.IQP_ERR_INVALID
+    assert fused(iqp, K=200, lda=256, ldw=256) == iqp.IQP_ERR_UNSUPPORTED
+    assert fused(iqp, D=64) == iqp.IQP_ERR_UNSUPPORTED
+    assert fused(iqp, rd=32) == iqp.IQP_ERR_UNSUPPORTED
+    assert fused(iqp, a=8) == iqp.IQP_ERR_UNSUPPORTED
+    assert fused(iqp, ldw=264) == iqp.IQP_ERR_UNSUPPORTED
+    assert fused(iqp, q=20) == iqp.IQP_ERR_UNSUPPORTED
+    assert fused(iqp, sm=3, sw=3) == iqp.IQP_ERR_INVALID
+    assert fused(iqp, M=0) == iqp.IQP_OK
+
+
+def test_debug_and_table_argument_checks(iqp):
+    lib = iqp._lib
+    args = [P(16), 256, P(16), 1, 1, P(16), 256, P(16), 4, 256, 2, 128, 64, P(16), P(16), 10]
+    assert lib.iqp_debug_indexer_q_f32(*args, P(16), 3, None) == iqp.IQP_ERR_INVALID
+    assert lib.iqp_debug_indexer_q_f32(*args, P(16), -1, None) == iqp.IQP_ERR_INVALID
+    assert lib.iqp_rope_cos_sin_table(10000.0, 10, 63, P(16), None) == iqp.IQP_ERR_INVALID
+    assert lib.iqp_rope_cos_sin_table(-1.0, 10, 64, P(16), None) == iqp.IQP_ERR_INVALID
+    assert lib.iqp_rope_cos_sin_table(10000.0, 10, 64, P(0), None) == iqp.IQP_ERR_INVALID
+    assert lib.iqp_rope_cos_sin_table(10000.0, 0, 64, P(0), None) == iqp.IQP_OK
+
+
+def test_python_wrapper_rejects_wrong_dtypes(iqp):
+    import torch
+    with pytest.raises(TypeError):
+        iqp.fp8_quant_1x128_ue8m0(torch.zeros(2, 128, dtype=torch.float32))

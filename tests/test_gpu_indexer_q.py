@@ -1,0 +1,218 @@
+"""GPU parity: fused indexer-Q kernel (block-scaled FP8 GEMM, RoPE,
+Hadamard-128, FP4) against the oracle.
+
+Stage-wise float32 checks go through the diagnostic entry point (same kernel,
+float32 output after the GEMM, after RoPE and after the Hadamard rotation);
+the FP4 output is checked with the acceptance rule (relative L2 <= 2e-2,
+boundary-only flips, at most 0.1 %). Token counts cover the pages' test set
+(1, 4, 5, 8, 128), ragged tails, the 4,632-token prefill (sampled tokens) and
+a 32,768-token heavy-tailed prefill (sampled tokens)."""
+import numpy as np
+import pytest
+import torch
+
+import synthetic as S
+from oracle import checker as C
+from oracle import formats as F
+from oracle import indexer_q as IQ
+from oracle import quant_fp8 as QO
+
+from gpu_util import oracle_chain_from_x, weights_for_heads
+
+pytestmark = pytest.mark.gpu
+
+THETA = S.ROPE_THETA
+
+
+@pytest.fixture(scope="module")
+def weights():
+    codes, sb = S.weights()
+    return codes, sb, codes.cuda(), sb.cuda()
+
+
+@pytest.fixture(scope="module")
+def table(gpu_lib):
+    return {mp: gpu_lib.rope_cos_sin_table(THETA, mp, 64) for mp in (4096, 4632, 32768, 131072)}
+
+
+def device_chain(iqp, x, wd, wsd, pos, cs, n_heads=64, layout="k"):
+    a, a_s = iqp.fp8_quant_1x128_ue8m0(x.cuda(), scale_layout=layout)
+    q, s = iqp.indexer_q_gemm_rope_fp4(a, a_s, wd, wsd, pos.cuda(), cs, n_heads=n_heads)
+    torch.cuda.synchronize()
+    return a, a_s, q.cpu().numpy(), s.cpu().numpy()
+
+
+def test_rope_table_matches_oracle(gpu_lib, table):
+    for mp, t in table.items():
+        got = t.cpu().numpy().astype(np.float64)
+        rows = np.unique(np.concatenate([np.arange(min(mp, 64)), np.random.default_rng(mp).integers(0, mp, 256), [mp - 1]]))
+        want = IQ.rope_cos_sin_table(THETA, mp, 64)[rows]
+        tol = np.spacing(np.abs(want).astype(np.float32)).astype(np.float64) + 1e-10
+        assert np.all(np.abs(got[rows] - want) <= tol), mp
+
+
+def mfma_error_bound(a_codes, a_sb, w_codes, w_sb):
+    """Per-element bound on |Q_device - Q_exact| for the FP8 matrix cores.
+
+    Measured on gfx950: one 64-deep FP8 MFMA returns its dot product with an
+    error of at most about 2^-11.3 of the largest product term (median 2^-14.5;
+    every FP8 MFMA form behaves alike), i.e. products are summed at a fixed
+    precision below the largest one rather than in float32. The bound allows
+    2^-9 (64 terms x 2^-15) of max|A| * max|W| per 64-deep chunk, times the
+    block scales, plus float32 rounding of the running sum.
+    """
+    A = F.e4m3_decode(a_codes)
+    W = F.e4m3_decode(w_codes)
+    M, K = A.shape
+    nc = K // 64
+    amax = np.abs(A).reshape(M, nc, 64).max(-1) * np.repeat(np.ldexp(1.0, a_sb.astype(np.int64) - 127), 2, axis=1)
+    wsc = np.repeat(np.repeat(np.ldexp(1.0, w_sb.astype(np.int64) - 127), 128, axis=0), 2, axis=1)
+    wmax = np.abs(W).reshape(W.shape[0], nc, 64).max(-1) * wsc
+    return 2.0 ** -9 * (amax @ wmax.T)
+
+
+def test_gemm_rope_hadamard_stages_float32(gpu_lib, weights, table):
+    codes, sb, wd, wsd = weights
+    inp = S.indexer_q_inputs("indexer_q_m128")
+    x, pos = inp["x"], inp["positions"]
+    ref = oracle_chain_from_x(x, codes, sb, pos, 64)
+    a, a_s = gpu_lib.fp8_quant_1x128_ue8m0(x.cuda())
+    cs = table[4096]
+    M = x.shape[0]
+    a_sb = QO.unpack_scale_words(ref["a_words"], 12)
+    bound = mfma_error_bound(ref["a_codes"], a_sb, codes.numpy(), sb.numpy()) + 2.0 ** -20 * np.abs(ref["q"].reshape(M, -1))
+    head_bound = np.linalg.norm(bound.reshape(M, 64, 128), axis=2)
+    for stage, key in ((0, "q"), (1, "q_rope"), (2, "z")):
+        out = gpu_lib.debug_indexer_q_f32(a, a_s, wd, wsd, pos.cuda(), cs, stage).cpu().numpy()
+        want = ref[key].reshape(M, -1)
+        err = C.rel_l2(out, want)
+        print(f"stage {stage}: rel_l2 {err:.3e}, max |err|/bound {np.max(np.abs(out - want) / bound):.3e}")
+        assert err <= 2e-4, (stage, err)
+        if stage == 0:
+            assert np.all(np.abs(out - want) <= bound), stage
+        else:
+            # RoPE is a rotation and the normalised Hadamard is orthonormal:
+            # the error norm of each head cannot grow past the GEMM's
+            d = np.linalg.norm((out - want).reshape(M, 64, 128), axis=2)
+            assert np.all(d <= head_bound * (1 + 1e-3) + 1e-6 * np.linalg.norm(ref[key], axis=2)), stage
+
+
+@pytest.mark.parametrize("M", [1, 4, 5, 8, 16, 128, 300])
+def test_fused_chain_small_and_ragged(gpu_lib, weights, table, M):
+    codes, sb, wd, wsd = weights
+    inp = S.indexer_q_inputs("indexer_q_m128", M=M)
+    x, pos = inp["x"], inp["positions"]
+    _, _, q, s = device_chain(gpu_lib, x, wd, wsd, pos, table[4096])
+    ref = oracle_chain_from_x(x, codes, sb, pos, 64)
+    rep = C.check_fp4(q, s, ref["z"], ref["q_fp4"], ref["q_scales"])
+    print(f"M={M}", rep)
+    assert rep["ok"], rep
+
+
+def test_fused_chain_mn_major_scales(gpu_lib, weights, table):
+    codes, sb, wd, wsd = weights
+    inp = S.indexer_q_inputs("indexer_q_m128", M=77)
+    x, pos = inp["x"], inp["positions"]
+    _, _, q, s = device_chain(gpu_lib, x, wd, wsd, pos, table[4096], layout="mn")
+    ref = oracle_chain_from_x(x, codes, sb, pos, 64)
+    assert C.check_fp4(q, s, ref["z"], ref["q_fp4"], ref["q_scales"])["ok"]
+
+
+@pytest.mark.parametrize("H", [1, 3, 8])
+def test_fused_chain_other_head_counts(gpu_lib, table, H):
+    codes, sb = weights_for_heads(H)
+    inp = S.indexer_q_inputs("indexer_q_m128", M=70)
+    x, pos = inp["x"], inp["positions"]
+    _, _, q, s = device_chain(gpu_lib, x, codes.cuda(), sb.cuda(), pos, table[4096], n_heads=H)
+    ref = oracle_chain_from_x(x, codes, sb, pos, H)
+    assert C.check_fp4(q, s, ref["z"], ref["q_fp4"], ref["q_scales"])["ok"]
+
+
+def _sampled_check(iqp, weights, x, pos, cs, n_sample, seed):
+    codes, sb, wd, wsd = weights
+    _, _, q, s = device_chain(iqp, x, wd, wsd, pos, cs)
+    M = x.shape[0]
+    rows = np.random.default_rng(seed).choice(M, n_sample, replace=False)
+    rows = np.unique(np.concatenate([rows, [0, M - 1]]))
+    ref = oracle_chain_from_x(x[rows], codes, sb, pos[rows], 64)
+    rep = C.check_fp4(q[rows], s[rows], ref["z"], ref["q_fp4"], ref["q_scales"])
+    print(f"M={M} sampled", rep)
+    assert rep["ok"], rep
+
+
+def test_fused_chain_m4632_sampled(gpu_lib, weights, table):
+    inp = S.indexer_q_inputs("indexer_q_m4632")
+    _sampled_check(gpu_lib, weights, inp["x"], inp["positions"], table[4632], 384, 1)
+
+
+def test_fused_chain_m32768_student_t_sampled(gpu_lib, weights, table):
+    inp = S.indexer_q_inputs("prefill_m32768")
+    _sampled_check(gpu_lib, weights, inp["x"], inp["positions"], table[32768], 384, 2)
+
+
+def test_decode_calls_large_positions(gpu_lib, weights, table):
+    codes, sb, wd, wsd = weights
+    for call in S.decode_calls(12):
+        x, pos = call["x"], call["positions"]
+        _, _, q, s = device_chain(gpu_lib, x, wd, wsd, pos, table[131072])
+        ref = oracle_chain_from_x(x, codes, sb, pos, 64)
+        rep = C.check_fp4(q, s, ref["z"], ref["q_fp4"], ref["q_scales"])
+        assert rep["ok"], (x.shape, rep)
+
+
+def test_every_output_byte_written_and_no_overrun(gpu_lib, weights, table):
+    codes, sb, wd, wsd = weights
+    inp = S.indexer_q_inputs("indexer_q_m128", M=37)
+    x, pos = inp["x"].cuda(), inp["positions"].cuda()
+    a, a_s = gpu_lib.fp8_quant_1x128_ue8m0(x)
+    M, H = 37, 64
+    results = []
+    for fill in (0x00, 0xFF):
+        qbuf = torch.full((M * H * 64 + 256,), fill, dtype=torch.uint8, device="cuda")
+        sbuf = torch.full((M * H * 4 + 256,), fill, dtype=torch.uint8, device="cuda")
+        q = qbuf[128:128 + M * H * 64].view(M, H, 64)
+        s = sbuf[128:128 + M * H * 4].view(M, H, 4)
+        gpu_lib.indexer_q_gemm_rope_fp4(a, a_s, wd, wsd, pos, table[4096], q_fp4=q, q_scales=s)
+        qh, sh = qbuf.cpu().numpy(), sbuf.cpu().numpy()
+        for buf, n in ((qh, M * H * 64), (sh, M * H * 4)):
+            assert np.all(buf[:128] == fill) and np.all(buf[128 + n:] == fill)
+        results.append((q.cpu(), s.cpu()))
+    assert torch.equal(results[0][0], results[1][0]) and torch.equal(results[0][1], results[1][1])
+
+
+def test_graph_capture_replays_match_eager(gpu_lib, weights, table):
+    codes, sb, wd, wsd = weights
+    inp = S.indexer_q_inputs("indexer_q_m128")
+    x, pos = inp["x"].cuda(), inp["positions"].cuda()
+    cs = table[4096]
+    q_e, s_e = gpu_lib.indexer_q_prep(x, wd, wsd, pos, cs)
+    q_e, s_e = q_e.clone(), s_e.clone()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        gpu_lib.indexer_q_prep(x, wd, wsd, pos, cs)          # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(stream)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        q_g, s_g = gpu_lib.indexer_q_prep(x, wd, wsd, pos, cs)
+    for _ in range(5):
+        q_g.zero_()
+        s_g.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(q_g, q_e) and torch.equal(s_g, s_e)
+        # eager work between replays
+        gpu_lib.indexer_q_prep(x, wd, wsd, pos, cs)
+        torch.cuda.synchronize()
+
+
+def test_unsupported_shapes_raise(gpu_lib, weights, table):
+    codes, sb, wd, wsd = weights
+    x = S.indexer_q_inputs("indexer_q_m128", M=4)["x"].cuda()
+    a, a_s = gpu_lib.fp8_quant_1x128_ue8m0(x)
+    pos = torch.zeros(4, dtype=torch.int64, device="cuda")
+    with pytest.raises(gpu_lib.IqpError) as e:
+        gpu_lib.indexer_q_gemm_rope_fp4(a, a_s, wd[:8192], wsd, pos, table[4096][:, :32].contiguous(),
+                                        rope_dim=32)
+    assert e.value.status == gpu_lib.IQP_ERR_UNSUPPORTED
