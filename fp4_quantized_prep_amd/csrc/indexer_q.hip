@@ -29,6 +29,8 @@
 //     (1.5 MiB at K = 1536) stay in that XCD's L2 while tokens stream.
 //   * Q never leaves registers; each lane writes 32 contiguous bytes of packed
 //     codes per token and head, and one lane per pair writes the 4 scale bytes.
+#include <atomic>
+
 #include "iqp_internal.h"
 
 namespace iqp {
@@ -80,9 +82,29 @@ __device__ __forceinline__ int fp4_exponent(float amax) {
 //   d = 32 tn + 8 (r >> 2) + 4 half + (r & 3)
 // of token t (lane % 32 of the tile). RoPE, the seven Hadamard stages and the
 // FP4 quantization all run on these registers.
+// cos / sin of the RoPE pairs one lane rotates (its 16 of the 32 pairs), from
+// the table row of its token's position (clamped to the table).
+struct RopeCS {
+  v4f c[4], s[4];
+};
+
+__device__ __forceinline__ RopeCS load_rope(int64_t t, int half, const IndexerQArgs& p) {
+  const int64_t tc = t < p.M ? t : p.M - 1;
+  int64_t pos = p.positions[tc];
+  pos = pos < 0 ? 0 : (pos >= p.max_pos ? p.max_pos - 1 : pos);
+  const float* cs = p.cos_sin + pos * 64;
+  RopeCS r;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    r.c[g] = *reinterpret_cast<const v4f*>(cs + 8 * g + 4 * half);
+    r.s[g] = *reinterpret_cast<const v4f*>(cs + 32 + 8 * g + 4 * half);
+  }
+  return r;
+}
+
 template <int STAGE>
 __device__ __forceinline__ void epilogue_tile(const v16f (&acc)[4], int64_t t, int head, bool store,
-                                              int half, const IndexerQArgs& p) {
+                                              int half, const IndexerQArgs& p, const RopeCS& rcs) {
   const int64_t tc = t < p.M ? t : p.M - 1;
   const bool live = store && t < p.M;
   float v[4][16];
@@ -107,13 +129,10 @@ __device__ __forceinline__ void epilogue_tile(const v16f (&acc)[4], int64_t t, i
 
   // RoPE on dims 0..63: the pair (i, i + 32), i = 8 g + 4 half + s, lives in
   // v[0][4g+s] and v[1][4g+s].
-  int64_t pos = p.positions[tc];
-  pos = pos < 0 ? 0 : (pos >= p.max_pos ? p.max_pos - 1 : pos);
-  const float* cs = p.cos_sin + pos * 64;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    const v4f cc = *reinterpret_cast<const v4f*>(cs + 8 * g + 4 * half);
-    const v4f ss = *reinterpret_cast<const v4f*>(cs + 32 + 8 * g + 4 * half);
+    const v4f cc = rcs.c[g];
+    const v4f ss = rcs.s[g];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const float x = v[0][4 * g + s], y = v[1][4 * g + s];
@@ -237,31 +256,50 @@ __device__ __forceinline__ void epilogue_tile(const v16f (&acc)[4], int64_t t, i
 }
 
 // ---------------------------------------------------------------------------
-// Main kernel. Workgroup tile: 256 weight rows (a pair of heads) x 256 tokens,
-// 8 waves; wave w owns head 2*pair + (w & 1) and tokens 64 (w >> 1) .. +63,
-// i.e. a 128 x 64 sub-tile held as 4 x 2 accumulators of 32 x 32.
+// Main kernel. One workgroup of 4 waves (one per SIMD) owns a pair of heads
+// (256 weight rows) and a contiguous range of tokens, which it walks in tiles
+// of up to 256 tokens (8 sub-tiles of 32). Wave w computes head 2 pair + (w&1)
+// for the sub-tiles s of the tile with s % 2 == w >> 1 (up to 4 of them), as
+// 4 x NTM accumulators of 32 x 32 (up to 256 registers, the matrix-core
+// accumulator file).
 //
-// Per 128-deep K block both operand tiles (W 256 x 128 B and A 256 x 128 B)
-// are copied global -> LDS by global_load_lds_dwordx4 (no staging registers):
-// one instruction moves 1 KiB = 8 rows, lane i writing bytes 16 i of it. Row
-// r's 16-byte chunks are stored XOR-swizzled (chunk c at slot c ^ (r % 8)),
-// so a lane loads the global chunk whose swizzled slot is its own, and the
-// MFMA operand reads (8 consecutive rows, one chunk column) hit distinct banks.
-// Two stages double-buffer the K loop; the barrier is a bare s_barrier with
-// explicit wait counts so the next stage's copies stay in flight.
-constexpr int NWAVES = 8;
+// Per 128-deep K block both operand tiles (W 256 x 128 B, A 256 x 128 B) and
+// the tokens' scale words are copied global -> LDS by buffer loads that write
+// LDS directly (no staging registers): one dwordx4 copy moves 8 full 128-byte
+// rows, lane i writing bytes 16 i. Buffer bounds return zeros for rows past
+// the last token or head. Row r's 16-byte chunks are stored XOR-swizzled
+// (chunk c at slot c ^ (r % 8)), so the MFMA operand reads (8 consecutive
+// rows, one chunk column) hit distinct banks. Two stages double-buffer the K
+// loop with one barrier per block, placed between the block's two 64-deep
+// halves:
+//
+//   read (j, second half) -> MFMAs (j, first half) -> barrier -> copies of
+//   block j+2 into j's stage, reads of (j+1, first half), MFMAs (j, second half)
+//
+// so every wave's MFMAs run on operands read one half-step earlier, and the
+// copies are spread among the MFMAs instead of stalling them. The last block
+// of a tile starts the copies of the next tile's first two blocks, which land
+// while the epilogue runs.
+constexpr int NWAVES = 4;
 constexpr int NTHREADS = NWAVES * 64;
-constexpr int TILE_ROWS = 256;                    // weight rows (2 heads) and tokens per workgroup
-constexpr int TILE_BYTES = TILE_ROWS * KB;        // one operand tile of one K block: 32 KiB
-constexpr int SLAB = 1024;                        // bytes written by one wave-wide LDS copy
-constexpr int COPIES = TILE_BYTES / SLAB / NWAVES;  // per operand per wave per stage: 4
-constexpr int VM_PER_STAGE = 2 * COPIES + 1;       // operand copies + the scale-word copy
-constexpr int SCALE_OFF = 2 * TILE_BYTES;           // scale words after the two operand tiles
-constexpr int STAGE_BYTES = SCALE_OFF + NWAVES * 256;
+constexpr int TILE_ROWS = 256;                       // weight rows (2 heads) and most tokens per tile
+constexpr int SUB = 32;                              // tokens per MFMA column tile
+constexpr int MAX_SUB = TILE_ROWS / SUB;             // sub-tiles per tile
+constexpr int MAX_TM = MAX_SUB / 2;                  // sub-tiles per wave
+constexpr int TILE_BYTES = TILE_ROWS * KB;           // one operand tile of one K block: 32 KiB
+constexpr int SLAB = 1024;                           // bytes written by one wave-wide LDS copy
+constexpr int COPIES = TILE_BYTES / SLAB / NWAVES;   // per operand per wave per block: 8
+// LDS: W stages at [0, 64K), A stages at [64K, 128K), then two stages of the
+// tile's 256 token scale words; every operand read is a lane base + immediate.
+constexpr int W_OFF = 0;
+constexpr int A_OFF = 2 * TILE_BYTES;
+constexpr int S_OFF = 4 * TILE_BYTES;
+constexpr int LDS_BYTES = S_OFF + 2 * TILE_ROWS * 4;
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14)
-constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+constexpr int WAITCNT_VM0 = 0 | (7 << 4) | (15 << 8) | (0 << 14);
 constexpr int WAITCNT_LGKM0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);
+constexpr int BUFFER_FLAGS = 0x00020000;   // raw untyped buffer, 32-bit data format
 
 __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
@@ -270,150 +308,368 @@ __device__ __forceinline__ void block_barrier() {
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
-template <int STAGE>
-__global__ __launch_bounds__(NTHREADS, 1)
-void indexer_q_kernel(IndexerQArgs p) {
-  // per stage: W tile, A tile, then the scale words [wave][64 tokens]
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][STAGE_BYTES];
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint64_t bytes) {
+  const uint32_t n = bytes > 0xFFFFFFF0ull ? 0xFFFFFFF0u : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)n, BUFFER_FLAGS);
+}
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int half = lane >> 5;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hn = wave & 1;          // head of the pair
-  const int q = wave >> 1;          // token quarter (64 tokens)
+template <int NTM>
+struct Frags {
+  v8i a[NTM > 0 ? NTM : 1];
+  v8i w[4];
+};
 
-  // ---- workgroup -> (head pair, token tile); XCD-aware when the pair count
-  // is a multiple of 8 (consecutive workgroup ids go to consecutive XCDs)
-  const int bid = blockIdx.x;
-  const int npairs = (p.H + 1) >> 1;
-  int pair, mtile;
-  if ((npairs & 7) == 0) {
-    const int ppx = npairs >> 3;
-    const int s = bid >> 3;
-    pair = (bid & 7) * ppx + s % ppx;
-    mtile = s / ppx;
-  } else {
-    pair = bid % npairs;
-    mtile = bid / npairs;
-  }
-  const int head = 2 * pair + hn;
-  const int head_c = head < p.H ? head : p.H - 1;   // odd H: the last pair's second head is a clamped copy, never stored
-  const int64_t mbase = (int64_t)mtile * TILE_ROWS;
-  const int nkb = p.nkb;
+struct Ctx {
+  const IndexerQArgs& p;
+  uint8_t* lds;
+  int lane, half, wave, hn, th;
+  int nkb;
+  int head;
+  uint32_t wsc_lane;
+  const uint8_t* wsc;
+  rsrc_t rw, ra, rs;                 // weights of the pair; activations and scale words of the tile
+  uint32_t vw, va, vs;               // this lane's byte offsets into them
+  uint32_t rd_w[2][2], rd_a[2][2];   // LDS operand-read bases [kh][lo/hi]
+  uint32_t rd_s;
 
-  // ---- LDS-copy sources: for copy i this lane lands in row r = 8 slab + lane/8,
-  // slot lane%8, which holds the row's chunk c = (lane%8) ^ (r%8).
-  const int chunk = (lane & 7) ^ ((lane >> 3) & 7);
-  const uint8_t* wsrc[COPIES];
-  const uint8_t* asrc[COPIES];
-  const int64_t wrow_max = (int64_t)p.H * HEAD_DIM - 1;
+  __device__ Ctx(const IndexerQArgs& p_, uint8_t* lds_, int pair) : p(p_), lds(lds_) {
+    const int tid = threadIdx.x;
+    lane = tid & 63;
+    half = lane >> 5;
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    hn = wave & 1;
+    th = wave >> 1;
+    nkb = p.nkb;
+    head = 2 * pair + hn;
+    const int head_c = head < p.H ? head : p.H - 1;   // odd H: the missing head reads zeros, never stored
+    wsc = p.w_scales + (int64_t)head_c * nkb;
+    wsc_lane = lane < nkb ? wsc[lane] : 0u;
+    // copy i of this wave lands in rows 8 (wave + 4 i) + lane / 8, slot lane % 8,
+    // which holds the row's chunk (lane % 8) ^ (row % 8)
+    const int chunk = (lane & 7) ^ ((lane >> 3) & 7);
+    const int64_t row0 = (int64_t)2 * pair * HEAD_DIM;
+    const int64_t wrows = (int64_t)p.H * HEAD_DIM - row0;
+    rw = make_rsrc(p.w + row0 * p.ldw, (uint64_t)(wrows < TILE_ROWS ? wrows : TILE_ROWS) * p.ldw);
+    vw = (uint32_t)((8 * wave + (lane >> 3)) * p.ldw + 16 * chunk);
+    va = (uint32_t)((8 * wave + (lane >> 3)) * p.lda + 16 * chunk);
+    vs = (uint32_t)(4 * (64 * wave + lane) * p.as_sm);
+    // operand reads: A row 64 tm + 32 th + lane % 32, W row 128 hn + 32 tn + lane % 32;
+    // all row bases are multiples of 8, so the swizzle term row % 8 is lane % 8
 #pragma unroll
-  for (int i = 0; i < COPIES; ++i) {
-    const int r = 8 * (wave + NWAVES * i) + (lane >> 3);
-    int64_t wr = (int64_t)2 * pair * HEAD_DIM + r;
-    wr = wr < wrow_max ? wr : wrow_max;
-    wsrc[i] = p.w + wr * p.ldw + 16 * chunk;
-    int64_t t = mbase + r;
-    t = t < p.M ? t : p.M - 1;
-    asrc[i] = p.a + t * p.lda + 16 * chunk;
-  }
-  // ---- scale-word copies: lane l fetches the packed UE8M0 word of token
-  // mbase + 64 q + l (one 256-byte LDS copy per wave per stage); a lane's two
-  // MFMA tokens are entries 32 tm + lane%32 of its wave's copy.
-  const uint8_t* ssrc;
-  {
-    int64_t t = mbase + 64 * q + lane;
-    t = t < p.M ? t : p.M - 1;
-    ssrc = p.a_scale_bytes + 4 * t * p.as_sm;
-  }
-  // ---- the head's weight-scale bytes, lane j holding K block 64 c + j of
-  // chunk c; read back per K block with readlane (a scalar, no memory op)
-  const uint8_t* wsc = p.w_scales + (int64_t)head_c * nkb;
-  uint32_t wsc_lane = lane < nkb ? wsc[lane] : 0u;
-
-  auto issue_stage = [&](int j, int st) {
+    for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-    for (int i = 0; i < COPIES; ++i) {
-      __builtin_amdgcn_global_load_lds((const void*)(wsrc[i] + (int64_t)KB * j),
-                                       (lds_void*)(&lds[st][SLAB * (wave + NWAVES * i)]), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(asrc[i] + (int64_t)KB * j),
-                                       (lds_void*)(&lds[st][TILE_BYTES + SLAB * (wave + NWAVES * i)]), 16, 0, 0);
+      for (int e = 0; e < 2; ++e) {
+        const uint32_t col = 16 * ((4 * kh + 2 * half + e) ^ (lane & 7));
+        rd_w[kh][e] = W_OFF + KB * (HEAD_DIM * hn + (lane & 31)) + col;
+        rd_a[kh][e] = A_OFF + KB * (32 * th + (lane & 31)) + col;
+      }
+    rd_s = S_OFF + 4 * (32 * th + (lane & 31));
+  }
+
+  // buffers of the tile whose first token is tbase
+  // (tbase = M: an empty range, every copy reads zeros)
+  __device__ __forceinline__ void set_tile(int64_t tbase) {
+    const int64_t rows = p.M - tbase;
+    const int64_t nw = (nkb + 3) / 4;
+    ra = make_rsrc(p.a + tbase * p.lda, rows > 0 ? (uint64_t)rows * p.lda : 0);
+    rs = make_rsrc(p.a_scale_bytes + 4 * tbase * p.as_sm,
+                   rows > 0 ? 4 * (uint64_t)((rows - 1) * p.as_sm + (nw - 1) * p.as_sw + 1) : 0);
+  }
+
+  // One of the 2 COPIES + 1 copies of K block j of the current tile into stage
+  // ST: w < COPIES a W slab, w < 2 COPIES an A slab, else the scale words.
+  // The whole offset goes in the lane offset, which the buffer bounds check
+  // covers (the scalar offset is not checked): a row past the buffer's last
+  // valid row starts at or beyond its size, so it reads zeros. The uniform
+  // part passes through readfirstlane so it is formed here, not hoisted.
+  template <int ST>
+  __device__ __forceinline__ void copy(int w, int j) {
+    if (w < COPIES) {
+      const uint32_t u = __builtin_amdgcn_readfirstlane((int)(32 * w * p.ldw + KB * j));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(lds + W_OFF + ST * TILE_BYTES + SLAB * (wave + NWAVES * w)),
+                                               16, vw + u, 0, 0, 0);
+    } else if (w < 2 * COPIES) {
+      const int i = w - COPIES;
+      const uint32_t u = __builtin_amdgcn_readfirstlane((int)(32 * i * p.lda + KB * j));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(lds + A_OFF + ST * TILE_BYTES + SLAB * (wave + NWAVES * i)),
+                                               16, va + u, 0, 0, 0);
+    } else {
+      const uint32_t u = __builtin_amdgcn_readfirstlane((int)(4 * (j >> 2) * p.as_sw));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + S_OFF + ST * TILE_ROWS * 4 + 256 * wave), 4,
+                                               vs + u, 0, 0, 0);
     }
-    __builtin_amdgcn_global_load_lds((const void*)(ssrc + 4 * (int64_t)(j >> 2) * p.as_sw),
-                                     (lds_void*)(&lds[st][SCALE_OFF + 256 * wave]), 4, 0, 0);
-  };
+  }
 
-  v16f acc[2][4];
+  // 16 operand bytes of half kh, column e (lo / hi 16 bytes of the lane's 32)
+  // of the A row 64 tm + 32 th + lane % 32 (rowoff = 64 tm) or the W row
+  // 128 hn + 32 tn + lane % 32 (rowoff = 32 tn), in stage ST
+  template <int ST>
+  __device__ __forceinline__ v4u read16(bool is_a, int kh, int e, int rowoff) const {
+    const uint32_t base = is_a ? rd_a[kh][e] : rd_w[kh][e];
+    return *reinterpret_cast<const v4u*>(lds + base + ST * TILE_BYTES + KB * rowoff);
+  }
+
+  // scale byte of block j for sub-tile tm (the packed word shifted to byte 0)
+  template <int ST>
+  __device__ __forceinline__ int read_scale(int tm, int j) const {
+    return (int)(*reinterpret_cast<const uint32_t*>(lds + rd_s + ST * TILE_ROWS * 4 + 4 * 64 * tm) >> (8 * (j & 3)));
+  }
+};
+
+// One half-step of the K loop, scheduled by hand: slot s issues MFMA s of the
+// 4 x NTM on the operands F (W tile tn = s / NTM, token tile tm = s % NTM),
+// then its share of the copies and of the LDS reads that fill N, the operands
+// of the next half-step. A scheduling fence closes every slot, so the order
+// below is the issue order: no copy or read waits behind a run of MFMAs, and
+// every MFMA's operands were read one half-step earlier.
+//   RKH >= 0: read the 64-deep half RKH of the block in stage RST into N;
+//   RSC: also the scale bytes of block jr (stage RST) into asn;
+//   NBLK copy blocks: block jd + b into stage (DST + b) & 1.
+template <int NTM, int RST, int RKH, bool RSC, int NBLK, int DST>
+__device__ __forceinline__ void half_step(Ctx& c, v16f (&acc)[MAX_TM][4], const Frags<NTM>& F,
+                                          const int (&as)[MAX_TM], int ws, Frags<NTM>& N, int (&asn)[MAX_TM],
+                                          int jr, int jd) {
+  constexpr int NM = 4 * NTM;
+  constexpr int NS = NM > 0 ? NM : 1;
+  constexpr int NCOPY = NBLK * (2 * COPIES + 1);
+  constexpr int NREAD = RKH >= 0 ? NTM + 4 + (RSC ? NTM : 0) : 0;   // whole fragments, then scale bytes
 #pragma unroll
-  for (int tm = 0; tm < 2; ++tm)
+  for (int slot = 0; slot < NS; ++slot) {
+    if (slot < NM) {
+      const int tn = slot / (NTM > 0 ? NTM : 1), tm = slot % (NTM > 0 ? NTM : 1);
+      acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.w[tn], F.a[tm], acc[tm][tn], 0, 0, 0, ws, 0,
+                                                                    as[tm]);
+    }
+#pragma unroll
+    for (int k = NCOPY * slot / NS; k < NCOPY * (slot + 1) / NS; ++k) {
+      const int b = k / (2 * COPIES + 1), w = k % (2 * COPIES + 1);
+      if ((DST + b) & 1)
+        c.copy<1>(w, jd + b);
+      else
+        c.copy<0>(w, jd + b);
+    }
+#pragma unroll
+    for (int r = NREAD * slot / NS; r < NREAD * (slot + 1) / NS; ++r) {
+      // a fragment is replaced whole: a partial update would keep the
+      // previous one (the operands of the half-step before) alive
+      if (r < NTM) {
+        N.a[r] = make_v8i(c.read16<RST>(true, RKH, 0, 64 * r), c.read16<RST>(true, RKH, 1, 64 * r));
+      } else if (r < NTM + 4) {
+        const int tn = r - NTM;
+        N.w[tn] = make_v8i(c.read16<RST>(false, RKH, 0, 32 * tn), c.read16<RST>(false, RKH, 1, 32 * tn));
+      } else {
+        asn[r - NTM - 4] = c.read_scale<RST>(r - NTM - 4, jr);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+enum { MODE_STEADY, MODE_NOCOPY, MODE_LAST };
+
+// One K block j in stage ST: the first half's MFMAs (reading the second
+// half), the block barrier, then the second half's MFMAs with the copies and
+// reads the mode asks for:
+//   STEADY: copy block j+2 into stage ST, read block j+1's first half;
+//   NOCOPY: read block j+1's first half;
+//   LAST:   copy blocks 0 and 1 of the next tile (whose buffers are set here)
+//           into stages 0 and 1; the RoPE table rows of the epilogue's first
+//           sub-tile are fetched before the barrier.
+template <int NTM, int MODE, int ST>
+__device__ __forceinline__ void k_block(Ctx& c, int j, v16f (&acc)[MAX_TM][4], Frags<NTM>& f0, Frags<NTM>& f1,
+                                        int (&as0)[MAX_TM], int (&as1)[MAX_TM], int64_t next_tbase,
+                                        RopeCS& rope0, int64_t t0) {
+  if (((j & 63) == 0) && j > 0) {   // next 64 weight-scale bytes (K > 8192 only)
+    __builtin_amdgcn_s_waitcnt(WAITCNT_VM0);
+    c.wsc_lane = j + c.lane < c.nkb ? c.wsc[j + c.lane] : 0u;
+    __builtin_amdgcn_s_waitcnt(WAITCNT_VM0);
+  }
+  const int ws = __builtin_amdgcn_readlane((int)c.wsc_lane, j & 63);
+  if constexpr (MODE == MODE_LAST) {
+    if constexpr (NTM > 0) rope0 = load_rope(t0, c.half, c.p);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  half_step<NTM, ST, 1, false, 0, 0>(c, acc, f0, as0, ws, f1, as1, j, 0);
+  __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);
+  __builtin_amdgcn_s_waitcnt(WAITCNT_VM0);
+  block_barrier();   // all of block j read by every wave; block j+1 has landed
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (MODE == MODE_STEADY)
+    half_step<NTM, ST ^ 1, 0, true, 1, ST>(c, acc, f1, as0, ws, f0, as1, j + 1, j + 2);
+  if constexpr (MODE == MODE_NOCOPY)
+    half_step<NTM, ST ^ 1, 0, true, 0, 0>(c, acc, f1, as0, ws, f0, as1, j + 1, 0);
+  if constexpr (MODE == MODE_LAST) {
+    c.set_tile(next_tbase);
+    half_step<NTM, 0, -1, false, 2, 0>(c, acc, f1, as0, ws, f0, as1, 0, 0);
+  }
+#pragma unroll
+  for (int tm = 0; tm < MAX_TM; ++tm) as0[tm] = as1[tm];
+}
+
+// Shapes of the K loop: 1 block, 2 blocks, an even count >= 4, an odd count >= 3.
+enum { SHAPE_ONE, SHAPE_TWO, SHAPE_EVEN, SHAPE_ODD };
+
+// The K loop of one tile for a wave owning NTM sub-tiles, then its epilogue.
+// On entry the copies of blocks 0 and 1 of this tile are in flight. Block j
+// sits in stage j % 2 and the schedule for the block count's SHAPE is
+// straight-line code around one loop: the accumulators never pass a branch.
+// The last block always starts the copies of the next tile (past the
+// workgroup's last tile they read zeros into stages nobody reads again).
+template <int STAGE, int NTM, int SHAPE>
+__device__ __forceinline__ void run_tile(Ctx& c, int64_t tbase, int64_t next_tbase) {
+  v16f acc[MAX_TM][4];
+#pragma unroll
+  for (int tm = 0; tm < MAX_TM; ++tm)
 #pragma unroll
     for (int tn = 0; tn < 4; ++tn)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[tm][tn][r] = 0.f;
 
-  issue_stage(0, 0);
-
-  for (int j = 0; j < nkb; ++j) {
-    const int st = j & 1;
-    if ((j & 63) == 0 && j > 0) {   // next 64 weight-scale bytes (only for K > 8192)
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-      wsc_lane = j + lane < nkb ? wsc[j + lane] : 0u;
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  Frags<NTM> f0, f1;
+  int as0[MAX_TM] = {0, 0, 0, 0}, as1[MAX_TM] = {0, 0, 0, 0};
+  RopeCS rope;
+  const int64_t t_lane = tbase + 32 * c.th + (c.lane & 31);   // token of sub-tile tm: t_lane + 64 tm
+  __builtin_amdgcn_s_waitcnt(WAITCNT_VM0);
+  block_barrier();
+#pragma unroll
+  for (int tm = 0; tm < NTM; ++tm) as0[tm] = c.read_scale<0>(tm, 0);
+#pragma unroll
+  for (int tm = 0; tm < NTM; ++tm)
+    f0.a[tm] = make_v8i(c.read16<0>(true, 0, 0, 64 * tm), c.read16<0>(true, 0, 1, 64 * tm));
+#pragma unroll
+  for (int tn = 0; tn < 4; ++tn)
+    f0.w[tn] = make_v8i(c.read16<0>(false, 0, 0, 32 * tn), c.read16<0>(false, 0, 1, 32 * tn));
+  // Block 0 is peeled (its MFMAs start from zero accumulators); blocks
+  // 1, 2, ... run in (stage 1, stage 0) pairs while both are STEADY; the
+  // remaining two or three blocks follow from the parity of the block count.
+  const int nkb = c.nkb;
+  if constexpr (SHAPE == SHAPE_ONE) {
+    k_block<NTM, MODE_LAST, 0>(c, 0, acc, f0, f1, as0, as1, next_tbase, rope, t_lane);
+  } else if constexpr (SHAPE == SHAPE_TWO) {
+    k_block<NTM, MODE_NOCOPY, 0>(c, 0, acc, f0, f1, as0, as1, 0, rope, 0);
+    k_block<NTM, MODE_LAST, 1>(c, 1, acc, f0, f1, as0, as1, next_tbase, rope, t_lane);
+  } else {
+    k_block<NTM, MODE_STEADY, 0>(c, 0, acc, f0, f1, as0, as1, 0, rope, 0);
+    int j = 1;
+    for (; j + 3 < nkb; j += 2) {
+      k_block<NTM, MODE_STEADY, 1>(c, j, acc, f0, f1, as0, as1, 0, rope, 0);
+      k_block<NTM, MODE_STEADY, 0>(c, j + 1, acc, f0, f1, as0, as1, 0, rope, 0);
     }
-    if (j + 1 < nkb) {
-      issue_stage(j + 1, st ^ 1);
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(VM_PER_STAGE));   // stage j's copies have landed
-    } else {
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    if constexpr (SHAPE == SHAPE_EVEN) {   // three left: j (stage 1), j+1, j+2
+      k_block<NTM, MODE_STEADY, 1>(c, j, acc, f0, f1, as0, as1, 0, rope, 0);
+      k_block<NTM, MODE_NOCOPY, 0>(c, j + 1, acc, f0, f1, as0, as1, 0, rope, 0);
+      k_block<NTM, MODE_LAST, 1>(c, j + 2, acc, f0, f1, as0, as1, next_tbase, rope, t_lane);
+    } else {                               // two left: j (stage 1), j+1
+      k_block<NTM, MODE_NOCOPY, 1>(c, j, acc, f0, f1, as0, as1, 0, rope, 0);
+      k_block<NTM, MODE_LAST, 0>(c, j + 1, acc, f0, f1, as0, as1, next_tbase, rope, t_lane);
     }
-    block_barrier();                                          // ... for every wave
-
-    const int wscale = __builtin_amdgcn_readlane((int)wsc_lane, j & 63);
-    const int sshift = 8 * (j & 3);
-    int asc[2];
-#pragma unroll
-    for (int tm = 0; tm < 2; ++tm)
-      asc[tm] = (int)(*reinterpret_cast<const uint32_t*>(&lds[st][SCALE_OFF + 256 * wave + 4 * (32 * tm + (lane & 31))]) >> sshift);
-    const uint8_t* wt = &lds[st][0];
-    const uint8_t* at = &lds[st][TILE_BYTES];
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      const int c0 = 4 * kh + 2 * half;
-      v8i af[2];
-#pragma unroll
-      for (int tm = 0; tm < 2; ++tm) {
-        const int row = 64 * q + 32 * tm + (lane & 31);
-        const v4u lo = *reinterpret_cast<const v4u*>(at + row * KB + 16 * (c0 ^ (row & 7)));
-        const v4u hi = *reinterpret_cast<const v4u*>(at + row * KB + 16 * ((c0 + 1) ^ (row & 7)));
-        af[tm] = make_v8i(lo, hi);
-      }
-#pragma unroll
-      for (int tn = 0; tn < 4; ++tn) {
-        const int row = HEAD_DIM * hn + 32 * tn + (lane & 31);
-        const v4u lo = *reinterpret_cast<const v4u*>(wt + row * KB + 16 * (c0 ^ (row & 7)));
-        const v4u hi = *reinterpret_cast<const v4u*>(wt + row * KB + 16 * ((c0 + 1) ^ (row & 7)));
-        const v8i wf = make_v8i(lo, hi);
-#pragma unroll
-        for (int tm = 0; tm < 2; ++tm)
-          acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              wf, af[tm], acc[tm][tn], 0, 0, 0, wscale, 0, asc[tm]);
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);               // this wave's LDS reads are done
-    block_barrier();                                          // stage st may be overwritten
   }
 
+  // every MFMA of the tile completes here: none is sunk into the epilogue,
+  // whose branches would then hold the operand registers live
 #pragma unroll
-  for (int tm = 0; tm < 2; ++tm)
-    epilogue_tile<STAGE>(acc[tm], mbase + 64 * q + 32 * tm + (lane & 31), head, head < p.H, half, p);
+  for (int tm = 0; tm < NTM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn) asm volatile("" : "+a"(acc[tm][tn]));
+  // one sub-tile's epilogue at a time keeps register use flat; the next
+  // sub-tile's RoPE rows are fetched while this one computes
+#pragma unroll
+  for (int tm = 0; tm < NTM; ++tm) {
+    __builtin_amdgcn_sched_barrier(0);
+    RopeCS next;
+    if (tm + 1 < NTM) next = load_rope(t_lane + 64 * (tm + 1), c.half, c.p);
+    epilogue_tile<STAGE>(acc[tm], t_lane + 64 * tm, c.head, c.head < c.p.H, c.half, c.p, rope);
+    if (tm + 1 < NTM) rope = next;
+  }
 }
 
-hipError_t launch_kernel(const IndexerQArgs& a, int stage, hipStream_t stream) {
-  const int64_t n_mt = (a.M + TILE_ROWS - 1) / TILE_ROWS;
-  const int64_t blocks = n_mt * ((a.H + 1) / 2);
+template <int STAGE, int SHAPE>
+__device__ __forceinline__ void run_tiles(Ctx& c, int64_t s_begin, int64_t s_end) {
+  for (int64_t s0 = s_begin; s0 < s_end; s0 += MAX_SUB) {
+    const int nsub = (int)(s_end - s0 < MAX_SUB ? s_end - s0 : MAX_SUB);
+    const int ntm = (nsub + 1 - c.th) >> 1;
+    const int64_t tbase = SUB * s0;
+    // past the chunk's last tile, an empty token range: its copies read zeros
+    const int64_t next_tbase = s0 + MAX_SUB < s_end ? SUB * (s0 + MAX_SUB) : c.p.M;
+    switch (ntm) {
+      case 4: run_tile<STAGE, 4, SHAPE>(c, tbase, next_tbase); break;
+      case 3: run_tile<STAGE, 3, SHAPE>(c, tbase, next_tbase); break;
+      case 2: run_tile<STAGE, 2, SHAPE>(c, tbase, next_tbase); break;
+      case 1: run_tile<STAGE, 1, SHAPE>(c, tbase, next_tbase); break;
+      default: run_tile<STAGE, 0, SHAPE>(c, tbase, next_tbase); break;
+    }
+  }
+}
+
+template <int STAGE>
+__global__ __launch_bounds__(NTHREADS, 1)
+void indexer_q_kernel(IndexerQArgs p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
+
+  // ---- workgroup -> (head pair, token chunk). Consecutive workgroup ids go
+  // to consecutive XCDs; when the pair count is a multiple of 8 each XCD
+  // works on pairs/8 head pairs, whose weights then stay in its L2.
+  const int bid = blockIdx.x;
+  const int npairs = (p.H + 1) >> 1;
+  const int cpp = p.chunks;
+  int pair, chunk;
+  if ((npairs & 7) == 0) {
+    const int ppx = npairs >> 3;
+    const int s = bid >> 3;
+    pair = (bid & 7) * ppx + s % ppx;
+    chunk = s / ppx;
+  } else {
+    pair = bid % npairs;
+    chunk = bid / npairs;
+  }
+  // the chunk's sub-tiles [s_begin, s_end) of the ceil(M / 32) token sub-tiles
+  const int64_t nsub_all = (p.M + SUB - 1) / SUB;
+  const int64_t s_begin = nsub_all * chunk / cpp;
+  const int64_t s_end = nsub_all * (chunk + 1) / cpp;
+  if (s_begin >= s_end) return;   // uniform over the workgroup
+
+  Ctx c(p, lds, pair);
+  c.set_tile(SUB * s_begin);
+  for (int w = 0; w < 2 * COPIES + 1; ++w) c.copy<0>(w, 0);
+  for (int w = 0; w < 2 * COPIES + 1; ++w) c.copy<1>(w, 1);   // with a single K block stage 1 is never read
+  if (c.nkb == 1)
+    run_tiles<STAGE, SHAPE_ONE>(c, s_begin, s_end);
+  else if (c.nkb == 2)
+    run_tiles<STAGE, SHAPE_TWO>(c, s_begin, s_end);
+  else if (c.nkb & 1)
+    run_tiles<STAGE, SHAPE_ODD>(c, s_begin, s_end);
+  else
+    run_tiles<STAGE, SHAPE_EVEN>(c, s_begin, s_end);
+  __builtin_amdgcn_s_waitcnt(WAITCNT_VM0);   // no LDS copy may outlive the workgroup
+}
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int n = g_cu_count[dev].load(std::memory_order_acquire);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    g_cu_count[dev].store(n, std::memory_order_release);
+  }
+  return n;
+}
+
+hipError_t launch_kernel(const IndexerQArgs& a_in, int stage, hipStream_t stream) {
+  IndexerQArgs a = a_in;
+  const int64_t npairs = (a.H + 1) / 2;
+  const int64_t nsub_all = (a.M + SUB - 1) / SUB;
+  // one workgroup per CU: each head pair gets CUs / pairs token chunks
+  int64_t cpp = cu_count() / npairs;
+  cpp = cpp < 1 ? 1 : cpp;
+  cpp = cpp < nsub_all ? cpp : nsub_all;
+  const int64_t blocks = npairs * cpp;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  a.chunks = (int32_t)cpp;
   const dim3 grid((unsigned)blocks), block(NTHREADS);
   switch (stage) {
     case -1: hipLaunchKernelGGL(indexer_q_kernel<-1>, grid, block, 0, stream, a); break;

@@ -24,6 +24,7 @@ struct IndexerQArgs {
   uint8_t* q_fp4;                // [M, H, 64]
   uint8_t* q_scales;             // [M, H, 4]
   float* dbg;                    // [M, H*128] for the diagnostic stages
+  int32_t chunks;                // token chunks per head pair (set by the launcher)
 };
 
 hipError_t launch_fp8_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
