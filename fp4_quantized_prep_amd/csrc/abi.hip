@@ -63,6 +63,8 @@ int check_indexer_q_args(const void* a, int64_t lda, const int32_t* a_scales, in
       !aligned(positions, 8) || !aligned(cos_sin, 16))
     return IQP_ERR_UNSUPPORTED;
   if ((int64_t)H * 128 > ((int64_t)1 << 31)) return IQP_ERR_UNSUPPORTED;
+  // the kernel keeps a head's weight-scale bytes in one register (4 per lane)
+  if (K / 128 > 256) return IQP_ERR_UNSUPPORTED;
   // the kernel addresses one 256-row tile (and its scale words) with 32-bit offsets
   if (lda >= ((int64_t)1 << 23) || ldw >= ((int64_t)1 << 23)) return IQP_ERR_UNSUPPORTED;
   if (as_sm >= ((int64_t)1 << 20) || nw * as_sw >= ((int64_t)1 << 28)) return IQP_ERR_UNSUPPORTED;

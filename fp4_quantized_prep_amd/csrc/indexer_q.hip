@@ -268,8 +268,10 @@ __device__ __forceinline__ void epilogue_tile(const v16f (&acc)[4], int64_t t, i
 // LDS directly (no staging registers): one dwordx4 copy moves 8 full 128-byte
 // rows, lane i writing bytes 16 i. Buffer bounds return zeros for rows past
 // the last token or head. Row r's 16-byte chunks are stored XOR-swizzled
-// (chunk c at slot c ^ (r % 8)), so the MFMA operand reads (8 consecutive
-// rows, one chunk column) hit distinct banks. Two stages double-buffer the K
+// (chunk c at slot c ^ ((r / 2) % 8)): a 128-byte row covers half of the 64
+// LDS banks, rows 2i and 2i+1 the two halves, so the 16 lanes of one read
+// cycle (16 consecutive rows, one chunk column) hit 64 distinct banks. Two
+// stages double-buffer the K
 // loop with one barrier per block, placed between the block's two 64-deep
 // halves:
 //
@@ -327,8 +329,7 @@ struct Ctx {
   int lane, half, wave, hn, th;
   int nkb;
   int head;
-  uint32_t wsc_lane;
-  const uint8_t* wsc;
+  uint32_t wsc_lane;   // weight-scale bytes 4 lane .. 4 lane + 3 of the head (K blocks)
   rsrc_t rw, ra, rs;                 // weights of the pair; activations and scale words of the tile
   uint32_t vw, va, vs;               // this lane's byte offsets into them
   uint32_t rd_w[2][2], rd_a[2][2];   // LDS operand-read bases [kh][lo/hi]
@@ -344,11 +345,15 @@ struct Ctx {
     nkb = p.nkb;
     head = 2 * pair + hn;
     const int head_c = head < p.H ? head : p.H - 1;   // odd H: the missing head reads zeros, never stored
-    wsc = p.w_scales + (int64_t)head_c * nkb;
-    wsc_lane = lane < nkb ? wsc[lane] : 0u;
+    const uint8_t* wsc = p.w_scales + (int64_t)head_c * nkb;
+    wsc_lane = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      if (4 * lane + b < nkb) wsc_lane |= (uint32_t)wsc[4 * lane + b] << (8 * b);
     // copy i of this wave lands in rows 8 (wave + 4 i) + lane / 8, slot lane % 8,
-    // which holds the row's chunk (lane % 8) ^ (row % 8)
-    const int chunk = (lane & 7) ^ ((lane >> 3) & 7);
+    // which holds the row's chunk (lane % 8) ^ ((row / 2) % 8); as the slab
+    // index wave + 4 i has the parity of wave, that is the same for every copy
+    const int chunk = (lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7);
     const int64_t row0 = (int64_t)2 * pair * HEAD_DIM;
     const int64_t wrows = (int64_t)p.H * HEAD_DIM - row0;
     rw = make_rsrc(p.w + row0 * p.ldw, (uint64_t)(wrows < TILE_ROWS ? wrows : TILE_ROWS) * p.ldw);
@@ -356,12 +361,13 @@ struct Ctx {
     va = (uint32_t)((8 * wave + (lane >> 3)) * p.lda + 16 * chunk);
     vs = (uint32_t)(4 * (64 * wave + lane) * p.as_sm);
     // operand reads: A row 64 tm + 32 th + lane % 32, W row 128 hn + 32 tn + lane % 32;
-    // all row bases are multiples of 8, so the swizzle term row % 8 is lane % 8
+    // all row bases are multiples of 32, so the swizzle term (row / 2) % 8 is
+    // (lane / 2) % 8
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const uint32_t col = 16 * ((4 * kh + 2 * half + e) ^ (lane & 7));
+        const uint32_t col = 16 * ((4 * kh + 2 * half + e) ^ ((lane >> 1) & 7));
         rd_w[kh][e] = W_OFF + KB * (HEAD_DIM * hn + (lane & 31)) + col;
         rd_a[kh][e] = A_OFF + KB * (32 * th + (lane & 31)) + col;
       }
@@ -411,10 +417,10 @@ struct Ctx {
     return *reinterpret_cast<const v4u*>(lds + base + ST * TILE_BYTES + KB * rowoff);
   }
 
-  // scale byte of block j for sub-tile tm (the packed word shifted to byte 0)
+  // packed scale word (K blocks 4 (j / 4) .. + 3) of sub-tile tm's token
   template <int ST>
-  __device__ __forceinline__ int read_scale(int tm, int j) const {
-    return (int)(*reinterpret_cast<const uint32_t*>(lds + rd_s + ST * TILE_ROWS * 4 + 4 * 64 * tm) >> (8 * (j & 3)));
+  __device__ __forceinline__ int read_scale(int tm) const {
+    return (int)*reinterpret_cast<const uint32_t*>(lds + rd_s + ST * TILE_ROWS * 4 + 4 * 64 * tm);
   }
 };
 
@@ -425,7 +431,7 @@ struct Ctx {
 // below is the issue order: no copy or read waits behind a run of MFMAs, and
 // every MFMA's operands were read one half-step earlier.
 //   RKH >= 0: read the 64-deep half RKH of the block in stage RST into N;
-//   RSC: also the scale bytes of block jr (stage RST) into asn;
+//   RSC: also the packed scale words of the block in stage RST into asn;
 //   NBLK copy blocks: block jd + b into stage (DST + b) & 1.
 template <int NTM, int RST, int RKH, bool RSC, int NBLK, int DST>
 __device__ __forceinline__ void half_step(Ctx& c, v16f (&acc)[MAX_TM][4], const Frags<NTM>& F,
@@ -441,6 +447,7 @@ __device__ __forceinline__ void half_step(Ctx& c, v16f (&acc)[MAX_TM][4], const 
       const int tn = slot / (NTM > 0 ? NTM : 1), tm = slot % (NTM > 0 ? NTM : 1);
       acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.w[tn], F.a[tm], acc[tm][tn], 0, 0, 0, ws, 0,
                                                                     as[tm]);
+      asm volatile("" : "+a"(acc[tm][tn]));   // the MFMA stays in its slot (no sinking past this)
     }
 #pragma unroll
     for (int k = NCOPY * slot / NS; k < NCOPY * (slot + 1) / NS; ++k) {
@@ -460,7 +467,7 @@ __device__ __forceinline__ void half_step(Ctx& c, v16f (&acc)[MAX_TM][4], const 
         const int tn = r - NTM;
         N.w[tn] = make_v8i(c.read16<RST>(false, RKH, 0, 32 * tn), c.read16<RST>(false, RKH, 1, 32 * tn));
       } else {
-        asn[r - NTM - 4] = c.read_scale<RST>(r - NTM - 4, jr);
+        asn[r - NTM - 4] = c.read_scale<RST>(r - NTM - 4);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -481,28 +488,29 @@ template <int NTM, int MODE, int ST>
 __device__ __forceinline__ void k_block(Ctx& c, int j, v16f (&acc)[MAX_TM][4], Frags<NTM>& f0, Frags<NTM>& f1,
                                         int (&as0)[MAX_TM], int (&as1)[MAX_TM], int64_t next_tbase,
                                         RopeCS& rope0, int64_t t0) {
-  if (((j & 63) == 0) && j > 0) {   // next 64 weight-scale bytes (K > 8192 only)
-    __builtin_amdgcn_s_waitcnt(WAITCNT_VM0);
-    c.wsc_lane = j + c.lane < c.nkb ? c.wsc[j + c.lane] : 0u;
-    __builtin_amdgcn_s_waitcnt(WAITCNT_VM0);
-  }
-  const int ws = __builtin_amdgcn_readlane((int)c.wsc_lane, j & 63);
+  // a branch here would let the compiler sink the MFMAs out of their slots:
+  // the block's weight-scale byte comes from a register, its activation
+  // scale bytes from the words read one half-step earlier
+  const int ws = (int)((uint32_t)__builtin_amdgcn_readlane((int)c.wsc_lane, j >> 2) >> (8 * (j & 3)));
+  int as[MAX_TM];
+#pragma unroll
+  for (int tm = 0; tm < MAX_TM; ++tm) as[tm] = (int)((uint32_t)as0[tm] >> (8 * (j & 3)));
   if constexpr (MODE == MODE_LAST) {
     if constexpr (NTM > 0) rope0 = load_rope(t0, c.half, c.p);
   }
   __builtin_amdgcn_sched_barrier(0);
-  half_step<NTM, ST, 1, false, 0, 0>(c, acc, f0, as0, ws, f1, as1, j, 0);
+  half_step<NTM, ST, 1, false, 0, 0>(c, acc, f0, as, ws, f1, as1, j, 0);
   __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);
   __builtin_amdgcn_s_waitcnt(WAITCNT_VM0);
   block_barrier();   // all of block j read by every wave; block j+1 has landed
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (MODE == MODE_STEADY)
-    half_step<NTM, ST ^ 1, 0, true, 1, ST>(c, acc, f1, as0, ws, f0, as1, j + 1, j + 2);
+    half_step<NTM, ST ^ 1, 0, true, 1, ST>(c, acc, f1, as, ws, f0, as1, j + 1, j + 2);
   if constexpr (MODE == MODE_NOCOPY)
-    half_step<NTM, ST ^ 1, 0, true, 0, 0>(c, acc, f1, as0, ws, f0, as1, j + 1, 0);
+    half_step<NTM, ST ^ 1, 0, true, 0, 0>(c, acc, f1, as, ws, f0, as1, j + 1, 0);
   if constexpr (MODE == MODE_LAST) {
     c.set_tile(next_tbase);
-    half_step<NTM, 0, -1, false, 2, 0>(c, acc, f1, as0, ws, f0, as1, 0, 0);
+    half_step<NTM, 0, -1, false, 2, 0>(c, acc, f1, as, ws, f0, as1, 0, 0);
   }
 #pragma unroll
   for (int tm = 0; tm < MAX_TM; ++tm) as0[tm] = as1[tm];
@@ -534,7 +542,7 @@ __device__ __forceinline__ void run_tile(Ctx& c, int64_t tbase, int64_t next_tba
   __builtin_amdgcn_s_waitcnt(WAITCNT_VM0);
   block_barrier();
 #pragma unroll
-  for (int tm = 0; tm < NTM; ++tm) as0[tm] = c.read_scale<0>(tm, 0);
+  for (int tm = 0; tm < NTM; ++tm) as0[tm] = c.read_scale<0>(tm);
 #pragma unroll
   for (int tm = 0; tm < NTM; ++tm)
     f0.a[tm] = make_v8i(c.read16<0>(true, 0, 0, 64 * tm), c.read16<0>(true, 0, 1, 64 * tm));

@@ -119,8 +119,11 @@ int fp8_quant_1x128_ue8m0(const void* x, int64_t M, int64_t K, int64_t ldx,
  *   w          E4M3 weights [H*D, K], K contiguous, row stride ldw (bytes);
  *              16-byte aligned, ldw a multiple of 16.
  *   w_scales   UE8M0 bytes [H*D/128, K/128], row-major (one per 128x128 tile).
- *   M          tokens (>= 0); K: multiple of 128; H >= 1; D must be 128 and
- *              rope_dim 64 (else IQP_ERR_UNSUPPORTED).
+ *   M          tokens (>= 0); K: multiple of 128, at most 32768; H >= 1; D must
+ *              be 128 and rope_dim 64 (else IQP_ERR_UNSUPPORTED). Row strides
+ *              below 2^23 bytes and scale-word strides with
+ *              as_stride_m < 2^20, (K/512) * as_stride_w < 2^28 (else
+ *              IQP_ERR_UNSUPPORTED).
  *   positions  int64 [M]. A position outside [0, max_pos) is a precondition
  *              violation: it is clamped into range (the row's output is then
  *              meaningless, but no memory outside the table is read).

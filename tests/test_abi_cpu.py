@@ -86,6 +86,7 @@ def test_fused_argument_checks(iqp):
     assert fused(iqp, ldw=264) == iqp.IQP_ERR_UNSUPPORTED
     assert fused(iqp, q=20) == iqp.IQP_ERR_UNSUPPORTED
     assert fused(iqp, sm=3, sw=3) == iqp.IQP_ERR_INVALID
+    assert fused(iqp, K=257 * 128, lda=257 * 128, ldw=257 * 128, sm=65) == iqp.IQP_ERR_UNSUPPORTED  # > 256 K blocks
     assert fused(iqp, M=0) == iqp.IQP_OK
 
 
