@@ -88,9 +88,11 @@ struct RopeCS {
   v4f c[4], s[4];
 };
 
-__device__ __forceinline__ RopeCS load_rope(int64_t t, int half, const IndexerQArgs& p) {
-  const int64_t tc = t < p.M ? t : p.M - 1;
-  int64_t pos = p.positions[tc];
+__device__ __forceinline__ int64_t load_position(int64_t t, const IndexerQArgs& p) {
+  return p.positions[t < p.M ? t : p.M - 1];
+}
+
+__device__ __forceinline__ RopeCS load_rope(int64_t pos, int half, const IndexerQArgs& p) {
   pos = pos < 0 ? 0 : (pos >= p.max_pos ? p.max_pos - 1 : pos);
   const float* cs = p.cos_sin + pos * 64;
   RopeCS r;
@@ -282,12 +284,17 @@ __device__ __forceinline__ void epilogue_tile(const v16f (&acc)[4], int64_t t, i
 // copies are spread among the MFMAs instead of stalling them. The last block
 // of a tile starts the copies of the next tile's first two blocks, which land
 // while the epilogue runs.
-constexpr int NWAVES = 4;
+#ifndef IQP_NWAVES
+#define IQP_NWAVES 4
+#endif
+constexpr int NWAVES = IQP_NWAVES;
+constexpr int TGROUPS = NWAVES / 2;                  // waves per head (token groups)
 constexpr int NTHREADS = NWAVES * 64;
 constexpr int TILE_ROWS = 256;                       // weight rows (2 heads) and most tokens per tile
 constexpr int SUB = 32;                              // tokens per MFMA column tile
 constexpr int MAX_SUB = TILE_ROWS / SUB;             // sub-tiles per tile
-constexpr int MAX_TM = MAX_SUB / 2;                  // sub-tiles per wave
+constexpr int MAX_TM = MAX_SUB / TGROUPS;            // sub-tiles per wave
+constexpr int TM_STRIDE = SUB * TGROUPS;             // tokens between a wave's sub-tiles
 constexpr int TILE_BYTES = TILE_ROWS * KB;           // one operand tile of one K block: 32 KiB
 constexpr int SLAB = 1024;                           // bytes written by one wave-wide LDS copy
 constexpr int COPIES = TILE_BYTES / SLAB / NWAVES;   // per operand per wave per block: 8
@@ -341,7 +348,7 @@ struct Ctx {
     half = lane >> 5;
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     hn = wave & 1;
-    th = wave >> 1;
+    th = wave >> 1;   // token group: sub-tiles s with s % TGROUPS == th
     nkb = p.nkb;
     head = 2 * pair + hn;
     const int head_c = head < p.H ? head : p.H - 1;   // odd H: the missing head reads zeros, never stored
@@ -359,7 +366,7 @@ struct Ctx {
     rw = make_rsrc(p.w + row0 * p.ldw, (uint64_t)(wrows < TILE_ROWS ? wrows : TILE_ROWS) * p.ldw);
     vw = (uint32_t)((8 * wave + (lane >> 3)) * p.ldw + 16 * chunk);
     va = (uint32_t)((8 * wave + (lane >> 3)) * p.lda + 16 * chunk);
-    vs = (uint32_t)(4 * (64 * wave + lane) * p.as_sm);
+    vs = (uint32_t)(4 * (64 * (wave & 3) + lane) * p.as_sm);   // with 8 waves, pairs copy the same words
     // operand reads: A row 64 tm + 32 th + lane % 32, W row 128 hn + 32 tn + lane % 32;
     // all row bases are multiples of 32, so the swizzle term (row / 2) % 8 is
     // (lane / 2) % 8
@@ -403,7 +410,7 @@ struct Ctx {
                                                16, va + u, 0, 0, 0);
     } else {
       const uint32_t u = __builtin_amdgcn_readfirstlane((int)(4 * (j >> 2) * p.as_sw));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + S_OFF + ST * TILE_ROWS * 4 + 256 * wave), 4,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + S_OFF + ST * TILE_ROWS * 4 + 256 * (wave & 3)), 4,
                                                vs + u, 0, 0, 0);
     }
   }
@@ -420,7 +427,7 @@ struct Ctx {
   // packed scale word (K blocks 4 (j / 4) .. + 3) of sub-tile tm's token
   template <int ST>
   __device__ __forceinline__ int read_scale(int tm) const {
-    return (int)*reinterpret_cast<const uint32_t*>(lds + rd_s + ST * TILE_ROWS * 4 + 4 * 64 * tm);
+    return (int)*reinterpret_cast<const uint32_t*>(lds + rd_s + ST * TILE_ROWS * 4 + 4 * TM_STRIDE * tm);
   }
 };
 
@@ -440,7 +447,12 @@ __device__ __forceinline__ void half_step(Ctx& c, v16f (&acc)[MAX_TM][4], const 
   constexpr int NM = 4 * NTM;
   constexpr int NS = NM > 0 ? NM : 1;
   constexpr int NCOPY = NBLK * (2 * COPIES + 1);
-  constexpr int NREAD = RKH >= 0 ? NTM + 4 + (RSC ? NTM : 0) : 0;   // whole fragments, then scale bytes
+  constexpr int NREAD = RKH >= 0 ? (RSC ? NTM : 0) + NTM + 4 : 0;   // scale words, then whole fragments
+  // front-loaded: copies in the first half of the slots, reads in the first
+  // three quarters, so both have landed by the waits that follow
+  constexpr int NSC = NS / 2 > 0 ? NS / 2 : 1;
+  constexpr int NSR = 3 * NS / 4 > 0 ? 3 * NS / 4 : 1;
+  constexpr int NSCALE = RSC ? NTM : 0;
 #pragma unroll
   for (int slot = 0; slot < NS; ++slot) {
     if (slot < NM) {
@@ -450,7 +462,7 @@ __device__ __forceinline__ void half_step(Ctx& c, v16f (&acc)[MAX_TM][4], const 
       asm volatile("" : "+a"(acc[tm][tn]));   // the MFMA stays in its slot (no sinking past this)
     }
 #pragma unroll
-    for (int k = NCOPY * slot / NS; k < NCOPY * (slot + 1) / NS; ++k) {
+    for (int k = NCOPY * slot / NSC; k < (slot < NSC ? NCOPY * (slot + 1) / NSC : 0); ++k) {
       const int b = k / (2 * COPIES + 1), w = k % (2 * COPIES + 1);
       if ((DST + b) & 1)
         c.copy<1>(w, jd + b);
@@ -458,36 +470,40 @@ __device__ __forceinline__ void half_step(Ctx& c, v16f (&acc)[MAX_TM][4], const 
         c.copy<0>(w, jd + b);
     }
 #pragma unroll
-    for (int r = NREAD * slot / NS; r < NREAD * (slot + 1) / NS; ++r) {
+    for (int r = NREAD * slot / NSR; r < (slot < NSR ? NREAD * (slot + 1) / NSR : 0); ++r) {
       // a fragment is replaced whole: a partial update would keep the
       // previous one (the operands of the half-step before) alive
-      if (r < NTM) {
-        N.a[r] = make_v8i(c.read16<RST>(true, RKH, 0, 64 * r), c.read16<RST>(true, RKH, 1, 64 * r));
-      } else if (r < NTM + 4) {
-        const int tn = r - NTM;
-        N.w[tn] = make_v8i(c.read16<RST>(false, RKH, 0, 32 * tn), c.read16<RST>(false, RKH, 1, 32 * tn));
+      if (r < NSCALE) {
+        asn[r] = c.read_scale<RST>(r);
+      } else if (r < NSCALE + NTM) {
+        const int tm = r - NSCALE;
+        N.a[tm] = make_v8i(c.read16<RST>(true, RKH, 0, TM_STRIDE * tm), c.read16<RST>(true, RKH, 1, TM_STRIDE * tm));
       } else {
-        asn[r - NTM - 4] = c.read_scale<RST>(r - NTM - 4);
+        const int tn = r - NSCALE - NTM;
+        N.w[tn] = make_v8i(c.read16<RST>(false, RKH, 0, 32 * tn), c.read16<RST>(false, RKH, 1, 32 * tn));
       }
     }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-enum { MODE_STEADY, MODE_NOCOPY, MODE_LAST };
+enum { MODE_STEADY, MODE_PENULT, MODE_LAST, MODE_ONLY };
 
 // One K block j in stage ST: the first half's MFMAs (reading the second
 // half), the block barrier, then the second half's MFMAs with the copies and
-// reads the mode asks for:
+// reads the mode asks for. Block b of the next tile goes to stage b, copied
+// as soon as that stage is free:
 //   STEADY: copy block j+2 into stage ST, read block j+1's first half;
-//   NOCOPY: read block j+1's first half;
-//   LAST:   copy blocks 0 and 1 of the next tile (whose buffers are set here)
-//           into stages 0 and 1; the RoPE table rows of the epilogue's first
-//           sub-tile are fetched before the barrier.
+//   PENULT (last but one): switch the copy buffers to the next tile, copy its
+//           block ST into stage ST, read block j+1's first half;
+//   LAST:   copy the next tile's block ST into stage ST;
+//   ONLY (a single K block): switch buffers, copy next blocks 0 and 1.
+// LAST and ONLY fetch the RoPE rows of the epilogue's first sub-tile before
+// the barrier.
 template <int NTM, int MODE, int ST>
 __device__ __forceinline__ void k_block(Ctx& c, int j, v16f (&acc)[MAX_TM][4], Frags<NTM>& f0, Frags<NTM>& f1,
                                         int (&as0)[MAX_TM], int (&as1)[MAX_TM], int64_t next_tbase,
-                                        RopeCS& rope0, int64_t t0) {
+                                        RopeCS& rope0, int64_t pos0) {
   // a branch here would let the compiler sink the MFMAs out of their slots:
   // the block's weight-scale byte comes from a register, its activation
   // scale bytes from the words read one half-step earlier
@@ -495,20 +511,26 @@ __device__ __forceinline__ void k_block(Ctx& c, int j, v16f (&acc)[MAX_TM][4], F
   int as[MAX_TM];
 #pragma unroll
   for (int tm = 0; tm < MAX_TM; ++tm) as[tm] = (int)((uint32_t)as0[tm] >> (8 * (j & 3)));
-  if constexpr (MODE == MODE_LAST) {
-    if constexpr (NTM > 0) rope0 = load_rope(t0, c.half, c.p);
+  if constexpr (MODE == MODE_LAST || MODE == MODE_ONLY) {
+    if constexpr (NTM > 0) rope0 = load_rope(pos0, c.half, c.p);
   }
   __builtin_amdgcn_sched_barrier(0);
   half_step<NTM, ST, 1, false, 0, 0>(c, acc, f0, as, ws, f1, as1, j, 0);
   __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);
-  __builtin_amdgcn_s_waitcnt(WAITCNT_VM0);
-  block_barrier();   // all of block j read by every wave; block j+1 has landed
+  // block j+1 must have landed, except after the last block: there only the
+  // next tile's copies are in flight, and the next tile's start waits for them
+  if constexpr (MODE == MODE_STEADY || MODE == MODE_PENULT) __builtin_amdgcn_s_waitcnt(WAITCNT_VM0);
+  block_barrier();   // all of block j read by every wave (and block j+1 landed)
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (MODE == MODE_STEADY)
     half_step<NTM, ST ^ 1, 0, true, 1, ST>(c, acc, f1, as, ws, f0, as1, j + 1, j + 2);
-  if constexpr (MODE == MODE_NOCOPY)
-    half_step<NTM, ST ^ 1, 0, true, 0, 0>(c, acc, f1, as, ws, f0, as1, j + 1, 0);
-  if constexpr (MODE == MODE_LAST) {
+  if constexpr (MODE == MODE_PENULT) {
+    c.set_tile(next_tbase);
+    half_step<NTM, ST ^ 1, 0, true, 1, ST>(c, acc, f1, as, ws, f0, as1, j + 1, ST);
+  }
+  if constexpr (MODE == MODE_LAST)
+    half_step<NTM, 0, -1, false, 1, ST>(c, acc, f1, as, ws, f0, as1, 0, ST);
+  if constexpr (MODE == MODE_ONLY) {
     c.set_tile(next_tbase);
     half_step<NTM, 0, -1, false, 2, 0>(c, acc, f1, as, ws, f0, as1, 0, 0);
   }
@@ -536,16 +558,21 @@ __device__ __forceinline__ void run_tile(Ctx& c, int64_t tbase, int64_t next_tba
       for (int r = 0; r < 16; ++r) acc[tm][tn][r] = 0.f;
 
   Frags<NTM> f0, f1;
-  int as0[MAX_TM] = {0, 0, 0, 0}, as1[MAX_TM] = {0, 0, 0, 0};
+  int as0[MAX_TM] = {}, as1[MAX_TM] = {};
   RopeCS rope;
-  const int64_t t_lane = tbase + 32 * c.th + (c.lane & 31);   // token of sub-tile tm: t_lane + 64 tm
+  const int64_t t_lane = tbase + 32 * c.th + (c.lane & 31);   // token of sub-tile tm: t_lane + TM_STRIDE tm
+  // the epilogue's positions, fetched now so its RoPE-row prefetches never
+  // wait on a dependent load
+  int64_t pos[MAX_TM > 0 ? MAX_TM : 1];
+#pragma unroll
+  for (int tm = 0; tm < NTM; ++tm) pos[tm] = load_position(t_lane + TM_STRIDE * tm, c.p);
   __builtin_amdgcn_s_waitcnt(WAITCNT_VM0);
   block_barrier();
 #pragma unroll
   for (int tm = 0; tm < NTM; ++tm) as0[tm] = c.read_scale<0>(tm);
 #pragma unroll
   for (int tm = 0; tm < NTM; ++tm)
-    f0.a[tm] = make_v8i(c.read16<0>(true, 0, 0, 64 * tm), c.read16<0>(true, 0, 1, 64 * tm));
+    f0.a[tm] = make_v8i(c.read16<0>(true, 0, 0, TM_STRIDE * tm), c.read16<0>(true, 0, 1, TM_STRIDE * tm));
 #pragma unroll
   for (int tn = 0; tn < 4; ++tn)
     f0.w[tn] = make_v8i(c.read16<0>(false, 0, 0, 32 * tn), c.read16<0>(false, 0, 1, 32 * tn));
@@ -553,11 +580,12 @@ __device__ __forceinline__ void run_tile(Ctx& c, int64_t tbase, int64_t next_tba
   // 1, 2, ... run in (stage 1, stage 0) pairs while both are STEADY; the
   // remaining two or three blocks follow from the parity of the block count.
   const int nkb = c.nkb;
+  const int64_t p0 = NTM > 0 ? pos[0] : 0;
   if constexpr (SHAPE == SHAPE_ONE) {
-    k_block<NTM, MODE_LAST, 0>(c, 0, acc, f0, f1, as0, as1, next_tbase, rope, t_lane);
+    k_block<NTM, MODE_ONLY, 0>(c, 0, acc, f0, f1, as0, as1, next_tbase, rope, p0);
   } else if constexpr (SHAPE == SHAPE_TWO) {
-    k_block<NTM, MODE_NOCOPY, 0>(c, 0, acc, f0, f1, as0, as1, 0, rope, 0);
-    k_block<NTM, MODE_LAST, 1>(c, 1, acc, f0, f1, as0, as1, next_tbase, rope, t_lane);
+    k_block<NTM, MODE_PENULT, 0>(c, 0, acc, f0, f1, as0, as1, next_tbase, rope, 0);
+    k_block<NTM, MODE_LAST, 1>(c, 1, acc, f0, f1, as0, as1, next_tbase, rope, p0);
   } else {
     k_block<NTM, MODE_STEADY, 0>(c, 0, acc, f0, f1, as0, as1, 0, rope, 0);
     int j = 1;
@@ -567,11 +595,11 @@ __device__ __forceinline__ void run_tile(Ctx& c, int64_t tbase, int64_t next_tba
     }
     if constexpr (SHAPE == SHAPE_EVEN) {   // three left: j (stage 1), j+1, j+2
       k_block<NTM, MODE_STEADY, 1>(c, j, acc, f0, f1, as0, as1, 0, rope, 0);
-      k_block<NTM, MODE_NOCOPY, 0>(c, j + 1, acc, f0, f1, as0, as1, 0, rope, 0);
-      k_block<NTM, MODE_LAST, 1>(c, j + 2, acc, f0, f1, as0, as1, next_tbase, rope, t_lane);
+      k_block<NTM, MODE_PENULT, 0>(c, j + 1, acc, f0, f1, as0, as1, next_tbase, rope, 0);
+      k_block<NTM, MODE_LAST, 1>(c, j + 2, acc, f0, f1, as0, as1, next_tbase, rope, p0);
     } else {                               // two left: j (stage 1), j+1
-      k_block<NTM, MODE_NOCOPY, 1>(c, j, acc, f0, f1, as0, as1, 0, rope, 0);
-      k_block<NTM, MODE_LAST, 0>(c, j + 1, acc, f0, f1, as0, as1, next_tbase, rope, t_lane);
+      k_block<NTM, MODE_PENULT, 1>(c, j, acc, f0, f1, as0, as1, next_tbase, rope, 0);
+      k_block<NTM, MODE_LAST, 0>(c, j + 1, acc, f0, f1, as0, as1, next_tbase, rope, p0);
     }
   }
 
@@ -587,8 +615,8 @@ __device__ __forceinline__ void run_tile(Ctx& c, int64_t tbase, int64_t next_tba
   for (int tm = 0; tm < NTM; ++tm) {
     __builtin_amdgcn_sched_barrier(0);
     RopeCS next;
-    if (tm + 1 < NTM) next = load_rope(t_lane + 64 * (tm + 1), c.half, c.p);
-    epilogue_tile<STAGE>(acc[tm], t_lane + 64 * tm, c.head, c.head < c.p.H, c.half, c.p, rope);
+    if (tm + 1 < NTM) next = load_rope(pos[tm + 1], c.half, c.p);
+    epilogue_tile<STAGE>(acc[tm], t_lane + TM_STRIDE * tm, c.head, c.head < c.p.H, c.half, c.p, rope);
     if (tm + 1 < NTM) rope = next;
   }
 }
@@ -597,13 +625,13 @@ template <int STAGE, int SHAPE>
 __device__ __forceinline__ void run_tiles(Ctx& c, int64_t s_begin, int64_t s_end) {
   for (int64_t s0 = s_begin; s0 < s_end; s0 += MAX_SUB) {
     const int nsub = (int)(s_end - s0 < MAX_SUB ? s_end - s0 : MAX_SUB);
-    const int ntm = (nsub + 1 - c.th) >> 1;
+    const int ntm = (nsub + TGROUPS - 1 - c.th) / TGROUPS;
     const int64_t tbase = SUB * s0;
     // past the chunk's last tile, an empty token range: its copies read zeros
     const int64_t next_tbase = s0 + MAX_SUB < s_end ? SUB * (s0 + MAX_SUB) : c.p.M;
     switch (ntm) {
-      case 4: run_tile<STAGE, 4, SHAPE>(c, tbase, next_tbase); break;
-      case 3: run_tile<STAGE, 3, SHAPE>(c, tbase, next_tbase); break;
+      case 4: if constexpr (MAX_TM >= 4) run_tile<STAGE, 4, SHAPE>(c, tbase, next_tbase); break;
+      case 3: if constexpr (MAX_TM >= 3) run_tile<STAGE, 3, SHAPE>(c, tbase, next_tbase); break;
       case 2: run_tile<STAGE, 2, SHAPE>(c, tbase, next_tbase); break;
       case 1: run_tile<STAGE, 1, SHAPE>(c, tbase, next_tbase); break;
       default: run_tile<STAGE, 0, SHAPE>(c, tbase, next_tbase); break;
