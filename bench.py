@@ -48,16 +48,28 @@ def fused_bytes(M):
             + M * 8 + M * 64 * 4 + M * N_HEADS * (HEAD_DIM // 2 + HEAD_DIM // 32))
 
 
+# the sources of the fused kernel that runs for K = 1536 (the pipelined one)
+FUSED_SOURCES = ("indexer_q_pipe.hip", "iq_common.h")
+
+
+def fused_source_digest():
+    """First 16 hex digits of the SHA-256 of the fused kernel's sources."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in FUSED_SOURCES:
+        with open(os.path.join(ROOT, "fp4_quantized_prep_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def measured_traffic():
     """HBM bytes per fused launch from the committed rocprofv3 counter summary
     (FETCH_SIZE and WRITE_SIZE scaled by a plain copy's readings), or None if
     the kernel source changed since the counters were taken."""
-    import hashlib
     prof = os.path.join(ROOT, "profiles", "indexer_q_chain_m4632_rocprofv3.md")
-    src = os.path.join(ROOT, "fp4_quantized_prep_amd", "csrc", "indexer_q.hip")
     try:
         fields = dict(line.strip().split(": ", 1) for line in open(prof) if line.strip().startswith("fused_"))
-        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        digest = fused_source_digest()
     except (OSError, ValueError):
         return None
     if fields.get("fused_kernel_source_sha256_16") != digest:
@@ -192,7 +204,7 @@ def main():
             "parallelism": "single GPU",
         },
         "roofline": {
-            "kernel": "indexer_q_kernel (fused GEMM + RoPE + Hadamard + FP4)",
+            "kernel": "indexer_q_pipe_kernel (fused GEMM + RoPE + Hadamard + FP4)",
             "bound": "mfma",
             "achieved": fused_tflops,
             "peak": PEAK_FP8_TFLOPS,

@@ -1,0 +1,612 @@
+// Pipelined variant of the fused indexer-Q kernel for K = 12 blocks of 128
+// (the 1536-wide input of the indexer's Q projection): the same computation
+// as indexer_q.hip (block-scaled FP8 GEMM on the matrix cores, RoPE,
+// Hadamard-128, FP4 with UE8M0 scales, all in registers), scheduled so that
+// the vector-ALU epilogue of one tile runs underneath the MFMAs of the next.
+//
+// TensorRT-LLM PR "Fuse DeepSeek-V4 Indexer Q projection with CuTe DSL",
+// sequence diagram (one GEMM whose epilogue applies RoPE and writes packed FP4
+// Q and scales); tokenspeed PR "perf(deepseek-v4): accelerate indexer Q and
+// packed FP8 quantization", Summary (RoPE, the Hadamard transform and FP4
+// quantization of Q).
+//
+// Why a second schedule. On gfx950 a wave that issues back-to-back MFMAs can
+// still issue about eight independent VALU instructions per 64-cycle MFMA for
+// free, but the epilogue (about 800 VALU instructions per 32-token sub-tile)
+// otherwise runs alone after each tile's K loop and costs about a third of
+// the kernel. Overlapping it needs two accumulator sets, so the tile shrinks:
+//   * 4 waves (one per SIMD); a workgroup owns a head pair (256 weight rows)
+//     and walks a contiguous range of 128-token tiles (4 sub-tiles of 32).
+//     Wave w computes head 2 pair + (w & 1) for the sub-tiles s of the tile
+//     with s % 2 == w >> 1: 2 sub-tiles, 128 accumulator registers (acc); the
+//     previous tile's 128 (accp) are read by its epilogue meanwhile.
+//   * The sets never swap roles: the epilogue has copied all of accp into
+//     VGPRs by the middle of the next K loop, and the MFMAs of a tile's last
+//     half-step write their sums into accp instead of acc. The tile loop is
+//     one body with no accumulator moves.
+//   * Three LDS stages of one 128-deep K block each (W 32 KiB + A 16 KiB + the
+//     tokens' scale words), 146 KiB in all. The copies of block b (13 per wave,
+//     bounds-checked buffer loads that write LDS directly) are split over the
+//     half-step after block b-3 is consumed and the half-step after it, so
+//     they have two blocks to land and never arrive as one burst; the block
+//     sequence runs straight across tile boundaries, so the next tile's first
+//     blocks stream in during the current tile's last ones. A copy costs one
+//     scalar add (its LDS address) and the load itself: row offsets are
+//     per-lane registers or per-slab scalars, the column within the K block
+//     is the instruction offset (added to the LDS address as well).
+//   * Each K block is two 64-deep half-steps with one barrier between them.
+//     A half-step issues one MFMA per slot and, in the same slot, its share
+//     of: the next half-step's LDS operand reads, the copies, and the
+//     previous tile's epilogue. The epilogue is cut into 24 phases (12 per
+//     sub-tile: loads from the accumulators, RoPE, seven butterfly stages,
+//     scaling, block maxima and FP4 conversion, stores), one phase per
+//     half-step of the 12-block loop.
+//   * The last tile's epilogue runs alone after its K loop.
+//   * The operand layout, scale handling, swizzle and epilogue arithmetic are
+//     those of indexer_q.hip (shared through iq_common.h).
+#include <type_traits>
+
+#include "iq_common.h"
+
+namespace iqp {
+namespace {
+namespace pipe {
+
+constexpr int NWAVES = 4;
+constexpr int NTHREADS = NWAVES * 64;
+constexpr int WROWS = 256;                          // weight rows: two heads
+constexpr int TOKS = 128;                           // tokens per tile
+constexpr int SUB = 32;                             // tokens per MFMA column tile
+constexpr int MAX_SUB = TOKS / SUB;                 // 4 sub-tiles per tile
+constexpr int MAX_TM = 2;                           // sub-tiles per wave
+constexpr int TM_STRIDE = 64;                       // tokens between a wave's two sub-tiles
+constexpr int NKB = 12;                             // K blocks (K = 1536)
+constexpr int NST = 3;                              // LDS stages
+constexpr int W_BYTES = WROWS * KB;                 // 32 KiB
+constexpr int A_BYTES = TOKS * KB;                  // 16 KiB
+constexpr int S_BYTES = TOKS * 4;                   // token scale words of one block
+constexpr int SLAB = 1024;                          // one wave-wide LDS copy
+constexpr int WCOPIES = W_BYTES / SLAB / NWAVES;    // 8
+constexpr int ACOPIES = A_BYTES / SLAB / NWAVES;    // 4
+constexpr int NCOPY = WCOPIES + ACOPIES + 1;        // 13 copies per wave per block
+constexpr int PART1 = 7;                            // copies issued in the first half-step of a block's window
+// scale words first: a copy's LDS address is given as (destination - its
+// column offset in the K block), which must not go below zero
+constexpr int S_OFF = 0;
+constexpr int W_OFF = S_OFF + NST * S_BYTES;
+constexpr int A_OFF = W_OFF + NST * W_BYTES;
+constexpr int LDS_BYTES = A_OFF + NST * A_BYTES;    // 148,992
+static_assert(W_OFF >= KB * (NKB - 1), "copy LDS bases must stay non-negative");
+// at a block barrier the copies of the block after next (13 per wave) may
+// still be in flight: s_waitcnt vmcnt(13)
+constexpr int WAITCNT_VM13 = (13 & 15) | (7 << 4) | (15 << 8) | ((13 >> 4) << 14);
+
+// A lane value the compiler must treat as new at each use: addresses built
+// from it are then computed where they are used instead of being hoisted out
+// of the tile loop, where each would hold a register pair for the whole loop.
+__device__ __forceinline__ int fresh(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// operands of one 64-deep half-step (a wave with NTM < 2 sub-tiles uses the first NTM)
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+struct Frags {
+  v8i a[MAX_TM];
+  v8i w[4];
+};
+
+// The previous tile's epilogue in flight: values of the sub-tile being
+// processed, its FP4 dwords and scale bytes, the RoPE rows of the next one.
+struct Epi {
+  float v[4][16];
+  uint32_t dw[4][2];
+  uint32_t sbytes;
+  RopeCS rope;      // RoPE rows of the sub-tile whose phase 0 comes next
+  int tlane;        // the epilogue tile's token of sub-tile 0 (sub-tile tm: + TM_STRIDE tm)
+  int pos1;         // the epilogue tile's sub-tile 1 position (clamped to the table)
+  int npos0, npos1; // the K-loop tile's positions (its epilogue comes next)
+};
+
+struct Ctx {
+  const IndexerQArgs& p;
+  uint8_t* lds;
+  int lane, half, wave, hn, th, head;
+  uint32_t wsc_lane;             // the head's weight-scale bytes, 4 per lane
+  rsrc_t rw, ra, rs, ra_n, rs_n; // weights; activations / scale words of this and the next tile
+  // Copy addressing. A copy's row part is a lane offset (bounds-checked:
+  // rows past the tokens read zeros) or, for the weights, a scalar offset per
+  // slab (rows that always exist); its column part within the K block is the
+  // instruction offset, which the hardware adds to the LDS address as well.
+  uint32_t vw;                   // weight lane offset (row within an 8-row slab, chunk)
+  uint32_t va[ACOPIES];          // activation lane offsets of the four slabs
+  uint32_t vs;                   // scale-word lane offset
+  int wrow[WCOPIES];             // weight slab row offsets (bytes)
+  int wave_lds;                  // 1 KiB per wave: this wave's part of each group of four slabs
+  int words_lds;                 // 256 bytes per wave pair: its half of the scale words
+  uint32_t rd_w[2][2], rd_a[2][2], rd_s;
+
+  __device__ Ctx(const IndexerQArgs& p_, uint8_t* lds_, int pair) : p(p_), lds(lds_) {
+    const int tid = threadIdx.x;
+    lane = tid & 63;
+    half = lane >> 5;
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    hn = wave & 1;
+    th = wave >> 1;
+    head = 2 * pair + hn;
+    const int head_c = head < p.H ? head : p.H - 1;   // odd H: the missing head reads zeros, never stored
+    const uint8_t* wsc = p.w_scales + (int64_t)head_c * NKB;
+    wsc_lane = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      if (4 * lane + b < NKB) wsc_lane |= (uint32_t)wsc[4 * lane + b] << (8 * b);
+    // copy i of this wave lands in rows 8 (wave + 4 i) + lane / 8, slot lane % 8,
+    // which holds the row's chunk (lane % 8) ^ ((row / 2) % 8): the slab index
+    // wave + 4 i has the parity of wave, so that is the same for every copy
+    const int chunk = (lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7);
+    const int64_t row0 = (int64_t)2 * pair * HEAD_DIM;
+    const int64_t wrows = (int64_t)p.H * HEAD_DIM - row0;
+    rw = make_rsrc(p.w + row0 * p.ldw, (uint64_t)(wrows < WROWS ? wrows : WROWS) * p.ldw);
+    vw = (uint32_t)((8 * wave + (lane >> 3)) * p.ldw + 16 * chunk);
+#pragma unroll
+    for (int i = 0; i < ACOPIES; ++i) va[i] = (uint32_t)((8 * wave + (lane >> 3) + 32 * i) * p.lda + 16 * chunk);
+    vs = (uint32_t)(4 * (64 * (wave & 1) + lane) * p.as_sm);   // waves w and w + 2 copy the same words
+    // slabs 4..7 hold the pair's second head; with an odd head count the last
+    // pair has none and they re-read the first head's rows (never stored)
+    const int hi = 2 * pair + 1 < p.H ? 128 * (int)p.ldw : 0;
+#pragma unroll
+    for (int w = 0; w < WCOPIES; ++w) wrow[w] = (w < 4 ? 0 : hi) + 32 * (w & 3) * (int)p.ldw;
+    wave_lds = SLAB * wave;
+    words_lds = 256 * (wave & 1);
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const uint32_t col = 16 * ((4 * kh + 2 * half + e) ^ ((lane >> 1) & 7));
+        rd_w[kh][e] = W_OFF + KB * (HEAD_DIM * hn + (lane & 31)) + col;
+        rd_a[kh][e] = A_OFF + KB * (32 * th + (lane & 31)) + col;
+      }
+    rd_s = S_OFF + 4 * (32 * th + (lane & 31));
+    // whole bases: the stage and row offsets fold into the reads' offset field
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        rd_w[kh][e] = (uint32_t)fresh((int)rd_w[kh][e]);
+        rd_a[kh][e] = (uint32_t)fresh((int)rd_a[kh][e]);
+      }
+    rd_s = (uint32_t)fresh((int)rd_s);
+  }
+
+  __device__ __forceinline__ void buffers(int64_t tbase, rsrc_t& a, rsrc_t& s) const {
+    const int64_t rows = p.M - tbase;
+    constexpr int64_t nw = (NKB + 3) / 4;
+    a = make_rsrc(p.a + tbase * p.lda, rows > 0 ? (uint64_t)rows * p.lda : 0);
+    s = make_rsrc(p.a_scale_bytes + 4 * tbase * p.as_sm,
+                  rows > 0 ? 4 * (uint64_t)((rows - 1) * p.as_sm + (nw - 1) * p.as_sw + 1) : 0);
+  }
+
+  // copy w (0..12) of K block j of this (NEXT: the next) tile into stage ST;
+  // w < 8: a W slab, w < 12: an A slab, 12: the scale words. The whole offset
+  // is in the lane offset, which the buffer bounds check covers.
+  // Copy WI (0..12) of K block J of this (NEXT: the next) tile into stage ST;
+  // WI < 8: a weight slab, < 12: an activation slab, 12: the scale words.
+  // The LDS address is formed by a scalar add in an asm statement: one per
+  // copy, at the copy (the compiler would otherwise keep all 39 per tile live).
+  template <int C>
+  __device__ __forceinline__ uint8_t* lds_at(int base) const {
+    int m;
+    asm volatile("s_add_u32 %0, %1, %2" : "=s"(m) : "s"(base), "i"(C) : "scc");
+    return lds + m;
+  }
+
+  template <int ST, bool NEXT, int WI, int J>
+  __device__ __forceinline__ void copy() const {
+    if constexpr (WI < WCOPIES) {
+      uint8_t* d = lds_at<W_OFF + ST * W_BYTES + SLAB * NWAVES * WI - KB * J>(wave_lds);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)d, 16, vw, wrow[WI], KB * J, 0);
+    } else if constexpr (WI < WCOPIES + ACOPIES) {
+      constexpr int i = WI - WCOPIES;
+      uint8_t* d = lds_at<A_OFF + ST * A_BYTES + SLAB * NWAVES * i - KB * J>(wave_lds);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(NEXT ? ra_n : ra, (lds_void*)d, 16, va[i], 0, KB * J, 0);
+    } else {
+      // the word offset stays in the lane offset, under the bounds check
+      const uint32_t u = (uint32_t)(4 * (J >> 2) * (int)p.as_sw);
+      uint8_t* d = lds_at<S_OFF + ST * S_BYTES>(words_lds);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(NEXT ? rs_n : rs, (lds_void*)d, 4, vs + u, 0, 0, 0);
+    }
+  }
+
+  template <int ST>
+  __device__ __forceinline__ v4u read16(bool is_a, int kh, int e, int rowoff) const {
+    const uint32_t base = is_a ? rd_a[kh][e] + ST * A_BYTES : rd_w[kh][e] + ST * W_BYTES;
+    return *reinterpret_cast<const v4u*>(lds + base + KB * rowoff);
+  }
+
+  template <int ST>
+  __device__ __forceinline__ int read_scale(int tm) const {
+    return (int)*reinterpret_cast<const uint32_t*>(lds + rd_s + ST * S_BYTES + 4 * TM_STRIDE * tm);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// The epilogue of one sub-tile as 12 phases of items that run in order. Phase
+// 0: the 64 dims past the RoPE slice out of the accumulators, then their
+// butterfly stage r-bit 0; 1: RoPE pairs (reading the accumulators), then
+// their r-bit 0; 2-4: r-bits 1-3; 5, 6: tn bits 0, 1; 7, 8: the cross-half
+// stage (v_permlane32_swap); 9: the 1/sqrt(128) scaling; 10, 11: block maxima,
+// exponents and FP4 conversion; 11 also fetches the RoPE rows of the next
+// sub-tile (once dims 0-63 are converted, into their registers' worth of
+// room, two half-steps ahead of their use) and ends with the stores.
+constexpr int phase_items(int h) {
+  return h == 0 ? 48 : h == 1 ? 32 : h <= 6 ? 32 : h <= 8 ? 16 : h == 9 ? 64 : h == 10 ? 2 : 4;
+}
+
+// index of the k-th r in 0..15 with bit rb clear
+__device__ __forceinline__ constexpr int r_clear(int k, int rb) { return (k & (rb - 1)) | ((k & ~(rb - 1)) << 1); }
+
+// LAST: no tile follows (the sub-tile after the last one has no RoPE rows to fetch)
+template <int H, int NTMP, bool LAST>
+__device__ __forceinline__ void epi_item(Epi& es, v16f (&accp)[MAX_TM][4], int i, const Ctx& c) {
+  constexpr int tm = H / 12, h = H % 12;
+  if constexpr (tm >= NTMP) {
+    return;
+  } else if constexpr (h == 0) {
+    // The accumulators are named in AGPRs right where the phase starts reading
+    // them: copies into VGPRs cannot be placed any earlier (a whole set
+    // copied out at the top of the K loop would not fit beside its operands).
+    if (i == 0) asm volatile("" : "+a"(accp[tm][2]), "+a"(accp[tm][3]));
+    if (i < 32) {
+      es.v[2 + (i >> 4)][i & 15] = accp[tm][2 + (i >> 4)][i & 15];
+    } else {
+      const int k = i - 32, tn = 2 + (k >> 3), r = r_clear(k & 7, 1);
+      const float a = es.v[tn][r], b = es.v[tn][r | 1];
+      es.v[tn][r] = a + b;
+      es.v[tn][r | 1] = a - b;
+    }
+  } else if constexpr (h == 1) {
+    if (i == 0) asm volatile("" : "+a"(accp[tm][0]), "+a"(accp[tm][1]));
+    if (i < 16) {                  // RoPE pair (i, i + 32), i = 8 g + 4 half + s
+      const int g = i >> 2, s = i & 3;
+      const float x = accp[tm][0][4 * g + s], y = accp[tm][1][4 * g + s];
+      const float cc = es.rope.c[g][s], ss = es.rope.s[g][s];
+      es.v[0][4 * g + s] = x * cc - y * ss;
+      es.v[1][4 * g + s] = y * cc + x * ss;
+    } else {
+      const int k = i - 16, tn = k >> 3, r = r_clear(k & 7, 1);
+      const float a = es.v[tn][r], b = es.v[tn][r | 1];
+      es.v[tn][r] = a + b;
+      es.v[tn][r | 1] = a - b;
+    }
+  } else if constexpr (h <= 4) {   // r bits 1..3
+    constexpr int rb = 1 << (h - 1);
+    const int tn = i >> 3, r = r_clear(i & 7, rb);
+    const float a = es.v[tn][r], b = es.v[tn][r | rb];
+    es.v[tn][r] = a + b;
+    es.v[tn][r | rb] = a - b;
+  } else if constexpr (h <= 6) {   // tn bits 0, 1
+    constexpr int tb = 1 << (h - 5);
+    const int tnp = i >> 4, r = i & 15;
+    const int tn = (tnp & (tb - 1)) | ((tnp & ~(tb - 1)) << 1);
+    const float a = es.v[tn][r], b = es.v[tn | tb][r];
+    es.v[tn][r] = a + b;
+    es.v[tn | tb][r] = a - b;
+  } else if constexpr (h <= 8) {   // dim bit 2, across the lane halves (see epilogue_tile)
+    const int k = (h - 7) * 16 + i, tn = k >> 3, r = r_clear(k & 7, 4);
+    float r0, r1;
+    swap32(es.v[tn][r], es.v[tn][r | 4], r0, r1);
+    es.v[tn][r] = r0 + r1;
+    es.v[tn][r | 4] = r0 - r1;
+  } else if constexpr (h == 9) {
+    es.v[i >> 4][i & 15] *= INV_SQRT_128;
+  } else {
+    if (h == 11 && i == 0) {       // RoPE rows of the next sub-tile: this tile's second, or the next tile's first
+      if (tm == 0)
+        es.rope = load_rope(es.pos1, fresh(c.half), c.p);
+      else if (!LAST)
+        es.rope = load_rope(es.npos0, fresh(c.half), c.p);
+      return;
+    }
+    if (h == 11 && i == 3) {       // assemble and store (dword (tn, r3) at 4 tn + 2 r3 + half)
+      const int64_t t = (int64_t)es.tlane + TM_STRIDE * tm;
+      uint32_t out[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int tn = q >> 1, r3 = q & 1;
+        uint32_t r1;
+        const uint32_t r0 = swap32_u(es.dw[tn][r3], es.dw[tn + 2][r3], r1);
+        out[2 * q] = r0;
+        out[2 * q + 1] = r1;
+      }
+      if (c.head < c.p.H && t < c.p.M) {
+        const int half = fresh(c.half);
+        uint8_t* dst = c.p.q_fp4 + (t * c.p.H + c.head) * (HEAD_DIM / 2) + 32 * half;
+        *reinterpret_cast<v4u*>(dst) = v4u{out[0], out[1], out[2], out[3]};
+        *reinterpret_cast<v4u*>(dst + 16) = v4u{out[4], out[5], out[6], out[7]};
+        if (half == 0) *reinterpret_cast<uint32_t*>(c.p.q_scales + (t * c.p.H + c.head) * 4) = es.sbytes;
+      }
+      return;
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {  // FP4 block tn over dims 32 tn .. 32 tn + 31 (16 here, 16 in the partner lane)
+      const int tn = 2 * (h - 10) + q;
+      if (q != (h == 11 ? i - 1 : i)) continue;
+      float m = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(es.v[tn][r]));
+      float m0, m1;
+      swap32(m, m, m0, m1);
+      const int e = fp4_exponent(fmaxf(m0, m1));
+      if (tn == 0) es.sbytes = 0;
+      es.sbytes |= (uint32_t)(e + 127) << (8 * tn);
+      const float scale = __uint_as_float((uint32_t)(e + 127) << 23);
+#pragma unroll
+      for (int r3 = 0; r3 < 2; ++r3) {
+        const float* x = &es.v[tn][8 * r3];
+        uint32_t d = 0;
+        d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, x[0], x[1], scale, 0);
+        d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, x[2], x[3], scale, 1);
+        d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, x[4], x[5], scale, 2);
+        d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, x[6], x[7], scale, 3);
+        es.dw[tn][r3] = d;
+      }
+    }
+  }
+}
+
+// slot s of NS runs items [n s / NS, n (s + 1) / NS) of epilogue half-step H
+template <int H, int NTMP, int NS>
+__device__ __forceinline__ void epi_slot(Epi& es, v16f (&accp)[MAX_TM][4], int slot, const Ctx& c) {
+  if constexpr (H < 24 && NTMP > 0) {
+    constexpr int n = phase_items(H % 12);
+#pragma unroll
+    for (int i = n * slot / NS; i < n * (slot + 1) / NS; ++i) epi_item<H, NTMP, false>(es, accp, i, c);
+  }
+}
+
+// the whole epilogue of a tile, alone (after the chunk's last K loop)
+template <int NTMP>
+__device__ __forceinline__ void epilogue_alone(Epi& es, v16f (&accp)[MAX_TM][4], const Ctx& c) {
+  auto run = [&](auto hc) __attribute__((always_inline)) {
+    constexpr int H = decltype(hc)::value;
+    constexpr int n = phase_items(H % 12);
+#pragma unroll
+    for (int i = 0; i < n; ++i) epi_item<H, NTMP, true>(es, accp, i, c);
+  };
+#define IQP_EPI_H(H) run(std::integral_constant<int, H>{});
+  IQP_EPI_H(0) IQP_EPI_H(1) IQP_EPI_H(2) IQP_EPI_H(3) IQP_EPI_H(4) IQP_EPI_H(5)
+  IQP_EPI_H(6) IQP_EPI_H(7) IQP_EPI_H(8) IQP_EPI_H(9) IQP_EPI_H(10) IQP_EPI_H(11)
+  IQP_EPI_H(12) IQP_EPI_H(13) IQP_EPI_H(14) IQP_EPI_H(15) IQP_EPI_H(16) IQP_EPI_H(17)
+  IQP_EPI_H(18) IQP_EPI_H(19) IQP_EPI_H(20) IQP_EPI_H(21) IQP_EPI_H(22) IQP_EPI_H(23)
+#undef IQP_EPI_H
+}
+
+// ---------------------------------------------------------------------------
+// One half-step: slot s issues MFMA s of 4 NTM on the operands F, then its
+// share of the LDS reads filling N (the next half-step's operands), of the
+// copies (COPY_LO .. COPY_HI of K block JD of this or the NEXT tile into stage
+// DST) and of epilogue half-step EH, then a scheduling fence.
+//   RKH >= 0: read half RKH of the block in stage RST; RSC: also its scale words
+//   TO_P: the tile's last half-step, whose MFMAs write the finished sums into
+//         accp (read by this tile's epilogue during the next K loop)
+template <int NTM, int RST, int RKH, bool RSC, int COPY_LO, int COPY_HI, int DST, bool NEXT, int JD, int EH,
+          int NTMP, bool TO_P>
+__device__ __forceinline__ void half_step(Ctx& c, v16f (&acc)[MAX_TM][4], const Frags& F, const int (&as)[MAX_TM],
+                                          int ws, Frags& N, int (&asn)[MAX_TM], Epi& es,
+                                          v16f (&accp)[MAX_TM][4]) {
+  constexpr int NM = 4 * NTM;
+  constexpr int NS = NM > 0 ? NM : 1;
+  constexpr int NCP = COPY_HI - COPY_LO;
+  constexpr int NSCALE = RSC ? NTM : 0;
+  constexpr int NSR = 3 * NS / 4 > 0 ? 3 * NS / 4 : 1;   // scale words and A fragments: first three quarters
+  static_for<0, NS>([&](auto sc) __attribute__((always_inline)) {
+    constexpr int slot = decltype(sc)::value;
+    if (slot < NM) {
+      const int tn = slot / (NTM > 0 ? NTM : 1), tm = slot % (NTM > 0 ? NTM : 1);
+      v16f& dst = TO_P ? accp[tm][tn] : acc[tm][tn];
+      dst = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.w[tn], F.a[tm], acc[tm][tn], 0, 0, 0, ws, 0, as[tm]);
+      asm volatile("" : "+a"(dst));   // the MFMA stays in its slot
+    }
+    static_for<NCP * slot / NS, NCP * (slot + 1) / NS>([&](auto kc) __attribute__((always_inline)) {
+      c.template copy<DST, NEXT, COPY_LO + decltype(kc)::value, JD>();
+    });
+    constexpr int NRA = RKH >= 0 ? NSCALE + NTM : 0;
+#pragma unroll
+    for (int r = NRA * slot / NSR; r < (slot < NSR ? NRA * (slot + 1) / NSR : 0); ++r) {
+      if (r < NSCALE) {
+        asn[r] = c.read_scale<RST>(r);
+      } else {
+        const int tm = r - NSCALE;
+        N.a[tm] = make_v8i(c.read16<RST>(true, RKH, 0, TM_STRIDE * tm), c.read16<RST>(true, RKH, 1, TM_STRIDE * tm));
+      }
+    }
+    // W fragment tn right after its last use in this half-step (slot NTM (tn + 1) - 1),
+    // so the next one takes over its registers
+    if constexpr (RKH >= 0) {
+#pragma unroll
+      for (int tn = 0; tn < 4; ++tn)
+        if (slot == (NTM > 0 ? NTM * (tn + 1) - 1 : 0))
+          N.w[tn] = make_v8i(c.read16<RST>(false, RKH, 0, 32 * tn), c.read16<RST>(false, RKH, 1, 32 * tn));
+    }
+    epi_slot<EH, NTMP, NS>(es, accp, slot, c);
+    __builtin_amdgcn_sched_barrier(0);
+  });
+}
+
+// K block j (compile time, stage j % 3) of a tile:
+//   half A: MFMAs on block j's first half, reads of its second half, copies
+//           PART1.. of block j+2, epilogue half-step 2j;
+//   barrier (block j+1 has landed, all of block j has been read);
+//   half B: MFMAs on block j's second half, reads of block j+1's first half
+//           and scale words, copies ..PART1 of block j+3 into stage j % 3,
+//           epilogue half-step 2j+1.
+// Blocks past the tile's 12 are the next tile's (the copies use its buffers).
+template <int NTM, int J, int NTMP, bool FIRST>
+__device__ __forceinline__ void k_block(Ctx& c, v16f (&acc)[MAX_TM][4], Frags& f0, Frags& f1,
+                                        int (&as0)[MAX_TM], int (&as1)[MAX_TM], Epi& es,
+                                        v16f (&accp)[MAX_TM][4]) {
+  constexpr int ST = J % NST;
+  const int ws = (int)((uint32_t)__builtin_amdgcn_readlane((int)c.wsc_lane, J >> 2) >> (8 * (J & 3)));
+  int as[MAX_TM];
+#pragma unroll
+  for (int tm = 0; tm < MAX_TM; ++tm) as[tm] = (int)((uint32_t)as0[tm] >> (8 * (J & 3)));
+  __builtin_amdgcn_sched_barrier(0);
+  // in a chunk's first tile the prologue copied blocks 0 and 1 whole and block 2's first part
+  constexpr int J2 = J + 2;
+  half_step<NTM, ST, 1, false, PART1, NCOPY, J2 % NST, (J2 >= NKB), J2 % NKB, 2 * J, NTMP, false>(
+      c, acc, f0, as, ws, f1, as1, es, accp);
+  __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);
+  __builtin_amdgcn_s_waitcnt(WAITCNT_VM13);
+  block_barrier();   // all of block j read by every wave; block j+1 has landed
+  __builtin_amdgcn_sched_barrier(0);
+  constexpr int J3 = J + 3;
+  half_step<NTM, (J + 1) % NST, 0, true, 0, PART1, ST, (J3 >= NKB), J3 % NKB, 2 * J + 1, NTMP, J == NKB - 1>(
+      c, acc, f1, as, ws, f0, as1, es, accp);
+#pragma unroll
+  for (int tm = 0; tm < MAX_TM; ++tm) as0[tm] = as1[tm];
+  (void)FIRST;
+}
+
+// The K loop of one tile (acc, zeroed here) with the previous tile's epilogue
+// (accp, NTMP sub-tiles per wave; 0: none) running underneath; the epilogue
+// has read all of accp by block 7, and the last half-step's MFMAs write this
+// tile's sums there (so the sets never swap roles). On entry the
+// operands of block 0's first half are in f0 / as0 and blocks 0, 1 (and part
+// of 2) are in flight or landed; on exit the same holds for the next tile.
+// The epilogue fetches the RoPE rows of its next sub-tile itself; with no
+// epilogue running, this tile's first ones are fetched after block 9.
+template <int NTM, int NTMP>
+__device__ __forceinline__ void k_loop(Ctx& c, v16f (&acc)[MAX_TM][4], Frags& f0, Frags& f1,
+                                       int (&as0)[MAX_TM], int (&as1)[MAX_TM], Epi& es,
+                                       v16f (&accp)[MAX_TM][4]) {
+#pragma unroll
+  for (int tm = 0; tm < MAX_TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[tm][tn][r] = 0.f;
+#define IQP_KB(J) k_block<NTM, J, NTMP, false>(c, acc, f0, f1, as0, as1, es, accp);
+  IQP_KB(0) IQP_KB(1) IQP_KB(2) IQP_KB(3) IQP_KB(4) IQP_KB(5) IQP_KB(6) IQP_KB(7) IQP_KB(8) IQP_KB(9)
+  if constexpr (NTMP == 0) es.rope = load_rope(es.npos0, c.half, c.p);
+  IQP_KB(10) IQP_KB(11)
+#undef IQP_KB
+  // every MFMA of the tile completes here
+#pragma unroll
+  for (int tm = 0; tm < NTM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn) asm volatile("" : "+a"(accp[tm][tn]));
+}
+
+// Before a tile's K loop: fetch its positions (the K loop fetches RoPE rows
+// from them). After it: the tile becomes the epilogue's.
+// positions clamped into the table (the launcher guarantees max_pos < 2^31 and M < 2^31)
+__device__ __forceinline__ int clamped_position(int64_t t, const IndexerQArgs& p) {
+  const int64_t pos = load_position(t, p);
+  return (int)(pos < 0 ? 0 : (pos >= p.max_pos ? p.max_pos - 1 : pos));
+}
+
+__device__ __forceinline__ void tile_positions(Ctx& c, Epi& es, int64_t tbase) {
+  const int64_t tl = tbase + 32 * c.th + (fresh(c.lane) & 31);
+  es.npos0 = clamped_position(tl, c.p);
+  es.npos1 = clamped_position(tl + TM_STRIDE, c.p);
+}
+
+__device__ __forceinline__ void hand_over(Ctx& c, Epi& es, int64_t tbase) {
+  es.tlane = (int)(tbase + 32 * c.th + (fresh(c.lane) & 31));
+  es.pos1 = es.npos1;
+}
+
+}  // namespace pipe
+
+// Workgroup = head pair x token chunk, as in indexer_q.hip.
+__global__ __launch_bounds__(pipe::NTHREADS, 1)
+void indexer_q_pipe_kernel(IndexerQArgs p) {
+  using namespace pipe;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
+
+  const int bid = blockIdx.x;
+  const int npairs = (p.H + 1) >> 1;
+  const int cpp = p.chunks;
+  int pair, chunk;
+  if ((npairs & 7) == 0) {
+    const int ppx = npairs >> 3;
+    const int s = bid >> 3;
+    pair = (bid & 7) * ppx + s % ppx;
+    chunk = s / ppx;
+  } else {
+    pair = bid % npairs;
+    chunk = bid / npairs;
+  }
+  // the chunk's tiles [t_begin, t_end) of the ceil(M / 128) tiles
+  const int64_t ntiles = (p.M + TOKS - 1) / TOKS;
+  const int64_t t_begin = ntiles * chunk / cpp;
+  const int64_t t_end = ntiles * (chunk + 1) / cpp;
+  if (t_begin >= t_end) return;   // uniform over the workgroup
+
+  Ctx c(p, lds, pair);
+  auto tbase_of = [&](int64_t tile) __attribute__((always_inline)) { return TOKS * tile; };
+
+  // prologue: blocks 0 and 1 of the first tile whole, block 2's first part
+  c.buffers(tbase_of(t_begin), c.ra, c.rs);
+  c.buffers(t_begin + 1 < t_end ? tbase_of(t_begin + 1) : p.M, c.ra_n, c.rs_n);
+  static_for<0, NCOPY>([&](auto w) __attribute__((always_inline)) { c.template copy<0, false, decltype(w)::value, 0>(); });
+  static_for<0, NCOPY>([&](auto w) __attribute__((always_inline)) { c.template copy<1, false, decltype(w)::value, 1>(); });
+  static_for<0, PART1>([&](auto w) __attribute__((always_inline)) { c.template copy<2, false, decltype(w)::value, 2>(); });
+  // block 0 has landed once only blocks 1 and 2's copies may be outstanding
+  __builtin_amdgcn_s_waitcnt((((NCOPY + PART1) & 15) | (7 << 4) | (15 << 8) | (((NCOPY + PART1) >> 4) << 14)));
+  block_barrier();
+
+  Frags f0, f1;
+  int as0[MAX_TM] = {}, as1[MAX_TM] = {};
+  Epi es;
+  v16f acc[MAX_TM][4], accp[MAX_TM][4];
+#pragma unroll
+  for (int tm = 0; tm < MAX_TM; ++tm) as0[tm] = c.read_scale<0>(tm);
+#pragma unroll
+  for (int tm = 0; tm < MAX_TM; ++tm)
+    f0.a[tm] = make_v8i(c.read16<0>(true, 0, 0, TM_STRIDE * tm), c.read16<0>(true, 0, 1, TM_STRIDE * tm));
+#pragma unroll
+  for (int tn = 0; tn < 4; ++tn)
+    f0.w[tn] = make_v8i(c.read16<0>(false, 0, 0, 32 * tn), c.read16<0>(false, 0, 1, 32 * tn));
+
+  // Every tile is computed whole (4 sub-tiles; past M the copies read zeros
+  // and nothing is stored), so the steady loop is one code path.
+  int64_t tile = t_begin;
+  auto one_tile = [&](auto ntmp_c) __attribute__((always_inline)) {
+    tile_positions(c, es, tbase_of(tile));
+    k_loop<MAX_TM, decltype(ntmp_c)::value>(c, acc, f0, f1, as0, as1, es, accp);
+    hand_over(c, es, tbase_of(tile));
+    // the copy buffers move to the next tile; the one after it streams in
+    // during the next tile's last blocks
+    c.ra = c.ra_n;
+    c.rs = c.rs_n;
+    c.buffers(tile + 2 < t_end ? tbase_of(tile + 2) : p.M, c.ra_n, c.rs_n);
+    ++tile;
+  };
+  one_tile(std::integral_constant<int, 0>{});
+  while (tile < t_end) one_tile(std::integral_constant<int, MAX_TM>{});
+  epilogue_alone<MAX_TM>(es, accp, c);
+  __builtin_amdgcn_s_waitcnt(WAITCNT_VM0);   // no LDS copy may outlive the workgroup
+}
+
+}  // namespace
+
+// token indices and positions are held in 32-bit registers
+bool indexer_q_pipe_supported(const IndexerQArgs& a) {
+  return a.nkb == pipe::NKB && a.M <= 0x7FFFFFFF - 2 * pipe::TOKS && a.max_pos <= 0x7FFFFFFF;
+}
+
+hipError_t launch_indexer_q_pipe(const IndexerQArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)((int64_t)((a.H + 1) / 2) * a.chunks)), block(pipe::NTHREADS);
+  hipLaunchKernelGGL(indexer_q_pipe_kernel, grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace iqp

@@ -34,6 +34,14 @@ hipError_t launch_fp8_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx
 // stage -1: FP4 output; 0, 1, 2: float32 diagnostics (see iqprep.h)
 hipError_t launch_indexer_q(const IndexerQArgs& args, int stage, hipStream_t stream);
 
+// the pipelined FP4-output kernel (indexer_q_pipe.hip) for the shapes it takes
+// (K = 1536, token counts and positions that fit in 31 bits); args.chunks set
+bool indexer_q_pipe_supported(const IndexerQArgs& args);
+hipError_t launch_indexer_q_pipe(const IndexerQArgs& args, hipStream_t stream);
+
+// compute units of the current device (cached per device)
+int cu_count();
+
 hipError_t launch_rope_table(double theta, int64_t max_pos, int32_t rope_dim,
                              float* cos_sin, hipStream_t stream);
 
