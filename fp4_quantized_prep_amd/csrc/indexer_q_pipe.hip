@@ -111,8 +111,10 @@ struct Epi {
   uint32_t sbytes;
   RopeCS rope;      // RoPE rows of the sub-tile whose phase 0 comes next
   int tlane;        // the epilogue tile's token of sub-tile 0 (sub-tile tm: + TM_STRIDE tm)
-  int pos1;         // the epilogue tile's sub-tile 1 position (clamped to the table)
-  int npos0, npos1; // the K-loop tile's positions (its epilogue comes next)
+  // positions as loaded (clamped into the table where the RoPE rows are
+  // fetched, so no load is waited for before then)
+  int64_t pos1;         // the epilogue tile's sub-tile 1
+  int64_t npos0, npos1; // the K-loop tile's (its epilogue comes next)
 };
 
 struct Ctx {
@@ -242,15 +244,28 @@ struct Ctx {
 // butterfly stage r-bit 0; 1: RoPE pairs (reading the accumulators), then
 // their r-bit 0; 2-4: r-bits 1-3; 5, 6: tn bits 0, 1; 7, 8: the cross-half
 // stage (v_permlane32_swap); 9: the 1/sqrt(128) scaling; 10, 11: block maxima,
-// exponents and FP4 conversion; 11 also fetches the RoPE rows of the next
-// sub-tile (once dims 0-63 are converted, into their registers' worth of
-// room, two half-steps ahead of their use) and ends with the stores.
+// exponents and FP4 conversion, 10 of dims 0-63 and 11 of dims 64-127. Once
+// dims 0-63 are converted, the RoPE rows of the next sub-tile are fetched
+// into their registers' worth of room, four loads in each of phases 10 and
+// 11 (the copies keep the memory pipeline busy, so loads come a few at a
+// time); 11 ends with the stores.
 constexpr int phase_items(int h) {
-  return h == 0 ? 48 : h == 1 ? 32 : h <= 6 ? 32 : h <= 8 ? 16 : h == 9 ? 64 : h == 10 ? 2 : 4;
+  return h == 0 ? 48 : h == 1 ? 32 : h <= 6 ? 32 : h <= 8 ? 16 : h == 9 ? 64 : h == 10 ? 6 : 7;
 }
 
 // index of the k-th r in 0..15 with bit rb clear
 __device__ __forceinline__ constexpr int r_clear(int k, int rb) { return (k & (rb - 1)) | ((k & ~(rb - 1)) << 1); }
+
+// load L (0..7) of the RoPE rows of position pos: cosines (even L) or sines
+// of angle group L / 2, this lane's half of it
+__device__ __forceinline__ void rope_part(Epi& es, int64_t pos, int L, const Ctx& c) {
+  pos = pos < 0 ? 0 : (pos >= c.p.max_pos ? c.p.max_pos - 1 : pos);
+  const float* cs = c.p.cos_sin + pos * 64 + 8 * (L >> 1) + 4 * fresh(c.half);
+  if (L & 1)
+    es.rope.s[L >> 1] = *reinterpret_cast<const v4f*>(cs + 32);
+  else
+    es.rope.c[L >> 1] = *reinterpret_cast<const v4f*>(cs);
+}
 
 // LAST: no tile follows (the sub-tile after the last one has no RoPE rows to fetch)
 template <int H, int NTMP, bool LAST>
@@ -307,14 +322,18 @@ __device__ __forceinline__ void epi_item(Epi& es, v16f (&accp)[MAX_TM][4], int i
   } else if constexpr (h == 9) {
     es.v[i >> 4][i & 15] *= INV_SQRT_128;
   } else {
-    if (h == 11 && i == 0) {       // RoPE rows of the next sub-tile: this tile's second, or the next tile's first
+    // item roles: phase 10: 0, 1 convert dims 0-63 (block tn = item), 2-5 RoPE
+    // loads 0-3; phase 11: 0-3 RoPE loads 4-7, 4, 5 convert dims 64-127, 6 stores
+    const int load = h == 10 ? i - 2 : i + 4;
+    if ((h == 10 && i >= 2) || (h == 11 && i < 4)) {
+      // RoPE rows of the next sub-tile: this tile's second, or the next tile's first
       if (tm == 0)
-        es.rope = load_rope(es.pos1, fresh(c.half), c.p);
+        rope_part(es, es.pos1, load, c);
       else if (!LAST)
-        es.rope = load_rope(es.npos0, fresh(c.half), c.p);
+        rope_part(es, es.npos0, load, c);
       return;
     }
-    if (h == 11 && i == 3) {       // assemble and store (dword (tn, r3) at 4 tn + 2 r3 + half)
+    if (h == 11 && i == 6) {       // assemble and store (dword (tn, r3) at 4 tn + 2 r3 + half)
       const int64_t t = (int64_t)es.tlane + TM_STRIDE * tm;
       uint32_t out[8];
 #pragma unroll
@@ -337,7 +356,7 @@ __device__ __forceinline__ void epi_item(Epi& es, v16f (&accp)[MAX_TM][4], int i
 #pragma unroll
     for (int q = 0; q < 2; ++q) {  // FP4 block tn over dims 32 tn .. 32 tn + 31 (16 here, 16 in the partner lane)
       const int tn = 2 * (h - 10) + q;
-      if (q != (h == 11 ? i - 1 : i)) continue;
+      if (q != (h == 11 ? i - 4 : i)) continue;
       float m = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(es.v[tn][r]));
@@ -413,6 +432,9 @@ __device__ __forceinline__ void half_step(Ctx& c, v16f (&acc)[MAX_TM][4], const 
       v16f& dst = TO_P ? accp[tm][tn] : acc[tm][tn];
       dst = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.w[tn], F.a[tm], acc[tm][tn], 0, 0, 0, ws, 0, as[tm]);
       asm volatile("" : "+a"(dst));   // the MFMA stays in its slot
+      // acc stays live past the MFMA writing accp, so accp cannot take acc's
+      // registers (it would have to move back into its own at the tile's end)
+      if constexpr (TO_P) asm volatile("" ::"a"(acc[tm][tn]));
     }
     static_for<NCP * slot / NS, NCP * (slot + 1) / NS>([&](auto kc) __attribute__((always_inline)) {
       c.template copy<DST, NEXT, COPY_LO + decltype(kc)::value, JD>();
@@ -505,17 +527,11 @@ __device__ __forceinline__ void k_loop(Ctx& c, v16f (&acc)[MAX_TM][4], Frags& f0
 }
 
 // Before a tile's K loop: fetch its positions (the K loop fetches RoPE rows
-// from them). After it: the tile becomes the epilogue's.
-// positions clamped into the table (the launcher guarantees max_pos < 2^31 and M < 2^31)
-__device__ __forceinline__ int clamped_position(int64_t t, const IndexerQArgs& p) {
-  const int64_t pos = load_position(t, p);
-  return (int)(pos < 0 ? 0 : (pos >= p.max_pos ? p.max_pos - 1 : pos));
-}
-
+// from them near its end). After it: the tile becomes the epilogue's.
 __device__ __forceinline__ void tile_positions(Ctx& c, Epi& es, int64_t tbase) {
   const int64_t tl = tbase + 32 * c.th + (fresh(c.lane) & 31);
-  es.npos0 = clamped_position(tl, c.p);
-  es.npos1 = clamped_position(tl + TM_STRIDE, c.p);
+  es.npos0 = load_position(tl, c.p);
+  es.npos1 = load_position(tl + TM_STRIDE, c.p);
 }
 
 __device__ __forceinline__ void hand_over(Ctx& c, Epi& es, int64_t tbase) {
@@ -598,9 +614,9 @@ void indexer_q_pipe_kernel(IndexerQArgs p) {
 
 }  // namespace
 
-// token indices and positions are held in 32-bit registers
+// token indices are held in 32-bit registers
 bool indexer_q_pipe_supported(const IndexerQArgs& a) {
-  return a.nkb == pipe::NKB && a.M <= 0x7FFFFFFF - 2 * pipe::TOKS && a.max_pos <= 0x7FFFFFFF;
+  return a.nkb == pipe::NKB && a.M <= 0x7FFFFFFF - 2 * pipe::TOKS;
 }
 
 hipError_t launch_indexer_q_pipe(const IndexerQArgs& a, hipStream_t stream) {

@@ -35,7 +35,7 @@ hipError_t launch_fp8_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx
 hipError_t launch_indexer_q(const IndexerQArgs& args, int stage, hipStream_t stream);
 
 // the pipelined FP4-output kernel (indexer_q_pipe.hip) for the shapes it takes
-// (K = 1536, token counts and positions that fit in 31 bits); args.chunks set
+// (K = 1536, token counts that fit in 31 bits); args.chunks set
 bool indexer_q_pipe_supported(const IndexerQArgs& args);
 hipError_t launch_indexer_q_pipe(const IndexerQArgs& args, hipStream_t stream);
 
