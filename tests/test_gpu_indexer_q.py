@@ -128,6 +128,36 @@ def test_fused_chain_other_head_counts(gpu_lib, table, H):
     assert C.check_fp4(q, s, ref["z"], ref["q_fp4"], ref["q_scales"])["ok"]
 
 
+@pytest.mark.parametrize("K", [1024, 2048])
+def test_fused_chain_other_k(gpu_lib, table, K):
+    """K other than 1536 runs the general (non-pipelined) fused kernel."""
+    H, M = 4, 70
+    codes, sb = S.weights(N=H * 128, K=K, seed=101)
+    g = S.rng("indexer_q_m128", 900 + K)
+    x = S.activations_outlier(g, M, K)
+    pos = S.positions_uniform(g, M, 4096)
+    _, _, q, s = device_chain(gpu_lib, x, codes.cuda(), sb.cuda(), pos, table[4096], n_heads=H)
+    ref = oracle_chain_from_x(x, codes, sb, pos, H)
+    rep = C.check_fp4(q, s, ref["z"], ref["q_fp4"], ref["q_scales"])
+    print(f"K={K}", rep)
+    assert rep["ok"], rep
+
+
+@pytest.mark.parametrize("M", [1157, 2309])
+def test_fused_chain_uneven_tile_chunks(gpu_lib, weights, table, M):
+    """Token counts whose 128-token tiles split unevenly over the 8 chunks of
+    each of the 32 head pairs (1 or 2 tiles per chunk at 1157, 2 or 3 at
+    2309), with a ragged last tile; every token checked."""
+    codes, sb, wd, wsd = weights
+    inp = S.indexer_q_inputs("indexer_q_m128", M=M)
+    x, pos = inp["x"], inp["positions"]
+    _, _, q, s = device_chain(gpu_lib, x, wd, wsd, pos, table[4096])
+    ref = oracle_chain_from_x(x, codes, sb, pos, 64)
+    rep = C.check_fp4(q, s, ref["z"], ref["q_fp4"], ref["q_scales"])
+    print(f"M={M}", rep)
+    assert rep["ok"], rep
+
+
 def _sampled_check(iqp, weights, x, pos, cs, n_sample, seed):
     codes, sb, wd, wsd = weights
     _, _, q, s = device_chain(iqp, x, wd, wsd, pos, cs)
