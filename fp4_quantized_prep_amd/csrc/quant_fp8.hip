@@ -7,35 +7,41 @@
 //
 // The work is HBM-bound (2 bytes in, 1 + 1/128 bytes out per element), so the
 // kernel is organised around wide, coalesced memory operations:
-//   * one wave64 owns one packed scale word = 4 blocks = 512 contiguous bf16 of
-//     a row (1 KiB); lane l loads 16 B (8 bf16), so the 16 lanes of a DPP row
-//     hold exactly one 128-element block;
-//   * the block amax is reduced with four DPP max steps inside the row, on the
-//     bf16 magnitude bits as integers (order-free and exact), with no LDS;
+//   * one wave64 owns two packed scale words = 8 blocks = 1024 bf16 (2 KiB of
+//     input); lane l loads 32 B (16 bf16), so 8 lanes hold one 128-element
+//     block and each half-wave one word;
+//   * the block amax is reduced with three DPP max steps inside each group of
+//     8 lanes, on the bf16 magnitude bits as integers (order-free and exact),
+//     with no LDS;
 //   * the scale exponent comes from the amax bits with integer arithmetic;
 //   * v_cvt_pk_fp8_f32 rounds x * 2^-e to E4M3 (OCP "fn", round to nearest
-//     even, subnormals kept); lanes store 8 B each, 512 B per wave contiguous;
-//   * the four block bytes are gathered with readlane and stored as one word;
-//   * each wave keeps QUNROLL words' loads in flight before converting.
+//     even, subnormals kept); lanes store 16 B each, 512 B per half-wave
+//     contiguous;
+//   * the four block bytes of each word are gathered with readlane and stored
+//     as one dword;
+//   * loads and stores are non-temporal (the data is streamed once): measured
+//     on MI355X at [4632, 7168], 19.1 us against 22.0 us for cached 16-byte
+//     loads and 8-byte stores, and a plain device copy of the same input
+//     runs at 5.05 TB/s.
 #include "iqp_internal.h"
 
 namespace iqp {
 namespace {
 
-constexpr int QWAVES = 4;   // waves per workgroup
-constexpr int QUNROLL = 4;  // scale words (1 KiB of input each) per wave
+constexpr int QWAVES = 4;  // waves per workgroup, two scale words each
 
 // DPP controls (gfx9 encoding)
 constexpr int DPP_QUAD_XOR1 = 0xB1;     // quad_perm [1,0,3,2]
 constexpr int DPP_QUAD_XOR2 = 0x4E;     // quad_perm [2,3,0,1]
 constexpr int DPP_ROW_HALF_MIRROR = 0x141;
-constexpr int DPP_ROW_MIRROR = 0x140;
 
-__device__ __forceinline__ uint32_t row16_max(uint32_t v) {
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+// maximum over each group of 8 lanes (a block)
+__device__ __forceinline__ uint32_t lanes8_max(uint32_t v) {
   v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, DPP_QUAD_XOR1, 0xF, 0xF, false));
   v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, DPP_QUAD_XOR2, 0xF, 0xF, false));
   v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, DPP_ROW_HALF_MIRROR, 0xF, 0xF, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, DPP_ROW_MIRROR, 0xF, 0xF, false));
   return v;
 }
 
@@ -66,54 +72,48 @@ __device__ __forceinline__ uint32_t cvt4(uint32_t d0, uint32_t d1, float mul) {
   return (uint32_t)r;
 }
 
+// Word index i (row-major over [M, nw]) of the whole tensor goes to half-wave
+// i % 2 of wave i / 2.
 __global__ __launch_bounds__(QWAVES * 64)
 void fp8_quant_1x128_kernel(const uint16_t* __restrict__ x, int64_t ldx,
                             uint8_t* __restrict__ q, int64_t ldq,
                             int32_t* __restrict__ scales, int64_t sm, int64_t sw,
-                            int32_t nw, int32_t nkb, int64_t units) {
+                            int32_t nw, int32_t nkb, int64_t words) {
   const int lane = threadIdx.x & 63;
-  const int blk = lane >> 4;  // block of this lane within the word
+  const int l32 = lane & 31;
+  const int blk = l32 >> 3;  // block of this lane within its word
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t u0 = ((int64_t)blockIdx.x * QWAVES + wave) * QUNROLL;
+  const int64_t word = 2 * ((int64_t)blockIdx.x * QWAVES + wave) + (lane >> 5);
+  if (2 * ((int64_t)blockIdx.x * QWAVES + wave) >= words) return;   // uniform across the wave
+  const int64_t row = word / nw;
+  const int w = (int)(word - row * nw);
+  const bool valid = word < words && 4 * w + blk < nkb;
 
-  uint4 d[QUNROLL];
-#pragma unroll
-  for (int i = 0; i < QUNROLL; ++i) {
-    const int64_t u = u0 + i;
-    d[i] = make_uint4(0u, 0u, 0u, 0u);
-    if (u < units) {
-      const int64_t row = u / nw;
-      const int w = (int)(u - row * nw);
-      if (4 * w + blk < nkb)
-        d[i] = *reinterpret_cast<const uint4*>(x + row * ldx + (int64_t)w * 512 + lane * 8);
-    }
+  v4u a = v4u{0u, 0u, 0u, 0u}, b = v4u{0u, 0u, 0u, 0u};
+  if (valid) {
+    const v4u* src = reinterpret_cast<const v4u*>(x + row * ldx + (int64_t)w * 512 + l32 * 16);
+    a = __builtin_nontemporal_load(src);
+    b = __builtin_nontemporal_load(src + 1);
   }
+  uint32_t m = max(max(max(mag2(a[0]), mag2(a[1])), max(mag2(a[2]), mag2(a[3]))),
+                   max(max(mag2(b[0]), mag2(b[1])), max(mag2(b[2]), mag2(b[3]))));
+  m = lanes8_max(m);
+  const int e = block_exponent(m);
+  const float mul = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, a normal float
+  const v4u o = v4u{cvt4(a[0], a[1], mul), cvt4(a[2], a[3], mul), cvt4(b[0], b[1], mul), cvt4(b[2], b[3], mul)};
+  if (valid) __builtin_nontemporal_store(o, reinterpret_cast<v4u*>(q + row * ldq + (int64_t)w * 512 + l32 * 16));
 
-#pragma unroll
-  for (int i = 0; i < QUNROLL; ++i) {
-    const int64_t u = u0 + i;
-    if (u >= units) break;  // uniform across the wave
-    const int64_t row = u / nw;
-    const int w = (int)(u - row * nw);
-    const bool valid = 4 * w + blk < nkb;
-
-    uint32_t m = max(max(mag2(d[i].x), mag2(d[i].y)), max(mag2(d[i].z), mag2(d[i].w)));
-    m = row16_max(m);
-    const int e = block_exponent(m);
-    const float mul = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, a normal float
-
-    const uint32_t lo = cvt4(d[i].x, d[i].y, mul);
-    const uint32_t hi = cvt4(d[i].z, d[i].w, mul);
-    if (valid)
-      *reinterpret_cast<uint2*>(q + row * ldq + (int64_t)w * 512 + lane * 8) = make_uint2(lo, hi);
-
-    const uint32_t byte = valid ? (uint32_t)(e + 127) : 0u;
-    const uint32_t word = (uint32_t)__builtin_amdgcn_readlane((int)byte, 0) |
-                          ((uint32_t)__builtin_amdgcn_readlane((int)byte, 16) << 8) |
-                          ((uint32_t)__builtin_amdgcn_readlane((int)byte, 32) << 16) |
-                          ((uint32_t)__builtin_amdgcn_readlane((int)byte, 48) << 24);
-    if (lane == 0) scales[row * sm + (int64_t)w * sw] = (int32_t)word;
-  }
+  // the four block bytes of each half-wave's word
+  const uint32_t byte = valid ? (uint32_t)(e + 127) : 0u;
+  const uint32_t w0 = (uint32_t)__builtin_amdgcn_readlane((int)byte, 0) |
+                      ((uint32_t)__builtin_amdgcn_readlane((int)byte, 8) << 8) |
+                      ((uint32_t)__builtin_amdgcn_readlane((int)byte, 16) << 16) |
+                      ((uint32_t)__builtin_amdgcn_readlane((int)byte, 24) << 24);
+  const uint32_t w1 = (uint32_t)__builtin_amdgcn_readlane((int)byte, 32) |
+                      ((uint32_t)__builtin_amdgcn_readlane((int)byte, 40) << 8) |
+                      ((uint32_t)__builtin_amdgcn_readlane((int)byte, 48) << 16) |
+                      ((uint32_t)__builtin_amdgcn_readlane((int)byte, 56) << 24);
+  if (l32 == 0 && word < words) scales[row * sm + (int64_t)w * sw] = (int32_t)(lane ? w1 : w0);
 }
 
 }  // namespace
@@ -123,12 +123,12 @@ hipError_t launch_fp8_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx
                             int64_t s_stride_m, int64_t s_stride_w, hipStream_t stream) {
   const int32_t nkb = (int32_t)(K / 128);
   const int32_t nw = (nkb + 3) / 4;
-  const int64_t units = M * nw;
-  const int64_t per_block = (int64_t)QWAVES * QUNROLL;
-  const int64_t blocks = (units + per_block - 1) / per_block;
+  const int64_t words = M * nw;
+  const int64_t per_block = (int64_t)QWAVES * 2;
+  const int64_t blocks = (words + per_block - 1) / per_block;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL(fp8_quant_1x128_kernel, dim3((unsigned)blocks), dim3(QWAVES * 64), 0, stream,
-                     x, ldx, q, ldq, scales, s_stride_m, s_stride_w, nw, nkb, units);
+                     x, ldx, q, ldq, scales, s_stride_m, s_stride_w, nw, nkb, words);
   return hipGetLastError();
 }
 
