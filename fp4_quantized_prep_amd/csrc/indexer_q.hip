@@ -484,6 +484,7 @@ hipError_t launch_kernel(const IndexerQArgs& a_in, int stage, hipStream_t stream
 }  // namespace
 
 hipError_t launch_indexer_q(const IndexerQArgs& a_in, int stage, hipStream_t stream) {
+  if (stage == -1 && indexer_q_small_supported(a_in)) return launch_indexer_q_small(a_in, stream);
   if (stage == -1 && indexer_q_pipe_supported(a_in)) {
     // one workgroup per CU: each head pair gets CUs / pairs chunks of whole 128-token tiles
     IndexerQArgs a = a_in;

@@ -109,6 +109,21 @@ def test_fused_chain_small_and_ragged(gpu_lib, weights, table, M):
     assert rep["ok"], rep
 
 
+@pytest.mark.parametrize("M", [31, 32, 33, 64, 65, 96, 97])
+def test_fused_chain_small_batch_boundaries(gpu_lib, weights, table, M):
+    """Token counts at the edges of the small-batch kernel's 32-token column
+    tiles (1 or 2 tiles up to 64 tokens) and past it (65 and more: the
+    128-token tile kernel); every token checked."""
+    codes, sb, wd, wsd = weights
+    inp = S.indexer_q_inputs("indexer_q_m128", M=M)
+    x, pos = inp["x"], inp["positions"]
+    _, _, q, s = device_chain(gpu_lib, x, wd, wsd, pos, table[4096])
+    ref = oracle_chain_from_x(x, codes, sb, pos, 64)
+    rep = C.check_fp4(q, s, ref["z"], ref["q_fp4"], ref["q_scales"])
+    print(f"M={M}", rep)
+    assert rep["ok"], rep
+
+
 def test_fused_chain_mn_major_scales(gpu_lib, weights, table):
     codes, sb, wd, wsd = weights
     inp = S.indexer_q_inputs("indexer_q_m128", M=77)
@@ -210,9 +225,10 @@ def test_every_output_byte_written_and_no_overrun(gpu_lib, weights, table):
     assert torch.equal(results[0][0], results[1][0]) and torch.equal(results[0][1], results[1][1])
 
 
-def test_graph_capture_replays_match_eager(gpu_lib, weights, table):
+@pytest.mark.parametrize("M", [8, 128])
+def test_graph_capture_replays_match_eager(gpu_lib, weights, table, M):
     codes, sb, wd, wsd = weights
-    inp = S.indexer_q_inputs("indexer_q_m128")
+    inp = S.indexer_q_inputs("indexer_q_m128", M=M)
     x, pos = inp["x"].cuda(), inp["positions"].cuda()
     cs = table[4096]
     q_e, s_e = gpu_lib.indexer_q_prep(x, wd, wsd, pos, cs)
