@@ -8,26 +8,32 @@
 // path); TensorRT-LLM PR "Fuse DeepSeek-V4 Indexer Q projection with CuTe
 // DSL", kernel routing (a separate small-M route with swapped operands).
 //
-// With at most 64 tokens the projection is a read of the 12.6 MB weight
-// matrix: the MFMA work is a few percent of the large-batch kernel's, so the
-// layout is chosen for streaming the weights through as many CUs as there
-// are heads and for latency, not for operand reuse:
-//   * one workgroup per head (4 waves); wave w owns the head's weight rows
-//     32 w .. 32 w + 31 (48 KiB) and streams them through a ring of LDS
-//     stages of its own (7 or 4 K blocks deep), with coalesced buffer-to-LDS
-//     copies of 8 rows x 128 bytes; no other wave reads them, so the ring
-//     needs no barrier, only the wave's own wait counts. (Loading the
-//     fragments straight into registers touches 32 rows per instruction and
-//     ran at a third of the rate.)
-//   * the activation rows of the batch (at most 64 x 1536 bytes) are copied
-//     once into LDS by the same path, 16-byte chunks permuted per row so
-//     that the operand reads of 32 rows hit distinct banks;
-//   * 32-token column tiles (NT = 1, 2) on the 32x32x64 scaled FP8 MFMA,
-//     weight rows as the first operand, as in the other kernels, so the
-//     accumulators have their layout;
-//   * the four waves' 32-row slices of each column tile meet in LDS, and
-//     wave tm runs the shared epilogue (RoPE, Hadamard, FP4, stores) of
-//     column tile tm.
+// Up to 256 tokens the projection is mostly a read of the 12.6 MB weight
+// matrix and the MFMA work is a few percent of the large-batch kernel's, so
+// the layout is chosen for streaming the weights through many CUs and for
+// latency rather than for operand reuse:
+//   * one workgroup per head and 32-token column tile, 4 waves. The tiles of
+//     a head are H workgroups apart, so with 64 heads they land on one XCD
+//     and share its L2 for the head's weights.
+//   * wave w owns the head's weight rows 32 w .. 32 w + 31 (48 KiB) and
+//     streams them through a ring of 7 LDS stages of its own, with coalesced
+//     buffer-to-LDS copies of 8 rows x 128 bytes. No other wave reads them,
+//     so the ring needs no barrier, only the wave's own wait counts. (Loading
+//     the fragments straight into registers touches 32 rows per instruction
+//     and ran at a third of the rate.)
+//   * the tile's activation rows (32 x 1536 bytes) are copied once into LDS
+//     by the same path, 16-byte chunks permuted per row so that the operand
+//     reads of 32 rows hit distinct banks.
+//   * the 32x32x64 scaled FP8 MFMA, weight rows as the first operand as in
+//     the other kernels, so the accumulators have their layout.
+//   * the four waves' 32-row slices meet in LDS as token rows of 128 floats,
+//     and the epilogue (RoPE, Hadamard-128, FP4, stores) is split over all
+//     four waves, 8 tokens each: lane l takes token 8 w + l % 8 and 16 of its
+//     dims, d = 64 b6 + 32 b5 + 16 b4 + 8 b3 + k with (b3, b4, b6) the lane
+//     bits 3..5 and (b5, k) in the lane. The RoPE pairs (d, d + 32) and the
+//     FP4 blocks' 8-dim runs are then in the lane, and the Hadamard stages
+//     over dim bits 3, 4, 6 are exchanges with lane l ^ 8 (DPP), l ^ 16 and
+//     l ^ 32 (permlane swaps).
 // Tokens past M: their LDS rows are never written (no copy reaches them) and
 // their results are never stored; an MFMA column depends on its own token's
 // row only, so whatever those rows hold stays in columns that are dropped.
@@ -42,23 +48,20 @@ namespace small {
 constexpr int NWAVES = 4;
 constexpr int NTHREADS = NWAVES * 64;
 constexpr int NKB = 12;                     // K blocks (K = 1536)
+constexpr int TILE = 32;                    // tokens per workgroup
+constexpr int MAX_TILES = 8;                // column tiles per head: up to 256 tokens
 constexpr int KROW = NKB * KB;              // bytes of one activation row in LDS
-constexpr int MAX_NT = 2;                   // 32-token column tiles
 constexpr int SLAB = 1024;                  // one wave-wide LDS copy
 constexpr int LDS_BYTES = 160 * 1024;
-constexpr int XTILE = 4 * 4 * SLAB;         // one column tile's accumulators (4 slices x 16 floats x 64 lanes)
+constexpr int XROW = 4 * (HEAD_DIM + 4);    // one token's 128 floats in LDS, padded against bank conflicts
 constexpr int WSTAGE = 32 * KB;             // one K block of a wave's 32 weight rows: 4 KiB
-
 // Activation rows first, then the four weight rings. A weight copy's LDS
 // address is given as its destination minus its column offset in the row
 // (at most 11 K blocks), which must not go below zero.
-template <int NT>
-struct Layout {
-  static constexpr int W_OFF = 32 * NT * KROW;
-  static constexpr int NST = (LDS_BYTES - W_OFF) / (NWAVES * WSTAGE);   // 7 or 4
-  static_assert(NT * XTILE <= W_OFF, "the accumulator exchange reuses the activation rows' LDS");
-  static_assert(W_OFF >= KB * (NKB - 1), "copy LDS bases must stay non-negative");
-};
+constexpr int W_OFF = TILE * KROW;                                  // 48 KiB
+constexpr int NST = (LDS_BYTES - W_OFF) / (NWAVES * WSTAGE);        // 7 stages per wave
+static_assert(TILE * XROW <= W_OFF, "the accumulator exchange reuses the activation rows' LDS");
+static_assert(W_OFF >= KB * (NKB - 1), "copy LDS bases must stay non-negative");
 
 __device__ __forceinline__ constexpr int waitcnt_vm(int n) {
   return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14);
@@ -75,25 +78,28 @@ __device__ __forceinline__ void static_for(F&& f) {
 // LDS byte of 16-byte chunk c (0..95) of activation row r
 __device__ __forceinline__ uint32_t a_slot(int r, int c) { return (uint32_t)(r * KROW + 16 * (c ^ (r & 15))); }
 
-template <int NT>
 __global__ __launch_bounds__(NTHREADS, 1)
-void indexer_q_small_kernel(IndexerQArgs p) {
+void indexer_q_small_kernel(IndexerQArgs pa) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
   const int head = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63, half = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int M = (int)p.M;   // at most 32 NT
-
-  // RoPE rows of the column tile this wave finishes (first: their latency
-  // then hides under everything else)
-  RopeCS rope;
-  if (wave < NT) rope = load_rope(load_position(32 * wave + (lane & 31), p), half, p);
+  // the column tile's tokens: the batch seen from token t0 on
+  const int64_t t0 = TILE * (int64_t)blockIdx.y;
+  IndexerQArgs p = pa;
+  p.a += t0 * p.lda;
+  p.a_scale_bytes += 4 * t0 * p.as_sm;
+  p.positions += t0;
+  p.q_fp4 += t0 * p.H * (HEAD_DIM / 2);
+  p.q_scales += t0 * p.H * 4;
+  p.M = pa.M - t0 < TILE ? pa.M - t0 : TILE;
+  const int M = (int)p.M;   // 1 .. 32
 
   // 1. the activation rows into LDS: slab k covers LDS bytes [1 KiB k, 1 KiB
   //    (k + 1)); its lane i fills byte 1 KiB k + 16 i, which is slot
   //    (1 KiB k + 16 i) % 1536 / 16 of row (1 KiB k + 16 i) / 1536 and holds
-  //    that row's chunk slot ^ (row % 16). Slabs past the batch's rows are
+  //    that row's chunk slot ^ (row % 16). Slabs past the tile's rows are
   //    skipped; rows past M inside the last one read zeros (bounds check).
   {
     const rsrc_t ra = make_rsrc(p.a, (uint64_t)M * p.lda);
@@ -107,28 +113,34 @@ void indexer_q_small_kernel(IndexerQArgs p) {
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // 2. the lane's token scale words (token 32 tm + lane % 32, clamped into the batch)
-  uint32_t asw[NT][3];
-#pragma unroll
-  for (int tm = 0; tm < NT; ++tm) {
-    int t = 32 * tm + (lane & 31);
-    t = t < M ? t : M - 1;
+  // 2. the lane's token scale words (token lane % 32, clamped into the tile)
+  uint32_t asw[3];
+  {
+    const int t = (lane & 31) < M ? (lane & 31) : M - 1;
     const uint32_t* w = reinterpret_cast<const uint32_t*>(p.a_scale_bytes) + (int64_t)t * p.as_sm;
 #pragma unroll
-    for (int k = 0; k < 3; ++k) asw[tm][k] = w[k * p.as_sw];
+    for (int k = 0; k < 3; ++k) asw[k] = w[k * p.as_sw];
   }
   // the head's weight scales, one byte per K block
   const uint32_t* wsp = reinterpret_cast<const uint32_t*>(p.w_scales + (int64_t)head * NKB);
   uint32_t wsw[3];
 #pragma unroll
   for (int k = 0; k < 3; ++k) wsw[k] = __builtin_amdgcn_readfirstlane(wsp[k]);
+  // Epilogue lanes: token 8 wave + l % 8 and the dims
+  // 64 b6 + 32 b5 + 8 (b3 + 2 b4) + k, (b3, b4, b6) = lane bits 3, 4, 5.
+  // The token's position now; its RoPE table row (the pairs
+  // i = 8 (b3 + 2 b4) + k) once the K loop runs, so that no load waits for
+  // another before the weight stream starts.
+  const int sub = lane >> 3;
+  const int eoff = 8 * (sub & 3) + 64 * (sub >> 2);   // the lane's dims: eoff + 32 b5 + k
+  const int et = 8 * wave + (lane & 7);                // the lane's epilogue token
+  const int64_t posv = load_position(et, p);
   __builtin_amdgcn_sched_barrier(0);
 
   // 3. the wave's weight ring. Copy c (0..3) of K block j moves rows
   //    8 c + l / 8 (of the wave's 32) into stage j % NST, LDS row 8 c + l / 8
   //    slot l % 8, which holds the row's 16-byte chunk (l % 8) ^ (row / 2 % 8);
   //    the column 128 j is the instruction offset (added to the LDS address too).
-  constexpr int NST = Layout<NT>::NST;
   const rsrc_t rw = make_rsrc(p.w + (int64_t)head * HEAD_DIM * p.ldw, (uint64_t)HEAD_DIM * p.ldw);
   uint32_t wv[4];
 #pragma unroll
@@ -136,7 +148,7 @@ void indexer_q_small_kernel(IndexerQArgs p) {
     const int r = 8 * c + (lane >> 3);
     wv[c] = (uint32_t)((32 * wave + r) * (int)p.ldw + 16 * ((lane & 7) ^ ((r >> 1) & 7)));
   }
-  uint8_t* const ring = lds + Layout<NT>::W_OFF + NST * WSTAGE * wave;
+  uint8_t* const ring = lds + W_OFF + NST * WSTAGE * wave;
   auto copies = [&](auto jc) __attribute__((always_inline)) {
     constexpr int j = decltype(jc)::value;
 #pragma unroll
@@ -146,8 +158,8 @@ void indexer_q_small_kernel(IndexerQArgs p) {
   };
   static_for<0, NST>([&](auto jc) __attribute__((always_inline)) { copies(jc); });
   __builtin_amdgcn_sched_barrier(0);
-  // the activation copies were issued before the ring's first copies: once
-  // only those may be outstanding, they have landed
+  // the activation copies, scale words and position were issued before the
+  // ring's first copies: once only those may be outstanding, they have landed
   {
     constexpr int WAIT = waitcnt_vm(4 * NST);
     __builtin_amdgcn_s_waitcnt(WAIT);
@@ -155,74 +167,157 @@ void indexer_q_small_kernel(IndexerQArgs p) {
   block_barrier();
 
   // 4. the K loop: block j's weights are in stage j % NST once only the
-  //    copies of the blocks after it may be outstanding; the stage is refilled
-  //    with block j + NST once its fragments are read
-  v16f acc[NT];
+  //    copies of the blocks after it may be outstanding (and the 4 RoPE row
+  //    loads issued after block NST's copies); the stage is refilled with
+  //    block j + NST once its fragments are read
+  v4f rc[2], rs[2];
+  v16f acc;
 #pragma unroll
-  for (int tm = 0; tm < NT; ++tm)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[tm][r] = 0.f;
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
   const int arow = lane & 31;
   const int wswz = (arow >> 1) & 7;
   static_for<0, NKB>([&](auto jc) __attribute__((always_inline)) {
     constexpr int j = decltype(jc)::value;
     constexpr int last = j + NST - 1 < NKB - 1 ? j + NST - 1 : NKB - 1;
-    constexpr int WAIT = waitcnt_vm(4 * (last - j));
+    constexpr int WAIT = waitcnt_vm(4 * (last - j) + (j >= 1 && j <= NST ? 4 : 0));
     __builtin_amdgcn_s_waitcnt(WAIT);
     const uint8_t* st = ring + (j % NST) * WSTAGE + KB * arow;
-    v8i wfr[2];
+    v8i wfr[2], afr[2];
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
-      const v4u w0 = *reinterpret_cast<const v4u*>(st + 16 * ((4 * kh + 2 * half) ^ wswz));
-      const v4u w1 = *reinterpret_cast<const v4u*>(st + 16 * ((4 * kh + 2 * half + 1) ^ wswz));
-      wfr[kh] = make_v8i(w0, w1);
+      const int c0 = 4 * kh + 2 * half;
+      wfr[kh] = make_v8i(*reinterpret_cast<const v4u*>(st + 16 * (c0 ^ wswz)),
+                         *reinterpret_cast<const v4u*>(st + 16 * ((c0 + 1) ^ wswz)));
+      afr[kh] = make_v8i(*reinterpret_cast<const v4u*>(lds + a_slot(arow, 8 * j + c0)),
+                         *reinterpret_cast<const v4u*>(lds + a_slot(arow, 8 * j + c0 + 1)));
     }
-    v8i afr[2][NT];
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-      for (int tm = 0; tm < NT; ++tm) {
-        const int r = 32 * tm + arow, c0 = 8 * j + 4 * kh + 2 * half;
-        afr[kh][tm] = make_v8i(*reinterpret_cast<const v4u*>(lds + a_slot(r, c0)),
-                               *reinterpret_cast<const v4u*>(lds + a_slot(r, c0 + 1)));
-      }
     if constexpr (j + NST < NKB) {
       __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);   // the stage's fragments are in registers
       copies(std::integral_constant<int, j + NST>{});
     }
+    if constexpr (j == 0) {
+      int64_t pos = posv;
+      pos = pos < 0 ? 0 : (pos >= p.max_pos ? p.max_pos - 1 : pos);
+      const float* row = p.cos_sin + pos * 64 + 8 * (sub & 3);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        rc[h] = *reinterpret_cast<const v4f*>(row + 4 * h);
+        rs[h] = *reinterpret_cast<const v4f*>(row + 32 + 4 * h);
+      }
+    }
     const int ws = (int)(wsw[j >> 2] >> (8 * (j & 3)));
+    const int as = (int)(asw[j >> 2] >> (8 * (j & 3)));
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-      for (int tm = 0; tm < NT; ++tm) {
-        const int as = (int)(asw[tm][j >> 2] >> (8 * (j & 3)));
-        acc[tm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wfr[kh], afr[kh][tm], acc[tm], 0, 0, 0, ws, 0, as);
-      }
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wfr[kh], afr[kh], acc, 0, 0, 0, ws, 0, as);
     __builtin_amdgcn_sched_barrier(0);
   });
 
-  // 5. the column tiles' four 32-row slices meet in LDS (over the activation
-  //    rows, once every wave is done reading them): slice tn of tile tm, group
-  //    g of 4 accumulators at ((tm * 4 + tn) * 4 + g) KiB + 16 lane
+  // 5. the four 32-row slices meet in LDS (over the activation rows, once
+  //    every wave is done reading them) as token rows: accumulator group g
+  //    of slice w holds dims 32 w + 8 g + 4 half + 0..3 of token lane % 32
   block_barrier();
 #pragma unroll
-  for (int tm = 0; tm < NT; ++tm)
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-      *reinterpret_cast<v4f*>(lds + XTILE * tm + SLAB * (4 * wave + g) + 16 * lane) =
-          v4f{acc[tm][4 * g], acc[tm][4 * g + 1], acc[tm][4 * g + 2], acc[tm][4 * g + 3]};
+  for (int g = 0; g < 4; ++g)
+    *reinterpret_cast<v4f*>(lds + XROW * (lane & 31) + 4 * (32 * wave + 8 * g + 4 * half)) =
+        v4f{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
   block_barrier();
-  if (wave < NT) {
-    v16f full[4];
+
+  // 6. the epilogue of token et
+  float v[2][8];   // v[b5][k]: dim eoff + 32 b5 + k
+  {
+    const uint8_t* xr = lds + XROW * et + 4 * eoff;
 #pragma unroll
-    for (int tn = 0; tn < 4; ++tn)
+    for (int b5 = 0; b5 < 2; ++b5)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const v4f x = *reinterpret_cast<const v4f*>(lds + XTILE * wave + SLAB * (4 * tn + g) + 16 * lane);
+      for (int h = 0; h < 2; ++h) {
+        const v4f x = *reinterpret_cast<const v4f*>(xr + 128 * b5 + 16 * h);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) full[tn][4 * g + q] = x[q];
+        for (int q = 0; q < 4; ++q) v[b5][4 * h + q] = x[q];
       }
-    epilogue_tile<-1>(full, 32 * wave + (lane & 31), head, true, half, p, rope);
+  }
+  // RoPE on dims 0..63 (b6 = 0): the pair (i, i + 32) is (v[0][k], v[1][k])
+  if (!(sub & 4)) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float x = v[0][k], y = v[1][k];
+      const float c = rc[k >> 2][k & 3], sn = rs[k >> 2][k & 3];
+      v[0][k] = x * c - y * sn;
+      v[1][k] = y * c + x * sn;
+    }
+  }
+  // Hadamard: dim bits 0, 1, 2 (k) and 5 (b5) in the lane ...
+#pragma unroll
+  for (int kb = 1; kb < 8; kb <<= 1)
+#pragma unroll
+    for (int b5 = 0; b5 < 2; ++b5)
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (!(k & kb)) {
+          const float a = v[b5][k], b = v[b5][k | kb];
+          v[b5][k] = a + b;
+          v[b5][k | kb] = a - b;
+        }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float a = v[0][k], b = v[1][k];
+    v[0][k] = a + b;
+    v[1][k] = a - b;
+  }
+  // ... and dim bits 3, 4, 6 across lanes l ^ 8, l ^ 16, l ^ 32: with a and
+  // b the values of the lanes with the bit clear and set, the first becomes
+  // a + b and the second a - b, i.e. partner + sign * own with sign -1 where
+  // the bit is set (one stage over all 16 values at a time, so that
+  // independent exchanges are in flight)
+  const float sg3 = (sub & 1) ? -1.f : 1.f, sg4 = (sub & 2) ? -1.f : 1.f, sg6 = (sub & 4) ? -1.f : 1.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float& x = v[i >> 3][i & 7];
+    x = fmaf(sg3, x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false)));
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float& x = v[i >> 3][i & 7];
+    const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaf(sg4, __uint_as_float(s16[1]), __uint_as_float(s16[0]));
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float& x = v[i >> 3][i & 7];
+    const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaf(sg6, __uint_as_float(s32[1]), __uint_as_float(s32[0])) * INV_SQRT_128;
+  }
+  // FP4 blocks q = 2 b6 + b5: 8 of the block's 32 values here, the rest in
+  // lanes l ^ 8, l ^ 16
+  uint32_t code[2], sb = 0;
+#pragma unroll
+  for (int b5 = 0; b5 < 2; ++b5) {
+    float m = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[b5][k]));
+    m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x128, 0xF, 0xF, false)));
+    const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    m = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+    const int e = fp4_exponent(m);
+    sb |= (uint32_t)(e + 127) << (8 * b5);
+    const float scale = __uint_as_float((uint32_t)(e + 127) << 23);   // codes are RNE(z / 2^e)
+    const float* x = v[b5];
+    uint32_t d = 0;
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, x[0], x[1], scale, 0);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, x[2], x[3], scale, 1);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, x[4], x[5], scale, 2);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, x[6], x[7], scale, 3);
+    code[b5] = d;
+  }
+  // the scale bytes of blocks 2, 3 come from lane l ^ 32
+  const auto ss = __builtin_amdgcn_permlane32_swap(sb, sb, false, false);
+  const uint32_t sbytes = ss[0] | (ss[1] << 16);
+  if (et < M) {
+    // codes of dims 32 q + 8 (b3 + 2 b4) + k: bytes 16 q + 4 (b3 + 2 b4) + k / 2
+    uint8_t* dst = p.q_fp4 + ((int64_t)et * p.H + head) * (HEAD_DIM / 2) + eoff / 2;
+    *reinterpret_cast<uint32_t*>(dst) = code[0];
+    *reinterpret_cast<uint32_t*>(dst + 16) = code[1];
+    if (sub == 0) *reinterpret_cast<uint32_t*>(p.q_scales + ((int64_t)et * p.H + head) * 4) = sbytes;
   }
 }
 
@@ -232,16 +327,13 @@ void indexer_q_small_kernel(IndexerQArgs p) {
 // activation and weight row offsets are formed in 32 bits; the weight scales
 // are read four at a time
 bool indexer_q_small_supported(const IndexerQArgs& a) {
-  return a.nkb == small::NKB && a.M >= 1 && a.M <= 32 * small::MAX_NT && a.lda <= (1 << 24) &&
+  return a.nkb == small::NKB && a.M >= 1 && a.M <= small::TILE * small::MAX_TILES && a.lda <= (1 << 24) &&
          a.ldw <= (1 << 22) && (reinterpret_cast<uintptr_t>(a.w_scales) & 3) == 0;
 }
 
 hipError_t launch_indexer_q_small(const IndexerQArgs& a, hipStream_t stream) {
-  const dim3 grid((unsigned)a.H), block(small::NTHREADS);
-  if (a.M <= 32)
-    hipLaunchKernelGGL(small::indexer_q_small_kernel<1>, grid, block, 0, stream, a);
-  else
-    hipLaunchKernelGGL(small::indexer_q_small_kernel<2>, grid, block, 0, stream, a);
+  const dim3 grid((unsigned)a.H, (unsigned)((a.M + small::TILE - 1) / small::TILE)), block(small::NTHREADS);
+  hipLaunchKernelGGL(small::indexer_q_small_kernel, grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

@@ -39,7 +39,7 @@ hipError_t launch_indexer_q(const IndexerQArgs& args, int stage, hipStream_t str
 bool indexer_q_pipe_supported(const IndexerQArgs& args);
 hipError_t launch_indexer_q_pipe(const IndexerQArgs& args, hipStream_t stream);
 
-// the small-batch FP4-output kernel (indexer_q_small.hip): K = 1536, 1 to 64
+// the small-batch FP4-output kernel (indexer_q_small.hip): K = 1536, 1 to 256
 // tokens, weight scales 4-byte aligned
 bool indexer_q_small_supported(const IndexerQArgs& args);
 hipError_t launch_indexer_q_small(const IndexerQArgs& args, hipStream_t stream);

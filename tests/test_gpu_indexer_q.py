@@ -109,10 +109,10 @@ def test_fused_chain_small_and_ragged(gpu_lib, weights, table, M):
     assert rep["ok"], rep
 
 
-@pytest.mark.parametrize("M", [31, 32, 33, 64, 65, 96, 97])
+@pytest.mark.parametrize("M", [31, 32, 33, 64, 65, 129, 255, 256, 257])
 def test_fused_chain_small_batch_boundaries(gpu_lib, weights, table, M):
     """Token counts at the edges of the small-batch kernel's 32-token column
-    tiles (1 or 2 tiles up to 64 tokens) and past it (65 and more: the
+    tiles (1 to 8 tiles up to 256 tokens) and just past it (257: the
     128-token tile kernel); every token checked."""
     codes, sb, wd, wsd = weights
     inp = S.indexer_q_inputs("indexer_q_m128", M=M)
