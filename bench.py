@@ -12,6 +12,12 @@ enough buffer sets to defeat the 256 MiB Infinity Cache), and the CPU oracle
 timed on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+
+`--workload decode` instead measures the decode-shaped mix: 256 independent
+calls with M drawn from {1, 2, 4, 8, 16, 32, 64} (each: quantize X [M, 1536],
+the fused kernel, and a standalone quantization of X' [M, 7168]), replayed
+from one captured HIP graph (sustained calls/s), with per-M latencies from
+graphs of repeated single calls.
 """
 import argparse
 import json
@@ -37,6 +43,7 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0: calibrate to ~15 s)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain device copy of 256 MiB (for HBM byte-counter scaling)")
+    ap.add_argument("--workload", choices=("prefill", "decode"), default="prefill")
     return ap.parse_args()
 
 
@@ -88,6 +95,10 @@ def main():
         print(f"bench.py measures one GPU only (this path has no cross-GPU step); got --gpus {args.gpus}",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == "decode":
+        decode_bench(args)
+        return
 
     import numpy as np
     import torch
@@ -226,6 +237,133 @@ def main():
             "in_chain_avg_launch_us": t_quant * 1e6,
         },
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def decode_bench(args):
+    """The decode-shaped mix (see the module docstring); prints one JSON line."""
+    import numpy as np
+    import torch
+
+    import fp4_quantized_prep_amd as iqp
+    import synthetic as S
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w_cpu, wsb_cpu = S.weights()
+    w, wsb = w_cpu.to(dev), wsb_cpu.to(dev)
+    max_pos = 131072
+    cs = iqp.rope_cos_sin_table(S.ROPE_THETA, max_pos, 64, device=dev)
+    calls = []
+    for c in S.decode_calls(256):
+        m = c["x"].shape[0]
+        calls.append({
+            "M": m, "x": c["x"].to(dev), "xw": c["x_wide"].to(dev), "pos": c["positions"].to(dev),
+            "a": torch.empty((m, K_PROJ), dtype=torch.uint8, device=dev),
+            "as": torch.empty((m, 3), dtype=torch.int32, device=dev),
+            "aw": torch.empty((m, QUANT_K), dtype=torch.uint8, device=dev),
+            "asw": torch.empty((m, (QUANT_K // 128 + 3) // 4), dtype=torch.int32, device=dev),
+            "q": torch.empty((m, N_HEADS, HEAD_DIM // 2), dtype=torch.uint8, device=dev),
+            "qs": torch.empty((m, N_HEADS, HEAD_DIM // 32), dtype=torch.uint8, device=dev),
+        })
+
+    def one(c):
+        iqp.fp8_quant_1x128_ue8m0(c["x"], q=c["a"], scales=c["as"])
+        iqp.indexer_q_gemm_rope_fp4(c["a"], c["as"], w, wsb, c["pos"], cs, n_heads=N_HEADS,
+                                    q_fp4=c["q"], q_scales=c["qs"])
+        iqp.fp8_quant_1x128_ue8m0(c["xw"], q=c["aw"], scales=c["asw"])
+
+    def graph_of(fn):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        return g
+
+    def replay_time(g, reps):
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps    # s per replay
+
+    for c in calls:
+        one(c)
+    torch.cuda.synchronize()
+    print(f"[bench] decode mix: {len(calls)} calls, M histogram "
+          f"{ {int(m): int(n) for m, n in zip(*np.unique([c['M'] for c in calls], return_counts=True))} }",
+          file=sys.stderr, flush=True)
+
+    # sustained: the whole mix as one graph
+    g_all = graph_of(lambda: [one(c) for c in calls])
+    reps = max(5, args.steps // 20)
+    t_mix = replay_time(g_all, reps)
+    calls_per_s = len(calls) / t_mix
+
+    # per-M latency of one call (quantize + fused + wide quantize), and of the fused kernel alone
+    lat, lat_fused = {}, {}
+    n_rep = 20
+    for m in sorted({c["M"] for c in calls}):
+        c = next(c for c in calls if c["M"] == m)
+        lat[m] = replay_time(graph_of(lambda: [one(c) for _ in range(n_rep)]), 5) / n_rep * 1e6
+        lat_fused[m] = replay_time(graph_of(lambda: [iqp.indexer_q_gemm_rope_fp4(
+            c["a"], c["as"], w, wsb, c["pos"], cs, n_heads=N_HEADS, q_fp4=c["q"], q_scales=c["qs"])
+            for _ in range(n_rep)]), 5) / n_rep * 1e6
+        print(f"[bench] M={m}: call {lat[m]:.2f} us, fused kernel {lat_fused[m]:.2f} us",
+              file=sys.stderr, flush=True)
+    per_call = np.array([lat[c["M"]] for c in calls])
+    # the fused kernel reads all of W (and its scales) once per call, which
+    # dominates its algorithmic bytes at these sizes: its bound is HBM
+    mix_bytes = float(sum(fused_bytes(c["M"]) for c in calls))
+    mix_fused_s = float(sum(lat_fused[c["M"]] for c in calls)) * 1e-6
+    mean_fused = mix_fused_s / len(calls) * 1e6
+    achieved = mix_bytes / mix_fused_s / 1e9
+    result = {
+        "metric": "decode-shaped indexer-Q calls/s (graph replay)",
+        "value": calls_per_s,
+        "unit": "calls/s",
+        "n_gpus": 1,
+        "steps": reps,
+        "warmup": 1,
+        "ms_per_step": t_mix * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-e4m3 (fp32 accumulate), bf16 in, fp4-e2m1 out",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode mix: 256 independent calls, M uniform over {1,2,4,8,16,32,64}; each call "
+                        "X bf16 [M,1536] -> FP8 quant -> fused GEMM + RoPE + Hadamard + FP4 (64 heads), "
+                        "plus a standalone FP8 quant of X' [M,7168]; positions U[0,131072)",
+            "calls": len(calls), "K": K_PROJ, "heads": N_HEADS, "head_dim": HEAD_DIM, "max_pos": max_pos,
+            "parallelism": "single GPU",
+        },
+        "latency_us": {"p50": float(np.percentile(per_call, 50)), "p99": float(np.percentile(per_call, 99)),
+                       "per_M_call": {str(k): v for k, v in lat.items()},
+                       "per_M_fused_kernel": {str(k): v for k, v in lat_fused.items()}},
+        "roofline": {
+            "kernel": "indexer_q_small_kernel (fused GEMM + RoPE + Hadamard + FP4, M <= 256)",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS,
+            "traffic": None,
+            "algorithmic_bytes_per_launch": mix_bytes / len(calls),
+            "avg_launch_us": mean_fused,
+        },
+        "cpu_baseline": None,
     }
     print(json.dumps(result), flush=True)
 
