@@ -84,6 +84,13 @@ def measured_traffic():
     return int(fields["fused_traffic_bytes_per_launch"])
 
 
+def epilogue_bytes(M, H=N_HEADS):
+    """Algorithmic HBM bytes of one standalone-epilogue launch: per (token, head)
+    256 B of bf16 Q in, 64 B of codes and 4 scale bytes out; per token its
+    position (8 B) and table row (64 float32)."""
+    return M * H * (2 * HEAD_DIM + HEAD_DIM // 2 + HEAD_DIM // 32) + M * (8 + 64 * 4)
+
+
 def quant_bytes(M, K):
     """Algorithmic HBM bytes of one quantizer launch: bf16 in, E4M3 + words out."""
     return M * K * 2 + M * K + M * 4 * ((K // 128 + 3) // 4)
@@ -168,7 +175,19 @@ def main():
     for i in range(10):
         iqp.fp8_quant_1x128_ue8m0(xs[i % n_sets], q=qq[i % n_sets], scales=ss[i % n_sets])
     torch.cuda.synchronize()
+    # Launches run back to back between two events on the kernel's stream, so the
+    # average is the kernel's own duration (an event pair around every launch adds
+    # ~2.5 us of dispatch gap per launch at this size); the per-launch-event figure
+    # is reported beside it.
     n_q = max(50, K)
+    qa, qb_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    qa.record(stream)
+    for i in range(n_q):
+        k = i % n_sets
+        iqp.fp8_quant_1x128_ue8m0(xs[k], q=qq[k], scales=ss[k])
+    qb_.record(stream)
+    torch.cuda.synchronize()
+    t_q_big = qa.elapsed_time(qb_) * 1e-3 / n_q
     qev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_q)]
     for i in range(n_q):
         k = i % n_sets
@@ -176,11 +195,38 @@ def main():
         iqp.fp8_quant_1x128_ue8m0(xs[k], q=qq[k], scales=ss[k])
         qev[i][1].record(stream)
     torch.cuda.synchronize()
-    t_q_big = float(np.mean([b.elapsed_time(e) for b, e in qev])) * 1e-3
+    t_q_ev = float(np.mean([b.elapsed_time(e) for b, e in qev])) * 1e-3
     qbytes = quant_bytes(QUANT_M, QUANT_K)
     q_gbs = qbytes / t_q_big / 1e9
-    print(f"[bench] quantizer [4632,7168]: {t_q_big * 1e6:.1f} us = {q_gbs:.0f} GB/s", file=sys.stderr, flush=True)
+    print(f"[bench] quantizer [4632,7168]: {t_q_big * 1e6:.1f} us = {q_gbs:.0f} GB/s back to back; "
+          f"{t_q_ev * 1e6:.1f} us with an event pair around each launch", file=sys.stderr, flush=True)
     del xs, qq, ss
+
+    # ---- standalone epilogue (bf16 Q -> RoPE, Hadamard, FP4) on [4632, 64*128],
+    # rotating buffer sets (> 256 MiB), launches back to back
+    qin = S.q_bf16_inputs("indexer_q_m4632")
+    e_sets = 4
+    eq = [qin["q"].to(dev) for _ in range(e_sets)]
+    eo = [torch.empty((M, N_HEADS, HEAD_DIM // 2), dtype=torch.uint8, device=dev) for _ in range(e_sets)]
+    es = [torch.empty((M, N_HEADS, HEAD_DIM // 32), dtype=torch.uint8, device=dev) for _ in range(e_sets)]
+    for i in range(8):
+        iqp.indexer_q_rope_hadamard_fp4(eq[i % e_sets], pos, cs, n_heads=N_HEADS, q_fp4=eo[i % e_sets],
+                                        q_scales=es[i % e_sets])
+    torch.cuda.synchronize()
+    n_e = max(40, K)
+    ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ea.record(stream)
+    for i in range(n_e):
+        k = i % e_sets
+        iqp.indexer_q_rope_hadamard_fp4(eq[k], pos, cs, n_heads=N_HEADS, q_fp4=eo[k], q_scales=es[k])
+    eb.record(stream)
+    torch.cuda.synchronize()
+    t_epi = ea.elapsed_time(eb) * 1e-3 / n_e
+    ebytes = epilogue_bytes(M)
+    e_gbs = ebytes / t_epi / 1e9
+    print(f"[bench] standalone epilogue [4632, 64x128] bf16: {t_epi * 1e6:.1f} us = {e_gbs:.0f} GB/s",
+          file=sys.stderr, flush=True)
+    del eq, eo, es
 
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -226,7 +272,7 @@ def main():
             "avg_launch_us": t_fused * 1e6,
         },
         "quant_roofline": {
-            "kernel": "fp8_quant_1x128_kernel on [4632,7168] (5 rotating buffer sets)",
+            "kernel": "fp8_quant_1x128_kernel on [4632,7168] (5 rotating buffer sets, launches back to back)",
             "bound": "hbm",
             "achieved": q_gbs,
             "peak": PEAK_HBM_GBS,
@@ -234,7 +280,19 @@ def main():
             "frac": q_gbs / PEAK_HBM_GBS,
             "algorithmic_bytes_per_launch": qbytes,
             "avg_launch_us": t_q_big * 1e6,
+            "avg_launch_us_event_pair_each": t_q_ev * 1e6,
             "in_chain_avg_launch_us": t_quant * 1e6,
+        },
+        "epilogue_roofline": {
+            "kernel": "indexer_q_epilogue_kernel (bf16 Q [4632, 64x128] -> RoPE, Hadamard-128, FP4; "
+                      "4 rotating buffer sets, launches back to back)",
+            "bound": "hbm",
+            "achieved": e_gbs,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": e_gbs / PEAK_HBM_GBS,
+            "algorithmic_bytes_per_launch": ebytes,
+            "avg_launch_us": t_epi * 1e6,
         },
         "cpu_baseline": cpu,
     }

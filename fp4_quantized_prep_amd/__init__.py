@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libiqprep.s
 
 __all__ = [
     "IqpError", "fp8_quant_1x128_ue8m0", "indexer_q_gemm_rope_fp4", "rope_cos_sin_table",
-    "debug_indexer_q_f32", "indexer_q_prep", "abi_version", "library_path",
+    "debug_indexer_q_f32", "indexer_q_rope_hadamard_fp4", "indexer_q_prep", "abi_version", "library_path",
     "IQP_OK", "IQP_ERR_INVALID", "IQP_ERR_UNSUPPORTED", "IQP_ERR_HIP",
 ]
 
@@ -42,6 +42,9 @@ def _load():
     lib.indexer_q_gemm_rope_fp4.restype = ctypes.c_int
     lib.iqp_debug_indexer_q_f32.argtypes = iq_args + [c_p, c_i32, c_p]
     lib.iqp_debug_indexer_q_f32.restype = ctypes.c_int
+    lib.indexer_q_rope_hadamard_fp4.argtypes = [c_p, c_i64, c_i64, c_i32, c_i32, c_i32, c_p, c_p, c_i64,
+                                                 c_p, c_p, c_p]
+    lib.indexer_q_rope_hadamard_fp4.restype = ctypes.c_int
     lib.iqp_rope_cos_sin_table.argtypes = [c_dbl, c_i64, c_i32, c_p, c_p]
     lib.iqp_rope_cos_sin_table.restype = ctypes.c_int
     lib.iqp_status_string.argtypes = [ctypes.c_int]
@@ -206,6 +209,41 @@ def debug_indexer_q_f32(a, a_scales, w, w_scales, positions, cos_sin, stage: int
     st = _lib.iqp_debug_indexer_q_f32(*args, _ptr(out), stage, _stream(a, stream))
     _check(st, "iqp_debug_indexer_q_f32")
     return out
+
+
+def indexer_q_rope_hadamard_fp4(q, positions, cos_sin, n_heads: int = 64, head_dim: int = 128,
+                                rope_dim: int = 64, q_fp4=None, q_scales=None, stream=None):
+    """Standalone epilogue over a bf16 Q [M, H*128] (rows contiguous, any row
+    stride): RoPE on each head's first 64 dims, Hadamard-128, FP4 e2m1.
+    Returns ``(q_fp4, q_scales)`` laid out as :func:`indexer_q_gemm_rope_fp4`'s."""
+    dev = q.device
+    _require(q, "q", torch.bfloat16, dev, 2)
+    _require(positions, "positions", torch.int64, dev, 1)
+    _require(cos_sin, "cos_sin", torch.float32, dev, 2)
+    if q.stride(1) != 1 or not positions.is_contiguous() or not cos_sin.is_contiguous():
+        raise ValueError("q needs contiguous rows; positions and cos_sin must be contiguous")
+    M = q.shape[0]
+    if q.shape[1] != n_heads * head_dim:
+        raise ValueError(f"q must be [M, {n_heads * head_dim}], got {tuple(q.shape)}")
+    if positions.shape[0] != M:
+        raise ValueError("positions needs one entry per token")
+    if cos_sin.shape[1] != rope_dim:
+        raise ValueError(f"cos_sin must have {rope_dim} columns")
+    if q_fp4 is None:
+        q_fp4 = torch.empty((M, n_heads, head_dim // 2), dtype=torch.uint8, device=dev)
+    if q_scales is None:
+        q_scales = torch.empty((M, n_heads, head_dim // 32), dtype=torch.uint8, device=dev)
+    _require(q_fp4, "q_fp4", torch.uint8, dev, 3)
+    _require(q_scales, "q_scales", torch.uint8, dev, 3)
+    if not (q_fp4.is_contiguous() and q_scales.is_contiguous()):
+        raise ValueError("q_fp4 and q_scales must be contiguous")
+    if tuple(q_fp4.shape) != (M, n_heads, head_dim // 2) or tuple(q_scales.shape) != (M, n_heads, head_dim // 32):
+        raise ValueError("q_fp4 / q_scales have the wrong shape")
+    st = _lib.indexer_q_rope_hadamard_fp4(_ptr(q), q.stride(0), M, n_heads, head_dim, rope_dim, _ptr(positions),
+                                          _ptr(cos_sin), cos_sin.shape[0], _ptr(q_fp4), _ptr(q_scales),
+                                          _stream(q, stream))
+    _check(st, "indexer_q_rope_hadamard_fp4")
+    return q_fp4, q_scales
 
 
 def rope_cos_sin_table(theta: float, max_pos: int, rope_dim: int = 64, device=None, out=None, stream=None):

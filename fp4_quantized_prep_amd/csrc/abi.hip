@@ -151,6 +151,26 @@ int iqp_debug_indexer_q_f32(const void* a, int64_t lda, const int32_t* a_scales,
   return from_hip(iqp::launch_indexer_q(p, stage, static_cast<hipStream_t>(stream)));
 }
 
+int indexer_q_rope_hadamard_fp4(const void* q, int64_t ldq, int64_t M, int32_t H, int32_t D,
+                                int32_t rope_dim, const int64_t* positions, const float* cos_sin,
+                                int64_t max_pos, uint8_t* q_fp4, uint8_t* q_scales, void* stream) {
+  if (M < 0 || H < 0 || D < 0 || rope_dim < 0 || max_pos < 0) return IQP_ERR_INVALID;
+  if (M == 0) return IQP_OK;
+  if (!q || !positions || !cos_sin || !q_fp4 || !q_scales) return IQP_ERR_INVALID;
+  if (H == 0 || max_pos == 0) return IQP_ERR_INVALID;
+  if (D != 128 || rope_dim != 64) return IQP_ERR_UNSUPPORTED;
+  if (ldq < (int64_t)H * D) return IQP_ERR_INVALID;
+  if (!aligned(q, 16) || ldq % 8 || !aligned(positions, 8) || !aligned(cos_sin, 16) ||
+      !aligned(q_fp4, 4) || !aligned(q_scales, 4))
+    return IQP_ERR_UNSUPPORTED;
+  if (M > 0x7FFFFFFF || H > 64 * 65535) return IQP_ERR_UNSUPPORTED;
+  const int st = device_status();
+  if (st != IQP_OK) return st;
+  return from_hip(iqp::launch_indexer_q_epilogue(static_cast<const uint16_t*>(q), ldq, M, H, positions,
+                                                 cos_sin, max_pos, q_fp4, q_scales,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
 int iqp_rope_cos_sin_table(double theta, int64_t max_pos, int32_t rope_dim, float* cos_sin,
                            void* stream) {
   if (max_pos < 0 || rope_dim <= 0 || rope_dim % 2 || !(theta > 0.0)) return IQP_ERR_INVALID;

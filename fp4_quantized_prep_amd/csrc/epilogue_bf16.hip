@@ -1,0 +1,172 @@
+// Standalone indexer-Q epilogue for gfx950: bf16 Q in, RoPE on each head's
+// rope slice, Hadamard-128, FP4 e2m1 with UE8M0 block scales out.
+//
+// This is the second half of the unfused chain the pages compare against:
+// TensorRT-LLM PR "Fuse DeepSeek-V4 Indexer Q projection with CuTe DSL",
+// Description / Paths compared (the Q GEMM writes a bf16 Q, then a RoPE
+// kernel and an FP4 quantization kernel run on it), and tokenspeed PR
+// "perf(deepseek-v4): accelerate indexer Q and packed FP8 quantization",
+// Summary (the MLA RoPE kernel, the Hadamard transform and the fused FP4 cat
+// kernel of the Q preparation). Here the three run as one launch.
+//
+// The work is HBM-bound: 256 bytes of bf16 in and 68 bytes out per
+// (token, head), plus a table row per token that stays in cache. Layout:
+//   * a workgroup takes one token and up to 64 of its heads (grid: tokens x
+//     head chunks), so token and head need no division;
+//   * four lanes (a quad) own one (token, head) vector of 128 dims; lane j
+//     holds dims d = 8 j + t + 32 u (t < 8, u < 4), loaded as four 16-byte
+//     non-temporal loads (one per u);
+//   * the RoPE pairs (i, i + 32), i < 32, are (u = 0, u = 1) of the same t in
+//     the same lane;
+//   * Hadamard butterflies over dim bits 0-2 (t) and 5-6 (u) run in the lane,
+//     those over bits 3 and 4 (lane bits 0 and 1) exchange with the quad
+//     neighbours by DPP;
+//   * FP4 block b = u (dims 32u .. 32u+31) is 8 values in each lane of the
+//     quad: an in-lane maximum, then two DPP maxima;
+//   * lane j writes the packed codes of dims 32u + 8j .. +7 (one dword per u)
+//     and lane 0 the four scale bytes.
+#include "iq_common.h"
+
+namespace iqp {
+namespace {
+
+constexpr int EPI_THREADS = 256;
+constexpr int DPP_QUAD_XOR1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;  // quad_perm [2,3,0,1]
+
+template <int CTRL>
+__device__ __forceinline__ float quad_xchg(float v) {
+  // quad permutes read a valid lane everywhere, so no "old" value is needed
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+__global__ __launch_bounds__(EPI_THREADS)
+void indexer_q_epilogue_kernel(const uint16_t* __restrict__ q, int64_t ldq, int32_t H,
+                               const int64_t* __restrict__ positions,
+                               const float* __restrict__ cos_sin, int64_t max_pos,
+                               uint8_t* __restrict__ q_fp4, uint8_t* __restrict__ q_scales) {
+  // workgroup (m, c): token m, heads 64c .. 64c + 63, one quad per head
+  const int j = threadIdx.x & 3;
+  const int64_t m = blockIdx.x;
+  const int hh = (int)blockIdx.y * (EPI_THREADS / 4) + (int)(threadIdx.x >> 2);
+  const bool live = hh < H;
+  const int h = live ? hh : H - 1;   // past the last head: read the last head, store nothing
+  const int64_t v = m * H + h;       // (token, head) vector index of the outputs
+
+  const uint16_t* src = q + m * ldq + (int64_t)h * HEAD_DIM + 8 * j;
+  v4u x[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) x[u] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(src + 32 * u));
+
+  int64_t pos = positions[m];
+  pos = pos < 0 ? 0 : (pos >= max_pos ? max_pos - 1 : pos);
+  const float* cs = cos_sin + pos * 64 + 8 * j;
+  const v4f c0 = *reinterpret_cast<const v4f*>(cs), c1 = *reinterpret_cast<const v4f*>(cs + 4);
+  const v4f s0 = *reinterpret_cast<const v4f*>(cs + 32), s1 = *reinterpret_cast<const v4f*>(cs + 36);
+
+  // bf16 -> float32: element 2k is the low half of dword k
+  float f[4][8];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      f[u][2 * k] = __uint_as_float(x[u][k] << 16);
+      f[u][2 * k + 1] = __uint_as_float(x[u][k] & 0xFFFF0000u);
+    }
+
+  // RoPE: pair i = 8j + t is (f[0][t], f[1][t])
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const float c = t < 4 ? c0[t] : c1[t - 4];
+    const float s = t < 4 ? s0[t] : s1[t - 4];
+    const float a = f[0][t], b = f[1][t];
+    f[0][t] = a * c - b * s;
+    f[1][t] = b * c + a * s;
+  }
+
+  // Unnormalised Hadamard butterflies: dim bits 0-2 (t) and 5-6 (u) in the lane
+#pragma unroll
+  for (int tb = 1; tb < 8; tb <<= 1)
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        if (!(t & tb)) {
+          const float a = f[u][t], b = f[u][t | tb];
+          f[u][t] = a + b;
+          f[u][t | tb] = a - b;
+        }
+#pragma unroll
+  for (int ub = 1; ub < 4; ub <<= 1)
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (!(u & ub))
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const float a = f[u][t], b = f[u | ub][t];
+          f[u][t] = a + b;
+          f[u | ub][t] = a - b;
+        }
+  // dim bit 3 = lane bit 0, dim bit 4 = lane bit 1: the lane with the bit
+  // clear keeps mine + partner, the other partner - mine
+  {
+    const float sg = (j & 1) ? -1.f : 1.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) f[u][t] = quad_xchg<DPP_QUAD_XOR1>(f[u][t]) + sg * f[u][t];
+  }
+  {
+    const float sg = (j & 2) ? -1.f : 1.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) f[u][t] = quad_xchg<DPP_QUAD_XOR2>(f[u][t]) + sg * f[u][t];
+  }
+
+  // FP4: z = butterfly sum / sqrt(128), formed explicitly (the conversion's
+  // scale operand carries only a power of two)
+  uint32_t sbytes = 0;
+  uint32_t dw[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    float mx = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      f[u][t] *= INV_SQRT_128;
+      mx = fmaxf(mx, fabsf(f[u][t]));
+    }
+    mx = fmaxf(mx, quad_xchg<DPP_QUAD_XOR1>(mx));
+    mx = fmaxf(mx, quad_xchg<DPP_QUAD_XOR2>(mx));
+    const int e = fp4_exponent(mx);
+    sbytes |= (uint32_t)(e + 127) << (8 * u);
+    const float scale = __uint_as_float((uint32_t)(e + 127) << 23);  // 2^e: codes are RNE(z / 2^e)
+    uint32_t d = 0;
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, f[u][0], f[u][1], scale, 0);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, f[u][2], f[u][3], scale, 1);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, f[u][4], f[u][5], scale, 2);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, f[u][6], f[u][7], scale, 3);
+    dw[u] = d;
+  }
+  if (live) {
+    // codes of dims 32u + 8j .. 32u + 8j + 7 sit at bytes 16u + 4j .. +3
+    uint8_t* dst = q_fp4 + v * (HEAD_DIM / 2) + 4 * j;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) __builtin_nontemporal_store(dw[u], reinterpret_cast<uint32_t*>(dst + 16 * u));
+    if (j == 0) __builtin_nontemporal_store(sbytes, reinterpret_cast<uint32_t*>(q_scales + v * 4));
+  }
+}
+
+}  // namespace
+
+hipError_t launch_indexer_q_epilogue(const uint16_t* q, int64_t ldq, int64_t M, int32_t H,
+                                     const int64_t* positions, const float* cos_sin, int64_t max_pos,
+                                     uint8_t* q_fp4, uint8_t* q_scales, hipStream_t stream) {
+  const int64_t chunks = ((int64_t)H + EPI_THREADS / 4 - 1) / (EPI_THREADS / 4);
+  if (M > 0x7FFFFFFF || chunks > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(indexer_q_epilogue_kernel, dim3((unsigned)M, (unsigned)chunks), dim3(EPI_THREADS), 0,
+                     stream, q, ldq, H, positions, cos_sin, max_pos, q_fp4, q_scales);
+  return hipGetLastError();
+}
+
+}  // namespace iqp

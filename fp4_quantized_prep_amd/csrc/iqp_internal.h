@@ -44,6 +44,12 @@ hipError_t launch_indexer_q_pipe(const IndexerQArgs& args, hipStream_t stream);
 bool indexer_q_small_supported(const IndexerQArgs& args);
 hipError_t launch_indexer_q_small(const IndexerQArgs& args, hipStream_t stream);
 
+// standalone epilogue: bf16 Q [M, H*128] (row stride ldq elements) -> RoPE,
+// Hadamard-128, FP4 codes [M, H, 64] and scale bytes [M, H, 4]
+hipError_t launch_indexer_q_epilogue(const uint16_t* q, int64_t ldq, int64_t M, int32_t H,
+                                     const int64_t* positions, const float* cos_sin, int64_t max_pos,
+                                     uint8_t* q_fp4, uint8_t* q_scales, hipStream_t stream);
+
 // compute units of the current device (cached per device)
 int cu_count();
 

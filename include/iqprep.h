@@ -2,7 +2,7 @@
  * iqprep.h — C ABI of libiqprep.so: DeepSeek-V4 indexer-Q preparation on
  * AMD Instinct MI355X (gfx950).
  *
- * The library computes, on the GPU, the two calls of indexer-Q preparation:
+ * The library computes, on the GPU, the calls of indexer-Q preparation:
  *
  *   1. fp8_quant_1x128_ue8m0     packed-UE8M0 FP8 1x128 activation quantization
  *      (tokenspeed PR "perf(deepseek-v4): accelerate indexer Q and packed FP8
@@ -13,6 +13,8 @@
  *      sequence diagram: FP8 input + UE8M0 scales in, packed FP4 Q and scales
  *      out; the same tokenspeed PR, Summary: RoPE, Hadamard and FP4 make up
  *      the Q preparation).
+ *   3. indexer_q_rope_hadamard_fp4   the same RoPE / Hadamard / FP4 epilogue as
+ *      a standalone launch over a bf16 Q (the unfused chain's second half).
  *
  * Conventions shared by every entry point:
  *
@@ -148,6 +150,40 @@ int indexer_q_gemm_rope_fp4(const void* a, int64_t lda,
                             const float* cos_sin, int64_t max_pos,
                             uint8_t* q_fp4, uint8_t* q_scales,
                             void* stream);
+
+/*
+ * indexer_q_rope_hadamard_fp4 — the epilogue of indexer_q_gemm_rope_fp4 as a
+ * standalone launch over a bf16 Q: RoPE + Hadamard-128 + FP4 e2m1.
+ *
+ * TensorRT-LLM PR "Fuse DeepSeek-V4 Indexer Q projection with CuTe DSL",
+ * Description / Paths compared (the unfused chain: the Q GEMM writes a bf16
+ * Q, then an in-place RoPE kernel and an FP4 quantization kernel with scale
+ * copies run on it); tokenspeed PR "perf(deepseek-v4): accelerate indexer Q
+ * and packed FP8 quantization", Summary (the RoPE kernel, the Hadamard
+ * transform and the fused FP4 cat kernel of the Q preparation).
+ *
+ * For every token m and head h, with Q_d = q[m * ldq + 128 h + d] widened to
+ * float32, the RoPE, Hadamard and FP4 steps are those of
+ * indexer_q_gemm_rope_fp4 (same table, same output layout and rounding).
+ *
+ *   q          bf16 [M, H*D], row stride ldq (elements, >= H*D); 16-byte
+ *              aligned and ldq a multiple of 8, else IQP_ERR_UNSUPPORTED.
+ *              Read only (no in-place RoPE).
+ *   M          tokens (>= 0); H >= 1; D must be 128 and rope_dim 64 (else
+ *              IQP_ERR_UNSUPPORTED); M < 2^31 and H <= 64 * 65535.
+ *   positions  int64 [M]; outside [0, max_pos) is a precondition violation,
+ *              clamped into range as in indexer_q_gemm_rope_fp4.
+ *   cos_sin    float32 [max_pos, rope_dim] as in indexer_q_gemm_rope_fp4,
+ *              16-byte aligned; max_pos >= 1.
+ *   q_fp4      uint8 [M, H, D/2] packed E2M1 codes, 4-byte aligned.
+ *   q_scales   uint8 [M, H, D/32] UE8M0 bytes, 4-byte aligned.
+ *
+ * Q must be finite.
+ */
+int indexer_q_rope_hadamard_fp4(const void* q, int64_t ldq, int64_t M, int32_t H, int32_t D,
+                                int32_t rope_dim, const int64_t* positions,
+                                const float* cos_sin, int64_t max_pos,
+                                uint8_t* q_fp4, uint8_t* q_scales, void* stream);
 
 /*
  * iqp_rope_cos_sin_table — builds the standard RoPE table that

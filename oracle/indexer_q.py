@@ -161,6 +161,30 @@ def fp4_quantize(z, decide_dtype=np.float32) -> tuple:
 
 
 # ----------------------------------------------------------------------------
+# Standalone epilogue (the unfused chain's second half)
+# ----------------------------------------------------------------------------
+
+
+def indexer_q_epilogue(q, positions, n_heads: int = 64, head_dim: int = 128, rope_dim: int = 64,
+                       theta: float = 10000.0) -> dict:
+    """RoPE, Hadamard rotation and FP4 quantization of an already projected Q.
+
+    This is the unfused chain's epilogue (TensorRT-LLM PR "Fuse DeepSeek-V4
+    Indexer Q projection with CuTe DSL", Description / Paths compared: the Q
+    GEMM writes a bf16 Q that a RoPE kernel and an FP4 quantization kernel then
+    consume). q is [M, H*D] (the bf16 values, widened exactly); the steps are
+    the same functions the fused chain applies after its GEMM.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    M = q.shape[0]
+    q = q.reshape(M, n_heads, head_dim)
+    q_rope = rope_half_split(q, positions, theta, rope_dim)
+    z = hadamard_rotate(q_rope)
+    packed, scales = fp4_quantize(z)
+    return {"q_rope": q_rope, "z": z, "q_fp4": packed, "q_scales": scales}
+
+
+# ----------------------------------------------------------------------------
 # Whole chain
 # ----------------------------------------------------------------------------
 

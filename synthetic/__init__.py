@@ -21,6 +21,11 @@ Workloads (token counts and widths from the pages' microbenchmarks: 128 and
 * ``prefill_m32768``   X[32768,1536] ~ Student-t (nu=3); positions 0..32767;
   plus a standalone X'[32768,7168] ~ t3
 
+The standalone epilogue takes a bf16 Q [M, 64*128] instead of X: each token
+row is N(0,1) times a per-token factor 2^u, u uniform in [-4, 4] (the spread
+of magnitudes a projection output has across tokens), with the positions of
+the workload it stands beside (``q_bf16_inputs``).
+
 Weights: W[8192,1536] ~ N(0, 0.02^2), stored as E4M3 codes with one UE8M0
 exponent per 128x128 tile. The tile exponents are drawn from {-12, -11}
 (about the natural exponent for N(0, 0.02^2) data), and the codes are the
@@ -124,6 +129,17 @@ def indexer_q_inputs(workload: str, M: int = None) -> dict:
     else:
         raise ValueError(workload)
     return {"x": x, "positions": pos, "max_pos": max_pos, "M": M}
+
+
+def q_bf16_inputs(workload: str, M: int = None, n_heads: int = N_HEADS) -> dict:
+    """bf16 Q [M, n_heads*128] and positions for the standalone epilogue, at the
+    token counts and positions of an indexer-Q workload."""
+    base = indexer_q_inputs(workload, M=M)
+    M = base["M"]
+    g = rng(workload, 5)
+    q = g.standard_normal((M, n_heads * HEAD_DIM), dtype=np.float32)
+    q *= np.exp2(g.uniform(-4.0, 4.0, size=(M, 1))).astype(np.float32)
+    return {"q": to_bf16(q), "positions": base["positions"], "max_pos": base["max_pos"], "M": M}
 
 
 def decode_calls(n_calls: int = 256) -> list:

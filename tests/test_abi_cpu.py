@@ -25,8 +25,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    assert {"fp8_quant_1x128_ue8m0", "indexer_q_gemm_rope_fp4", "iqp_status_string",
-            "iqp_abi_version"} <= set(names)
+    assert {"fp8_quant_1x128_ue8m0", "indexer_q_gemm_rope_fp4", "indexer_q_rope_hadamard_fp4",
+            "iqp_status_string", "iqp_abi_version"} <= set(names)
 
 
 def test_library_exports_every_declared_symbol(iqp):
@@ -99,6 +99,28 @@ def test_debug_and_table_argument_checks(iqp):
     assert lib.iqp_rope_cos_sin_table(-1.0, 10, 64, P(16), None) == iqp.IQP_ERR_INVALID
     assert lib.iqp_rope_cos_sin_table(10000.0, 10, 64, P(0), None) == iqp.IQP_ERR_INVALID
     assert lib.iqp_rope_cos_sin_table(10000.0, 0, 64, P(0), None) == iqp.IQP_OK
+
+
+def epilogue(iqp, q=16, ldq=256, M=4, H=2, D=128, rd=64, pos=16, cs=16, mp=10, out=16, sc=16):
+    return iqp._lib.indexer_q_rope_hadamard_fp4(P(q), ldq, M, H, D, rd, P(pos), P(cs), mp, P(out), P(sc), None)
+
+
+def test_epilogue_argument_checks(iqp):
+    inv, uns = iqp.IQP_ERR_INVALID, iqp.IQP_ERR_UNSUPPORTED
+    assert epilogue(iqp, M=0, q=0) == iqp.IQP_OK                  # M == 0: no-op before pointer checks
+    assert epilogue(iqp, M=-1) == inv
+    assert epilogue(iqp, q=0) == inv
+    assert epilogue(iqp, pos=0) == inv
+    assert epilogue(iqp, out=0) == inv
+    assert epilogue(iqp, H=0) == inv
+    assert epilogue(iqp, mp=0) == inv
+    assert epilogue(iqp, ldq=255) == inv                          # row stride below H * 128
+    assert epilogue(iqp, D=64, ldq=128) == uns
+    assert epilogue(iqp, rd=32) == uns
+    assert epilogue(iqp, q=8) == uns                              # bf16 input must be 16-byte aligned
+    assert epilogue(iqp, ldq=260) == uns                          # row stride not a multiple of 8
+    assert epilogue(iqp, cs=8) == uns
+    assert epilogue(iqp, out=2) == uns
 
 
 def test_python_wrapper_rejects_wrong_dtypes(iqp):

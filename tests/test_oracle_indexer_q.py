@@ -278,3 +278,74 @@ def test_chain_composes_the_stages():
     p, s = IQ.fp4_quantize(z)
     assert np.array_equal(out["q_fp4"], p) and np.array_equal(out["q_scales"], s)
     assert out["q_fp4"].shape == (M, H, 64) and out["q_scales"].shape == (M, H, 4)
+
+
+# ----------------------------------------------------------------------------
+# Standalone epilogue (bf16 Q in): hand-derived closed forms
+# ----------------------------------------------------------------------------
+
+
+def _one_hot_q(d, value=1.0, n_heads=1):
+    q = np.zeros((1, n_heads * 128))
+    q[0, d] = value
+    return q
+
+
+def test_epilogue_pass_through_dim_gives_hadamard_column():
+    # dim 69 >= 64 is not rotated; z = column 69 of H / sqrt(128), every entry
+    # +-1/sqrt(128) = +-0.0884. amax/6 = 0.01473 lies in (2^-7, 2^-6]: e = -6,
+    # byte 121; 0.0884 * 64 = 5.657 is above the 4|6 midpoint 5 -> magnitude 6,
+    # code 7; the sign is (-1)^popcount(r & 69).
+    out = IQ.indexer_q_epilogue(_one_hot_q(69), np.array([1234]), n_heads=1)
+    assert out["q_scales"].tolist() == [[[121, 121, 121, 121]]]
+    codes = F.e2m1_unpack(out["q_fp4"].reshape(-1))
+    want = [7 | (8 if bin(r & 69).count("1") % 2 else 0) for r in range(128)]
+    assert codes.tolist() == want
+
+
+def test_epilogue_rotated_dim0_at_position_one():
+    # dim 0 at position 1 rotates by 1 rad into (cos 1, sin 1) on dims (0, 32).
+    # z_r = (cos 1 + (-1)^bit5(r) sin 1) / sqrt(128): 0.12213 where bit 5 of r
+    # is clear, -0.02662 where it is set.
+    #   blocks 0, 2: 0.12213/6 in (2^-6, 2^-5]: e = -5, byte 122; 0.12213*32 = 3.908
+    #                is above the 3|4 midpoint 3.5 -> 4, code 6 -> bytes 0x66
+    #   blocks 1, 3: 0.02662/6 in (2^-8, 2^-7]: e = -7, byte 120; 0.02662*128 = 3.407
+    #                is below 3.5 -> 3, code 5, negative -> 0xD -> bytes 0xDD
+    hi = (math.cos(1) + math.sin(1)) / math.sqrt(128)
+    lo = (math.cos(1) - math.sin(1)) / math.sqrt(128)
+    assert abs(hi * 32 - 3.5) > 0.3 and abs(abs(lo) * 128 - 3.5) > 0.05   # far from a boundary
+    out = IQ.indexer_q_epilogue(_one_hot_q(0), np.array([1]), n_heads=1)
+    assert out["q_scales"].tolist() == [[[122, 120, 122, 120]]]
+    assert out["q_fp4"].reshape(-1).tolist() == [0x66] * 16 + [0xDD] * 16 + [0x66] * 16 + [0xDD] * 16
+
+
+def test_epilogue_frequency_index_of_pair_16():
+    # dim 16 at position 1000: angle 1000 * 10000^(-32/64) = 10 rad, into dims
+    # (16, 48). z_r = (-1)^bit4(r) (cos 10 + (-1)^bit5(r) sin 10) / sqrt(128):
+    #   bit 5 clear: |z| = 0.12225, sign -(-1)^bit4 -> e = -5 (byte 122),
+    #                0.12225*32 = 3.912 -> 4, code 6: 0xE for r%32 < 16, 0x6 above
+    #   bit 5 set:   |z| = 0.02608, sign -(-1)^bit4 -> e = -7 (byte 120),
+    #                0.02608*128 = 3.338 -> 3, code 5: 0xD for r%32 < 16, 0x5 above
+    a = abs(math.cos(10) + math.sin(10)) / math.sqrt(128)
+    b = abs(math.cos(10) - math.sin(10)) / math.sqrt(128)
+    assert abs(a * 32 - 3.5) > 0.3 and abs(b * 128 - 3.5) > 0.1
+    out = IQ.indexer_q_epilogue(_one_hot_q(16), np.array([1000]), n_heads=1)
+    assert out["q_scales"].tolist() == [[[122, 120, 122, 120]]]
+    blk_hi = [0xEE] * 8 + [0x66] * 8
+    blk_lo = [0xDD] * 8 + [0x55] * 8
+    assert out["q_fp4"].reshape(-1).tolist() == blk_hi + blk_lo + blk_hi + blk_lo
+
+
+def test_epilogue_heads_are_independent_and_match_the_chain_stages():
+    rng = np.random.default_rng(7)
+    M, H = 5, 3
+    q = rng.standard_normal((M, H * 128))
+    pos = rng.integers(0, 4096, M)
+    out = IQ.indexer_q_epilogue(q, pos, n_heads=H)
+    for h in range(H):
+        one = IQ.indexer_q_epilogue(q[:, 128 * h:128 * (h + 1)], pos, n_heads=1)
+        assert np.array_equal(one["q_fp4"][:, 0], out["q_fp4"][:, h])
+        assert np.array_equal(one["q_scales"][:, 0], out["q_scales"][:, h])
+    # rotation and Hadamard preserve each head's norm
+    np.testing.assert_allclose(np.linalg.norm(out["z"], axis=-1),
+                               np.linalg.norm(q.reshape(M, H, 128), axis=-1), rtol=1e-13)
