@@ -55,33 +55,39 @@ def fused_bytes(M):
             + M * 8 + M * 64 * 4 + M * N_HEADS * (HEAD_DIM // 2 + HEAD_DIM // 32))
 
 
-# the sources of the fused kernel that runs for K = 1536 (the pipelined one)
-FUSED_SOURCES = ("indexer_q_pipe.hip", "iq_common.h")
+# The sources each measured kernel is built from: a committed traffic figure is
+# used only while these files hash to the digest recorded beside it.
+KERNEL_SOURCES = {
+    "fused": ("indexer_q_pipe.hip", "iq_common.h"),        # the K = 1536 kernel
+    "quant": ("quant_fp8.hip",),
+    "epilogue": ("epilogue_bf16.hip", "iq_common.h"),
+}
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "indexer_q_chain_m4632_rocprofv3.md")
 
 
-def fused_source_digest():
-    """First 16 hex digits of the SHA-256 of the fused kernel's sources."""
+def source_digest(kernel):
+    """First 16 hex digits of the SHA-256 of a kernel's sources."""
     import hashlib
     h = hashlib.sha256()
-    for name in FUSED_SOURCES:
+    for name in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "fp4_quantized_prep_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per fused launch from the committed rocprofv3 counter summary
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary
     (FETCH_SIZE and WRITE_SIZE scaled by a plain copy's readings), or None if
-    the kernel source changed since the counters were taken."""
-    prof = os.path.join(ROOT, "profiles", "indexer_q_chain_m4632_rocprofv3.md")
+    the kernel's sources changed since the counters were taken."""
     try:
-        fields = dict(line.strip().split(": ", 1) for line in open(prof) if line.strip().startswith("fused_"))
-        digest = fused_source_digest()
+        fields = dict(line.strip().split(": ", 1) for line in open(TRAFFIC_PROFILE)
+                      if line.strip().startswith(kernel + "_"))
+        digest = source_digest(kernel)
     except (OSError, ValueError):
         return None
-    if fields.get("fused_kernel_source_sha256_16") != digest:
+    if fields.get(f"{kernel}_kernel_source_sha256_16") != digest:
         return None
-    return int(fields["fused_traffic_bytes_per_launch"])
+    return int(fields[f"{kernel}_traffic_bytes_per_launch"])
 
 
 def epilogue_bytes(M, H=N_HEADS):
@@ -267,7 +273,7 @@ def main():
             "peak": PEAK_FP8_TFLOPS,
             "unit": "TFLOP/s",
             "frac": fused_tflops / PEAK_FP8_TFLOPS,
-            "traffic": measured_traffic(),
+            "traffic": measured_traffic("fused"),
             "algorithmic_flops_per_launch": flops,
             "avg_launch_us": t_fused * 1e6,
         },
@@ -279,6 +285,7 @@ def main():
             "unit": "GB/s",
             "frac": q_gbs / PEAK_HBM_GBS,
             "algorithmic_bytes_per_launch": qbytes,
+            "traffic": measured_traffic("quant"),
             "avg_launch_us": t_q_big * 1e6,
             "avg_launch_us_event_pair_each": t_q_ev * 1e6,
             "in_chain_avg_launch_us": t_quant * 1e6,
@@ -292,6 +299,7 @@ def main():
             "unit": "GB/s",
             "frac": e_gbs / PEAK_HBM_GBS,
             "algorithmic_bytes_per_launch": ebytes,
+            "traffic": measured_traffic("epilogue"),
             "avg_launch_us": t_epi * 1e6,
         },
         "cpu_baseline": cpu,

@@ -161,7 +161,7 @@ int indexer_q_rope_hadamard_fp4(const void* q, int64_t ldq, int64_t M, int32_t H
   if (D != 128 || rope_dim != 64) return IQP_ERR_UNSUPPORTED;
   if (ldq < (int64_t)H * D) return IQP_ERR_INVALID;
   if (!aligned(q, 16) || ldq % 8 || !aligned(positions, 8) || !aligned(cos_sin, 16) ||
-      !aligned(q_fp4, 4) || !aligned(q_scales, 4))
+      !aligned(q_fp4, 16) || !aligned(q_scales, 4))
     return IQP_ERR_UNSUPPORTED;
   if (M > 0x7FFFFFFF || H > 64 * 65535) return IQP_ERR_UNSUPPORTED;
   const int st = device_status();

@@ -15,7 +15,7 @@
 //     head chunks), so token and head need no division;
 //   * four lanes (a quad) own one (token, head) vector of 128 dims; lane j
 //     holds dims d = 8 j + t + 32 u (t < 8, u < 4), loaded as four 16-byte
-//     non-temporal loads (one per u);
+//     loads (one per u);
 //   * the RoPE pairs (i, i + 32), i < 32, are (u = 0, u = 1) of the same t in
 //     the same lane;
 //   * Hadamard butterflies over dim bits 0-2 (t) and 5-6 (u) run in the lane,
@@ -23,8 +23,13 @@
 //     neighbours by DPP;
 //   * FP4 block b = u (dims 32u .. 32u+31) is 8 values in each lane of the
 //     quad: an in-lane maximum, then two DPP maxima;
-//   * lane j writes the packed codes of dims 32u + 8j .. +7 (one dword per u)
-//     and lane 0 the four scale bytes.
+//   * the packed codes (one dword per lane and block) are transposed within
+//     the quad through LDS so that lane j stores block j's 16 bytes: a wave
+//     writes 1 KiB of whole lines per store; lane 0 stores the scale bytes.
+// Measured on MI355X at 4632 tokens x 64 heads (four rotating buffer sets):
+// 18.5 us; a copy of the kernel with the arithmetic removed (same loads and
+// stores) takes 17.4 us. Storing one dword per block from each lane, or
+// non-temporal loads, cost 20.0-21.6 us.
 #include "iq_common.h"
 
 namespace iqp {
@@ -56,7 +61,7 @@ void indexer_q_epilogue_kernel(const uint16_t* __restrict__ q, int64_t ldq, int3
   const uint16_t* src = q + m * ldq + (int64_t)h * HEAD_DIM + 8 * j;
   v4u x[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) x[u] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(src + 32 * u));
+  for (int u = 0; u < 4; ++u) x[u] = *reinterpret_cast<const v4u*>(src + 32 * u);
 
   int64_t pos = positions[m];
   pos = pos < 0 ? 0 : (pos >= max_pos ? max_pos - 1 : pos);
@@ -148,11 +153,21 @@ void indexer_q_epilogue_kernel(const uint16_t* __restrict__ q, int64_t ldq, int3
     d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, f[u][6], f[u][7], scale, 3);
     dw[u] = d;
   }
-  if (live) {
-    // codes of dims 32u + 8j .. 32u + 8j + 7 sit at bytes 16u + 4j .. +3
-    uint8_t* dst = q_fp4 + v * (HEAD_DIM / 2) + 4 * j;
+  // The codes of dims 32u + 8j .. 32u + 8j + 7 belong at bytes 16u + 4j .. +3
+  // of the vector's 64-byte row. Each quad's row goes through 16 dwords of LDS
+  // (rows 20 dwords apart, so the 64 lanes of a write hit 64 distinct banks);
+  // lane j reads back dwords 4j .. 4j + 3. Only the lanes of one wave touch a
+  // row, so a wave-level barrier orders the writes before the reads.
+  __shared__ __attribute__((aligned(16))) uint32_t rows[EPI_THREADS / 64][16 * 20];
+  uint32_t* row = rows[threadIdx.x >> 6] + 20 * ((threadIdx.x >> 2) & 15);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) __builtin_nontemporal_store(dw[u], reinterpret_cast<uint32_t*>(dst + 16 * u));
+  for (int u = 0; u < 4; ++u) row[4 * u + j] = dw[u];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const v4u codes = *reinterpret_cast<const v4u*>(row + 4 * j);
+  if (live) {
+    __builtin_nontemporal_store(codes, reinterpret_cast<v4u*>(q_fp4 + v * (HEAD_DIM / 2) + 16 * j));
     if (j == 0) __builtin_nontemporal_store(sbytes, reinterpret_cast<uint32_t*>(q_scales + v * 4));
   }
 }

@@ -175,7 +175,7 @@ int indexer_q_gemm_rope_fp4(const void* a, int64_t lda,
  *              clamped into range as in indexer_q_gemm_rope_fp4.
  *   cos_sin    float32 [max_pos, rope_dim] as in indexer_q_gemm_rope_fp4,
  *              16-byte aligned; max_pos >= 1.
- *   q_fp4      uint8 [M, H, D/2] packed E2M1 codes, 4-byte aligned.
+ *   q_fp4      uint8 [M, H, D/2] packed E2M1 codes, 16-byte aligned.
  *   q_scales   uint8 [M, H, D/32] UE8M0 bytes, 4-byte aligned.
  *
  * Q must be finite.

@@ -121,6 +121,7 @@ def test_epilogue_argument_checks(iqp):
     assert epilogue(iqp, ldq=260) == uns                          # row stride not a multiple of 8
     assert epilogue(iqp, cs=8) == uns
     assert epilogue(iqp, out=2) == uns
+    assert epilogue(iqp, out=8) == uns                            # codes are stored 16 bytes at a time
 
 
 def test_python_wrapper_rejects_wrong_dtypes(iqp):
