@@ -18,6 +18,13 @@ calls with M drawn from {1, 2, 4, 8, 16, 32, 64} (each: quantize X [M, 1536],
 the fused kernel, and a standalone quantization of X' [M, 7168]), replayed
 from one captured HIP graph (sustained calls/s), with per-M latencies from
 graphs of repeated single calls.
+
+`--workload prefill32k` measures the long-prefill workload: the chain at
+32,768 tokens (X Student-t, nu = 3; positions 0..32767) and the standalone
+quantizer on X' [32768, 7168]. The default line also carries the standalone
+epilogue (bf16 Q [4632, 64x128] -> RoPE, Hadamard, FP4) against its HBM
+roofline; `--vendor-gemm` adds the vendor FP8 GEMM (hipBLASLt) timed at the
+projection shape, as context only.
 """
 import argparse
 import json
@@ -43,7 +50,10 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0: calibrate to ~15 s)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain device copy of 256 MiB (for HBM byte-counter scaling)")
-    ap.add_argument("--workload", choices=("prefill", "decode"), default="prefill")
+    ap.add_argument("--workload", choices=("prefill", "prefill32k", "decode"), default="prefill")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="also time the vendor FP8 GEMM (hipBLASLt via torch._scaled_mm, per-tensor scales, "
+                         "bf16 out) at the projection shape, as context for the fused kernel's MFMA fraction")
     return ap.parse_args()
 
 
@@ -111,6 +121,9 @@ def main():
 
     if args.workload == "decode":
         decode_bench(args)
+        return
+    if args.workload == "prefill32k":
+        prefill32k_bench(args)
         return
 
     import numpy as np
@@ -181,19 +194,13 @@ def main():
     for i in range(10):
         iqp.fp8_quant_1x128_ue8m0(xs[i % n_sets], q=qq[i % n_sets], scales=ss[i % n_sets])
     torch.cuda.synchronize()
-    # Launches run back to back between two events on the kernel's stream, so the
-    # average is the kernel's own duration (an event pair around every launch adds
-    # ~2.5 us of dispatch gap per launch at this size); the per-launch-event figure
-    # is reported beside it.
+    # Launches replayed back to back from a captured graph between two events on
+    # the kernel's stream, so the average is the kernel's own duration (an event
+    # pair around every launch adds ~2.5 us of dispatch gap at this size); the
+    # per-launch-event figure is reported beside it.
     n_q = max(50, K)
-    qa, qb_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    qa.record(stream)
-    for i in range(n_q):
-        k = i % n_sets
-        iqp.fp8_quant_1x128_ue8m0(xs[k], q=qq[k], scales=ss[k])
-    qb_.record(stream)
-    torch.cuda.synchronize()
-    t_q_big = qa.elapsed_time(qb_) * 1e-3 / n_q
+    t_q_big = graph_launch_time(
+        lambda i: iqp.fp8_quant_1x128_ue8m0(xs[i % n_sets], q=qq[i % n_sets], scales=ss[i % n_sets]), n_q)
     qev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_q)]
     for i in range(n_q):
         k = i % n_sets
@@ -204,7 +211,7 @@ def main():
     t_q_ev = float(np.mean([b.elapsed_time(e) for b, e in qev])) * 1e-3
     qbytes = quant_bytes(QUANT_M, QUANT_K)
     q_gbs = qbytes / t_q_big / 1e9
-    print(f"[bench] quantizer [4632,7168]: {t_q_big * 1e6:.1f} us = {q_gbs:.0f} GB/s back to back; "
+    print(f"[bench] quantizer [4632,7168]: {t_q_big * 1e6:.1f} us = {q_gbs:.0f} GB/s back to back (graph); "
           f"{t_q_ev * 1e6:.1f} us with an event pair around each launch", file=sys.stderr, flush=True)
     del xs, qq, ss
 
@@ -220,19 +227,16 @@ def main():
                                         q_scales=es[i % e_sets])
     torch.cuda.synchronize()
     n_e = max(40, K)
-    ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ea.record(stream)
-    for i in range(n_e):
-        k = i % e_sets
-        iqp.indexer_q_rope_hadamard_fp4(eq[k], pos, cs, n_heads=N_HEADS, q_fp4=eo[k], q_scales=es[k])
-    eb.record(stream)
-    torch.cuda.synchronize()
-    t_epi = ea.elapsed_time(eb) * 1e-3 / n_e
+    t_epi = graph_launch_time(
+        lambda i: iqp.indexer_q_rope_hadamard_fp4(eq[i % e_sets], pos, cs, n_heads=N_HEADS, q_fp4=eo[i % e_sets],
+                                                  q_scales=es[i % e_sets]), n_e)
     ebytes = epilogue_bytes(M)
     e_gbs = ebytes / t_epi / 1e9
     print(f"[bench] standalone epilogue [4632, 64x128] bf16: {t_epi * 1e6:.1f} us = {e_gbs:.0f} GB/s",
           file=sys.stderr, flush=True)
     del eq, eo, es
+
+    vendor = vendor_gemm_context(M, dev) if args.vendor_gemm else None
 
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -278,7 +282,8 @@ def main():
             "avg_launch_us": t_fused * 1e6,
         },
         "quant_roofline": {
-            "kernel": "fp8_quant_1x128_kernel on [4632,7168] (5 rotating buffer sets, launches back to back)",
+            "kernel": "fp8_quant_1x128_kernel on [4632,7168] (5 rotating buffer sets, launches back to back "
+                      "from a captured graph)",
             "bound": "hbm",
             "achieved": q_gbs,
             "peak": PEAK_HBM_GBS,
@@ -292,7 +297,7 @@ def main():
         },
         "epilogue_roofline": {
             "kernel": "indexer_q_epilogue_kernel (bf16 Q [4632, 64x128] -> RoPE, Hadamard-128, FP4; "
-                      "4 rotating buffer sets, launches back to back)",
+                      "4 rotating buffer sets, launches back to back from a captured graph)",
             "bound": "hbm",
             "achieved": e_gbs,
             "peak": PEAK_HBM_GBS,
@@ -301,6 +306,177 @@ def main():
             "algorithmic_bytes_per_launch": ebytes,
             "traffic": measured_traffic("epilogue"),
             "avg_launch_us": t_epi * 1e6,
+        },
+        "cpu_baseline": cpu,
+    }
+    if vendor is not None:
+        result["vendor_gemm_context"] = vendor
+    print(json.dumps(result), flush=True)
+
+
+def graph_launch_time(launch, n_calls, reps=5):
+    """Average device time per call of launch(0..n_calls-1), replayed from one
+    captured HIP graph between two events on the current stream: host-side
+    launch cost (the Python binding's checks) is out of the measurement, so a
+    short kernel is not starved by its own launches."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        launch(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n_calls):
+            launch(i)
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e-3 / (reps * n_calls)
+
+
+def vendor_gemm_context(M, dev, reps=100):
+    """The vendor FP8 GEMM at the projection shape [M, 1536] x [8192, 1536]^T:
+    hipBLASLt through torch._scaled_mm with per-tensor scales and a bf16 output,
+    no epilogue. Not part of the path: a reference for what a plain library GEMM
+    reaches on this chip at this shape."""
+    import torch
+    x = torch.randn(M, K_PROJ, device=dev).to(torch.float8_e4m3fn)
+    w = torch.randn(N_HEADS * HEAD_DIM, K_PROJ, device=dev).to(torch.float8_e4m3fn)
+    one = torch.tensor(1.0, device=dev)
+    fn = lambda: torch._scaled_mm(x, w.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+    for _ in range(10):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / reps
+    tflops = 2.0 * M * N_HEADS * HEAD_DIM * K_PROJ / us * 1e-6
+    print(f"[bench] vendor FP8 GEMM (hipBLASLt, per-tensor scales, bf16 out): {us:.1f} us = {tflops:.0f} TFLOP/s",
+          file=sys.stderr, flush=True)
+    return {"what": "torch._scaled_mm (hipBLASLt) e4m3 [M,1536] x [8192,1536]^T, per-tensor scales, bf16 out, "
+                    "no epilogue; launches back to back", "avg_launch_us": us, "achieved_tflops": tflops,
+            "frac": tflops / PEAK_FP8_TFLOPS}
+
+
+def prefill32k_bench(args):
+    """The long-prefill workload: the chain at 32,768 tokens (X Student-t nu=3,
+    positions 0..32767) and the standalone quantizer on X' [32768, 7168];
+    prints one JSON line in the same form as the default workload."""
+    import numpy as np
+    import torch
+
+    import fp4_quantized_prep_amd as iqp
+    import synthetic as S
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    inp = S.indexer_q_inputs("prefill_m32768")
+    x, pos = inp["x"].to(dev), inp["positions"].to(dev)
+    w_cpu, wsb_cpu = S.weights()
+    w, wsb = w_cpu.to(dev), wsb_cpu.to(dev)
+    cs = iqp.rope_cos_sin_table(S.ROPE_THETA, inp["max_pos"], 64, device=dev)
+    M = x.shape[0]
+    a = torch.empty((M, K_PROJ), dtype=torch.uint8, device=dev)
+    a_s = torch.empty((M, (K_PROJ // 128 + 3) // 4), dtype=torch.int32, device=dev)
+    q = torch.empty((M, N_HEADS, HEAD_DIM // 2), dtype=torch.uint8, device=dev)
+    qs = torch.empty((M, N_HEADS, HEAD_DIM // 32), dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup):
+        iqp.fp8_quant_1x128_ue8m0(x, q=a, scales=a_s)
+        iqp.indexer_q_gemm_rope_fp4(a, a_s, w, wsb, pos, cs, n_heads=N_HEADS, q_fp4=q, q_scales=qs)
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(K):
+        ev[i][0].record(stream)
+        iqp.fp8_quant_1x128_ue8m0(x, q=a, scales=a_s)
+        ev[i][1].record(stream)
+        iqp.indexer_q_gemm_rope_fp4(a, a_s, w, wsb, pos, cs, n_heads=N_HEADS, q_fp4=q, q_scales=qs)
+        ev[i][2].record(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    t_quant = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3
+    t_fused = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e-3
+    flops = 2.0 * M * (N_HEADS * HEAD_DIM) * K_PROJ
+    fused_tflops = flops / t_fused / 1e12
+    print(f"[bench] chain at {M} tokens: {total_ms / K * 1e3:.1f} us/step; quant {t_quant * 1e6:.1f} us, "
+          f"fused {t_fused * 1e6:.1f} us = {fused_tflops:.0f} TFLOP/s", file=sys.stderr, flush=True)
+    del a, a_s, q, qs
+
+    xw_cpu = S.quant_input("prefill_m32768")
+    n_sets = 2        # 2 x (470 MB in + 235 MB out): beyond the 256 MiB cache
+    xs = [xw_cpu.to(dev) for _ in range(n_sets)]
+    qq = [torch.empty((M, QUANT_K), dtype=torch.uint8, device=dev) for _ in range(n_sets)]
+    ss = [torch.empty((M, (QUANT_K // 128 + 3) // 4), dtype=torch.int32, device=dev) for _ in range(n_sets)]
+    for i in range(4):
+        iqp.fp8_quant_1x128_ue8m0(xs[i % n_sets], q=qq[i % n_sets], scales=ss[i % n_sets])
+    torch.cuda.synchronize()
+    n_q = max(20, K // 4)
+    t_qw = graph_launch_time(
+        lambda i: iqp.fp8_quant_1x128_ue8m0(xs[i % n_sets], q=qq[i % n_sets], scales=ss[i % n_sets]), n_q, reps=2)
+    qbytes = quant_bytes(M, QUANT_K)
+    q_gbs = qbytes / t_qw / 1e9
+    print(f"[bench] quantizer [{M},{QUANT_K}]: {t_qw * 1e6:.1f} us = {q_gbs:.0f} GB/s", file=sys.stderr, flush=True)
+    del xs, qq, ss
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_tokens, inp, w_cpu, wsb_cpu)
+    result = {
+        "metric": "tokens/sec & % roofline: FP8 quant (HBM GB/s) + fused indexer-Q (MFMA util)",
+        "value": M * K / (total_ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": total_ms / K,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-e4m3 (fp32 accumulate), bf16 in, fp4-e2m1 out",
+        "data": "synthetic",
+        "config": {
+            "workload": "long prefill, 32768 tokens: X bf16 [32768,1536] Student-t nu=3 -> FP8 1x128 UE8M0 -> "
+                        "fused Q projection + RoPE + Hadamard-128 + FP4; plus the standalone quantizer on "
+                        "X' [32768,7168]",
+            "tokens": M, "K": K_PROJ, "heads": N_HEADS, "head_dim": HEAD_DIM, "rope_dim": 64,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "kernel": "indexer_q_pipe_kernel (fused GEMM + RoPE + Hadamard + FP4)",
+            "bound": "mfma",
+            "achieved": fused_tflops,
+            "peak": PEAK_FP8_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": fused_tflops / PEAK_FP8_TFLOPS,
+            "traffic": None,
+            "algorithmic_flops_per_launch": flops,
+            "avg_launch_us": t_fused * 1e6,
+        },
+        "quant_roofline": {
+            "kernel": f"fp8_quant_1x128_kernel on [{M},{QUANT_K}] (2 rotating buffer sets, launches back to back "
+                      "from a captured graph)",
+            "bound": "hbm",
+            "achieved": q_gbs,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": q_gbs / PEAK_HBM_GBS,
+            "algorithmic_bytes_per_launch": qbytes,
+            "avg_launch_us": t_qw * 1e6,
+            "in_chain_avg_launch_us": t_quant * 1e6,
         },
         "cpu_baseline": cpu,
     }
@@ -463,17 +639,18 @@ def cpu_baseline(n_tokens, inp, w_cpu, wsb_cpu):
     # than that, else the whole batch repeated
     target = 15.0
     reps = 1
+    total = x.shape[0]
     if n_tokens <= 0:
-        est_full = run(128) * M_TOKENS / 128
+        est_full = run(128) * total / 128
         if est_full > target:
-            n_tokens = int(max(128, M_TOKENS * target / est_full))
+            n_tokens = int(max(128, total * target / est_full))
         else:
-            n_tokens = M_TOKENS
+            n_tokens = total
             reps = max(1, int(round(target / max(est_full, 1e-3))))
     dt = sum(run(n_tokens) for _ in range(reps))
     print(f"[bench] oracle: {reps} x {n_tokens} tokens in {dt:.2f} s on {threads} threads", file=sys.stderr, flush=True)
     return {"value": reps * n_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{reps} pass(es) over the first {n_tokens} of the 4632 tokens, whole chain (quantize + "
+            "sample": f"{reps} pass(es) over the first {n_tokens} of the {total} tokens, whole chain (quantize + "
                       f"GEMM + RoPE + Hadamard + FP4), numpy float64, {dt:.1f} s"}
 
 
