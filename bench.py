@@ -14,10 +14,11 @@ timed on a bounded sample of the same workload.
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 
 `--workload decode` instead measures the decode-shaped mix: 256 independent
-calls with M drawn from {1, 2, 4, 8, 16, 32, 64} (each: quantize X [M, 1536],
-the fused kernel, and a standalone quantization of X' [M, 7168]), replayed
-from one captured HIP graph (sustained calls/s), with per-M latencies from
-graphs of repeated single calls.
+calls with M drawn from {1, 2, 4, 8, 16, 32, 64} (each: the indexer-Q
+preparation of X [M, 1536] in one launch, and a standalone quantization of
+X' [M, 7168]), replayed from one captured HIP graph (sustained calls/s), with
+per-M latencies from graphs of repeated single calls; the two-call path
+(quantize, then the fused kernel) is measured beside it.
 
 `--workload prefill32k` measures the long-prefill workload: the chain at
 32,768 tokens (X Student-t, nu = 3; positions 0..32767) and the standalone
@@ -98,6 +99,14 @@ def measured_traffic(kernel):
     if fields.get(f"{kernel}_kernel_source_sha256_16") != digest:
         return None
     return int(fields[f"{kernel}_traffic_bytes_per_launch"])
+
+
+def one_launch_bytes(M):
+    """Algorithmic HBM bytes of one one-launch call: bf16 X, W + its scales,
+    positions, the table rows read, and the FP4 codes + scales written."""
+    nkb = K_PROJ // 128
+    return (M * K_PROJ * 2 + N_HEADS * HEAD_DIM * K_PROJ + N_HEADS * nkb + M * 8 + M * 64 * 4
+            + M * N_HEADS * (HEAD_DIM // 2 + HEAD_DIM // 32))
 
 
 def epilogue_bytes(M, H=N_HEADS):
@@ -510,11 +519,21 @@ def decode_bench(args):
             "qs": torch.empty((m, N_HEADS, HEAD_DIM // 32), dtype=torch.uint8, device=dev),
         })
 
-    def one(c):
+    def two(c):
+        # two calls: quantize, then the fused projection
         iqp.fp8_quant_1x128_ue8m0(c["x"], q=c["a"], scales=c["as"])
         iqp.indexer_q_gemm_rope_fp4(c["a"], c["as"], w, wsb, c["pos"], cs, n_heads=N_HEADS,
                                     q_fp4=c["q"], q_scales=c["qs"])
         iqp.fp8_quant_1x128_ue8m0(c["xw"], q=c["aw"], scales=c["asw"])
+
+    def one(c):
+        # one launch from bf16 X to FP4 Q
+        iqp.indexer_q_prep_bf16(c["x"], w, wsb, c["pos"], cs, n_heads=N_HEADS, q_fp4=c["q"], q_scales=c["qs"])
+        iqp.fp8_quant_1x128_ue8m0(c["xw"], q=c["aw"], scales=c["asw"])
+
+    def routed(c):
+        # the serving policy: one launch up to ONE_LAUNCH_MAX_TOKENS tokens, two calls above
+        (one if c["M"] <= iqp.ONE_LAUNCH_MAX_TOKENS else two)(c)
 
     def graph_of(fn):
         side = torch.cuda.Stream()
@@ -541,36 +560,47 @@ def decode_bench(args):
         return e0.elapsed_time(e1) * 1e-3 / reps    # s per replay
 
     for c in calls:
+        two(c)
         one(c)
     torch.cuda.synchronize()
     print(f"[bench] decode mix: {len(calls)} calls, M histogram "
           f"{ {int(m): int(n) for m, n in zip(*np.unique([c['M'] for c in calls], return_counts=True))} }",
           file=sys.stderr, flush=True)
 
-    # sustained: the whole mix as one graph
-    g_all = graph_of(lambda: [one(c) for c in calls])
+    # sustained: the whole mix as one graph, one-launch path and two-call path
     reps = max(5, args.steps // 20)
-    t_mix = replay_time(g_all, reps)
+    t_mix = replay_time(graph_of(lambda: [routed(c) for c in calls]), reps)
+    t_mix1 = replay_time(graph_of(lambda: [one(c) for c in calls]), reps)
+    t_mix2 = replay_time(graph_of(lambda: [two(c) for c in calls]), reps)
     calls_per_s = len(calls) / t_mix
+    print(f"[bench] mix: {calls_per_s:.0f} calls/s routed (one launch up to {iqp.ONE_LAUNCH_MAX_TOKENS} tokens), "
+          f"{len(calls) / t_mix1:.0f} one launch, {len(calls) / t_mix2:.0f} two calls", file=sys.stderr, flush=True)
 
-    # per-M latency of one call (quantize + fused + wide quantize), and of the fused kernel alone
-    lat, lat_fused = {}, {}
+    # per-M latency of one call (the indexer-Q preparation + the wide quantization),
+    # and of the indexer-Q kernel(s) alone
+    lat, lat2, lat_k, lat_k2 = {}, {}, {}, {}
     n_rep = 20
     for m in sorted({c["M"] for c in calls}):
         c = next(c for c in calls if c["M"] == m)
         lat[m] = replay_time(graph_of(lambda: [one(c) for _ in range(n_rep)]), 5) / n_rep * 1e6
-        lat_fused[m] = replay_time(graph_of(lambda: [iqp.indexer_q_gemm_rope_fp4(
+        lat2[m] = replay_time(graph_of(lambda: [two(c) for _ in range(n_rep)]), 5) / n_rep * 1e6
+        lat_k[m] = replay_time(graph_of(lambda: [iqp.indexer_q_prep_bf16(
+            c["x"], w, wsb, c["pos"], cs, n_heads=N_HEADS, q_fp4=c["q"], q_scales=c["qs"])
+            for _ in range(n_rep)]), 5) / n_rep * 1e6
+        lat_k2[m] = replay_time(graph_of(lambda: [iqp.indexer_q_gemm_rope_fp4(
             c["a"], c["as"], w, wsb, c["pos"], cs, n_heads=N_HEADS, q_fp4=c["q"], q_scales=c["qs"])
             for _ in range(n_rep)]), 5) / n_rep * 1e6
-        print(f"[bench] M={m}: call {lat[m]:.2f} us, fused kernel {lat_fused[m]:.2f} us",
-              file=sys.stderr, flush=True)
-    per_call = np.array([lat[c["M"]] for c in calls])
-    # the fused kernel reads all of W (and its scales) once per call, which
-    # dominates its algorithmic bytes at these sizes: its bound is HBM
-    mix_bytes = float(sum(fused_bytes(c["M"]) for c in calls))
-    mix_fused_s = float(sum(lat_fused[c["M"]] for c in calls)) * 1e-6
-    mean_fused = mix_fused_s / len(calls) * 1e6
-    achieved = mix_bytes / mix_fused_s / 1e9
+        print(f"[bench] M={m}: call {lat[m]:.2f} us one launch ({lat_k[m]:.2f} us kernel), "
+              f"{lat2[m]:.2f} us two calls ({lat_k2[m]:.2f} us fused kernel)", file=sys.stderr, flush=True)
+    per_call = np.array([(lat if c["M"] <= iqp.ONE_LAUNCH_MAX_TOKENS else lat2)[c["M"]] for c in calls])
+    per_call1 = np.array([lat[c["M"]] for c in calls])
+    per_call2 = np.array([lat2[c["M"]] for c in calls])
+    # the one-launch kernel reads bf16 X and all of W (and its scales) once per
+    # call; W dominates its algorithmic bytes at these sizes: its bound is HBM
+    mix_bytes = float(sum(one_launch_bytes(c["M"]) for c in calls))
+    mix_k_s = float(sum(lat_k[c["M"]] for c in calls)) * 1e-6
+    mean_k = mix_k_s / len(calls) * 1e6
+    achieved = mix_bytes / mix_k_s / 1e9
     result = {
         "metric": "decode-shaped indexer-Q calls/s (graph replay)",
         "value": calls_per_s,
@@ -586,16 +616,25 @@ def decode_bench(args):
         "data": "synthetic",
         "config": {
             "workload": "decode mix: 256 independent calls, M uniform over {1,2,4,8,16,32,64}; each call "
-                        "X bf16 [M,1536] -> FP8 quant -> fused GEMM + RoPE + Hadamard + FP4 (64 heads), "
-                        "plus a standalone FP8 quant of X' [M,7168]; positions U[0,131072)",
+                        "X bf16 [M,1536] -> FP8 quant -> GEMM + RoPE + Hadamard + FP4 (64 heads), one launch "
+                        "up to 16 tokens and two calls above, plus a standalone FP8 quant of X' [M,7168]; "
+                        "positions U[0,131072)",
             "calls": len(calls), "K": K_PROJ, "heads": N_HEADS, "head_dim": HEAD_DIM, "max_pos": max_pos,
             "parallelism": "single GPU",
         },
-        "latency_us": {"p50": float(np.percentile(per_call, 50)), "p99": float(np.percentile(per_call, 99)),
-                       "per_M_call": {str(k): v for k, v in lat.items()},
-                       "per_M_fused_kernel": {str(k): v for k, v in lat_fused.items()}},
+        "latency_us": {"p50": float(np.percentile(per_call, 50)), "p99": float(np.percentile(per_call, 99))},
+        "one_launch_path": {"calls_per_s": len(calls) / t_mix1,
+                            "p50_us": float(np.percentile(per_call1, 50)),
+                            "p99_us": float(np.percentile(per_call1, 99)),
+                            "per_M_call": {str(k): v for k, v in lat.items()},
+                            "per_M_kernel": {str(k): v for k, v in lat_k.items()}},
+        "two_call_path": {"calls_per_s": len(calls) / t_mix2,
+                          "p50_us": float(np.percentile(per_call2, 50)),
+                          "p99_us": float(np.percentile(per_call2, 99)),
+                          "per_M_call": {str(k): v for k, v in lat2.items()},
+                          "per_M_fused_kernel": {str(k): v for k, v in lat_k2.items()}},
         "roofline": {
-            "kernel": "indexer_q_small_kernel (fused GEMM + RoPE + Hadamard + FP4, M <= 256)",
+            "kernel": "indexer_q_small_kernel<bf16 in> (FP8 quant + GEMM + RoPE + Hadamard + FP4, M <= 256)",
             "bound": "hbm",
             "achieved": achieved,
             "peak": PEAK_HBM_GBS,
@@ -603,7 +642,7 @@ def decode_bench(args):
             "frac": achieved / PEAK_HBM_GBS,
             "traffic": None,
             "algorithmic_bytes_per_launch": mix_bytes / len(calls),
-            "avg_launch_us": mean_fused,
+            "avg_launch_us": mean_k,
         },
         "cpu_baseline": None,
     }

@@ -18,9 +18,13 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libiqprep.s
 
 __all__ = [
     "IqpError", "fp8_quant_1x128_ue8m0", "indexer_q_gemm_rope_fp4", "rope_cos_sin_table",
-    "debug_indexer_q_f32", "indexer_q_rope_hadamard_fp4", "indexer_q_prep", "abi_version", "library_path",
-    "IQP_OK", "IQP_ERR_INVALID", "IQP_ERR_UNSUPPORTED", "IQP_ERR_HIP",
+    "debug_indexer_q_f32", "indexer_q_rope_hadamard_fp4", "indexer_q_prep_bf16", "indexer_q_prep", "abi_version", "library_path",
+    "IQP_OK", "IQP_ERR_INVALID", "IQP_ERR_UNSUPPORTED", "IQP_ERR_HIP", "ONE_LAUNCH_MAX_TOKENS",
 ]
+
+#: Up to this many tokens indexer_q_prep takes the one-launch path (measured on
+#: MI355X: faster there; from 32 tokens the two calls are as fast or faster).
+ONE_LAUNCH_MAX_TOKENS = 16
 
 IQP_OK = 0
 IQP_ERR_INVALID = 1
@@ -42,6 +46,9 @@ def _load():
     lib.indexer_q_gemm_rope_fp4.restype = ctypes.c_int
     lib.iqp_debug_indexer_q_f32.argtypes = iq_args + [c_p, c_i32, c_p]
     lib.iqp_debug_indexer_q_f32.restype = ctypes.c_int
+    lib.indexer_q_prep_bf16.argtypes = [c_p, c_i64, c_p, c_i64, c_p, c_i64, c_i64, c_i32, c_i32, c_i32,
+                                         c_p, c_p, c_i64, c_p, c_p, c_p]
+    lib.indexer_q_prep_bf16.restype = ctypes.c_int
     lib.indexer_q_rope_hadamard_fp4.argtypes = [c_p, c_i64, c_i64, c_i32, c_i32, c_i32, c_p, c_p, c_i64,
                                                  c_p, c_p, c_p]
     lib.indexer_q_rope_hadamard_fp4.restype = ctypes.c_int
@@ -260,10 +267,56 @@ def rope_cos_sin_table(theta: float, max_pos: int, rope_dim: int = 64, device=No
     return out
 
 
+def indexer_q_prep_bf16(x, w, w_scales, positions, cos_sin, n_heads: int = 64, head_dim: int = 128,
+                        rope_dim: int = 64, q_fp4=None, q_scales=None, stream=None):
+    """The whole preparation in one launch for up to 256 tokens (K = 1536):
+    bf16 x [M, K] -> FP8 quantization (in the kernel, never stored) -> fused
+    projection / RoPE / Hadamard / FP4. Returns ``(q_fp4, q_scales)``."""
+    w = _bytes_u8(w)
+    dev = x.device
+    _require(x, "x", torch.bfloat16, dev, 2)
+    _require(w, "w", torch.uint8, dev, 2)
+    _require(w_scales, "w_scales", torch.uint8, dev, 2)
+    _require(positions, "positions", torch.int64, dev, 1)
+    _require(cos_sin, "cos_sin", torch.float32, dev, 2)
+    if x.stride(1) != 1 or w.stride(1) != 1 or not w_scales.is_contiguous() or not positions.is_contiguous() \
+            or not cos_sin.is_contiguous():
+        raise ValueError("x, w need contiguous rows; w_scales, positions, cos_sin must be contiguous")
+    M, K = x.shape
+    if w.shape[1] != K or w.shape[0] != n_heads * head_dim:
+        raise ValueError(f"w must be [{n_heads * head_dim}, {K}], got {tuple(w.shape)}")
+    if tuple(w_scales.shape) != (n_heads * head_dim // 128, K // 128):
+        raise ValueError(f"w_scales must be [{n_heads * head_dim // 128}, {K // 128}]")
+    if positions.shape[0] != M:
+        raise ValueError("positions needs one entry per token")
+    if cos_sin.shape[1] != rope_dim:
+        raise ValueError(f"cos_sin must have {rope_dim} columns")
+    if q_fp4 is None:
+        q_fp4 = torch.empty((M, n_heads, head_dim // 2), dtype=torch.uint8, device=dev)
+    if q_scales is None:
+        q_scales = torch.empty((M, n_heads, head_dim // 32), dtype=torch.uint8, device=dev)
+    _require(q_fp4, "q_fp4", torch.uint8, dev, 3)
+    _require(q_scales, "q_scales", torch.uint8, dev, 3)
+    if not (q_fp4.is_contiguous() and q_scales.is_contiguous()):
+        raise ValueError("q_fp4 and q_scales must be contiguous")
+    if tuple(q_fp4.shape) != (M, n_heads, head_dim // 2) or tuple(q_scales.shape) != (M, n_heads, head_dim // 32):
+        raise ValueError("q_fp4 / q_scales have the wrong shape")
+    st = _lib.indexer_q_prep_bf16(_ptr(x), x.stride(0), _ptr(w), w.stride(0), _ptr(w_scales), M, K, n_heads,
+                                  head_dim, rope_dim, _ptr(positions), _ptr(cos_sin), cos_sin.shape[0],
+                                  _ptr(q_fp4), _ptr(q_scales), _stream(x, stream))
+    _check(st, "indexer_q_prep_bf16")
+    return q_fp4, q_scales
+
+
 def indexer_q_prep(x, w, w_scales, positions, cos_sin, n_heads: int = 64, stream=None):
-    """The whole indexer-Q preparation for a bf16 [M, 1536] activation batch:
-    FP8 quantization, then the fused projection / RoPE / Hadamard / FP4 call,
-    both on one stream. Returns ``(q_fp4, q_scales)``."""
+    """The whole indexer-Q preparation for a bf16 [M, K] activation batch:
+    up to ONE_LAUNCH_MAX_TOKENS tokens at K = 1536 the one-launch call, else
+    FP8 quantization then the fused projection / RoPE / Hadamard / FP4 call,
+    both on one stream. Returns ``(q_fp4, q_scales)``; the paths give the same
+    bytes."""
+    if (1 <= x.shape[0] <= ONE_LAUNCH_MAX_TOKENS and x.dim() == 2 and x.shape[1] == 1536
+            and x.data_ptr() % 16 == 0 and x.stride(0) % 8 == 0 and w_scales.data_ptr() % 4 == 0):
+        return indexer_q_prep_bf16(x, w, w_scales, positions, cos_sin, n_heads=n_heads, stream=stream)
     a, a_scales = fp8_quant_1x128_ue8m0(x, stream=stream)
     return indexer_q_gemm_rope_fp4(a, a_scales, w, w_scales, positions, cos_sin, n_heads=n_heads,
                                    stream=stream)

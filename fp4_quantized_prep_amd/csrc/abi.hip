@@ -133,6 +133,41 @@ int indexer_q_gemm_rope_fp4(const void* a, int64_t lda, const int32_t* a_scales,
   return from_hip(iqp::launch_indexer_q(p, -1, static_cast<hipStream_t>(stream)));
 }
 
+int indexer_q_prep_bf16(const void* x, int64_t ldx, const void* w, int64_t ldw, const uint8_t* w_scales,
+                        int64_t M, int64_t K, int32_t H, int32_t D, int32_t rope_dim,
+                        const int64_t* positions, const float* cos_sin, int64_t max_pos,
+                        uint8_t* q_fp4, uint8_t* q_scales, void* stream) {
+  if (M < 0 || K < 0 || H < 0 || D < 0 || rope_dim < 0 || max_pos < 0) return IQP_ERR_INVALID;
+  if (M == 0) return IQP_OK;
+  if (!x || !w || !w_scales || !positions || !cos_sin || !q_fp4 || !q_scales) return IQP_ERR_INVALID;
+  if (K == 0 || H == 0 || max_pos == 0) return IQP_ERR_INVALID;
+  if (ldx < K || ldw < K) return IQP_ERR_INVALID;
+  if (K != 1536 || M > 256 || D != 128 || rope_dim != 64) return IQP_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || ldx % 8 || !aligned(w, 16) || ldw % 16 || !aligned(w_scales, 4) ||
+      !aligned(positions, 8) || !aligned(cos_sin, 16) || !aligned(q_fp4, 16) || !aligned(q_scales, 4))
+    return IQP_ERR_UNSUPPORTED;
+  if ((int64_t)H * 128 > ((int64_t)1 << 31) || H > 65535 || ldw >= ((int64_t)1 << 22))
+    return IQP_ERR_UNSUPPORTED;
+  const int st = device_status();
+  if (st != IQP_OK) return st;
+  iqp::IndexerQArgs p{};
+  p.x = static_cast<const uint16_t*>(x);
+  p.ldx = ldx;
+  p.w = static_cast<const uint8_t*>(w);
+  p.ldw = ldw;
+  p.w_scales = w_scales;
+  p.M = M;
+  p.nkb = (int32_t)(K / 128);
+  p.H = H;
+  p.positions = positions;
+  p.cos_sin = cos_sin;
+  p.max_pos = max_pos;
+  p.q_fp4 = q_fp4;
+  p.q_scales = q_scales;
+  if (!iqp::indexer_q_small_bf16_supported(p)) return IQP_ERR_UNSUPPORTED;
+  return from_hip(iqp::launch_indexer_q_small_bf16(p, static_cast<hipStream_t>(stream)));
+}
+
 int iqp_debug_indexer_q_f32(const void* a, int64_t lda, const int32_t* a_scales, int64_t as_stride_m,
                             int64_t as_stride_w, const void* w, int64_t ldw, const uint8_t* w_scales,
                             int64_t M, int64_t K, int32_t H, int32_t D, int32_t rope_dim,

@@ -37,8 +37,19 @@
 // Tokens past M: their LDS rows are never written (no copy reaches them) and
 // their results are never stored; an MFMA column depends on its own token's
 // row only, so whatever those rows hold stays in columns that are dropped.
+//
+// One-launch variant (XIN): the workgroup takes bf16 activations and
+// quantizes its own rows (the packed-UE8M0 FP8 1x128 rule, with the
+// standalone quantizer's arithmetic) straight into the LDS layout above,
+// while the weight ring fills: the rows are loaded into registers first,
+// then the ring's copies are issued, then the blocks are quantized (8 lanes a
+// block). The blocks' scale bytes cross waves through LDS; all 160 KiB are
+// in use, so the ring's seventh block is issued after that exchange and the
+// exchange borrows its stage (the blocks keep their issue order, so the K
+// loop's wait counts hold).
 #include <type_traits>
 
+#include "fp8_block.h"
 #include "iq_common.h"
 
 namespace iqp {
@@ -78,6 +89,9 @@ __device__ __forceinline__ void static_for(F&& f) {
 // LDS byte of 16-byte chunk c (0..95) of activation row r
 __device__ __forceinline__ uint32_t a_slot(int r, int c) { return (uint32_t)(r * KROW + 16 * (c ^ (r & 15))); }
 
+constexpr int XSTEPS = TILE * NKB / 32;      // one-launch variant: 32 blocks per step, up to 12 steps
+
+template <bool XIN>
 __global__ __launch_bounds__(NTHREADS, 1)
 void indexer_q_small_kernel(IndexerQArgs pa) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
@@ -88,20 +102,45 @@ void indexer_q_small_kernel(IndexerQArgs pa) {
   // the column tile's tokens: the batch seen from token t0 on
   const int64_t t0 = TILE * (int64_t)blockIdx.y;
   IndexerQArgs p = pa;
-  p.a += t0 * p.lda;
-  p.a_scale_bytes += 4 * t0 * p.as_sm;
+  if constexpr (XIN) {
+    p.x += t0 * p.ldx;
+  } else {
+    p.a += t0 * p.lda;
+    p.a_scale_bytes += 4 * t0 * p.as_sm;
+  }
   p.positions += t0;
   p.q_fp4 += t0 * p.H * (HEAD_DIM / 2);
   p.q_scales += t0 * p.H * 4;
   p.M = pa.M - t0 < TILE ? pa.M - t0 : TILE;
   const int M = (int)p.M;   // 1 .. 32
 
+  // 1x. (one-launch variant) the tile's bf16 rows into registers: block
+  //     b = 12 r + j (row r, K block j) is step b / 32, wave b / 8 % 4, lanes
+  //     8 (b % 8) .. +7 of it, 16 values a lane; steps past the tile's 12 M
+  //     blocks are not loaded, lanes past them reload the last block.
+  fp8q::v4u xa[XSTEPS], xb[XSTEPS];
+  const int nblk = NKB * M;
+  const int nsteps = (nblk + 31) / 32;
+  if constexpr (XIN) {
+#pragma unroll
+    for (int s = 0; s < XSTEPS; ++s) {
+      if (s < nsteps) {
+        const int b = min(32 * s + 8 * wave + (lane >> 3), nblk - 1);
+        const int r = b / NKB, j = b - NKB * r;
+        const fp8q::v4u* src = reinterpret_cast<const fp8q::v4u*>(p.x + (int64_t)r * p.ldx + KB * j + 16 * (lane & 7));
+        xa[s] = src[0];
+        xb[s] = src[1];
+      }
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
   // 1. the activation rows into LDS: slab k covers LDS bytes [1 KiB k, 1 KiB
   //    (k + 1)); its lane i fills byte 1 KiB k + 16 i, which is slot
   //    (1 KiB k + 16 i) % 1536 / 16 of row (1 KiB k + 16 i) / 1536 and holds
   //    that row's chunk slot ^ (row % 16). Slabs past the tile's rows are
   //    skipped; rows past M inside the last one read zeros (bounds check).
-  {
+  if constexpr (!XIN) {
     const rsrc_t ra = make_rsrc(p.a, (uint64_t)M * p.lda);
     const int nslab = (M * KROW + SLAB - 1) / SLAB;
     for (int k = wave; k < nslab; k += NWAVES) {
@@ -113,9 +152,10 @@ void indexer_q_small_kernel(IndexerQArgs pa) {
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // 2. the lane's token scale words (token lane % 32, clamped into the tile)
+  // 2. the lane's token scale words (token lane % 32, clamped into the tile);
+  //    the one-launch variant forms them from its own blocks below
   uint32_t asw[3];
-  {
+  if constexpr (!XIN) {
     const int t = (lane & 31) < M ? (lane & 31) : M - 1;
     const uint32_t* w = reinterpret_cast<const uint32_t*>(p.a_scale_bytes) + (int64_t)t * p.as_sm;
 #pragma unroll
@@ -156,15 +196,49 @@ void indexer_q_small_kernel(IndexerQArgs pa) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(ring + (j % NST) * WSTAGE + SLAB * c - KB * j), 16,
                                                wv[c], 0, KB * j, 0);
   };
-  static_for<0, NST>([&](auto jc) __attribute__((always_inline)) { copies(jc); });
-  __builtin_amdgcn_sched_barrier(0);
-  // the activation copies, scale words and position were issued before the
-  // ring's first copies: once only those may be outstanding, they have landed
-  {
+  if constexpr (!XIN) {
+    static_for<0, NST>([&](auto jc) __attribute__((always_inline)) { copies(jc); });
+    __builtin_amdgcn_sched_barrier(0);
+    // the activation copies, scale words and position were issued before the
+    // ring's first copies: once only those may be outstanding, they have landed
     constexpr int WAIT = waitcnt_vm(4 * NST);
     __builtin_amdgcn_s_waitcnt(WAIT);
+    block_barrier();
+  } else {
+    // the ring's first NST - 1 blocks; the last stage of wave 0's ring holds
+    // the scale-byte exchange (byte 12 r + j: row r, block j) until its block
+    // is issued
+    static_for<0, NST - 1>([&](auto jc) __attribute__((always_inline)) { copies(jc); });
+    __builtin_amdgcn_sched_barrier(0);
+    uint8_t* const xch = lds + W_OFF + (NST - 1) * WSTAGE;
+    {
+      constexpr int WAIT = waitcnt_vm(4 * (NST - 1));   // the rows and the position have landed
+      __builtin_amdgcn_s_waitcnt(WAIT);
+    }
+#pragma unroll
+    for (int s = 0; s < XSTEPS; ++s) {
+      if (s < nsteps) {
+        const int b = 32 * s + 8 * wave + (lane >> 3);
+        const int e = fp8q::block_exponent(fp8q::lanes8_max(fp8q::mag16(xa[s], xb[s])));
+        const fp8q::v4u codes = fp8q::codes16(xa[s], xb[s], e);
+        if (b < nblk) {
+          const int r = b / NKB, j = b - NKB * r;
+          *reinterpret_cast<fp8q::v4u*>(lds + a_slot(r, 8 * j + (lane & 7))) = codes;
+          if ((lane & 7) == 0) xch[b] = (uint8_t)(e + 127);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);   // this wave's LDS writes are done
+    block_barrier();
+    // token lane % 32's twelve bytes (rows past M: never written, columns dropped)
+    const uint32_t* xw = reinterpret_cast<const uint32_t*>(xch + NKB * (lane & 31));
+#pragma unroll
+    for (int k = 0; k < 3; ++k) asw[k] = xw[k];
+    __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);
+    block_barrier();   // every wave has its words: the stage may be refilled
+    copies(std::integral_constant<int, NST - 1>{});
+    __builtin_amdgcn_sched_barrier(0);
   }
-  block_barrier();
 
   // 4. the K loop: block j's weights are in stage j % NST once only the
   //    copies of the blocks after it may be outstanding (and the 4 RoPE row
@@ -333,7 +407,20 @@ bool indexer_q_small_supported(const IndexerQArgs& a) {
 
 hipError_t launch_indexer_q_small(const IndexerQArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)a.H, (unsigned)((a.M + small::TILE - 1) / small::TILE)), block(small::NTHREADS);
-  hipLaunchKernelGGL(small::indexer_q_small_kernel, grid, block, 0, stream, a);
+  hipLaunchKernelGGL(small::indexer_q_small_kernel<false>, grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+// bf16 rows are addressed through 64-bit pointers (16-byte loads)
+bool indexer_q_small_bf16_supported(const IndexerQArgs& a) {
+  return a.nkb == small::NKB && a.M >= 1 && a.M <= small::TILE * small::MAX_TILES && a.x != nullptr &&
+         (reinterpret_cast<uintptr_t>(a.x) & 15) == 0 && a.ldx % 8 == 0 && a.ldw <= (1 << 22) &&
+         (reinterpret_cast<uintptr_t>(a.w_scales) & 3) == 0;
+}
+
+hipError_t launch_indexer_q_small_bf16(const IndexerQArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)a.H, (unsigned)((a.M + small::TILE - 1) / small::TILE)), block(small::NTHREADS);
+  hipLaunchKernelGGL(small::indexer_q_small_kernel<true>, grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

@@ -24,6 +24,8 @@ struct IndexerQArgs {
   uint8_t* q_fp4;                // [M, H, 64]
   uint8_t* q_scales;             // [M, H, 4]
   float* dbg;                    // [M, H*128] for the diagnostic stages
+  const uint16_t* x;             // bf16 activations [M, K], row stride ldx elements (one-launch small path)
+  int64_t ldx;
   int32_t chunks;                // token chunks per head pair (set by the launcher)
 };
 
@@ -43,6 +45,10 @@ hipError_t launch_indexer_q_pipe(const IndexerQArgs& args, hipStream_t stream);
 // tokens, weight scales 4-byte aligned
 bool indexer_q_small_supported(const IndexerQArgs& args);
 hipError_t launch_indexer_q_small(const IndexerQArgs& args, hipStream_t stream);
+// the same kernel quantizing bf16 activations (args.x, args.ldx) itself: one
+// launch from X to FP4 Q; K = 1536, 1 to 256 tokens
+bool indexer_q_small_bf16_supported(const IndexerQArgs& args);
+hipError_t launch_indexer_q_small_bf16(const IndexerQArgs& args, hipStream_t stream);
 
 // standalone epilogue: bf16 Q [M, H*128] (row stride ldq elements) -> RoPE,
 // Hadamard-128, FP4 codes [M, H, 64] and scale bytes [M, H, 4]

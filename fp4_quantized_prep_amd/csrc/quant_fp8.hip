@@ -23,54 +23,14 @@
 //     on MI355X at [4632, 7168], 19.1 us against 22.0 us for cached 16-byte
 //     loads and 8-byte stores, and a plain device copy of the same input
 //     runs at 5.05 TB/s.
+#include "fp8_block.h"
 #include "iqp_internal.h"
 
 namespace iqp {
 namespace {
 
 constexpr int QWAVES = 4;  // waves per workgroup, two scale words each
-
-// DPP controls (gfx9 encoding)
-constexpr int DPP_QUAD_XOR1 = 0xB1;     // quad_perm [1,0,3,2]
-constexpr int DPP_QUAD_XOR2 = 0x4E;     // quad_perm [2,3,0,1]
-constexpr int DPP_ROW_HALF_MIRROR = 0x141;
-
-typedef unsigned v4u __attribute__((ext_vector_type(4)));
-
-// maximum over each group of 8 lanes (a block)
-__device__ __forceinline__ uint32_t lanes8_max(uint32_t v) {
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, DPP_QUAD_XOR1, 0xF, 0xF, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, DPP_QUAD_XOR2, 0xF, 0xF, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, DPP_ROW_HALF_MIRROR, 0xF, 0xF, false));
-  return v;
-}
-
-// Largest |bf16| of the two halves of a dword, as 15-bit magnitude codes.
-__device__ __forceinline__ uint32_t mag2(uint32_t d) {
-  return max(d & 0x7FFFu, (d >> 16) & 0x7FFFu);
-}
-
-// Scale exponent from the bf16 magnitude code of the block amax:
-// e = max(ceil(log2(amax / 448)), -22). With amax = (1 + f/128) 2^(E-127) and
-// 448 = (1 + 96/128) 2^8, amax/448 <= 2^(E-135) exactly when f <= 96. E = 0
-// (zero or subnormal amax) lands on the floor.
-__device__ __forceinline__ int block_exponent(uint32_t amag) {
-  const int E = (int)(amag >> 7);
-  const int f = (int)(amag & 0x7F);
-  const int e = E - 135 + (f > 96 ? 1 : 0);
-  return max(e, -22);
-}
-
-__device__ __forceinline__ uint32_t cvt4(uint32_t d0, uint32_t d1, float mul) {
-  // bf16 -> f32 is a 16-bit shift; element 2k is the low half of dword k
-  const float f0 = __uint_as_float(d0 << 16) * mul;
-  const float f1 = __uint_as_float(d0 & 0xFFFF0000u) * mul;
-  const float f2 = __uint_as_float(d1 << 16) * mul;
-  const float f3 = __uint_as_float(d1 & 0xFFFF0000u) * mul;
-  int r = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false);
-  r = __builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, r, true);
-  return (uint32_t)r;
-}
+using namespace fp8q;
 
 // Word index i (row-major over [M, nw]) of the whole tensor goes to half-wave
 // i % 2 of wave i / 2.
@@ -95,12 +55,8 @@ void fp8_quant_1x128_kernel(const uint16_t* __restrict__ x, int64_t ldx,
     a = __builtin_nontemporal_load(src);
     b = __builtin_nontemporal_load(src + 1);
   }
-  uint32_t m = max(max(max(mag2(a[0]), mag2(a[1])), max(mag2(a[2]), mag2(a[3]))),
-                   max(max(mag2(b[0]), mag2(b[1])), max(mag2(b[2]), mag2(b[3]))));
-  m = lanes8_max(m);
-  const int e = block_exponent(m);
-  const float mul = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, a normal float
-  const v4u o = v4u{cvt4(a[0], a[1], mul), cvt4(a[2], a[3], mul), cvt4(b[0], b[1], mul), cvt4(b[2], b[3], mul)};
+  const int e = block_exponent(lanes8_max(mag16(a, b)));
+  const v4u o = codes16(a, b, e);
   if (valid) __builtin_nontemporal_store(o, reinterpret_cast<v4u*>(q + row * ldq + (int64_t)w * 512 + l32 * 16));
 
   // the four block bytes of each half-wave's word

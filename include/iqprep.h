@@ -15,6 +15,8 @@
  *      the Q preparation).
  *   3. indexer_q_rope_hadamard_fp4   the same RoPE / Hadamard / FP4 epilogue as
  *      a standalone launch over a bf16 Q (the unfused chain's second half).
+ *   4. indexer_q_prep_bf16   calls 1 and 2 as one launch for decode-sized
+ *      batches (up to 256 tokens).
  *
  * Conventions shared by every entry point:
  *
@@ -150,6 +152,34 @@ int indexer_q_gemm_rope_fp4(const void* a, int64_t lda,
                             const float* cos_sin, int64_t max_pos,
                             uint8_t* q_fp4, uint8_t* q_scales,
                             void* stream);
+
+/*
+ * indexer_q_prep_bf16 — the whole indexer-Q preparation in one launch for
+ * decode-sized batches: bf16 activations in, packed FP4 Q and scales out.
+ *
+ * tokenspeed PR "perf(deepseek-v4): accelerate indexer Q and packed FP8
+ * quantization", Summary and Perf (small shapes are kept off the multi-launch
+ * path); TensorRT-LLM PR "Fuse DeepSeek-V4 Indexer Q projection with CuTe
+ * DSL", kernel routing (a dedicated small-M route) and sequence diagram (FP8
+ * quantization of the input, then the GEMM with the RoPE / FP4 epilogue).
+ *
+ * Computes exactly fp8_quant_1x128_ue8m0 on x followed by
+ * indexer_q_gemm_rope_fp4 on its result (the same codes, scales and
+ * rounding), without writing the FP8 activations anywhere.
+ *
+ *   x          bf16 [M, K], row stride ldx (elements, >= K); 16-byte aligned
+ *              and ldx a multiple of 8.
+ *   w, ldw, w_scales, H, D, rope_dim, positions, cos_sin, max_pos, q_fp4,
+ *   q_scales   as in indexer_q_gemm_rope_fp4 (w_scales 4-byte aligned here).
+ *   M          0 (no-op) to 256 tokens; K must be 1536; ldw below 2^22 bytes;
+ *              H <= 65535. Anything else is IQP_ERR_UNSUPPORTED: a caller
+ *              with more tokens uses the two calls above.
+ */
+int indexer_q_prep_bf16(const void* x, int64_t ldx, const void* w, int64_t ldw,
+                        const uint8_t* w_scales,
+                        int64_t M, int64_t K, int32_t H, int32_t D, int32_t rope_dim,
+                        const int64_t* positions, const float* cos_sin, int64_t max_pos,
+                        uint8_t* q_fp4, uint8_t* q_scales, void* stream);
 
 /*
  * indexer_q_rope_hadamard_fp4 — the epilogue of indexer_q_gemm_rope_fp4 as a

@@ -26,7 +26,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert {"fp8_quant_1x128_ue8m0", "indexer_q_gemm_rope_fp4", "indexer_q_rope_hadamard_fp4",
-            "iqp_status_string", "iqp_abi_version"} <= set(names)
+            "indexer_q_prep_bf16", "iqp_status_string", "iqp_abi_version"} <= set(names)
 
 
 def test_library_exports_every_declared_symbol(iqp):
@@ -122,6 +122,30 @@ def test_epilogue_argument_checks(iqp):
     assert epilogue(iqp, cs=8) == uns
     assert epilogue(iqp, out=2) == uns
     assert epilogue(iqp, out=8) == uns                            # codes are stored 16 bytes at a time
+
+
+def prep(iqp, x=16, ldx=1536, w=16, ldw=1536, ws=16, M=4, K=1536, H=2, D=128, rd=64, pos=16, cs=16, mp=10,
+         out=16, sc=16):
+    return iqp._lib.indexer_q_prep_bf16(P(x), ldx, P(w), ldw, P(ws), M, K, H, D, rd, P(pos), P(cs), mp,
+                                        P(out), P(sc), None)
+
+
+def test_one_launch_argument_checks(iqp):
+    inv, uns = iqp.IQP_ERR_INVALID, iqp.IQP_ERR_UNSUPPORTED
+    assert prep(iqp, M=0, x=0) == iqp.IQP_OK
+    assert prep(iqp, M=-1) == inv
+    assert prep(iqp, x=0) == inv
+    assert prep(iqp, w=0) == inv
+    assert prep(iqp, out=0) == inv
+    assert prep(iqp, ldx=1535) == inv
+    assert prep(iqp, ldw=1024) == inv
+    assert prep(iqp, M=257) == uns                 # more tokens: the two-call path
+    assert prep(iqp, K=1024, ldx=1024, ldw=1024) == uns
+    assert prep(iqp, D=64) == uns
+    assert prep(iqp, x=8) == uns                   # bf16 rows must be 16-byte aligned
+    assert prep(iqp, ldx=1540) == uns
+    assert prep(iqp, ws=2) == uns                  # weight scales are read four at a time
+    assert prep(iqp, out=4) == uns
 
 
 def test_python_wrapper_rejects_wrong_dtypes(iqp):
