@@ -78,3 +78,37 @@ def fp8_quant_1x128_ue8m0(x) -> tuple:
     q = e4m3_encode_rne(x.astype(np.float64) * inv)
     scale_bytes = (e + 127).astype(np.uint8)
     return q.reshape(M, K), pack_scale_bytes(scale_bytes)
+
+
+WEIGHT_TILE = 128
+
+
+def fp8_quant_weight_128x128_ue8m0(w) -> tuple:
+    """Weight preparation: E4M3 codes with one UE8M0 scale per 128x128 tile.
+
+    The pages only say the Q projection is a block-scaled FP8 GEMM
+    (tokenspeed PR "perf(deepseek-v4): accelerate indexer Q and packed FP8
+    quantization", Summary; TensorRT-LLM PR "Fuse DeepSeek-V4 Indexer Q
+    projection with CuTe DSL", sequence diagram). Reading: DeepSeek-style
+    weights with one scale per 128x128 tile, the scale chosen by the same
+    steps as the activations' (amax over the tile, the 1e-4 floor, the
+    exact e = ceil(log2(amax / 448)), codes E4M3 RNE of w * 2^-e).
+
+    w: [N, K] bf16 values (as float32), N and K multiples of 128. Returns
+    ``(q, scales)``: uint8 codes [N, K] and uint8 scale bytes [N/128, K/128].
+    """
+    w = np.asarray(w, dtype=np.float32)
+    if w.ndim != 2:
+        raise ValueError("w must be 2-D")
+    N, K = w.shape
+    if N % WEIGHT_TILE or K % WEIGHT_TILE:
+        raise ValueError("N and K must be divisible by 128")
+    if not is_bf16_exact(w):
+        raise ValueError("w must hold bfloat16 values")
+    tiles = np.abs(w.astype(np.float64)).reshape(N // WEIGHT_TILE, WEIGHT_TILE, K // WEIGHT_TILE, WEIGHT_TILE)
+    amax = np.maximum(tiles.max(axis=(1, 3)), AMAX_FLOOR)              # [N/128, K/128]
+    e = ceil_log2_ratio(amax, E4M3_MAX)
+    inv = np.ldexp(1.0, -np.repeat(np.repeat(e, WEIGHT_TILE, axis=0), WEIGHT_TILE, axis=1))
+    q = e4m3_encode_rne(w.astype(np.float64) * inv)
+    return q.reshape(N, K), (e + 127).astype(np.uint8)
+

@@ -161,3 +161,69 @@ def test_rejects_bad_inputs():
         Q.fp8_quant_1x128_ue8m0(np.zeros((2, 100), np.float32))
     with pytest.raises(ValueError):
         Q.fp8_quant_1x128_ue8m0(np.full((1, 128), 1.0 + 2 ** -10, np.float32))
+
+
+# ----------------------------------------------------------------------------
+# Weight preparation: one UE8M0 scale per 128x128 tile
+# ----------------------------------------------------------------------------
+
+
+def S_bf16(x):
+    """float values rounded to bf16 (torch's RNE cast), returned as float32."""
+    return torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.bfloat16).float().numpy()
+
+
+def test_weight_quant_worked_example():
+    # Tile (0, 0): amax 3.0; 3/448 = 0.0067 lies in (2^-8, 2^-7], e = -7, byte
+    # 120. 3 * 2^7 = 384 = 1.5 * 2^8 -> 0x7C; 1.0 * 2^7 = 128 -> 0x70;
+    # bf16(0.1) = 0.10009765625, * 2^7 = 12.8125, between 12 (0x54) and 13
+    # (0x55), nearer 13 -> 0x55; -2^-7 * 2^7 = -1 -> 0xB8.
+    # Tile (0, 1): all zero -> amax floored to 1e-4, e = -22, byte 105.
+    # Tile (1, 0): amax 448 -> e = 0, byte 127; 448 -> 0x7E.
+    # Tile (1, 1): amax 450 (one bf16 step above 448) -> e = 1, byte 128;
+    # 450 / 2 = 225 between 224 (0x76) and 240 (0x77) -> 0x76.
+    w = np.zeros((256, 256), dtype=np.float32)
+    w[3, 7], w[100, 127], w[0, 0], w[127, 64] = 3.0, 1.0, np.float32(0.10009765625), -2.0 ** -7
+    w[128, 5] = 448.0
+    w[200, 200] = 450.0
+    q, s = Q.fp8_quant_weight_128x128_ue8m0(w)
+    assert s.tolist() == [[120, 105], [127, 128]]
+    assert (q[3, 7], q[100, 127], q[0, 0], q[127, 64]) == (0x7C, 0x70, 0x55, 0xB8)
+    assert q[128, 5] == 0x7E and q[200, 200] == 0x76
+    assert np.count_nonzero(q) == 6
+
+
+def test_weight_quant_tiles_are_independent_and_transpose():
+    rng = np.random.default_rng(11)
+    w = S_bf16(rng.standard_normal((256, 384)) * 0.02)
+    q, s = Q.fp8_quant_weight_128x128_ue8m0(w)
+    w2 = w.copy()
+    w2[130, 300] = 7.0          # tile (1, 2) only
+    q2, s2 = Q.fp8_quant_weight_128x128_ue8m0(w2)
+    diff_tiles = {(r // 128, c // 128) for r, c in zip(*np.nonzero(q2 != q))}
+    assert diff_tiles == {(1, 2)}
+    assert np.array_equal(np.argwhere(s2 != s), [[1, 2]])
+    # square tiles: quantizing the transpose gives the transposed result
+    qt, st = Q.fp8_quant_weight_128x128_ue8m0(np.ascontiguousarray(w.T))
+    assert np.array_equal(qt, q.T) and np.array_equal(st, s.T)
+
+
+def test_weight_quant_reduces_to_row_blocks_when_each_shares_the_tile_max():
+    # if every 1x128 block of a tile holds the tile's largest magnitude, the
+    # tile exponent equals every block exponent: the 128x128 result is the
+    # (independently pinned) 1x128 result
+    rng = np.random.default_rng(12)
+    w = S_bf16(rng.uniform(-1.0, 1.0, (256, 256)))
+    for r in range(256):
+        for jb in range(2):
+            w[r, 128 * jb + (r * 7 + jb) % 128] = 2.5 if (r // 128 + jb) % 2 else -2.5
+    q, s = Q.fp8_quant_weight_128x128_ue8m0(w)
+    q1, words = Q.fp8_quant_1x128_ue8m0(w)
+    b1 = Q.unpack_scale_words(words, 2)
+    assert np.array_equal(q, q1)
+    assert np.array_equal(np.repeat(s, 128, axis=0), b1)
+
+
+def test_weight_quant_rejects_ragged_shapes():
+    with pytest.raises(ValueError):
+        Q.fp8_quant_weight_128x128_ue8m0(np.zeros((128, 200), dtype=np.float32))
