@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libiqprep.s
 
 __all__ = [
     "IqpError", "fp8_quant_1x128_ue8m0", "indexer_q_gemm_rope_fp4", "rope_cos_sin_table",
-    "debug_indexer_q_f32", "indexer_q_rope_hadamard_fp4", "indexer_q_prep_bf16", "indexer_q_prep", "abi_version", "library_path",
+    "debug_indexer_q_f32", "indexer_q_rope_hadamard_fp4", "indexer_q_prep_bf16", "indexer_q_prep", "fp8_quant_weight_128x128_ue8m0", "abi_version", "library_path",
     "IQP_OK", "IQP_ERR_INVALID", "IQP_ERR_UNSUPPORTED", "IQP_ERR_HIP", "ONE_LAUNCH_MAX_TOKENS",
 ]
 
@@ -49,6 +49,8 @@ def _load():
     lib.indexer_q_prep_bf16.argtypes = [c_p, c_i64, c_p, c_i64, c_p, c_i64, c_i64, c_i32, c_i32, c_i32,
                                          c_p, c_p, c_i64, c_p, c_p, c_p]
     lib.indexer_q_prep_bf16.restype = ctypes.c_int
+    lib.fp8_quant_weight_128x128_ue8m0.argtypes = [c_p, c_i64, c_i64, c_i64, c_p, c_i64, c_p, c_i64, c_p]
+    lib.fp8_quant_weight_128x128_ue8m0.restype = ctypes.c_int
     lib.indexer_q_rope_hadamard_fp4.argtypes = [c_p, c_i64, c_i64, c_i32, c_i32, c_i32, c_p, c_p, c_i64,
                                                  c_p, c_p, c_p]
     lib.indexer_q_rope_hadamard_fp4.restype = ctypes.c_int
@@ -142,6 +144,32 @@ def fp8_quant_1x128_ue8m0(x: torch.Tensor, scale_layout: str = "k", q: torch.Ten
     st = _lib.fp8_quant_1x128_ue8m0(_ptr(x), M, K, x.stride(0), _ptr(q), q.stride(0), _ptr(scales),
                                     scales.stride(0), scales.stride(1), _stream(x, stream))
     _check(st, "fp8_quant_1x128_ue8m0")
+    return q, scales
+
+
+def fp8_quant_weight_128x128_ue8m0(w: torch.Tensor, q: torch.Tensor = None, scales: torch.Tensor = None,
+                                   stream=None):
+    """Weight preparation: bf16 w [N, K] (rows contiguous, N and K multiples
+    of 128) -> ``(q, scales)``: uint8 E4M3 codes [N, K] and uint8 UE8M0 bytes
+    [N/128, K/128], one per 128x128 tile (any row strides)."""
+    dev = w.device
+    _require(w, "w", torch.bfloat16, dev, 2)
+    if w.stride(1) != 1:
+        raise ValueError("w rows must be contiguous")
+    N, K = w.shape
+    if q is None:
+        q = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    q = _bytes_u8(q)
+    if scales is None:
+        scales = torch.empty((N // 128, K // 128), dtype=torch.uint8, device=dev)
+    _require(q, "q", torch.uint8, dev, 2)
+    _require(scales, "scales", torch.uint8, dev, 2)
+    if q.stride(1) != 1 or scales.stride(1) != 1 or tuple(q.shape) != (N, K) or \
+            tuple(scales.shape) != (N // 128, K // 128):
+        raise ValueError("q must be [N, K] and scales [N/128, K/128], rows contiguous")
+    st = _lib.fp8_quant_weight_128x128_ue8m0(_ptr(w), N, K, w.stride(0), _ptr(q), q.stride(0), _ptr(scales),
+                                             scales.stride(0), _stream(w, stream))
+    _check(st, "fp8_quant_weight_128x128_ue8m0")
     return q, scales
 
 

@@ -206,6 +206,21 @@ int indexer_q_rope_hadamard_fp4(const void* q, int64_t ldq, int64_t M, int32_t H
                                                  static_cast<hipStream_t>(stream)));
 }
 
+int fp8_quant_weight_128x128_ue8m0(const void* w, int64_t N, int64_t K, int64_t ldw, void* q, int64_t ldq,
+                                   uint8_t* scales, int64_t ld_scales, void* stream) {
+  if (N < 0 || K < 0) return IQP_ERR_INVALID;
+  if (N == 0 || K == 0) return IQP_OK;
+  if (!w || !q || !scales) return IQP_ERR_INVALID;
+  if (ldw < K || ldq < K || ld_scales < (K + 127) / 128) return IQP_ERR_INVALID;
+  if (N % 128 || K % 128) return IQP_ERR_UNSUPPORTED;
+  if (!aligned(w, 16) || ldw % 8 || !aligned(q, 8) || ldq % 8) return IQP_ERR_UNSUPPORTED;
+  if (N / 128 > 65535 || K / 128 > 0x7FFFFFFF) return IQP_ERR_UNSUPPORTED;
+  const int st = device_status();
+  if (st != IQP_OK) return st;
+  return from_hip(iqp::launch_fp8_quant_weight(static_cast<const uint16_t*>(w), N, K, ldw, static_cast<uint8_t*>(q),
+                                               ldq, scales, ld_scales, static_cast<hipStream_t>(stream)));
+}
+
 int iqp_rope_cos_sin_table(double theta, int64_t max_pos, int32_t rope_dim, float* cos_sin,
                            void* stream) {
   if (max_pos < 0 || rope_dim <= 0 || rope_dim % 2 || !(theta > 0.0)) return IQP_ERR_INVALID;

@@ -56,6 +56,10 @@ hipError_t launch_indexer_q_epilogue(const uint16_t* q, int64_t ldq, int64_t M, 
                                      const int64_t* positions, const float* cos_sin, int64_t max_pos,
                                      uint8_t* q_fp4, uint8_t* q_scales, hipStream_t stream);
 
+// weight preparation: bf16 [N, K] -> E4M3 [N, K] + UE8M0 [N/128, K/128]
+hipError_t launch_fp8_quant_weight(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q, int64_t ldq,
+                                   uint8_t* scales, int64_t ld_scales, hipStream_t stream);
+
 // compute units of the current device (cached per device)
 int cu_count();
 

@@ -17,6 +17,9 @@
  *      a standalone launch over a bf16 Q (the unfused chain's second half).
  *   4. indexer_q_prep_bf16   calls 1 and 2 as one launch for decode-sized
  *      batches (up to 256 tokens).
+ *   5. fp8_quant_weight_128x128_ue8m0   the weights' E4M3 codes and per-tile
+ *      scales that calls 2 and 4 take (weight preparation, off the
+ *      per-token path).
  *
  * Conventions shared by every entry point:
  *
@@ -214,6 +217,33 @@ int indexer_q_rope_hadamard_fp4(const void* q, int64_t ldq, int64_t M, int32_t H
                                 int32_t rope_dim, const int64_t* positions,
                                 const float* cos_sin, int64_t max_pos,
                                 uint8_t* q_fp4, uint8_t* q_scales, void* stream);
+
+/*
+ * fp8_quant_weight_128x128_ue8m0 — weight preparation: bf16 weights to the
+ * E4M3 codes and per-tile UE8M0 scales that indexer_q_gemm_rope_fp4 and
+ * indexer_q_prep_bf16 take as w / w_scales. Not on the per-token path: it
+ * runs when weights are loaded or updated.
+ *
+ * The pages only say the Q projection is a block-scaled FP8 GEMM (tokenspeed
+ * PR "perf(deepseek-v4): accelerate indexer Q and packed FP8 quantization",
+ * Summary; TensorRT-LLM PR "Fuse DeepSeek-V4 Indexer Q projection with CuTe
+ * DSL", sequence diagram); the weight format is a reading: one scale per
+ * 128x128 tile, chosen like the activations' scales. For every tile (a, b):
+ *   amax = max(max |w| over rows 128a.., columns 128b.., 1e-4)
+ *   e    = ceil(log2(amax / 448)) exact;  scales[a * ld_scales + b] = e + 127
+ *   q    = E4M3 round-to-nearest-even of w * 2^-e (never saturates)
+ *
+ *   w          bf16 [N, K], row stride ldw (elements, >= K); 16-byte aligned,
+ *              ldw a multiple of 8.
+ *   q          E4M3 bytes [N, K], row stride ldq (bytes, >= K); 8-byte
+ *              aligned, ldq a multiple of 8.
+ *   scales     uint8 [N/128, K/128], row stride ld_scales (bytes, >= K/128).
+ *   N, K       multiples of 128 (else IQP_ERR_UNSUPPORTED); N/128 <= 65535.
+ * Inputs must be finite.
+ */
+int fp8_quant_weight_128x128_ue8m0(const void* w, int64_t N, int64_t K, int64_t ldw,
+                                   void* q, int64_t ldq, uint8_t* scales, int64_t ld_scales,
+                                   void* stream);
 
 /*
  * iqp_rope_cos_sin_table — builds the standard RoPE table that

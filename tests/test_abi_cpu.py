@@ -26,7 +26,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert {"fp8_quant_1x128_ue8m0", "indexer_q_gemm_rope_fp4", "indexer_q_rope_hadamard_fp4",
-            "indexer_q_prep_bf16", "iqp_status_string", "iqp_abi_version"} <= set(names)
+            "indexer_q_prep_bf16", "fp8_quant_weight_128x128_ue8m0", "iqp_status_string",
+            "iqp_abi_version"} <= set(names)
 
 
 def test_library_exports_every_declared_symbol(iqp):
@@ -146,6 +147,26 @@ def test_one_launch_argument_checks(iqp):
     assert prep(iqp, ldx=1540) == uns
     assert prep(iqp, ws=2) == uns                  # weight scales are read four at a time
     assert prep(iqp, out=4) == uns
+
+
+def wq(iqp, w=16, N=256, K=384, ldw=384, q=16, ldq=384, s=16, lds=3):
+    return iqp._lib.fp8_quant_weight_128x128_ue8m0(P(w), N, K, ldw, P(q), ldq, P(s), lds, None)
+
+
+def test_weight_quant_argument_checks(iqp):
+    inv, uns = iqp.IQP_ERR_INVALID, iqp.IQP_ERR_UNSUPPORTED
+    assert wq(iqp, N=0, w=0) == iqp.IQP_OK
+    assert wq(iqp, N=-128) == inv
+    assert wq(iqp, w=0) == inv
+    assert wq(iqp, s=0) == inv
+    assert wq(iqp, ldw=256) == inv
+    assert wq(iqp, ldq=256) == inv
+    assert wq(iqp, lds=2) == inv
+    assert wq(iqp, N=200) == uns
+    assert wq(iqp, K=200, ldw=384, ldq=384, lds=2) == uns
+    assert wq(iqp, w=8) == uns
+    assert wq(iqp, ldw=388) == uns
+    assert wq(iqp, q=4) == uns
 
 
 def test_python_wrapper_rejects_wrong_dtypes(iqp):
