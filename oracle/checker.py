@@ -67,12 +67,17 @@ def dequant_fp4(packed, scale_bytes) -> np.ndarray:
     return vals * scale
 
 
-def check_fp4(q_dev, s_dev, z_ref, q_ref, s_ref) -> dict:
+def check_fp4(q_dev, s_dev, z_ref, q_ref, s_ref, scale_rule: str = "ceil") -> dict:
     """Apply the FP4 acceptance rule.
 
     q_dev / q_ref: packed codes [..., 64]; s_dev / s_ref: scale bytes [..., 4];
     z_ref: the oracle's float64 values before quantization [..., 128].
+    scale_rule: "ceil" (e = ceil(log2(amax / 6)): the exponent steps where
+    amax / 6 crosses a power of two) or "ocp_floor" (e = floor(log2 amax) - 2:
+    it steps where amax crosses a power of two).
     """
+    if scale_rule not in ("ceil", "ocp_floor"):
+        raise ValueError(scale_rule)
     q_dev = np.asarray(q_dev, dtype=np.uint8)
     q_ref = np.asarray(q_ref, dtype=np.uint8)
     s_dev = np.asarray(s_dev, dtype=np.uint8).astype(np.int64)
@@ -90,7 +95,7 @@ def check_fp4(q_dev, s_dev, z_ref, q_ref, s_ref) -> dict:
 
     # 2. scale bytes
     amax = np.maximum(np.abs(zb).max(axis=-1), FP4_AMAX_FLOOR)
-    ratio = amax / E2M1_MAX
+    ratio = amax / (E2M1_MAX if scale_rule == "ceil" else 4.0)
     nearest_pow2 = np.ldexp(1.0, np.round(np.log2(ratio)).astype(np.int64))
     near_boundary = np.abs(ratio / nearest_pow2 - 1.0) <= WINDOW
     s_diff = s_dev != s_ref

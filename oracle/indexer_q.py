@@ -110,6 +110,27 @@ def rope_half_split(q, positions, theta: float = 10000.0, rope_dim: int = 64) ->
     return out
 
 
+def rope_interleaved(q, positions, theta: float = 10000.0, rope_dim: int = 64) -> np.ndarray:
+    """The interleaved RoPE layout: pair i < rope_dim/2 is dims (2i, 2i + 1),
+    rotated by the same angle pos * theta^(-2i/rope_dim); dims rope_dim..D-1
+    are unchanged. q is [M, H, D] float64.
+
+    A convention variant: the pages leave the pair layout open (tokenspeed PR
+    "perf(deepseek-v4): accelerate indexer Q and packed FP8 quantization",
+    Summary, names only an MLA RoPE kernel); both common layouts are offered.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    ang = rope_angles(positions, theta, rope_dim)
+    c = np.cos(ang)[:, None, :]
+    s = np.sin(ang)[:, None, :]
+    out = q.copy()
+    x1 = q[..., 0:rope_dim:2]
+    x2 = q[..., 1:rope_dim:2]
+    out[..., 0:rope_dim:2] = x1 * c - x2 * s
+    out[..., 1:rope_dim:2] = x2 * c + x1 * s
+    return out
+
+
 # ----------------------------------------------------------------------------
 # Hadamard
 # ----------------------------------------------------------------------------
@@ -138,14 +159,22 @@ def hadamard_rotate(y) -> np.ndarray:
 # ----------------------------------------------------------------------------
 
 
-def fp4_quantize(z, decide_dtype=np.float32) -> tuple:
+def fp4_quantize(z, decide_dtype=np.float32, scale_rule: str = "ceil") -> tuple:
     """Quantize the last axis (a multiple of 32) in 32-element blocks.
 
     The scale and code decisions are taken on z rounded to ``decide_dtype``
     (float32 by default: the precision the device path holds z in); the
     decision itself is exact. Returns ``(packed, scale_bytes)``: packed codes
     [..., n/2] uint8 and scale bytes [..., n/32] uint8.
+
+    scale_rule "ceil" (the default reading): e = ceil(log2(amax / 6)), the
+    smallest power of two that keeps the block within E2M1's range, so codes
+    never saturate. "ocp_floor": the OCP MX rule, e = floor(log2 amax) - 2
+    (2 being E2M1's largest exponent), codes saturating at +-6. Both floor
+    amax at 1e-4 first.
     """
+    if scale_rule not in ("ceil", "ocp_floor"):
+        raise ValueError(scale_rule)
     z = np.asarray(z, dtype=np.float64)
     if decide_dtype is not None:
         z = z.astype(decide_dtype).astype(np.float64)
@@ -154,8 +183,12 @@ def fp4_quantize(z, decide_dtype=np.float32) -> tuple:
         raise ValueError("fp4_quantize: last axis must be a multiple of 32")
     blocks = z.reshape(z.shape[:-1] + (n // FP4_BLOCK, FP4_BLOCK))
     amax = np.maximum(np.abs(blocks).max(axis=-1), FP4_AMAX_FLOOR)
-    e = ceil_log2_ratio(amax, E2M1_MAX)
+    if scale_rule == "ceil":
+        e = ceil_log2_ratio(amax, E2M1_MAX)
+    else:
+        e = np.frexp(amax)[1].astype(np.int64) - 1 - 2     # frexp: amax = f 2^k, f in [0.5, 1)
     scaled = blocks * np.ldexp(1.0, -e)[..., None]
+    scaled = np.clip(scaled, -E2M1_MAX, E2M1_MAX)          # saturation (reached only by "ocp_floor")
     codes = e2m1_encode_rne(scaled).reshape(z.shape)
     return e2m1_pack(codes), (e + 127).astype(np.uint8)
 
@@ -166,21 +199,29 @@ def fp4_quantize(z, decide_dtype=np.float32) -> tuple:
 
 
 def indexer_q_epilogue(q, positions, n_heads: int = 64, head_dim: int = 128, rope_dim: int = 64,
-                       theta: float = 10000.0) -> dict:
+                       theta: float = 10000.0, rope_layout: str = "half_split",
+                       scale_rule: str = "ceil") -> dict:
     """RoPE, Hadamard rotation and FP4 quantization of an already projected Q.
 
     This is the unfused chain's epilogue (TensorRT-LLM PR "Fuse DeepSeek-V4
     Indexer Q projection with CuTe DSL", Description / Paths compared: the Q
     GEMM writes a bf16 Q that a RoPE kernel and an FP4 quantization kernel then
     consume). q is [M, H*D] (the bf16 values, widened exactly); the steps are
-    the same functions the fused chain applies after its GEMM.
+    the same functions the fused chain applies after its GEMM. rope_layout
+    ("half_split" or "interleaved") and scale_rule ("ceil" or "ocp_floor")
+    select the convention variants.
     """
     q = np.asarray(q, dtype=np.float64)
     M = q.shape[0]
     q = q.reshape(M, n_heads, head_dim)
-    q_rope = rope_half_split(q, positions, theta, rope_dim)
+    if rope_layout == "half_split":
+        q_rope = rope_half_split(q, positions, theta, rope_dim)
+    elif rope_layout == "interleaved":
+        q_rope = rope_interleaved(q, positions, theta, rope_dim)
+    else:
+        raise ValueError(rope_layout)
     z = hadamard_rotate(q_rope)
-    packed, scales = fp4_quantize(z)
+    packed, scales = fp4_quantize(z, scale_rule=scale_rule)
     return {"q_rope": q_rope, "z": z, "q_fp4": packed, "q_scales": scales}
 
 

@@ -349,3 +349,69 @@ def test_epilogue_heads_are_independent_and_match_the_chain_stages():
     # rotation and Hadamard preserve each head's norm
     np.testing.assert_allclose(np.linalg.norm(out["z"], axis=-1),
                                np.linalg.norm(q.reshape(M, H, 128), axis=-1), rtol=1e-13)
+
+
+# ----------------------------------------------------------------------------
+# Convention variants: interleaved RoPE pairs, OCP floor-rule FP4 scales
+# ----------------------------------------------------------------------------
+
+
+def test_rope_interleaved_closed_forms_and_invariants():
+    rng = np.random.default_rng(21)
+    q = rng.standard_normal((3, 2, 128))
+    pos = np.array([0, 5, 4000])
+    out = IQ.rope_interleaved(q, pos)
+    assert np.array_equal(out[0], q[0])                       # position 0: identity
+    assert np.array_equal(out[:, :, 64:], q[:, :, 64:])       # pass-through dims
+    n_in = q[..., 0:64:2] ** 2 + q[..., 1:64:2] ** 2
+    n_out = out[..., 0:64:2] ** 2 + out[..., 1:64:2] ** 2
+    np.testing.assert_allclose(n_out, n_in, rtol=1e-13)       # pair norms
+    # composition: rotating by p1 then p2 is rotating by p1 + p2
+    two = IQ.rope_interleaved(IQ.rope_interleaved(q, np.array([7, 7, 7])), np.array([11, 11, 11]))
+    np.testing.assert_allclose(two, IQ.rope_interleaved(q, np.array([18, 18, 18])), atol=1e-12)
+    # e_32 (pair i = 16) at position 1000: angle 1000 * 10000^(-32/64) = 10 rad onto dims (32, 33)
+    e = np.zeros((1, 1, 128))
+    e[0, 0, 32] = 1.0
+    r = IQ.rope_interleaved(e, np.array([1000]))
+    assert abs(r[0, 0, 32] - math.cos(10)) < 1e-12 and abs(r[0, 0, 33] - math.sin(10)) < 1e-12
+    assert np.count_nonzero(r) == 2
+    # and it is not the half-split layout
+    assert not np.allclose(r, IQ.rope_half_split(e, np.array([1000])))
+
+
+def test_fp4_ocp_floor_rule_worked_example():
+    # e = floor(log2 amax) - 2, codes saturate at 6:
+    #   block 0: amax 6 = 1.5 * 2^2 -> e = 0 (byte 127); 6 -> 7; 5 -> tie 4|6 -> even code 6 (4);
+    #            -0.25 -> tie 0|0.5 -> 0 (negative zero 8)
+    #   block 1: amax 7 -> e = 0 (byte 127); 7 saturates to 6 (code 7); 3 -> 5
+    #   block 2: amax 3.9 -> e = -1 (byte 126); 3.9 * 2 = 7.8 -> 6 (code 7); 1 * 2 = 2 -> 4
+    #   block 3: amax 1e-5, floored to 1e-4 = 1.6384 * 2^-14 -> e = -16 (byte 111);
+    #            1e-5 * 2^16 = 0.655 -> below the 0.5|1 midpoint 0.75 -> 0.5 (code 1)
+    z = np.zeros(128)
+    z[0], z[1], z[2] = 6.0, 5.0, -0.25
+    z[32], z[33] = 7.0, 3.0
+    z[64], z[65] = 3.9, 1.0
+    z[96] = 1e-5
+    packed, sb = IQ.fp4_quantize(z, scale_rule="ocp_floor")
+    assert sb.tolist() == [127, 127, 126, 111]
+    codes = F.e2m1_unpack(packed).tolist()
+    assert codes[0:3] == [7, 6, 8] and codes[32:34] == [7, 5] and codes[64:66] == [7, 4] and codes[96] == 1
+    # the default rule on the same block 1 never saturates: e = 1, 7/2 = 3.5 -> tie 3|4 -> 4 (code 6)
+    packed_c, sb_c = IQ.fp4_quantize(z)
+    assert sb_c[1] == 128 and F.e2m1_unpack(packed_c)[32] == 6
+
+
+def test_epilogue_variants_closed_forms():
+    # dim 0 at position 1, interleaved: (cos 1, sin 1) on dims (0, 1), so
+    # z_r = (cos 1 + (-1)^bit0(r) sin 1) / sqrt(128): 0.12213 at even r,
+    # -0.02662 at odd r, in every block.
+    #   ceil rule: e = -5 (byte 122); 3.908 -> 4 (code 6), -0.852 -> above the
+    #   0.5|1 midpoint -> -1 (code 0xA): bytes 0xA6
+    #   OCP floor: 0.12213 = 1.954 * 2^-4 -> e = -6 (byte 121); 7.82 -> 6 (code 7),
+    #   -1.704 -> below the 1.5|2 midpoint -> -1.5 (code 0xB): bytes 0xB7
+    q = np.zeros((1, 128))
+    q[0, 0] = 1.0
+    out = IQ.indexer_q_epilogue(q, np.array([1]), n_heads=1, rope_layout="interleaved")
+    assert out["q_scales"].tolist() == [[[122] * 4]] and out["q_fp4"].reshape(-1).tolist() == [0xA6] * 64
+    out = IQ.indexer_q_epilogue(q, np.array([1]), n_heads=1, rope_layout="interleaved", scale_rule="ocp_floor")
+    assert out["q_scales"].tolist() == [[[121] * 4]] and out["q_fp4"].reshape(-1).tolist() == [0xB7] * 64
