@@ -20,11 +20,15 @@ __all__ = [
     "IqpError", "fp8_quant_1x128_ue8m0", "indexer_q_gemm_rope_fp4", "rope_cos_sin_table",
     "debug_indexer_q_f32", "indexer_q_rope_hadamard_fp4", "indexer_q_prep_bf16", "indexer_q_prep", "fp8_quant_weight_128x128_ue8m0", "abi_version", "library_path",
     "IQP_OK", "IQP_ERR_INVALID", "IQP_ERR_UNSUPPORTED", "IQP_ERR_HIP", "ONE_LAUNCH_MAX_TOKENS",
+    "IQP_ROPE_INTERLEAVED", "IQP_FP4_SCALE_OCP_FLOOR",
 ]
 
 #: Up to this many tokens indexer_q_prep takes the one-launch path (measured on
 #: MI355X: faster there; from 32 tokens the two calls are as fast or faster).
 ONE_LAUNCH_MAX_TOKENS = 16
+
+IQP_ROPE_INTERLEAVED = 0x1
+IQP_FP4_SCALE_OCP_FLOOR = 0x2
 
 IQP_OK = 0
 IQP_ERR_INVALID = 1
@@ -52,7 +56,7 @@ def _load():
     lib.fp8_quant_weight_128x128_ue8m0.argtypes = [c_p, c_i64, c_i64, c_i64, c_p, c_i64, c_p, c_i64, c_p]
     lib.fp8_quant_weight_128x128_ue8m0.restype = ctypes.c_int
     lib.indexer_q_rope_hadamard_fp4.argtypes = [c_p, c_i64, c_i64, c_i32, c_i32, c_i32, c_p, c_p, c_i64,
-                                                 c_p, c_p, c_p]
+                                                 c_p, c_p, c_i32, c_p]
     lib.indexer_q_rope_hadamard_fp4.restype = ctypes.c_int
     lib.iqp_rope_cos_sin_table.argtypes = [c_dbl, c_i64, c_i32, c_p, c_p]
     lib.iqp_rope_cos_sin_table.restype = ctypes.c_int
@@ -247,10 +251,17 @@ def debug_indexer_q_f32(a, a_scales, w, w_scales, positions, cos_sin, stage: int
 
 
 def indexer_q_rope_hadamard_fp4(q, positions, cos_sin, n_heads: int = 64, head_dim: int = 128,
-                                rope_dim: int = 64, q_fp4=None, q_scales=None, stream=None):
+                                rope_dim: int = 64, q_fp4=None, q_scales=None, rope_layout: str = "half_split",
+                                scale_rule: str = "ceil", stream=None):
     """Standalone epilogue over a bf16 Q [M, H*128] (rows contiguous, any row
     stride): RoPE on each head's first 64 dims, Hadamard-128, FP4 e2m1.
-    Returns ``(q_fp4, q_scales)`` laid out as :func:`indexer_q_gemm_rope_fp4`'s."""
+    Returns ``(q_fp4, q_scales)`` laid out as :func:`indexer_q_gemm_rope_fp4`'s.
+    rope_layout "interleaved" pairs dims (2i, 2i+1); scale_rule "ocp_floor"
+    takes the OCP MX scale rule (codes saturate at 6)."""
+    if rope_layout not in ("half_split", "interleaved") or scale_rule not in ("ceil", "ocp_floor"):
+        raise ValueError("rope_layout must be 'half_split' or 'interleaved', scale_rule 'ceil' or 'ocp_floor'")
+    flags = (IQP_ROPE_INTERLEAVED if rope_layout == "interleaved" else 0) | \
+        (IQP_FP4_SCALE_OCP_FLOOR if scale_rule == "ocp_floor" else 0)
     dev = q.device
     _require(q, "q", torch.bfloat16, dev, 2)
     _require(positions, "positions", torch.int64, dev, 1)
@@ -275,7 +286,7 @@ def indexer_q_rope_hadamard_fp4(q, positions, cos_sin, n_heads: int = 64, head_d
     if tuple(q_fp4.shape) != (M, n_heads, head_dim // 2) or tuple(q_scales.shape) != (M, n_heads, head_dim // 32):
         raise ValueError("q_fp4 / q_scales have the wrong shape")
     st = _lib.indexer_q_rope_hadamard_fp4(_ptr(q), q.stride(0), M, n_heads, head_dim, rope_dim, _ptr(positions),
-                                          _ptr(cos_sin), cos_sin.shape[0], _ptr(q_fp4), _ptr(q_scales),
+                                          _ptr(cos_sin), cos_sin.shape[0], _ptr(q_fp4), _ptr(q_scales), flags,
                                           _stream(q, stream))
     _check(st, "indexer_q_rope_hadamard_fp4")
     return q_fp4, q_scales

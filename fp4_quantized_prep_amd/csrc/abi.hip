@@ -188,8 +188,10 @@ int iqp_debug_indexer_q_f32(const void* a, int64_t lda, const int32_t* a_scales,
 
 int indexer_q_rope_hadamard_fp4(const void* q, int64_t ldq, int64_t M, int32_t H, int32_t D,
                                 int32_t rope_dim, const int64_t* positions, const float* cos_sin,
-                                int64_t max_pos, uint8_t* q_fp4, uint8_t* q_scales, void* stream) {
+                                int64_t max_pos, uint8_t* q_fp4, uint8_t* q_scales, int32_t flags,
+                                void* stream) {
   if (M < 0 || H < 0 || D < 0 || rope_dim < 0 || max_pos < 0) return IQP_ERR_INVALID;
+  if (flags & ~(IQP_ROPE_INTERLEAVED | IQP_FP4_SCALE_OCP_FLOOR)) return IQP_ERR_INVALID;
   if (M == 0) return IQP_OK;
   if (!q || !positions || !cos_sin || !q_fp4 || !q_scales) return IQP_ERR_INVALID;
   if (H == 0 || max_pos == 0) return IQP_ERR_INVALID;
@@ -203,6 +205,8 @@ int indexer_q_rope_hadamard_fp4(const void* q, int64_t ldq, int64_t M, int32_t H
   if (st != IQP_OK) return st;
   return from_hip(iqp::launch_indexer_q_epilogue(static_cast<const uint16_t*>(q), ldq, M, H, positions,
                                                  cos_sin, max_pos, q_fp4, q_scales,
+                                                 (flags & IQP_ROPE_INTERLEAVED) != 0,
+                                                 (flags & IQP_FP4_SCALE_OCP_FLOOR) != 0,
                                                  static_cast<hipStream_t>(stream)));
 }
 

@@ -45,6 +45,15 @@ __device__ __forceinline__ float quad_xchg(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
+// FP4 block exponent by the OCP MX rule, e = max(floor(log2 amax), floor(log2 1e-4)) - 2,
+// from the float bits of amax >= 0 (floor(log2 1e-4) = -14)
+__device__ __forceinline__ int fp4_exponent_floor(float amax) {
+  return max((int)(__float_as_uint(amax) >> 23) - 129, -16);
+}
+
+// INTERLEAVED: RoPE pairs (2i, 2i + 1) instead of (i, i + 32); FLOOR: FP4
+// scales by the OCP MX rule (codes saturate at 6) instead of the ceil rule.
+template <bool INTERLEAVED, bool FLOOR>
 __global__ __launch_bounds__(EPI_THREADS)
 void indexer_q_epilogue_kernel(const uint16_t* __restrict__ q, int64_t ldq, int32_t H,
                                const int64_t* __restrict__ positions,
@@ -65,9 +74,11 @@ void indexer_q_epilogue_kernel(const uint16_t* __restrict__ q, int64_t ldq, int3
 
   int64_t pos = positions[m];
   pos = pos < 0 ? 0 : (pos >= max_pos ? max_pos - 1 : pos);
-  const float* cs = cos_sin + pos * 64 + 8 * j;
-  const v4f c0 = *reinterpret_cast<const v4f*>(cs), c1 = *reinterpret_cast<const v4f*>(cs + 4);
-  const v4f s0 = *reinterpret_cast<const v4f*>(cs + 32), s1 = *reinterpret_cast<const v4f*>(cs + 36);
+  // half-split: pairs i = 8j + t (t < 8); interleaved: pairs i = 4j + k (dims
+  // (2k, 2k + 1) of u = 0) and 16 + 4j + k (u = 1), k < 4
+  const float* cs = cos_sin + pos * 64 + (INTERLEAVED ? 4 * j : 8 * j);
+  const v4f c0 = *reinterpret_cast<const v4f*>(cs), c1 = *reinterpret_cast<const v4f*>(cs + (INTERLEAVED ? 16 : 4));
+  const v4f s0 = *reinterpret_cast<const v4f*>(cs + 32), s1 = *reinterpret_cast<const v4f*>(cs + (INTERLEAVED ? 48 : 36));
 
   // bf16 -> float32: element 2k is the low half of dword k
   float f[4][8];
@@ -79,14 +90,28 @@ void indexer_q_epilogue_kernel(const uint16_t* __restrict__ q, int64_t ldq, int3
       f[u][2 * k + 1] = __uint_as_float(x[u][k] & 0xFFFF0000u);
     }
 
-  // RoPE: pair i = 8j + t is (f[0][t], f[1][t])
+  if (!INTERLEAVED) {
+    // RoPE: pair i = 8j + t is (f[0][t], f[1][t])
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const float c = t < 4 ? c0[t] : c1[t - 4];
-    const float s = t < 4 ? s0[t] : s1[t - 4];
-    const float a = f[0][t], b = f[1][t];
-    f[0][t] = a * c - b * s;
-    f[1][t] = b * c + a * s;
+    for (int t = 0; t < 8; ++t) {
+      const float c = t < 4 ? c0[t] : c1[t - 4];
+      const float s = t < 4 ? s0[t] : s1[t - 4];
+      const float a = f[0][t], b = f[1][t];
+      f[0][t] = a * c - b * s;
+      f[1][t] = b * c + a * s;
+    }
+  } else {
+    // RoPE: pair 16u + 4j + k is (f[u][2k], f[u][2k + 1]), u < 2
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float c = u ? c1[k] : c0[k];
+        const float s = u ? s1[k] : s0[k];
+        const float a = f[u][2 * k], b = f[u][2 * k + 1];
+        f[u][2 * k] = a * c - b * s;
+        f[u][2 * k + 1] = b * c + a * s;
+      }
   }
 
   // Unnormalised Hadamard butterflies: dim bits 0-2 (t) and 5-6 (u) in the lane
@@ -143,7 +168,7 @@ void indexer_q_epilogue_kernel(const uint16_t* __restrict__ q, int64_t ldq, int3
     }
     mx = fmaxf(mx, quad_xchg<DPP_QUAD_XOR1>(mx));
     mx = fmaxf(mx, quad_xchg<DPP_QUAD_XOR2>(mx));
-    const int e = fp4_exponent(mx);
+    const int e = FLOOR ? fp4_exponent_floor(mx) : fp4_exponent(mx);
     sbytes |= (uint32_t)(e + 127) << (8 * u);
     const float scale = __uint_as_float((uint32_t)(e + 127) << 23);  // 2^e: codes are RNE(z / 2^e)
     uint32_t d = 0;
@@ -176,10 +201,13 @@ void indexer_q_epilogue_kernel(const uint16_t* __restrict__ q, int64_t ldq, int3
 
 hipError_t launch_indexer_q_epilogue(const uint16_t* q, int64_t ldq, int64_t M, int32_t H,
                                      const int64_t* positions, const float* cos_sin, int64_t max_pos,
-                                     uint8_t* q_fp4, uint8_t* q_scales, hipStream_t stream) {
+                                     uint8_t* q_fp4, uint8_t* q_scales, bool interleaved, bool floor_rule,
+                                     hipStream_t stream) {
   const int64_t chunks = ((int64_t)H + EPI_THREADS / 4 - 1) / (EPI_THREADS / 4);
   if (M > 0x7FFFFFFF || chunks > 65535) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(indexer_q_epilogue_kernel, dim3((unsigned)M, (unsigned)chunks), dim3(EPI_THREADS), 0,
+  auto kern = interleaved ? (floor_rule ? indexer_q_epilogue_kernel<true, true> : indexer_q_epilogue_kernel<true, false>)
+                          : (floor_rule ? indexer_q_epilogue_kernel<false, true> : indexer_q_epilogue_kernel<false, false>);
+  hipLaunchKernelGGL(kern, dim3((unsigned)M, (unsigned)chunks), dim3(EPI_THREADS), 0,
                      stream, q, ldq, H, positions, cos_sin, max_pos, q_fp4, q_scales);
   return hipGetLastError();
 }

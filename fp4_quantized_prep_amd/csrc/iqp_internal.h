@@ -52,9 +52,11 @@ hipError_t launch_indexer_q_small_bf16(const IndexerQArgs& args, hipStream_t str
 
 // standalone epilogue: bf16 Q [M, H*128] (row stride ldq elements) -> RoPE,
 // Hadamard-128, FP4 codes [M, H, 64] and scale bytes [M, H, 4]
+// (interleaved: RoPE pairs (2i, 2i+1); floor_rule: OCP MX FP4 scales)
 hipError_t launch_indexer_q_epilogue(const uint16_t* q, int64_t ldq, int64_t M, int32_t H,
                                      const int64_t* positions, const float* cos_sin, int64_t max_pos,
-                                     uint8_t* q_fp4, uint8_t* q_scales, hipStream_t stream);
+                                     uint8_t* q_fp4, uint8_t* q_scales, bool interleaved, bool floor_rule,
+                                     hipStream_t stream);
 
 // weight preparation: bf16 [N, K] -> E4M3 [N, K] + UE8M0 [N/128, K/128]
 hipError_t launch_fp8_quant_weight(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q, int64_t ldq,

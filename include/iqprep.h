@@ -60,6 +60,12 @@ extern "C" {
 
 #define IQP_ABI_VERSION     1
 
+/* Convention flags of indexer_q_rope_hadamard_fp4 (0: the defaults of
+ * indexer_q_gemm_rope_fp4). The pages leave these conventions open. */
+#define IQP_ROPE_INTERLEAVED     0x1  /* RoPE pairs (2i, 2i+1), i < rope_dim/2, instead of (i, i + rope_dim/2) */
+#define IQP_FP4_SCALE_OCP_FLOOR  0x2  /* FP4 scale e = floor(log2 max(amax, 1e-4)) - 2 (OCP MX rule), codes
+                                         saturating at +-6, instead of e = ceil(log2(amax / 6)) */
+
 /*
  * fp8_quant_1x128_ue8m0 — packed-UE8M0 FP8 activation quantization.
  *
@@ -197,7 +203,13 @@ int indexer_q_prep_bf16(const void* x, int64_t ldx, const void* w, int64_t ldw,
  *
  * For every token m and head h, with Q_d = q[m * ldq + 128 h + d] widened to
  * float32, the RoPE, Hadamard and FP4 steps are those of
- * indexer_q_gemm_rope_fp4 (same table, same output layout and rounding).
+ * indexer_q_gemm_rope_fp4 (same table, same output layout and rounding)
+ * when flags is 0. flags may select convention variants:
+ *   IQP_ROPE_INTERLEAVED      pair i (angle row entries i and rope_dim/2 + i of
+ *                             the table, as before) is dims (2i, 2i + 1);
+ *   IQP_FP4_SCALE_OCP_FLOOR   e = floor(log2 max(amax, 1e-4)) - 2 (so e >= -16),
+ *                             codes = E2M1 RNE of z * 2^-e saturated at +-6.
+ * Other bits: IQP_ERR_INVALID.
  *
  *   q          bf16 [M, H*D], row stride ldq (elements, >= H*D); 16-byte
  *              aligned and ldq a multiple of 8, else IQP_ERR_UNSUPPORTED.
@@ -216,7 +228,7 @@ int indexer_q_prep_bf16(const void* x, int64_t ldx, const void* w, int64_t ldw,
 int indexer_q_rope_hadamard_fp4(const void* q, int64_t ldq, int64_t M, int32_t H, int32_t D,
                                 int32_t rope_dim, const int64_t* positions,
                                 const float* cos_sin, int64_t max_pos,
-                                uint8_t* q_fp4, uint8_t* q_scales, void* stream);
+                                uint8_t* q_fp4, uint8_t* q_scales, int32_t flags, void* stream);
 
 /*
  * fp8_quant_weight_128x128_ue8m0 — weight preparation: bf16 weights to the

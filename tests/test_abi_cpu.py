@@ -102,8 +102,9 @@ def test_debug_and_table_argument_checks(iqp):
     assert lib.iqp_rope_cos_sin_table(10000.0, 0, 64, P(0), None) == iqp.IQP_OK
 
 
-def epilogue(iqp, q=16, ldq=256, M=4, H=2, D=128, rd=64, pos=16, cs=16, mp=10, out=16, sc=16):
-    return iqp._lib.indexer_q_rope_hadamard_fp4(P(q), ldq, M, H, D, rd, P(pos), P(cs), mp, P(out), P(sc), None)
+def epilogue(iqp, q=16, ldq=256, M=4, H=2, D=128, rd=64, pos=16, cs=16, mp=10, out=16, sc=16, flags=0):
+    return iqp._lib.indexer_q_rope_hadamard_fp4(P(q), ldq, M, H, D, rd, P(pos), P(cs), mp, P(out), P(sc), flags,
+                                                None)
 
 
 def test_epilogue_argument_checks(iqp):
@@ -123,6 +124,8 @@ def test_epilogue_argument_checks(iqp):
     assert epilogue(iqp, cs=8) == uns
     assert epilogue(iqp, out=2) == uns
     assert epilogue(iqp, out=8) == uns                            # codes are stored 16 bytes at a time
+    assert epilogue(iqp, flags=4) == inv                          # unknown convention bit
+    assert epilogue(iqp, flags=-1) == inv
 
 
 def prep(iqp, x=16, ldx=1536, w=16, ldw=1536, ws=16, M=4, K=1536, H=2, D=128, rd=64, pos=16, cs=16, mp=10,
