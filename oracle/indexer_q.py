@@ -232,17 +232,25 @@ def indexer_q_epilogue(q, positions, n_heads: int = 64, head_dim: int = 128, rop
 
 def indexer_q_chain(a_codes, a_scale_bytes, w_codes, w_scale_bytes, positions,
                     n_heads: int = 64, head_dim: int = 128, rope_dim: int = 64,
-                    theta: float = 10000.0) -> dict:
+                    theta: float = 10000.0, rope_layout: str = "half_split",
+                    scale_rule: str = "ceil") -> dict:
     """The whole indexer-Q preparation for one batch of tokens.
 
     Returns a dict with ``q_fp4`` [M, H, D/2] uint8, ``q_scales`` [M, H, D/32]
     uint8, and the float64 intermediates ``q`` (GEMM output, [M, H, D]),
     ``q_rope`` and ``z`` (the Hadamard-rotated values that were quantized).
+    rope_layout ("half_split" or "interleaved") and scale_rule ("ceil" or
+    "ocp_floor") select the convention variants, as in indexer_q_epilogue.
     """
     M = np.asarray(a_codes).shape[0]
     q = block_scaled_gemm(a_codes, a_scale_bytes, w_codes, w_scale_bytes)
     q = q.reshape(M, n_heads, head_dim)
-    q_rope = rope_half_split(q, positions, theta, rope_dim)
+    if rope_layout == "half_split":
+        q_rope = rope_half_split(q, positions, theta, rope_dim)
+    elif rope_layout == "interleaved":
+        q_rope = rope_interleaved(q, positions, theta, rope_dim)
+    else:
+        raise ValueError(rope_layout)
     z = hadamard_rotate(q_rope)
-    packed, scales = fp4_quantize(z)
+    packed, scales = fp4_quantize(z, scale_rule=scale_rule)
     return {"q": q, "q_rope": q_rope, "z": z, "q_fp4": packed, "q_scales": scales}

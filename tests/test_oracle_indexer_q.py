@@ -280,6 +280,34 @@ def test_chain_composes_the_stages():
     assert out["q_fp4"].shape == (M, H, 64) and out["q_scales"].shape == (M, H, 4)
 
 
+def test_chain_variants_closed_form():
+    # A = e_0 (E4M3 1.0 = 0x38) and W row 0 = e_0, unit scales: Q = e_0 for
+    # head 0 and 0 for head 1. At position 1 the interleaved pair (0, 1) turns
+    # by 1 rad: z_r = (cos 1 + (-1)^bit0(r) sin 1) / sqrt(128), 0.12213 at even
+    # r and -0.02662 at odd r. Ceil rule: e = -5 (byte 122), codes 4 (0x6) and
+    # -1 (0xA), bytes 0xA6. OCP floor: e = -6 (byte 121), 7.82 saturates to 6
+    # (0x7), -1.704 -> -1.5 (0xB), bytes 0xB7. Head 1 is all zero: floor
+    # exponents -15 (ceil) and -16 (OCP floor), codes 0.
+    K, H = 128, 2
+    a = np.zeros((1, K), dtype=np.uint8)
+    a[0, 0] = 0x38
+    w = np.zeros((H * 128, K), dtype=np.uint8)
+    w[0, 0] = 0x38
+    sa = np.full((1, 1), 127, dtype=np.uint8)
+    sw = np.full((H, 1), 127, dtype=np.uint8)
+    pos = np.array([1])
+    for rule, byte, code in (("ceil", 122, 0xA6), ("ocp_floor", 121, 0xB7)):
+        out = IQ.indexer_q_chain(a, sa, w, sw, pos, n_heads=H, rope_layout="interleaved", scale_rule=rule)
+        assert out["q_scales"][0, 0].tolist() == [byte] * 4
+        assert out["q_fp4"][0, 0].tolist() == [code] * 64
+        assert out["q_scales"][0, 1].tolist() == [127 + (-15 if rule == "ceil" else -16)] * 4
+        assert out["q_fp4"][0, 1].tolist() == [0] * 64
+    # the default layout at the same input: pair (0, 32), so dim 32 carries
+    # sin 1 and the codes differ from the interleaved ones
+    base = IQ.indexer_q_chain(a, sa, w, sw, pos, n_heads=H)
+    assert not np.array_equal(base["q_fp4"][0, 0], np.full(64, 0xA6, dtype=np.uint8))
+
+
 # ----------------------------------------------------------------------------
 # Standalone epilogue (bf16 Q in): hand-derived closed forms
 # ----------------------------------------------------------------------------
