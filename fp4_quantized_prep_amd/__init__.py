@@ -48,6 +48,8 @@ def _load():
                c_p, c_p, c_i64]
     lib.indexer_q_gemm_rope_fp4.argtypes = iq_args + [c_p, c_p, c_p]
     lib.indexer_q_gemm_rope_fp4.restype = ctypes.c_int
+    lib.indexer_q_gemm_rope_fp4_ex.argtypes = iq_args + [c_p, c_p, c_i32, c_p]
+    lib.indexer_q_gemm_rope_fp4_ex.restype = ctypes.c_int
     lib.iqp_debug_indexer_q_f32.argtypes = iq_args + [c_p, c_i32, c_p]
     lib.iqp_debug_indexer_q_f32.restype = ctypes.c_int
     lib.indexer_q_prep_bf16.argtypes = [c_p, c_i64, c_p, c_i64, c_p, c_i64, c_i64, c_i32, c_i32, c_i32,
@@ -205,17 +207,26 @@ def _indexer_q_common(a, a_scales, w, w_scales, positions, cos_sin, n_heads, hea
     return a, args
 
 
+def _convention_flags(rope_layout: str, scale_rule: str) -> int:
+    if rope_layout not in ("half_split", "interleaved") or scale_rule not in ("ceil", "ocp_floor"):
+        raise ValueError("rope_layout must be 'half_split' or 'interleaved', scale_rule 'ceil' or 'ocp_floor'")
+    return (IQP_ROPE_INTERLEAVED if rope_layout == "interleaved" else 0) | \
+        (IQP_FP4_SCALE_OCP_FLOOR if scale_rule == "ocp_floor" else 0)
+
+
 def indexer_q_gemm_rope_fp4(a, a_scales, w, w_scales, positions, cos_sin, n_heads: int = 64,
                             head_dim: int = 128, rope_dim: int = 64, q_fp4=None, q_scales=None,
-                            stream=None):
+                            rope_layout: str = "half_split", scale_rule: str = "ceil", stream=None):
     """Fused block-scaled FP8 Q projection + RoPE + Hadamard-128 + FP4 e2m1.
 
     a: E4M3 [M, K] (uint8 or float8_e4m3fn) and a_scales: the packed words from
     :func:`fp8_quant_1x128_ue8m0`; w: E4M3 [H*128, K]; w_scales: uint8
     [H, K/128]; positions: int64 [M]; cos_sin: float32 [max_pos, 64].
     Returns ``(q_fp4, q_scales)``: uint8 [M, H, 64] packed codes and uint8
-    [M, H, 4] UE8M0 scale bytes.
+    [M, H, 4] UE8M0 scale bytes. rope_layout "interleaved" / scale_rule
+    "ocp_floor" select the convention variants (indexer_q_gemm_rope_fp4_ex).
     """
+    flags = _convention_flags(rope_layout, scale_rule)
     a, args = _indexer_q_common(a, a_scales, w, w_scales, positions, cos_sin, n_heads, head_dim, rope_dim)
     M = a.shape[0]
     dev = a.device
@@ -229,8 +240,12 @@ def indexer_q_gemm_rope_fp4(a, a_scales, w, w_scales, positions, cos_sin, n_head
         raise ValueError("q_fp4 and q_scales must be contiguous")
     if tuple(q_fp4.shape) != (M, n_heads, head_dim // 2) or tuple(q_scales.shape) != (M, n_heads, head_dim // 32):
         raise ValueError("q_fp4 / q_scales have the wrong shape")
-    st = _lib.indexer_q_gemm_rope_fp4(*args, _ptr(q_fp4), _ptr(q_scales), _stream(a, stream))
-    _check(st, "indexer_q_gemm_rope_fp4")
+    if flags == 0:
+        st = _lib.indexer_q_gemm_rope_fp4(*args, _ptr(q_fp4), _ptr(q_scales), _stream(a, stream))
+        _check(st, "indexer_q_gemm_rope_fp4")
+    else:
+        st = _lib.indexer_q_gemm_rope_fp4_ex(*args, _ptr(q_fp4), _ptr(q_scales), flags, _stream(a, stream))
+        _check(st, "indexer_q_gemm_rope_fp4_ex")
     return q_fp4, q_scales
 
 
@@ -258,10 +273,7 @@ def indexer_q_rope_hadamard_fp4(q, positions, cos_sin, n_heads: int = 64, head_d
     Returns ``(q_fp4, q_scales)`` laid out as :func:`indexer_q_gemm_rope_fp4`'s.
     rope_layout "interleaved" pairs dims (2i, 2i+1); scale_rule "ocp_floor"
     takes the OCP MX scale rule (codes saturate at 6)."""
-    if rope_layout not in ("half_split", "interleaved") or scale_rule not in ("ceil", "ocp_floor"):
-        raise ValueError("rope_layout must be 'half_split' or 'interleaved', scale_rule 'ceil' or 'ocp_floor'")
-    flags = (IQP_ROPE_INTERLEAVED if rope_layout == "interleaved" else 0) | \
-        (IQP_FP4_SCALE_OCP_FLOOR if scale_rule == "ocp_floor" else 0)
+    flags = _convention_flags(rope_layout, scale_rule)
     dev = q.device
     _require(q, "q", torch.bfloat16, dev, 2)
     _require(positions, "positions", torch.int64, dev, 1)

@@ -120,6 +120,16 @@ int indexer_q_gemm_rope_fp4(const void* a, int64_t lda, const int32_t* a_scales,
                             int64_t M, int64_t K, int32_t H, int32_t D, int32_t rope_dim,
                             const int64_t* positions, const float* cos_sin, int64_t max_pos,
                             uint8_t* q_fp4, uint8_t* q_scales, void* stream) {
+  return indexer_q_gemm_rope_fp4_ex(a, lda, a_scales, as_stride_m, as_stride_w, w, ldw, w_scales, M, K, H, D,
+                                    rope_dim, positions, cos_sin, max_pos, q_fp4, q_scales, 0, stream);
+}
+
+int indexer_q_gemm_rope_fp4_ex(const void* a, int64_t lda, const int32_t* a_scales, int64_t as_stride_m,
+                               int64_t as_stride_w, const void* w, int64_t ldw, const uint8_t* w_scales,
+                               int64_t M, int64_t K, int32_t H, int32_t D, int32_t rope_dim,
+                               const int64_t* positions, const float* cos_sin, int64_t max_pos,
+                               uint8_t* q_fp4, uint8_t* q_scales, int32_t flags, void* stream) {
+  if (flags & ~(IQP_ROPE_INTERLEAVED | IQP_FP4_SCALE_OCP_FLOOR)) return IQP_ERR_INVALID;
   int st = check_indexer_q_args(a, lda, a_scales, as_stride_m, as_stride_w, w, ldw, w_scales, M, K,
                                 H, D, rope_dim, positions, cos_sin, max_pos, q_fp4, q_scales);
   if (st != IQP_OK || M == 0) return st;
@@ -130,7 +140,7 @@ int indexer_q_gemm_rope_fp4(const void* a, int64_t lda, const int32_t* a_scales,
                                   K, H, positions, cos_sin, max_pos);
   p.q_fp4 = q_fp4;
   p.q_scales = q_scales;
-  return from_hip(iqp::launch_indexer_q(p, -1, static_cast<hipStream_t>(stream)));
+  return from_hip(iqp::launch_indexer_q_variant(p, flags, static_cast<hipStream_t>(stream)));
 }
 
 int indexer_q_prep_bf16(const void* x, int64_t ldx, const void* w, int64_t ldw, const uint8_t* w_scales,

@@ -45,12 +45,6 @@ __device__ __forceinline__ float quad_xchg(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
-// FP4 block exponent by the OCP MX rule, e = max(floor(log2 amax), floor(log2 1e-4)) - 2,
-// from the float bits of amax >= 0 (floor(log2 1e-4) = -14)
-__device__ __forceinline__ int fp4_exponent_floor(float amax) {
-  return max((int)(__float_as_uint(amax) >> 23) - 129, -16);
-}
-
 // INTERLEAVED: RoPE pairs (2i, 2i + 1) instead of (i, i + 32); FLOOR: FP4
 // scales by the OCP MX rule (codes saturate at 6) instead of the ceil rule.
 template <bool INTERLEAVED, bool FLOOR>

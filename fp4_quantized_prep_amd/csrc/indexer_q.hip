@@ -260,7 +260,7 @@ enum { MODE_STEADY, MODE_PENULT, MODE_LAST, MODE_ONLY };
 //   ONLY (a single K block): switch buffers, copy next blocks 0 and 1.
 // LAST and ONLY fetch the RoPE rows of the epilogue's first sub-tile before
 // the barrier.
-template <int NTM, int MODE, int ST>
+template <int NTM, int MODE, int ST, bool IL>
 __device__ __forceinline__ void k_block(Ctx& c, int j, v16f (&acc)[MAX_TM][4], Frags<NTM>& f0, Frags<NTM>& f1,
                                         int (&as0)[MAX_TM], int (&as1)[MAX_TM], int64_t next_tbase,
                                         RopeCS& rope0, int64_t pos0) {
@@ -272,7 +272,7 @@ __device__ __forceinline__ void k_block(Ctx& c, int j, v16f (&acc)[MAX_TM][4], F
 #pragma unroll
   for (int tm = 0; tm < MAX_TM; ++tm) as[tm] = (int)((uint32_t)as0[tm] >> (8 * (j & 3)));
   if constexpr (MODE == MODE_LAST || MODE == MODE_ONLY) {
-    if constexpr (NTM > 0) rope0 = load_rope(pos0, c.half, c.p);
+    if constexpr (NTM > 0) rope0 = load_rope<IL>(pos0, c.half, c.p);
   }
   __builtin_amdgcn_sched_barrier(0);
   half_step<NTM, ST, 1, false, 0, 0>(c, acc, f0, as, ws, f1, as1, j, 0);
@@ -342,24 +342,24 @@ __device__ __forceinline__ void run_tile(Ctx& c, int64_t tbase, int64_t next_tba
   const int nkb = c.nkb;
   const int64_t p0 = NTM > 0 ? pos[0] : 0;
   if constexpr (SHAPE == SHAPE_ONE) {
-    k_block<NTM, MODE_ONLY, 0>(c, 0, acc, f0, f1, as0, as1, next_tbase, rope, p0);
+    k_block<NTM, MODE_ONLY, 0, stage_interleaved(STAGE)>(c, 0, acc, f0, f1, as0, as1, next_tbase, rope, p0);
   } else if constexpr (SHAPE == SHAPE_TWO) {
-    k_block<NTM, MODE_PENULT, 0>(c, 0, acc, f0, f1, as0, as1, next_tbase, rope, 0);
-    k_block<NTM, MODE_LAST, 1>(c, 1, acc, f0, f1, as0, as1, next_tbase, rope, p0);
+    k_block<NTM, MODE_PENULT, 0, stage_interleaved(STAGE)>(c, 0, acc, f0, f1, as0, as1, next_tbase, rope, 0);
+    k_block<NTM, MODE_LAST, 1, stage_interleaved(STAGE)>(c, 1, acc, f0, f1, as0, as1, next_tbase, rope, p0);
   } else {
-    k_block<NTM, MODE_STEADY, 0>(c, 0, acc, f0, f1, as0, as1, 0, rope, 0);
+    k_block<NTM, MODE_STEADY, 0, stage_interleaved(STAGE)>(c, 0, acc, f0, f1, as0, as1, 0, rope, 0);
     int j = 1;
     for (; j + 3 < nkb; j += 2) {
-      k_block<NTM, MODE_STEADY, 1>(c, j, acc, f0, f1, as0, as1, 0, rope, 0);
-      k_block<NTM, MODE_STEADY, 0>(c, j + 1, acc, f0, f1, as0, as1, 0, rope, 0);
+      k_block<NTM, MODE_STEADY, 1, stage_interleaved(STAGE)>(c, j, acc, f0, f1, as0, as1, 0, rope, 0);
+      k_block<NTM, MODE_STEADY, 0, stage_interleaved(STAGE)>(c, j + 1, acc, f0, f1, as0, as1, 0, rope, 0);
     }
     if constexpr (SHAPE == SHAPE_EVEN) {   // three left: j (stage 1), j+1, j+2
-      k_block<NTM, MODE_STEADY, 1>(c, j, acc, f0, f1, as0, as1, 0, rope, 0);
-      k_block<NTM, MODE_PENULT, 0>(c, j + 1, acc, f0, f1, as0, as1, next_tbase, rope, 0);
-      k_block<NTM, MODE_LAST, 1>(c, j + 2, acc, f0, f1, as0, as1, next_tbase, rope, p0);
+      k_block<NTM, MODE_STEADY, 1, stage_interleaved(STAGE)>(c, j, acc, f0, f1, as0, as1, 0, rope, 0);
+      k_block<NTM, MODE_PENULT, 0, stage_interleaved(STAGE)>(c, j + 1, acc, f0, f1, as0, as1, next_tbase, rope, 0);
+      k_block<NTM, MODE_LAST, 1, stage_interleaved(STAGE)>(c, j + 2, acc, f0, f1, as0, as1, next_tbase, rope, p0);
     } else {                               // two left: j (stage 1), j+1
-      k_block<NTM, MODE_PENULT, 1>(c, j, acc, f0, f1, as0, as1, next_tbase, rope, 0);
-      k_block<NTM, MODE_LAST, 0>(c, j + 1, acc, f0, f1, as0, as1, next_tbase, rope, p0);
+      k_block<NTM, MODE_PENULT, 1, stage_interleaved(STAGE)>(c, j, acc, f0, f1, as0, as1, next_tbase, rope, 0);
+      k_block<NTM, MODE_LAST, 0, stage_interleaved(STAGE)>(c, j + 1, acc, f0, f1, as0, as1, next_tbase, rope, p0);
     }
   }
 
@@ -375,7 +375,7 @@ __device__ __forceinline__ void run_tile(Ctx& c, int64_t tbase, int64_t next_tba
   for (int tm = 0; tm < NTM; ++tm) {
     __builtin_amdgcn_sched_barrier(0);
     RopeCS next;
-    if (tm + 1 < NTM) next = load_rope(pos[tm + 1], c.half, c.p);
+    if (tm + 1 < NTM) next = load_rope<stage_interleaved(STAGE)>(pos[tm + 1], c.half, c.p);
     epilogue_tile<STAGE>(acc[tm], t_lane + TM_STRIDE * tm, c.head, c.head < c.p.H, c.half, c.p, rope);
     if (tm + 1 < NTM) rope = next;
   }
@@ -476,12 +476,21 @@ hipError_t launch_kernel(const IndexerQArgs& a_in, int stage, hipStream_t stream
     case 0: hipLaunchKernelGGL(indexer_q_kernel<0>, grid, block, 0, stream, a); break;
     case 1: hipLaunchKernelGGL(indexer_q_kernel<1>, grid, block, 0, stream, a); break;
     case 2: hipLaunchKernelGGL(indexer_q_kernel<2>, grid, block, 0, stream, a); break;
+    case stage_of_variant(1): hipLaunchKernelGGL(indexer_q_kernel<stage_of_variant(1)>, grid, block, 0, stream, a); break;
+    case stage_of_variant(2): hipLaunchKernelGGL(indexer_q_kernel<stage_of_variant(2)>, grid, block, 0, stream, a); break;
+    case stage_of_variant(3): hipLaunchKernelGGL(indexer_q_kernel<stage_of_variant(3)>, grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 }  // namespace
+
+hipError_t launch_indexer_q_variant(const IndexerQArgs& a, int variant, hipStream_t stream) {
+  if (variant == 0) return launch_indexer_q(a, -1, stream);
+  if (variant < 0 || variant > 3) return hipErrorInvalidValue;
+  return launch_kernel(a, stage_of_variant(variant), stream);
+}
 
 hipError_t launch_indexer_q(const IndexerQArgs& a_in, int stage, hipStream_t stream) {
   if (stage == -1 && indexer_q_small_supported(a_in)) return launch_indexer_q_small(a_in, stream);

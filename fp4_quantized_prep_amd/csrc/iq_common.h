@@ -49,6 +49,20 @@ __device__ __forceinline__ int fp4_exponent(float amax) {
   return max(e, -15);
 }
 
+// FP4 block exponent by the OCP MX rule, e = max(floor(log2 amax), floor(log2 1e-4)) - 2,
+// from the float bits of amax >= 0 (floor(log2 1e-4) = -14)
+__device__ __forceinline__ int fp4_exponent_floor(float amax) {
+  return max((int)(__float_as_uint(amax) >> 23) - 129, -16);
+}
+
+// Convention variants of the FP4-output kernels ride on the STAGE template
+// argument: STAGE = -1 - v with v bit 0 = interleaved RoPE pairs (2i, 2i+1),
+// bit 1 = OCP floor-rule FP4 scales; the diagnostic stages (>= 0) and
+// STAGE = -1 take the defaults (pairs (i, i+32), e = ceil(log2(amax / 6))).
+constexpr int stage_of_variant(int v) { return -1 - v; }
+constexpr bool stage_interleaved(int stage) { return stage < 0 && ((-1 - stage) & 1); }
+constexpr bool stage_floor(int stage) { return stage < 0 && ((-1 - stage) & 2); }
+
 // ---------------------------------------------------------------------------
 // Epilogue for one 32-token column tile of one head: acc[tn][r] holds head dim
 //   d = 32 tn + 8 (r >> 2) + 4 half + (r & 3)
@@ -64,14 +78,31 @@ __device__ __forceinline__ int64_t load_position(int64_t t, const IndexerQArgs& 
   return p.positions[t < p.M ? t : p.M - 1];
 }
 
+// Half-split: c[g][s] is the cosine of pair 8g + 4half + s. Interleaved: the
+// lane's pairs are i = 16tn + 4g + 2half + k (dims 2i, 2i+1 in registers
+// 4g + 2k, 4g + 2k + 1 of acc[tn], tn < 2), held as c[2tn + (g >> 1)][2(g & 1) + k],
+// i.e. table entries 8j + 2half + {0, 1} and 8j + 2half + {4, 5} of c[j].
+template <bool INTERLEAVED = false>
 __device__ __forceinline__ RopeCS load_rope(int64_t pos, int half, const IndexerQArgs& p) {
   pos = pos < 0 ? 0 : (pos >= p.max_pos ? p.max_pos - 1 : pos);
   const float* cs = p.cos_sin + pos * 64;
   RopeCS r;
+  if constexpr (!INTERLEAVED) {
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    r.c[g] = *reinterpret_cast<const v4f*>(cs + 8 * g + 4 * half);
-    r.s[g] = *reinterpret_cast<const v4f*>(cs + 32 + 8 * g + 4 * half);
+    for (int g = 0; g < 4; ++g) {
+      r.c[g] = *reinterpret_cast<const v4f*>(cs + 8 * g + 4 * half);
+      r.s[g] = *reinterpret_cast<const v4f*>(cs + 32 + 8 * g + 4 * half);
+    }
+  } else {
+    typedef float v2f __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float* b = cs + 8 * j + 2 * half;
+      const v2f c0 = *reinterpret_cast<const v2f*>(b), c1 = *reinterpret_cast<const v2f*>(b + 4);
+      const v2f s0 = *reinterpret_cast<const v2f*>(b + 32), s1 = *reinterpret_cast<const v2f*>(b + 36);
+      r.c[j] = v4f{c0[0], c0[1], c1[0], c1[1]};
+      r.s[j] = v4f{s0[0], s0[1], s1[0], s1[1]};
+    }
   }
   return r;
 }
@@ -101,18 +132,34 @@ __device__ __forceinline__ void epilogue_tile(const v16f (&acc)[4], int64_t t, i
     return;
   }
 
-  // RoPE on dims 0..63: the pair (i, i + 32), i = 8 g + 4 half + s, lives in
-  // v[0][4g+s] and v[1][4g+s].
+  if constexpr (!stage_interleaved(STAGE)) {
+    // RoPE on dims 0..63: the pair (i, i + 32), i = 8 g + 4 half + s, lives in
+    // v[0][4g+s] and v[1][4g+s].
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const v4f cc = rcs.c[g];
-    const v4f ss = rcs.s[g];
+    for (int g = 0; g < 4; ++g) {
+      const v4f cc = rcs.c[g];
+      const v4f ss = rcs.s[g];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const float x = v[0][4 * g + s], y = v[1][4 * g + s];
-      v[0][4 * g + s] = x * cc[s] - y * ss[s];
-      v[1][4 * g + s] = y * cc[s] + x * ss[s];
+      for (int s = 0; s < 4; ++s) {
+        const float x = v[0][4 * g + s], y = v[1][4 * g + s];
+        v[0][4 * g + s] = x * cc[s] - y * ss[s];
+        v[1][4 * g + s] = y * cc[s] + x * ss[s];
+      }
     }
+  } else {
+    // interleaved: pair i = 16tn + 4g + 2half + k is (v[tn][4g+2k], v[tn][4g+2k+1]), tn < 2
+#pragma unroll
+    for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const float cc = rcs.c[2 * tn + (g >> 1)][2 * (g & 1) + k];
+          const float ss = rcs.s[2 * tn + (g >> 1)][2 * (g & 1) + k];
+          const float x = v[tn][4 * g + 2 * k], y = v[tn][4 * g + 2 * k + 1];
+          v[tn][4 * g + 2 * k] = x * cc - y * ss;
+          v[tn][4 * g + 2 * k + 1] = y * cc + x * ss;
+        }
   }
 
   if (STAGE == 1) {
@@ -194,7 +241,7 @@ __device__ __forceinline__ void epilogue_tile(const v16f (&acc)[4], int64_t t, i
     for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(v[tn][r]));
     float m0, m1;
     swap32(m, m, m0, m1);
-    const int e = fp4_exponent(fmaxf(m0, m1));
+    const int e = stage_floor(STAGE) ? fp4_exponent_floor(fmaxf(m0, m1)) : fp4_exponent(fmaxf(m0, m1));
     sbytes |= (uint32_t)(e + 127) << (8 * tn);
     const float scale = __uint_as_float((uint32_t)(e + 127) << 23);  // 2^e: codes are RNE(z / 2^e)
     // dword (tn, r3) holds the packed codes of dims 32tn + 16r3 + 8half + [0, 8)

@@ -35,6 +35,10 @@ hipError_t launch_fp8_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx
 
 // stage -1: FP4 output; 0, 1, 2: float32 diagnostics (see iqprep.h)
 hipError_t launch_indexer_q(const IndexerQArgs& args, int stage, hipStream_t stream);
+// FP4 output with convention variant v (bit 0: interleaved RoPE pairs, bit 1:
+// OCP floor-rule FP4 scales); v = 0 is launch_indexer_q(args, -1, stream), any
+// other v runs the general kernel
+hipError_t launch_indexer_q_variant(const IndexerQArgs& args, int variant, hipStream_t stream);
 
 // the pipelined FP4-output kernel (indexer_q_pipe.hip) for the shapes it takes
 // (K = 1536, token counts that fit in 31 bits); args.chunks set

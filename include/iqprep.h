@@ -12,7 +12,7 @@
  *      (TensorRT-LLM PR "Fuse DeepSeek-V4 Indexer Q projection with CuTe DSL",
  *      sequence diagram: FP8 input + UE8M0 scales in, packed FP4 Q and scales
  *      out; the same tokenspeed PR, Summary: RoPE, Hadamard and FP4 make up
- *      the Q preparation).
+ *      the Q preparation); indexer_q_gemm_rope_fp4_ex takes convention flags.
  *   3. indexer_q_rope_hadamard_fp4   the same RoPE / Hadamard / FP4 epilogue as
  *      a standalone launch over a bf16 Q (the unfused chain's second half).
  *   4. indexer_q_prep_bf16   calls 1 and 2 as one launch for decode-sized
@@ -60,8 +60,9 @@ extern "C" {
 
 #define IQP_ABI_VERSION     1
 
-/* Convention flags of indexer_q_rope_hadamard_fp4 (0: the defaults of
- * indexer_q_gemm_rope_fp4). The pages leave these conventions open. */
+/* Convention flags of indexer_q_gemm_rope_fp4_ex and indexer_q_rope_hadamard_fp4
+ * (0: the defaults of indexer_q_gemm_rope_fp4). The pages leave these
+ * conventions open. */
 #define IQP_ROPE_INTERLEAVED     0x1  /* RoPE pairs (2i, 2i+1), i < rope_dim/2, instead of (i, i + rope_dim/2) */
 #define IQP_FP4_SCALE_OCP_FLOOR  0x2  /* FP4 scale e = floor(log2 max(amax, 1e-4)) - 2 (OCP MX rule), codes
                                          saturating at +-6, instead of e = ceil(log2(amax / 6)) */
@@ -161,6 +162,30 @@ int indexer_q_gemm_rope_fp4(const void* a, int64_t lda,
                             const float* cos_sin, int64_t max_pos,
                             uint8_t* q_fp4, uint8_t* q_scales,
                             void* stream);
+
+/*
+ * indexer_q_gemm_rope_fp4_ex — indexer_q_gemm_rope_fp4 with convention flags.
+ *
+ * The same pages as indexer_q_gemm_rope_fp4: they name the MLA RoPE kernel
+ * and MX-style FP4 block scales but fix neither the RoPE pair layout nor the
+ * scale rule. flags 0 is exactly indexer_q_gemm_rope_fp4 (same kernels, same
+ * output). Otherwise, with the arguments, layouts and errors of that call:
+ *   IQP_ROPE_INTERLEAVED      pair i < 32 is (Q_2i, Q_2i+1), rotated by the
+ *                             angle of table columns i and 32 + i as before;
+ *   IQP_FP4_SCALE_OCP_FLOOR   e = floor(log2 max(amax, 1e-4)) - 2 (so e >= -16),
+ *                             codes = E2M1 RNE of z * 2^-e saturated at +-6.
+ * Other bits: IQP_ERR_INVALID. A non-zero flags value always runs the general
+ * tiled kernel (slower than the K = 1536 production kernels).
+ */
+int indexer_q_gemm_rope_fp4_ex(const void* a, int64_t lda,
+                               const int32_t* a_scales, int64_t as_stride_m, int64_t as_stride_w,
+                               const void* w, int64_t ldw,
+                               const uint8_t* w_scales,
+                               int64_t M, int64_t K, int32_t H, int32_t D, int32_t rope_dim,
+                               const int64_t* positions,
+                               const float* cos_sin, int64_t max_pos,
+                               uint8_t* q_fp4, uint8_t* q_scales,
+                               int32_t flags, void* stream);
 
 /*
  * indexer_q_prep_bf16 — the whole indexer-Q preparation in one launch for

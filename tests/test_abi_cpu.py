@@ -91,6 +91,21 @@ def test_fused_argument_checks(iqp):
     assert fused(iqp, M=0) == iqp.IQP_OK
 
 
+def fused_ex(iqp, flags, M=4, K=256, H=2, D=128, rd=64, lda=256, ldw=256):
+    return iqp._lib.indexer_q_gemm_rope_fp4_ex(P(16), lda, P(16), 1, 1, P(16), ldw, P(16), M, K, H, D, rd,
+                                               P(16), P(16), 10, P(16), P(16), flags, None)
+
+
+def test_fused_ex_argument_checks(iqp):
+    inv, uns = iqp.IQP_ERR_INVALID, iqp.IQP_ERR_UNSUPPORTED
+    assert fused_ex(iqp, 4) == inv                              # unknown convention bit
+    assert fused_ex(iqp, -1) == inv
+    assert fused_ex(iqp, iqp.IQP_ROPE_INTERLEAVED, M=-3) == inv  # the base call's checks still apply
+    assert fused_ex(iqp, iqp.IQP_FP4_SCALE_OCP_FLOOR, D=64) == uns
+    assert fused_ex(iqp, 3, lda=128) == inv
+    assert fused_ex(iqp, 3, M=0) == iqp.IQP_OK
+
+
 def test_debug_and_table_argument_checks(iqp):
     lib = iqp._lib
     args = [P(16), 256, P(16), 1, 1, P(16), 256, P(16), 4, 256, 2, 128, 64, P(16), P(16), 10]

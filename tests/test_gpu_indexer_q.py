@@ -262,3 +262,78 @@ def test_unsupported_shapes_raise(gpu_lib, weights, table):
         gpu_lib.indexer_q_gemm_rope_fp4(a, a_s, wd[:8192], wsd, pos, table[4096][:, :32].contiguous(),
                                         rope_dim=32)
     assert e.value.status == gpu_lib.IQP_ERR_UNSUPPORTED
+
+
+# ---------------------------------------------------------------- convention variants
+
+FUSED_VARIANTS = [("interleaved", "ceil"), ("half_split", "ocp_floor"), ("interleaved", "ocp_floor")]
+
+
+def device_chain_variant(iqp, x, wd, wsd, pos, cs, n_heads, layout, rule):
+    a, a_s = iqp.fp8_quant_1x128_ue8m0(x.cuda())
+    q, s = iqp.indexer_q_gemm_rope_fp4(a, a_s, wd, wsd, pos.cuda(), cs, n_heads=n_heads, rope_layout=layout,
+                                       scale_rule=rule)
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), s.cpu().numpy()
+
+
+@pytest.mark.parametrize("layout,rule", FUSED_VARIANTS)
+@pytest.mark.parametrize("M", [1, 5, 128, 300])
+def test_fused_chain_variants(gpu_lib, weights, table, layout, rule, M):
+    """The flags call (indexer_q_gemm_rope_fp4_ex) against the oracle's chain
+    with the same conventions; every token checked."""
+    codes, sb, wd, wsd = weights
+    inp = S.indexer_q_inputs("indexer_q_m128", M=M)
+    x, pos = inp["x"], inp["positions"]
+    print(f"[variant] M={M} {layout} {rule}", flush=True)
+    q, s = device_chain_variant(gpu_lib, x, wd, wsd, pos, table[4096], 64, layout, rule)
+    ref = oracle_chain_from_x(x, codes, sb, pos, 64, layout, rule)
+    rep = C.check_fp4(q, s, ref["z"], ref["q_fp4"], ref["q_scales"], scale_rule=rule)
+    print(rep)
+    assert rep["ok"], rep
+    if M == 128:
+        assert rep["rel_l2"] < 2e-2
+
+
+@pytest.mark.parametrize("layout,rule", FUSED_VARIANTS)
+def test_fused_chain_variants_other_k_and_heads(gpu_lib, table, layout, rule):
+    H, M, K = 3, 70, 1024
+    codes, sb = S.weights(N=H * 128, K=K, seed=101)
+    g = S.rng("indexer_q_m128", 900 + K)
+    x = S.activations_outlier(g, M, K)
+    pos = S.positions_uniform(g, M, 4096)
+    q, s = device_chain_variant(gpu_lib, x, codes.cuda(), sb.cuda(), pos, table[4096], H, layout, rule)
+    ref = oracle_chain_from_x(x, codes, sb, pos, H, layout, rule)
+    rep = C.check_fp4(q, s, ref["z"], ref["q_fp4"], ref["q_scales"], scale_rule=rule)
+    assert rep["ok"], rep
+
+
+def test_fused_chain_variant_m4632_sampled(gpu_lib, weights, table):
+    codes, sb, wd, wsd = weights
+    inp = S.indexer_q_inputs("indexer_q_m4632")
+    x, pos = inp["x"], inp["positions"]
+    q, s = device_chain_variant(gpu_lib, x, wd, wsd, pos, table[4632], 64, "interleaved", "ocp_floor")
+    rows = np.unique(np.concatenate([np.arange(8), np.random.default_rng(4634).integers(0, 4632, 120),
+                                     np.arange(4632 - 8, 4632)]))
+    ref = oracle_chain_from_x(x[rows], codes, sb, pos[rows], 64, "interleaved", "ocp_floor")
+    rep = C.check_fp4(q[rows], s[rows], ref["z"], ref["q_fp4"], ref["q_scales"], scale_rule="ocp_floor")
+    assert rep["ok"], rep
+
+
+def test_fused_ex_flags_zero_is_the_base_call(gpu_lib, weights, table):
+    """flags = 0 through indexer_q_gemm_rope_fp4_ex writes the base call's
+    bytes (every output byte, over guard-filled buffers)."""
+    codes, sb, wd, wsd = weights
+    inp = S.indexer_q_inputs("indexer_q_m128", M=40)
+    x, pos = inp["x"], inp["positions"]
+    a, a_s = gpu_lib.fp8_quant_1x128_ue8m0(x.cuda())
+    pd = pos.cuda()
+    q0, s0 = gpu_lib.indexer_q_gemm_rope_fp4(a, a_s, wd, wsd, pd, table[4096], n_heads=64)
+    _, args = gpu_lib._indexer_q_common(a, a_s, wd, wsd, pd, table[4096], 64, 128, 64)
+    q1 = torch.full_like(q0, 0x5A)
+    s1 = torch.full_like(s0, 0xA5)
+    st = gpu_lib._lib.indexer_q_gemm_rope_fp4_ex(*args, q1.data_ptr(), s1.data_ptr(), 0,
+                                                 torch.cuda.current_stream().cuda_stream)
+    assert st == gpu_lib.IQP_OK
+    torch.cuda.synchronize()
+    assert torch.equal(q0.cpu(), q1.cpu()) and torch.equal(s0.cpu(), s1.cpu())
