@@ -76,11 +76,18 @@ def block_scaled_gemm(a_codes, a_scale_bytes, w_codes, w_scale_bytes) -> np.ndar
 # ----------------------------------------------------------------------------
 
 
-def rope_angles(positions, theta: float, rope_dim: int) -> np.ndarray:
-    """Angles [M, rope_dim/2]: pos * theta^(-2i/rope_dim), in float64."""
+def rope_angles(positions, theta: float, rope_dim: int, inv_freq=None) -> np.ndarray:
+    """Angles [M, rope_dim/2]: pos * theta^(-2i/rope_dim), in float64; or
+    pos * inv_freq[i] when explicit per-pair frequencies are given (a
+    rescaled schedule such as YaRN's: the table the kernels read may hold any
+    frequencies)."""
     half = rope_dim // 2
-    i = np.arange(half, dtype=np.float64)
-    inv_freq = np.power(float(theta), -2.0 * i / rope_dim)
+    if inv_freq is None:
+        i = np.arange(half, dtype=np.float64)
+        inv_freq = np.power(float(theta), -2.0 * i / rope_dim)
+    inv_freq = np.asarray(inv_freq, dtype=np.float64)
+    if inv_freq.shape != (half,):
+        raise ValueError("inv_freq must hold rope_dim/2 frequencies")
     return np.asarray(positions, dtype=np.float64)[:, None] * inv_freq[None, :]
 
 
@@ -91,17 +98,20 @@ def rope_cos_sin_table(theta: float, max_pos: int, rope_dim: int) -> np.ndarray:
     return np.concatenate([np.cos(ang), np.sin(ang)], axis=1)
 
 
-def rope_half_split(q, positions, theta: float = 10000.0, rope_dim: int = 64) -> np.ndarray:
+def rope_half_split(q, positions, theta: float = 10000.0, rope_dim: int = 64, inv_freq=None,
+                    mscale: float = 1.0) -> np.ndarray:
     """Rotate each head's first rope_dim dims; q is [M, H, D] float64.
 
     For i < rope_dim/2: (x_i, x_{i+half}) -> (x_i c - x_{i+half} s,
-    x_{i+half} c + x_i s); dims rope_dim..D-1 are unchanged.
+    x_{i+half} c + x_i s); dims rope_dim..D-1 are unchanged. c and s are
+    mscale * cos / sin of the angle (mscale: an attention factor folded into
+    the table, 1 by default), the angle from rope_angles.
     """
     q = np.asarray(q, dtype=np.float64)
     half = rope_dim // 2
-    ang = rope_angles(positions, theta, rope_dim)
-    c = np.cos(ang)[:, None, :]
-    s = np.sin(ang)[:, None, :]
+    ang = rope_angles(positions, theta, rope_dim, inv_freq)
+    c = mscale * np.cos(ang)[:, None, :]
+    s = mscale * np.sin(ang)[:, None, :]
     out = q.copy()
     x1 = q[..., :half]
     x2 = q[..., half:rope_dim]
@@ -110,7 +120,8 @@ def rope_half_split(q, positions, theta: float = 10000.0, rope_dim: int = 64) ->
     return out
 
 
-def rope_interleaved(q, positions, theta: float = 10000.0, rope_dim: int = 64) -> np.ndarray:
+def rope_interleaved(q, positions, theta: float = 10000.0, rope_dim: int = 64, inv_freq=None,
+                     mscale: float = 1.0) -> np.ndarray:
     """The interleaved RoPE layout: pair i < rope_dim/2 is dims (2i, 2i + 1),
     rotated by the same angle pos * theta^(-2i/rope_dim); dims rope_dim..D-1
     are unchanged. q is [M, H, D] float64.
@@ -120,9 +131,9 @@ def rope_interleaved(q, positions, theta: float = 10000.0, rope_dim: int = 64) -
     Summary, names only an MLA RoPE kernel); both common layouts are offered.
     """
     q = np.asarray(q, dtype=np.float64)
-    ang = rope_angles(positions, theta, rope_dim)
-    c = np.cos(ang)[:, None, :]
-    s = np.sin(ang)[:, None, :]
+    ang = rope_angles(positions, theta, rope_dim, inv_freq)
+    c = mscale * np.cos(ang)[:, None, :]
+    s = mscale * np.sin(ang)[:, None, :]
     out = q.copy()
     x1 = q[..., 0:rope_dim:2]
     x2 = q[..., 1:rope_dim:2]
@@ -200,7 +211,7 @@ def fp4_quantize(z, decide_dtype=np.float32, scale_rule: str = "ceil") -> tuple:
 
 def indexer_q_epilogue(q, positions, n_heads: int = 64, head_dim: int = 128, rope_dim: int = 64,
                        theta: float = 10000.0, rope_layout: str = "half_split",
-                       scale_rule: str = "ceil") -> dict:
+                       scale_rule: str = "ceil", inv_freq=None, mscale: float = 1.0) -> dict:
     """RoPE, Hadamard rotation and FP4 quantization of an already projected Q.
 
     This is the unfused chain's epilogue (TensorRT-LLM PR "Fuse DeepSeek-V4
@@ -209,15 +220,16 @@ def indexer_q_epilogue(q, positions, n_heads: int = 64, head_dim: int = 128, rop
     consume). q is [M, H*D] (the bf16 values, widened exactly); the steps are
     the same functions the fused chain applies after its GEMM. rope_layout
     ("half_split" or "interleaved") and scale_rule ("ceil" or "ocp_floor")
-    select the convention variants.
+    select the convention variants; inv_freq / mscale give an explicit
+    frequency schedule (rope_angles).
     """
     q = np.asarray(q, dtype=np.float64)
     M = q.shape[0]
     q = q.reshape(M, n_heads, head_dim)
     if rope_layout == "half_split":
-        q_rope = rope_half_split(q, positions, theta, rope_dim)
+        q_rope = rope_half_split(q, positions, theta, rope_dim, inv_freq, mscale)
     elif rope_layout == "interleaved":
-        q_rope = rope_interleaved(q, positions, theta, rope_dim)
+        q_rope = rope_interleaved(q, positions, theta, rope_dim, inv_freq, mscale)
     else:
         raise ValueError(rope_layout)
     z = hadamard_rotate(q_rope)
@@ -233,22 +245,23 @@ def indexer_q_epilogue(q, positions, n_heads: int = 64, head_dim: int = 128, rop
 def indexer_q_chain(a_codes, a_scale_bytes, w_codes, w_scale_bytes, positions,
                     n_heads: int = 64, head_dim: int = 128, rope_dim: int = 64,
                     theta: float = 10000.0, rope_layout: str = "half_split",
-                    scale_rule: str = "ceil") -> dict:
+                    scale_rule: str = "ceil", inv_freq=None, mscale: float = 1.0) -> dict:
     """The whole indexer-Q preparation for one batch of tokens.
 
     Returns a dict with ``q_fp4`` [M, H, D/2] uint8, ``q_scales`` [M, H, D/32]
     uint8, and the float64 intermediates ``q`` (GEMM output, [M, H, D]),
     ``q_rope`` and ``z`` (the Hadamard-rotated values that were quantized).
     rope_layout ("half_split" or "interleaved") and scale_rule ("ceil" or
-    "ocp_floor") select the convention variants, as in indexer_q_epilogue.
+    "ocp_floor") select the convention variants, as in indexer_q_epilogue;
+    inv_freq / mscale give an explicit frequency schedule (rope_angles).
     """
     M = np.asarray(a_codes).shape[0]
     q = block_scaled_gemm(a_codes, a_scale_bytes, w_codes, w_scale_bytes)
     q = q.reshape(M, n_heads, head_dim)
     if rope_layout == "half_split":
-        q_rope = rope_half_split(q, positions, theta, rope_dim)
+        q_rope = rope_half_split(q, positions, theta, rope_dim, inv_freq, mscale)
     elif rope_layout == "interleaved":
-        q_rope = rope_interleaved(q, positions, theta, rope_dim)
+        q_rope = rope_interleaved(q, positions, theta, rope_dim, inv_freq, mscale)
     else:
         raise ValueError(rope_layout)
     z = hadamard_rotate(q_rope)

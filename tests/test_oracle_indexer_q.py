@@ -443,3 +443,36 @@ def test_epilogue_variants_closed_forms():
     assert out["q_scales"].tolist() == [[[122] * 4]] and out["q_fp4"].reshape(-1).tolist() == [0xA6] * 64
     out = IQ.indexer_q_epilogue(q, np.array([1]), n_heads=1, rope_layout="interleaved", scale_rule="ocp_floor")
     assert out["q_scales"].tolist() == [[[121] * 4]] and out["q_fp4"].reshape(-1).tolist() == [0xB7] * 64
+
+
+# ----------------------------------------------------------------------------
+# Explicit frequency schedules (a table of any frequencies, YaRN-style scaling)
+# ----------------------------------------------------------------------------
+
+
+def test_rope_explicit_frequencies_closed_forms():
+    # inv_freq[0] = 0.5 at position 2: pair 0 turns by exactly 1 rad; mscale
+    # 1.25 scales cos and sin. Half-split puts the pair on dims (0, 32),
+    # interleaved on dims (0, 1).
+    inv = np.zeros(32)
+    inv[0] = 0.5
+    e = np.zeros((1, 1, 128))
+    e[0, 0, 0] = 1.0
+    hs = IQ.rope_half_split(e, np.array([2]), inv_freq=inv, mscale=1.25)
+    assert abs(hs[0, 0, 0] - 1.25 * math.cos(1)) < 1e-15 and abs(hs[0, 0, 32] - 1.25 * math.sin(1)) < 1e-15
+    assert np.count_nonzero(hs) == 2
+    il = IQ.rope_interleaved(e, np.array([2]), inv_freq=inv, mscale=1.25)
+    assert abs(il[0, 0, 0] - 1.25 * math.cos(1)) < 1e-15 and abs(il[0, 0, 1] - 1.25 * math.sin(1)) < 1e-15
+    assert np.count_nonzero(il) == 2
+    # a zero frequency leaves its pair alone at any position (mscale 1)
+    rng = np.random.default_rng(31)
+    q = rng.standard_normal((2, 3, 128))
+    out = IQ.rope_half_split(q, np.array([5, 77]), inv_freq=np.zeros(32))
+    assert np.array_equal(out, q)
+    # mscale scales the rotated dims' norm and leaves the pass-through dims
+    out = IQ.rope_half_split(q, np.array([5, 77]), inv_freq=np.linspace(0.0, 1.0, 32), mscale=0.5)
+    np.testing.assert_allclose(np.linalg.norm(out[..., :64], axis=-1), 0.5 * np.linalg.norm(q[..., :64], axis=-1),
+                               rtol=1e-13)
+    assert np.array_equal(out[..., 64:], q[..., 64:])
+    with pytest.raises(ValueError):
+        IQ.rope_angles(np.array([1]), 10000.0, 64, inv_freq=np.ones(31))
