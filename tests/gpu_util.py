@@ -15,13 +15,14 @@ def bf16_to_np(x: torch.Tensor) -> np.ndarray:
 
 def oracle_chain_from_x(x_bf16: torch.Tensor, w_codes: torch.Tensor, w_sb: torch.Tensor,
                         positions: torch.Tensor, n_heads: int, rope_layout: str = "half_split",
-                        scale_rule: str = "ceil") -> dict:
-    """The oracle's whole chain (its own FP8 quantization, then the fused stages)."""
+                        scale_rule: str = "ceil", **rope) -> dict:
+    """The oracle's whole chain (its own FP8 quantization, then the fused
+    stages); rope: inv_freq / mscale of an explicit frequency schedule."""
     xn = bf16_to_np(x_bf16)
     a_codes, a_words = QO.fp8_quant_1x128_ue8m0(xn)
     a_sb = QO.unpack_scale_words(a_words, xn.shape[1] // 128)
     out = IQ.indexer_q_chain(a_codes, a_sb, w_codes.numpy(), w_sb.numpy(), positions.numpy(),
-                             n_heads=n_heads, rope_layout=rope_layout, scale_rule=scale_rule)
+                             n_heads=n_heads, rope_layout=rope_layout, scale_rule=scale_rule, **rope)
     out["a_codes"] = a_codes
     out["a_words"] = a_words
     return out
