@@ -564,21 +564,22 @@ def decode_bench(args):
             "qs": torch.empty((m, N_HEADS, HEAD_DIM // 32), dtype=torch.uint8, device=dev),
         })
 
-    def two(c):
+    def two(c, wt=(w, wsb)):
         # two calls: quantize, then the fused projection
         iqp.fp8_quant_1x128_ue8m0(c["x"], q=c["a"], scales=c["as"])
-        iqp.indexer_q_gemm_rope_fp4(c["a"], c["as"], w, wsb, c["pos"], cs, n_heads=N_HEADS,
+        iqp.indexer_q_gemm_rope_fp4(c["a"], c["as"], wt[0], wt[1], c["pos"], cs, n_heads=N_HEADS,
                                     q_fp4=c["q"], q_scales=c["qs"])
         iqp.fp8_quant_1x128_ue8m0(c["xw"], q=c["aw"], scales=c["asw"])
 
-    def one(c):
+    def one(c, wt=(w, wsb)):
         # one launch from bf16 X to FP4 Q
-        iqp.indexer_q_prep_bf16(c["x"], w, wsb, c["pos"], cs, n_heads=N_HEADS, q_fp4=c["q"], q_scales=c["qs"])
+        iqp.indexer_q_prep_bf16(c["x"], wt[0], wt[1], c["pos"], cs, n_heads=N_HEADS, q_fp4=c["q"],
+                                q_scales=c["qs"])
         iqp.fp8_quant_1x128_ue8m0(c["xw"], q=c["aw"], scales=c["asw"])
 
-    def routed(c):
+    def routed(c, wt=(w, wsb)):
         # the serving policy: one launch up to ONE_LAUNCH_MAX_TOKENS tokens, two calls above
-        (one if c["M"] <= iqp.ONE_LAUNCH_MAX_TOKENS else two)(c)
+        (one if c["M"] <= iqp.ONE_LAUNCH_MAX_TOKENS else two)(c, wt)
 
     def graph_of(fn):
         side = torch.cuda.Stream()
@@ -620,6 +621,14 @@ def decode_bench(args):
     calls_per_s = len(calls) / t_mix
     print(f"[bench] mix: {calls_per_s:.0f} calls/s routed (one launch up to {iqp.ONE_LAUNCH_MAX_TOKENS} tokens), "
           f"{len(calls) / t_mix1:.0f} one launch, {len(calls) / t_mix2:.0f} two calls", file=sys.stderr, flush=True)
+    # cold weights: call i reads weight copy i % n_w, 24 copies of 12.6 MB (302 MB, beyond the
+    # 256 MiB Infinity Cache), so every call's W streams from HBM
+    n_w = 24
+    w_sets = [(w.clone(), wsb.clone()) for _ in range(n_w)]
+    t_cold = replay_time(graph_of(lambda: [routed(c, w_sets[i % n_w]) for i, c in enumerate(calls)]), reps)
+    del w_sets
+    print(f"[bench] mix with cold weights ({n_w} rotating copies): {len(calls) / t_cold:.0f} calls/s routed",
+          file=sys.stderr, flush=True)
 
     # per-M latency of one call (the indexer-Q preparation + the wide quantization),
     # and of the indexer-Q kernel(s) alone
@@ -668,6 +677,8 @@ def decode_bench(args):
             "parallelism": "single GPU",
         },
         "latency_us": {"p50": float(np.percentile(per_call, 50)), "p99": float(np.percentile(per_call, 99))},
+        "cold_weights": {"calls_per_s": len(calls) / t_cold, "weight_copies": n_w,
+                         "note": "routed mix, call i reads weight copy i % 24 (302 MB, beyond the Infinity Cache)"},
         "one_launch_path": {"calls_per_s": len(calls) / t_mix1,
                             "p50_us": float(np.percentile(per_call1, 50)),
                             "p99_us": float(np.percentile(per_call1, 99)),
