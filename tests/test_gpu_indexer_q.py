@@ -337,3 +337,41 @@ def test_fused_ex_flags_zero_is_the_base_call(gpu_lib, weights, table):
     assert st == gpu_lib.IQP_OK
     torch.cuda.synchronize()
     assert torch.equal(q0.cpu(), q1.cpu()) and torch.equal(s0.cpu(), s1.cpu())
+
+
+# ---------------------------------------------------------------- maximum K, zero rows
+
+
+def test_fused_chain_maximum_k(gpu_lib, table):
+    """K = 32768, the largest K the fused call takes (256 K blocks, the general
+    kernel), 40 tokens x 2 heads; every token checked."""
+    H, M, K = 2, 40, 32768
+    codes, sb = S.weights(N=H * 128, K=K, seed=102)
+    g = S.rng("indexer_q_m128", 950)
+    x = S.activations_outlier(g, M, K)
+    pos = S.positions_uniform(g, M, 4096)
+    print(f"[max K] M={M} K={K} H={H}", flush=True)
+    _, _, q, s = device_chain(gpu_lib, x, codes.cuda(), sb.cuda(), pos, table[4096], n_heads=H)
+    ref = oracle_chain_from_x(x, codes, sb, pos, H)
+    rep = C.check_fp4(q, s, ref["z"], ref["q_fp4"], ref["q_scales"])
+    print(rep)
+    assert rep["ok"], rep
+
+
+@pytest.mark.parametrize("M", [5, 300])
+def test_fused_chain_zero_token_rows(gpu_lib, weights, table, M):
+    """All-zero activation rows (the small-batch kernel at 5 tokens, the
+    pipelined kernel at 300): their Q is exactly zero, so every FP4 block of
+    theirs takes the floor exponent -15 (byte 112) and every code is a zero
+    (+0 or -0: RoPE with a negative cosine turns 0 into -0); the other rows
+    are unaffected."""
+    codes, sb, wd, wsd = weights
+    inp = S.indexer_q_inputs("indexer_q_m128", M=M)
+    x, pos = inp["x"].clone(), inp["positions"]
+    zero_rows = [0, M // 2, M - 1]
+    x[zero_rows] = 0
+    _, _, q, s = device_chain(gpu_lib, x, wd, wsd, pos, table[4096])
+    assert np.all(s[zero_rows] == 112) and np.all((q[zero_rows] & 0x77) == 0)
+    ref = oracle_chain_from_x(x, codes, sb, pos, 64)
+    rep = C.check_fp4(q, s, ref["z"], ref["q_fp4"], ref["q_scales"])
+    assert rep["ok"], rep
