@@ -45,7 +45,9 @@ def block_scaled_gemm(a_codes, a_scale_bytes, w_codes, w_scale_bytes) -> np.ndar
     """Q[m, n] = sum_j 2^(ea[m,j] + ew[n/128, j]) * sum_{k in block j} A[m,k] W[n,k].
 
     a_codes [M, K] and w_codes [N, K] are E4M3 codes; a_scale_bytes [M, K/128]
-    and w_scale_bytes [N/128, K/128] are UE8M0 bytes.
+    and w_scale_bytes [N/128, K/128] are UE8M0 bytes (one per 128x128 weight
+    tile). With w_scale_bytes [N, K/128] (one per weight row and K block, the
+    1x128 weight-scale variant) the exponent is ew[n, j] instead.
 
     Each E4M3 value is an integer multiple of 2^-9 below 2^9, so every product
     is a multiple of 2^-18 and every partial sum of one 128-block stays below
@@ -61,8 +63,13 @@ def block_scaled_gemm(a_codes, a_scale_bytes, w_codes, w_scale_bytes) -> np.ndar
         raise ValueError("block_scaled_gemm: bad shapes")
     nb = K // KBLOCK
     sa = np.ldexp(1.0, np.asarray(a_scale_bytes, dtype=np.int64) - 127)      # [M, nb]
-    sw = np.ldexp(1.0, np.asarray(w_scale_bytes, dtype=np.int64) - 127)      # [N/128, nb]
-    sw_n = np.repeat(sw, WBLOCK_N, axis=0)                                   # [N, nb]
+    sw = np.ldexp(1.0, np.asarray(w_scale_bytes, dtype=np.int64) - 127)      # [N/128, nb] or [N, nb]
+    if sw.shape == (N // WBLOCK_N, nb):
+        sw_n = np.repeat(sw, WBLOCK_N, axis=0)                               # [N, nb]
+    elif sw.shape == (N, nb):
+        sw_n = sw
+    else:
+        raise ValueError("block_scaled_gemm: weight scales must be [N/128, K/128] or [N, K/128]")
     Q = np.zeros((M, N), dtype=np.float64)
     for j in range(nb):
         ks = slice(j * KBLOCK, (j + 1) * KBLOCK)

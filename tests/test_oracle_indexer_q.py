@@ -107,6 +107,33 @@ def test_gemm_weight_scale_applies_per_128_rows():
     assert np.array_equal(moved[:, 128:], base[:, 128:] * 8)
 
 
+def test_gemm_weight_scales_per_row_closed_form():
+    # A = [1, 2] in block 0 and [3] in block 1 (E4M3 1.0 = 0x38, 2.0 = 0x40,
+    # 3.0 = 0x44); W rows are one-hot: row 0 picks k = 0, row 1 picks k = 1,
+    # row 2 picks k = 128. Per-row, per-block exponents: row 0 block 0: +1,
+    # row 1 block 0: -2, row 2 block 1: +3, the rest 0, and activation
+    # exponent 0: Q = [1 * 2, 2 * 2^-2, 3 * 8] = [2, 0.5, 24] (exact).
+    a = np.zeros((1, 256), np.uint8)
+    a[0, 0], a[0, 1], a[0, 128] = 0x38, 0x40, 0x44
+    w = np.zeros((128, 256), np.uint8)
+    w[0, 0] = w[1, 1] = w[2, 128] = 0x38
+    sw = np.full((128, 2), 127, np.uint8)
+    sw[0, 0], sw[1, 0], sw[2, 1] = 128, 125, 130
+    sa = np.full((1, 2), 127, np.uint8)
+    q = IQ.block_scaled_gemm(a, sa, w, sw)
+    assert q[0, :3].tolist() == [2.0, 0.5, 24.0] and not np.any(q[0, 3:])
+    # rows of a 128-row group sharing one exponent reduce to the per-tile layout
+    g = np.random.default_rng(41)
+    a2 = rand_codes(g, (3, 256))
+    w2 = rand_codes(g, (256, 256))
+    tile = g.integers(115, 130, size=(2, 2)).astype(np.uint8)
+    sa2 = g.integers(120, 130, size=(3, 2)).astype(np.uint8)
+    assert np.array_equal(IQ.block_scaled_gemm(a2, sa2, w2, np.repeat(tile, 128, axis=0)),
+                          IQ.block_scaled_gemm(a2, sa2, w2, tile))
+    with pytest.raises(ValueError):
+        IQ.block_scaled_gemm(a2, sa2, w2, np.full((3, 2), 127, np.uint8))
+
+
 # ---------------------------------------------------------------- RoPE
 
 
