@@ -20,7 +20,7 @@ __all__ = [
     "IqpError", "fp8_quant_1x128_ue8m0", "indexer_q_gemm_rope_fp4", "rope_cos_sin_table",
     "debug_indexer_q_f32", "indexer_q_rope_hadamard_fp4", "indexer_q_prep_bf16", "indexer_q_prep", "fp8_quant_weight_128x128_ue8m0", "abi_version", "library_path",
     "IQP_OK", "IQP_ERR_INVALID", "IQP_ERR_UNSUPPORTED", "IQP_ERR_HIP", "ONE_LAUNCH_MAX_TOKENS",
-    "IQP_ROPE_INTERLEAVED", "IQP_FP4_SCALE_OCP_FLOOR",
+    "IQP_ROPE_INTERLEAVED", "IQP_FP4_SCALE_OCP_FLOOR", "IQP_W_SCALES_PER_ROW",
 ]
 
 #: Up to this many tokens indexer_q_prep takes the one-launch path (measured on
@@ -29,6 +29,7 @@ ONE_LAUNCH_MAX_TOKENS = 16
 
 IQP_ROPE_INTERLEAVED = 0x1
 IQP_FP4_SCALE_OCP_FLOOR = 0x2
+IQP_W_SCALES_PER_ROW = 0x4
 
 IQP_OK = 0
 IQP_ERR_INVALID = 1
@@ -179,7 +180,8 @@ def fp8_quant_weight_128x128_ue8m0(w: torch.Tensor, q: torch.Tensor = None, scal
     return q, scales
 
 
-def _indexer_q_common(a, a_scales, w, w_scales, positions, cos_sin, n_heads, head_dim, rope_dim):
+def _indexer_q_common(a, a_scales, w, w_scales, positions, cos_sin, n_heads, head_dim, rope_dim,
+                      w_scale_rows: bool = False):
     a = _bytes_u8(a)
     w = _bytes_u8(w)
     dev = a.device
@@ -195,8 +197,9 @@ def _indexer_q_common(a, a_scales, w, w_scales, positions, cos_sin, n_heads, hea
     M, K = a.shape
     if w.shape[1] != K or w.shape[0] != n_heads * head_dim:
         raise ValueError(f"w must be [{n_heads * head_dim}, {K}], got {tuple(w.shape)}")
-    if tuple(w_scales.shape) != (n_heads * head_dim // 128, K // 128):
-        raise ValueError(f"w_scales must be [{n_heads * head_dim // 128}, {K // 128}]")
+    ws_rows = n_heads * head_dim if w_scale_rows else n_heads * head_dim // 128
+    if tuple(w_scales.shape) != (ws_rows, K // 128):
+        raise ValueError(f"w_scales must be [{ws_rows}, {K // 128}]")
     if positions.shape[0] != M or a_scales.shape[0] != M:
         raise ValueError("positions and a_scales need one row per token")
     if cos_sin.shape[1] != rope_dim:
@@ -216,7 +219,8 @@ def _convention_flags(rope_layout: str, scale_rule: str) -> int:
 
 def indexer_q_gemm_rope_fp4(a, a_scales, w, w_scales, positions, cos_sin, n_heads: int = 64,
                             head_dim: int = 128, rope_dim: int = 64, q_fp4=None, q_scales=None,
-                            rope_layout: str = "half_split", scale_rule: str = "ceil", stream=None):
+                            rope_layout: str = "half_split", scale_rule: str = "ceil",
+                            w_scale_layout: str = "tile_128x128", stream=None):
     """Fused block-scaled FP8 Q projection + RoPE + Hadamard-128 + FP4 e2m1.
 
     a: E4M3 [M, K] (uint8 or float8_e4m3fn) and a_scales: the packed words from
@@ -224,10 +228,14 @@ def indexer_q_gemm_rope_fp4(a, a_scales, w, w_scales, positions, cos_sin, n_head
     [H, K/128]; positions: int64 [M]; cos_sin: float32 [max_pos, 64].
     Returns ``(q_fp4, q_scales)``: uint8 [M, H, 64] packed codes and uint8
     [M, H, 4] UE8M0 scale bytes. rope_layout "interleaved" / scale_rule
-    "ocp_floor" select the convention variants (indexer_q_gemm_rope_fp4_ex).
+    "ocp_floor" / w_scale_layout "row_1x128" (w_scales uint8 [H*128, K/128])
+    select the convention variants (indexer_q_gemm_rope_fp4_ex).
     """
-    flags = _convention_flags(rope_layout, scale_rule)
-    a, args = _indexer_q_common(a, a_scales, w, w_scales, positions, cos_sin, n_heads, head_dim, rope_dim)
+    if w_scale_layout not in ("tile_128x128", "row_1x128"):
+        raise ValueError("w_scale_layout must be 'tile_128x128' or 'row_1x128'")
+    rows = w_scale_layout == "row_1x128"
+    flags = _convention_flags(rope_layout, scale_rule) | (IQP_W_SCALES_PER_ROW if rows else 0)
+    a, args = _indexer_q_common(a, a_scales, w, w_scales, positions, cos_sin, n_heads, head_dim, rope_dim, rows)
     M = a.shape[0]
     dev = a.device
     if q_fp4 is None:

@@ -129,7 +129,7 @@ int indexer_q_gemm_rope_fp4_ex(const void* a, int64_t lda, const int32_t* a_scal
                                int64_t M, int64_t K, int32_t H, int32_t D, int32_t rope_dim,
                                const int64_t* positions, const float* cos_sin, int64_t max_pos,
                                uint8_t* q_fp4, uint8_t* q_scales, int32_t flags, void* stream) {
-  if (flags & ~(IQP_ROPE_INTERLEAVED | IQP_FP4_SCALE_OCP_FLOOR)) return IQP_ERR_INVALID;
+  if (flags & ~(IQP_ROPE_INTERLEAVED | IQP_FP4_SCALE_OCP_FLOOR | IQP_W_SCALES_PER_ROW)) return IQP_ERR_INVALID;
   int st = check_indexer_q_args(a, lda, a_scales, as_stride_m, as_stride_w, w, ldw, w_scales, M, K,
                                 H, D, rope_dim, positions, cos_sin, max_pos, q_fp4, q_scales);
   if (st != IQP_OK || M == 0) return st;

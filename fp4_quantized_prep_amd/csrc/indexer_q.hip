@@ -97,6 +97,10 @@ struct Ctx {
   int nkb;
   int head;
   uint32_t wsc_lane;   // weight-scale bytes 4 lane .. 4 lane + 3 of the head (K blocks)
+  // per-row weight scales [H*128, nkb] (that variant only): the bytes of W row
+  // 32 tn + lane % 32 of the head are at wsr_row + tn * wsr_tn_stride
+  const uint8_t* wsr_row;
+  int64_t wsr_tn_stride;
   rsrc_t rw, ra, rs;                 // weights of the pair; activations and scale words of the tile
   uint32_t vw, va, vs;               // this lane's byte offsets into them
   uint32_t rd_w[2][2], rd_a[2][2];   // LDS operand-read bases [kh][lo/hi]
@@ -117,6 +121,8 @@ struct Ctx {
 #pragma unroll
     for (int b = 0; b < 4; ++b)
       if (4 * lane + b < nkb) wsc_lane |= (uint32_t)wsc[4 * lane + b] << (8 * b);
+    wsr_row = p.w_scales + ((int64_t)head_c * HEAD_DIM + (lane & 31)) * nkb;
+    wsr_tn_stride = (int64_t)32 * nkb;
     // copy i of this wave lands in rows 8 (wave + 4 i) + lane / 8, slot lane % 8,
     // which holds the row's chunk (lane % 8) ^ ((row / 2) % 8); as the slab
     // index wave + 4 i has the parity of wave, that is the same for every copy
@@ -200,10 +206,11 @@ struct Ctx {
 //   RKH >= 0: read the 64-deep half RKH of the block in stage RST into N;
 //   RSC: also the packed scale words of the block in stage RST into asn;
 //   NBLK copy blocks: block jd + b into stage (DST + b) & 1.
-template <int NTM, int RST, int RKH, bool RSC, int NBLK, int DST>
+//   ROW: the weight scale of MFMA tn is this lane's row's byte wsr[tn], not ws
+template <int NTM, int RST, int RKH, bool RSC, int NBLK, int DST, bool ROW>
 __device__ __forceinline__ void half_step(Ctx& c, v16f (&acc)[MAX_TM][4], const Frags<NTM>& F,
-                                          const int (&as)[MAX_TM], int ws, Frags<NTM>& N, int (&asn)[MAX_TM],
-                                          int jr, int jd) {
+                                          const int (&as)[MAX_TM], int ws, const int (&wsr)[4], Frags<NTM>& N,
+                                          int (&asn)[MAX_TM], int jr, int jd) {
   constexpr int NM = 4 * NTM;
   constexpr int NS = NM > 0 ? NM : 1;
   constexpr int NCOPY = NBLK * (2 * COPIES + 1);
@@ -217,8 +224,8 @@ __device__ __forceinline__ void half_step(Ctx& c, v16f (&acc)[MAX_TM][4], const 
   for (int slot = 0; slot < NS; ++slot) {
     if (slot < NM) {
       const int tn = slot / (NTM > 0 ? NTM : 1), tm = slot % (NTM > 0 ? NTM : 1);
-      acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.w[tn], F.a[tm], acc[tm][tn], 0, 0, 0, ws, 0,
-                                                                    as[tm]);
+      acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.w[tn], F.a[tm], acc[tm][tn], 0, 0, 0,
+                                                                    ROW ? wsr[tn] : ws, 0, as[tm]);
       asm volatile("" : "+a"(acc[tm][tn]));   // the MFMA stays in its slot (no sinking past this)
     }
 #pragma unroll
@@ -260,10 +267,12 @@ enum { MODE_STEADY, MODE_PENULT, MODE_LAST, MODE_ONLY };
 //   ONLY (a single K block): switch buffers, copy next blocks 0 and 1.
 // LAST and ONLY fetch the RoPE rows of the epilogue's first sub-tile before
 // the barrier.
-template <int NTM, int MODE, int ST, bool IL>
+// ROW (per-row weight scales): wsr holds block j's bytes on entry and block
+// j+1's on exit, loaded here one block ahead so the barrier's wait covers them.
+template <int NTM, int MODE, int ST, bool IL, bool ROW>
 __device__ __forceinline__ void k_block(Ctx& c, int j, v16f (&acc)[MAX_TM][4], Frags<NTM>& f0, Frags<NTM>& f1,
                                         int (&as0)[MAX_TM], int (&as1)[MAX_TM], int64_t next_tbase,
-                                        RopeCS& rope0, int64_t pos0) {
+                                        RopeCS& rope0, int64_t pos0, int (&wsr)[4]) {
   // a branch here would let the compiler sink the MFMAs out of their slots:
   // the block's weight-scale byte comes from a register, its activation
   // scale bytes from the words read one half-step earlier
@@ -274,8 +283,14 @@ __device__ __forceinline__ void k_block(Ctx& c, int j, v16f (&acc)[MAX_TM][4], F
   if constexpr (MODE == MODE_LAST || MODE == MODE_ONLY) {
     if constexpr (NTM > 0) rope0 = load_rope<IL>(pos0, c.half, c.p);
   }
+  constexpr bool PREFETCH = ROW && (MODE == MODE_STEADY || MODE == MODE_PENULT);
+  int wsn[4] = {0, 0, 0, 0};
+  if constexpr (PREFETCH) {
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn) wsn[tn] = c.wsr_row[tn * c.wsr_tn_stride + j + 1];
+  }
   __builtin_amdgcn_sched_barrier(0);
-  half_step<NTM, ST, 1, false, 0, 0>(c, acc, f0, as, ws, f1, as1, j, 0);
+  half_step<NTM, ST, 1, false, 0, 0, ROW>(c, acc, f0, as, ws, wsr, f1, as1, j, 0);
   __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);
   // block j+1 must have landed, except after the last block: there only the
   // next tile's copies are in flight, and the next tile's start waits for them
@@ -283,19 +298,23 @@ __device__ __forceinline__ void k_block(Ctx& c, int j, v16f (&acc)[MAX_TM][4], F
   block_barrier();   // all of block j read by every wave (and block j+1 landed)
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (MODE == MODE_STEADY)
-    half_step<NTM, ST ^ 1, 0, true, 1, ST>(c, acc, f1, as, ws, f0, as1, j + 1, j + 2);
+    half_step<NTM, ST ^ 1, 0, true, 1, ST, ROW>(c, acc, f1, as, ws, wsr, f0, as1, j + 1, j + 2);
   if constexpr (MODE == MODE_PENULT) {
     c.set_tile(next_tbase);
-    half_step<NTM, ST ^ 1, 0, true, 1, ST>(c, acc, f1, as, ws, f0, as1, j + 1, ST);
+    half_step<NTM, ST ^ 1, 0, true, 1, ST, ROW>(c, acc, f1, as, ws, wsr, f0, as1, j + 1, ST);
   }
   if constexpr (MODE == MODE_LAST)
-    half_step<NTM, 0, -1, false, 1, ST>(c, acc, f1, as, ws, f0, as1, 0, ST);
+    half_step<NTM, 0, -1, false, 1, ST, ROW>(c, acc, f1, as, ws, wsr, f0, as1, 0, ST);
   if constexpr (MODE == MODE_ONLY) {
     c.set_tile(next_tbase);
-    half_step<NTM, 0, -1, false, 2, 0>(c, acc, f1, as, ws, f0, as1, 0, 0);
+    half_step<NTM, 0, -1, false, 2, 0, ROW>(c, acc, f1, as, ws, wsr, f0, as1, 0, 0);
   }
 #pragma unroll
   for (int tm = 0; tm < MAX_TM; ++tm) as0[tm] = as1[tm];
+  if constexpr (PREFETCH) {
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn) wsr[tn] = wsn[tn];
+  }
 }
 
 // Shapes of the K loop: 1 block, 2 blocks, an even count >= 4, an odd count >= 3.
@@ -326,6 +345,11 @@ __device__ __forceinline__ void run_tile(Ctx& c, int64_t tbase, int64_t next_tba
   int64_t pos[MAX_TM > 0 ? MAX_TM : 1];
 #pragma unroll
   for (int tm = 0; tm < NTM; ++tm) pos[tm] = load_position(t_lane + TM_STRIDE * tm, c.p);
+  int wsr[4] = {0, 0, 0, 0};   // per-row weight scales of block 0 (that variant only)
+  if constexpr (stage_row_scales(STAGE)) {
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn) wsr[tn] = c.wsr_row[tn * c.wsr_tn_stride];
+  }
   __builtin_amdgcn_s_waitcnt(WAITCNT_VM0);
   block_barrier();
 #pragma unroll
@@ -342,24 +366,24 @@ __device__ __forceinline__ void run_tile(Ctx& c, int64_t tbase, int64_t next_tba
   const int nkb = c.nkb;
   const int64_t p0 = NTM > 0 ? pos[0] : 0;
   if constexpr (SHAPE == SHAPE_ONE) {
-    k_block<NTM, MODE_ONLY, 0, stage_interleaved(STAGE)>(c, 0, acc, f0, f1, as0, as1, next_tbase, rope, p0);
+    k_block<NTM, MODE_ONLY, 0, stage_interleaved(STAGE), stage_row_scales(STAGE)>(c, 0, acc, f0, f1, as0, as1, next_tbase, rope, p0, wsr);
   } else if constexpr (SHAPE == SHAPE_TWO) {
-    k_block<NTM, MODE_PENULT, 0, stage_interleaved(STAGE)>(c, 0, acc, f0, f1, as0, as1, next_tbase, rope, 0);
-    k_block<NTM, MODE_LAST, 1, stage_interleaved(STAGE)>(c, 1, acc, f0, f1, as0, as1, next_tbase, rope, p0);
+    k_block<NTM, MODE_PENULT, 0, stage_interleaved(STAGE), stage_row_scales(STAGE)>(c, 0, acc, f0, f1, as0, as1, next_tbase, rope, 0, wsr);
+    k_block<NTM, MODE_LAST, 1, stage_interleaved(STAGE), stage_row_scales(STAGE)>(c, 1, acc, f0, f1, as0, as1, next_tbase, rope, p0, wsr);
   } else {
-    k_block<NTM, MODE_STEADY, 0, stage_interleaved(STAGE)>(c, 0, acc, f0, f1, as0, as1, 0, rope, 0);
+    k_block<NTM, MODE_STEADY, 0, stage_interleaved(STAGE), stage_row_scales(STAGE)>(c, 0, acc, f0, f1, as0, as1, 0, rope, 0, wsr);
     int j = 1;
     for (; j + 3 < nkb; j += 2) {
-      k_block<NTM, MODE_STEADY, 1, stage_interleaved(STAGE)>(c, j, acc, f0, f1, as0, as1, 0, rope, 0);
-      k_block<NTM, MODE_STEADY, 0, stage_interleaved(STAGE)>(c, j + 1, acc, f0, f1, as0, as1, 0, rope, 0);
+      k_block<NTM, MODE_STEADY, 1, stage_interleaved(STAGE), stage_row_scales(STAGE)>(c, j, acc, f0, f1, as0, as1, 0, rope, 0, wsr);
+      k_block<NTM, MODE_STEADY, 0, stage_interleaved(STAGE), stage_row_scales(STAGE)>(c, j + 1, acc, f0, f1, as0, as1, 0, rope, 0, wsr);
     }
     if constexpr (SHAPE == SHAPE_EVEN) {   // three left: j (stage 1), j+1, j+2
-      k_block<NTM, MODE_STEADY, 1, stage_interleaved(STAGE)>(c, j, acc, f0, f1, as0, as1, 0, rope, 0);
-      k_block<NTM, MODE_PENULT, 0, stage_interleaved(STAGE)>(c, j + 1, acc, f0, f1, as0, as1, next_tbase, rope, 0);
-      k_block<NTM, MODE_LAST, 1, stage_interleaved(STAGE)>(c, j + 2, acc, f0, f1, as0, as1, next_tbase, rope, p0);
+      k_block<NTM, MODE_STEADY, 1, stage_interleaved(STAGE), stage_row_scales(STAGE)>(c, j, acc, f0, f1, as0, as1, 0, rope, 0, wsr);
+      k_block<NTM, MODE_PENULT, 0, stage_interleaved(STAGE), stage_row_scales(STAGE)>(c, j + 1, acc, f0, f1, as0, as1, next_tbase, rope, 0, wsr);
+      k_block<NTM, MODE_LAST, 1, stage_interleaved(STAGE), stage_row_scales(STAGE)>(c, j + 2, acc, f0, f1, as0, as1, next_tbase, rope, p0, wsr);
     } else {                               // two left: j (stage 1), j+1
-      k_block<NTM, MODE_PENULT, 1, stage_interleaved(STAGE)>(c, j, acc, f0, f1, as0, as1, next_tbase, rope, 0);
-      k_block<NTM, MODE_LAST, 0, stage_interleaved(STAGE)>(c, j + 1, acc, f0, f1, as0, as1, next_tbase, rope, p0);
+      k_block<NTM, MODE_PENULT, 1, stage_interleaved(STAGE), stage_row_scales(STAGE)>(c, j, acc, f0, f1, as0, as1, next_tbase, rope, 0, wsr);
+      k_block<NTM, MODE_LAST, 0, stage_interleaved(STAGE), stage_row_scales(STAGE)>(c, j + 1, acc, f0, f1, as0, as1, next_tbase, rope, p0, wsr);
     }
   }
 
@@ -479,6 +503,10 @@ hipError_t launch_kernel(const IndexerQArgs& a_in, int stage, hipStream_t stream
     case stage_of_variant(1): hipLaunchKernelGGL(indexer_q_kernel<stage_of_variant(1)>, grid, block, 0, stream, a); break;
     case stage_of_variant(2): hipLaunchKernelGGL(indexer_q_kernel<stage_of_variant(2)>, grid, block, 0, stream, a); break;
     case stage_of_variant(3): hipLaunchKernelGGL(indexer_q_kernel<stage_of_variant(3)>, grid, block, 0, stream, a); break;
+    case stage_of_variant(4): hipLaunchKernelGGL(indexer_q_kernel<stage_of_variant(4)>, grid, block, 0, stream, a); break;
+    case stage_of_variant(5): hipLaunchKernelGGL(indexer_q_kernel<stage_of_variant(5)>, grid, block, 0, stream, a); break;
+    case stage_of_variant(6): hipLaunchKernelGGL(indexer_q_kernel<stage_of_variant(6)>, grid, block, 0, stream, a); break;
+    case stage_of_variant(7): hipLaunchKernelGGL(indexer_q_kernel<stage_of_variant(7)>, grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -488,7 +516,7 @@ hipError_t launch_kernel(const IndexerQArgs& a_in, int stage, hipStream_t stream
 
 hipError_t launch_indexer_q_variant(const IndexerQArgs& a, int variant, hipStream_t stream) {
   if (variant == 0) return launch_indexer_q(a, -1, stream);
-  if (variant < 0 || variant > 3) return hipErrorInvalidValue;
+  if (variant < 0 || variant > 7) return hipErrorInvalidValue;
   return launch_kernel(a, stage_of_variant(variant), stream);
 }
 

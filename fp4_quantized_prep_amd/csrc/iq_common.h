@@ -57,11 +57,13 @@ __device__ __forceinline__ int fp4_exponent_floor(float amax) {
 
 // Convention variants of the FP4-output kernels ride on the STAGE template
 // argument: STAGE = -1 - v with v bit 0 = interleaved RoPE pairs (2i, 2i+1),
-// bit 1 = OCP floor-rule FP4 scales; the diagnostic stages (>= 0) and
-// STAGE = -1 take the defaults (pairs (i, i+32), e = ceil(log2(amax / 6))).
+// bit 1 = OCP floor-rule FP4 scales, bit 2 = one weight scale per row and K
+// block; the diagnostic stages (>= 0) and STAGE = -1 take the defaults (pairs
+// (i, i+32), e = ceil(log2(amax / 6)), one weight scale per 128x128 tile).
 constexpr int stage_of_variant(int v) { return -1 - v; }
 constexpr bool stage_interleaved(int stage) { return stage < 0 && ((-1 - stage) & 1); }
 constexpr bool stage_floor(int stage) { return stage < 0 && ((-1 - stage) & 2); }
+constexpr bool stage_row_scales(int stage) { return stage < 0 && ((-1 - stage) & 4); }
 
 // ---------------------------------------------------------------------------
 // Epilogue for one 32-token column tile of one head: acc[tn][r] holds head dim

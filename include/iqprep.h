@@ -66,6 +66,9 @@ extern "C" {
 #define IQP_ROPE_INTERLEAVED     0x1  /* RoPE pairs (2i, 2i+1), i < rope_dim/2, instead of (i, i + rope_dim/2) */
 #define IQP_FP4_SCALE_OCP_FLOOR  0x2  /* FP4 scale e = floor(log2 max(amax, 1e-4)) - 2 (OCP MX rule), codes
                                          saturating at +-6, instead of e = ceil(log2(amax / 6)) */
+#define IQP_W_SCALES_PER_ROW     0x4  /* indexer_q_gemm_rope_fp4_ex only: w_scales holds one UE8M0 byte per
+                                         weight row and K block, [H*D, K/128] row-major, instead of one per
+                                         128x128 tile */
 
 /*
  * fp8_quant_1x128_ue8m0 — packed-UE8M0 FP8 activation quantization.
@@ -173,7 +176,10 @@ int indexer_q_gemm_rope_fp4(const void* a, int64_t lda,
  *   IQP_ROPE_INTERLEAVED      pair i < 32 is (Q_2i, Q_2i+1), rotated by the
  *                             angle of table columns i and 32 + i as before;
  *   IQP_FP4_SCALE_OCP_FLOOR   e = floor(log2 max(amax, 1e-4)) - 2 (so e >= -16),
- *                             codes = E2M1 RNE of z * 2^-e saturated at +-6.
+ *                             codes = E2M1 RNE of z * 2^-e saturated at +-6;
+ *   IQP_W_SCALES_PER_ROW      w_scales is UE8M0 [H*D, K/128] row-major (one
+ *                             byte per weight row n and K block j), and the
+ *                             projection uses ew(n, j) in place of ew(h, j).
  * Other bits: IQP_ERR_INVALID. A non-zero flags value always runs the general
  * tiled kernel (slower than the K = 1536 production kernels).
  */

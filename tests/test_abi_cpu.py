@@ -98,8 +98,10 @@ def fused_ex(iqp, flags, M=4, K=256, H=2, D=128, rd=64, lda=256, ldw=256):
 
 def test_fused_ex_argument_checks(iqp):
     inv, uns = iqp.IQP_ERR_INVALID, iqp.IQP_ERR_UNSUPPORTED
-    assert fused_ex(iqp, 4) == inv                              # unknown convention bit
+    assert fused_ex(iqp, 8) == inv                              # unknown convention bit
     assert fused_ex(iqp, -1) == inv
+    assert fused_ex(iqp, iqp.IQP_W_SCALES_PER_ROW | 3, M=0) == iqp.IQP_OK
+    assert epilogue(iqp, flags=iqp.IQP_W_SCALES_PER_ROW) == inv  # no weights in the standalone epilogue
     assert fused_ex(iqp, iqp.IQP_ROPE_INTERLEAVED, M=-3) == inv  # the base call's checks still apply
     assert fused_ex(iqp, iqp.IQP_FP4_SCALE_OCP_FLOOR, D=64) == uns
     assert fused_ex(iqp, 3, lda=128) == inv

@@ -375,3 +375,72 @@ def test_fused_chain_zero_token_rows(gpu_lib, weights, table, M):
     ref = oracle_chain_from_x(x, codes, sb, pos, 64)
     rep = C.check_fp4(q, s, ref["z"], ref["q_fp4"], ref["q_scales"])
     assert rep["ok"], rep
+
+
+# ---------------------------------------------------------------- per-row (1x128) weight scales
+
+
+def row_scale_weights(H, K, seed):
+    """E4M3 weight codes [H*128, K] with one UE8M0 byte per row and K block:
+    the synthetic tile bytes, each row's moved by -1, 0 or +1 per block."""
+    codes, sb = S.weights(N=H * 128, K=K, seed=seed)
+    g = np.random.default_rng([seed, 7])
+    rows = np.repeat(sb.numpy().astype(np.int64), 128, axis=0) + g.integers(-1, 2, size=(H * 128, K // 128))
+    return codes, torch.from_numpy(rows.astype(np.uint8))
+
+
+@pytest.mark.parametrize("M,H,K", [(5, 64, 1536), (128, 64, 1536), (300, 64, 1536), (70, 3, 1024)])
+def test_fused_chain_row_weight_scales(gpu_lib, table, M, H, K):
+    codes, wsr = row_scale_weights(H, K, 103)
+    if K == 1536:
+        inp = S.indexer_q_inputs("indexer_q_m128", M=M)
+        x, pos = inp["x"], inp["positions"]
+    else:
+        g = S.rng("indexer_q_m128", 960)
+        x = S.activations_outlier(g, M, K)
+        pos = S.positions_uniform(g, M, 4096)
+    print(f"[row scales] M={M} H={H} K={K}", flush=True)
+    a, a_s = gpu_lib.fp8_quant_1x128_ue8m0(x.cuda())
+    q, s = gpu_lib.indexer_q_gemm_rope_fp4(a, a_s, codes.cuda(), wsr.cuda(), pos.cuda(), table[4096], n_heads=H,
+                                           w_scale_layout="row_1x128")
+    torch.cuda.synchronize()
+    ref = oracle_chain_from_x(x, codes, wsr, pos, H)
+    rep = C.check_fp4(q.cpu().numpy(), s.cpu().numpy(), ref["z"], ref["q_fp4"], ref["q_scales"])
+    print(rep)
+    assert rep["ok"], rep
+
+
+def test_row_weight_scales_equal_to_tile_scales_give_the_same_bytes(gpu_lib, table):
+    """Per-row bytes that repeat each tile's byte over its 128 rows: the same
+    output bytes as the per-tile call (both on the general kernel, K = 1024),
+    for the default and the interleaved / floor-rule conventions."""
+    H, M, K = 4, 90, 1024
+    codes, sb = S.weights(N=H * 128, K=K, seed=104)
+    rows = torch.from_numpy(np.repeat(sb.numpy(), 128, axis=0).copy())
+    g = S.rng("indexer_q_m128", 961)
+    x = S.activations_outlier(g, M, K)
+    pos = S.positions_uniform(g, M, 4096).cuda()
+    a, a_s = gpu_lib.fp8_quant_1x128_ue8m0(x.cuda())
+    for layout, rule in (("half_split", "ceil"), ("interleaved", "ocp_floor")):
+        q0, s0 = gpu_lib.indexer_q_gemm_rope_fp4(a, a_s, codes.cuda(), sb.cuda(), pos, table[4096], n_heads=H,
+                                                 rope_layout=layout, scale_rule=rule)
+        q1, s1 = gpu_lib.indexer_q_gemm_rope_fp4(a, a_s, codes.cuda(), rows.cuda(), pos, table[4096], n_heads=H,
+                                                 rope_layout=layout, scale_rule=rule, w_scale_layout="row_1x128")
+        torch.cuda.synchronize()
+        assert torch.equal(q0.cpu(), q1.cpu()) and torch.equal(s0.cpu(), s1.cpu()), (layout, rule)
+
+
+def test_row_weight_scales_with_variants(gpu_lib, table):
+    H, M, K = 3, 70, 1536
+    codes, wsr = row_scale_weights(H, K, 105)
+    inp = S.indexer_q_inputs("indexer_q_m128", M=M)
+    x, pos = inp["x"], inp["positions"]
+    a, a_s = gpu_lib.fp8_quant_1x128_ue8m0(x.cuda())
+    q, s = gpu_lib.indexer_q_gemm_rope_fp4(a, a_s, codes.cuda(), wsr.cuda(), pos.cuda(), table[4096], n_heads=H,
+                                           rope_layout="interleaved", scale_rule="ocp_floor",
+                                           w_scale_layout="row_1x128")
+    torch.cuda.synchronize()
+    ref = oracle_chain_from_x(x, codes, wsr, pos, H, "interleaved", "ocp_floor")
+    rep = C.check_fp4(q.cpu().numpy(), s.cpu().numpy(), ref["z"], ref["q_fp4"], ref["q_scales"],
+                      scale_rule="ocp_floor")
+    assert rep["ok"], rep
