@@ -51,6 +51,16 @@ def test_weight_quant_edge_tiles(gpu_lib):
     check(gpu_lib, bf16(w))
 
 
+@pytest.mark.parametrize("N,K", [(128, 128), (256, 128), (640, 896), (1152, 1408)])
+def test_weight_quant_tile_counts(gpu_lib, N, K):
+    """Tile counts of 1, 2, 35 and 99: workgroups that walk one, two or three
+    tiles, and a last workgroup with fewer than the others."""
+    g = np.random.default_rng([100, 10, N, K])
+    w = g.standard_normal((N, K)) * 0.02 * np.exp2(g.integers(-3, 4, size=(N // 128, 1, K // 128, 1)).repeat(
+        128, axis=1).repeat(128, axis=3).reshape(N, K))
+    check(gpu_lib, bf16(w))
+
+
 def test_weight_quant_projection_weight_sampled_tile_rows(gpu_lib):
     g = np.random.default_rng([100, 9])
     w = bf16(g.standard_normal((8192, 1536)) * 0.02)
