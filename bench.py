@@ -203,10 +203,16 @@ def main():
         max(20, min(K, 100)))
     flops = 2.0 * M * (N_HEADS * HEAD_DIM) * K_PROJ
     fused_tflops = flops / t_fused / 1e12
+    # context: the same projection with both convention flags (interleaved RoPE,
+    # OCP floor-rule FP4 scales), the pipelined kernel's variant build
+    t_variant = graph_launch_time(
+        lambda i: iqp.indexer_q_gemm_rope_fp4(a, a_s, w, wsb, pos, cs, n_heads=N_HEADS, q_fp4=q, q_scales=qs,
+                                              rope_layout="interleaved", scale_rule="ocp_floor"),
+        max(20, min(K, 100)))
     print(f"[bench] chain: {ms_per_step * 1e3:.1f} us/step (wall {wall * 1e6 / K:.1f} us); "
           f"fused kernel {t_fused * 1e6:.1f} us back to back = {fused_tflops:.0f} TFLOP/s; with an event "
-          f"pair around each kernel: quant {t_quant * 1e6:.1f} us, fused {t_fused_ev * 1e6:.1f} us",
-          file=sys.stderr, flush=True)
+          f"pair around each kernel: quant {t_quant * 1e6:.1f} us, fused {t_fused_ev * 1e6:.1f} us; "
+          f"with both convention flags {t_variant * 1e6:.1f} us", file=sys.stderr, flush=True)
 
     # ---- standalone quantizer on [4632, 7168], rotating buffer sets (> 256 MiB)
     xq_cpu = S.quant_input("quant_4632x7168")
@@ -322,6 +328,7 @@ def main():
             "algorithmic_flops_per_launch": flops,
             "avg_launch_us": t_fused * 1e6,
             "avg_launch_us_event_pair_each": t_fused_ev * 1e6,
+            "avg_launch_us_interleaved_rope_ocp_floor_scales": t_variant * 1e6,
         },
         "quant_roofline": {
             "kernel": "fp8_quant_1x128_kernel on [4632,7168] (5 rotating buffer sets, launches back to back "

@@ -514,24 +514,38 @@ hipError_t launch_kernel(const IndexerQArgs& a_in, int stage, hipStream_t stream
 
 }  // namespace
 
-hipError_t launch_indexer_q_variant(const IndexerQArgs& a, int variant, hipStream_t stream) {
-  if (variant == 0) return launch_indexer_q(a, -1, stream);
+// the pipelined kernel's launch arguments: one workgroup per CU, each head
+// pair gets CUs / pairs chunks of whole 128-token tiles
+static bool pipe_args(const IndexerQArgs& a_in, IndexerQArgs& a) {
+  a = a_in;
+  const int64_t npairs = (a.H + 1) / 2;
+  const int64_t ntiles = (a.M + 127) / 128;
+  int64_t cpp = cu_count() / npairs;
+  cpp = cpp < 1 ? 1 : cpp;
+  cpp = cpp < ntiles ? cpp : ntiles;
+  if (npairs * cpp > 0x7FFFFFFF) return false;
+  a.chunks = (int32_t)cpp;
+  return true;
+}
+
+hipError_t launch_indexer_q_variant(const IndexerQArgs& a_in, int variant, hipStream_t stream) {
+  if (variant == 0) return launch_indexer_q(a_in, -1, stream);
   if (variant < 0 || variant > 7) return hipErrorInvalidValue;
-  return launch_kernel(a, stage_of_variant(variant), stream);
+  if (variant <= 3 && !indexer_q_small_supported(a_in) && indexer_q_pipe_supported(a_in)) {
+    IndexerQArgs a;
+    if (!pipe_args(a_in, a)) return hipErrorInvalidValue;
+    return variant == 1 ? launch_indexer_q_pipe_v1(a, stream)
+         : variant == 2 ? launch_indexer_q_pipe_v2(a, stream)
+                        : launch_indexer_q_pipe_v3(a, stream);
+  }
+  return launch_kernel(a_in, stage_of_variant(variant), stream);
 }
 
 hipError_t launch_indexer_q(const IndexerQArgs& a_in, int stage, hipStream_t stream) {
   if (stage == -1 && indexer_q_small_supported(a_in)) return launch_indexer_q_small(a_in, stream);
   if (stage == -1 && indexer_q_pipe_supported(a_in)) {
-    // one workgroup per CU: each head pair gets CUs / pairs chunks of whole 128-token tiles
-    IndexerQArgs a = a_in;
-    const int64_t npairs = (a.H + 1) / 2;
-    const int64_t ntiles = (a.M + 127) / 128;
-    int64_t cpp = cu_count() / npairs;
-    cpp = cpp < 1 ? 1 : cpp;
-    cpp = cpp < ntiles ? cpp : ntiles;
-    if (npairs * cpp > 0x7FFFFFFF) return hipErrorInvalidValue;
-    a.chunks = (int32_t)cpp;
+    IndexerQArgs a;
+    if (!pipe_args(a_in, a)) return hipErrorInvalidValue;
     return launch_indexer_q_pipe(a, stream);
   }
   return launch_kernel(a_in, stage, stream);

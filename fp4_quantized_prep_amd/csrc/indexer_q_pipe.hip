@@ -48,9 +48,20 @@
 
 #include "iq_common.h"
 
+// Convention variant compiled into this translation unit (bit 0: interleaved
+// RoPE pairs, bit 1: OCP floor-rule FP4 scales; 0: the defaults). The variant
+// units define it and the launcher's name before including this file.
+#ifndef IQP_PIPE_VARIANT
+#define IQP_PIPE_VARIANT 0
+#define IQP_PIPE_LAUNCH launch_indexer_q_pipe
+#endif
+
 namespace iqp {
 namespace {
 namespace pipe {
+
+constexpr bool VAR_IL = (IQP_PIPE_VARIANT & 1) != 0;
+constexpr bool VAR_FLOOR = (IQP_PIPE_VARIANT & 2) != 0;
 
 constexpr int NWAVES = 4;
 constexpr int NTHREADS = NWAVES * 64;
@@ -258,13 +269,26 @@ __device__ __forceinline__ constexpr int r_clear(int k, int rb) { return (k & (r
 
 // load L (0..7) of the RoPE rows of position pos: cosines (even L) or sines
 // of angle group L / 2, this lane's half of it
+// (interleaved: group j is table entries 8j + 2half + {0, 1, 4, 5}, the
+// layout load_rope<true> gives)
 __device__ __forceinline__ void rope_part(Epi& es, int64_t pos, int L, const Ctx& c) {
   pos = pos < 0 ? 0 : (pos >= c.p.max_pos ? c.p.max_pos - 1 : pos);
-  const float* cs = c.p.cos_sin + pos * 64 + 8 * (L >> 1) + 4 * fresh(c.half);
-  if (L & 1)
-    es.rope.s[L >> 1] = *reinterpret_cast<const v4f*>(cs + 32);
-  else
-    es.rope.c[L >> 1] = *reinterpret_cast<const v4f*>(cs);
+  if constexpr (!VAR_IL) {
+    const float* cs = c.p.cos_sin + pos * 64 + 8 * (L >> 1) + 4 * fresh(c.half);
+    if (L & 1)
+      es.rope.s[L >> 1] = *reinterpret_cast<const v4f*>(cs + 32);
+    else
+      es.rope.c[L >> 1] = *reinterpret_cast<const v4f*>(cs);
+  } else {
+    typedef float v2f __attribute__((ext_vector_type(2)));
+    const float* cs = c.p.cos_sin + pos * 64 + 8 * (L >> 1) + 2 * fresh(c.half) + ((L & 1) ? 32 : 0);
+    const v2f lo = *reinterpret_cast<const v2f*>(cs), hi = *reinterpret_cast<const v2f*>(cs + 4);
+    const v4f r = v4f{lo[0], lo[1], hi[0], hi[1]};
+    if (L & 1)
+      es.rope.s[L >> 1] = r;
+    else
+      es.rope.c[L >> 1] = r;
+  }
 }
 
 // LAST: no tile follows (the sub-tile after the last one has no RoPE rows to fetch)
@@ -288,12 +312,19 @@ __device__ __forceinline__ void epi_item(Epi& es, v16f (&accp)[MAX_TM][4], int i
     }
   } else if constexpr (h == 1) {
     if (i == 0) asm volatile("" : "+a"(accp[tm][0]), "+a"(accp[tm][1]));
-    if (i < 16) {                  // RoPE pair (i, i + 32), i = 8 g + 4 half + s
+    if (i < 16 && !VAR_IL) {       // RoPE pair (i, i + 32), i = 8 g + 4 half + s
       const int g = i >> 2, s = i & 3;
       const float x = accp[tm][0][4 * g + s], y = accp[tm][1][4 * g + s];
       const float cc = es.rope.c[g][s], ss = es.rope.s[g][s];
       es.v[0][4 * g + s] = x * cc - y * ss;
       es.v[1][4 * g + s] = y * cc + x * ss;
+    } else if (i < 16) {           // interleaved pair 16 tn + 4 g + 2 half + k: registers 4g + 2k, 4g + 2k + 1
+      const int tn = i >> 3, g = (i >> 1) & 3, k = i & 1, r = 4 * g + 2 * k;
+      const float x = accp[tm][tn][r], y = accp[tm][tn][r + 1];
+      const float cc = es.rope.c[2 * tn + (g >> 1)][2 * (g & 1) + k];
+      const float ss = es.rope.s[2 * tn + (g >> 1)][2 * (g & 1) + k];
+      es.v[tn][r] = x * cc - y * ss;
+      es.v[tn][r + 1] = y * cc + x * ss;
     } else {
       const int k = i - 16, tn = k >> 3, r = r_clear(k & 7, 1);
       const float a = es.v[tn][r], b = es.v[tn][r | 1];
@@ -362,7 +393,7 @@ __device__ __forceinline__ void epi_item(Epi& es, v16f (&accp)[MAX_TM][4], int i
       for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(es.v[tn][r]));
       float m0, m1;
       swap32(m, m, m0, m1);
-      const int e = fp4_exponent(fmaxf(m0, m1));
+      const int e = VAR_FLOOR ? fp4_exponent_floor(fmaxf(m0, m1)) : fp4_exponent(fmaxf(m0, m1));
       if (tn == 0) es.sbytes = 0;
       es.sbytes |= (uint32_t)(e + 127) << (8 * tn);
       const float scale = __uint_as_float((uint32_t)(e + 127) << 23);
@@ -516,7 +547,7 @@ __device__ __forceinline__ void k_loop(Ctx& c, v16f (&acc)[MAX_TM][4], Frags& f0
       for (int r = 0; r < 16; ++r) acc[tm][tn][r] = 0.f;
 #define IQP_KB(J) k_block<NTM, J, NTMP, false>(c, acc, f0, f1, as0, as1, es, accp);
   IQP_KB(0) IQP_KB(1) IQP_KB(2) IQP_KB(3) IQP_KB(4) IQP_KB(5) IQP_KB(6) IQP_KB(7) IQP_KB(8) IQP_KB(9)
-  if constexpr (NTMP == 0) es.rope = load_rope(es.npos0, c.half, c.p);
+  if constexpr (NTMP == 0) es.rope = load_rope<VAR_IL>(es.npos0, c.half, c.p);
   IQP_KB(10) IQP_KB(11)
 #undef IQP_KB
   // every MFMA of the tile completes here
@@ -614,12 +645,14 @@ void indexer_q_pipe_kernel(IndexerQArgs p) {
 
 }  // namespace
 
+#if IQP_PIPE_VARIANT == 0
 // token indices are held in 32-bit registers
 bool indexer_q_pipe_supported(const IndexerQArgs& a) {
   return a.nkb == pipe::NKB && a.M <= 0x7FFFFFFF - 2 * pipe::TOKS;
 }
+#endif
 
-hipError_t launch_indexer_q_pipe(const IndexerQArgs& a, hipStream_t stream) {
+hipError_t IQP_PIPE_LAUNCH(const IndexerQArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)((a.H + 1) / 2) * a.chunks)), block(pipe::NTHREADS);
   hipLaunchKernelGGL(indexer_q_pipe_kernel, grid, block, 0, stream, a);
   return hipGetLastError();

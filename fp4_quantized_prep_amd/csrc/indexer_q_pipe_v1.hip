@@ -1,0 +1,5 @@
+// The pipelined fused indexer-Q kernel of indexer_q_pipe.hip compiled with a
+// convention variant: interleaved RoPE pairs (2i, 2i + 1).
+#define IQP_PIPE_VARIANT 1
+#define IQP_PIPE_LAUNCH launch_indexer_q_pipe_v1
+#include "indexer_q_pipe.hip"

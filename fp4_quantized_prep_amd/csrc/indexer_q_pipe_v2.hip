@@ -1,0 +1,5 @@
+// The pipelined fused indexer-Q kernel of indexer_q_pipe.hip compiled with a
+// convention variant: OCP floor-rule FP4 scales.
+#define IQP_PIPE_VARIANT 2
+#define IQP_PIPE_LAUNCH launch_indexer_q_pipe_v2
+#include "indexer_q_pipe.hip"

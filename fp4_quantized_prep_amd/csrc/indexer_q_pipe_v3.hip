@@ -1,0 +1,5 @@
+// The pipelined fused indexer-Q kernel of indexer_q_pipe.hip compiled with a
+// convention variant: interleaved RoPE pairs and OCP floor-rule FP4 scales.
+#define IQP_PIPE_VARIANT 3
+#define IQP_PIPE_LAUNCH launch_indexer_q_pipe_v3
+#include "indexer_q_pipe.hip"
