@@ -180,7 +180,9 @@ int indexer_q_gemm_rope_fp4(const void* a, int64_t lda,
  *   IQP_W_SCALES_PER_ROW      w_scales is UE8M0 [H*D, K/128] row-major (one
  *                             byte per weight row n and K block j), and the
  *                             projection uses ew(n, j) in place of ew(h, j).
- * Other bits: IQP_ERR_INVALID. A non-zero flags value always runs the general
+ * Other bits: IQP_ERR_INVALID. With only the RoPE / FP4 flags the call runs
+ * the pipelined kernel's variant build wherever the base call would run the
+ * pipelined kernel (K = 1536 above 256 tokens); otherwise it runs the general
  * tiled kernel (slower than the K = 1536 production kernels).
  */
 int indexer_q_gemm_rope_fp4_ex(const void* a, int64_t lda,
