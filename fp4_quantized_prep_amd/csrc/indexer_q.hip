@@ -531,7 +531,11 @@ static bool pipe_args(const IndexerQArgs& a_in, IndexerQArgs& a) {
 hipError_t launch_indexer_q_variant(const IndexerQArgs& a_in, int variant, hipStream_t stream) {
   if (variant == 0) return launch_indexer_q(a_in, -1, stream);
   if (variant < 0 || variant > 7) return hipErrorInvalidValue;
-  if (variant <= 3 && !indexer_q_small_supported(a_in) && indexer_q_pipe_supported(a_in)) {
+  if (variant <= 3 && indexer_q_small_supported(a_in))
+    return variant == 1 ? launch_indexer_q_small_v1(a_in, stream)
+         : variant == 2 ? launch_indexer_q_small_v2(a_in, stream)
+                        : launch_indexer_q_small_v3(a_in, stream);
+  if (variant <= 3 && indexer_q_pipe_supported(a_in)) {
     IndexerQArgs a;
     if (!pipe_args(a_in, a)) return hipErrorInvalidValue;
     return variant == 1 ? launch_indexer_q_pipe_v1(a, stream)

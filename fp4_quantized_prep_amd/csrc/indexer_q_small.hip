@@ -52,9 +52,20 @@
 #include "fp8_block.h"
 #include "iq_common.h"
 
+// Convention variant compiled into this translation unit (bit 0: interleaved
+// RoPE pairs, bit 1: OCP floor-rule FP4 scales; 0: the defaults). The variant
+// units define it and the FP8-input launcher's name before including this
+// file; they build only that launcher.
+#ifndef IQP_SMALL_VARIANT
+#define IQP_SMALL_VARIANT 0
+#endif
+
 namespace iqp {
 namespace {
 namespace small {
+
+constexpr bool VAR_IL = (IQP_SMALL_VARIANT & 1) != 0;
+constexpr bool VAR_FLOOR = (IQP_SMALL_VARIANT & 2) != 0;
 
 constexpr int NWAVES = 4;
 constexpr int NTHREADS = NWAVES * 64;
@@ -272,11 +283,13 @@ void indexer_q_small_kernel(IndexerQArgs pa) {
     if constexpr (j == 0) {
       int64_t pos = posv;
       pos = pos < 0 ? 0 : (pos >= p.max_pos ? p.max_pos - 1 : pos);
-      const float* row = p.cos_sin + pos * 64 + 8 * (sub & 3);
+      // half-split: rc[h][s] is pair 8 (sub & 3) + 4 h + s; interleaved: pair
+      // 4 (sub & 3) + 16 h + s (dims (2i, 2i + 1) = v[h][2s], v[h][2s + 1])
+      const float* row = p.cos_sin + pos * 64 + (VAR_IL ? 4 : 8) * (sub & 3);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        rc[h] = *reinterpret_cast<const v4f*>(row + 4 * h);
-        rs[h] = *reinterpret_cast<const v4f*>(row + 32 + 4 * h);
+        rc[h] = *reinterpret_cast<const v4f*>(row + (VAR_IL ? 16 : 4) * h);
+        rs[h] = *reinterpret_cast<const v4f*>(row + 32 + (VAR_IL ? 16 : 4) * h);
       }
     }
     const int ws = (int)(wsw[j >> 2] >> (8 * (j & 3)));
@@ -311,7 +324,7 @@ void indexer_q_small_kernel(IndexerQArgs pa) {
       }
   }
   // RoPE on dims 0..63 (b6 = 0): the pair (i, i + 32) is (v[0][k], v[1][k])
-  if (!(sub & 4)) {
+  if (!(sub & 4) && !VAR_IL) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const float x = v[0][k], y = v[1][k];
@@ -319,6 +332,16 @@ void indexer_q_small_kernel(IndexerQArgs pa) {
       v[0][k] = x * c - y * sn;
       v[1][k] = y * c + x * sn;
     }
+  } else if (!(sub & 4)) {   // interleaved: the pair (v[b5][2m], v[b5][2m + 1])
+#pragma unroll
+    for (int b5 = 0; b5 < 2; ++b5)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const float x = v[b5][2 * m], y = v[b5][2 * m + 1];
+        const float c = rc[b5][m], sn = rs[b5][m];
+        v[b5][2 * m] = x * c - y * sn;
+        v[b5][2 * m + 1] = y * c + x * sn;
+      }
   }
   // Hadamard: dim bits 0, 1, 2 (k) and 5 (b5) in the lane ...
 #pragma unroll
@@ -372,7 +395,7 @@ void indexer_q_small_kernel(IndexerQArgs pa) {
     m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x128, 0xF, 0xF, false)));
     const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
     m = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
-    const int e = fp4_exponent(m);
+    const int e = VAR_FLOOR ? fp4_exponent_floor(m) : fp4_exponent(m);
     sb |= (uint32_t)(e + 127) << (8 * b5);
     const float scale = __uint_as_float((uint32_t)(e + 127) << 23);   // codes are RNE(z / 2^e)
     const float* x = v[b5];
@@ -398,6 +421,7 @@ void indexer_q_small_kernel(IndexerQArgs pa) {
 }  // namespace small
 }  // namespace
 
+#if IQP_SMALL_VARIANT == 0
 // activation and weight row offsets are formed in 32 bits; the weight scales
 // are read four at a time
 bool indexer_q_small_supported(const IndexerQArgs& a) {
@@ -423,5 +447,12 @@ hipError_t launch_indexer_q_small_bf16(const IndexerQArgs& a, hipStream_t stream
   hipLaunchKernelGGL(small::indexer_q_small_kernel<true>, grid, block, 0, stream, a);
   return hipGetLastError();
 }
+#else
+hipError_t IQP_SMALL_LAUNCH(const IndexerQArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)a.H, (unsigned)((a.M + small::TILE - 1) / small::TILE)), block(small::NTHREADS);
+  hipLaunchKernelGGL(small::indexer_q_small_kernel<false>, grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+#endif
 
 }  // namespace iqp

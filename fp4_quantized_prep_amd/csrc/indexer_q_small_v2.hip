@@ -1,0 +1,5 @@
+// The small-batch fused indexer-Q kernel of indexer_q_small.hip (FP8 input)
+// compiled with a convention variant: OCP floor-rule FP4 scales.
+#define IQP_SMALL_VARIANT 2
+#define IQP_SMALL_LAUNCH launch_indexer_q_small_v2
+#include "indexer_q_small.hip"

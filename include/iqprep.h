@@ -181,9 +181,9 @@ int indexer_q_gemm_rope_fp4(const void* a, int64_t lda,
  *                             byte per weight row n and K block j), and the
  *                             projection uses ew(n, j) in place of ew(h, j).
  * Other bits: IQP_ERR_INVALID. With only the RoPE / FP4 flags the call runs
- * the pipelined kernel's variant build wherever the base call would run the
- * pipelined kernel (K = 1536 above 256 tokens); otherwise it runs the general
- * tiled kernel (slower than the K = 1536 production kernels).
+ * the variant build of whichever K = 1536 kernel the base call would run
+ * (small-batch up to 256 tokens, pipelined above); otherwise it runs the
+ * general tiled kernel (slower than the K = 1536 production kernels).
  */
 int indexer_q_gemm_rope_fp4_ex(const void* a, int64_t lda,
                                const int32_t* a_scales, int64_t as_stride_m, int64_t as_stride_w,

@@ -278,12 +278,12 @@ def device_chain_variant(iqp, x, wd, wsd, pos, cs, n_heads, layout, rule):
 
 
 @pytest.mark.parametrize("layout,rule", FUSED_VARIANTS)
-@pytest.mark.parametrize("M", [1, 5, 128, 300, 1157])
+@pytest.mark.parametrize("M", [1, 5, 33, 128, 256, 300, 1157])
 def test_fused_chain_variants(gpu_lib, weights, table, layout, rule, M):
     """The flags call (indexer_q_gemm_rope_fp4_ex) against the oracle's chain
     with the same conventions; every token checked. Up to 256 tokens the
-    general kernel runs the variant, above it the pipelined kernel's variant
-    build (1157: uneven tile chunks)."""
+    small-batch kernel's variant build runs, above it the pipelined kernel's
+    (1157: uneven tile chunks)."""
     codes, sb, wd, wsd = weights
     inp = S.indexer_q_inputs("indexer_q_m128", M=M)
     x, pos = inp["x"], inp["positions"]
