@@ -54,6 +54,7 @@
 #ifndef IQP_PIPE_VARIANT
 #define IQP_PIPE_VARIANT 0
 #define IQP_PIPE_LAUNCH launch_indexer_q_pipe
+#define IQP_PIPE_KERNEL indexer_q_pipe_kernel
 #endif
 
 namespace iqp {
@@ -574,7 +575,7 @@ __device__ __forceinline__ void hand_over(Ctx& c, Epi& es, int64_t tbase) {
 
 // Workgroup = head pair x token chunk, as in indexer_q.hip.
 __global__ __launch_bounds__(pipe::NTHREADS, 1)
-void indexer_q_pipe_kernel(IndexerQArgs p) {
+void IQP_PIPE_KERNEL(IndexerQArgs p) {
   using namespace pipe;
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
 
@@ -654,7 +655,7 @@ bool indexer_q_pipe_supported(const IndexerQArgs& a) {
 
 hipError_t IQP_PIPE_LAUNCH(const IndexerQArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)((a.H + 1) / 2) * a.chunks)), block(pipe::NTHREADS);
-  hipLaunchKernelGGL(indexer_q_pipe_kernel, grid, block, 0, stream, a);
+  hipLaunchKernelGGL(IQP_PIPE_KERNEL, grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

@@ -2,4 +2,5 @@
 // convention variant: interleaved RoPE pairs and OCP floor-rule FP4 scales.
 #define IQP_PIPE_VARIANT 3
 #define IQP_PIPE_LAUNCH launch_indexer_q_pipe_v3
+#define IQP_PIPE_KERNEL indexer_q_pipe_kernel_v3
 #include "indexer_q_pipe.hip"

@@ -58,6 +58,7 @@
 // file; they build only that launcher.
 #ifndef IQP_SMALL_VARIANT
 #define IQP_SMALL_VARIANT 0
+#define IQP_SMALL_KERNEL indexer_q_small_kernel
 #endif
 
 namespace iqp {
@@ -104,7 +105,7 @@ constexpr int XSTEPS = TILE * NKB / 32;      // one-launch variant: 32 blocks pe
 
 template <bool XIN>
 __global__ __launch_bounds__(NTHREADS, 1)
-void indexer_q_small_kernel(IndexerQArgs pa) {
+void IQP_SMALL_KERNEL(IndexerQArgs pa) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
   const int head = blockIdx.x;
   const int tid = threadIdx.x;
@@ -431,7 +432,7 @@ bool indexer_q_small_supported(const IndexerQArgs& a) {
 
 hipError_t launch_indexer_q_small(const IndexerQArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)a.H, (unsigned)((a.M + small::TILE - 1) / small::TILE)), block(small::NTHREADS);
-  hipLaunchKernelGGL(small::indexer_q_small_kernel<false>, grid, block, 0, stream, a);
+  hipLaunchKernelGGL(small::IQP_SMALL_KERNEL<false>, grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
@@ -444,13 +445,13 @@ bool indexer_q_small_bf16_supported(const IndexerQArgs& a) {
 
 hipError_t launch_indexer_q_small_bf16(const IndexerQArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)a.H, (unsigned)((a.M + small::TILE - 1) / small::TILE)), block(small::NTHREADS);
-  hipLaunchKernelGGL(small::indexer_q_small_kernel<true>, grid, block, 0, stream, a);
+  hipLaunchKernelGGL(small::IQP_SMALL_KERNEL<true>, grid, block, 0, stream, a);
   return hipGetLastError();
 }
 #else
 hipError_t IQP_SMALL_LAUNCH(const IndexerQArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)a.H, (unsigned)((a.M + small::TILE - 1) / small::TILE)), block(small::NTHREADS);
-  hipLaunchKernelGGL(small::indexer_q_small_kernel<false>, grid, block, 0, stream, a);
+  hipLaunchKernelGGL(small::IQP_SMALL_KERNEL<false>, grid, block, 0, stream, a);
   return hipGetLastError();
 }
 #endif

@@ -2,4 +2,5 @@
 // compiled with a convention variant: interleaved RoPE pairs (2i, 2i + 1).
 #define IQP_SMALL_VARIANT 1
 #define IQP_SMALL_LAUNCH launch_indexer_q_small_v1
+#define IQP_SMALL_KERNEL indexer_q_small_kernel_v1
 #include "indexer_q_small.hip"

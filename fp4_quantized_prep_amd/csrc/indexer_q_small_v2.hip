@@ -2,4 +2,5 @@
 // compiled with a convention variant: OCP floor-rule FP4 scales.
 #define IQP_SMALL_VARIANT 2
 #define IQP_SMALL_LAUNCH launch_indexer_q_small_v2
+#define IQP_SMALL_KERNEL indexer_q_small_kernel_v2
 #include "indexer_q_small.hip"

@@ -2,4 +2,5 @@
 // compiled with a convention variant: interleaved RoPE pairs and OCP floor-rule FP4 scales.
 #define IQP_SMALL_VARIANT 3
 #define IQP_SMALL_LAUNCH launch_indexer_q_small_v3
+#define IQP_SMALL_KERNEL indexer_q_small_kernel_v3
 #include "indexer_q_small.hip"
