@@ -139,3 +139,33 @@ def test_fp8_check():
     assert not r["ok"] and r["q_mismatch"] == 1
     with pytest.raises(ValueError):
         C.check_fp8_quant(q[:1], s, q, s)
+
+
+def test_one_boundary_flip_allowed_in_a_small_sample_two_are_not():
+    """256 blocks (one token, 64 heads): 0.1 % of them is below one, so one
+    legal scale flip passes and two do not."""
+    z, p, s = make_case(5, rows=32)          # 32 x 2 x 4 = 256 blocks
+    z = z.copy()
+    flips = []
+    for m, h, b in ((3, 0, 1), (9, 1, 2)):
+        blk = z[m, h, 32 * b:32 * b + 32]
+        i = int(np.argmax(np.abs(blk)))
+        z[m, h, 32 * b + i] = np.sign(blk[i]) * 6.0                 # amax / 6 exactly 2^0
+        z[m, h, 32 * b:32 * b + 32] = np.clip(z[m, h, 32 * b:32 * b + 32], -6.0, 6.0)
+        flips.append((m, h, b))
+    p, s = IQ.fp4_quantize(z)
+
+    def flipped(n):
+        s_dev = s.copy()
+        codes = F.e2m1_unpack(p)
+        for m, h, b in flips[:n]:
+            s_dev[m, h, b] += 1
+            codes[m, h, 32 * b:32 * b + 32] = F.e2m1_encode_rne(z[m, h, 32 * b:32 * b + 32] * 0.5)
+        return F.e2m1_pack(codes), s_dev
+
+    p1, s1 = flipped(1)
+    r1 = C.check_fp4(p1, s1, z, p, s)
+    assert r1["blocks"] == 256 and r1["scale_mismatch"] == 1 and r1["scale_illegal"] == 0 and r1["ok"]
+    p2, s2 = flipped(2)
+    r2 = C.check_fp4(p2, s2, z, p, s)
+    assert r2["scale_mismatch"] == 2 and r2["scale_illegal"] == 0 and not r2["ok"]
