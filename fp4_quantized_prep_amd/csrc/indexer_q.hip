@@ -531,10 +531,17 @@ static bool pipe_args(const IndexerQArgs& a_in, IndexerQArgs& a) {
 hipError_t launch_indexer_q_variant(const IndexerQArgs& a_in, int variant, hipStream_t stream) {
   if (variant == 0) return launch_indexer_q(a_in, -1, stream);
   if (variant < 0 || variant > 7) return hipErrorInvalidValue;
-  if (variant <= 3 && indexer_q_small_supported(a_in))
-    return variant == 1 ? launch_indexer_q_small_v1(a_in, stream)
-         : variant == 2 ? launch_indexer_q_small_v2(a_in, stream)
-                        : launch_indexer_q_small_v3(a_in, stream);
+  if (indexer_q_small_supported(a_in)) {
+    switch (variant) {
+      case 1: return launch_indexer_q_small_v1(a_in, stream);
+      case 2: return launch_indexer_q_small_v2(a_in, stream);
+      case 3: return launch_indexer_q_small_v3(a_in, stream);
+      case 4: return launch_indexer_q_small_v4(a_in, stream);
+      case 5: return launch_indexer_q_small_v5(a_in, stream);
+      case 6: return launch_indexer_q_small_v6(a_in, stream);
+      default: return launch_indexer_q_small_v7(a_in, stream);
+    }
+  }
   if (variant <= 3 && indexer_q_pipe_supported(a_in)) {
     IndexerQArgs a;
     if (!pipe_args(a_in, a)) return hipErrorInvalidValue;

@@ -53,9 +53,10 @@
 #include "iq_common.h"
 
 // Convention variant compiled into this translation unit (bit 0: interleaved
-// RoPE pairs, bit 1: OCP floor-rule FP4 scales; 0: the defaults). The variant
-// units define it and the FP8-input launcher's name before including this
-// file; they build only that launcher.
+// RoPE pairs, bit 1: OCP floor-rule FP4 scales, bit 2: one weight scale per
+// row and K block; 0: the defaults). The variant units define it and the
+// FP8-input launcher's name before including this file; they build only that
+// launcher.
 #ifndef IQP_SMALL_VARIANT
 #define IQP_SMALL_VARIANT 0
 #define IQP_SMALL_KERNEL indexer_q_small_kernel
@@ -67,6 +68,7 @@ namespace small {
 
 constexpr bool VAR_IL = (IQP_SMALL_VARIANT & 1) != 0;
 constexpr bool VAR_FLOOR = (IQP_SMALL_VARIANT & 2) != 0;
+constexpr bool VAR_ROWS = (IQP_SMALL_VARIANT & 4) != 0;
 
 constexpr int NWAVES = 4;
 constexpr int NTHREADS = NWAVES * 64;
@@ -173,11 +175,14 @@ void IQP_SMALL_KERNEL(IndexerQArgs pa) {
 #pragma unroll
     for (int k = 0; k < 3; ++k) asw[k] = w[k * p.as_sw];
   }
-  // the head's weight scales, one byte per K block
-  const uint32_t* wsp = reinterpret_cast<const uint32_t*>(p.w_scales + (int64_t)head * NKB);
+  // the head's weight scales, one byte per K block (per-row variant: the
+  // 12 bytes of this lane's MFMA row 32 wave + lane % 32, 4-byte aligned
+  // since the array is and 12 divides by 4)
+  const uint32_t* wsp = reinterpret_cast<const uint32_t*>(
+      p.w_scales + (VAR_ROWS ? ((int64_t)head * HEAD_DIM + 32 * wave + (lane & 31)) * NKB : (int64_t)head * NKB));
   uint32_t wsw[3];
 #pragma unroll
-  for (int k = 0; k < 3; ++k) wsw[k] = __builtin_amdgcn_readfirstlane(wsp[k]);
+  for (int k = 0; k < 3; ++k) wsw[k] = VAR_ROWS ? wsp[k] : __builtin_amdgcn_readfirstlane(wsp[k]);
   // Epilogue lanes: token 8 wave + l % 8 and the dims
   // 64 b6 + 32 b5 + 8 (b3 + 2 b4) + k, (b3, b4, b6) = lane bits 3, 4, 5.
   // The token's position now; its RoPE table row (the pairs

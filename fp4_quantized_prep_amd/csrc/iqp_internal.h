@@ -37,9 +37,10 @@ hipError_t launch_fp8_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx
 hipError_t launch_indexer_q(const IndexerQArgs& args, int stage, hipStream_t stream);
 // FP4 output with convention variant v (bit 0: interleaved RoPE pairs, bit 1:
 // OCP floor-rule FP4 scales, bit 2: per-row weight scales); v = 0 is
-// launch_indexer_q(args, -1, stream); v = 1..3 runs the small-batch or
-// pipelined kernel's variant build where the default call would run that
-// kernel, the general kernel otherwise; v >= 4 runs the general kernel
+// launch_indexer_q(args, -1, stream); otherwise the small-batch kernel's
+// variant build where the default call would run that kernel, the pipelined
+// kernel's for v = 1..3 where the default call would run it, and the general
+// kernel everywhere else
 hipError_t launch_indexer_q_variant(const IndexerQArgs& args, int variant, hipStream_t stream);
 
 // the pipelined FP4-output kernel (indexer_q_pipe.hip) for the shapes it takes
@@ -56,11 +57,15 @@ hipError_t launch_indexer_q_pipe_v3(const IndexerQArgs& args, hipStream_t stream
 // tokens, weight scales 4-byte aligned
 bool indexer_q_small_supported(const IndexerQArgs& args);
 hipError_t launch_indexer_q_small(const IndexerQArgs& args, hipStream_t stream);
-// the same kernel with convention variant 1 (interleaved RoPE), 2 (OCP floor
-// FP4 scales) or 3 (both) compiled in (indexer_q_small_v1/2/3.hip)
+// the same kernel with convention variant v = 1..7 compiled in
+// (indexer_q_small_v<v>.hip; bits as in launch_indexer_q_variant)
 hipError_t launch_indexer_q_small_v1(const IndexerQArgs& args, hipStream_t stream);
 hipError_t launch_indexer_q_small_v2(const IndexerQArgs& args, hipStream_t stream);
 hipError_t launch_indexer_q_small_v3(const IndexerQArgs& args, hipStream_t stream);
+hipError_t launch_indexer_q_small_v4(const IndexerQArgs& args, hipStream_t stream);
+hipError_t launch_indexer_q_small_v5(const IndexerQArgs& args, hipStream_t stream);
+hipError_t launch_indexer_q_small_v6(const IndexerQArgs& args, hipStream_t stream);
+hipError_t launch_indexer_q_small_v7(const IndexerQArgs& args, hipStream_t stream);
 // the same kernel quantizing bf16 activations (args.x, args.ldx) itself: one
 // launch from X to FP4 Q; K = 1536, 1 to 256 tokens
 bool indexer_q_small_bf16_supported(const IndexerQArgs& args);

@@ -391,8 +391,11 @@ def row_scale_weights(H, K, seed):
     return codes, torch.from_numpy(rows.astype(np.uint8))
 
 
-@pytest.mark.parametrize("M,H,K", [(5, 64, 1536), (128, 64, 1536), (300, 64, 1536), (70, 3, 1024)])
+@pytest.mark.parametrize("M,H,K", [(1, 64, 1536), (5, 64, 1536), (128, 64, 1536), (256, 64, 1536),
+                                   (300, 64, 1536), (70, 3, 1024)])
 def test_fused_chain_row_weight_scales(gpu_lib, table, M, H, K):
+    """Up to 256 tokens at K = 1536 the small-batch kernel's per-row build runs,
+    otherwise the general kernel."""
     codes, wsr = row_scale_weights(H, K, 103)
     if K == 1536:
         inp = S.indexer_q_inputs("indexer_q_m128", M=M)
@@ -412,11 +415,13 @@ def test_fused_chain_row_weight_scales(gpu_lib, table, M, H, K):
     assert rep["ok"], rep
 
 
-def test_row_weight_scales_equal_to_tile_scales_give_the_same_bytes(gpu_lib, table):
+@pytest.mark.parametrize("K", [1024, 1536])
+def test_row_weight_scales_equal_to_tile_scales_give_the_same_bytes(gpu_lib, table, K):
     """Per-row bytes that repeat each tile's byte over its 128 rows: the same
-    output bytes as the per-tile call (both on the general kernel, K = 1024),
-    for the default and the interleaved / floor-rule conventions."""
-    H, M, K = 4, 90, 1024
+    output bytes as the per-tile call (the general kernel at K = 1024, the
+    small-batch kernel's builds at K = 1536), for the default and the
+    interleaved / floor-rule conventions."""
+    H, M = 4, 90
     codes, sb = S.weights(N=H * 128, K=K, seed=104)
     rows = torch.from_numpy(np.repeat(sb.numpy(), 128, axis=0).copy())
     g = S.rng("indexer_q_m128", 961)
