@@ -542,12 +542,19 @@ hipError_t launch_indexer_q_variant(const IndexerQArgs& a_in, int variant, hipSt
       default: return launch_indexer_q_small_v7(a_in, stream);
     }
   }
-  if (variant <= 3 && indexer_q_pipe_supported(a_in)) {
+  if (indexer_q_pipe_supported(a_in) &&
+      (variant <= 3 || (reinterpret_cast<uintptr_t>(a_in.w_scales) & 3) == 0)) {
     IndexerQArgs a;
     if (!pipe_args(a_in, a)) return hipErrorInvalidValue;
-    return variant == 1 ? launch_indexer_q_pipe_v1(a, stream)
-         : variant == 2 ? launch_indexer_q_pipe_v2(a, stream)
-                        : launch_indexer_q_pipe_v3(a, stream);
+    switch (variant) {
+      case 1: return launch_indexer_q_pipe_v1(a, stream);
+      case 2: return launch_indexer_q_pipe_v2(a, stream);
+      case 3: return launch_indexer_q_pipe_v3(a, stream);
+      case 4: return launch_indexer_q_pipe_v4(a, stream);
+      case 5: return launch_indexer_q_pipe_v5(a, stream);
+      case 6: return launch_indexer_q_pipe_v6(a, stream);
+      default: return launch_indexer_q_pipe_v7(a, stream);
+    }
   }
   return launch_kernel(a_in, stage_of_variant(variant), stream);
 }

@@ -49,8 +49,9 @@
 #include "iq_common.h"
 
 // Convention variant compiled into this translation unit (bit 0: interleaved
-// RoPE pairs, bit 1: OCP floor-rule FP4 scales; 0: the defaults). The variant
-// units define it and the launcher's name before including this file.
+// RoPE pairs, bit 1: OCP floor-rule FP4 scales, bit 2: one weight scale per
+// row and K block; 0: the defaults). The variant units define it and the
+// launcher's name before including this file.
 #ifndef IQP_PIPE_VARIANT
 #define IQP_PIPE_VARIANT 0
 #define IQP_PIPE_LAUNCH launch_indexer_q_pipe
@@ -63,6 +64,7 @@ namespace pipe {
 
 constexpr bool VAR_IL = (IQP_PIPE_VARIANT & 1) != 0;
 constexpr bool VAR_FLOOR = (IQP_PIPE_VARIANT & 2) != 0;
+constexpr bool VAR_ROWS = (IQP_PIPE_VARIANT & 4) != 0;
 
 constexpr int NWAVES = 4;
 constexpr int NTHREADS = NWAVES * 64;
@@ -134,6 +136,7 @@ struct Ctx {
   uint8_t* lds;
   int lane, half, wave, hn, th, head;
   uint32_t wsc_lane;             // the head's weight-scale bytes, 4 per lane
+  uint32_t wsr[4][3];            // per-row variant: the 12 bytes of W row 32 tn + lane % 32 of the head
   rsrc_t rw, ra, rs, ra_n, rs_n; // weights; activations / scale words of this and the next tile
   // Copy addressing. A copy's row part is a lane offset (bounds-checked:
   // rows past the tokens read zeros) or, for the weights, a scalar offset per
@@ -161,6 +164,16 @@ struct Ctx {
 #pragma unroll
     for (int b = 0; b < 4; ++b)
       if (4 * lane + b < NKB) wsc_lane |= (uint32_t)wsc[4 * lane + b] << (8 * b);
+    if constexpr (VAR_ROWS) {
+      // [H*128, 12] bytes, 4-byte aligned (the launcher checks): three words a row
+#pragma unroll
+      for (int tn = 0; tn < 4; ++tn) {
+        const uint32_t* row = reinterpret_cast<const uint32_t*>(
+            p.w_scales + ((int64_t)head_c * HEAD_DIM + 32 * tn + (lane & 31)) * NKB);
+#pragma unroll
+        for (int k = 0; k < 3; ++k) wsr[tn][k] = row[k];
+      }
+    }
     // copy i of this wave lands in rows 8 (wave + 4 i) + lane / 8, slot lane % 8,
     // which holds the row's chunk (lane % 8) ^ ((row / 2) % 8): the slab index
     // wave + 4 i has the parity of wave, so that is the same for every copy
@@ -450,7 +463,7 @@ __device__ __forceinline__ void epilogue_alone(Epi& es, v16f (&accp)[MAX_TM][4],
 template <int NTM, int RST, int RKH, bool RSC, int COPY_LO, int COPY_HI, int DST, bool NEXT, int JD, int EH,
           int NTMP, bool TO_P>
 __device__ __forceinline__ void half_step(Ctx& c, v16f (&acc)[MAX_TM][4], const Frags& F, const int (&as)[MAX_TM],
-                                          int ws, Frags& N, int (&asn)[MAX_TM], Epi& es,
+                                          int ws, const int (&ws4)[4], Frags& N, int (&asn)[MAX_TM], Epi& es,
                                           v16f (&accp)[MAX_TM][4]) {
   constexpr int NM = 4 * NTM;
   constexpr int NS = NM > 0 ? NM : 1;
@@ -462,7 +475,8 @@ __device__ __forceinline__ void half_step(Ctx& c, v16f (&acc)[MAX_TM][4], const 
     if (slot < NM) {
       const int tn = slot / (NTM > 0 ? NTM : 1), tm = slot % (NTM > 0 ? NTM : 1);
       v16f& dst = TO_P ? accp[tm][tn] : acc[tm][tn];
-      dst = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.w[tn], F.a[tm], acc[tm][tn], 0, 0, 0, ws, 0, as[tm]);
+      dst = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.w[tn], F.a[tm], acc[tm][tn], 0, 0, 0,
+                                                            VAR_ROWS ? ws4[tn] : ws, 0, as[tm]);
       asm volatile("" : "+a"(dst));   // the MFMA stays in its slot
       // acc stays live past the MFMA writing accp, so accp cannot take acc's
       // registers (it would have to move back into its own at the tile's end)
@@ -508,6 +522,11 @@ __device__ __forceinline__ void k_block(Ctx& c, v16f (&acc)[MAX_TM][4], Frags& f
                                         v16f (&accp)[MAX_TM][4]) {
   constexpr int ST = J % NST;
   const int ws = (int)((uint32_t)__builtin_amdgcn_readlane((int)c.wsc_lane, J >> 2) >> (8 * (J & 3)));
+  int ws4[4] = {0, 0, 0, 0};   // per-row variant: this lane's rows' bytes of block J
+  if constexpr (VAR_ROWS) {
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn) ws4[tn] = (int)(c.wsr[tn][J >> 2] >> (8 * (J & 3)));
+  }
   int as[MAX_TM];
 #pragma unroll
   for (int tm = 0; tm < MAX_TM; ++tm) as[tm] = (int)((uint32_t)as0[tm] >> (8 * (J & 3)));
@@ -515,14 +534,14 @@ __device__ __forceinline__ void k_block(Ctx& c, v16f (&acc)[MAX_TM][4], Frags& f
   // in a chunk's first tile the prologue copied blocks 0 and 1 whole and block 2's first part
   constexpr int J2 = J + 2;
   half_step<NTM, ST, 1, false, PART1, NCOPY, J2 % NST, (J2 >= NKB), J2 % NKB, 2 * J, NTMP, false>(
-      c, acc, f0, as, ws, f1, as1, es, accp);
+      c, acc, f0, as, ws, ws4, f1, as1, es, accp);
   __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);
   __builtin_amdgcn_s_waitcnt(WAITCNT_VM13);
   block_barrier();   // all of block j read by every wave; block j+1 has landed
   __builtin_amdgcn_sched_barrier(0);
   constexpr int J3 = J + 3;
   half_step<NTM, (J + 1) % NST, 0, true, 0, PART1, ST, (J3 >= NKB), J3 % NKB, 2 * J + 1, NTMP, J == NKB - 1>(
-      c, acc, f1, as, ws, f0, as1, es, accp);
+      c, acc, f1, as, ws, ws4, f0, as1, es, accp);
 #pragma unroll
   for (int tm = 0; tm < MAX_TM; ++tm) as0[tm] = as1[tm];
   (void)FIRST;

@@ -37,21 +37,26 @@ hipError_t launch_fp8_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx
 hipError_t launch_indexer_q(const IndexerQArgs& args, int stage, hipStream_t stream);
 // FP4 output with convention variant v (bit 0: interleaved RoPE pairs, bit 1:
 // OCP floor-rule FP4 scales, bit 2: per-row weight scales); v = 0 is
-// launch_indexer_q(args, -1, stream); otherwise the small-batch kernel's
-// variant build where the default call would run that kernel, the pipelined
-// kernel's for v = 1..3 where the default call would run it, and the general
-// kernel everywhere else
+// launch_indexer_q(args, -1, stream); otherwise the variant build of the
+// small-batch or pipelined kernel where the default call would run that
+// kernel (per-row weight scales in the pipelined one: 4-byte aligned), and
+// the general kernel everywhere else
 hipError_t launch_indexer_q_variant(const IndexerQArgs& args, int variant, hipStream_t stream);
 
 // the pipelined FP4-output kernel (indexer_q_pipe.hip) for the shapes it takes
 // (K = 1536, token counts that fit in 31 bits); args.chunks set
 bool indexer_q_pipe_supported(const IndexerQArgs& args);
 hipError_t launch_indexer_q_pipe(const IndexerQArgs& args, hipStream_t stream);
-// the same kernel with convention variant 1 (interleaved RoPE), 2 (OCP floor
-// FP4 scales) or 3 (both) compiled in (indexer_q_pipe_v1/2/3.hip)
+// the same kernel with convention variant v = 1..7 compiled in
+// (indexer_q_pipe_v<v>.hip; bits as in launch_indexer_q_variant; v >= 4 needs
+// 4-byte aligned weight scales)
 hipError_t launch_indexer_q_pipe_v1(const IndexerQArgs& args, hipStream_t stream);
 hipError_t launch_indexer_q_pipe_v2(const IndexerQArgs& args, hipStream_t stream);
 hipError_t launch_indexer_q_pipe_v3(const IndexerQArgs& args, hipStream_t stream);
+hipError_t launch_indexer_q_pipe_v4(const IndexerQArgs& args, hipStream_t stream);
+hipError_t launch_indexer_q_pipe_v5(const IndexerQArgs& args, hipStream_t stream);
+hipError_t launch_indexer_q_pipe_v6(const IndexerQArgs& args, hipStream_t stream);
+hipError_t launch_indexer_q_pipe_v7(const IndexerQArgs& args, hipStream_t stream);
 
 // the small-batch FP4-output kernel (indexer_q_small.hip): K = 1536, 1 to 256
 // tokens, weight scales 4-byte aligned

@@ -180,11 +180,11 @@ int indexer_q_gemm_rope_fp4(const void* a, int64_t lda,
  *   IQP_W_SCALES_PER_ROW      w_scales is UE8M0 [H*D, K/128] row-major (one
  *                             byte per weight row n and K block j), and the
  *                             projection uses ew(n, j) in place of ew(h, j).
- * Other bits: IQP_ERR_INVALID. Where the base call would run the K = 1536
- * small-batch kernel (up to 256 tokens) any flags run its variant build;
- * where it would run the pipelined kernel the RoPE / FP4 flags run its
- * variant build; otherwise the general tiled kernel runs (slower than the
- * K = 1536 production kernels).
+ * Other bits: IQP_ERR_INVALID. Where the base call would run one of the
+ * K = 1536 production kernels (small-batch up to 256 tokens, pipelined
+ * above) the flags run that kernel's variant build (per-row weight scales
+ * in the pipelined one need w_scales 4-byte aligned); otherwise the general
+ * tiled kernel runs (slower than the K = 1536 production kernels).
  */
 int indexer_q_gemm_rope_fp4_ex(const void* a, int64_t lda,
                                const int32_t* a_scales, int64_t as_stride_m, int64_t as_stride_w,

@@ -392,10 +392,11 @@ def row_scale_weights(H, K, seed):
 
 
 @pytest.mark.parametrize("M,H,K", [(1, 64, 1536), (5, 64, 1536), (128, 64, 1536), (256, 64, 1536),
-                                   (300, 64, 1536), (70, 3, 1024)])
+                                   (300, 64, 1536), (1157, 64, 1536), (300, 3, 1536), (70, 3, 1024)])
 def test_fused_chain_row_weight_scales(gpu_lib, table, M, H, K):
-    """Up to 256 tokens at K = 1536 the small-batch kernel's per-row build runs,
-    otherwise the general kernel."""
+    """At K = 1536 the small-batch kernel's per-row build runs up to 256
+    tokens and the pipelined kernel's above (1157: uneven tile chunks; 3
+    heads: a pair without its second head); the general kernel at K = 1024."""
     codes, wsr = row_scale_weights(H, K, 103)
     if K == 1536:
         inp = S.indexer_q_inputs("indexer_q_m128", M=M)
@@ -415,13 +416,14 @@ def test_fused_chain_row_weight_scales(gpu_lib, table, M, H, K):
     assert rep["ok"], rep
 
 
-@pytest.mark.parametrize("K", [1024, 1536])
-def test_row_weight_scales_equal_to_tile_scales_give_the_same_bytes(gpu_lib, table, K):
+@pytest.mark.parametrize("K,M", [(1024, 90), (1536, 90), (1536, 600)])
+def test_row_weight_scales_equal_to_tile_scales_give_the_same_bytes(gpu_lib, table, K, M):
     """Per-row bytes that repeat each tile's byte over its 128 rows: the same
     output bytes as the per-tile call (the general kernel at K = 1024, the
-    small-batch kernel's builds at K = 1536), for the default and the
-    interleaved / floor-rule conventions."""
-    H, M = 4, 90
+    small-batch kernel's builds at 90 tokens and the pipelined kernel's at 600
+    when K = 1536), for the default and the interleaved / floor-rule
+    conventions."""
+    H = 4
     codes, sb = S.weights(N=H * 128, K=K, seed=104)
     rows = torch.from_numpy(np.repeat(sb.numpy(), 128, axis=0).copy())
     g = S.rng("indexer_q_m128", 961)
@@ -437,8 +439,9 @@ def test_row_weight_scales_equal_to_tile_scales_give_the_same_bytes(gpu_lib, tab
         assert torch.equal(q0.cpu(), q1.cpu()) and torch.equal(s0.cpu(), s1.cpu()), (layout, rule)
 
 
-def test_row_weight_scales_with_variants(gpu_lib, table):
-    H, M, K = 3, 70, 1536
+@pytest.mark.parametrize("M", [70, 300])
+def test_row_weight_scales_with_variants(gpu_lib, table, M):
+    H, K = 3, 1536
     codes, wsr = row_scale_weights(H, K, 105)
     inp = S.indexer_q_inputs("indexer_q_m128", M=M)
     x, pos = inp["x"], inp["positions"]
