@@ -56,6 +56,8 @@ def _load():
     lib.indexer_q_prep_bf16.argtypes = [c_p, c_i64, c_p, c_i64, c_p, c_i64, c_i64, c_i32, c_i32, c_i32,
                                          c_p, c_p, c_i64, c_p, c_p, c_p]
     lib.indexer_q_prep_bf16.restype = ctypes.c_int
+    lib.indexer_q_prep_bf16_ex.argtypes = lib.indexer_q_prep_bf16.argtypes[:-1] + [c_i32, c_p]
+    lib.indexer_q_prep_bf16_ex.restype = ctypes.c_int
     lib.fp8_quant_weight_128x128_ue8m0.argtypes = [c_p, c_i64, c_i64, c_i64, c_p, c_i64, c_p, c_i64, c_p]
     lib.fp8_quant_weight_128x128_ue8m0.restype = ctypes.c_int
     lib.indexer_q_rope_hadamard_fp4.argtypes = [c_p, c_i64, c_i64, c_i32, c_i32, c_i32, c_p, c_p, c_i64,
@@ -327,10 +329,17 @@ def rope_cos_sin_table(theta: float, max_pos: int, rope_dim: int = 64, device=No
 
 
 def indexer_q_prep_bf16(x, w, w_scales, positions, cos_sin, n_heads: int = 64, head_dim: int = 128,
-                        rope_dim: int = 64, q_fp4=None, q_scales=None, stream=None):
+                        rope_dim: int = 64, q_fp4=None, q_scales=None, rope_layout: str = "half_split",
+                        scale_rule: str = "ceil", w_scale_layout: str = "tile_128x128", stream=None):
     """The whole preparation in one launch for up to 256 tokens (K = 1536):
     bf16 x [M, K] -> FP8 quantization (in the kernel, never stored) -> fused
-    projection / RoPE / Hadamard / FP4. Returns ``(q_fp4, q_scales)``."""
+    projection / RoPE / Hadamard / FP4. Returns ``(q_fp4, q_scales)``. The
+    convention arguments are those of :func:`indexer_q_gemm_rope_fp4`
+    (indexer_q_prep_bf16_ex)."""
+    if w_scale_layout not in ("tile_128x128", "row_1x128"):
+        raise ValueError("w_scale_layout must be 'tile_128x128' or 'row_1x128'")
+    rows = w_scale_layout == "row_1x128"
+    flags = _convention_flags(rope_layout, scale_rule) | (IQP_W_SCALES_PER_ROW if rows else 0)
     w = _bytes_u8(w)
     dev = x.device
     _require(x, "x", torch.bfloat16, dev, 2)
@@ -344,8 +353,9 @@ def indexer_q_prep_bf16(x, w, w_scales, positions, cos_sin, n_heads: int = 64, h
     M, K = x.shape
     if w.shape[1] != K or w.shape[0] != n_heads * head_dim:
         raise ValueError(f"w must be [{n_heads * head_dim}, {K}], got {tuple(w.shape)}")
-    if tuple(w_scales.shape) != (n_heads * head_dim // 128, K // 128):
-        raise ValueError(f"w_scales must be [{n_heads * head_dim // 128}, {K // 128}]")
+    ws_rows = n_heads * head_dim if rows else n_heads * head_dim // 128
+    if tuple(w_scales.shape) != (ws_rows, K // 128):
+        raise ValueError(f"w_scales must be [{ws_rows}, {K // 128}]")
     if positions.shape[0] != M:
         raise ValueError("positions needs one entry per token")
     if cos_sin.shape[1] != rope_dim:
@@ -360,10 +370,14 @@ def indexer_q_prep_bf16(x, w, w_scales, positions, cos_sin, n_heads: int = 64, h
         raise ValueError("q_fp4 and q_scales must be contiguous")
     if tuple(q_fp4.shape) != (M, n_heads, head_dim // 2) or tuple(q_scales.shape) != (M, n_heads, head_dim // 32):
         raise ValueError("q_fp4 / q_scales have the wrong shape")
-    st = _lib.indexer_q_prep_bf16(_ptr(x), x.stride(0), _ptr(w), w.stride(0), _ptr(w_scales), M, K, n_heads,
-                                  head_dim, rope_dim, _ptr(positions), _ptr(cos_sin), cos_sin.shape[0],
-                                  _ptr(q_fp4), _ptr(q_scales), _stream(x, stream))
-    _check(st, "indexer_q_prep_bf16")
+    args = [_ptr(x), x.stride(0), _ptr(w), w.stride(0), _ptr(w_scales), M, K, n_heads, head_dim, rope_dim,
+            _ptr(positions), _ptr(cos_sin), cos_sin.shape[0], _ptr(q_fp4), _ptr(q_scales)]
+    if flags == 0:
+        st = _lib.indexer_q_prep_bf16(*args, _stream(x, stream))
+        _check(st, "indexer_q_prep_bf16")
+    else:
+        st = _lib.indexer_q_prep_bf16_ex(*args, flags, _stream(x, stream))
+        _check(st, "indexer_q_prep_bf16_ex")
     return q_fp4, q_scales
 
 

@@ -147,6 +147,15 @@ int indexer_q_prep_bf16(const void* x, int64_t ldx, const void* w, int64_t ldw, 
                         int64_t M, int64_t K, int32_t H, int32_t D, int32_t rope_dim,
                         const int64_t* positions, const float* cos_sin, int64_t max_pos,
                         uint8_t* q_fp4, uint8_t* q_scales, void* stream) {
+  return indexer_q_prep_bf16_ex(x, ldx, w, ldw, w_scales, M, K, H, D, rope_dim, positions, cos_sin, max_pos,
+                                q_fp4, q_scales, 0, stream);
+}
+
+int indexer_q_prep_bf16_ex(const void* x, int64_t ldx, const void* w, int64_t ldw, const uint8_t* w_scales,
+                           int64_t M, int64_t K, int32_t H, int32_t D, int32_t rope_dim,
+                           const int64_t* positions, const float* cos_sin, int64_t max_pos,
+                           uint8_t* q_fp4, uint8_t* q_scales, int32_t flags, void* stream) {
+  if (flags & ~(IQP_ROPE_INTERLEAVED | IQP_FP4_SCALE_OCP_FLOOR | IQP_W_SCALES_PER_ROW)) return IQP_ERR_INVALID;
   if (M < 0 || K < 0 || H < 0 || D < 0 || rope_dim < 0 || max_pos < 0) return IQP_ERR_INVALID;
   if (M == 0) return IQP_OK;
   if (!x || !w || !w_scales || !positions || !cos_sin || !q_fp4 || !q_scales) return IQP_ERR_INVALID;
@@ -175,7 +184,7 @@ int indexer_q_prep_bf16(const void* x, int64_t ldx, const void* w, int64_t ldw, 
   p.q_fp4 = q_fp4;
   p.q_scales = q_scales;
   if (!iqp::indexer_q_small_bf16_supported(p)) return IQP_ERR_UNSUPPORTED;
-  return from_hip(iqp::launch_indexer_q_small_bf16(p, static_cast<hipStream_t>(stream)));
+  return from_hip(iqp::launch_indexer_q_small_bf16_variant(p, flags, static_cast<hipStream_t>(stream)));
 }
 
 int iqp_debug_indexer_q_f32(const void* a, int64_t lda, const int32_t* a_scales, int64_t as_stride_m,

@@ -528,6 +528,28 @@ static bool pipe_args(const IndexerQArgs& a_in, IndexerQArgs& a) {
   return true;
 }
 
+hipError_t launch_indexer_q_small_bf16_v1(const IndexerQArgs& args, hipStream_t stream);
+hipError_t launch_indexer_q_small_bf16_v2(const IndexerQArgs& args, hipStream_t stream);
+hipError_t launch_indexer_q_small_bf16_v3(const IndexerQArgs& args, hipStream_t stream);
+hipError_t launch_indexer_q_small_bf16_v4(const IndexerQArgs& args, hipStream_t stream);
+hipError_t launch_indexer_q_small_bf16_v5(const IndexerQArgs& args, hipStream_t stream);
+hipError_t launch_indexer_q_small_bf16_v6(const IndexerQArgs& args, hipStream_t stream);
+hipError_t launch_indexer_q_small_bf16_v7(const IndexerQArgs& args, hipStream_t stream);
+
+hipError_t launch_indexer_q_small_bf16_variant(const IndexerQArgs& a, int variant, hipStream_t stream) {
+  switch (variant) {
+    case 0: return launch_indexer_q_small_bf16(a, stream);
+    case 1: return launch_indexer_q_small_bf16_v1(a, stream);
+    case 2: return launch_indexer_q_small_bf16_v2(a, stream);
+    case 3: return launch_indexer_q_small_bf16_v3(a, stream);
+    case 4: return launch_indexer_q_small_bf16_v4(a, stream);
+    case 5: return launch_indexer_q_small_bf16_v5(a, stream);
+    case 6: return launch_indexer_q_small_bf16_v6(a, stream);
+    case 7: return launch_indexer_q_small_bf16_v7(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_indexer_q_variant(const IndexerQArgs& a_in, int variant, hipStream_t stream) {
   if (variant == 0) return launch_indexer_q(a_in, -1, stream);
   if (variant < 0 || variant > 7) return hipErrorInvalidValue;

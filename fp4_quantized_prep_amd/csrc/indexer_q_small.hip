@@ -55,8 +55,7 @@
 // Convention variant compiled into this translation unit (bit 0: interleaved
 // RoPE pairs, bit 1: OCP floor-rule FP4 scales, bit 2: one weight scale per
 // row and K block; 0: the defaults). The variant units define it and the
-// FP8-input launcher's name before including this file; they build only that
-// launcher.
+// names of the FP8-input and bf16-input launchers before including this file.
 #ifndef IQP_SMALL_VARIANT
 #define IQP_SMALL_VARIANT 0
 #define IQP_SMALL_KERNEL indexer_q_small_kernel
@@ -457,6 +456,12 @@ hipError_t launch_indexer_q_small_bf16(const IndexerQArgs& a, hipStream_t stream
 hipError_t IQP_SMALL_LAUNCH(const IndexerQArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)a.H, (unsigned)((a.M + small::TILE - 1) / small::TILE)), block(small::NTHREADS);
   hipLaunchKernelGGL(small::IQP_SMALL_KERNEL<false>, grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t IQP_SMALL_LAUNCH_BF16(const IndexerQArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)a.H, (unsigned)((a.M + small::TILE - 1) / small::TILE)), block(small::NTHREADS);
+  hipLaunchKernelGGL(small::IQP_SMALL_KERNEL<true>, grid, block, 0, stream, a);
   return hipGetLastError();
 }
 #endif

@@ -1,6 +1,7 @@
-// The small-batch fused indexer-Q kernel of indexer_q_small.hip (FP8 input)
-// compiled with a convention variant: OCP floor-rule FP4 scales.
+// The small-batch fused indexer-Q kernel of indexer_q_small.hip (FP8 and
+// bf16 inputs) compiled with a convention variant: OCP floor-rule FP4 scales.
 #define IQP_SMALL_VARIANT 2
 #define IQP_SMALL_LAUNCH launch_indexer_q_small_v2
+#define IQP_SMALL_LAUNCH_BF16 launch_indexer_q_small_bf16_v2
 #define IQP_SMALL_KERNEL indexer_q_small_kernel_v2
 #include "indexer_q_small.hip"

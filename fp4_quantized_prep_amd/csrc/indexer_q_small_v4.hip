@@ -1,6 +1,7 @@
-// The small-batch fused indexer-Q kernel of indexer_q_small.hip (FP8 input)
-// compiled with a convention variant: one weight scale per row and K block.
+// The small-batch fused indexer-Q kernel of indexer_q_small.hip (FP8 and
+// bf16 inputs) compiled with a convention variant: one weight scale per row and K block.
 #define IQP_SMALL_VARIANT 4
 #define IQP_SMALL_LAUNCH launch_indexer_q_small_v4
+#define IQP_SMALL_LAUNCH_BF16 launch_indexer_q_small_bf16_v4
 #define IQP_SMALL_KERNEL indexer_q_small_kernel_v4
 #include "indexer_q_small.hip"

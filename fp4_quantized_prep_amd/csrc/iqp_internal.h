@@ -75,6 +75,9 @@ hipError_t launch_indexer_q_small_v7(const IndexerQArgs& args, hipStream_t strea
 // launch from X to FP4 Q; K = 1536, 1 to 256 tokens
 bool indexer_q_small_bf16_supported(const IndexerQArgs& args);
 hipError_t launch_indexer_q_small_bf16(const IndexerQArgs& args, hipStream_t stream);
+// the same with convention variant v = 1..7 (launch_indexer_q_small_bf16_v<v>);
+// v = 0 is launch_indexer_q_small_bf16
+hipError_t launch_indexer_q_small_bf16_variant(const IndexerQArgs& args, int variant, hipStream_t stream);
 
 // standalone epilogue: bf16 Q [M, H*128] (row stride ldq elements) -> RoPE,
 // Hadamard-128, FP4 codes [M, H, 64] and scale bytes [M, H, 4]

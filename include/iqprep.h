@@ -16,7 +16,7 @@
  *   3. indexer_q_rope_hadamard_fp4   the same RoPE / Hadamard / FP4 epilogue as
  *      a standalone launch over a bf16 Q (the unfused chain's second half).
  *   4. indexer_q_prep_bf16   calls 1 and 2 as one launch for decode-sized
- *      batches (up to 256 tokens).
+ *      batches (up to 256 tokens); indexer_q_prep_bf16_ex takes the flags.
  *   5. fp8_quant_weight_128x128_ue8m0   the weights' E4M3 codes and per-tile
  *      scales that calls 2 and 4 take (weight preparation, off the
  *      per-token path).
@@ -223,6 +223,21 @@ int indexer_q_prep_bf16(const void* x, int64_t ldx, const void* w, int64_t ldw,
                         int64_t M, int64_t K, int32_t H, int32_t D, int32_t rope_dim,
                         const int64_t* positions, const float* cos_sin, int64_t max_pos,
                         uint8_t* q_fp4, uint8_t* q_scales, void* stream);
+
+/*
+ * indexer_q_prep_bf16_ex — indexer_q_prep_bf16 with the convention flags of
+ * indexer_q_gemm_rope_fp4_ex (same pages, same meaning: IQP_ROPE_INTERLEAVED,
+ * IQP_FP4_SCALE_OCP_FLOOR, IQP_W_SCALES_PER_ROW with w_scales [H*D, K/128]
+ * row-major, 4-byte aligned). flags 0 is exactly indexer_q_prep_bf16; the
+ * output equals fp8_quant_1x128_ue8m0 followed by indexer_q_gemm_rope_fp4_ex
+ * with the same flags. Other bits: IQP_ERR_INVALID; the other arguments,
+ * limits and errors are those of indexer_q_prep_bf16.
+ */
+int indexer_q_prep_bf16_ex(const void* x, int64_t ldx, const void* w, int64_t ldw,
+                           const uint8_t* w_scales,
+                           int64_t M, int64_t K, int32_t H, int32_t D, int32_t rope_dim,
+                           const int64_t* positions, const float* cos_sin, int64_t max_pos,
+                           uint8_t* q_fp4, uint8_t* q_scales, int32_t flags, void* stream);
 
 /*
  * indexer_q_rope_hadamard_fp4 — the epilogue of indexer_q_gemm_rope_fp4 as a

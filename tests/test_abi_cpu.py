@@ -108,6 +108,19 @@ def test_fused_ex_argument_checks(iqp):
     assert fused_ex(iqp, 3, M=0) == iqp.IQP_OK
 
 
+def test_one_launch_ex_argument_checks(iqp):
+    lib = iqp._lib
+    args = [P(16), 1536, P(16), 1536, P(16), 4, 1536, 2, 128, 64, P(16), P(16), 10, P(16), P(16)]
+    assert lib.indexer_q_prep_bf16_ex(*args, 8, None) == iqp.IQP_ERR_INVALID      # unknown convention bit
+    assert lib.indexer_q_prep_bf16_ex(*args, -1, None) == iqp.IQP_ERR_INVALID
+    zero = list(args)
+    zero[5] = 0
+    assert lib.indexer_q_prep_bf16_ex(*zero, 7, None) == iqp.IQP_OK               # M = 0: no-op
+    wide = list(args)
+    wide[6], wide[1], wide[3] = 1024, 1024, 1024
+    assert lib.indexer_q_prep_bf16_ex(*wide, 1, None) == iqp.IQP_ERR_UNSUPPORTED  # K must be 1536
+
+
 def test_debug_and_table_argument_checks(iqp):
     lib = iqp._lib
     args = [P(16), 256, P(16), 1, 1, P(16), 256, P(16), 4, 256, 2, 128, 64, P(16), P(16), 10]

@@ -147,3 +147,35 @@ def test_one_launch_declines_large_batches_and_other_k(gpu_lib, weights, table):
     with pytest.raises(gpu_lib.IqpError) as e:
         gpu_lib.indexer_q_prep_bf16(x2, codes2.cuda(), sb2.cuda(), pos[:4], table[4096])
     assert e.value.status == gpu_lib.IQP_ERR_UNSUPPORTED
+
+
+# ---------------------------------------------------------------- convention flags (indexer_q_prep_bf16_ex)
+
+FLAG_CASES = [("interleaved", "ceil", "tile_128x128"), ("half_split", "ocp_floor", "tile_128x128"),
+              ("interleaved", "ocp_floor", "tile_128x128"), ("half_split", "ceil", "row_1x128"),
+              ("interleaved", "ocp_floor", "row_1x128")]
+
+
+@pytest.mark.parametrize("layout,rule,wlayout", FLAG_CASES)
+@pytest.mark.parametrize("M", [1, 16, 33, 256])
+def test_one_launch_flags_match_two_calls_and_oracle(gpu_lib, weights, table, layout, rule, wlayout, M):
+    """With convention flags the one-launch call is byte for byte the two-call
+    path with the same flags, and passes the oracle's rule for them."""
+    codes, sb, wd, wsd = weights
+    if wlayout == "row_1x128":
+        g = np.random.default_rng([103, 8])
+        rows = np.repeat(sb.numpy().astype(np.int64), 128, axis=0) + g.integers(-1, 2, size=(64 * 128, 12))
+        sb = torch.from_numpy(rows.astype(np.uint8))
+        wsd = sb.cuda()
+    inp = S.indexer_q_inputs("indexer_q_m128", M=M)
+    x, pos = inp["x"], inp["positions"]
+    print(f"[prep_bf16 flags] M={M} {layout} {rule} {wlayout}", flush=True)
+    kw = dict(rope_layout=layout, scale_rule=rule, w_scale_layout=wlayout)
+    q1, s1 = gpu_lib.indexer_q_prep_bf16(x.cuda(), wd, wsd, pos.cuda(), table[4096], **kw)
+    a, a_s = gpu_lib.fp8_quant_1x128_ue8m0(x.cuda())
+    q2, s2 = gpu_lib.indexer_q_gemm_rope_fp4(a, a_s, wd, wsd, pos.cuda(), table[4096], **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(q1, q2) and torch.equal(s1, s2), "one launch differs from the two-call path"
+    ref = oracle_chain_from_x(x, codes, sb, pos, 64, layout, rule)
+    rep = C.check_fp4(q1.cpu().numpy(), s1.cpu().numpy(), ref["z"], ref["q_fp4"], ref["q_scales"], scale_rule=rule)
+    assert rep["ok"], rep
