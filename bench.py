@@ -101,6 +101,23 @@ def measured_traffic(kernel):
     return int(fields[f"{kernel}_traffic_bytes_per_launch"])
 
 
+MFMA_PROFILE = os.path.join(ROOT, "profiles", "indexer_q_pipe_mfma_counters_m4632.md")
+
+
+def measured_mfma_util():
+    """The fused kernel's MFMA busy share (SQ_VALU_MFMA_BUSY_CYCLES over the
+    SIMDs' active cycles) from the committed rocprofv3 counter summary, or
+    None if the kernel's sources changed since the counters were taken."""
+    try:
+        fields = dict(line.strip().split(": ", 1) for line in open(MFMA_PROFILE)
+                      if line.strip().startswith("fused_"))
+    except (OSError, ValueError):
+        return None
+    if fields.get("fused_kernel_source_sha256_16") != source_digest("fused"):
+        return None
+    return float(fields["fused_mfma_util_pct"]) / 100.0
+
+
 def one_launch_bytes(M):
     """Algorithmic HBM bytes of one one-launch call: bf16 X, W + its scales,
     positions, the table rows read, and the FP4 codes + scales written."""
@@ -329,6 +346,7 @@ def main():
             "avg_launch_us": t_fused * 1e6,
             "avg_launch_us_event_pair_each": t_fused_ev * 1e6,
             "avg_launch_us_interleaved_rope_ocp_floor_scales": t_variant * 1e6,
+            "mfma_busy_frac_counters": measured_mfma_util(),
         },
         "quant_roofline": {
             "kernel": "fp8_quant_1x128_kernel on [4632,7168] (5 rotating buffer sets, launches back to back "
