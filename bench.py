@@ -213,6 +213,9 @@ def main():
     torch.cuda.synchronize()
     t_quant = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3       # s
     t_fused_ev = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e-3
+    pct = lambda v: {f"p{q}": float(np.percentile(v, q)) * 1e3 for q in (10, 50, 90)}   # ms -> us
+    in_chain_us = {"quant": pct([e[0].elapsed_time(e[1]) for e in ev]),
+                   "fused": pct([e[1].elapsed_time(e[2]) for e in ev])}
     # the fused kernel's own duration: K launches back to back from a captured
     # graph between two events on its stream (the input A stays the chain's)
     t_fused = graph_launch_time(
@@ -386,6 +389,9 @@ def main():
             "avg_launch_us": t_wq * 1e6,
         },
         "cpu_baseline": cpu,
+        "in_chain_kernel_us": in_chain_us,
+        "runtime": {"hip": torch.version.hip, "torch": torch.__version__,
+                    "device": torch.cuda.get_device_name(dev)},
     }
     if vendor is not None:
         result["vendor_gemm_context"] = vendor
