@@ -60,13 +60,13 @@ extern "C" {
 
 #define IQP_ABI_VERSION     1
 
-/* Convention flags of indexer_q_gemm_rope_fp4_ex and indexer_q_rope_hadamard_fp4
- * (0: the defaults of indexer_q_gemm_rope_fp4). The pages leave these
- * conventions open. */
+/* Convention flags of indexer_q_gemm_rope_fp4_ex, indexer_q_prep_bf16_ex and
+ * indexer_q_rope_hadamard_fp4 (0: the defaults of indexer_q_gemm_rope_fp4).
+ * The pages leave these conventions open. */
 #define IQP_ROPE_INTERLEAVED     0x1  /* RoPE pairs (2i, 2i+1), i < rope_dim/2, instead of (i, i + rope_dim/2) */
 #define IQP_FP4_SCALE_OCP_FLOOR  0x2  /* FP4 scale e = floor(log2 max(amax, 1e-4)) - 2 (OCP MX rule), codes
                                          saturating at +-6, instead of e = ceil(log2(amax / 6)) */
-#define IQP_W_SCALES_PER_ROW     0x4  /* indexer_q_gemm_rope_fp4_ex only: w_scales holds one UE8M0 byte per
+#define IQP_W_SCALES_PER_ROW     0x4  /* the projection calls only (not the standalone epilogue): w_scales holds one UE8M0 byte per
                                          weight row and K block, [H*D, K/128] row-major, instead of one per
                                          128x128 tile */
 
