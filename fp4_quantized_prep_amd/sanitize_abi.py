@@ -58,7 +58,7 @@ def main() -> int:
         subprocess.run([B.hipcc()] + B.compile_flags() + SAN + ["-c", os.path.join(PKG_DIR, "csrc", "abi.hip"),
                        "-o", abi_o], check=True, capture_output=True)
         # the host object must carry the instrumentation (ASan report hooks)
-        nm = subprocess.run(["/opt/rocm/lib/llvm/bin/llvm-nm", "-u", abi_o], check=True, capture_output=True,
+        nm = subprocess.run(["nm", "-u", abi_o], check=True, capture_output=True,
                             text=True).stdout
         if "__asan_report" not in nm or "__ubsan_handle" not in nm:
             raise RuntimeError("abi.hip's host object is not instrumented")
