@@ -528,14 +528,6 @@ static bool pipe_args(const IndexerQArgs& a_in, IndexerQArgs& a) {
   return true;
 }
 
-hipError_t launch_indexer_q_small_bf16_v1(const IndexerQArgs& args, hipStream_t stream);
-hipError_t launch_indexer_q_small_bf16_v2(const IndexerQArgs& args, hipStream_t stream);
-hipError_t launch_indexer_q_small_bf16_v3(const IndexerQArgs& args, hipStream_t stream);
-hipError_t launch_indexer_q_small_bf16_v4(const IndexerQArgs& args, hipStream_t stream);
-hipError_t launch_indexer_q_small_bf16_v5(const IndexerQArgs& args, hipStream_t stream);
-hipError_t launch_indexer_q_small_bf16_v6(const IndexerQArgs& args, hipStream_t stream);
-hipError_t launch_indexer_q_small_bf16_v7(const IndexerQArgs& args, hipStream_t stream);
-
 hipError_t launch_indexer_q_small_bf16_variant(const IndexerQArgs& a, int variant, hipStream_t stream) {
   switch (variant) {
     case 0: return launch_indexer_q_small_bf16(a, stream);

@@ -75,8 +75,15 @@ hipError_t launch_indexer_q_small_v7(const IndexerQArgs& args, hipStream_t strea
 // launch from X to FP4 Q; K = 1536, 1 to 256 tokens
 bool indexer_q_small_bf16_supported(const IndexerQArgs& args);
 hipError_t launch_indexer_q_small_bf16(const IndexerQArgs& args, hipStream_t stream);
-// the same with convention variant v = 1..7 (launch_indexer_q_small_bf16_v<v>);
-// v = 0 is launch_indexer_q_small_bf16
+// the same with convention variant v = 1..7 compiled in (indexer_q_small_v<v>.hip),
+// and a dispatcher over v = 0..7 (0: launch_indexer_q_small_bf16)
+hipError_t launch_indexer_q_small_bf16_v1(const IndexerQArgs& args, hipStream_t stream);
+hipError_t launch_indexer_q_small_bf16_v2(const IndexerQArgs& args, hipStream_t stream);
+hipError_t launch_indexer_q_small_bf16_v3(const IndexerQArgs& args, hipStream_t stream);
+hipError_t launch_indexer_q_small_bf16_v4(const IndexerQArgs& args, hipStream_t stream);
+hipError_t launch_indexer_q_small_bf16_v5(const IndexerQArgs& args, hipStream_t stream);
+hipError_t launch_indexer_q_small_bf16_v6(const IndexerQArgs& args, hipStream_t stream);
+hipError_t launch_indexer_q_small_bf16_v7(const IndexerQArgs& args, hipStream_t stream);
 hipError_t launch_indexer_q_small_bf16_variant(const IndexerQArgs& args, int variant, hipStream_t stream);
 
 // standalone epilogue: bf16 Q [M, H*128] (row stride ldq elements) -> RoPE,
