@@ -381,15 +381,17 @@ def indexer_q_prep_bf16(x, w, w_scales, positions, cos_sin, n_heads: int = 64, h
     return q_fp4, q_scales
 
 
-def indexer_q_prep(x, w, w_scales, positions, cos_sin, n_heads: int = 64, stream=None):
+def indexer_q_prep(x, w, w_scales, positions, cos_sin, n_heads: int = 64, rope_layout: str = "half_split",
+                   scale_rule: str = "ceil", w_scale_layout: str = "tile_128x128", stream=None):
     """The whole indexer-Q preparation for a bf16 [M, K] activation batch:
     up to ONE_LAUNCH_MAX_TOKENS tokens at K = 1536 the one-launch call, else
     FP8 quantization then the fused projection / RoPE / Hadamard / FP4 call,
     both on one stream. Returns ``(q_fp4, q_scales)``; the paths give the same
-    bytes."""
+    bytes. The convention arguments are those of :func:`indexer_q_gemm_rope_fp4`."""
+    conv = dict(rope_layout=rope_layout, scale_rule=scale_rule, w_scale_layout=w_scale_layout)
     if (1 <= x.shape[0] <= ONE_LAUNCH_MAX_TOKENS and x.dim() == 2 and x.shape[1] == 1536
             and x.data_ptr() % 16 == 0 and x.stride(0) % 8 == 0 and w_scales.data_ptr() % 4 == 0):
-        return indexer_q_prep_bf16(x, w, w_scales, positions, cos_sin, n_heads=n_heads, stream=stream)
+        return indexer_q_prep_bf16(x, w, w_scales, positions, cos_sin, n_heads=n_heads, stream=stream, **conv)
     a, a_scales = fp8_quant_1x128_ue8m0(x, stream=stream)
     return indexer_q_gemm_rope_fp4(a, a_scales, w, w_scales, positions, cos_sin, n_heads=n_heads,
-                                   stream=stream)
+                                   stream=stream, **conv)

@@ -179,3 +179,20 @@ def test_one_launch_flags_match_two_calls_and_oracle(gpu_lib, weights, table, la
     ref = oracle_chain_from_x(x, codes, sb, pos, 64, layout, rule)
     rep = C.check_fp4(q1.cpu().numpy(), s1.cpu().numpy(), ref["z"], ref["q_fp4"], ref["q_scales"], scale_rule=rule)
     assert rep["ok"], rep
+
+
+@pytest.mark.parametrize("M", [8, 300])
+def test_routing_helper_passes_the_flags(gpu_lib, weights, table, M):
+    """indexer_q_prep (one launch at 8 tokens, two calls at 300) with flags
+    gives the bytes of the direct two-call path with the same flags."""
+    codes, sb, wd, wsd = weights
+    inp = S.indexer_q_inputs("indexer_q_m128", M=M)
+    x, pos = inp["x"].cuda(), inp["positions"].cuda()
+    kw = dict(rope_layout="interleaved", scale_rule="ocp_floor")
+    q1, s1 = gpu_lib.indexer_q_prep(x, wd, wsd, pos, table[4096], **kw)
+    a, a_s = gpu_lib.fp8_quant_1x128_ue8m0(x)
+    q2, s2 = gpu_lib.indexer_q_gemm_rope_fp4(a, a_s, wd, wsd, pos, table[4096], **kw)
+    q0, _ = gpu_lib.indexer_q_prep(x, wd, wsd, pos, table[4096])
+    torch.cuda.synchronize()
+    assert torch.equal(q1, q2) and torch.equal(s1, s2)
+    assert not torch.equal(q1, q0)
