@@ -513,6 +513,13 @@ def prefill32k_bench(args):
     t_fused = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e-3
     flops = 2.0 * M * (N_HEADS * HEAD_DIM) * K_PROJ
     fused_tflops = flops / t_fused / 1e12
+    def step32k(i):
+        iqp.fp8_quant_1x128_ue8m0(x, q=a, scales=a_s)
+        iqp.indexer_q_gemm_rope_fp4(a, a_s, w, wsb, pos, cs, n_heads=N_HEADS, q_fp4=q, q_scales=qs)
+
+    t_step_graph = graph_launch_time(step32k, K, reps=1)   # the timed `value`, as in the default workload
+    print(f"[bench] chain at {M} tokens from a captured graph: {t_step_graph * 1e6:.1f} us/step",
+          file=sys.stderr, flush=True)
     print(f"[bench] chain at {M} tokens: {total_ms / K * 1e3:.1f} us/step; quant {t_quant * 1e6:.1f} us, "
           f"fused {t_fused * 1e6:.1f} us = {fused_tflops:.0f} TFLOP/s", file=sys.stderr, flush=True)
     del a, a_s, q, qs
@@ -536,12 +543,14 @@ def prefill32k_bench(args):
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_tokens, inp, w_cpu, wsb_cpu)
     result = {
         "metric": "tokens/sec & % roofline: FP8 quant (HBM GB/s) + fused indexer-Q (MFMA util)",
-        "value": M * K / (total_ms * 1e-3),
+        "value": M / t_step_graph,
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
-        "ms_per_step": total_ms / K,
+        "ms_per_step": t_step_graph * 1e3,
+        "timing": "K whole steps captured into one HIP graph, one untimed replay, then one timed",
+        "eager_with_kernel_events": {"ms_per_step": total_ms / K, "tokens_per_s": M * K / (total_ms * 1e-3)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
