@@ -111,6 +111,8 @@ def check_fp4(q_dev, s_dev, z_ref, q_ref, s_ref, scale_rule: str = "ceil") -> di
     # 3. codes, compared at the device's scale
     e_dev = s_dev - 127
     scaled = zb * np.ldexp(1.0, -e_dev)[..., None]
+    # clipping a saturating value (floor rule) changes no verdict: beyond +-6
+    # the nearest E2M1 value is +-6 either way and no midpoint is near
     scaled = np.clip(scaled, -E2M1_MAX, E2M1_MAX).reshape(z.shape)
     v_dev = E2M1_VALUES[e2m1_unpack(q_dev)]
     # reference value at the device's scale: where the scale agrees this is

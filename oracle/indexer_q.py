@@ -177,13 +177,16 @@ def hadamard_rotate(y) -> np.ndarray:
 # ----------------------------------------------------------------------------
 
 
-def fp4_quantize(z, decide_dtype=np.float32, scale_rule: str = "ceil") -> tuple:
+def fp4_quantize(z, decide_dtype=None, scale_rule: str = "ceil") -> tuple:
     """Quantize the last axis (a multiple of 32) in 32-element blocks.
 
-    The scale and code decisions are taken on z rounded to ``decide_dtype``
-    (float32 by default: the precision the device path holds z in); the
-    decision itself is exact. Returns ``(packed, scale_bytes)``: packed codes
-    [..., n/2] uint8 and scale bytes [..., n/32] uint8.
+    The scale and code decisions are taken exactly on the float64 z (the
+    pages fix no precision for them: they only note that evaluation order can
+    move a value across an FP4 rounding boundary, tokenspeed PR
+    "perf(deepseek-v4): accelerate indexer Q and packed FP8 quantization",
+    Risk and fallback). ``decide_dtype`` (e.g. np.float32) rounds z to that
+    type first, for diagnostics. Returns ``(packed, scale_bytes)``: packed
+    codes [..., n/2] uint8 and scale bytes [..., n/32] uint8.
 
     scale_rule "ceil" (the default reading): e = ceil(log2(amax / 6)), the
     smallest power of two that keeps the block within E2M1's range, so codes

@@ -169,3 +169,116 @@ def test_one_boundary_flip_allowed_in_a_small_sample_two_are_not():
     p2, s2 = flipped(2)
     r2 = C.check_fp4(p2, s2, z, p, s)
     assert r2["scale_mismatch"] == 2 and r2["scale_illegal"] == 0 and not r2["ok"]
+
+
+# ---------------------------------------------------------------- OCP floor rule
+#
+# Under scale_rule="ocp_floor" the exponent is floor(log2 amax) - 2: it steps
+# where amax itself (equivalently amax / 4) crosses a power of two, not where
+# amax / 6 does, and codes saturate at +-6.
+
+
+def _floor_block(amax, rows=64, seed=11):
+    """rows x 2 heads x 128 dims of N(0, (amax/4)^2) whose block (0, 0, 0)
+    has the given amax (its other elements kept below it)."""
+    z = np.random.default_rng(seed).standard_normal((rows, 2, 128)) * (amax / 4)
+    blk = np.clip(z[0, 0, :32], -0.9 * amax, 0.9 * amax)
+    blk[7] = amax
+    z[0, 0, :32] = blk
+    return z
+
+
+def _requantize_block(p, s, z, e_dev):
+    """Device output whose block (0, 0, 0) uses exponent e_dev with codes
+    rounded at that scale (saturating at +-6)."""
+    s_dev = s.copy()
+    s_dev[0, 0, 0] = 127 + e_dev
+    codes = F.e2m1_unpack(p)
+    codes[0, 0, :32] = F.e2m1_encode_rne(np.clip(z[0, 0, :32] * 2.0 ** -e_dev, -6.0, 6.0))
+    return F.e2m1_pack(codes), s_dev
+
+
+@pytest.mark.parametrize("k", [-3, 0, 4])
+def test_floor_rule_scale_flip_legal_within_window_of_a_power_of_two(k):
+    # amax just below 2^(k+2): the oracle's exponent is k - 1; a device that
+    # rounded amax up onto 2^(k+2) takes k. amax / 4 is within 2^-10 of 2^k.
+    amax = 2.0 ** (k + 2) * (1 - 2.0 ** -12)
+    z = _floor_block(amax)
+    p, s = IQ.fp4_quantize(z, scale_rule="ocp_floor")
+    assert s[0, 0, 0] == 127 + k - 1
+    p_dev, s_dev = _requantize_block(p, s, z, k)
+    r = C.check_fp4(p_dev, s_dev, z, p, s, scale_rule="ocp_floor")
+    assert r["scale_mismatch"] == 1 and r["scale_illegal"] == 0 and r["code_illegal"] == 0 and r["ok"], r
+    # the ceil rule's window (amax / 6 near a power of two) does not cover it
+    r_ceil = C.check_fp4(p_dev, s_dev, z, p, s)
+    assert r_ceil["scale_illegal"] == 1 and not r_ceil["ok"]
+    # and a flip in the other direction (amax just above 2^(k+2)) is legal too
+    amax = 2.0 ** (k + 2) * (1 + 2.0 ** -12)
+    z = _floor_block(amax)
+    p, s = IQ.fp4_quantize(z, scale_rule="ocp_floor")
+    assert s[0, 0, 0] == 127 + k
+    p_dev, s_dev = _requantize_block(p, s, z, k - 1)
+    r = C.check_fp4(p_dev, s_dev, z, p, s, scale_rule="ocp_floor")
+    assert r["scale_mismatch"] == 1 and r["scale_illegal"] == 0 and r["code_illegal"] == 0 and r["ok"], r
+
+
+def test_floor_rule_scale_flip_just_outside_the_window_is_illegal():
+    amax = 4.0 * (1 - 2.0 ** -9)          # amax / 4 is 2^-9 away from 2^0
+    z = _floor_block(amax)
+    p, s = IQ.fp4_quantize(z, scale_rule="ocp_floor")
+    assert s[0, 0, 0] == 126
+    p_dev, s_dev = _requantize_block(p, s, z, 0)
+    r = C.check_fp4(p_dev, s_dev, z, p, s, scale_rule="ocp_floor")
+    assert r["scale_illegal"] == 1 and not r["ok"]
+
+
+def test_floor_rule_flip_at_a_ceil_boundary_is_illegal():
+    # amax / 6 = 2^0 exactly: a legal flip under the ceil rule, but under the
+    # floor rule amax = 6 is far (6 / 4 = 1.5) from any power of two
+    z = _floor_block(6.0)
+    p, s = IQ.fp4_quantize(z, scale_rule="ocp_floor")
+    assert s[0, 0, 0] == 127
+    p_dev, s_dev = _requantize_block(p, s, z, 1)
+    r = C.check_fp4(p_dev, s_dev, z, p, s, scale_rule="ocp_floor")
+    assert r["scale_illegal"] == 1 and not r["ok"]
+
+
+def test_floor_rule_saturated_codes():
+    # amax 7.5 * 2^-1 -> e = floor(log2 3.75) - 2 = -1; the element scales to
+    # 7.5 and saturates to 6 (code 7); its negative twin to code 0xF
+    z = _floor_block(3.75)
+    z[0, 0, 9] = -3.75
+    p, s = IQ.fp4_quantize(z, scale_rule="ocp_floor")
+    assert s[0, 0, 0] == 126
+    codes = F.e2m1_unpack(p)
+    assert codes[0, 0, 7] == 7 and codes[0, 0, 9] == 15
+    assert C.check_fp4(p, s, z, p, s, scale_rule="ocp_floor")["ok"]
+    # a device that wrote 4 (code 6) for the saturated 6 is wrong: 7.5 is not
+    # within the window of the 4|6 midpoint
+    bad = C.check_fp4(set_code(p, (0, 0, 7), 6), s, z, p, s, scale_rule="ocp_floor")
+    assert bad["code_illegal"] == 1 and not bad["ok"]
+    bad = C.check_fp4(set_code(p, (0, 0, 9), 14), s, z, p, s, scale_rule="ocp_floor")
+    assert bad["code_illegal"] == 1 and not bad["ok"]
+
+
+def test_floor_rule_code_flip_only_at_a_midpoint():
+    z = _floor_block(3.75)
+    z[0, 0, 3] = 2.5 * 0.5                 # scaled 2.5: the 2|3 midpoint
+    z[0, 0, 4] = 2.2 * 0.5                 # scaled 2.2: interior
+    p, s = IQ.fp4_quantize(z, scale_rule="ocp_floor")
+    codes = F.e2m1_unpack(p)
+    assert codes[0, 0, 3] == 4 and codes[0, 0, 4] == 4      # 2.5 ties to even code 4 (2.0)
+    ok = C.check_fp4(set_code(p, (0, 0, 3), 5), s, z, p, s, scale_rule="ocp_floor")
+    assert ok["code_mismatch"] == 1 and ok["code_illegal"] == 0 and ok["ok"]
+    bad = C.check_fp4(set_code(p, (0, 0, 4), 5), s, z, p, s, scale_rule="ocp_floor")
+    assert bad["code_illegal"] == 1 and not bad["ok"]
+
+
+def test_floor_rule_floor_byte():
+    # amax below 1e-4 = 1.6384 * 2^-14: exponent -16 (byte 111) on both sides
+    z = _floor_block(3e-5)
+    z[0, 0, :32] *= 1e-4
+    z[0, 0, 7] = 3e-5
+    p, s = IQ.fp4_quantize(z, scale_rule="ocp_floor")
+    assert s[0, 0, 0] == 111
+    assert C.check_fp4(p, s, z, p, s, scale_rule="ocp_floor")["ok"]

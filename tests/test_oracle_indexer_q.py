@@ -237,7 +237,7 @@ def test_fp4_golden_worked_example():
     for base, entries in gd["z"].items():
         for i, v in entries:
             z[int(base) + i] = v
-    packed, sb = IQ.fp4_quantize(z[None, :], decide_dtype=None)
+    packed, sb = IQ.fp4_quantize(z[None, :])
     assert sb[0].tolist() == gd["scale_bytes"]
     for base, vals in gd["packed"].items():
         b = int(base)
@@ -246,11 +246,12 @@ def test_fp4_golden_worked_example():
 
 @pytest.mark.parametrize("k", [-15, -7, 0, 5, 20])
 def test_fp4_scale_closed_form(k):
-    z = np.zeros((2, 32))
+    z = np.zeros((3, 32))
     z[0, 3] = 6.0 * 2.0 ** k
     z[1, 3] = np.nextafter(np.float32(6.0 * 2.0 ** k), np.float32(np.inf))
+    z[2, 3] = np.nextafter(6.0 * 2.0 ** k, np.inf)          # one float64 ulp above
     _, sb = IQ.fp4_quantize(z)
-    assert sb[0, 0] == 127 + k and sb[1, 0] == 128 + k
+    assert sb[0, 0] == 127 + k and sb[1, 0] == 128 + k and sb[2, 0] == 128 + k
 
 
 def test_fp4_floor():
@@ -268,22 +269,28 @@ def test_fp4_dequant_error_bound():
     codes = F.e2m1_unpack(packed)
     scale = np.repeat(np.ldexp(1.0, sb.astype(np.int64) - 127), 32, axis=1)
     deq = F.e2m1_decode(codes) * scale
-    z32 = z.astype(np.float32).astype(np.float64)
-    t = np.abs(z32) / scale
+    t = np.abs(z) / scale
     step = np.where(t < 2, 0.5, np.where(t < 4, 1.0, 2.0))
-    assert np.all(np.abs(deq - z32) <= step / 2 * scale)
+    assert np.all(np.abs(deq - z) <= step / 2 * scale)
 
 
-def test_fp4_decision_uses_float32_value():
-    """A float64 value a hair above a midpoint that rounds to the midpoint in
-    float32 is decided on the float32 value (tie -> even code)."""
+def test_fp4_decision_is_taken_on_the_float64_value():
+    """A float64 value a hair above a midpoint (one that float32 would round
+    onto the midpoint) is decided on its exact value by default: it rounds
+    up; rounded to float32 first it is a tie and goes to the even code."""
     z = np.zeros((1, 32))
     z[0, 0] = 6.0
     z[0, 1] = 0.25 + 2.0 ** -40
     packed, _ = IQ.fp4_quantize(z)
-    assert F.e2m1_unpack(packed)[0, 1] == 0
-    packed64, _ = IQ.fp4_quantize(z, decide_dtype=None)
-    assert F.e2m1_unpack(packed64)[0, 1] == 1
+    assert F.e2m1_unpack(packed)[0, 1] == 1
+    packed32, _ = IQ.fp4_quantize(z, decide_dtype=np.float32)
+    assert F.e2m1_unpack(packed32)[0, 1] == 0
+    # the same at a scale boundary: amax / 6 a hair above 2^0 takes e = 1 in
+    # float64, e = 0 once rounded to float32
+    z[0, 0] = 6.0 * (1.0 + 2.0 ** -40)
+    _, sb = IQ.fp4_quantize(z)
+    _, sb32 = IQ.fp4_quantize(z, decide_dtype=np.float32)
+    assert sb[0, 0] == 128 and sb32[0, 0] == 127
 
 
 # ---------------------------------------------------------------- chain
