@@ -9,7 +9,9 @@ If the library has not been built, importing this package raises ImportError
 (build it with ``python fp4_quantized_prep_amd/build.py``); there is no
 fallback implementation.
 """
+import contextlib
 import ctypes
+import functools
 import os
 
 import torch
@@ -100,6 +102,19 @@ def _stream(t: torch.Tensor, stream=None):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _on_stream(fn):
+    """Run a wrapper with its explicit ``stream`` (if any) current, so that
+    every tensor it allocates (outputs, the preparation's FP8 intermediates)
+    comes from that stream's pool: the caching allocator then never hands
+    that memory to another stream while the call's kernels may still use it."""
+    @functools.wraps(fn)
+    def wrapper(*args, stream=None, **kwargs):
+        ctx = torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+        with ctx:
+            return fn(*args, stream=stream, **kwargs)
+    return wrapper
+
+
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
@@ -119,6 +134,7 @@ def _bytes_u8(t: torch.Tensor) -> torch.Tensor:
     return t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t
 
 
+@_on_stream
 def fp8_quant_1x128_ue8m0(x: torch.Tensor, scale_layout: str = "k", q: torch.Tensor = None,
                           scales: torch.Tensor = None, stream=None):
     """Packed-UE8M0 FP8 1x128 quantization of a bf16 [M, K] matrix.
@@ -141,6 +157,8 @@ def fp8_quant_1x128_ue8m0(x: torch.Tensor, scale_layout: str = "k", q: torch.Ten
         q = torch.empty((M, K), dtype=torch.uint8, device=dev)
     q = _bytes_u8(q)
     _require(q, "q", torch.uint8, dev, 2)
+    if tuple(q.shape) != (M, K) or q.stride(1) != 1:
+        raise ValueError(f"q must be [{M}, {K}] with contiguous rows, got shape {tuple(q.shape)}")
     if scales is None:
         if scale_layout == "k":
             scales = torch.empty((M, nw), dtype=torch.int32, device=dev)
@@ -150,12 +168,15 @@ def fp8_quant_1x128_ue8m0(x: torch.Tensor, scale_layout: str = "k", q: torch.Ten
         else:
             raise ValueError("scale_layout must be 'k' or 'mn'")
     _require(scales, "scales", torch.int32, dev, 2)
+    if tuple(scales.shape) != (M, nw):
+        raise ValueError(f"scales must be [{M}, {nw}] (one packed word per 512 columns), got {tuple(scales.shape)}")
     st = _lib.fp8_quant_1x128_ue8m0(_ptr(x), M, K, x.stride(0), _ptr(q), q.stride(0), _ptr(scales),
                                     scales.stride(0), scales.stride(1), _stream(x, stream))
     _check(st, "fp8_quant_1x128_ue8m0")
     return q, scales
 
 
+@_on_stream
 def fp8_quant_weight_128x128_ue8m0(w: torch.Tensor, q: torch.Tensor = None, scales: torch.Tensor = None,
                                    stream=None):
     """Weight preparation: bf16 w [N, K] (rows contiguous, N and K multiples
@@ -204,6 +225,9 @@ def _indexer_q_common(a, a_scales, w, w_scales, positions, cos_sin, n_heads, hea
         raise ValueError(f"w_scales must be [{ws_rows}, {K // 128}]")
     if positions.shape[0] != M or a_scales.shape[0] != M:
         raise ValueError("positions and a_scales need one row per token")
+    nw = (K // 128 + 3) // 4
+    if a_scales.shape[1] != nw:
+        raise ValueError(f"a_scales must be [M, {nw}] (one packed word per 512 columns), got {tuple(a_scales.shape)}")
     if cos_sin.shape[1] != rope_dim:
         raise ValueError(f"cos_sin must have {rope_dim} columns")
     args = [_ptr(a), a.stride(0), _ptr(a_scales), a_scales.stride(0), a_scales.stride(1),
@@ -219,6 +243,7 @@ def _convention_flags(rope_layout: str, scale_rule: str) -> int:
         (IQP_FP4_SCALE_OCP_FLOOR if scale_rule == "ocp_floor" else 0)
 
 
+@_on_stream
 def indexer_q_gemm_rope_fp4(a, a_scales, w, w_scales, positions, cos_sin, n_heads: int = 64,
                             head_dim: int = 128, rope_dim: int = 64, q_fp4=None, q_scales=None,
                             rope_layout: str = "half_split", scale_rule: str = "ceil",
@@ -259,6 +284,7 @@ def indexer_q_gemm_rope_fp4(a, a_scales, w, w_scales, positions, cos_sin, n_head
     return q_fp4, q_scales
 
 
+@_on_stream
 def debug_indexer_q_f32(a, a_scales, w, w_scales, positions, cos_sin, stage: int, n_heads: int = 64,
                         head_dim: int = 128, rope_dim: int = 64, out=None, stream=None):
     """float32 [M, H*128] after stage 0 (GEMM), 1 (RoPE) or 2 (Hadamard) of the
@@ -275,6 +301,7 @@ def debug_indexer_q_f32(a, a_scales, w, w_scales, positions, cos_sin, stage: int
     return out
 
 
+@_on_stream
 def indexer_q_rope_hadamard_fp4(q, positions, cos_sin, n_heads: int = 64, head_dim: int = 128,
                                 rope_dim: int = 64, q_fp4=None, q_scales=None, rope_layout: str = "half_split",
                                 scale_rule: str = "ceil", stream=None):
@@ -314,6 +341,7 @@ def indexer_q_rope_hadamard_fp4(q, positions, cos_sin, n_heads: int = 64, head_d
     return q_fp4, q_scales
 
 
+@_on_stream
 def rope_cos_sin_table(theta: float, max_pos: int, rope_dim: int = 64, device=None, out=None, stream=None):
     """float32 [max_pos, rope_dim] table of cos (first half) and sin (second
     half) of pos * theta^(-2i/rope_dim), computed on the device in float64."""
@@ -328,6 +356,7 @@ def rope_cos_sin_table(theta: float, max_pos: int, rope_dim: int = 64, device=No
     return out
 
 
+@_on_stream
 def indexer_q_prep_bf16(x, w, w_scales, positions, cos_sin, n_heads: int = 64, head_dim: int = 128,
                         rope_dim: int = 64, q_fp4=None, q_scales=None, rope_layout: str = "half_split",
                         scale_rule: str = "ceil", w_scale_layout: str = "tile_128x128", stream=None):
@@ -381,6 +410,7 @@ def indexer_q_prep_bf16(x, w, w_scales, positions, cos_sin, n_heads: int = 64, h
     return q_fp4, q_scales
 
 
+@_on_stream
 def indexer_q_prep(x, w, w_scales, positions, cos_sin, n_heads: int = 64, rope_layout: str = "half_split",
                    scale_rule: str = "ceil", w_scale_layout: str = "tile_128x128", stream=None):
     """The whole indexer-Q preparation for a bf16 [M, K] activation batch:

@@ -7,6 +7,7 @@
 Compiles every csrc/*.hip with hipcc into fp4_quantized_prep_amd/libiqprep.so.
 hipcc cross-compiles, so no GPU is needed to build.
 """
+import concurrent.futures
 import glob
 import os
 import subprocess
@@ -49,8 +50,8 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"no HIP sources under {CSRC}")
     obj_dir = os.path.join(PKG_DIR, "_build")
     os.makedirs(obj_dir, exist_ok=True)
-    objs = []
-    for src in sources:
+
+    def compile_one(src):
         obj = os.path.join(obj_dir, os.path.basename(src) + ".o")
         cmd = [hipcc()] + compile_flags() + ["-c", src, "-o", obj]
         if verbose:
@@ -58,7 +59,12 @@ def build(verbose: bool = False) -> str:
         res = subprocess.run(cmd, capture_output=True, text=True)
         if res.returncode != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n{res.stdout}\n{res.stderr}")
-        objs.append(obj)
+        return obj
+
+    # one hipcc per source, a few at a time (each is single-threaded)
+    jobs = max(1, min(8, len(os.sched_getaffinity(0))))
+    with concurrent.futures.ThreadPoolExecutor(jobs) as pool:
+        objs = list(pool.map(compile_one, sources))
     tmp = LIB_PATH + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:

@@ -8,7 +8,7 @@ argument-check tests (tests/test_abi_cpu.py, the ones that take only the
 library) against it in a child process with the ASan runtime preloaded. No
 GPU is used: every call returns from validation before touching a device.
 
-    python fp4_quantized_prep_amd/sanitize_abi.py      # exit status 0 = clean
+    python tests/sanitize_abi.py      # exit status 0 = clean
 """
 import glob
 import os
@@ -16,8 +16,8 @@ import subprocess
 import sys
 import tempfile
 
-PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-ROOT = os.path.dirname(PKG_DIR)
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PKG_DIR = os.path.join(ROOT, "fp4_quantized_prep_amd")
 sys.path.insert(0, PKG_DIR)
 import build as B  # noqa: E402
 

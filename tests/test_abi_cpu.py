@@ -206,3 +206,40 @@ def test_python_wrapper_rejects_wrong_dtypes(iqp):
     import torch
     with pytest.raises(TypeError):
         iqp.fp8_quant_1x128_ue8m0(torch.zeros(2, 128, dtype=torch.float32))
+
+
+# ---------------------------------------------------------------- binding shape checks
+#
+# The C ABI takes row strides, not buffer sizes, so an output or scale buffer
+# with too few rows or words could only be caught by the binding: it must
+# raise before any launch. CPU tensors are used; every case fails in Python.
+
+
+def test_binding_rejects_undersized_quant_outputs(iqp):
+    import torch
+    x = torch.zeros((4, 1536), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="q must be"):
+        iqp.fp8_quant_1x128_ue8m0(x, q=torch.empty((3, 1536), dtype=torch.uint8))
+    with pytest.raises(ValueError, match="q must be"):
+        iqp.fp8_quant_1x128_ue8m0(x, q=torch.empty((4, 1024), dtype=torch.uint8))
+    with pytest.raises(ValueError, match="scales must be"):
+        iqp.fp8_quant_1x128_ue8m0(x, q=torch.empty((4, 1536), dtype=torch.uint8),
+                                  scales=torch.empty((3, 3), dtype=torch.int32))
+    with pytest.raises(ValueError, match="scales must be"):
+        iqp.fp8_quant_1x128_ue8m0(x, q=torch.empty((4, 1536), dtype=torch.uint8),
+                                  scales=torch.empty((4, 2), dtype=torch.int32))
+
+
+def test_binding_rejects_short_activation_scale_rows(iqp):
+    import torch
+    M, K, H = 1, 1536, 2
+    a = torch.zeros((M, K), dtype=torch.uint8)
+    w = torch.zeros((H * 128, K), dtype=torch.uint8)
+    ws = torch.zeros((H, K // 128), dtype=torch.uint8)
+    pos = torch.zeros((M,), dtype=torch.int64)
+    cs = torch.zeros((16, 64), dtype=torch.float32)
+    # [M, 1] words for K = 1536 (12 blocks need 3 words): the kernel would read past them
+    with pytest.raises(ValueError, match="a_scales must be"):
+        iqp.indexer_q_gemm_rope_fp4(a, torch.zeros((M, 1), dtype=torch.int32), w, ws, pos, cs, n_heads=H)
+    with pytest.raises(ValueError, match="a_scales must be"):
+        iqp.debug_indexer_q_f32(a, torch.zeros((M, 2), dtype=torch.int32), w, ws, pos, cs, stage=0, n_heads=H)

@@ -1,6 +1,6 @@
 """The C ABI's argument validation under host ASan and UBSan (CPU only): a
 sanitized copy of the library runs the argument-check tests in a child
-process (fp4_quantized_prep_amd/sanitize_abi.py)."""
+process (tests/sanitize_abi.py)."""
 import glob
 import os
 import subprocess
@@ -9,7 +9,7 @@ import sys
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SCRIPT = os.path.join(ROOT, "fp4_quantized_prep_amd", "sanitize_abi.py")
+SCRIPT = os.path.join(ROOT, "tests", "sanitize_abi.py")
 
 
 def test_abi_validation_clean_under_asan_ubsan():
