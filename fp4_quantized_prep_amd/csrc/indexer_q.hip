@@ -514,6 +514,10 @@ hipError_t launch_kernel(const IndexerQArgs& a_in, int stage, hipStream_t stream
 
 }  // namespace
 
+// token count from which the fused FP4 call runs the split-role build of the
+// pipelined kernel (measured: below it the one-role build is as fast or faster)
+constexpr int64_t SPLIT_MIN_TOKENS = 1024;
+
 // the pipelined kernel's launch arguments: one workgroup per CU, each head
 // pair gets CUs / pairs chunks of whole 128-token tiles
 static bool pipe_args(const IndexerQArgs& a_in, IndexerQArgs& a) {
@@ -578,6 +582,9 @@ hipError_t launch_indexer_q(const IndexerQArgs& a_in, int stage, hipStream_t str
   if (stage == -1 && indexer_q_pipe_supported(a_in)) {
     IndexerQArgs a;
     if (!pipe_args(a_in, a)) return hipErrorInvalidValue;
+    // from SPLIT_MIN_TOKENS on, the split-role build: its epilogue runs in
+    // its own waves, which pays once most workgroups hold two tiles or more
+    if (a.M >= SPLIT_MIN_TOKENS && indexer_q_split_supported(a)) return launch_indexer_q_split(a, stream);
     return launch_indexer_q_pipe(a, stream);
   }
   return launch_kernel(a_in, stage, stream);

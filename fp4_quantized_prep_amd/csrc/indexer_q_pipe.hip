@@ -57,6 +57,17 @@
 #define IQP_PIPE_LAUNCH launch_indexer_q_pipe
 #define IQP_PIPE_KERNEL indexer_q_pipe_kernel
 #endif
+// Split-role build (IQP_PIPE_SPLIT 1): eight waves, two per SIMD. The two
+// accumulator sets of one schedule live in two waves instead of one: tile t
+// is computed by wave group t % 2 (K loop: MFMAs and operand reads only)
+// while the other group runs the epilogue of the tile it computed before and
+// issues the weight and scale-word copies (the computing group issues the
+// activation copies, which balances the two). Measured on gfx950: a wave's VALU and memory
+// instructions cost a co-resident wave's MFMAs almost nothing, while the same
+// instructions in the MFMA wave itself cost it issue cycles.
+#ifndef IQP_PIPE_SPLIT
+#define IQP_PIPE_SPLIT 0
+#endif
 
 namespace iqp {
 namespace {
@@ -66,8 +77,11 @@ constexpr bool VAR_IL = (IQP_PIPE_VARIANT & 1) != 0;
 constexpr bool VAR_FLOOR = (IQP_PIPE_VARIANT & 2) != 0;
 constexpr bool VAR_ROWS = (IQP_PIPE_VARIANT & 4) != 0;
 
-constexpr int NWAVES = 4;
-constexpr int NTHREADS = NWAVES * 64;
+constexpr bool SPLIT = IQP_PIPE_SPLIT != 0;
+constexpr int NWAVES = 4;                           // waves of one role (one per SIMD)
+constexpr int NTHREADS = (SPLIT ? 2 : 1) * NWAVES * 64;
+// the parts of a half-step a wave issues
+enum Role { ROLE_ALL, ROLE_MFMA, ROLE_EPI };
 constexpr int WROWS = 256;                          // weight rows: two heads
 constexpr int TOKS = 128;                           // tokens per tile
 constexpr int SUB = 32;                             // tokens per MFMA column tile
@@ -94,6 +108,8 @@ static_assert(W_OFF >= KB * (NKB - 1), "copy LDS bases must stay non-negative");
 // at a block barrier the copies of the block after next (13 per wave) may
 // still be in flight: s_waitcnt vmcnt(13)
 constexpr int WAITCNT_VM13 = (13 & 15) | (7 << 4) | (15 << 8) | ((13 >> 4) << 14);
+// s_waitcnt vmcnt(n), n < 64
+constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
 // A lane value the compiler must treat as new at each use: addresses built
 // from it are then computed where they are used instead of being hoisted out
@@ -127,8 +143,10 @@ struct Epi {
   int tlane;        // the epilogue tile's token of sub-tile 0 (sub-tile tm: + TM_STRIDE tm)
   // positions as loaded (clamped into the table where the RoPE rows are
   // fetched, so no load is waited for before then)
-  int64_t pos1;         // the epilogue tile's sub-tile 1
-  int64_t npos0, npos1; // the K-loop tile's (its epilogue comes next)
+  // (the split build holds them clamped into the table as 32-bit values)
+  using pos_t = std::conditional_t<SPLIT, int32_t, int64_t>;
+  pos_t pos1;           // the epilogue tile's sub-tile 1
+  pos_t npos0, npos1;   // the K-loop tile's (its epilogue comes next)
 };
 
 struct Ctx {
@@ -143,7 +161,8 @@ struct Ctx {
   // slab (rows that always exist); its column part within the K block is the
   // instruction offset, which the hardware adds to the LDS address as well.
   uint32_t vw;                   // weight lane offset (row within an 8-row slab, chunk)
-  uint32_t va[ACOPIES];          // activation lane offsets of the four slabs
+  uint32_t va[SPLIT ? 1 : ACOPIES];   // activation lane offsets of the four slabs (split: slab 0, the
+                                      // others a scalar stride on)
   uint32_t vs;                   // scale-word lane offset
   int wrow[WCOPIES];             // weight slab row offsets (bytes)
   int wave_lds;                  // 1 KiB per wave: this wave's part of each group of four slabs
@@ -154,7 +173,7 @@ struct Ctx {
     const int tid = threadIdx.x;
     lane = tid & 63;
     half = lane >> 5;
-    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6) & (NWAVES - 1);   // within its group
     hn = wave & 1;
     th = wave >> 1;
     head = 2 * pair + hn;
@@ -174,17 +193,10 @@ struct Ctx {
         for (int k = 0; k < 3; ++k) wsr[tn][k] = row[k];
       }
     }
-    // copy i of this wave lands in rows 8 (wave + 4 i) + lane / 8, slot lane % 8,
-    // which holds the row's chunk (lane % 8) ^ ((row / 2) % 8): the slab index
-    // wave + 4 i has the parity of wave, so that is the same for every copy
-    const int chunk = (lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7);
     const int64_t row0 = (int64_t)2 * pair * HEAD_DIM;
     const int64_t wrows = (int64_t)p.H * HEAD_DIM - row0;
     rw = make_rsrc(p.w + row0 * p.ldw, (uint64_t)(wrows < WROWS ? wrows : WROWS) * p.ldw);
-    vw = (uint32_t)((8 * wave + (lane >> 3)) * p.ldw + 16 * chunk);
-#pragma unroll
-    for (int i = 0; i < ACOPIES; ++i) va[i] = (uint32_t)((8 * wave + (lane >> 3) + 32 * i) * p.lda + 16 * chunk);
-    vs = (uint32_t)(4 * (64 * (wave & 1) + lane) * p.as_sm);   // waves w and w + 2 copy the same words
+    copy_offsets(lane);
     // slabs 4..7 hold the pair's second head; with an odd head count the last
     // pair has none and they re-read the first head's rows (never stored)
     const int hi = 2 * pair + 1 < p.H ? 128 * (int)p.ldw : 0;
@@ -192,24 +204,36 @@ struct Ctx {
     for (int w = 0; w < WCOPIES; ++w) wrow[w] = (w < 4 ? 0 : hi) + 32 * (w & 3) * (int)p.ldw;
     wave_lds = SLAB * wave;
     words_lds = 256 * (wave & 1);
+    read_bases(lane);
+  }
+
+  // Lane offsets of the copies. copy i of this wave lands in rows 8 (wave +
+  // 4 i) + lane / 8, slot lane % 8, which holds the row's chunk (lane % 8) ^
+  // ((row / 2) % 8): the slab index wave + 4 i has the parity of wave, so that
+  // is the same for every copy. (The split build re-forms them from a fresh
+  // lane id at every epilogue role.)
+  __device__ __forceinline__ void copy_offsets(int ln) {
+    const int chunk = (ln & 7) ^ ((4 * (wave & 1) + (ln >> 4)) & 7);
+    vw = (uint32_t)((8 * wave + (ln >> 3)) * p.ldw + 16 * chunk);
+#pragma unroll
+    for (int i = 0; i < (SPLIT ? 1 : ACOPIES); ++i)
+      va[i] = (uint32_t)((8 * wave + (ln >> 3) + 32 * i) * p.lda + 16 * chunk);
+    vs = (uint32_t)(4 * (64 * (wave & 1) + ln) * p.as_sm);   // waves w and w + 2 copy the same words
+  }
+
+  // LDS bases of the operand reads (the split build re-forms them at every
+  // MFMA role); whole bases: the stage and row offsets fold into the reads'
+  // offset field
+  __device__ __forceinline__ void read_bases(int ln) {
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const uint32_t col = 16 * ((4 * kh + 2 * half + e) ^ ((lane >> 1) & 7));
-        rd_w[kh][e] = W_OFF + KB * (HEAD_DIM * hn + (lane & 31)) + col;
-        rd_a[kh][e] = A_OFF + KB * (32 * th + (lane & 31)) + col;
+        const uint32_t col = 16 * ((4 * kh + 2 * (ln >> 5) + e) ^ ((ln >> 1) & 7));
+        rd_w[kh][e] = (uint32_t)fresh((int)(W_OFF + KB * (HEAD_DIM * hn + (ln & 31)) + col));
+        rd_a[kh][e] = (uint32_t)fresh((int)(A_OFF + KB * (32 * th + (ln & 31)) + col));
       }
-    rd_s = S_OFF + 4 * (32 * th + (lane & 31));
-    // whole bases: the stage and row offsets fold into the reads' offset field
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        rd_w[kh][e] = (uint32_t)fresh((int)rd_w[kh][e]);
-        rd_a[kh][e] = (uint32_t)fresh((int)rd_a[kh][e]);
-      }
-    rd_s = (uint32_t)fresh((int)rd_s);
+    rd_s = (uint32_t)fresh((int)(S_OFF + 4 * (32 * th + (ln & 31))));
   }
 
   __device__ __forceinline__ void buffers(int64_t tbase, rsrc_t& a, rsrc_t& s) const {
@@ -242,7 +266,8 @@ struct Ctx {
     } else if constexpr (WI < WCOPIES + ACOPIES) {
       constexpr int i = WI - WCOPIES;
       uint8_t* d = lds_at<A_OFF + ST * A_BYTES + SLAB * NWAVES * i - KB * J>(wave_lds);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(NEXT ? ra_n : ra, (lds_void*)d, 16, va[i], 0, KB * J, 0);
+      const uint32_t vo = SPLIT ? va[0] + (uint32_t)(32 * i) * (uint32_t)p.lda : va[SPLIT ? 0 : i];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(NEXT ? ra_n : ra, (lds_void*)d, 16, vo, 0, KB * J, 0);
     } else {
       // the word offset stays in the lane offset, under the bounds check
       const uint32_t u = (uint32_t)(4 * (J >> 2) * (int)p.as_sw);
@@ -316,6 +341,12 @@ __device__ __forceinline__ void epi_item(Epi& es, v16f (&accp)[MAX_TM][4], int i
     // them: copies into VGPRs cannot be placed any earlier (a whole set
     // copied out at the top of the K loop would not fit beside its operands).
     if (i == 0) asm volatile("" : "+a"(accp[tm][2]), "+a"(accp[tm][3]));
+    // split build: the second sub-tile's RoPE rows are fetched here, a
+    // phase before their use (fetched during the first sub-tile's last
+    // phases they would be held beside all of its values)
+    if constexpr (SPLIT && tm == 1) {
+      if (i == 0) es.rope = load_rope<VAR_IL>(es.pos1, c.half, c.p);
+    }
     if (i < 32) {
       es.v[2 + (i >> 4)][i & 15] = accp[tm][2 + (i >> 4)][i & 15];
     } else {
@@ -362,19 +393,26 @@ __device__ __forceinline__ void epi_item(Epi& es, v16f (&accp)[MAX_TM][4], int i
     const int k = (h - 7) * 16 + i, tn = k >> 3, r = r_clear(k & 7, 4);
     float r0, r1;
     swap32(es.v[tn][r], es.v[tn][r | 4], r0, r1);
-    es.v[tn][r] = r0 + r1;
-    es.v[tn][r | 4] = r0 - r1;
+    if constexpr (SPLIT) {
+      // the 1/sqrt(128) scaling folded in: (r0 +- r1) / sqrt(128)
+      const float t = r1 * INV_SQRT_128;
+      es.v[tn][r] = __builtin_fmaf(r0, INV_SQRT_128, t);
+      es.v[tn][r | 4] = __builtin_fmaf(r0, INV_SQRT_128, -t);
+    } else {
+      es.v[tn][r] = r0 + r1;
+      es.v[tn][r | 4] = r0 - r1;
+    }
   } else if constexpr (h == 9) {
-    es.v[i >> 4][i & 15] *= INV_SQRT_128;
+    if constexpr (!SPLIT) es.v[i >> 4][i & 15] *= INV_SQRT_128;
   } else {
     // item roles: phase 10: 0, 1 convert dims 0-63 (block tn = item), 2-5 RoPE
     // loads 0-3; phase 11: 0-3 RoPE loads 4-7, 4, 5 convert dims 64-127, 6 stores
     const int load = h == 10 ? i - 2 : i + 4;
     if ((h == 10 && i >= 2) || (h == 11 && i < 4)) {
       // RoPE rows of the next sub-tile: this tile's second, or the next tile's first
-      if (tm == 0)
+      if (tm == 0 && !SPLIT)
         rope_part(es, es.pos1, load, c);
-      else if (!LAST)
+      else if (tm != 0 && !LAST)
         rope_part(es, es.npos0, load, c);
       return;
     }
@@ -426,13 +464,72 @@ __device__ __forceinline__ void epi_item(Epi& es, v16f (&accp)[MAX_TM][4], int i
 }
 
 // slot s of NS runs items [n s / NS, n (s + 1) / NS) of epilogue half-step H
-template <int H, int NTMP, int NS>
+// (LAST: no tile's rows follow this one's in the same wave)
+template <int H, int NTMP, int NS, bool LAST = false>
 __device__ __forceinline__ void epi_slot(Epi& es, v16f (&accp)[MAX_TM][4], int slot, const Ctx& c) {
   if constexpr (H < 24 && NTMP > 0) {
     constexpr int n = phase_items(H % 12);
 #pragma unroll
-    for (int i = n * slot / NS; i < n * (slot + 1) / NS; ++i) epi_item<H, NTMP, false>(es, accp, i, c);
+    for (int i = n * slot / NS; i < n * (slot + 1) / NS; ++i) epi_item<H, NTMP, LAST>(es, accp, i, c);
   }
+}
+
+// Split build: the epilogue of a tile (both sub-tiles' 24 phases, in order)
+// is cut into 24 pieces of about equal cost, one per half-step, by a
+// compile-time estimate of each item's instructions; only the cut points
+// move, so the items keep their order. (In one wave the phase cut of
+// phase_items is fine: there the MFMAs set the pace.)
+constexpr int UNITS_SUB = 349;   // items of one sub-tile's 12 phases
+static_assert(UNITS_SUB == 48 + 32 + 5 * 32 + 2 * 16 + 64 + 6 + 7, "phase_items");
+constexpr int unit_phase(int k) {
+  int h = 0;
+  while (k >= phase_items(h)) k -= phase_items(h++);
+  return h;
+}
+constexpr int unit_item(int k) {
+  int h = 0;
+  while (k >= phase_items(h)) k -= phase_items(h++);
+  return k;
+}
+// instructions of item i of phase h of sub-tile tm (the split build's roles:
+// RoPE rows fetched at the second sub-tile's first item, none in phases 10, 11)
+constexpr int unit_cost(int tm, int h, int i) {
+  if (h == 0) return (i < 32 ? 1 : 2) + (tm == 1 && i == 0 ? 16 : 0);
+  if (h == 1) return i < 16 ? 6 : 2;
+  if (h <= 6) return 2;
+  if (h <= 8) return 4;
+  if (h == 9) return 0;
+  if (h == 10) return i < 2 ? 31 : 0;
+  return i < 4 ? 0 : (i < 6 ? 31 : 13);
+}
+constexpr int unit_cost_flat(int u) { return unit_cost(u / UNITS_SUB, unit_phase(u % UNITS_SUB), unit_item(u % UNITS_SUB)); }
+constexpr int cost_before(int u) {
+  int c = 0;
+  for (int k = 0; k < u; ++k) c += unit_cost_flat(k);
+  return c;
+}
+constexpr int TOTAL_COST = cost_before(2 * UNITS_SUB);
+// first unit of half-step H: the first whose cost starts at or after H / 24 of the total
+constexpr int unit_begin(int H) {
+  int u = 0, c = 0;
+  while (u < 2 * UNITS_SUB && c < (int64_t)TOTAL_COST * H / 24) c += unit_cost_flat(u++);
+  return u;
+}
+
+template <int U>
+__device__ __forceinline__ void epi_unit(Epi& es, v16f (&accp)[MAX_TM][4], const Ctx& c) {
+  constexpr int tm = U / UNITS_SUB, k = U % UNITS_SUB;
+  constexpr int item = unit_item(k);   // a constant before any pass looks at the indexing
+  epi_item<12 * tm + unit_phase(k), MAX_TM, true>(es, accp, item, c);
+}
+
+// slot s of NS runs units [b + (e - b) s / NS, b + (e - b) (s + 1) / NS) of half-step H's share
+template <int H, int NS, int SLOT>
+__device__ __forceinline__ void epi_slot_even(Epi& es, v16f (&accp)[MAX_TM][4], const Ctx& c) {
+  constexpr int b = unit_begin(H), e = unit_begin(H + 1);
+  static_for<b + (e - b) * SLOT / NS, b + (e - b) * (SLOT + 1) / NS>([&](auto uc) __attribute__((always_inline)) {
+    epi_unit<decltype(uc)::value>(es, accp, c);
+  });
 }
 
 // the whole epilogue of a tile, alone (after the chunk's last K loop)
@@ -460,13 +557,19 @@ __device__ __forceinline__ void epilogue_alone(Epi& es, v16f (&accp)[MAX_TM][4],
 //   RKH >= 0: read half RKH of the block in stage RST; RSC: also its scale words
 //   TO_P: the tile's last half-step, whose MFMAs write the finished sums into
 //         accp (read by this tile's epilogue during the next K loop)
-template <int NTM, int RST, int RKH, bool RSC, int COPY_LO, int COPY_HI, int DST, bool NEXT, int JD, int EH,
-          int NTMP, bool TO_P>
+//   ROLE: ROLE_ALL issues everything; ROLE_MFMA only the MFMAs and the
+//         operand reads; ROLE_EPI only the copies and the epilogue (of the
+//         tile this wave computed before: no prefetch of a following tile's
+//         RoPE rows)
+template <int ROLE, int NTM, int RST, int RKH, bool RSC, int COPY_LO, int COPY_HI, int DST, bool NEXT, int JD,
+          int EH, int NTMP, bool TO_P>
 __device__ __forceinline__ void half_step(Ctx& c, v16f (&acc)[MAX_TM][4], const Frags& F, const int (&as)[MAX_TM],
                                           int ws, const int (&ws4)[4], Frags& N, int (&asn)[MAX_TM], Epi& es,
                                           v16f (&accp)[MAX_TM][4]) {
-  constexpr int NM = 4 * NTM;
-  constexpr int NS = NM > 0 ? NM : 1;
+  constexpr int NM = ROLE == ROLE_EPI ? 0 : 4 * NTM;
+  // the epilogue role keeps the fenced slots too (they bound how far the
+  // scheduler moves its items, and so its register use)
+  constexpr int NS = ROLE == ROLE_EPI ? 4 * MAX_TM : (NM > 0 ? NM : 1);
   constexpr int NCP = COPY_HI - COPY_LO;
   constexpr int NSCALE = RSC ? NTM : 0;
   constexpr int NSR = 3 * NS / 4 > 0 ? 3 * NS / 4 : 1;   // scale words and A fragments: first three quarters
@@ -483,9 +586,13 @@ __device__ __forceinline__ void half_step(Ctx& c, v16f (&acc)[MAX_TM][4], const 
       if constexpr (TO_P) asm volatile("" ::"a"(acc[tm][tn]));
     }
     static_for<NCP * slot / NS, NCP * (slot + 1) / NS>([&](auto kc) __attribute__((always_inline)) {
-      c.template copy<DST, NEXT, COPY_LO + decltype(kc)::value, JD>();
+      constexpr int WI = COPY_LO + decltype(kc)::value;
+      // split roles: the MFMA role copies the activation slabs, the epilogue
+      // role the weight slabs and the scale words
+      constexpr bool A_SLAB = WI >= WCOPIES && WI < WCOPIES + ACOPIES;
+      if constexpr (ROLE == ROLE_ALL || (ROLE == ROLE_MFMA) == A_SLAB) c.template copy<DST, NEXT, WI, JD>();
     });
-    constexpr int NRA = RKH >= 0 ? NSCALE + NTM : 0;
+    constexpr int NRA = (RKH >= 0 && ROLE != ROLE_EPI) ? NSCALE + NTM : 0;
 #pragma unroll
     for (int r = NRA * slot / NSR; r < (slot < NSR ? NRA * (slot + 1) / NSR : 0); ++r) {
       if (r < NSCALE) {
@@ -497,13 +604,15 @@ __device__ __forceinline__ void half_step(Ctx& c, v16f (&acc)[MAX_TM][4], const 
     }
     // W fragment tn right after its last use in this half-step (slot NTM (tn + 1) - 1),
     // so the next one takes over its registers
-    if constexpr (RKH >= 0) {
+    if constexpr (RKH >= 0 && ROLE != ROLE_EPI) {
 #pragma unroll
       for (int tn = 0; tn < 4; ++tn)
         if (slot == (NTM > 0 ? NTM * (tn + 1) - 1 : 0))
           N.w[tn] = make_v8i(c.read16<RST>(false, RKH, 0, 32 * tn), c.read16<RST>(false, RKH, 1, 32 * tn));
     }
-    epi_slot<EH, NTMP, NS>(es, accp, slot, c);
+    if constexpr (ROLE == ROLE_ALL) epi_slot<EH, NTMP, NS>(es, accp, slot, c);
+    if constexpr (ROLE == ROLE_EPI && NTMP > 0 && EH < 24)
+      epi_slot_even<EH, NS, slot>(es, accp, c);
     __builtin_amdgcn_sched_barrier(0);
   });
 }
@@ -516,7 +625,18 @@ __device__ __forceinline__ void half_step(Ctx& c, v16f (&acc)[MAX_TM][4], const 
 //           and scale words, copies ..PART1 of block j+3 into stage j % 3,
 //           epilogue half-step 2j+1.
 // Blocks past the tile's 12 are the next tile's (the copies use its buffers).
-template <int NTM, int J, int NTMP, bool FIRST>
+// Split roles: block b's weight slabs 0-6 are copied by the epilogue role in
+// the half-step after block b-3's barrier, its weight slab 7 and scale words
+// by the epilogue role and its activation slabs by the MFMA role in the
+// half-step before block b-2's barrier. At block j's barrier block j+1 must
+// have landed, so each wave may leave outstanding only what it issued after
+// its own copies of block j+1: the MFMA role block j+2's activation slabs
+// (4); the epilogue role block j+2's weight slabs and words (7 + 2). At block
+// 0 the copies of block 1 came from the other role of the previous tile:
+// the MFMA role (then in the epilogue role) has issued 7 + 4 after them, the
+// epilogue role (then the MFMA role) 2. The MFMA role reads no operands of
+// the following tile (the other group computes it).
+template <int ROLE, int NTM, int J, int NTMP, bool FIRST>
 __device__ __forceinline__ void k_block(Ctx& c, v16f (&acc)[MAX_TM][4], Frags& f0, Frags& f1,
                                         int (&as0)[MAX_TM], int (&as1)[MAX_TM], Epi& es,
                                         v16f (&accp)[MAX_TM][4]) {
@@ -533,15 +653,20 @@ __device__ __forceinline__ void k_block(Ctx& c, v16f (&acc)[MAX_TM][4], Frags& f
   __builtin_amdgcn_sched_barrier(0);
   // in a chunk's first tile the prologue copied blocks 0 and 1 whole and block 2's first part
   constexpr int J2 = J + 2;
-  half_step<NTM, ST, 1, false, PART1, NCOPY, J2 % NST, (J2 >= NKB), J2 % NKB, 2 * J, NTMP, false>(
+  half_step<ROLE, NTM, ST, 1, false, PART1, NCOPY, J2 % NST, (J2 >= NKB), J2 % NKB, 2 * J, NTMP, false>(
       c, acc, f0, as, ws, ws4, f1, as1, es, accp);
-  __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);
-  __builtin_amdgcn_s_waitcnt(WAITCNT_VM13);
+  if constexpr (ROLE != ROLE_EPI) __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);
+  if constexpr (ROLE == ROLE_ALL) __builtin_amdgcn_s_waitcnt(WAITCNT_VM13);
+  if constexpr (ROLE == ROLE_MFMA) __builtin_amdgcn_s_waitcnt(J == 0 ? waitcnt_vm(PART1 + ACOPIES) : waitcnt_vm(ACOPIES));
+  if constexpr (ROLE == ROLE_EPI)
+    __builtin_amdgcn_s_waitcnt(J == 0 ? waitcnt_vm(NCOPY - PART1 - ACOPIES) : waitcnt_vm(NCOPY - ACOPIES));
   block_barrier();   // all of block j read by every wave; block j+1 has landed
   __builtin_amdgcn_sched_barrier(0);
   constexpr int J3 = J + 3;
-  half_step<NTM, (J + 1) % NST, 0, true, 0, PART1, ST, (J3 >= NKB), J3 % NKB, 2 * J + 1, NTMP, J == NKB - 1>(
-      c, acc, f1, as, ws, ws4, f0, as1, es, accp);
+  // the split MFMA role reads no operands of the following tile (another group computes it)
+  constexpr int RKH_B = (ROLE == ROLE_MFMA && J == NKB - 1) ? -1 : 0;
+  half_step<ROLE, NTM, (J + 1) % NST, RKH_B, true, 0, PART1, ST, (J3 >= NKB), J3 % NKB, 2 * J + 1, NTMP,
+            ROLE == ROLE_ALL && J == NKB - 1>(c, acc, f1, as, ws, ws4, f0, as1, es, accp);
 #pragma unroll
   for (int tm = 0; tm < MAX_TM; ++tm) as0[tm] = as1[tm];
   (void)FIRST;
@@ -555,34 +680,68 @@ __device__ __forceinline__ void k_block(Ctx& c, v16f (&acc)[MAX_TM][4], Frags& f
 // of 2) are in flight or landed; on exit the same holds for the next tile.
 // The epilogue fetches the RoPE rows of its next sub-tile itself; with no
 // epilogue running, this tile's first ones are fetched after block 9.
-template <int NTM, int NTMP>
+// Split roles: the MFMA role starts by reading block 0's first half (it
+// landed before the previous tile's last barrier) and its sums stay in acc;
+// the epilogue role runs the epilogue of accp (this wave's previous tile),
+// fetching its first sub-tile's RoPE rows as it starts.
+template <int ROLE, int NTM, int NTMP>
 __device__ __forceinline__ void k_loop(Ctx& c, v16f (&acc)[MAX_TM][4], Frags& f0, Frags& f1,
                                        int (&as0)[MAX_TM], int (&as1)[MAX_TM], Epi& es,
                                        v16f (&accp)[MAX_TM][4]) {
+  if constexpr (ROLE != ROLE_EPI) {
 #pragma unroll
-  for (int tm = 0; tm < MAX_TM; ++tm)
+    for (int tm = 0; tm < MAX_TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[tm][tn][r] = 0.f;
+  }
+  if constexpr (ROLE == ROLE_MFMA) {
+#pragma unroll
+    for (int tm = 0; tm < MAX_TM; ++tm) as0[tm] = c.read_scale<0>(tm);
+#pragma unroll
+    for (int tm = 0; tm < MAX_TM; ++tm)
+      f0.a[tm] = make_v8i(c.read16<0>(true, 0, 0, TM_STRIDE * tm), c.read16<0>(true, 0, 1, TM_STRIDE * tm));
 #pragma unroll
     for (int tn = 0; tn < 4; ++tn)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[tm][tn][r] = 0.f;
-#define IQP_KB(J) k_block<NTM, J, NTMP, false>(c, acc, f0, f1, as0, as1, es, accp);
+      f0.w[tn] = make_v8i(c.read16<0>(false, 0, 0, 32 * tn), c.read16<0>(false, 0, 1, 32 * tn));
+  }
+  if constexpr (ROLE == ROLE_EPI && NTMP > 0) es.rope = load_rope<VAR_IL>(es.npos0, c.half, c.p);
+#define IQP_KB(J) k_block<ROLE, NTM, J, NTMP, false>(c, acc, f0, f1, as0, as1, es, accp);
   IQP_KB(0) IQP_KB(1) IQP_KB(2) IQP_KB(3) IQP_KB(4) IQP_KB(5) IQP_KB(6) IQP_KB(7) IQP_KB(8) IQP_KB(9)
-  if constexpr (NTMP == 0) es.rope = load_rope<VAR_IL>(es.npos0, c.half, c.p);
+  if constexpr (ROLE == ROLE_ALL && NTMP == 0) es.rope = load_rope<VAR_IL>(es.npos0, c.half, c.p);
   IQP_KB(10) IQP_KB(11)
 #undef IQP_KB
   // every MFMA of the tile completes here
+  if constexpr (ROLE == ROLE_ALL) {
 #pragma unroll
-  for (int tm = 0; tm < NTM; ++tm)
+    for (int tm = 0; tm < NTM; ++tm)
 #pragma unroll
-    for (int tn = 0; tn < 4; ++tn) asm volatile("" : "+a"(accp[tm][tn]));
+      for (int tn = 0; tn < 4; ++tn) asm volatile("" : "+a"(accp[tm][tn]));
+  }
+  if constexpr (ROLE == ROLE_MFMA) {
+#pragma unroll
+    for (int tm = 0; tm < NTM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < 4; ++tn) asm volatile("" : "+a"(acc[tm][tn]));
+  }
 }
 
 // Before a tile's K loop: fetch its positions (the K loop fetches RoPE rows
 // from them near its end). After it: the tile becomes the epilogue's.
 __device__ __forceinline__ void tile_positions(Ctx& c, Epi& es, int64_t tbase) {
   const int64_t tl = tbase + 32 * c.th + (fresh(c.lane) & 31);
-  es.npos0 = load_position(tl, c.p);
-  es.npos1 = load_position(tl + TM_STRIDE, c.p);
+  if constexpr (SPLIT) {
+    // clamped into [0, max_pos) once, here (max_pos < 2^31: the launcher checks)
+    auto clamp = [&](int64_t v) __attribute__((always_inline)) {
+      return (int32_t)(v < 0 ? 0 : (v >= c.p.max_pos ? c.p.max_pos - 1 : v));
+    };
+    es.npos0 = clamp(load_position(tl, c.p));
+    es.npos1 = clamp(load_position(tl + TM_STRIDE, c.p));
+  } else {
+    es.npos0 = load_position(tl, c.p);
+    es.npos1 = load_position(tl + TM_STRIDE, c.p);
+  }
 }
 
 __device__ __forceinline__ void hand_over(Ctx& c, Epi& es, int64_t tbase) {
@@ -621,35 +780,38 @@ void IQP_PIPE_KERNEL(IndexerQArgs p) {
   auto tbase_of = [&](int64_t tile) __attribute__((always_inline)) { return TOKS * tile; };
 
   // prologue: blocks 0 and 1 of the first tile whole, block 2's first part
+  // (split build: by the first tile's MFMA group, the one whose epilogue role
+  // would have copied them)
   c.buffers(tbase_of(t_begin), c.ra, c.rs);
   c.buffers(t_begin + 1 < t_end ? tbase_of(t_begin + 1) : p.M, c.ra_n, c.rs_n);
-  static_for<0, NCOPY>([&](auto w) __attribute__((always_inline)) { c.template copy<0, false, decltype(w)::value, 0>(); });
-  static_for<0, NCOPY>([&](auto w) __attribute__((always_inline)) { c.template copy<1, false, decltype(w)::value, 1>(); });
-  static_for<0, PART1>([&](auto w) __attribute__((always_inline)) { c.template copy<2, false, decltype(w)::value, 2>(); });
-  // block 0 has landed once only blocks 1 and 2's copies may be outstanding
-  __builtin_amdgcn_s_waitcnt((((NCOPY + PART1) & 15) | (7 << 4) | (15 << 8) | (((NCOPY + PART1) >> 4) << 14)));
+  if (!SPLIT || ((int)threadIdx.x >> 8) == 0) {
+    static_for<0, NCOPY>([&](auto w) __attribute__((always_inline)) { c.template copy<0, false, decltype(w)::value, 0>(); });
+    static_for<0, NCOPY>([&](auto w) __attribute__((always_inline)) { c.template copy<1, false, decltype(w)::value, 1>(); });
+    static_for<0, PART1>([&](auto w) __attribute__((always_inline)) { c.template copy<2, false, decltype(w)::value, 2>(); });
+    // block 0 has landed once only blocks 1 and 2's copies may be outstanding
+    __builtin_amdgcn_s_waitcnt((((NCOPY + PART1) & 15) | (7 << 4) | (15 << 8) | (((NCOPY + PART1) >> 4) << 14)));
+  }
   block_barrier();
 
   Frags f0, f1;
   int as0[MAX_TM] = {}, as1[MAX_TM] = {};
   Epi es;
-  v16f acc[MAX_TM][4], accp[MAX_TM][4];
+  v16f acc[MAX_TM][4], accp[MAX_TM][4];   // the split build uses acc only
+  if constexpr (!SPLIT) {
 #pragma unroll
-  for (int tm = 0; tm < MAX_TM; ++tm) as0[tm] = c.read_scale<0>(tm);
+    for (int tm = 0; tm < MAX_TM; ++tm) as0[tm] = c.read_scale<0>(tm);
 #pragma unroll
-  for (int tm = 0; tm < MAX_TM; ++tm)
-    f0.a[tm] = make_v8i(c.read16<0>(true, 0, 0, TM_STRIDE * tm), c.read16<0>(true, 0, 1, TM_STRIDE * tm));
+    for (int tm = 0; tm < MAX_TM; ++tm)
+      f0.a[tm] = make_v8i(c.read16<0>(true, 0, 0, TM_STRIDE * tm), c.read16<0>(true, 0, 1, TM_STRIDE * tm));
 #pragma unroll
-  for (int tn = 0; tn < 4; ++tn)
-    f0.w[tn] = make_v8i(c.read16<0>(false, 0, 0, 32 * tn), c.read16<0>(false, 0, 1, 32 * tn));
+    for (int tn = 0; tn < 4; ++tn)
+      f0.w[tn] = make_v8i(c.read16<0>(false, 0, 0, 32 * tn), c.read16<0>(false, 0, 1, 32 * tn));
+  }
 
   // Every tile is computed whole (4 sub-tiles; past M the copies read zeros
   // and nothing is stored), so the steady loop is one code path.
   int64_t tile = t_begin;
-  auto one_tile = [&](auto ntmp_c) __attribute__((always_inline)) {
-    tile_positions(c, es, tbase_of(tile));
-    k_loop<MAX_TM, decltype(ntmp_c)::value>(c, acc, f0, f1, as0, as1, es, accp);
-    hand_over(c, es, tbase_of(tile));
+  auto advance = [&]() __attribute__((always_inline)) {
     // the copy buffers move to the next tile; the one after it streams in
     // during the next tile's last blocks
     c.ra = c.ra_n;
@@ -657,18 +819,59 @@ void IQP_PIPE_KERNEL(IndexerQArgs p) {
     c.buffers(tile + 2 < t_end ? tbase_of(tile + 2) : p.M, c.ra_n, c.rs_n);
     ++tile;
   };
-  one_tile(std::integral_constant<int, 0>{});
-  while (tile < t_end) one_tile(std::integral_constant<int, MAX_TM>{});
-  epilogue_alone<MAX_TM>(es, accp, c);
+  if constexpr (!SPLIT) {
+    auto one_tile = [&](auto ntmp_c) __attribute__((always_inline)) {
+      tile_positions(c, es, tbase_of(tile));
+      k_loop<ROLE_ALL, MAX_TM, decltype(ntmp_c)::value>(c, acc, f0, f1, as0, as1, es, accp);
+      hand_over(c, es, tbase_of(tile));
+      advance();
+    };
+    one_tile(std::integral_constant<int, 0>{});
+    while (tile < t_end) one_tile(std::integral_constant<int, MAX_TM>{});
+    epilogue_alone<MAX_TM>(es, accp, c);
+  } else {
+    // Tile i is computed by group i % 2 while the other group runs the
+    // epilogue of its own previous tile (none before the first) and copies.
+    // Each iteration below is one group's K loop followed by its epilogue
+    // role on the next tile (or, after the chunk's last tile, its epilogue
+    // alone), so no accumulator is carried from one iteration to the next.
+    const int group = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) >> 2;
+    if (group == 1) {
+      c.copy_offsets(fresh(c.lane));
+      k_loop<ROLE_EPI, MAX_TM, 0>(c, acc, f0, f1, as0, as1, es, acc);
+      advance();
+    }
+    while (tile < t_end) {
+      c.read_bases(fresh(c.lane));
+      tile_positions(c, es, tbase_of(tile));
+      k_loop<ROLE_MFMA, MAX_TM, 0>(c, acc, f0, f1, as0, as1, es, acc);
+      hand_over(c, es, tbase_of(tile));
+      advance();
+      if (tile < t_end) {
+        c.copy_offsets(fresh(c.lane));
+        k_loop<ROLE_EPI, MAX_TM, MAX_TM>(c, acc, f0, f1, as0, as1, es, acc);
+        advance();
+      } else {
+        es.rope = load_rope<VAR_IL>(es.npos0, c.half, c.p);
+        epilogue_alone<MAX_TM>(es, acc, c);
+      }
+    }
+  }
   __builtin_amdgcn_s_waitcnt(WAITCNT_VM0);   // no LDS copy may outlive the workgroup
 }
 
 }  // namespace
 
-#if IQP_PIPE_VARIANT == 0
+#if IQP_PIPE_VARIANT == 0 && !IQP_PIPE_SPLIT
 // token indices are held in 32-bit registers
 bool indexer_q_pipe_supported(const IndexerQArgs& a) {
   return a.nkb == pipe::NKB && a.M <= 0x7FFFFFFF - 2 * pipe::TOKS;
+}
+#endif
+#if IQP_PIPE_VARIANT == 0 && IQP_PIPE_SPLIT
+// as the pipelined kernel, with table positions held in 32-bit registers
+bool indexer_q_split_supported(const IndexerQArgs& a) {
+  return a.nkb == pipe::NKB && a.M <= 0x7FFFFFFF - 2 * pipe::TOKS && a.max_pos <= 0x7FFFFFFF;
 }
 #endif
 

@@ -58,6 +58,11 @@ hipError_t launch_indexer_q_pipe_v5(const IndexerQArgs& args, hipStream_t stream
 hipError_t launch_indexer_q_pipe_v6(const IndexerQArgs& args, hipStream_t stream);
 hipError_t launch_indexer_q_pipe_v7(const IndexerQArgs& args, hipStream_t stream);
 
+// the split-role build of the pipelined kernel (indexer_q_split.hip): the
+// pipelined kernel's shapes and arguments, table positions below 2^31
+bool indexer_q_split_supported(const IndexerQArgs& args);
+hipError_t launch_indexer_q_split(const IndexerQArgs& args, hipStream_t stream);
+
 // the small-batch FP4-output kernel (indexer_q_small.hip): K = 1536, 1 to 256
 // tokens, weight scales 4-byte aligned
 bool indexer_q_small_supported(const IndexerQArgs& args);

@@ -173,6 +173,24 @@ def test_fused_chain_uneven_tile_chunks(gpu_lib, weights, table, M):
     assert rep["ok"], rep
 
 
+@pytest.mark.parametrize("M,H,max_pos", [(1023, 64, 4096), (1024, 64, 4096), (1300, 3, 131072),
+                                         (1100, 1, 4096), (2100, 8, 131072), (1500, 64, 131072)])
+def test_fused_chain_split_build(gpu_lib, table, M, H, max_pos):
+    """Token counts on both sides of the switch to the split-role build of the
+    pipelined kernel (1024 tokens), odd and single head counts (a head pair
+    with no second head), positions up to 131071; every token checked."""
+    codes, sb = weights_for_heads(H)
+    g = S.rng("indexer_q_m128", 1200 + M)
+    x = S.activations_outlier(g, M, 1536)
+    pos = S.positions_uniform(g, M, max_pos)
+    pos[0], pos[-1] = 0, max_pos - 1
+    _, _, q, s = device_chain(gpu_lib, x, codes.cuda(), sb.cuda(), pos, table[max_pos], n_heads=H)
+    ref = oracle_chain_from_x(x, codes, sb, pos, H)
+    rep = C.check_fp4(q, s, ref["z"], ref["q_fp4"], ref["q_scales"])
+    print(f"M={M} H={H}", rep)
+    assert rep["ok"], rep
+
+
 def _sampled_check(iqp, weights, x, pos, cs, n_sample, seed):
     codes, sb, wd, wsd = weights
     _, _, q, s = device_chain(iqp, x, wd, wsd, pos, cs)
