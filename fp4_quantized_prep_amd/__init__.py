@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libiqprep.s
 
 __all__ = [
     "IqpError", "fp8_quant_1x128_ue8m0", "indexer_q_gemm_rope_fp4", "rope_cos_sin_table",
-    "debug_indexer_q_f32", "indexer_q_rope_hadamard_fp4", "indexer_q_prep_bf16", "indexer_q_prep", "fp8_quant_weight_128x128_ue8m0", "abi_version", "library_path",
+    "debug_indexer_q_f32", "debug_indexer_q_prep_bf16_f32", "debug_indexer_q_clock", "device_clock_rates",
+    "indexer_q_rope_hadamard_fp4", "indexer_q_prep_bf16", "indexer_q_prep", "fp8_quant_weight_128x128_ue8m0", "abi_version", "library_path",
     "IQP_OK", "IQP_ERR_INVALID", "IQP_ERR_UNSUPPORTED", "IQP_ERR_HIP", "ONE_LAUNCH_MAX_TOKENS",
     "IQP_ROPE_INTERLEAVED", "IQP_FP4_SCALE_OCP_FLOOR", "IQP_W_SCALES_PER_ROW",
 ]
@@ -71,6 +72,12 @@ def _load():
     lib.iqp_status_string.restype = ctypes.c_char_p
     lib.iqp_abi_version.argtypes = []
     lib.iqp_abi_version.restype = ctypes.c_int
+    lib.iqp_debug_indexer_q_prep_bf16_f32.argtypes = lib.indexer_q_prep_bf16.argtypes[:-3] + [c_p, c_p]
+    lib.iqp_debug_indexer_q_prep_bf16_f32.restype = ctypes.c_int
+    lib.iqp_debug_indexer_q_clock.argtypes = iq_args + [c_p, c_p, c_p, c_i64, c_p, c_p]
+    lib.iqp_debug_indexer_q_clock.restype = ctypes.c_int
+    lib.iqp_device_clock_rates.argtypes = [c_p, c_p]
+    lib.iqp_device_clock_rates.restype = ctypes.c_int
     return lib
 
 
@@ -288,7 +295,9 @@ def indexer_q_gemm_rope_fp4(a, a_scales, w, w_scales, positions, cos_sin, n_head
 def debug_indexer_q_f32(a, a_scales, w, w_scales, positions, cos_sin, stage: int, n_heads: int = 64,
                         head_dim: int = 128, rope_dim: int = 64, out=None, stream=None):
     """float32 [M, H*128] after stage 0 (GEMM), 1 (RoPE) or 2 (Hadamard) of the
-    fused kernel, for stage-wise parity checks."""
+    general fused kernel, or the GEMM output (stage 3) of the kernel that
+    :func:`indexer_q_gemm_rope_fp4` runs for these arguments, for stage-wise
+    parity checks."""
     a, args = _indexer_q_common(a, a_scales, w, w_scales, positions, cos_sin, n_heads, head_dim, rope_dim)
     M = a.shape[0]
     if out is None:
@@ -369,6 +378,30 @@ def indexer_q_prep_bf16(x, w, w_scales, positions, cos_sin, n_heads: int = 64, h
         raise ValueError("w_scale_layout must be 'tile_128x128' or 'row_1x128'")
     rows = w_scale_layout == "row_1x128"
     flags = _convention_flags(rope_layout, scale_rule) | (IQP_W_SCALES_PER_ROW if rows else 0)
+    args = _prep_bf16_common(x, w, w_scales, positions, cos_sin, n_heads, head_dim, rope_dim, rows)
+    M, dev = x.shape[0], x.device
+    if q_fp4 is None:
+        q_fp4 = torch.empty((M, n_heads, head_dim // 2), dtype=torch.uint8, device=dev)
+    if q_scales is None:
+        q_scales = torch.empty((M, n_heads, head_dim // 32), dtype=torch.uint8, device=dev)
+    _require(q_fp4, "q_fp4", torch.uint8, dev, 3)
+    _require(q_scales, "q_scales", torch.uint8, dev, 3)
+    if not (q_fp4.is_contiguous() and q_scales.is_contiguous()):
+        raise ValueError("q_fp4 and q_scales must be contiguous")
+    if tuple(q_fp4.shape) != (M, n_heads, head_dim // 2) or tuple(q_scales.shape) != (M, n_heads, head_dim // 32):
+        raise ValueError("q_fp4 / q_scales have the wrong shape")
+    args += [_ptr(q_fp4), _ptr(q_scales)]
+    if flags == 0:
+        st = _lib.indexer_q_prep_bf16(*args, _stream(x, stream))
+        _check(st, "indexer_q_prep_bf16")
+    else:
+        st = _lib.indexer_q_prep_bf16_ex(*args, flags, _stream(x, stream))
+        _check(st, "indexer_q_prep_bf16_ex")
+    return q_fp4, q_scales
+
+
+def _prep_bf16_common(x, w, w_scales, positions, cos_sin, n_heads, head_dim, rope_dim, w_scale_rows):
+    """Checks of the one-launch call's inputs; its C arguments up to max_pos."""
     w = _bytes_u8(w)
     dev = x.device
     _require(x, "x", torch.bfloat16, dev, 2)
@@ -382,32 +415,71 @@ def indexer_q_prep_bf16(x, w, w_scales, positions, cos_sin, n_heads: int = 64, h
     M, K = x.shape
     if w.shape[1] != K or w.shape[0] != n_heads * head_dim:
         raise ValueError(f"w must be [{n_heads * head_dim}, {K}], got {tuple(w.shape)}")
-    ws_rows = n_heads * head_dim if rows else n_heads * head_dim // 128
+    ws_rows = n_heads * head_dim if w_scale_rows else n_heads * head_dim // 128
     if tuple(w_scales.shape) != (ws_rows, K // 128):
         raise ValueError(f"w_scales must be [{ws_rows}, {K // 128}]")
     if positions.shape[0] != M:
         raise ValueError("positions needs one entry per token")
     if cos_sin.shape[1] != rope_dim:
         raise ValueError(f"cos_sin must have {rope_dim} columns")
+    return [_ptr(x), x.stride(0), _ptr(w), w.stride(0), _ptr(w_scales), M, K, n_heads, head_dim, rope_dim,
+            _ptr(positions), _ptr(cos_sin), cos_sin.shape[0]]
+
+
+@_on_stream
+def debug_indexer_q_prep_bf16_f32(x, w, w_scales, positions, cos_sin, n_heads: int = 64, head_dim: int = 128,
+                                  rope_dim: int = 64, out=None, stream=None):
+    """float32 [M, H*128]: the GEMM output of the one-launch kernel of
+    :func:`indexer_q_prep_bf16` (its own FP8 quantization of x included)."""
+    args = _prep_bf16_common(x, w, w_scales, positions, cos_sin, n_heads, head_dim, rope_dim, False)
+    M = x.shape[0]
+    if out is None:
+        out = torch.empty((M, n_heads * head_dim), dtype=torch.float32, device=x.device)
+    _require(out, "out", torch.float32, x.device, 2)
+    if not out.is_contiguous() or tuple(out.shape) != (M, n_heads * head_dim):
+        raise ValueError("out must be a contiguous [M, H*128] float32 tensor")
+    st = _lib.iqp_debug_indexer_q_prep_bf16_f32(*args, _ptr(out), _stream(x, stream))
+    _check(st, "iqp_debug_indexer_q_prep_bf16_f32")
+    return out
+
+
+@_on_stream
+def debug_indexer_q_clock(a, a_scales, w, w_scales, positions, cos_sin, n_heads: int = 64, head_dim: int = 128,
+                          rope_dim: int = 64, q_fp4=None, q_scales=None, stamps=None, stream=None):
+    """:func:`indexer_q_gemm_rope_fp4` from the clock-stamp build of its
+    split-role kernel. Returns ``(q_fp4, q_scales, stamps)`` with stamps an
+    int64 [workgroups, 4] device tensor (shader clock counter at start, end;
+    constant-rate counter at start, end; all 0 for a workgroup with no
+    tokens). Raises IqpError (IQP_ERR_UNSUPPORTED) where the call would not
+    run the split-role kernel."""
+    a, args = _indexer_q_common(a, a_scales, w, w_scales, positions, cos_sin, n_heads, head_dim, rope_dim)
+    M, dev = a.shape[0], a.device
     if q_fp4 is None:
         q_fp4 = torch.empty((M, n_heads, head_dim // 2), dtype=torch.uint8, device=dev)
     if q_scales is None:
         q_scales = torch.empty((M, n_heads, head_dim // 32), dtype=torch.uint8, device=dev)
     _require(q_fp4, "q_fp4", torch.uint8, dev, 3)
     _require(q_scales, "q_scales", torch.uint8, dev, 3)
-    if not (q_fp4.is_contiguous() and q_scales.is_contiguous()):
-        raise ValueError("q_fp4 and q_scales must be contiguous")
-    if tuple(q_fp4.shape) != (M, n_heads, head_dim // 2) or tuple(q_scales.shape) != (M, n_heads, head_dim // 32):
-        raise ValueError("q_fp4 / q_scales have the wrong shape")
-    args = [_ptr(x), x.stride(0), _ptr(w), w.stride(0), _ptr(w_scales), M, K, n_heads, head_dim, rope_dim,
-            _ptr(positions), _ptr(cos_sin), cos_sin.shape[0], _ptr(q_fp4), _ptr(q_scales)]
-    if flags == 0:
-        st = _lib.indexer_q_prep_bf16(*args, _stream(x, stream))
-        _check(st, "indexer_q_prep_bf16")
-    else:
-        st = _lib.indexer_q_prep_bf16_ex(*args, flags, _stream(x, stream))
-        _check(st, "indexer_q_prep_bf16_ex")
-    return q_fp4, q_scales
+    if not (q_fp4.is_contiguous() and q_scales.is_contiguous()) or \
+            tuple(q_fp4.shape) != (M, n_heads, head_dim // 2) or tuple(q_scales.shape) != (M, n_heads, head_dim // 32):
+        raise ValueError("q_fp4 / q_scales must be contiguous [M, H, 64] / [M, H, 4]")
+    if stamps is None:
+        stamps = torch.empty((4 * 4096,), dtype=torch.int64, device=dev)
+    _require(stamps, "stamps", torch.int64, dev, 1)
+    if not stamps.is_contiguous():
+        raise ValueError("stamps must be contiguous")
+    nwg = ctypes.c_int64(0)
+    st = _lib.iqp_debug_indexer_q_clock(*args, _ptr(q_fp4), _ptr(q_scales), _ptr(stamps), stamps.numel(),
+                                        ctypes.byref(nwg), _stream(a, stream))
+    _check(st, "iqp_debug_indexer_q_clock")
+    return q_fp4, q_scales, stamps[: 4 * nwg.value].view(nwg.value, 4)
+
+
+def device_clock_rates():
+    """(constant-rate counter Hz, peak shader clock Hz) of the current device."""
+    wall, sclk = ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(_lib.iqp_device_clock_rates(ctypes.byref(wall), ctypes.byref(sclk)), "iqp_device_clock_rates")
+    return wall.value, sclk.value
 
 
 @_on_stream

@@ -93,6 +93,41 @@ iqp::IndexerQArgs make_args(const void* a, int64_t lda, const int32_t* a_scales,
   return p;
 }
 
+// Checks of the one-launch call and its diagnostic twin (outputs: 16-byte
+// aligned out0, 4-byte aligned out1); fills p on success (M == 0: IQP_OK,
+// nothing filled).
+int prep_bf16_args(const void* x, int64_t ldx, const void* w, int64_t ldw, const uint8_t* w_scales,
+                   int64_t M, int64_t K, int32_t H, int32_t D, int32_t rope_dim,
+                   const int64_t* positions, const float* cos_sin, int64_t max_pos,
+                   const void* out0, const void* out1, iqp::IndexerQArgs& p) {
+  if (M < 0 || K < 0 || H < 0 || D < 0 || rope_dim < 0 || max_pos < 0) return IQP_ERR_INVALID;
+  if (M == 0) return IQP_OK;
+  if (!x || !w || !w_scales || !positions || !cos_sin || !out0 || !out1) return IQP_ERR_INVALID;
+  if (K == 0 || H == 0 || max_pos == 0) return IQP_ERR_INVALID;
+  if (ldx < K || ldw < K) return IQP_ERR_INVALID;
+  if (K != 1536 || M > 256 || D != 128 || rope_dim != 64) return IQP_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || ldx % 8 || !aligned(w, 16) || ldw % 16 || !aligned(w_scales, 4) ||
+      !aligned(positions, 8) || !aligned(cos_sin, 16) || !aligned(out0, 16) || !aligned(out1, 4))
+    return IQP_ERR_UNSUPPORTED;
+  if ((int64_t)H * 128 > ((int64_t)1 << 31) || H > 65535 || ldw >= ((int64_t)1 << 22))
+    return IQP_ERR_UNSUPPORTED;
+  const int st = device_status();
+  if (st != IQP_OK) return st;
+  p.x = static_cast<const uint16_t*>(x);
+  p.ldx = ldx;
+  p.w = static_cast<const uint8_t*>(w);
+  p.ldw = ldw;
+  p.w_scales = w_scales;
+  p.M = M;
+  p.nkb = (int32_t)(K / 128);
+  p.H = H;
+  p.positions = positions;
+  p.cos_sin = cos_sin;
+  p.max_pos = max_pos;
+  if (!iqp::indexer_q_small_bf16_supported(p)) return IQP_ERR_UNSUPPORTED;
+  return IQP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -156,35 +191,25 @@ int indexer_q_prep_bf16_ex(const void* x, int64_t ldx, const void* w, int64_t ld
                            const int64_t* positions, const float* cos_sin, int64_t max_pos,
                            uint8_t* q_fp4, uint8_t* q_scales, int32_t flags, void* stream) {
   if (flags & ~(IQP_ROPE_INTERLEAVED | IQP_FP4_SCALE_OCP_FLOOR | IQP_W_SCALES_PER_ROW)) return IQP_ERR_INVALID;
-  if (M < 0 || K < 0 || H < 0 || D < 0 || rope_dim < 0 || max_pos < 0) return IQP_ERR_INVALID;
-  if (M == 0) return IQP_OK;
-  if (!x || !w || !w_scales || !positions || !cos_sin || !q_fp4 || !q_scales) return IQP_ERR_INVALID;
-  if (K == 0 || H == 0 || max_pos == 0) return IQP_ERR_INVALID;
-  if (ldx < K || ldw < K) return IQP_ERR_INVALID;
-  if (K != 1536 || M > 256 || D != 128 || rope_dim != 64) return IQP_ERR_UNSUPPORTED;
-  if (!aligned(x, 16) || ldx % 8 || !aligned(w, 16) || ldw % 16 || !aligned(w_scales, 4) ||
-      !aligned(positions, 8) || !aligned(cos_sin, 16) || !aligned(q_fp4, 16) || !aligned(q_scales, 4))
-    return IQP_ERR_UNSUPPORTED;
-  if ((int64_t)H * 128 > ((int64_t)1 << 31) || H > 65535 || ldw >= ((int64_t)1 << 22))
-    return IQP_ERR_UNSUPPORTED;
-  const int st = device_status();
-  if (st != IQP_OK) return st;
   iqp::IndexerQArgs p{};
-  p.x = static_cast<const uint16_t*>(x);
-  p.ldx = ldx;
-  p.w = static_cast<const uint8_t*>(w);
-  p.ldw = ldw;
-  p.w_scales = w_scales;
-  p.M = M;
-  p.nkb = (int32_t)(K / 128);
-  p.H = H;
-  p.positions = positions;
-  p.cos_sin = cos_sin;
-  p.max_pos = max_pos;
+  const int st = prep_bf16_args(x, ldx, w, ldw, w_scales, M, K, H, D, rope_dim, positions, cos_sin, max_pos,
+                                q_fp4, q_scales, p);
+  if (st != IQP_OK || M == 0) return st;
   p.q_fp4 = q_fp4;
   p.q_scales = q_scales;
-  if (!iqp::indexer_q_small_bf16_supported(p)) return IQP_ERR_UNSUPPORTED;
   return from_hip(iqp::launch_indexer_q_small_bf16_variant(p, flags, static_cast<hipStream_t>(stream)));
+}
+
+int iqp_debug_indexer_q_prep_bf16_f32(const void* x, int64_t ldx, const void* w, int64_t ldw,
+                                      const uint8_t* w_scales, int64_t M, int64_t K, int32_t H, int32_t D,
+                                      int32_t rope_dim, const int64_t* positions, const float* cos_sin,
+                                      int64_t max_pos, float* out, void* stream) {
+  iqp::IndexerQArgs p{};
+  const int st = prep_bf16_args(x, ldx, w, ldw, w_scales, M, K, H, D, rope_dim, positions, cos_sin, max_pos,
+                                out, out, p);
+  if (st != IQP_OK || M == 0) return st;
+  p.dbg = out;
+  return from_hip(iqp::launch_indexer_q_small_dump(p, static_cast<hipStream_t>(stream)));
 }
 
 int iqp_debug_indexer_q_f32(const void* a, int64_t lda, const int32_t* a_scales, int64_t as_stride_m,
@@ -192,7 +217,7 @@ int iqp_debug_indexer_q_f32(const void* a, int64_t lda, const int32_t* a_scales,
                             int64_t M, int64_t K, int32_t H, int32_t D, int32_t rope_dim,
                             const int64_t* positions, const float* cos_sin, int64_t max_pos,
                             float* out, int32_t stage, void* stream) {
-  if (stage < 0 || stage > 2) return IQP_ERR_INVALID;
+  if (stage < 0 || stage > 3) return IQP_ERR_INVALID;
   int st = check_indexer_q_args(a, lda, a_scales, as_stride_m, as_stride_w, w, ldw, w_scales, M, K,
                                 H, D, rope_dim, positions, cos_sin, max_pos, out, out);
   if (st != IQP_OK || M == 0) return st;
@@ -202,7 +227,48 @@ int iqp_debug_indexer_q_f32(const void* a, int64_t lda, const int32_t* a_scales,
   iqp::IndexerQArgs p = make_args(a, lda, a_scales, as_stride_m, as_stride_w, w, ldw, w_scales, M,
                                   K, H, positions, cos_sin, max_pos);
   p.dbg = out;
+  if (stage == 3) return from_hip(iqp::launch_indexer_q_gemm_dump(p, static_cast<hipStream_t>(stream)));
   return from_hip(iqp::launch_indexer_q(p, stage, static_cast<hipStream_t>(stream)));
+}
+
+int iqp_debug_indexer_q_clock(const void* a, int64_t lda, const int32_t* a_scales, int64_t as_stride_m,
+                              int64_t as_stride_w, const void* w, int64_t ldw, const uint8_t* w_scales,
+                              int64_t M, int64_t K, int32_t H, int32_t D, int32_t rope_dim,
+                              const int64_t* positions, const float* cos_sin, int64_t max_pos,
+                              uint8_t* q_fp4, uint8_t* q_scales, uint64_t* stamps, int64_t stamp_capacity,
+                              int64_t* n_workgroups, void* stream) {
+  if (!n_workgroups) return IQP_ERR_INVALID;
+  *n_workgroups = 0;
+  if (stamp_capacity < 0) return IQP_ERR_INVALID;
+  int st = check_indexer_q_args(a, lda, a_scales, as_stride_m, as_stride_w, w, ldw, w_scales, M, K,
+                                H, D, rope_dim, positions, cos_sin, max_pos, q_fp4, q_scales);
+  if (st != IQP_OK) return st;
+  if (M == 0) return IQP_ERR_UNSUPPORTED;
+  if (!stamps) return IQP_ERR_INVALID;
+  if (!aligned(q_fp4, 16) || !aligned(q_scales, 4) || !aligned(stamps, 16)) return IQP_ERR_UNSUPPORTED;
+  st = device_status();
+  if (st != IQP_OK) return st;
+  iqp::IndexerQArgs p = make_args(a, lda, a_scales, as_stride_m, as_stride_w, w, ldw, w_scales, M,
+                                  K, H, positions, cos_sin, max_pos);
+  p.q_fp4 = q_fp4;
+  p.q_scales = q_scales;
+  p.dbg = reinterpret_cast<float*>(stamps);
+  const hipError_t e = iqp::launch_indexer_q_clock(p, stamp_capacity, n_workgroups, static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported) return IQP_ERR_UNSUPPORTED;
+  if (e == hipErrorInvalidValue) return IQP_ERR_INVALID;
+  return from_hip(e);
+}
+
+int iqp_device_clock_rates(int64_t* wall_clock_hz, int64_t* peak_shader_clock_hz) {
+  if (!wall_clock_hz || !peak_shader_clock_hz) return IQP_ERR_INVALID;
+  int dev = 0, wall_khz = 0, sclk_khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess ||
+      hipDeviceGetAttribute(&sclk_khz, hipDeviceAttributeClockRate, dev) != hipSuccess)
+    return IQP_ERR_HIP;
+  *wall_clock_hz = (int64_t)wall_khz * 1000;
+  *peak_shader_clock_hz = (int64_t)sclk_khz * 1000;
+  return IQP_OK;
 }
 
 int indexer_q_rope_hadamard_fp4(const void* q, int64_t ldq, int64_t M, int32_t H, int32_t D,

@@ -532,6 +532,29 @@ static bool pipe_args(const IndexerQArgs& a_in, IndexerQArgs& a) {
   return true;
 }
 
+hipError_t launch_indexer_q_gemm_dump(const IndexerQArgs& a_in, hipStream_t stream) {
+  if (indexer_q_small_supported(a_in)) return launch_indexer_q_small_dump(a_in, stream);
+  if (indexer_q_pipe_supported(a_in)) {
+    IndexerQArgs a;
+    if (!pipe_args(a_in, a)) return hipErrorInvalidValue;
+    if (a.M >= SPLIT_MIN_TOKENS && indexer_q_split_supported(a)) return launch_indexer_q_split_dump(a, stream);
+    return launch_indexer_q_pipe_dump(a, stream);
+  }
+  return launch_kernel(a_in, 0, stream);
+}
+
+hipError_t launch_indexer_q_clock(const IndexerQArgs& a_in, int64_t stamp_capacity, int64_t* workgroups,
+                                  hipStream_t stream) {
+  *workgroups = 0;
+  if (indexer_q_small_supported(a_in) || !indexer_q_pipe_supported(a_in)) return hipErrorNotSupported;
+  IndexerQArgs a;
+  if (!pipe_args(a_in, a)) return hipErrorInvalidValue;
+  if (a.M < SPLIT_MIN_TOKENS || !indexer_q_split_supported(a)) return hipErrorNotSupported;
+  *workgroups = (int64_t)((a.H + 1) / 2) * a.chunks;
+  if (stamp_capacity < 4 * *workgroups) return hipErrorInvalidValue;
+  return launch_indexer_q_split_clock(a, stream);
+}
+
 hipError_t launch_indexer_q_small_bf16_variant(const IndexerQArgs& a, int variant, hipStream_t stream) {
   switch (variant) {
     case 0: return launch_indexer_q_small_bf16(a, stream);

@@ -68,6 +68,18 @@
 #ifndef IQP_PIPE_SPLIT
 #define IQP_PIPE_SPLIT 0
 #endif
+// Diagnostic builds (default configuration only):
+//   IQP_PIPE_DUMP 1: the same K loop, but each tile's float32 sums (Q before
+//     RoPE) are written to args.dbg [M, H*128] and no epilogue runs;
+//   IQP_PIPE_STAMP 1: the FP4 kernel unchanged, plus four 64-bit stamps per
+//     workgroup in args.dbg: s_memtime (shader clock cycles) and
+//     s_memrealtime (constant-rate counter) at its start and end.
+#ifndef IQP_PIPE_DUMP
+#define IQP_PIPE_DUMP 0
+#endif
+#ifndef IQP_PIPE_STAMP
+#define IQP_PIPE_STAMP 0
+#endif
 
 namespace iqp {
 namespace {
@@ -78,6 +90,9 @@ constexpr bool VAR_FLOOR = (IQP_PIPE_VARIANT & 2) != 0;
 constexpr bool VAR_ROWS = (IQP_PIPE_VARIANT & 4) != 0;
 
 constexpr bool SPLIT = IQP_PIPE_SPLIT != 0;
+constexpr bool DUMP = IQP_PIPE_DUMP != 0;
+constexpr bool STAMP = IQP_PIPE_STAMP != 0;
+static_assert(IQP_PIPE_VARIANT == 0 || !(DUMP || STAMP), "diagnostic builds of the default configuration only");
 constexpr int NWAVES = 4;                           // waves of one role (one per SIMD)
 constexpr int NTHREADS = (SPLIT ? 2 : 1) * NWAVES * 64;
 // the parts of a half-step a wave issues
@@ -749,6 +764,26 @@ __device__ __forceinline__ void hand_over(Ctx& c, Epi& es, int64_t tbase) {
   es.pos1 = es.npos1;
 }
 
+// Diagnostic build: a tile's float32 sums to dbg [M, H*128]. Sub-tile tm of
+// this wave holds tokens tbase + 32 th + TM_STRIDE tm + lane % 32; its
+// accumulator tn, registers 4 g .. 4 g + 3, holds dims 32 tn + 8 g + 4 half
+// + 0..3 of the head (the layout the epilogue starts from).
+__device__ __forceinline__ void dump_sums(const v16f (&s)[MAX_TM][4], const Ctx& c, int64_t tbase) {
+  if (c.head >= c.p.H) return;   // odd head count: the pair's missing head
+#pragma unroll
+  for (int tm = 0; tm < MAX_TM; ++tm) {
+    const int64_t t = tbase + 32 * c.th + TM_STRIDE * tm + (c.lane & 31);
+    if (t >= c.p.M) continue;
+    float* row = c.p.dbg + (t * c.p.H + c.head) * HEAD_DIM + 4 * c.half;
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<v4f*>(row + 32 * tn + 8 * g) =
+            v4f{s[tm][tn][4 * g], s[tm][tn][4 * g + 1], s[tm][tn][4 * g + 2], s[tm][tn][4 * g + 3]};
+  }
+}
+
 }  // namespace pipe
 
 // Workgroup = head pair x token chunk, as in indexer_q.hip.
@@ -758,6 +793,24 @@ void IQP_PIPE_KERNEL(IndexerQArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
 
   const int bid = blockIdx.x;
+  uint64_t stamp0 = 0, rstamp0 = 0;   // the clock-stamp build's start stamps
+  if constexpr (STAMP) {
+    stamp0 = __builtin_amdgcn_s_memtime();
+    rstamp0 = __builtin_amdgcn_s_memrealtime();
+  }
+  auto write_stamps = [&](bool ran) __attribute__((always_inline)) {
+    // all four by thread 0, after its own waits; zeros for a workgroup with no tiles
+    if (threadIdx.x == 0) {
+      uint64_t* st = reinterpret_cast<uint64_t*>(p.dbg) + 4 * (int64_t)bid;
+      const uint64_t t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+      *reinterpret_cast<v4u*>(st) = ran ? v4u{(uint32_t)stamp0, (uint32_t)(stamp0 >> 32), (uint32_t)t1,
+                                              (uint32_t)(t1 >> 32)}
+                                        : v4u{0, 0, 0, 0};
+      *reinterpret_cast<v4u*>(st + 2) = ran ? v4u{(uint32_t)rstamp0, (uint32_t)(rstamp0 >> 32), (uint32_t)r1,
+                                                  (uint32_t)(r1 >> 32)}
+                                            : v4u{0, 0, 0, 0};
+    }
+  };
   const int npairs = (p.H + 1) >> 1;
   const int cpp = p.chunks;
   int pair, chunk;
@@ -774,7 +827,10 @@ void IQP_PIPE_KERNEL(IndexerQArgs p) {
   const int64_t ntiles = (p.M + TOKS - 1) / TOKS;
   const int64_t t_begin = ntiles * chunk / cpp;
   const int64_t t_end = ntiles * (chunk + 1) / cpp;
-  if (t_begin >= t_end) return;   // uniform over the workgroup
+  if (t_begin >= t_end) {   // uniform over the workgroup
+    if constexpr (STAMP) write_stamps(false);
+    return;
+  }
 
   Ctx c(p, lds, pair);
   auto tbase_of = [&](int64_t tile) __attribute__((always_inline)) { return TOKS * tile; };
@@ -823,12 +879,13 @@ void IQP_PIPE_KERNEL(IndexerQArgs p) {
     auto one_tile = [&](auto ntmp_c) __attribute__((always_inline)) {
       tile_positions(c, es, tbase_of(tile));
       k_loop<ROLE_ALL, MAX_TM, decltype(ntmp_c)::value>(c, acc, f0, f1, as0, as1, es, accp);
+      if constexpr (DUMP) dump_sums(accp, c, tbase_of(tile));
       hand_over(c, es, tbase_of(tile));
       advance();
     };
     one_tile(std::integral_constant<int, 0>{});
-    while (tile < t_end) one_tile(std::integral_constant<int, MAX_TM>{});
-    epilogue_alone<MAX_TM>(es, accp, c);
+    while (tile < t_end) one_tile(std::integral_constant<int, DUMP ? 0 : MAX_TM>{});
+    if constexpr (!DUMP) epilogue_alone<MAX_TM>(es, accp, c);
   } else {
     // Tile i is computed by group i % 2 while the other group runs the
     // epilogue of its own previous tile (none before the first) and copies.
@@ -845,30 +902,35 @@ void IQP_PIPE_KERNEL(IndexerQArgs p) {
       c.read_bases(fresh(c.lane));
       tile_positions(c, es, tbase_of(tile));
       k_loop<ROLE_MFMA, MAX_TM, 0>(c, acc, f0, f1, as0, as1, es, acc);
+      if constexpr (DUMP) dump_sums(acc, c, tbase_of(tile));
       hand_over(c, es, tbase_of(tile));
       advance();
       if (tile < t_end) {
         c.copy_offsets(fresh(c.lane));
-        k_loop<ROLE_EPI, MAX_TM, MAX_TM>(c, acc, f0, f1, as0, as1, es, acc);
+        k_loop<ROLE_EPI, MAX_TM, DUMP ? 0 : MAX_TM>(c, acc, f0, f1, as0, as1, es, acc);
         advance();
-      } else {
+      } else if constexpr (!DUMP) {
         es.rope = load_rope<VAR_IL>(es.npos0, c.half, c.p);
         epilogue_alone<MAX_TM>(es, acc, c);
       }
     }
   }
   __builtin_amdgcn_s_waitcnt(WAITCNT_VM0);   // no LDS copy may outlive the workgroup
+  if constexpr (STAMP) {
+    block_barrier();   // the workgroup's last wave is done
+    write_stamps(true);
+  }
 }
 
 }  // namespace
 
-#if IQP_PIPE_VARIANT == 0 && !IQP_PIPE_SPLIT
+#if IQP_PIPE_VARIANT == 0 && !IQP_PIPE_SPLIT && !IQP_PIPE_DUMP && !IQP_PIPE_STAMP
 // token indices are held in 32-bit registers
 bool indexer_q_pipe_supported(const IndexerQArgs& a) {
   return a.nkb == pipe::NKB && a.M <= 0x7FFFFFFF - 2 * pipe::TOKS;
 }
 #endif
-#if IQP_PIPE_VARIANT == 0 && IQP_PIPE_SPLIT
+#if IQP_PIPE_VARIANT == 0 && IQP_PIPE_SPLIT && !IQP_PIPE_DUMP && !IQP_PIPE_STAMP
 // as the pipelined kernel, with table positions held in 32-bit registers
 bool indexer_q_split_supported(const IndexerQArgs& a) {
   return a.nkb == pipe::NKB && a.M <= 0x7FFFFFFF - 2 * pipe::TOKS && a.max_pos <= 0x7FFFFFFF;

@@ -104,7 +104,9 @@ __device__ __forceinline__ uint32_t a_slot(int r, int c) { return (uint32_t)(r *
 
 constexpr int XSTEPS = TILE * NKB / 32;      // one-launch variant: 32 blocks per step, up to 12 steps
 
-template <bool XIN>
+// DUMP (diagnostic build, default configuration only): the float32 GEMM
+// sums (Q before RoPE) go to pa.dbg [M, H*128] in place of the epilogue.
+template <bool XIN, bool DUMP = false>
 __global__ __launch_bounds__(NTHREADS, 1)
 void IQP_SMALL_KERNEL(IndexerQArgs pa) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
@@ -328,6 +330,18 @@ void IQP_SMALL_KERNEL(IndexerQArgs pa) {
         for (int q = 0; q < 4; ++q) v[b5][4 * h + q] = x[q];
       }
   }
+  if constexpr (DUMP) {
+    if (et < M) {
+      float* row = pa.dbg + ((t0 + et) * p.H + head) * HEAD_DIM + eoff;
+#pragma unroll
+      for (int b5 = 0; b5 < 2; ++b5)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          *reinterpret_cast<v4f*>(row + 32 * b5 + 4 * h) =
+              v4f{v[b5][4 * h], v[b5][4 * h + 1], v[b5][4 * h + 2], v[b5][4 * h + 3]};
+    }
+    return;
+  }
   // RoPE on dims 0..63 (b6 = 0): the pair (i, i + 32) is (v[0][k], v[1][k])
   if (!(sub & 4) && !VAR_IL) {
 #pragma unroll
@@ -450,6 +464,15 @@ bool indexer_q_small_bf16_supported(const IndexerQArgs& a) {
 hipError_t launch_indexer_q_small_bf16(const IndexerQArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)a.H, (unsigned)((a.M + small::TILE - 1) / small::TILE)), block(small::NTHREADS);
   hipLaunchKernelGGL(small::IQP_SMALL_KERNEL<true>, grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_indexer_q_small_dump(const IndexerQArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)a.H, (unsigned)((a.M + small::TILE - 1) / small::TILE)), block(small::NTHREADS);
+  if (a.x != nullptr)
+    hipLaunchKernelGGL((small::IQP_SMALL_KERNEL<true, true>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((small::IQP_SMALL_KERNEL<false, true>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 #else

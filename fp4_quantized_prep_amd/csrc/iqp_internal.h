@@ -35,6 +35,15 @@ hipError_t launch_fp8_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx
 
 // stage -1: FP4 output; 0, 1, 2: float32 diagnostics (see iqprep.h)
 hipError_t launch_indexer_q(const IndexerQArgs& args, int stage, hipStream_t stream);
+// the float32 GEMM sums of the kernel that launch_indexer_q(args, -1) runs
+// (its diagnostic build; the general kernel's stage 0 where that one runs)
+hipError_t launch_indexer_q_gemm_dump(const IndexerQArgs& args, hipStream_t stream);
+// launch_indexer_q(args, -1) with shader-clock stamps (args.dbg, uint64
+// [4 * workgroups]) where it runs the split-role kernel; *workgroups is set
+// first; hipErrorNotSupported where another kernel would run, and
+// hipErrorInvalidValue when stamp_capacity < 4 * workgroups (nothing launched)
+hipError_t launch_indexer_q_clock(const IndexerQArgs& args, int64_t stamp_capacity, int64_t* workgroups,
+                                  hipStream_t stream);
 // FP4 output with convention variant v (bit 0: interleaved RoPE pairs, bit 1:
 // OCP floor-rule FP4 scales, bit 2: per-row weight scales); v = 0 is
 // launch_indexer_q(args, -1, stream); otherwise the variant build of the
@@ -62,6 +71,19 @@ hipError_t launch_indexer_q_pipe_v7(const IndexerQArgs& args, hipStream_t stream
 // pipelined kernel's shapes and arguments, table positions below 2^31
 bool indexer_q_split_supported(const IndexerQArgs& args);
 hipError_t launch_indexer_q_split(const IndexerQArgs& args, hipStream_t stream);
+
+// diagnostic builds: the float32 GEMM sums (Q before RoPE) of the pipelined,
+// split-role and small-batch kernels' K loops in args.dbg [M, H*128]; the
+// pipelined and split ones take the arguments of their FP4 launchers
+// (args.chunks set); the small-batch one quantizes bf16 args.x itself when
+// that is set (the one-launch kernel), else reads args.a
+hipError_t launch_indexer_q_pipe_dump(const IndexerQArgs& args, hipStream_t stream);
+hipError_t launch_indexer_q_split_dump(const IndexerQArgs& args, hipStream_t stream);
+hipError_t launch_indexer_q_small_dump(const IndexerQArgs& args, hipStream_t stream);
+// the split-role FP4 kernel with four uint64 stamps per workgroup in args.dbg
+// (s_memtime start, end; s_memrealtime start, end; zeros for a workgroup with
+// no tiles); args.chunks set
+hipError_t launch_indexer_q_split_clock(const IndexerQArgs& args, hipStream_t stream);
 
 // the small-batch FP4-output kernel (indexer_q_small.hip): K = 1536, 1 to 256
 // tokens, weight scales 4-byte aligned

@@ -324,11 +324,18 @@ int iqp_rope_cos_sin_table(double theta, int64_t max_pos, int32_t rope_dim,
 
 /*
  * iqp_debug_indexer_q_f32 — diagnostic twin of indexer_q_gemm_rope_fp4 for
- * parity testing of its stages: same inputs and same kernel, but instead of
- * FP4 codes it writes float32 out[M, H*D] holding
+ * parity testing of its stages (TensorRT-LLM PR "Fuse DeepSeek-V4 Indexer Q
+ * projection with CuTe DSL", sequence diagram: the GEMM result feeds the
+ * RoPE / FP4 epilogue): same inputs, but instead of FP4 codes it writes
+ * float32 out[M, H*D] holding
  *   stage 0: Q (the GEMM output),
  *   stage 1: Q after RoPE,
- *   stage 2: z (after RoPE and the normalized Hadamard rotation).
+ *   stage 2: z (after RoPE and the normalized Hadamard rotation),
+ * all three from the general fused kernel (every supported shape), or
+ *   stage 3: Q from the K loop of the kernel indexer_q_gemm_rope_fp4 runs
+ *            for these arguments (the small-batch, pipelined or split-role
+ *            kernel, built with its epilogue replaced by a float32 store; the
+ *            general kernel's stage 0 where that is the kernel it runs).
  * out is 16-byte aligned; any other stage is IQP_ERR_INVALID.
  */
 int iqp_debug_indexer_q_f32(const void* a, int64_t lda,
@@ -340,6 +347,60 @@ int iqp_debug_indexer_q_f32(const void* a, int64_t lda,
                             const float* cos_sin, int64_t max_pos,
                             float* out, int32_t stage,
                             void* stream);
+
+/*
+ * iqp_debug_indexer_q_prep_bf16_f32 — diagnostic twin of indexer_q_prep_bf16
+ * (same pages, same arguments and limits): the one-launch kernel, quantizing
+ * x itself, with its epilogue replaced by a float32 store of Q (the GEMM
+ * output) to out[M, H*D], 16-byte aligned.
+ */
+int iqp_debug_indexer_q_prep_bf16_f32(const void* x, int64_t ldx, const void* w, int64_t ldw,
+                                      const uint8_t* w_scales,
+                                      int64_t M, int64_t K, int32_t H, int32_t D, int32_t rope_dim,
+                                      const int64_t* positions, const float* cos_sin, int64_t max_pos,
+                                      float* out, void* stream);
+
+/*
+ * iqp_debug_indexer_q_clock — indexer_q_gemm_rope_fp4 (same arguments, same
+ * q_fp4 / q_scales bytes) from a build of its kernel that also records the
+ * shader clock, for reading measured throughput against the clock the chip
+ * ran at (tokenspeed PR "perf(deepseek-v4): accelerate indexer Q and packed
+ * FP8 quantization", Performance: the pages quote kernel times with no
+ * clock). Supported where the call runs the split-role kernel (K = 1536,
+ * 1024 tokens or more); elsewhere IQP_ERR_UNSUPPORTED with nothing enqueued.
+ *
+ *   stamps          uint64 [4 * workgroups], 16-byte aligned: for workgroup
+ *                   g, stamps[4g], [4g+1] = the shader clock counter
+ *                   (s_memtime) at its start and end, [4g+2], [4g+3] = the
+ *                   constant-rate counter (s_memrealtime, ticking at the
+ *                   wall clock rate of iqp_device_clock_rates) at the same
+ *                   points; all four 0 for a workgroup given no tokens.
+ *   stamp_capacity  elements of stamps; below 4 * workgroups: IQP_ERR_INVALID,
+ *                   nothing enqueued.
+ *   n_workgroups    host pointer, set to the launch's workgroup count before
+ *                   any other check of the stamps (0 when unsupported or
+ *                   invalid otherwise).
+ * Mean shader clock of a workgroup = (end - start of s_memtime) / (end -
+ * start of s_memrealtime) * wall clock rate.
+ */
+int iqp_debug_indexer_q_clock(const void* a, int64_t lda,
+                              const int32_t* a_scales, int64_t as_stride_m, int64_t as_stride_w,
+                              const void* w, int64_t ldw,
+                              const uint8_t* w_scales,
+                              int64_t M, int64_t K, int32_t H, int32_t D, int32_t rope_dim,
+                              const int64_t* positions,
+                              const float* cos_sin, int64_t max_pos,
+                              uint8_t* q_fp4, uint8_t* q_scales,
+                              uint64_t* stamps, int64_t stamp_capacity, int64_t* n_workgroups,
+                              void* stream);
+
+/*
+ * iqp_device_clock_rates — the current device's constant-rate counter
+ * frequency (the rate of iqp_debug_indexer_q_clock's realtime stamps) and its
+ * peak shader clock, in Hz, into two host int64 values. IQP_ERR_HIP if the
+ * runtime cannot report them.
+ */
+int iqp_device_clock_rates(int64_t* wall_clock_hz, int64_t* peak_shader_clock_hz);
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* iqp_status_string(int status);

@@ -124,7 +124,7 @@ def test_one_launch_ex_argument_checks(iqp):
 def test_debug_and_table_argument_checks(iqp):
     lib = iqp._lib
     args = [P(16), 256, P(16), 1, 1, P(16), 256, P(16), 4, 256, 2, 128, 64, P(16), P(16), 10]
-    assert lib.iqp_debug_indexer_q_f32(*args, P(16), 3, None) == iqp.IQP_ERR_INVALID
+    assert lib.iqp_debug_indexer_q_f32(*args, P(16), 4, None) == iqp.IQP_ERR_INVALID
     assert lib.iqp_debug_indexer_q_f32(*args, P(16), -1, None) == iqp.IQP_ERR_INVALID
     assert lib.iqp_rope_cos_sin_table(10000.0, 10, 63, P(16), None) == iqp.IQP_ERR_INVALID
     assert lib.iqp_rope_cos_sin_table(-1.0, 10, 64, P(16), None) == iqp.IQP_ERR_INVALID
@@ -243,3 +243,37 @@ def test_binding_rejects_short_activation_scale_rows(iqp):
         iqp.indexer_q_gemm_rope_fp4(a, torch.zeros((M, 1), dtype=torch.int32), w, ws, pos, cs, n_heads=H)
     with pytest.raises(ValueError, match="a_scales must be"):
         iqp.debug_indexer_q_f32(a, torch.zeros((M, 2), dtype=torch.int32), w, ws, pos, cs, stage=0, n_heads=H)
+
+
+def clock(iqp, M=2048, K=1536, H=64, stamps=16, cap=1024, nwg=True, q=16, qs=16):
+    n = ctypes.c_int64(-1)
+    st = iqp._lib.iqp_debug_indexer_q_clock(P(16), K, P(16), 3, 1, P(16), K, P(16), M, K, H, 128, 64,
+                                            P(16), P(16), 10, P(q), P(qs), P(stamps), cap,
+                                            ctypes.byref(n) if nwg else None, None)
+    return st, n.value
+
+
+def test_clock_and_debug_argument_checks(iqp):
+    assert clock(iqp, nwg=False)[0] == iqp.IQP_ERR_INVALID
+    assert clock(iqp, cap=-1) == (iqp.IQP_ERR_INVALID, 0)
+    assert clock(iqp, M=-1) == (iqp.IQP_ERR_INVALID, 0)
+    assert clock(iqp, q=0) == (iqp.IQP_ERR_INVALID, 0)
+    assert clock(iqp, stamps=0) == (iqp.IQP_ERR_INVALID, 0)
+    assert clock(iqp, stamps=24) == (iqp.IQP_ERR_UNSUPPORTED, 0)   # stamps not 16-byte aligned
+    assert clock(iqp, M=0) == (iqp.IQP_ERR_UNSUPPORTED, 0)
+    lib = iqp._lib
+    assert lib.iqp_device_clock_rates(None, None) == iqp.IQP_ERR_INVALID
+    # the debug GEMM stage 3 and the one-launch twin reject before any device call
+    assert lib.iqp_debug_indexer_q_f32(P(16), 256, P(16), 1, 1, P(16), 256, P(16), 4, 256, 2, 128, 64,
+                                       P(16), P(16), 10, P(16), 4, None) == iqp.IQP_ERR_INVALID
+    assert lib.iqp_debug_indexer_q_f32(P(16), 256, P(16), 1, 1, P(16), 256, P(16), 4, 256, 2, 128, 64,
+                                       P(16), P(16), 10, P(0), 3, None) == iqp.IQP_ERR_INVALID
+    bf16 = lambda M=4, K=1536, x=16, out=16: lib.iqp_debug_indexer_q_prep_bf16_f32(
+        P(x), K, P(16), K, P(16), M, K, 64, 128, 64, P(16), P(16), 10, P(out), None)
+    assert bf16(M=-1) == iqp.IQP_ERR_INVALID
+    assert bf16(x=0) == iqp.IQP_ERR_INVALID
+    assert bf16(out=0) == iqp.IQP_ERR_INVALID
+    assert bf16(M=257) == iqp.IQP_ERR_UNSUPPORTED
+    assert bf16(K=1024) == iqp.IQP_ERR_UNSUPPORTED
+    assert bf16(out=24) == iqp.IQP_ERR_UNSUPPORTED
+    assert bf16(M=0) == iqp.IQP_OK

@@ -13,11 +13,10 @@ import torch
 
 import synthetic as S
 from oracle import checker as C
-from oracle import formats as F
 from oracle import indexer_q as IQ
 from oracle import quant_fp8 as QO
 
-from gpu_util import oracle_chain_from_x, weights_for_heads
+from gpu_util import mfma_error_bound, oracle_chain_from_x, weights_for_heads
 
 pytestmark = pytest.mark.gpu
 
@@ -49,26 +48,6 @@ def test_rope_table_matches_oracle(gpu_lib, table):
         want = IQ.rope_cos_sin_table(THETA, mp, 64)[rows]
         tol = np.spacing(np.abs(want).astype(np.float32)).astype(np.float64) + 1e-10
         assert np.all(np.abs(got[rows] - want) <= tol), mp
-
-
-def mfma_error_bound(a_codes, a_sb, w_codes, w_sb):
-    """Per-element bound on |Q_device - Q_exact| for the FP8 matrix cores.
-
-    Measured on gfx950: one 64-deep FP8 MFMA returns its dot product with an
-    error of at most about 2^-11.3 of the largest product term (median 2^-14.5;
-    every FP8 MFMA form behaves alike), i.e. products are summed at a fixed
-    precision below the largest one rather than in float32. The bound allows
-    2^-9 (64 terms x 2^-15) of max|A| * max|W| per 64-deep chunk, times the
-    block scales, plus float32 rounding of the running sum.
-    """
-    A = F.e4m3_decode(a_codes)
-    W = F.e4m3_decode(w_codes)
-    M, K = A.shape
-    nc = K // 64
-    amax = np.abs(A).reshape(M, nc, 64).max(-1) * np.repeat(np.ldexp(1.0, a_sb.astype(np.int64) - 127), 2, axis=1)
-    wsc = np.repeat(np.repeat(np.ldexp(1.0, w_sb.astype(np.int64) - 127), 128, axis=0), 2, axis=1)
-    wmax = np.abs(W).reshape(W.shape[0], nc, 64).max(-1) * wsc
-    return 2.0 ** -9 * (amax @ wmax.T)
 
 
 def test_gemm_rope_hadamard_stages_float32(gpu_lib, weights, table):
