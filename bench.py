@@ -1,33 +1,37 @@
 """Benchmark of the indexer-Q preparation hot path on one MI355X.
 
-One step = the whole path over one batch of 4,632 tokens (X bf16 [4632, 1536]):
+One step = the whole path over one batch of tokens (X bf16 [M, 1536]):
 packed-UE8M0 FP8 quantization, then the fused block-scaled FP8 Q projection +
 RoPE + Hadamard-128 + FP4 kernel (64 heads x 128). Inputs are synthetic and
 already resident in HBM when timing starts; outputs are preallocated.
 
-The K timed steps are captured into one HIP graph and replayed (the eager
-launch rate of the same steps is reported beside it). Prints ONE JSON line
-with whole-job tokens/s, the fused kernel's MFMA roofline
-(algorithmic FLOPs / measured average kernel time, against the dense FP8 peak),
-the standalone quantizer's HBM roofline on a [4632, 7168] matrix (rotated over
-enough buffer sets to defeat the 256 MiB Infinity Cache), and the CPU oracle
-timed on a bounded sample of the same workload.
+The headline `value` is the 4,632-token chain (tokens/s). Every chain config
+(128, 4,632 and 32,768 tokens) is timed the way the TensorRT-LLM PR page
+(Description / Results) times its paths: K steps captured into one HIP graph,
+the graph replayed R times with an event pair around each replay, the median
+replay taken; the configs run once in forward and once in reverse order and
+the two medians are averaged. p10 / p90 over all 2R replays are reported
+beside. The same line carries:
+
+* the fused kernel's MFMA roofline (algorithmic FLOPs / median kernel time
+  against the 5.0 PFLOP/s dense FP8 spec), and the shader clock it ran at,
+  read from the kernel's clock-stamp build (s_memtime / s_memrealtime deltas
+  per workgroup), with the fraction against the peak scaled to that clock;
+* the standalone quantizer's HBM roofline on X' [4632, 7168] and on
+  X' [32768, 7168] (rotated over enough buffer sets to defeat the 256 MiB
+  Infinity Cache), beside a plain device copy's rate;
+* the decode-shaped mix: 256 independent calls with M from {1, 2, 4, 8, 16,
+  32, 64}, sustained calls/s from one captured graph, with hot and cold
+  (rotating) weights, and per-call latency percentiles;
+* the standalone epilogue and the weight preparation against HBM;
+* the CPU oracle timed on a bounded sample of the 4,632-token workload.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 
-`--workload decode` instead measures the decode-shaped mix: 256 independent
-calls with M drawn from {1, 2, 4, 8, 16, 32, 64} (each: the indexer-Q
-preparation of X [M, 1536] in one launch, and a standalone quantization of
-X' [M, 7168]), replayed from one captured HIP graph (sustained calls/s), with
-per-M latencies from graphs of repeated single calls; the two-call path
-(quantize, then the fused kernel) is measured beside it.
-
-`--workload prefill32k` measures the long-prefill workload: the chain at
-32,768 tokens (X Student-t, nu = 3; positions 0..32767) and the standalone
-quantizer on X' [32768, 7168]. The default line also carries the standalone
-epilogue (bf16 Q [4632, 64x128] -> RoPE, Hadamard, FP4) against its HBM
-roofline; `--vendor-gemm` adds the vendor FP8 GEMM (hipBLASLt) timed at the
-projection shape, as context only.
+`--workload` picks one part alone (for profiling runs): `prefill` (the
+4,632-token chain), `prefill128`, `prefill32k`, `decode`; `all` (default) is
+the whole line. `--vendor-gemm` adds the vendor FP8 GEMM (hipBLASLt) timed at
+the projection shape, as context only.
 """
 import argparse
 import json
@@ -38,94 +42,57 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA, TFLOP/s
+PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA, TFLOP/s, at the 2.4 GHz peak clock
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
-M_TOKENS, K_PROJ, N_HEADS, HEAD_DIM = 4632, 1536, 64, 128
-QUANT_M, QUANT_K = 4632, 7168
+K_PROJ, N_HEADS, HEAD_DIM = 1536, 64, 128
+QUANT_K = 7168
+W_BYTES = N_HEADS * HEAD_DIM * K_PROJ + N_HEADS * (K_PROJ // 128)   # E4M3 weights + tile scales
+
+# chain configs: name -> (tokens, synthetic workload)
+CHAINS = {
+    "c0_chain_m128": (128, "indexer_q_m128"),
+    "c2_chain_m4632": (4632, "indexer_q_m4632"),
+    "c4_chain_m32768": (32768, "prefill_m32768"),
+}
+HEADLINE = "c2_chain_m4632"
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100, help="steps per captured graph (one replay)")
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--replays", type=int, default=10, help="timed replays per config and order (>= 5)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0: calibrate to ~15 s)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain device copy of 256 MiB (for HBM byte-counter scaling)")
-    ap.add_argument("--workload", choices=("prefill", "prefill32k", "decode"), default="prefill")
+    ap.add_argument("--workload", choices=("all", "prefill", "prefill128", "prefill32k", "decode"), default="all")
     ap.add_argument("--vendor-gemm", action="store_true",
                     help="also time the vendor FP8 GEMM (hipBLASLt via torch._scaled_mm, per-tensor scales, "
                          "bf16 out) at the projection shape, as context for the fused kernel's MFMA fraction")
     return ap.parse_args()
 
 
+# ---------------------------------------------------------------------------
+# algorithmic work per launch
+
+def fused_flops(M):
+    return 2.0 * M * (N_HEADS * HEAD_DIM) * K_PROJ
+
+
 def fused_bytes(M):
     """Algorithmic HBM bytes of one fused launch: A + its scale words, W + its
     scales, positions, the table rows read, and the FP4 codes + scales written."""
     nkb = K_PROJ // 128
-    return (M * K_PROJ + M * 4 * ((nkb + 3) // 4) + N_HEADS * HEAD_DIM * K_PROJ + N_HEADS * nkb
-            + M * 8 + M * 64 * 4 + M * N_HEADS * (HEAD_DIM // 2 + HEAD_DIM // 32))
-
-
-# The sources each measured kernel is built from: a committed traffic figure is
-# used only while these files hash to the digest recorded beside it.
-KERNEL_SOURCES = {
-    "fused": ("indexer_q_pipe.hip", "iq_common.h"),        # the K = 1536 kernel
-    "quant": ("quant_fp8.hip",),
-    "epilogue": ("epilogue_bf16.hip", "iq_common.h"),
-}
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "indexer_q_chain_m4632_rocprofv3.md")
-
-
-def source_digest(kernel):
-    """First 16 hex digits of the SHA-256 of a kernel's sources."""
-    import hashlib
-    h = hashlib.sha256()
-    for name in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, "fp4_quantized_prep_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
-
-
-def measured_traffic(kernel):
-    """HBM bytes per launch from the committed rocprofv3 counter summary
-    (FETCH_SIZE and WRITE_SIZE scaled by a plain copy's readings), or None if
-    the kernel's sources changed since the counters were taken."""
-    try:
-        fields = dict(line.strip().split(": ", 1) for line in open(TRAFFIC_PROFILE)
-                      if line.strip().startswith(kernel + "_"))
-        digest = source_digest(kernel)
-    except (OSError, ValueError):
-        return None
-    if fields.get(f"{kernel}_kernel_source_sha256_16") != digest:
-        return None
-    return int(fields[f"{kernel}_traffic_bytes_per_launch"])
-
-
-MFMA_PROFILE = os.path.join(ROOT, "profiles", "indexer_q_pipe_mfma_counters_m4632.md")
-
-
-def measured_mfma_util():
-    """The fused kernel's MFMA busy share (SQ_VALU_MFMA_BUSY_CYCLES over the
-    SIMDs' active cycles) from the committed rocprofv3 counter summary, or
-    None if the kernel's sources changed since the counters were taken."""
-    try:
-        fields = dict(line.strip().split(": ", 1) for line in open(MFMA_PROFILE)
-                      if line.strip().startswith("fused_"))
-    except (OSError, ValueError):
-        return None
-    if fields.get("fused_kernel_source_sha256_16") != source_digest("fused"):
-        return None
-    return float(fields["fused_mfma_util_pct"]) / 100.0
+    return (M * K_PROJ + M * 4 * ((nkb + 3) // 4) + W_BYTES + M * 8 + M * 64 * 4
+            + M * N_HEADS * (HEAD_DIM // 2 + HEAD_DIM // 32))
 
 
 def one_launch_bytes(M):
     """Algorithmic HBM bytes of one one-launch call: bf16 X, W + its scales,
     positions, the table rows read, and the FP4 codes + scales written."""
-    nkb = K_PROJ // 128
-    return (M * K_PROJ * 2 + N_HEADS * HEAD_DIM * K_PROJ + N_HEADS * nkb + M * 8 + M * 64 * 4
-            + M * N_HEADS * (HEAD_DIM // 2 + HEAD_DIM // 32))
+    return M * K_PROJ * 2 + W_BYTES + M * 8 + M * 64 * 4 + M * N_HEADS * (HEAD_DIM // 2 + HEAD_DIM // 32)
 
 
 def epilogue_bytes(M, H=N_HEADS):
@@ -140,284 +107,60 @@ def quant_bytes(M, K):
     return M * K * 2 + M * K + M * 4 * ((K // 128 + 3) // 4)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (this path has no cross-GPU step); got --gpus {args.gpus}",
-              file=sys.stderr)
-        sys.exit(2)
+# ---------------------------------------------------------------------------
+# committed counter figures (used only while the kernel sources are unchanged)
 
-    if args.workload == "decode":
-        decode_bench(args)
-        return
-    if args.workload == "prefill32k":
-        prefill32k_bench(args)
-        return
-
-    import numpy as np
-    import torch
-
-    import fp4_quantized_prep_amd as iqp
-    import synthetic as S
-
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    stream = torch.cuda.current_stream(dev)
-    print(f"[bench] device {torch.cuda.get_device_name(dev)}; preparing inputs", file=sys.stderr, flush=True)
-
-    inp = S.indexer_q_inputs("indexer_q_m4632")
-    x = inp["x"].to(dev)
-    pos = inp["positions"].to(dev)
-    w_cpu, wsb_cpu = S.weights()
-    w, wsb = w_cpu.to(dev), wsb_cpu.to(dev)
-    cs = iqp.rope_cos_sin_table(S.ROPE_THETA, inp["max_pos"], 64, device=dev)
-    M = x.shape[0]
-    a = torch.empty((M, K_PROJ), dtype=torch.uint8, device=dev)
-    a_s = torch.empty((M, (K_PROJ // 128 + 3) // 4), dtype=torch.int32, device=dev)
-    q = torch.empty((M, N_HEADS, HEAD_DIM // 2), dtype=torch.uint8, device=dev)
-    qs = torch.empty((M, N_HEADS, HEAD_DIM // 32), dtype=torch.uint8, device=dev)
-
-    def step():
-        iqp.fp8_quant_1x128_ue8m0(x, q=a, scales=a_s)
-        iqp.indexer_q_gemm_rope_fp4(a, a_s, w, wsb, pos, cs, n_heads=N_HEADS, q_fp4=q, q_scales=qs)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # ---- K whole steps launched one after another, as an eager caller would,
-    # with events only at the two ends (an event between two kernels adds a
-    # dispatch gap of its own); reported beside the timed region below
-    K = args.steps
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(K):
-        step()
-    stop.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    total_ms = start.elapsed_time(stop)
-    ms_per_step = total_ms / K
-    tokens_per_s = M * K / (total_ms * 1e-3)
-
-    # ---- timed region (`value`): the same K steps captured into one HIP graph
-    # and replayed, one untimed replay, then one timed between two events on
-    # the stream: every kernel of every step runs, without the host's
-    # per-launch dispatch gaps
-    t_step_graph = graph_launch_time(lambda i: step(), K, reps=1)
-    tokens_per_s_graph = M / t_step_graph
-
-    # ---- the same K steps again with an event pair around each kernel: each
-    # kernel's average in the chain (the events' own gaps are in these figures)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    for i in range(K):
-        ev[i][0].record(stream)
-        iqp.fp8_quant_1x128_ue8m0(x, q=a, scales=a_s)
-        ev[i][1].record(stream)
-        iqp.indexer_q_gemm_rope_fp4(a, a_s, w, wsb, pos, cs, n_heads=N_HEADS, q_fp4=q, q_scales=qs)
-        ev[i][2].record(stream)
-    torch.cuda.synchronize()
-    t_quant = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3       # s
-    t_fused_ev = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e-3
-    pct = lambda v: {f"p{q}": float(np.percentile(v, q)) * 1e3 for q in (10, 50, 90)}   # ms -> us
-    in_chain_us = {"quant": pct([e[0].elapsed_time(e[1]) for e in ev]),
-                   "fused": pct([e[1].elapsed_time(e[2]) for e in ev])}
-    # the fused kernel's own duration: K launches back to back from a captured
-    # graph between two events on its stream (the input A stays the chain's)
-    t_fused = graph_launch_time(
-        lambda i: iqp.indexer_q_gemm_rope_fp4(a, a_s, w, wsb, pos, cs, n_heads=N_HEADS, q_fp4=q, q_scales=qs),
-        max(20, min(K, 100)))
-    flops = 2.0 * M * (N_HEADS * HEAD_DIM) * K_PROJ
-    fused_tflops = flops / t_fused / 1e12
-    # context: the same projection with both convention flags (interleaved RoPE,
-    # OCP floor-rule FP4 scales), the pipelined kernel's variant build
-    t_variant = graph_launch_time(
-        lambda i: iqp.indexer_q_gemm_rope_fp4(a, a_s, w, wsb, pos, cs, n_heads=N_HEADS, q_fp4=q, q_scales=qs,
-                                              rope_layout="interleaved", scale_rule="ocp_floor"),
-        max(20, min(K, 100)))
-    print(f"[bench] chain from a captured graph: {t_step_graph * 1e6:.1f} us/step = {tokens_per_s_graph:.3e} tokens/s",
-          file=sys.stderr, flush=True)
-    print(f"[bench] chain: {ms_per_step * 1e3:.1f} us/step (wall {wall * 1e6 / K:.1f} us); "
-          f"fused kernel {t_fused * 1e6:.1f} us back to back = {fused_tflops:.0f} TFLOP/s; with an event "
-          f"pair around each kernel: quant {t_quant * 1e6:.1f} us, fused {t_fused_ev * 1e6:.1f} us; "
-          f"with both convention flags {t_variant * 1e6:.1f} us", file=sys.stderr, flush=True)
-
-    # ---- standalone quantizer on [4632, 7168], rotating buffer sets (> 256 MiB)
-    xq_cpu = S.quant_input("quant_4632x7168")
-    n_sets = 5
-    xs = [xq_cpu.to(dev) for _ in range(n_sets)]
-    qq = [torch.empty((QUANT_M, QUANT_K), dtype=torch.uint8, device=dev) for _ in range(n_sets)]
-    ss = [torch.empty((QUANT_M, (QUANT_K // 128 + 3) // 4), dtype=torch.int32, device=dev) for _ in range(n_sets)]
-    for i in range(10):
-        iqp.fp8_quant_1x128_ue8m0(xs[i % n_sets], q=qq[i % n_sets], scales=ss[i % n_sets])
-    torch.cuda.synchronize()
-    # Launches replayed back to back from a captured graph between two events on
-    # the kernel's stream, so the average is the kernel's own duration (an event
-    # pair around every launch adds ~2.5 us of dispatch gap at this size); the
-    # per-launch-event figure is reported beside it.
-    n_q = max(50, K)
-    t_q_big = graph_launch_time(
-        lambda i: iqp.fp8_quant_1x128_ue8m0(xs[i % n_sets], q=qq[i % n_sets], scales=ss[i % n_sets]), n_q)
-    qev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_q)]
-    for i in range(n_q):
-        k = i % n_sets
-        qev[i][0].record(stream)
-        iqp.fp8_quant_1x128_ue8m0(xs[k], q=qq[k], scales=ss[k])
-        qev[i][1].record(stream)
-    torch.cuda.synchronize()
-    t_q_ev = float(np.mean([b.elapsed_time(e) for b, e in qev])) * 1e-3
-    qbytes = quant_bytes(QUANT_M, QUANT_K)
-    q_gbs = qbytes / t_q_big / 1e9
-    print(f"[bench] quantizer [4632,7168]: {t_q_big * 1e6:.1f} us = {q_gbs:.0f} GB/s back to back (graph); "
-          f"{t_q_ev * 1e6:.1f} us with an event pair around each launch", file=sys.stderr, flush=True)
-    del xs, qq, ss
-
-    # ---- standalone epilogue (bf16 Q -> RoPE, Hadamard, FP4) on [4632, 64*128],
-    # rotating buffer sets (> 256 MiB), launches back to back
-    qin = S.q_bf16_inputs("indexer_q_m4632")
-    e_sets = 4
-    eq = [qin["q"].to(dev) for _ in range(e_sets)]
-    eo = [torch.empty((M, N_HEADS, HEAD_DIM // 2), dtype=torch.uint8, device=dev) for _ in range(e_sets)]
-    es = [torch.empty((M, N_HEADS, HEAD_DIM // 32), dtype=torch.uint8, device=dev) for _ in range(e_sets)]
-    for i in range(8):
-        iqp.indexer_q_rope_hadamard_fp4(eq[i % e_sets], pos, cs, n_heads=N_HEADS, q_fp4=eo[i % e_sets],
-                                        q_scales=es[i % e_sets])
-    torch.cuda.synchronize()
-    n_e = max(40, K)
-    t_epi = graph_launch_time(
-        lambda i: iqp.indexer_q_rope_hadamard_fp4(eq[i % e_sets], pos, cs, n_heads=N_HEADS, q_fp4=eo[i % e_sets],
-                                                  q_scales=es[i % e_sets]), n_e)
-    ebytes = epilogue_bytes(M)
-    e_gbs = ebytes / t_epi / 1e9
-    print(f"[bench] standalone epilogue [4632, 64x128] bf16: {t_epi * 1e6:.1f} us = {e_gbs:.0f} GB/s",
-          file=sys.stderr, flush=True)
-    del eq, eo, es
-
-    # ---- weight preparation (off the per-token path): bf16 W [8192, 1536] ->
-    # E4M3 + 128x128 UE8M0, 10 rotating sets (376 MB), graph-replayed
-    wg = np.random.default_rng([100, 1])
-    wb = torch.from_numpy((wg.standard_normal((N_HEADS * HEAD_DIM, K_PROJ)) * 0.02).astype(np.float32)).to(
-        torch.bfloat16)
-    w_sets = 10
-    wbs = [wb.to(dev) for _ in range(w_sets)]
-    wqs = [torch.empty((N_HEADS * HEAD_DIM, K_PROJ), dtype=torch.uint8, device=dev) for _ in range(w_sets)]
-    wss = [torch.empty((N_HEADS * HEAD_DIM // 128, K_PROJ // 128), dtype=torch.uint8, device=dev)
-           for _ in range(w_sets)]
-    t_wq = graph_launch_time(lambda i: iqp.fp8_quant_weight_128x128_ue8m0(
-        wbs[i % w_sets], q=wqs[i % w_sets], scales=wss[i % w_sets]), 40)
-    wq_bytes = N_HEADS * HEAD_DIM * K_PROJ * 3 + (N_HEADS * HEAD_DIM // 128) * (K_PROJ // 128)
-    print(f"[bench] weight preparation [8192, 1536]: {t_wq * 1e6:.1f} us = {wq_bytes / t_wq / 1e9:.0f} GB/s",
-          file=sys.stderr, flush=True)
-    del wbs, wqs, wss
-
-    vendor = vendor_gemm_context(M, dev) if args.vendor_gemm else None
-
-    if args.copy_calibration:
-        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
-    # ---- CPU baseline: the oracle on a bounded sample of the same workload
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(args.cpu_tokens, inp, w_cpu, wsb_cpu)
-
-    result = {
-        "metric": "tokens/sec & % roofline: FP8 quant (HBM GB/s) + fused indexer-Q (MFMA util)",
-        "value": tokens_per_s_graph,
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
-        "ms_per_step": t_step_graph * 1e3,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "fp8-e4m3 (fp32 accumulate), bf16 in, fp4-e2m1 out",
-        "data": "synthetic",
-        "config": {
-            "workload": "indexer-Q chain, 4632 tokens: X bf16 [4632,1536] -> FP8 1x128 UE8M0 -> "
-                        "Q = A W^T (W [8192,1536] E4M3, 128x128 UE8M0) -> RoPE(64 of 128) -> "
-                        "Hadamard-128 -> FP4 e2m1 [4632,64,64] + UE8M0 [4632,64,4]",
-            "tokens": M, "K": K_PROJ, "heads": N_HEADS, "head_dim": HEAD_DIM, "rope_dim": 64,
-            "parallelism": "single GPU",
-        },
-        "roofline": {
-            "kernel": "indexer_q_pipe_kernel (fused GEMM + RoPE + Hadamard + FP4; launches back to back from a "
-                      "captured graph on the chain's A)",
-            "bound": "mfma",
-            "achieved": fused_tflops,
-            "peak": PEAK_FP8_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": fused_tflops / PEAK_FP8_TFLOPS,
-            "traffic": measured_traffic("fused"),
-            "algorithmic_flops_per_launch": flops,
-            "avg_launch_us": t_fused * 1e6,
-            "avg_launch_us_event_pair_each": t_fused_ev * 1e6,
-            "avg_launch_us_interleaved_rope_ocp_floor_scales": t_variant * 1e6,
-            "mfma_busy_frac_counters": measured_mfma_util(),
-        },
-        "quant_roofline": {
-            "kernel": "fp8_quant_1x128_kernel on [4632,7168] (5 rotating buffer sets, launches back to back "
-                      "from a captured graph)",
-            "bound": "hbm",
-            "achieved": q_gbs,
-            "peak": PEAK_HBM_GBS,
-            "unit": "GB/s",
-            "frac": q_gbs / PEAK_HBM_GBS,
-            "algorithmic_bytes_per_launch": qbytes,
-            "traffic": measured_traffic("quant"),
-            "avg_launch_us": t_q_big * 1e6,
-            "avg_launch_us_event_pair_each": t_q_ev * 1e6,
-            "in_chain_avg_launch_us": t_quant * 1e6,
-        },
-        "epilogue_roofline": {
-            "kernel": "indexer_q_epilogue_kernel (bf16 Q [4632, 64x128] -> RoPE, Hadamard-128, FP4; "
-                      "4 rotating buffer sets, launches back to back from a captured graph)",
-            "bound": "hbm",
-            "achieved": e_gbs,
-            "peak": PEAK_HBM_GBS,
-            "unit": "GB/s",
-            "frac": e_gbs / PEAK_HBM_GBS,
-            "algorithmic_bytes_per_launch": ebytes,
-            "traffic": measured_traffic("epilogue"),
-            "avg_launch_us": t_epi * 1e6,
-        },
-        "weight_prep_roofline": {
-            "kernel": "fp8_quant_weight_kernel (bf16 W [8192,1536] -> E4M3 + 128x128 UE8M0; off the per-token "
-                      "path; 10 rotating sets, graph-replayed)",
-            "bound": "hbm",
-            "achieved": wq_bytes / t_wq / 1e9,
-            "peak": PEAK_HBM_GBS,
-            "unit": "GB/s",
-            "frac": wq_bytes / t_wq / 1e9 / PEAK_HBM_GBS,
-            "algorithmic_bytes_per_launch": wq_bytes,
-            "avg_launch_us": t_wq * 1e6,
-        },
-        "cpu_baseline": cpu,
-        "in_chain_kernel_us": in_chain_us,
-        "timing": "K whole steps captured into one HIP graph, one untimed replay, then one replay between two "
-                  "events on the stream (synchronized before and after)",
-        "eager": {"ms_per_step": ms_per_step, "tokens_per_s": tokens_per_s,
-                  "note": "the same K steps launched one after another from Python, events only at the ends"},
-        "runtime": {"hip": torch.version.hip, "torch": torch.__version__,
-                    "device": torch.cuda.get_device_name(dev)},
-    }
-    if vendor is not None:
-        result["vendor_gemm_context"] = vendor
-    print(json.dumps(result), flush=True)
+KERNEL_SOURCES = {
+    "fused": ("indexer_q_pipe.hip", "indexer_q_split.hip", "iq_common.h"),   # the split-role kernel
+    "quant": ("quant_fp8.hip", "fp8_block.h"),
+    "epilogue": ("epilogue_bf16.hip", "iq_common.h"),
+}
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "indexer_q_chain_m4632_rocprofv3.md")
+MFMA_PROFILE = os.path.join(ROOT, "profiles", "indexer_q_split_mfma_counters_m4632.md")
 
 
-def graph_launch_time(launch, n_calls, reps=5):
-    """Average device time per call of launch(0..n_calls-1), replayed from one
-    captured HIP graph between two events on the current stream: host-side
-    launch cost (the Python binding's checks) is out of the measurement, so a
-    short kernel is not starved by its own launches."""
+def source_digest(kernel):
+    """First 16 hex digits of the SHA-256 of a kernel's sources."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "fp4_quantized_prep_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _profile_fields(path, prefix):
+    try:
+        return dict(line.strip().split(": ", 1) for line in open(path) if line.strip().startswith(prefix))
+    except (OSError, ValueError):
+        return {}
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE scaled by a plain copy's readings), or None if
+    the kernel's sources changed since the counters were taken."""
+    fields = _profile_fields(TRAFFIC_PROFILE, kernel + "_")
+    if fields.get(f"{kernel}_kernel_source_sha256_16") != source_digest(kernel):
+        return None
+    return int(fields[f"{kernel}_traffic_bytes_per_launch"])
+
+
+def measured_mfma_util():
+    """The fused kernel's MFMA busy share from the committed rocprofv3 counter
+    summary, or None if the kernel's sources changed since."""
+    fields = _profile_fields(MFMA_PROFILE, "fused_")
+    if fields.get("fused_kernel_source_sha256_16") != source_digest("fused"):
+        return None
+    return float(fields["fused_mfma_util_pct"]) / 100.0
+
+
+# ---------------------------------------------------------------------------
+# timing helpers
+
+def capture(launch, n_calls):
+    """One HIP graph of launch(0..n_calls-1), captured after one eager call on
+    a side stream."""
     import torch
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -429,16 +172,377 @@ def graph_launch_time(launch, n_calls, reps=5):
     with torch.cuda.graph(g):
         for i in range(n_calls):
             launch(i)
+    torch.cuda.synchronize()
+    return g
+
+
+def replay_times(g, n_calls, reps):
+    """Per-call device time (s) of each of `reps` replays of g, each between an
+    event pair on the current stream, after one untimed replay."""
+    import torch
     g.replay()
     torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(reps):
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
         g.replay()
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) * 1e-3 / n_calls for a, b in ev]
+
+
+def stats_us(samples):
+    import numpy as np
+    s = np.asarray(samples) * 1e6
+    return {"p10_us": float(np.percentile(s, 10)), "p50_us": float(np.percentile(s, 50)),
+            "p90_us": float(np.percentile(s, 90)), "n": int(s.size)}
+
+
+def graph_launch_time(launch, n_calls, reps=5):
+    """Median per-call device time (s) of launch(0..n_calls-1) replayed from
+    one captured graph (host launch cost out of the measurement), and the
+    per-replay samples."""
+    import numpy as np
+    t = replay_times(capture(launch, n_calls), n_calls, reps)
+    return float(np.median(t)), t
+
+
+# ---------------------------------------------------------------------------
+# the chain configs
+
+class Chain:
+    """Inputs, preallocated outputs and the step of one chain config."""
+
+    def __init__(self, iqp, S, dev, w, wsb, tables, name):
+        import torch
+        M, workload = CHAINS[name]
+        inp = S.indexer_q_inputs(workload)
+        assert inp["x"].shape[0] == M
+        self.name, self.M, self.iqp = name, M, iqp
+        self.inp = inp
+        self.x = inp["x"].to(dev)
+        self.pos = inp["positions"].to(dev)
+        self.w, self.wsb = w, wsb
+        if inp["max_pos"] not in tables:
+            tables[inp["max_pos"]] = iqp.rope_cos_sin_table(S.ROPE_THETA, inp["max_pos"], 64, device=dev)
+        self.cs = tables[inp["max_pos"]]
+        self.a = torch.empty((M, K_PROJ), dtype=torch.uint8, device=dev)
+        self.a_s = torch.empty((M, (K_PROJ // 128 + 3) // 4), dtype=torch.int32, device=dev)
+        self.q = torch.empty((M, N_HEADS, HEAD_DIM // 2), dtype=torch.uint8, device=dev)
+        self.qs = torch.empty((M, N_HEADS, HEAD_DIM // 32), dtype=torch.uint8, device=dev)
+
+    def quant(self):
+        self.iqp.fp8_quant_1x128_ue8m0(self.x, q=self.a, scales=self.a_s)
+
+    def fused(self):
+        self.iqp.indexer_q_gemm_rope_fp4(self.a, self.a_s, self.w, self.wsb, self.pos, self.cs, n_heads=N_HEADS,
+                                         q_fp4=self.q, q_scales=self.qs)
+
+    def step(self, i=0):
+        self.quant()
+        self.fused()
+
+
+def steps_for(M, K):
+    """Steps per replay: K at the headline size, scaled so one replay of a
+    config stays between about 2 and 20 ms."""
+    return int(min(max(K * 4632 // max(M, 1), 20), 1000)) if M != 4632 else K
+
+
+def time_chains(chains, K, reps):
+    """Forward then reverse order over the chain configs: per config, its
+    graph of steps_for(M, K) steps replayed `reps` times in each order."""
+    import numpy as np
+    graphs = {n: (capture(c.step, steps_for(c.M, K)), steps_for(c.M, K)) for n, c in chains.items()}
+    order = list(chains)
+    res = {n: {"forward": [], "reverse": []} for n in order}
+    for direction, seq in (("forward", order), ("reverse", order[::-1])):
+        for n in seq:
+            g, k = graphs[n]
+            res[n][direction] = replay_times(g, k, reps)
+    out = {}
+    for n in order:
+        f, r = res[n]["forward"], res[n]["reverse"]
+        med = 0.5 * (float(np.median(f)) + float(np.median(r)))
+        out[n] = {"step_s": med, "forward_median_us": float(np.median(f)) * 1e6,
+                  "reverse_median_us": float(np.median(r)) * 1e6, "steps_per_replay": graphs[n][1],
+                  "spread": stats_us(f + r)}
+    return out, order
+
+
+def fused_alone(c, reps):
+    """The fused kernel's own duration: launches back to back from a captured
+    graph on the chain's A."""
+    n = max(20, min(200, 400_000 // max(c.M, 1)))
+    t, samples = graph_launch_time(lambda i: c.fused(), n, reps)
+    return t, samples
+
+
+def clock_during(c, iqp, n_launch=30):
+    """Mean shader clock during the fused kernel: the clock-stamp build of the
+    split-role kernel launched n_launch times back to back on the chain's A;
+    per launch, (sum of s_memtime deltas) / (sum of s_memrealtime deltas) x the
+    counter rate over its workgroups; the median of the last two thirds."""
+    import numpy as np
+    import torch
+    wall_hz, peak_hz = iqp.device_clock_rates()
+    stamps = torch.zeros((n_launch, 4 * 4096), dtype=torch.int64, device=c.x.device)
+    views = []
+    for i in range(n_launch):
+        _, _, st = iqp.debug_indexer_q_clock(c.a, c.a_s, c.w, c.wsb, c.pos, c.cs, q_fp4=c.q, q_scales=c.qs,
+                                             stamps=stamps[i])
+        views.append(st)
+    torch.cuda.synchronize()
+    clocks = []
+    for st in views:
+        s = st.cpu().numpy().astype(np.float64)
+        live = s[:, 3] != 0
+        clocks.append((s[live, 1] - s[live, 0]).sum() / (s[live, 3] - s[live, 2]).sum() * wall_hz)
+    tail = clocks[n_launch // 3:]
+    return {"sclk_ghz": float(np.median(tail)) / 1e9, "sclk_ghz_p10": float(np.percentile(tail, 10)) / 1e9,
+            "sclk_ghz_p90": float(np.percentile(tail, 90)) / 1e9, "peak_sclk_ghz": peak_hz / 1e9,
+            "counter_mhz": wall_hz / 1e6,
+            "method": f"clock-stamp build of the split-role kernel, {n_launch} launches back to back on the "
+                      "chain's A; per launch sum(s_memtime deltas) / sum(s_memrealtime deltas) x counter rate "
+                      "over its workgroups; median of the last two thirds"}
+
+
+def fused_roofline(M, t_fused, samples, clock, name):
+    ach = fused_flops(M) / t_fused / 1e12
+    r = {"kernel": name, "bound": "mfma", "achieved": ach, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+         "frac": ach / PEAK_FP8_TFLOPS, "algorithmic_flops_per_launch": fused_flops(M),
+         "avg_launch_us": t_fused * 1e6, "launch_spread": stats_us(samples)}
+    if clock is not None:
+        peak_at = PEAK_FP8_TFLOPS * clock["sclk_ghz"] / clock["peak_sclk_ghz"]
+        r.update({"sclk_ghz": clock["sclk_ghz"], "peak_at_measured_clock": peak_at,
+                  "frac_at_measured_clock": ach / peak_at})
+    return r
+
+
+def fused_kernel_name(M):
+    if M <= 256:
+        return "indexer_q_small_kernel (small-batch fused kernel)"
+    if M < 1024:
+        return "indexer_q_pipe_kernel (pipelined fused kernel)"
+    return "indexer_q_split_kernel (split-role fused kernel: GEMM + RoPE + Hadamard + FP4)"
+
+
+def chain_record(c, timing, t_fused, fused_samples, clock):
+    M = c.M
+    st = timing["step_s"]
+    rec = {"tokens": M, "us_per_step": st * 1e6, "tokens_per_s": M / st,
+           "forward_median_us": timing["forward_median_us"], "reverse_median_us": timing["reverse_median_us"],
+           "step_spread": timing["spread"], "steps_per_replay": timing["steps_per_replay"],
+           "fused_kernel": fused_roofline(M, t_fused, fused_samples, clock, fused_kernel_name(M)),
+           "chain_minus_fused_us": (st - t_fused) * 1e6}
+    if M <= 256:
+        # at decode-like sizes the fused kernel streams W: its HBM rate
+        gbs = fused_bytes(M) / t_fused / 1e9
+        rec["fused_kernel_hbm"] = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                   "frac": gbs / PEAK_HBM_GBS, "algorithmic_bytes_per_launch": fused_bytes(M),
+                                   "w_stream_gbs": W_BYTES / t_fused / 1e9}
+    return rec
+
+
+def in_chain_events(c, K):
+    """The chain's two kernels with an event pair around each (the events' own
+    gaps are in these figures)."""
+    import numpy as np
+    import torch
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    for i in range(K):
+        ev[i][0].record()
+        c.quant()
+        ev[i][1].record()
+        c.fused()
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    pct = lambda v: {f"p{q}": float(np.percentile(v, q)) * 1e3 for q in (10, 50, 90)}   # ms -> us
+    return {"quant": pct([e[0].elapsed_time(e[1]) for e in ev]), "fused": pct([e[1].elapsed_time(e[2]) for e in ev])}
+
+
+def eager_chain(c, K):
+    """K whole steps launched one after another from Python, events only at
+    the two ends."""
+    import torch
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    a.record()
+    for _ in range(K):
+        c.step()
     b.record()
     torch.cuda.synchronize()
-    return a.elapsed_time(b) * 1e-3 / (reps * n_calls)
+    wall = time.perf_counter() - t0
+    ms = a.elapsed_time(b) / K
+    return {"ms_per_step": ms, "tokens_per_s": c.M / (ms * 1e-3), "wall_us_per_step": wall * 1e6 / K,
+            "note": "the same steps launched one after another from Python, events only at the ends"}
 
+
+# ---------------------------------------------------------------------------
+# standalone kernels
+
+def quant_roofline(iqp, S, dev, M, workload, n_sets, reps):
+    """The standalone quantizer on X' [M, 7168], rotating buffer sets."""
+    import torch
+    xq = S.quant_input(workload)
+    xs = [xq.to(dev) for _ in range(n_sets)]
+    qq = [torch.empty((M, QUANT_K), dtype=torch.uint8, device=dev) for _ in range(n_sets)]
+    ss = [torch.empty((M, (QUANT_K // 128 + 3) // 4), dtype=torch.int32, device=dev) for _ in range(n_sets)]
+    n = max(4 * n_sets, min(100, 400_000_000 // quant_bytes(M, QUANT_K) * n_sets))
+    t, samples = graph_launch_time(lambda i: iqp.fp8_quant_1x128_ue8m0(xs[i % n_sets], q=qq[i % n_sets],
+                                                                       scales=ss[i % n_sets]), n, reps)
+    del xs, qq, ss
+    b = quant_bytes(M, QUANT_K)
+    return {"kernel": f"fp8_quant_1x128_kernel on [{M},{QUANT_K}] ({n_sets} rotating buffer sets, launches "
+                      "back to back from a captured graph)",
+            "bound": "hbm", "achieved": b / t / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": b / t / 1e9 / PEAK_HBM_GBS, "algorithmic_bytes_per_launch": b, "avg_launch_us": t * 1e6,
+            "launch_spread": stats_us(samples)}
+
+
+def copy_ceiling(dev, reps):
+    """A plain device copy of 1 GiB (read + write bytes / time): the HBM rate a
+    streaming kernel reaches on this machine, as context for the HBM fractions."""
+    import torch
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    t, samples = graph_launch_time(lambda i: dst.copy_(src), 4, reps)
+    del src, dst
+    return {"what": "torch copy_ of 1 GiB device to device, read + write bytes", "gbs": 2 * (1 << 30) / t / 1e9,
+            "frac": 2 * (1 << 30) / t / 1e9 / PEAK_HBM_GBS}
+
+
+def epilogue_roofline(iqp, S, dev, pos, cs, M, reps):
+    import torch
+    qin = S.q_bf16_inputs("indexer_q_m4632")
+    n_sets = 4
+    eq = [qin["q"].to(dev) for _ in range(n_sets)]
+    eo = [torch.empty((M, N_HEADS, HEAD_DIM // 2), dtype=torch.uint8, device=dev) for _ in range(n_sets)]
+    es = [torch.empty((M, N_HEADS, HEAD_DIM // 32), dtype=torch.uint8, device=dev) for _ in range(n_sets)]
+    t, samples = graph_launch_time(
+        lambda i: iqp.indexer_q_rope_hadamard_fp4(eq[i % n_sets], pos, cs, n_heads=N_HEADS, q_fp4=eo[i % n_sets],
+                                                  q_scales=es[i % n_sets]), 40, reps)
+    del eq, eo, es
+    b = epilogue_bytes(M)
+    return {"kernel": f"indexer_q_epilogue_kernel (bf16 Q [{M}, 64x128] -> RoPE, Hadamard-128, FP4; {n_sets} "
+                      "rotating buffer sets, launches back to back from a captured graph)",
+            "bound": "hbm", "achieved": b / t / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": b / t / 1e9 / PEAK_HBM_GBS, "algorithmic_bytes_per_launch": b, "avg_launch_us": t * 1e6,
+            "traffic": measured_traffic("epilogue"), "launch_spread": stats_us(samples)}
+
+
+def weight_prep_roofline(iqp, dev, reps):
+    import numpy as np
+    import torch
+    wg = np.random.default_rng([100, 1])
+    wb = torch.from_numpy((wg.standard_normal((N_HEADS * HEAD_DIM, K_PROJ)) * 0.02).astype(np.float32)).to(
+        torch.bfloat16)
+    n_sets = 10
+    wbs = [wb.to(dev) for _ in range(n_sets)]
+    wqs = [torch.empty((N_HEADS * HEAD_DIM, K_PROJ), dtype=torch.uint8, device=dev) for _ in range(n_sets)]
+    wss = [torch.empty((N_HEADS * HEAD_DIM // 128, K_PROJ // 128), dtype=torch.uint8, device=dev)
+           for _ in range(n_sets)]
+    t, _ = graph_launch_time(lambda i: iqp.fp8_quant_weight_128x128_ue8m0(
+        wbs[i % n_sets], q=wqs[i % n_sets], scales=wss[i % n_sets]), 40, reps)
+    del wbs, wqs, wss
+    b = N_HEADS * HEAD_DIM * K_PROJ * 3 + (N_HEADS * HEAD_DIM // 128) * (K_PROJ // 128)
+    return {"kernel": "fp8_quant_weight_kernel (bf16 W [8192,1536] -> E4M3 + 128x128 UE8M0; off the per-token "
+                      "path; 10 rotating sets, graph-replayed)",
+            "bound": "hbm", "achieved": b / t / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": b / t / 1e9 / PEAK_HBM_GBS, "algorithmic_bytes_per_launch": b, "avg_launch_us": t * 1e6}
+
+
+# ---------------------------------------------------------------------------
+# the decode-shaped mix
+
+def decode_mix(iqp, S, dev, w, wsb, reps):
+    """256 independent calls, M from {1, 2, 4, 8, 16, 32, 64}: each the
+    indexer-Q preparation of X [M, 1536] (one launch up to
+    ONE_LAUNCH_MAX_TOKENS tokens, two calls above) and a standalone
+    quantization of X' [M, 7168]. Sustained calls/s from one captured graph of
+    the whole mix, hot (one weight copy) and cold (call i reads weight copy
+    i % 24: 302 MB, beyond the Infinity Cache); per-call latency = the mean
+    call time of its M in a graph of 20 such calls (hot) or of 24 calls over
+    the 24 copies (cold), with p50 / p99 over the mix's calls."""
+    import numpy as np
+    import torch
+    max_pos = 131072
+    cs = iqp.rope_cos_sin_table(S.ROPE_THETA, max_pos, 64, device=dev)
+    calls = []
+    for c in S.decode_calls(256):
+        m = c["x"].shape[0]
+        calls.append({
+            "M": m, "x": c["x"].to(dev), "xw": c["x_wide"].to(dev), "pos": c["positions"].to(dev),
+            "a": torch.empty((m, K_PROJ), dtype=torch.uint8, device=dev),
+            "as": torch.empty((m, 3), dtype=torch.int32, device=dev),
+            "aw": torch.empty((m, QUANT_K), dtype=torch.uint8, device=dev),
+            "asw": torch.empty((m, (QUANT_K // 128 + 3) // 4), dtype=torch.int32, device=dev),
+            "q": torch.empty((m, N_HEADS, HEAD_DIM // 2), dtype=torch.uint8, device=dev),
+            "qs": torch.empty((m, N_HEADS, HEAD_DIM // 32), dtype=torch.uint8, device=dev),
+        })
+
+    def two(c, wt):
+        iqp.fp8_quant_1x128_ue8m0(c["x"], q=c["a"], scales=c["as"])
+        iqp.indexer_q_gemm_rope_fp4(c["a"], c["as"], wt[0], wt[1], c["pos"], cs, n_heads=N_HEADS,
+                                    q_fp4=c["q"], q_scales=c["qs"])
+        iqp.fp8_quant_1x128_ue8m0(c["xw"], q=c["aw"], scales=c["asw"])
+
+    def one(c, wt):
+        iqp.indexer_q_prep_bf16(c["x"], wt[0], wt[1], c["pos"], cs, n_heads=N_HEADS, q_fp4=c["q"],
+                                q_scales=c["qs"])
+        iqp.fp8_quant_1x128_ue8m0(c["xw"], q=c["aw"], scales=c["asw"])
+
+    def routed(c, wt):
+        (one if c["M"] <= iqp.ONE_LAUNCH_MAX_TOKENS else two)(c, wt)
+
+    hot = (w, wsb)
+    n_w = 24
+    cold = [(w.clone(), wsb.clone()) for _ in range(n_w)]
+    med = lambda v: float(np.median(v))
+    t_hot = med(replay_times(capture(lambda _: [routed(c, hot) for c in calls], 1), 1, reps))
+    t_cold = med(replay_times(capture(lambda _: [routed(c, cold[i % n_w]) for i, c in enumerate(calls)], 1),
+                              1, reps))
+    t_one = med(replay_times(capture(lambda _: [one(c, hot) for c in calls], 1), 1, reps))
+    t_two = med(replay_times(capture(lambda _: [two(c, hot) for c in calls], 1), 1, reps))
+    lat_hot, lat_cold, lat_k = {}, {}, {}
+    for m in sorted({c["M"] for c in calls}):
+        c = next(c for c in calls if c["M"] == m)
+        lat_hot[m] = med(replay_times(capture(lambda _: [routed(c, hot) for _ in range(20)], 1), 20, 5)) * 1e6
+        lat_cold[m] = med(replay_times(capture(lambda _: [routed(c, cold[j]) for j in range(n_w)], 1), n_w, 5)) * 1e6
+        if m <= 256:
+            lat_k[m] = med(replay_times(capture(lambda _: [iqp.indexer_q_prep_bf16(
+                c["x"], w, wsb, c["pos"], cs, n_heads=N_HEADS, q_fp4=c["q"], q_scales=c["qs"])
+                for _ in range(20)], 1), 20, 5)) * 1e6
+        print(f"[bench] decode M={m}: {lat_hot[m]:.2f} us hot, {lat_cold[m]:.2f} us cold per call",
+              file=sys.stderr, flush=True)
+    del cold
+    per_hot = np.array([lat_hot[c["M"]] for c in calls])
+    per_cold = np.array([lat_cold[c["M"]] for c in calls])
+    mix_bytes = float(sum(one_launch_bytes(c["M"]) for c in calls))
+    mix_k_s = float(sum(lat_k[c["M"]] for c in calls)) * 1e-6
+    return {
+        "workload": "decode mix: 256 independent calls, M uniform over {1,2,4,8,16,32,64}; each call X bf16 "
+                    "[M,1536] -> FP8 quant -> GEMM + RoPE + Hadamard + FP4 (64 heads), one launch up to "
+                    f"{iqp.ONE_LAUNCH_MAX_TOKENS} tokens and two calls above, plus a standalone FP8 quant of "
+                    "X' [M,7168]; positions U[0,131072)",
+        "calls_per_s": len(calls) / t_hot, "calls_per_s_cold": len(calls) / t_cold,
+        "latency_us_hot": {"p50": float(np.percentile(per_hot, 50)), "p99": float(np.percentile(per_hot, 99))},
+        "latency_us_cold": {"p50": float(np.percentile(per_cold, 50)), "p99": float(np.percentile(per_cold, 99))},
+        "per_M_call_us_hot": {str(k): v for k, v in lat_hot.items()},
+        "per_M_call_us_cold": {str(k): v for k, v in lat_cold.items()},
+        "one_launch_path_calls_per_s": len(calls) / t_one, "two_call_path_calls_per_s": len(calls) / t_two,
+        "one_launch_kernel_roofline": {
+            "kernel": "indexer_q_small_kernel<bf16 in> (FP8 quant + GEMM + RoPE + Hadamard + FP4, M <= 256)",
+            "bound": "hbm", "achieved": mix_bytes / mix_k_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": mix_bytes / mix_k_s / 1e9 / PEAK_HBM_GBS,
+            "algorithmic_bytes_per_launch": mix_bytes / len(calls),
+            "avg_launch_us": mix_k_s / len(calls) * 1e6},
+        "timing": f"median of {reps} replays of one captured graph of the whole mix",
+    }
+
+
+# ---------------------------------------------------------------------------
 
 def vendor_gemm_context(M, dev, reps=100):
     """The vendor FP8 GEMM at the projection shape [M, 1536] x [8192, 1536]^T:
@@ -460,311 +564,15 @@ def vendor_gemm_context(M, dev, reps=100):
     b.record()
     torch.cuda.synchronize()
     us = a.elapsed_time(b) * 1e3 / reps
-    tflops = 2.0 * M * N_HEADS * HEAD_DIM * K_PROJ / us * 1e-6
-    print(f"[bench] vendor FP8 GEMM (hipBLASLt, per-tensor scales, bf16 out): {us:.1f} us = {tflops:.0f} TFLOP/s",
-          file=sys.stderr, flush=True)
+    tflops = fused_flops(M) / us * 1e-6
     return {"what": "torch._scaled_mm (hipBLASLt) e4m3 [M,1536] x [8192,1536]^T, per-tensor scales, bf16 out, "
                     "no epilogue; launches back to back", "avg_launch_us": us, "achieved_tflops": tflops,
             "frac": tflops / PEAK_FP8_TFLOPS}
 
 
-def prefill32k_bench(args):
-    """The long-prefill workload: the chain at 32,768 tokens (X Student-t nu=3,
-    positions 0..32767) and the standalone quantizer on X' [32768, 7168];
-    prints one JSON line in the same form as the default workload."""
-    import numpy as np
-    import torch
-
-    import fp4_quantized_prep_amd as iqp
-    import synthetic as S
-
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    stream = torch.cuda.current_stream(dev)
-    inp = S.indexer_q_inputs("prefill_m32768")
-    x, pos = inp["x"].to(dev), inp["positions"].to(dev)
-    w_cpu, wsb_cpu = S.weights()
-    w, wsb = w_cpu.to(dev), wsb_cpu.to(dev)
-    cs = iqp.rope_cos_sin_table(S.ROPE_THETA, inp["max_pos"], 64, device=dev)
-    M = x.shape[0]
-    a = torch.empty((M, K_PROJ), dtype=torch.uint8, device=dev)
-    a_s = torch.empty((M, (K_PROJ // 128 + 3) // 4), dtype=torch.int32, device=dev)
-    q = torch.empty((M, N_HEADS, HEAD_DIM // 2), dtype=torch.uint8, device=dev)
-    qs = torch.empty((M, N_HEADS, HEAD_DIM // 32), dtype=torch.uint8, device=dev)
-    for _ in range(args.warmup):
-        iqp.fp8_quant_1x128_ue8m0(x, q=a, scales=a_s)
-        iqp.indexer_q_gemm_rope_fp4(a, a_s, w, wsb, pos, cs, n_heads=N_HEADS, q_fp4=q, q_scales=qs)
-    torch.cuda.synchronize()
-    K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(K):
-        ev[i][0].record(stream)
-        iqp.fp8_quant_1x128_ue8m0(x, q=a, scales=a_s)
-        ev[i][1].record(stream)
-        iqp.indexer_q_gemm_rope_fp4(a, a_s, w, wsb, pos, cs, n_heads=N_HEADS, q_fp4=q, q_scales=qs)
-        ev[i][2].record(stream)
-    stop.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-    t_quant = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3
-    t_fused = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e-3
-    flops = 2.0 * M * (N_HEADS * HEAD_DIM) * K_PROJ
-    fused_tflops = flops / t_fused / 1e12
-    def step32k(i):
-        iqp.fp8_quant_1x128_ue8m0(x, q=a, scales=a_s)
-        iqp.indexer_q_gemm_rope_fp4(a, a_s, w, wsb, pos, cs, n_heads=N_HEADS, q_fp4=q, q_scales=qs)
-
-    t_step_graph = graph_launch_time(step32k, K, reps=1)   # the timed `value`, as in the default workload
-    print(f"[bench] chain at {M} tokens from a captured graph: {t_step_graph * 1e6:.1f} us/step",
-          file=sys.stderr, flush=True)
-    print(f"[bench] chain at {M} tokens: {total_ms / K * 1e3:.1f} us/step; quant {t_quant * 1e6:.1f} us, "
-          f"fused {t_fused * 1e6:.1f} us = {fused_tflops:.0f} TFLOP/s", file=sys.stderr, flush=True)
-    del a, a_s, q, qs
-
-    xw_cpu = S.quant_input("prefill_m32768")
-    n_sets = 2        # 2 x (470 MB in + 235 MB out): beyond the 256 MiB cache
-    xs = [xw_cpu.to(dev) for _ in range(n_sets)]
-    qq = [torch.empty((M, QUANT_K), dtype=torch.uint8, device=dev) for _ in range(n_sets)]
-    ss = [torch.empty((M, (QUANT_K // 128 + 3) // 4), dtype=torch.int32, device=dev) for _ in range(n_sets)]
-    for i in range(4):
-        iqp.fp8_quant_1x128_ue8m0(xs[i % n_sets], q=qq[i % n_sets], scales=ss[i % n_sets])
-    torch.cuda.synchronize()
-    n_q = max(20, K // 4)
-    t_qw = graph_launch_time(
-        lambda i: iqp.fp8_quant_1x128_ue8m0(xs[i % n_sets], q=qq[i % n_sets], scales=ss[i % n_sets]), n_q, reps=2)
-    qbytes = quant_bytes(M, QUANT_K)
-    q_gbs = qbytes / t_qw / 1e9
-    print(f"[bench] quantizer [{M},{QUANT_K}]: {t_qw * 1e6:.1f} us = {q_gbs:.0f} GB/s", file=sys.stderr, flush=True)
-    del xs, qq, ss
-
-    cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_tokens, inp, w_cpu, wsb_cpu)
-    result = {
-        "metric": "tokens/sec & % roofline: FP8 quant (HBM GB/s) + fused indexer-Q (MFMA util)",
-        "value": M / t_step_graph,
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
-        "ms_per_step": t_step_graph * 1e3,
-        "timing": "K whole steps captured into one HIP graph, one untimed replay, then one timed",
-        "eager_with_kernel_events": {"ms_per_step": total_ms / K, "tokens_per_s": M * K / (total_ms * 1e-3)},
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "fp8-e4m3 (fp32 accumulate), bf16 in, fp4-e2m1 out",
-        "data": "synthetic",
-        "config": {
-            "workload": "long prefill, 32768 tokens: X bf16 [32768,1536] Student-t nu=3 -> FP8 1x128 UE8M0 -> "
-                        "fused Q projection + RoPE + Hadamard-128 + FP4; plus the standalone quantizer on "
-                        "X' [32768,7168]",
-            "tokens": M, "K": K_PROJ, "heads": N_HEADS, "head_dim": HEAD_DIM, "rope_dim": 64,
-            "parallelism": "single GPU",
-        },
-        "roofline": {
-            "kernel": "indexer_q_pipe_kernel (fused GEMM + RoPE + Hadamard + FP4; launches back to back from a "
-                      "captured graph on the chain's A)",
-            "bound": "mfma",
-            "achieved": fused_tflops,
-            "peak": PEAK_FP8_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": fused_tflops / PEAK_FP8_TFLOPS,
-            "traffic": None,
-            "algorithmic_flops_per_launch": flops,
-            "avg_launch_us": t_fused * 1e6,
-        },
-        "quant_roofline": {
-            "kernel": f"fp8_quant_1x128_kernel on [{M},{QUANT_K}] (2 rotating buffer sets, launches back to back "
-                      "from a captured graph)",
-            "bound": "hbm",
-            "achieved": q_gbs,
-            "peak": PEAK_HBM_GBS,
-            "unit": "GB/s",
-            "frac": q_gbs / PEAK_HBM_GBS,
-            "algorithmic_bytes_per_launch": qbytes,
-            "avg_launch_us": t_qw * 1e6,
-            "in_chain_avg_launch_us": t_quant * 1e6,
-        },
-        "cpu_baseline": cpu,
-    }
-    print(json.dumps(result), flush=True)
-
-
-def decode_bench(args):
-    """The decode-shaped mix (see the module docstring); prints one JSON line."""
-    import numpy as np
-    import torch
-
-    import fp4_quantized_prep_amd as iqp
-    import synthetic as S
-
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    w_cpu, wsb_cpu = S.weights()
-    w, wsb = w_cpu.to(dev), wsb_cpu.to(dev)
-    max_pos = 131072
-    cs = iqp.rope_cos_sin_table(S.ROPE_THETA, max_pos, 64, device=dev)
-    calls = []
-    for c in S.decode_calls(256):
-        m = c["x"].shape[0]
-        calls.append({
-            "M": m, "x": c["x"].to(dev), "xw": c["x_wide"].to(dev), "pos": c["positions"].to(dev),
-            "a": torch.empty((m, K_PROJ), dtype=torch.uint8, device=dev),
-            "as": torch.empty((m, 3), dtype=torch.int32, device=dev),
-            "aw": torch.empty((m, QUANT_K), dtype=torch.uint8, device=dev),
-            "asw": torch.empty((m, (QUANT_K // 128 + 3) // 4), dtype=torch.int32, device=dev),
-            "q": torch.empty((m, N_HEADS, HEAD_DIM // 2), dtype=torch.uint8, device=dev),
-            "qs": torch.empty((m, N_HEADS, HEAD_DIM // 32), dtype=torch.uint8, device=dev),
-        })
-
-    def two(c, wt=(w, wsb)):
-        # two calls: quantize, then the fused projection
-        iqp.fp8_quant_1x128_ue8m0(c["x"], q=c["a"], scales=c["as"])
-        iqp.indexer_q_gemm_rope_fp4(c["a"], c["as"], wt[0], wt[1], c["pos"], cs, n_heads=N_HEADS,
-                                    q_fp4=c["q"], q_scales=c["qs"])
-        iqp.fp8_quant_1x128_ue8m0(c["xw"], q=c["aw"], scales=c["asw"])
-
-    def one(c, wt=(w, wsb)):
-        # one launch from bf16 X to FP4 Q
-        iqp.indexer_q_prep_bf16(c["x"], wt[0], wt[1], c["pos"], cs, n_heads=N_HEADS, q_fp4=c["q"],
-                                q_scales=c["qs"])
-        iqp.fp8_quant_1x128_ue8m0(c["xw"], q=c["aw"], scales=c["asw"])
-
-    def routed(c, wt=(w, wsb)):
-        # the serving policy: one launch up to ONE_LAUNCH_MAX_TOKENS tokens, two calls above
-        (one if c["M"] <= iqp.ONE_LAUNCH_MAX_TOKENS else two)(c, wt)
-
-    def graph_of(fn):
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            fn()
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            fn()
-        torch.cuda.synchronize()
-        return g
-
-    def replay_time(g, reps):
-        g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e-3 / reps    # s per replay
-
-    for c in calls:
-        two(c)
-        one(c)
-    torch.cuda.synchronize()
-    print(f"[bench] decode mix: {len(calls)} calls, M histogram "
-          f"{ {int(m): int(n) for m, n in zip(*np.unique([c['M'] for c in calls], return_counts=True))} }",
-          file=sys.stderr, flush=True)
-
-    # sustained: the whole mix as one graph, one-launch path and two-call path
-    reps = max(5, args.steps // 20)
-    t_mix = replay_time(graph_of(lambda: [routed(c) for c in calls]), reps)
-    t_mix1 = replay_time(graph_of(lambda: [one(c) for c in calls]), reps)
-    t_mix2 = replay_time(graph_of(lambda: [two(c) for c in calls]), reps)
-    calls_per_s = len(calls) / t_mix
-    print(f"[bench] mix: {calls_per_s:.0f} calls/s routed (one launch up to {iqp.ONE_LAUNCH_MAX_TOKENS} tokens), "
-          f"{len(calls) / t_mix1:.0f} one launch, {len(calls) / t_mix2:.0f} two calls", file=sys.stderr, flush=True)
-    # cold weights: call i reads weight copy i % n_w, 24 copies of 12.6 MB (302 MB, beyond the
-    # 256 MiB Infinity Cache), so every call's W streams from HBM
-    n_w = 24
-    w_sets = [(w.clone(), wsb.clone()) for _ in range(n_w)]
-    t_cold = replay_time(graph_of(lambda: [routed(c, w_sets[i % n_w]) for i, c in enumerate(calls)]), reps)
-    del w_sets
-    print(f"[bench] mix with cold weights ({n_w} rotating copies): {len(calls) / t_cold:.0f} calls/s routed",
-          file=sys.stderr, flush=True)
-
-    # per-M latency of one call (the indexer-Q preparation + the wide quantization),
-    # and of the indexer-Q kernel(s) alone
-    lat, lat2, lat_k, lat_k2 = {}, {}, {}, {}
-    n_rep = 20
-    for m in sorted({c["M"] for c in calls}):
-        c = next(c for c in calls if c["M"] == m)
-        lat[m] = replay_time(graph_of(lambda: [one(c) for _ in range(n_rep)]), 5) / n_rep * 1e6
-        lat2[m] = replay_time(graph_of(lambda: [two(c) for _ in range(n_rep)]), 5) / n_rep * 1e6
-        lat_k[m] = replay_time(graph_of(lambda: [iqp.indexer_q_prep_bf16(
-            c["x"], w, wsb, c["pos"], cs, n_heads=N_HEADS, q_fp4=c["q"], q_scales=c["qs"])
-            for _ in range(n_rep)]), 5) / n_rep * 1e6
-        lat_k2[m] = replay_time(graph_of(lambda: [iqp.indexer_q_gemm_rope_fp4(
-            c["a"], c["as"], w, wsb, c["pos"], cs, n_heads=N_HEADS, q_fp4=c["q"], q_scales=c["qs"])
-            for _ in range(n_rep)]), 5) / n_rep * 1e6
-        print(f"[bench] M={m}: call {lat[m]:.2f} us one launch ({lat_k[m]:.2f} us kernel), "
-              f"{lat2[m]:.2f} us two calls ({lat_k2[m]:.2f} us fused kernel)", file=sys.stderr, flush=True)
-    per_call = np.array([(lat if c["M"] <= iqp.ONE_LAUNCH_MAX_TOKENS else lat2)[c["M"]] for c in calls])
-    per_call1 = np.array([lat[c["M"]] for c in calls])
-    per_call2 = np.array([lat2[c["M"]] for c in calls])
-    # the one-launch kernel reads bf16 X and all of W (and its scales) once per
-    # call; W dominates its algorithmic bytes at these sizes: its bound is HBM
-    mix_bytes = float(sum(one_launch_bytes(c["M"]) for c in calls))
-    mix_k_s = float(sum(lat_k[c["M"]] for c in calls)) * 1e-6
-    mean_k = mix_k_s / len(calls) * 1e6
-    achieved = mix_bytes / mix_k_s / 1e9
-    result = {
-        "metric": "decode-shaped indexer-Q calls/s (graph replay)",
-        "value": calls_per_s,
-        "unit": "calls/s",
-        "n_gpus": 1,
-        "steps": reps,
-        "warmup": 1,
-        "ms_per_step": t_mix * 1e3,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "fp8-e4m3 (fp32 accumulate), bf16 in, fp4-e2m1 out",
-        "data": "synthetic",
-        "config": {
-            "workload": "decode mix: 256 independent calls, M uniform over {1,2,4,8,16,32,64}; each call "
-                        "X bf16 [M,1536] -> FP8 quant -> GEMM + RoPE + Hadamard + FP4 (64 heads), one launch "
-                        "up to 16 tokens and two calls above, plus a standalone FP8 quant of X' [M,7168]; "
-                        "positions U[0,131072)",
-            "calls": len(calls), "K": K_PROJ, "heads": N_HEADS, "head_dim": HEAD_DIM, "max_pos": max_pos,
-            "parallelism": "single GPU",
-        },
-        "latency_us": {"p50": float(np.percentile(per_call, 50)), "p99": float(np.percentile(per_call, 99))},
-        "cold_weights": {"calls_per_s": len(calls) / t_cold, "weight_copies": n_w,
-                         "note": "routed mix, call i reads weight copy i % 24 (302 MB, beyond the Infinity Cache)"},
-        "one_launch_path": {"calls_per_s": len(calls) / t_mix1,
-                            "p50_us": float(np.percentile(per_call1, 50)),
-                            "p99_us": float(np.percentile(per_call1, 99)),
-                            "per_M_call": {str(k): v for k, v in lat.items()},
-                            "per_M_kernel": {str(k): v for k, v in lat_k.items()}},
-        "two_call_path": {"calls_per_s": len(calls) / t_mix2,
-                          "p50_us": float(np.percentile(per_call2, 50)),
-                          "p99_us": float(np.percentile(per_call2, 99)),
-                          "per_M_call": {str(k): v for k, v in lat2.items()},
-                          "per_M_fused_kernel": {str(k): v for k, v in lat_k2.items()}},
-        "roofline": {
-            "kernel": "indexer_q_small_kernel<bf16 in> (FP8 quant + GEMM + RoPE + Hadamard + FP4, M <= 256)",
-            "bound": "hbm",
-            "achieved": achieved,
-            "peak": PEAK_HBM_GBS,
-            "unit": "GB/s",
-            "frac": achieved / PEAK_HBM_GBS,
-            "traffic": None,
-            "algorithmic_bytes_per_launch": mix_bytes / len(calls),
-            "avg_launch_us": mean_k,
-        },
-        "cpu_baseline": None,
-    }
-    print(json.dumps(result), flush=True)
-
-
 def cpu_baseline(n_tokens, inp, w_cpu, wsb_cpu):
     """Time the oracle (as it stands) on the first n tokens of the workload:
     its FP8 quantization and its whole fused chain."""
-    import numpy as np
-
     from oracle import indexer_q as IQ
     from oracle import quant_fp8 as QO
 
@@ -802,6 +610,142 @@ def cpu_baseline(n_tokens, inp, w_cpu, wsb_cpu):
     return {"value": reps * n_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{reps} pass(es) over the first {n_tokens} of the {total} tokens, whole chain (quantize + "
                       f"GEMM + RoPE + Hadamard + FP4), numpy float64, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this path has no cross-GPU step); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.replays < 5:
+        print("--replays must be at least 5", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import fp4_quantized_prep_amd as iqp
+    import synthetic as S
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] device {torch.cuda.get_device_name(dev)}; preparing inputs", file=sys.stderr, flush=True)
+    w_cpu, wsb_cpu = S.weights()
+    w, wsb = w_cpu.to(dev), wsb_cpu.to(dev)
+    K, R = args.steps, args.replays
+    wl = args.workload
+
+    if wl == "decode":
+        rec = decode_mix(iqp, S, dev, w, wsb, R)
+        print(json.dumps({"metric": "decode-shaped indexer-Q calls/s (graph replay)", "value": rec["calls_per_s"],
+                          "unit": "calls/s", "n_gpus": 1, "steps": 256, "warmup": 1,
+                          "ms_per_step": 256 / rec["calls_per_s"] * 1e3, "higher_is_better": True,
+                          "scaling": "weak", "vs_baseline": None, "data": "synthetic",
+                          "dtype": "fp8-e4m3 (fp32 accumulate), bf16 in, fp4-e2m1 out",
+                          "config": {"workload": rec["workload"]}, "decode": rec}), flush=True)
+        return
+
+    names = {"all": list(CHAINS), "prefill": [HEADLINE], "prefill128": ["c0_chain_m128"],
+             "prefill32k": ["c4_chain_m32768"]}[wl]
+    tables = {}
+    chains = {n: Chain(iqp, S, dev, w, wsb, tables, n) for n in names}
+    for c in chains.values():
+        for _ in range(args.warmup):
+            c.step()
+    torch.cuda.synchronize()
+
+    timing, order = time_chains(chains, K, R)
+    records = {}
+    for n, c in chains.items():
+        t_fused, fs = fused_alone(c, R)
+        clock = clock_during(c, iqp) if c.M >= 1024 else None
+        records[n] = chain_record(c, timing[n], t_fused, fs, clock)
+        if clock is not None:
+            records[n]["clock"] = clock
+        r = records[n]
+        print(f"[bench] {n}: {r['us_per_step']:.1f} us/step (fwd {r['forward_median_us']:.1f}, rev "
+              f"{r['reverse_median_us']:.1f}, p10 {r['step_spread']['p10_us']:.1f}, p90 "
+              f"{r['step_spread']['p90_us']:.1f}) = {r['tokens_per_s']:.3e} tokens/s; fused "
+              f"{t_fused * 1e6:.1f} us = {r['fused_kernel']['achieved']:.0f} TFLOP/s"
+              + (f" at {clock['sclk_ghz']:.2f} GHz" if clock else ""), file=sys.stderr, flush=True)
+
+    head = HEADLINE if HEADLINE in chains else names[0]
+    hc = chains[head]
+    hr = records[head]
+    extra = {}
+    if wl in ("all", "prefill"):
+        extra["in_chain_kernel_us"] = in_chain_events(hc, min(K, 100))
+        extra["eager"] = eager_chain(hc, K)
+        extra["quant_roofline"] = quant_roofline(iqp, S, dev, 4632, "quant_4632x7168", 5, R)
+        extra["quant_roofline"]["traffic"] = measured_traffic("quant")
+        print(f"[bench] quantizer [4632,7168]: {extra['quant_roofline']['avg_launch_us']:.1f} us = "
+              f"{extra['quant_roofline']['achieved']:.0f} GB/s", file=sys.stderr, flush=True)
+        extra["hbm_copy_ceiling"] = copy_ceiling(dev, R)
+    if wl in ("all", "prefill32k"):
+        q32 = quant_roofline(iqp, S, dev, 32768, "prefill_m32768", 2, R)
+        records["c4_chain_m32768"]["quant_32768x7168"] = q32
+        print(f"[bench] quantizer [32768,7168]: {q32['avg_launch_us']:.1f} us = {q32['achieved']:.0f} GB/s",
+              file=sys.stderr, flush=True)
+    if wl == "all":
+        records["c3_decode_mix"] = decode_mix(iqp, S, dev, w, wsb, R)
+        extra["epilogue_roofline"] = epilogue_roofline(iqp, S, dev, chains[HEADLINE].pos, chains[HEADLINE].cs,
+                                                       4632, R)
+        extra["weight_prep_roofline"] = weight_prep_roofline(iqp, dev, R)
+        if args.vendor_gemm:
+            extra["vendor_gemm_context"] = vendor_gemm_context(4632, dev)
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    cpu = None
+    if not args.no_cpu_baseline and head == HEADLINE:
+        cpu = cpu_baseline(args.cpu_tokens, hc.inp, w_cpu, wsb_cpu)
+
+    roof = dict(hr["fused_kernel"])
+    roof["traffic"] = measured_traffic("fused") if head == HEADLINE else None
+    roof["mfma_busy_frac_counters"] = measured_mfma_util() if head == HEADLINE else None
+    M = hc.M
+    result = {
+        "metric": "tokens/sec & % roofline: FP8 quant (HBM GB/s) + fused indexer-Q (MFMA util)",
+        "value": hr["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": timing[head]["steps_per_replay"],
+        "warmup": args.warmup,
+        "ms_per_step": hr["us_per_step"] * 1e-3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-e4m3 (fp32 accumulate), bf16 in, fp4-e2m1 out",
+        "data": "synthetic",
+        "config": {
+            "workload": f"indexer-Q chain, {M} tokens: X bf16 [{M},1536] -> FP8 1x128 UE8M0 -> "
+                        "Q = A W^T (W [8192,1536] E4M3, 128x128 UE8M0) -> RoPE(64 of 128) -> "
+                        f"Hadamard-128 -> FP4 e2m1 [{M},64,64] + UE8M0 [{M},64,4]",
+            "tokens": M, "K": K_PROJ, "heads": N_HEADS, "head_dim": HEAD_DIM, "rope_dim": 64,
+            "parallelism": "single GPU",
+        },
+        "timing": {
+            "method": f"per config, {timing[head]['steps_per_replay']} steps (4632 tokens; other configs scaled "
+                      f"to a similar replay length) captured into one HIP graph, {R} timed replays (event pair "
+                      "around each) in forward config order then again in reverse order; the value is the "
+                      "average of the two orders' median replays",
+            "order_forward": order, "replays_per_order": R,
+            "forward_median_us": hr["forward_median_us"], "reverse_median_us": hr["reverse_median_us"],
+            **{k: v for k, v in hr["step_spread"].items()},
+        },
+        "roofline": roof,
+        "chain_minus_fused_us": hr["chain_minus_fused_us"],
+        "configs": records,
+        "cpu_baseline": cpu,
+        **extra,
+        "runtime": {"hip": torch.version.hip, "torch": torch.__version__,
+                    "device": torch.cuda.get_device_name(dev)},
+    }
+    print(json.dumps(result), flush=True)
 
 
 if __name__ == "__main__":
