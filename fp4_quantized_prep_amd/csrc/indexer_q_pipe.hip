@@ -118,11 +118,23 @@ constexpr int PART1 = 7;                            // copies issued in the firs
 constexpr int S_OFF = 0;
 constexpr int W_OFF = S_OFF + NST * S_BYTES;
 constexpr int A_OFF = W_OFF + NST * W_BYTES;
-constexpr int LDS_BYTES = A_OFF + NST * A_BYTES;    // 148,992
+// split build: the K-loop tile's token positions (int64), two tiles' worth
+constexpr int P_OFF = A_OFF + NST * A_BYTES;
+constexpr int P_BYTES = TOKS * 8;
+constexpr int LDS_BYTES = P_OFF + (SPLIT ? 2 * P_BYTES : 0);   // 148,992 (split: 151,040)
 static_assert(W_OFF >= KB * (NKB - 1), "copy LDS bases must stay non-negative");
 // at a block barrier the copies of the block after next (13 per wave) may
 // still be in flight: s_waitcnt vmcnt(13)
 constexpr int WAITCNT_VM13 = (13 & 15) | (7 << 4) | (15 << 8) | ((13 >> 4) << 14);
+// Split build: RoPE rows are fetched where no copy is waited for behind them
+// (vmcnt counts in issue order, so a load queued behind copies lands only as
+// late as they do): the first sub-tile's by the MFMA role right after its
+// last barrier, the second's by the epilogue role at the start of block
+// ROPE1_BLOCK (its first sub-tile's RoPE is done by then), ahead of that
+// half-step's copies, whose barrier then leaves ROPE_LOADS more outstanding.
+constexpr int ROPE1_BLOCK = 2;
+constexpr int ROPE_LOADS = 8;                       // load_rope: 8 loads of 16 bytes
+static_assert(!(SPLIT && VAR_IL), "the split build's wait counts assume the half-split RoPE rows");
 // s_waitcnt vmcnt(n), n < 64
 constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
@@ -157,11 +169,11 @@ struct Epi {
   RopeCS rope;      // RoPE rows of the sub-tile whose phase 0 comes next
   int tlane;        // the epilogue tile's token of sub-tile 0 (sub-tile tm: + TM_STRIDE tm)
   // positions as loaded (clamped into the table where the RoPE rows are
-  // fetched, so no load is waited for before then)
-  // (the split build holds them clamped into the table as 32-bit values)
-  using pos_t = std::conditional_t<SPLIT, int32_t, int64_t>;
-  pos_t pos1;           // the epilogue tile's sub-tile 1
-  pos_t npos0, npos1;   // the K-loop tile's (its epilogue comes next)
+  // fetched, so no load is waited for before then); the split build keeps
+  // pos1 only, clamped, and reads the K-loop tile's from LDS
+  std::conditional_t<SPLIT, int32_t, int64_t> pos1;    // the epilogue tile's sub-tile 1
+  std::conditional_t<SPLIT, int32_t, int64_t> npos0;   // the K-loop tile's (its epilogue comes next)
+  int64_t npos1;
 };
 
 struct Ctx {
@@ -183,6 +195,8 @@ struct Ctx {
   int wave_lds;                  // 1 KiB per wave: this wave's part of each group of four slabs
   int words_lds;                 // 256 bytes per wave pair: its half of the scale words
   uint32_t rd_w[2][2], rd_a[2][2], rd_s;
+  rsrc_t rp;                     // split build: the K-loop tile's positions
+  int pos_lds;                   // split build: their LDS area (by tile parity)
 
   __device__ Ctx(const IndexerQArgs& p_, uint8_t* lds_, int pair) : p(p_), lds(lds_) {
     const int tid = threadIdx.x;
@@ -356,12 +370,6 @@ __device__ __forceinline__ void epi_item(Epi& es, v16f (&accp)[MAX_TM][4], int i
     // them: copies into VGPRs cannot be placed any earlier (a whole set
     // copied out at the top of the K loop would not fit beside its operands).
     if (i == 0) asm volatile("" : "+a"(accp[tm][2]), "+a"(accp[tm][3]));
-    // split build: the second sub-tile's RoPE rows are fetched here, a
-    // phase before their use (fetched during the first sub-tile's last
-    // phases they would be held beside all of its values)
-    if constexpr (SPLIT && tm == 1) {
-      if (i == 0) es.rope = load_rope<VAR_IL>(es.pos1, c.half, c.p);
-    }
     if (i < 32) {
       es.v[2 + (i >> 4)][i & 15] = accp[tm][2 + (i >> 4)][i & 15];
     } else {
@@ -507,9 +515,9 @@ constexpr int unit_item(int k) {
   return k;
 }
 // instructions of item i of phase h of sub-tile tm (the split build's roles:
-// RoPE rows fetched at the second sub-tile's first item, none in phases 10, 11)
+// no RoPE rows fetched in phases 10, 11)
 constexpr int unit_cost(int tm, int h, int i) {
-  if (h == 0) return (i < 32 ? 1 : 2) + (tm == 1 && i == 0 ? 16 : 0);
+  if (h == 0) return i < 32 ? 1 : 2;
   if (h == 1) return i < 16 ? 6 : 2;
   if (h <= 6) return 2;
   if (h <= 8) return 4;
@@ -557,7 +565,14 @@ __device__ __forceinline__ void epilogue_alone(Epi& es, v16f (&accp)[MAX_TM][4],
     for (int i = 0; i < n; ++i) epi_item<H, NTMP, true>(es, accp, i, c);
   };
 #define IQP_EPI_H(H) run(std::integral_constant<int, H>{});
-  IQP_EPI_H(0) IQP_EPI_H(1) IQP_EPI_H(2) IQP_EPI_H(3) IQP_EPI_H(4) IQP_EPI_H(5)
+  IQP_EPI_H(0) IQP_EPI_H(1)
+  // split build: the second sub-tile's RoPE rows (no copies in flight here)
+  if constexpr (SPLIT && NTMP > 1) {
+    es.rope = load_rope<VAR_IL>(es.pos1, c.half, c.p);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) asm volatile("" : "+a"(es.rope.c[g]), "+a"(es.rope.s[g]));
+  }
+  IQP_EPI_H(2) IQP_EPI_H(3) IQP_EPI_H(4) IQP_EPI_H(5)
   IQP_EPI_H(6) IQP_EPI_H(7) IQP_EPI_H(8) IQP_EPI_H(9) IQP_EPI_H(10) IQP_EPI_H(11)
   IQP_EPI_H(12) IQP_EPI_H(13) IQP_EPI_H(14) IQP_EPI_H(15) IQP_EPI_H(16) IQP_EPI_H(17)
   IQP_EPI_H(18) IQP_EPI_H(19) IQP_EPI_H(20) IQP_EPI_H(21) IQP_EPI_H(22) IQP_EPI_H(23)
@@ -666,17 +681,42 @@ __device__ __forceinline__ void k_block(Ctx& c, v16f (&acc)[MAX_TM][4], Frags& f
 #pragma unroll
   for (int tm = 0; tm < MAX_TM; ++tm) as[tm] = (int)((uint32_t)as0[tm] >> (8 * (J & 3)));
   __builtin_amdgcn_sched_barrier(0);
+  // split epilogue role: the second sub-tile's RoPE rows, ahead of this
+  // half-step's copies (see above)
+  if constexpr (ROLE == ROLE_EPI && NTMP > 1 && J == ROPE1_BLOCK) {
+    es.rope = load_rope<VAR_IL>(es.pos1, c.half, c.p);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // a block later (landed by then), held in the accumulator registers the
+  // first sub-tile has left until the second sub-tile's RoPE
+  if constexpr (ROLE == ROLE_EPI && NTMP > 1 && J == ROPE1_BLOCK + 1) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) asm volatile("" : "+a"(es.rope.c[g]), "+a"(es.rope.s[g]));
+    __builtin_amdgcn_sched_barrier(0);
+  }
   // in a chunk's first tile the prologue copied blocks 0 and 1 whole and block 2's first part
   constexpr int J2 = J + 2;
   half_step<ROLE, NTM, ST, 1, false, PART1, NCOPY, J2 % NST, (J2 >= NKB), J2 % NKB, 2 * J, NTMP, false>(
       c, acc, f0, as, ws, ws4, f1, as1, es, accp);
   if constexpr (ROLE != ROLE_EPI) __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);
   if constexpr (ROLE == ROLE_ALL) __builtin_amdgcn_s_waitcnt(WAITCNT_VM13);
-  if constexpr (ROLE == ROLE_MFMA) __builtin_amdgcn_s_waitcnt(J == 0 ? waitcnt_vm(PART1 + ACOPIES) : waitcnt_vm(ACOPIES));
+  if constexpr (ROLE == ROLE_MFMA) __builtin_amdgcn_s_waitcnt(J == 0 ? waitcnt_vm(PART1 + 1 + ACOPIES) : waitcnt_vm(ACOPIES));
   if constexpr (ROLE == ROLE_EPI)
-    __builtin_amdgcn_s_waitcnt(J == 0 ? waitcnt_vm(NCOPY - PART1 - ACOPIES) : waitcnt_vm(NCOPY - ACOPIES));
+    __builtin_amdgcn_s_waitcnt(J == 0 ? waitcnt_vm(NCOPY - PART1 - ACOPIES + (NTMP > 0 ? ROPE_LOADS : 0))
+                                      : waitcnt_vm(NCOPY - ACOPIES + (J == ROPE1_BLOCK && NTMP > 1 ? ROPE_LOADS : 0)));
   block_barrier();   // all of block j read by every wave; block j+1 has landed
   __builtin_amdgcn_sched_barrier(0);
+  // split MFMA role, last block: this wave's positions of the tile (clamped
+  // into the table; max_pos < 2^31), for the epilogue it runs next
+  if constexpr (ROLE == ROLE_MFMA && J == NKB - 1) {
+    const int64_t* pl = reinterpret_cast<const int64_t*>(c.lds + c.pos_lds) + 32 * c.th + (fresh(c.lane) & 31);
+    auto clamp = [&](int64_t v) __attribute__((always_inline)) {
+      return (int32_t)(v < 0 ? 0 : (v >= c.p.max_pos ? c.p.max_pos - 1 : v));
+    };
+    es.npos0 = clamp(pl[0]);
+    es.pos1 = clamp(pl[TM_STRIDE]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   constexpr int J3 = J + 3;
   // the split MFMA role reads no operands of the following tile (another group computes it)
   constexpr int RKH_B = (ROLE == ROLE_MFMA && J == NKB - 1) ? -1 : 0;
@@ -711,7 +751,13 @@ __device__ __forceinline__ void k_loop(Ctx& c, v16f (&acc)[MAX_TM][4], Frags& f0
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[tm][tn][r] = 0.f;
   }
+  if constexpr (ROLE == ROLE_EPI && NTMP > 0) es.rope = load_rope<VAR_IL>(es.npos0, c.half, c.p);
   if constexpr (ROLE == ROLE_MFMA) {
+    // the tile's 128 positions into LDS, 16 bytes a lane (every wave of the
+    // group issues the same copy, so that the wait counts are the group's);
+    // landed by block 1's barrier, read after block 11's
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rp, (lds_void*)(c.lds + c.pos_lds), 16,
+                                             (uint32_t)(16 * fresh(c.lane)), 0, 0, 0);
 #pragma unroll
     for (int tm = 0; tm < MAX_TM; ++tm) as0[tm] = c.read_scale<0>(tm);
 #pragma unroll
@@ -721,7 +767,6 @@ __device__ __forceinline__ void k_loop(Ctx& c, v16f (&acc)[MAX_TM][4], Frags& f0
     for (int tn = 0; tn < 4; ++tn)
       f0.w[tn] = make_v8i(c.read16<0>(false, 0, 0, 32 * tn), c.read16<0>(false, 0, 1, 32 * tn));
   }
-  if constexpr (ROLE == ROLE_EPI && NTMP > 0) es.rope = load_rope<VAR_IL>(es.npos0, c.half, c.p);
 #define IQP_KB(J) k_block<ROLE, NTM, J, NTMP, false>(c, acc, f0, f1, as0, as1, es, accp);
   IQP_KB(0) IQP_KB(1) IQP_KB(2) IQP_KB(3) IQP_KB(4) IQP_KB(5) IQP_KB(6) IQP_KB(7) IQP_KB(8) IQP_KB(9)
   if constexpr (ROLE == ROLE_ALL && NTMP == 0) es.rope = load_rope<VAR_IL>(es.npos0, c.half, c.p);
@@ -746,22 +791,13 @@ __device__ __forceinline__ void k_loop(Ctx& c, v16f (&acc)[MAX_TM][4], Frags& f0
 // from them near its end). After it: the tile becomes the epilogue's.
 __device__ __forceinline__ void tile_positions(Ctx& c, Epi& es, int64_t tbase) {
   const int64_t tl = tbase + 32 * c.th + (fresh(c.lane) & 31);
-  if constexpr (SPLIT) {
-    // clamped into [0, max_pos) once, here (max_pos < 2^31: the launcher checks)
-    auto clamp = [&](int64_t v) __attribute__((always_inline)) {
-      return (int32_t)(v < 0 ? 0 : (v >= c.p.max_pos ? c.p.max_pos - 1 : v));
-    };
-    es.npos0 = clamp(load_position(tl, c.p));
-    es.npos1 = clamp(load_position(tl + TM_STRIDE, c.p));
-  } else {
-    es.npos0 = load_position(tl, c.p);
-    es.npos1 = load_position(tl + TM_STRIDE, c.p);
-  }
+  es.npos0 = load_position(tl, c.p);
+  es.npos1 = load_position(tl + TM_STRIDE, c.p);
 }
 
 __device__ __forceinline__ void hand_over(Ctx& c, Epi& es, int64_t tbase) {
   es.tlane = (int)(tbase + 32 * c.th + (fresh(c.lane) & 31));
-  es.pos1 = es.npos1;
+  if constexpr (!SPLIT) es.pos1 = es.npos1;   // the split build set it at block 11
 }
 
 // Diagnostic build: a tile's float32 sums to dbg [M, H*128]. Sub-tile tm of
@@ -900,7 +936,11 @@ void IQP_PIPE_KERNEL(IndexerQArgs p) {
     }
     while (tile < t_end) {
       c.read_bases(fresh(c.lane));
-      tile_positions(c, es, tbase_of(tile));
+      {
+        const int64_t tb = tbase_of(tile);
+        c.rp = make_rsrc(p.positions + tb, 8 * (uint64_t)(p.M - tb));
+        c.pos_lds = P_OFF + P_BYTES * (int)(tile & 1);
+      }
       k_loop<ROLE_MFMA, MAX_TM, 0>(c, acc, f0, f1, as0, as1, es, acc);
       if constexpr (DUMP) dump_sums(acc, c, tbase_of(tile));
       hand_over(c, es, tbase_of(tile));
