@@ -19,6 +19,7 @@ typedef unsigned v4u __attribute__((ext_vector_type(4)));
 constexpr int DPP_QUAD_XOR1 = 0xB1;     // quad_perm [1,0,3,2]
 constexpr int DPP_QUAD_XOR2 = 0x4E;     // quad_perm [2,3,0,1]
 constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_ROW_MIRROR = 0x140;
 
 // maximum over each group of 8 lanes (a block)
 __device__ __forceinline__ uint32_t lanes8_max(uint32_t v) {
