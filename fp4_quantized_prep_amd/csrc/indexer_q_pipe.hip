@@ -383,7 +383,10 @@ __device__ __forceinline__ void epi_item(Epi& es, v16f (&accp)[MAX_TM][4], int i
     if (i < 16 && !VAR_IL) {       // RoPE pair (i, i + 32), i = 8 g + 4 half + s
       const int g = i >> 2, s = i & 3;
       const float x = accp[tm][0][4 * g + s], y = accp[tm][1][4 * g + s];
-      const float cc = es.rope.c[g][s], ss = es.rope.s[g][s];
+      // split build, second sub-tile: its rows sit in the first sub-tile's
+      // accumulators 0 (cosines) and 1 (sines)
+      const float cc = (SPLIT && tm == 1) ? accp[0][0][4 * g + s] : es.rope.c[g][s];
+      const float ss = (SPLIT && tm == 1) ? accp[0][1][4 * g + s] : es.rope.s[g][s];
       es.v[0][4 * g + s] = x * cc - y * ss;
       es.v[1][4 * g + s] = y * cc + x * ss;
     } else if (i < 16) {           // interleaved pair 16 tn + 4 g + 2 half + k: registers 4g + 2k, 4g + 2k + 1
@@ -555,6 +558,18 @@ __device__ __forceinline__ void epi_slot_even(Epi& es, v16f (&accp)[MAX_TM][4], 
   });
 }
 
+// split build: the second sub-tile's RoPE rows into the first sub-tile's
+// accumulators 0 (cosines) and 1 (sines), whose values its RoPE has used
+__device__ __forceinline__ void rope_into_acc(const RopeCS& r, v16f (&accp)[MAX_TM][4]) {
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      accp[0][0][4 * g + s] = r.c[g][s];
+      accp[0][1][4 * g + s] = r.s[g][s];
+    }
+}
+
 // the whole epilogue of a tile, alone (after the chunk's last K loop)
 template <int NTMP>
 __device__ __forceinline__ void epilogue_alone(Epi& es, v16f (&accp)[MAX_TM][4], const Ctx& c) {
@@ -568,9 +583,8 @@ __device__ __forceinline__ void epilogue_alone(Epi& es, v16f (&accp)[MAX_TM][4],
   IQP_EPI_H(0) IQP_EPI_H(1)
   // split build: the second sub-tile's RoPE rows (no copies in flight here)
   if constexpr (SPLIT && NTMP > 1) {
-    es.rope = load_rope<VAR_IL>(es.pos1, c.half, c.p);
-#pragma unroll
-    for (int g = 0; g < 4; ++g) asm volatile("" : "+a"(es.rope.c[g]), "+a"(es.rope.s[g]));
+    rope_into_acc(load_rope<VAR_IL>(es.pos1, c.half, c.p), accp);
+    asm volatile("" : "+a"(accp[0][0]), "+a"(accp[0][1]));
   }
   IQP_EPI_H(2) IQP_EPI_H(3) IQP_EPI_H(4) IQP_EPI_H(5)
   IQP_EPI_H(6) IQP_EPI_H(7) IQP_EPI_H(8) IQP_EPI_H(9) IQP_EPI_H(10) IQP_EPI_H(11)
@@ -683,15 +697,15 @@ __device__ __forceinline__ void k_block(Ctx& c, v16f (&acc)[MAX_TM][4], Frags& f
   __builtin_amdgcn_sched_barrier(0);
   // split epilogue role: the second sub-tile's RoPE rows, ahead of this
   // half-step's copies (see above)
+  // (held in the first sub-tile's accumulators 0 and 1, which its RoPE has
+  // read by then, so the rows take no registers of their own; pinned there
+  // a block later, once landed)
   if constexpr (ROLE == ROLE_EPI && NTMP > 1 && J == ROPE1_BLOCK) {
-    es.rope = load_rope<VAR_IL>(es.pos1, c.half, c.p);
+    rope_into_acc(load_rope<VAR_IL>(es.pos1, c.half, c.p), accp);
     __builtin_amdgcn_sched_barrier(0);
   }
-  // a block later (landed by then), held in the accumulator registers the
-  // first sub-tile has left until the second sub-tile's RoPE
   if constexpr (ROLE == ROLE_EPI && NTMP > 1 && J == ROPE1_BLOCK + 1) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) asm volatile("" : "+a"(es.rope.c[g]), "+a"(es.rope.s[g]));
+    asm volatile("" : "+a"(accp[0][0]), "+a"(accp[0][1]));
     __builtin_amdgcn_sched_barrier(0);
   }
   // in a chunk's first tile the prologue copied blocks 0 and 1 whole and block 2's first part
