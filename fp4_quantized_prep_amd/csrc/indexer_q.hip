@@ -118,9 +118,13 @@ struct Ctx {
     const int head_c = head < p.H ? head : p.H - 1;   // odd H: the missing head reads zeros, never stored
     const uint8_t* wsc = p.w_scales + (int64_t)head_c * nkb;
     wsc_lane = 0;
+    uint8_t wsc_b[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)   // all four loads in flight before the first use
+      wsc_b[b] = wsc[4 * lane + b < nkb ? 4 * lane + b : 0];
 #pragma unroll
     for (int b = 0; b < 4; ++b)
-      if (4 * lane + b < nkb) wsc_lane |= (uint32_t)wsc[4 * lane + b] << (8 * b);
+      if (4 * lane + b < nkb) wsc_lane |= (uint32_t)wsc_b[b] << (8 * b);
     wsr_row = p.w_scales + ((int64_t)head_c * HEAD_DIM + (lane & 31)) * nkb;
     wsr_tn_stride = (int64_t)32 * nkb;
     // copy i of this wave lands in rows 8 (wave + 4 i) + lane / 8, slot lane % 8,

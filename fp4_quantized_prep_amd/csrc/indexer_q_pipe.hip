@@ -183,6 +183,7 @@ struct Ctx {
   uint32_t wsc_lane;             // the head's weight-scale bytes, 4 per lane
   uint32_t wsr[4][3];            // per-row variant: the 12 bytes of W row 32 tn + lane % 32 of the head
   rsrc_t rw, ra, rs, ra_n, rs_n; // weights; activations / scale words of this and the next tile
+  rsrc_t rw_n;                   // the weights for the next tile's copies (empty past the chunk's last tile)
   // Copy addressing. A copy's row part is a lane offset (bounds-checked:
   // rows past the tokens read zeros) or, for the weights, a scalar offset per
   // slab (rows that always exist); its column part within the K block is the
@@ -209,9 +210,13 @@ struct Ctx {
     const int head_c = head < p.H ? head : p.H - 1;   // odd H: the missing head reads zeros, never stored
     const uint8_t* wsc = p.w_scales + (int64_t)head_c * NKB;
     wsc_lane = 0;
+    uint8_t wsc_b[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)   // all four loads in flight before the first use
+      wsc_b[b] = wsc[4 * lane + b < NKB ? 4 * lane + b : 0];
 #pragma unroll
     for (int b = 0; b < 4; ++b)
-      if (4 * lane + b < NKB) wsc_lane |= (uint32_t)wsc[4 * lane + b] << (8 * b);
+      if (4 * lane + b < NKB) wsc_lane |= (uint32_t)wsc_b[b] << (8 * b);
     if constexpr (VAR_ROWS) {
       // [H*128, 12] bytes, 4-byte aligned (the launcher checks): three words a row
 #pragma unroll
@@ -291,7 +296,7 @@ struct Ctx {
   __device__ __forceinline__ void copy() const {
     if constexpr (WI < WCOPIES) {
       uint8_t* d = lds_at<W_OFF + ST * W_BYTES + SLAB * NWAVES * WI - KB * J>(wave_lds);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)d, 16, vw, wrow[WI], KB * J, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(NEXT ? rw_n : rw, (lds_void*)d, 16, vw, wrow[WI], KB * J, 0);
     } else if constexpr (WI < WCOPIES + ACOPIES) {
       constexpr int i = WI - WCOPIES;
       uint8_t* d = lds_at<A_OFF + ST * A_BYTES + SLAB * NWAVES * i - KB * J>(wave_lds);
@@ -890,6 +895,9 @@ void IQP_PIPE_KERNEL(IndexerQArgs p) {
   // would have copied them)
   c.buffers(tbase_of(t_begin), c.ra, c.rs);
   c.buffers(t_begin + 1 < t_end ? tbase_of(t_begin + 1) : p.M, c.ra_n, c.rs_n);
+  // past the chunk's last tile the next-tile copies read nothing (an empty buffer returns zeros)
+  const rsrc_t rw_none = make_rsrc(p.w, 0);
+  c.rw_n = t_begin + 1 < t_end ? c.rw : rw_none;
   if (!SPLIT || ((int)threadIdx.x >> 8) == 0) {
     static_for<0, NCOPY>([&](auto w) __attribute__((always_inline)) { c.template copy<0, false, decltype(w)::value, 0>(); });
     static_for<0, NCOPY>([&](auto w) __attribute__((always_inline)) { c.template copy<1, false, decltype(w)::value, 1>(); });
@@ -923,6 +931,7 @@ void IQP_PIPE_KERNEL(IndexerQArgs p) {
     c.ra = c.ra_n;
     c.rs = c.rs_n;
     c.buffers(tile + 2 < t_end ? tbase_of(tile + 2) : p.M, c.ra_n, c.rs_n);
+    c.rw_n = tile + 2 < t_end ? c.rw : rw_none;
     ++tile;
   };
   if constexpr (!SPLIT) {
