@@ -22,6 +22,7 @@ __all__ = [
     "IqpError", "fp8_quant_1x128_ue8m0", "indexer_q_gemm_rope_fp4", "rope_cos_sin_table",
     "debug_indexer_q_f32", "debug_indexer_q_prep_bf16_f32", "debug_indexer_q_clock", "device_clock_rates",
     "indexer_q_rope_hadamard_fp4", "indexer_q_prep_bf16", "indexer_q_prep", "fp8_quant_weight_128x128_ue8m0", "abi_version", "library_path",
+    "rope_table_lanes", "rope_table_lanes_size",
     "IQP_OK", "IQP_ERR_INVALID", "IQP_ERR_UNSUPPORTED", "IQP_ERR_HIP", "ONE_LAUNCH_MAX_TOKENS",
     "IQP_ROPE_INTERLEAVED", "IQP_FP4_SCALE_OCP_FLOOR", "IQP_W_SCALES_PER_ROW",
 ]
@@ -54,6 +55,10 @@ def _load():
     lib.indexer_q_gemm_rope_fp4.restype = ctypes.c_int
     lib.indexer_q_gemm_rope_fp4_ex.argtypes = iq_args + [c_p, c_p, c_i32, c_p]
     lib.indexer_q_gemm_rope_fp4_ex.restype = ctypes.c_int
+    lib.indexer_q_gemm_rope_fp4_lanes.argtypes = iq_args[:-1] + [c_p, c_i64, c_p, c_p, c_p]
+    lib.indexer_q_gemm_rope_fp4_lanes.restype = ctypes.c_int
+    lib.iqp_rope_table_lanes.argtypes = [c_p, c_i64, c_i32, c_p, c_p]
+    lib.iqp_rope_table_lanes.restype = ctypes.c_int
     lib.iqp_debug_indexer_q_f32.argtypes = iq_args + [c_p, c_i32, c_p]
     lib.iqp_debug_indexer_q_f32.restype = ctypes.c_int
     lib.indexer_q_prep_bf16.argtypes = [c_p, c_i64, c_p, c_i64, c_p, c_i64, c_i64, c_i32, c_i32, c_i32,
@@ -74,7 +79,7 @@ def _load():
     lib.iqp_abi_version.restype = ctypes.c_int
     lib.iqp_debug_indexer_q_prep_bf16_f32.argtypes = lib.indexer_q_prep_bf16.argtypes[:-3] + [c_p, c_p]
     lib.iqp_debug_indexer_q_prep_bf16_f32.restype = ctypes.c_int
-    lib.iqp_debug_indexer_q_clock.argtypes = iq_args + [c_p, c_p, c_p, c_i64, c_p, c_p]
+    lib.iqp_debug_indexer_q_clock.argtypes = iq_args[:-1] + [c_p, c_i64] + [c_p, c_p, c_p, c_i64, c_p, c_p]
     lib.iqp_debug_indexer_q_clock.restype = ctypes.c_int
     lib.iqp_device_clock_rates.argtypes = [c_p, c_p]
     lib.iqp_device_clock_rates.restype = ctypes.c_int
@@ -254,7 +259,7 @@ def _convention_flags(rope_layout: str, scale_rule: str) -> int:
 def indexer_q_gemm_rope_fp4(a, a_scales, w, w_scales, positions, cos_sin, n_heads: int = 64,
                             head_dim: int = 128, rope_dim: int = 64, q_fp4=None, q_scales=None,
                             rope_layout: str = "half_split", scale_rule: str = "ceil",
-                            w_scale_layout: str = "tile_128x128", stream=None):
+                            w_scale_layout: str = "tile_128x128", cos_sin_lanes=None, stream=None):
     """Fused block-scaled FP8 Q projection + RoPE + Hadamard-128 + FP4 e2m1.
 
     a: E4M3 [M, K] (uint8 or float8_e4m3fn) and a_scales: the packed words from
@@ -264,6 +269,9 @@ def indexer_q_gemm_rope_fp4(a, a_scales, w, w_scales, positions, cos_sin, n_head
     [M, H, 4] UE8M0 scale bytes. rope_layout "interleaved" / scale_rule
     "ocp_floor" / w_scale_layout "row_1x128" (w_scales uint8 [H*128, K/128])
     select the convention variants (indexer_q_gemm_rope_fp4_ex).
+    cos_sin_lanes: the table's lane-ordered copy from :func:`rope_table_lanes`
+    (default conventions only; indexer_q_gemm_rope_fp4_lanes): the same
+    output, faster for prefill batches whose positions run consecutively.
     """
     if w_scale_layout not in ("tile_128x128", "row_1x128"):
         raise ValueError("w_scale_layout must be 'tile_128x128' or 'row_1x128'")
@@ -282,7 +290,16 @@ def indexer_q_gemm_rope_fp4(a, a_scales, w, w_scales, positions, cos_sin, n_head
         raise ValueError("q_fp4 and q_scales must be contiguous")
     if tuple(q_fp4.shape) != (M, n_heads, head_dim // 2) or tuple(q_scales.shape) != (M, n_heads, head_dim // 32):
         raise ValueError("q_fp4 / q_scales have the wrong shape")
-    if flags == 0:
+    if cos_sin_lanes is not None:
+        if flags != 0:
+            raise ValueError("cos_sin_lanes serves the default conventions only")
+        _require(cos_sin_lanes, "cos_sin_lanes", torch.float32, dev, 1)
+        if not cos_sin_lanes.is_contiguous() or cos_sin_lanes.numel() < rope_table_lanes_size(cos_sin.shape[0]):
+            raise ValueError("cos_sin_lanes must be the contiguous copy rope_table_lanes builds from cos_sin")
+        st = _lib.indexer_q_gemm_rope_fp4_lanes(*args[:-1], _ptr(cos_sin_lanes), args[-1], _ptr(q_fp4),
+                                                _ptr(q_scales), _stream(a, stream))
+        _check(st, "indexer_q_gemm_rope_fp4_lanes")
+    elif flags == 0:
         st = _lib.indexer_q_gemm_rope_fp4(*args, _ptr(q_fp4), _ptr(q_scales), _stream(a, stream))
         _check(st, "indexer_q_gemm_rope_fp4")
     else:
@@ -362,6 +379,33 @@ def rope_cos_sin_table(theta: float, max_pos: int, rope_dim: int = 64, device=No
         raise ValueError("out must be a contiguous [max_pos, rope_dim] float32 tensor")
     st = _lib.iqp_rope_cos_sin_table(float(theta), max_pos, rope_dim, _ptr(out), _stream(out, stream))
     _check(st, "iqp_rope_cos_sin_table")
+    return out
+
+
+def rope_table_lanes_size(max_pos: int) -> int:
+    """float32 elements of the lane-ordered copy of a [max_pos, 64] table."""
+    return (max_pos + 31) // 32 * 2048
+
+
+@_on_stream
+def rope_table_lanes(cos_sin, out=None, stream=None):
+    """The lane-ordered copy of a float32 [max_pos, 64] RoPE table that
+    :func:`indexer_q_gemm_rope_fp4` takes as ``cos_sin_lanes`` (the same
+    values rearranged, iqp_rope_table_lanes): a 1-D float32 tensor of
+    :func:`rope_table_lanes_size` elements. Build it once per table."""
+    dev = cos_sin.device
+    _require(cos_sin, "cos_sin", torch.float32, dev, 2)
+    if not cos_sin.is_contiguous():
+        raise ValueError("cos_sin must be contiguous")
+    max_pos, rope_dim = cos_sin.shape
+    n = rope_table_lanes_size(max_pos)
+    if out is None:
+        out = torch.empty((n,), dtype=torch.float32, device=dev)
+    _require(out, "out", torch.float32, dev, 1)
+    if not out.is_contiguous() or out.numel() != n:
+        raise ValueError(f"out must be a contiguous float32 tensor of {n} elements")
+    st = _lib.iqp_rope_table_lanes(_ptr(cos_sin), max_pos, rope_dim, _ptr(out), _stream(cos_sin, stream))
+    _check(st, "iqp_rope_table_lanes")
     return out
 
 
@@ -445,9 +489,10 @@ def debug_indexer_q_prep_bf16_f32(x, w, w_scales, positions, cos_sin, n_heads: i
 
 @_on_stream
 def debug_indexer_q_clock(a, a_scales, w, w_scales, positions, cos_sin, n_heads: int = 64, head_dim: int = 128,
-                          rope_dim: int = 64, q_fp4=None, q_scales=None, stamps=None, stream=None):
+                          rope_dim: int = 64, q_fp4=None, q_scales=None, stamps=None, cos_sin_lanes=None,
+                          stream=None):
     """:func:`indexer_q_gemm_rope_fp4` from the clock-stamp build of its
-    split-role kernel. Returns ``(q_fp4, q_scales, stamps)`` with stamps an
+    split-role kernel (the build reading ``cos_sin_lanes`` when that is given). Returns ``(q_fp4, q_scales, stamps)`` with stamps an
     int64 [workgroups, 4] device tensor (shader clock counter at start, end;
     constant-rate counter at start, end; all 0 for a workgroup with no
     tokens). Raises IqpError (IQP_ERR_UNSUPPORTED) where the call would not
@@ -469,8 +514,12 @@ def debug_indexer_q_clock(a, a_scales, w, w_scales, positions, cos_sin, n_heads:
     if not stamps.is_contiguous():
         raise ValueError("stamps must be contiguous")
     nwg = ctypes.c_int64(0)
-    st = _lib.iqp_debug_indexer_q_clock(*args, _ptr(q_fp4), _ptr(q_scales), _ptr(stamps), stamps.numel(),
-                                        ctypes.byref(nwg), _stream(a, stream))
+    if cos_sin_lanes is not None:
+        _require(cos_sin_lanes, "cos_sin_lanes", torch.float32, dev, 1)
+        if not cos_sin_lanes.is_contiguous() or cos_sin_lanes.numel() < rope_table_lanes_size(cos_sin.shape[0]):
+            raise ValueError("cos_sin_lanes must be the contiguous copy rope_table_lanes builds from cos_sin")
+    st = _lib.iqp_debug_indexer_q_clock(*args[:-1], _ptr(cos_sin_lanes), args[-1], _ptr(q_fp4), _ptr(q_scales),
+                                        _ptr(stamps), stamps.numel(), ctypes.byref(nwg), _stream(a, stream))
     _check(st, "iqp_debug_indexer_q_clock")
     return q_fp4, q_scales, stamps[: 4 * nwg.value].view(nwg.value, 4)
 
@@ -484,16 +533,18 @@ def device_clock_rates():
 
 @_on_stream
 def indexer_q_prep(x, w, w_scales, positions, cos_sin, n_heads: int = 64, rope_layout: str = "half_split",
-                   scale_rule: str = "ceil", w_scale_layout: str = "tile_128x128", stream=None):
+                   scale_rule: str = "ceil", w_scale_layout: str = "tile_128x128", cos_sin_lanes=None,
+                   stream=None):
     """The whole indexer-Q preparation for a bf16 [M, K] activation batch:
     up to ONE_LAUNCH_MAX_TOKENS tokens at K = 1536 the one-launch call, else
     FP8 quantization then the fused projection / RoPE / Hadamard / FP4 call,
     both on one stream. Returns ``(q_fp4, q_scales)``; the paths give the same
-    bytes. The convention arguments are those of :func:`indexer_q_gemm_rope_fp4`."""
+    bytes. The convention arguments and ``cos_sin_lanes`` are those of
+    :func:`indexer_q_gemm_rope_fp4` (the one-launch call reads the table)."""
     conv = dict(rope_layout=rope_layout, scale_rule=scale_rule, w_scale_layout=w_scale_layout)
     if (1 <= x.shape[0] <= ONE_LAUNCH_MAX_TOKENS and x.dim() == 2 and x.shape[1] == 1536
             and x.data_ptr() % 16 == 0 and x.stride(0) % 8 == 0 and w_scales.data_ptr() % 4 == 0):
         return indexer_q_prep_bf16(x, w, w_scales, positions, cos_sin, n_heads=n_heads, stream=stream, **conv)
     a, a_scales = fp8_quant_1x128_ue8m0(x, stream=stream)
     return indexer_q_gemm_rope_fp4(a, a_scales, w, w_scales, positions, cos_sin, n_heads=n_heads,
-                                   stream=stream, **conv)
+                                   cos_sin_lanes=cos_sin_lanes, stream=stream, **conv)

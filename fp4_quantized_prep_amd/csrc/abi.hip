@@ -178,6 +178,26 @@ int indexer_q_gemm_rope_fp4_ex(const void* a, int64_t lda, const int32_t* a_scal
   return from_hip(iqp::launch_indexer_q_variant(p, flags, static_cast<hipStream_t>(stream)));
 }
 
+int indexer_q_gemm_rope_fp4_lanes(const void* a, int64_t lda, const int32_t* a_scales, int64_t as_stride_m,
+                                  int64_t as_stride_w, const void* w, int64_t ldw, const uint8_t* w_scales,
+                                  int64_t M, int64_t K, int32_t H, int32_t D, int32_t rope_dim,
+                                  const int64_t* positions, const float* cos_sin, const float* cos_sin_lanes,
+                                  int64_t max_pos, uint8_t* q_fp4, uint8_t* q_scales, void* stream) {
+  int st = check_indexer_q_args(a, lda, a_scales, as_stride_m, as_stride_w, w, ldw, w_scales, M, K,
+                                H, D, rope_dim, positions, cos_sin, max_pos, q_fp4, q_scales);
+  if (st != IQP_OK || M == 0) return st;
+  if (!cos_sin_lanes) return IQP_ERR_INVALID;
+  if (!aligned(q_fp4, 16) || !aligned(q_scales, 4) || !aligned(cos_sin_lanes, 16)) return IQP_ERR_UNSUPPORTED;
+  st = device_status();
+  if (st != IQP_OK) return st;
+  iqp::IndexerQArgs p = make_args(a, lda, a_scales, as_stride_m, as_stride_w, w, ldw, w_scales, M,
+                                  K, H, positions, cos_sin, max_pos);
+  p.cos_sin_lanes = cos_sin_lanes;
+  p.q_fp4 = q_fp4;
+  p.q_scales = q_scales;
+  return from_hip(iqp::launch_indexer_q(p, -1, static_cast<hipStream_t>(stream)));
+}
+
 int indexer_q_prep_bf16(const void* x, int64_t ldx, const void* w, int64_t ldw, const uint8_t* w_scales,
                         int64_t M, int64_t K, int32_t H, int32_t D, int32_t rope_dim,
                         const int64_t* positions, const float* cos_sin, int64_t max_pos,
@@ -234,9 +254,9 @@ int iqp_debug_indexer_q_f32(const void* a, int64_t lda, const int32_t* a_scales,
 int iqp_debug_indexer_q_clock(const void* a, int64_t lda, const int32_t* a_scales, int64_t as_stride_m,
                               int64_t as_stride_w, const void* w, int64_t ldw, const uint8_t* w_scales,
                               int64_t M, int64_t K, int32_t H, int32_t D, int32_t rope_dim,
-                              const int64_t* positions, const float* cos_sin, int64_t max_pos,
-                              uint8_t* q_fp4, uint8_t* q_scales, uint64_t* stamps, int64_t stamp_capacity,
-                              int64_t* n_workgroups, void* stream) {
+                              const int64_t* positions, const float* cos_sin, const float* cos_sin_lanes,
+                              int64_t max_pos, uint8_t* q_fp4, uint8_t* q_scales, uint64_t* stamps,
+                              int64_t stamp_capacity, int64_t* n_workgroups, void* stream) {
   if (!n_workgroups) return IQP_ERR_INVALID;
   *n_workgroups = 0;
   if (stamp_capacity < 0) return IQP_ERR_INVALID;
@@ -245,11 +265,13 @@ int iqp_debug_indexer_q_clock(const void* a, int64_t lda, const int32_t* a_scale
   if (st != IQP_OK) return st;
   if (M == 0) return IQP_ERR_UNSUPPORTED;
   if (!stamps) return IQP_ERR_INVALID;
-  if (!aligned(q_fp4, 16) || !aligned(q_scales, 4) || !aligned(stamps, 16)) return IQP_ERR_UNSUPPORTED;
+  if (!aligned(q_fp4, 16) || !aligned(q_scales, 4) || !aligned(stamps, 16) || !aligned(cos_sin_lanes, 16))
+    return IQP_ERR_UNSUPPORTED;
   st = device_status();
   if (st != IQP_OK) return st;
   iqp::IndexerQArgs p = make_args(a, lda, a_scales, as_stride_m, as_stride_w, w, ldw, w_scales, M,
                                   K, H, positions, cos_sin, max_pos);
+  p.cos_sin_lanes = cos_sin_lanes;
   p.q_fp4 = q_fp4;
   p.q_scales = q_scales;
   p.dbg = reinterpret_cast<float*>(stamps);
@@ -320,6 +342,17 @@ int iqp_rope_cos_sin_table(double theta, int64_t max_pos, int32_t rope_dim, floa
   if (st != IQP_OK) return st;
   return from_hip(iqp::launch_rope_table(theta, max_pos, rope_dim, cos_sin,
                                          static_cast<hipStream_t>(stream)));
+}
+
+int iqp_rope_table_lanes(const float* cos_sin, int64_t max_pos, int32_t rope_dim, float* out, void* stream) {
+  if (max_pos < 0 || rope_dim < 0) return IQP_ERR_INVALID;
+  if (max_pos == 0) return IQP_OK;
+  if (!cos_sin || !out) return IQP_ERR_INVALID;
+  if (rope_dim != 64) return IQP_ERR_UNSUPPORTED;
+  if (!aligned(cos_sin, 16) || !aligned(out, 16)) return IQP_ERR_UNSUPPORTED;
+  const int st = device_status();
+  if (st != IQP_OK) return st;
+  return from_hip(iqp::launch_rope_table_lanes(cos_sin, max_pos, out, static_cast<hipStream_t>(stream)));
 }
 
 const char* iqp_status_string(int status) {

@@ -556,7 +556,7 @@ hipError_t launch_indexer_q_clock(const IndexerQArgs& a_in, int64_t stamp_capaci
   if (a.M < SPLIT_MIN_TOKENS || !indexer_q_split_supported(a)) return hipErrorNotSupported;
   *workgroups = (int64_t)((a.H + 1) / 2) * a.chunks;
   if (stamp_capacity < 4 * *workgroups) return hipErrorInvalidValue;
-  return launch_indexer_q_split_clock(a, stream);
+  return a.cos_sin_lanes ? launch_indexer_q_split_lanes_clock(a, stream) : launch_indexer_q_split_clock(a, stream);
 }
 
 hipError_t launch_indexer_q_small_bf16_variant(const IndexerQArgs& a, int variant, hipStream_t stream) {
@@ -611,7 +611,8 @@ hipError_t launch_indexer_q(const IndexerQArgs& a_in, int stage, hipStream_t str
     if (!pipe_args(a_in, a)) return hipErrorInvalidValue;
     // from SPLIT_MIN_TOKENS on, the split-role build: its epilogue runs in
     // its own waves, which pays once most workgroups hold two tiles or more
-    if (a.M >= SPLIT_MIN_TOKENS && indexer_q_split_supported(a)) return launch_indexer_q_split(a, stream);
+    if (a.M >= SPLIT_MIN_TOKENS && indexer_q_split_supported(a))
+      return a.cos_sin_lanes ? launch_indexer_q_split_lanes(a, stream) : launch_indexer_q_split(a, stream);
     return launch_indexer_q_pipe(a, stream);
   }
   return launch_kernel(a_in, stage, stream);

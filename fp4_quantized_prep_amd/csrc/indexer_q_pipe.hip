@@ -77,6 +77,11 @@
 #ifndef IQP_PIPE_DUMP
 #define IQP_PIPE_DUMP 0
 #endif
+// Split build reading the RoPE rows from the table's lane-ordered copy
+// (args.cos_sin_lanes, rope_table.hip): IQP_PIPE_LANES 1.
+#ifndef IQP_PIPE_LANES
+#define IQP_PIPE_LANES 0
+#endif
 #ifndef IQP_PIPE_STAMP
 #define IQP_PIPE_STAMP 0
 #endif
@@ -92,6 +97,8 @@ constexpr bool VAR_ROWS = (IQP_PIPE_VARIANT & 4) != 0;
 constexpr bool SPLIT = IQP_PIPE_SPLIT != 0;
 constexpr bool DUMP = IQP_PIPE_DUMP != 0;
 constexpr bool STAMP = IQP_PIPE_STAMP != 0;
+constexpr bool LANES = IQP_PIPE_LANES != 0;
+static_assert(!LANES || (SPLIT && IQP_PIPE_VARIANT == 0 && !DUMP), "the lane-ordered table: split FP4 build only");
 static_assert(IQP_PIPE_VARIANT == 0 || !(DUMP || STAMP), "diagnostic builds of the default configuration only");
 constexpr int NWAVES = 4;                           // waves of one role (one per SIMD)
 constexpr int NTHREADS = (SPLIT ? 2 : 1) * NWAVES * 64;
@@ -563,6 +570,25 @@ __device__ __forceinline__ void epi_slot_even(Epi& es, v16f (&accp)[MAX_TM][4], 
   });
 }
 
+// split build: the RoPE rows of a position clamped into the table, from the
+// table or (LANES) its lane-ordered copy, where load L of position p, half h
+// sits at float 2048 (p / 32) + 256 L + 4 (2 (p % 32) + h): for a sub-tile of
+// consecutive positions each load reads one 1 KiB segment instead of 32 rows
+__device__ __forceinline__ RopeCS rope_rows(int pos, const Ctx& c) {
+  if constexpr (LANES) {
+    const float* tl = c.p.cos_sin_lanes + (int64_t)(pos >> 5) * 2048 + 4 * (2 * (pos & 31) + c.half);
+    RopeCS r;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      r.c[g] = *reinterpret_cast<const v4f*>(tl + 256 * (2 * g));
+      r.s[g] = *reinterpret_cast<const v4f*>(tl + 256 * (2 * g + 1));
+    }
+    return r;
+  } else {
+    return load_rope<VAR_IL>(pos, c.half, c.p);
+  }
+}
+
 // split build: the second sub-tile's RoPE rows into the first sub-tile's
 // accumulators 0 (cosines) and 1 (sines), whose values its RoPE has used
 __device__ __forceinline__ void rope_into_acc(const RopeCS& r, v16f (&accp)[MAX_TM][4]) {
@@ -588,7 +614,7 @@ __device__ __forceinline__ void epilogue_alone(Epi& es, v16f (&accp)[MAX_TM][4],
   IQP_EPI_H(0) IQP_EPI_H(1)
   // split build: the second sub-tile's RoPE rows (no copies in flight here)
   if constexpr (SPLIT && NTMP > 1) {
-    rope_into_acc(load_rope<VAR_IL>(es.pos1, c.half, c.p), accp);
+    rope_into_acc(rope_rows(es.pos1, c), accp);
     asm volatile("" : "+a"(accp[0][0]), "+a"(accp[0][1]));
   }
   IQP_EPI_H(2) IQP_EPI_H(3) IQP_EPI_H(4) IQP_EPI_H(5)
@@ -706,7 +732,7 @@ __device__ __forceinline__ void k_block(Ctx& c, v16f (&acc)[MAX_TM][4], Frags& f
   // read by then, so the rows take no registers of their own; pinned there
   // a block later, once landed)
   if constexpr (ROLE == ROLE_EPI && NTMP > 1 && J == ROPE1_BLOCK) {
-    rope_into_acc(load_rope<VAR_IL>(es.pos1, c.half, c.p), accp);
+    rope_into_acc(rope_rows(es.pos1, c), accp);
     __builtin_amdgcn_sched_barrier(0);
   }
   if constexpr (ROLE == ROLE_EPI && NTMP > 1 && J == ROPE1_BLOCK + 1) {
@@ -770,7 +796,7 @@ __device__ __forceinline__ void k_loop(Ctx& c, v16f (&acc)[MAX_TM][4], Frags& f0
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[tm][tn][r] = 0.f;
   }
-  if constexpr (ROLE == ROLE_EPI && NTMP > 0) es.rope = load_rope<VAR_IL>(es.npos0, c.half, c.p);
+  if constexpr (ROLE == ROLE_EPI && NTMP > 0) es.rope = rope_rows(es.npos0, c);
   if constexpr (ROLE == ROLE_MFMA) {
     // the tile's 128 positions into LDS, 16 bytes a lane (every wave of the
     // group issues the same copy, so that the wait counts are the group's);
@@ -973,7 +999,7 @@ void IQP_PIPE_KERNEL(IndexerQArgs p) {
         k_loop<ROLE_EPI, MAX_TM, DUMP ? 0 : MAX_TM>(c, acc, f0, f1, as0, as1, es, acc);
         advance();
       } else if constexpr (!DUMP) {
-        es.rope = load_rope<VAR_IL>(es.npos0, c.half, c.p);
+        es.rope = rope_rows(es.npos0, c);
         epilogue_alone<MAX_TM>(es, acc, c);
       }
     }
@@ -993,7 +1019,7 @@ bool indexer_q_pipe_supported(const IndexerQArgs& a) {
   return a.nkb == pipe::NKB && a.M <= 0x7FFFFFFF - 2 * pipe::TOKS;
 }
 #endif
-#if IQP_PIPE_VARIANT == 0 && IQP_PIPE_SPLIT && !IQP_PIPE_DUMP && !IQP_PIPE_STAMP
+#if IQP_PIPE_VARIANT == 0 && IQP_PIPE_SPLIT && !IQP_PIPE_DUMP && !IQP_PIPE_STAMP && !IQP_PIPE_LANES
 // as the pipelined kernel, with table positions held in 32-bit registers
 bool indexer_q_split_supported(const IndexerQArgs& a) {
   return a.nkb == pipe::NKB && a.M <= 0x7FFFFFFF - 2 * pipe::TOKS && a.max_pos <= 0x7FFFFFFF;

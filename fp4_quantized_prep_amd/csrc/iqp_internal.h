@@ -21,6 +21,8 @@ struct IndexerQArgs {
   const int64_t* positions;      // [M]
   const float* cos_sin;          // [max_pos, 64]
   int64_t max_pos;
+  const float* cos_sin_lanes;    // null, or the table's lane-ordered copy (launch_rope_table_lanes),
+                                 // which the split-role kernel then reads instead of cos_sin
   uint8_t* q_fp4;                // [M, H, 64]
   uint8_t* q_scales;             // [M, H, 4]
   float* dbg;                    // [M, H*128] for the diagnostic stages
@@ -71,6 +73,8 @@ hipError_t launch_indexer_q_pipe_v7(const IndexerQArgs& args, hipStream_t stream
 // pipelined kernel's shapes and arguments, table positions below 2^31
 bool indexer_q_split_supported(const IndexerQArgs& args);
 hipError_t launch_indexer_q_split(const IndexerQArgs& args, hipStream_t stream);
+// the same kernel reading the RoPE rows from args.cos_sin_lanes (indexer_q_split_lanes.hip)
+hipError_t launch_indexer_q_split_lanes(const IndexerQArgs& args, hipStream_t stream);
 
 // diagnostic builds: the float32 GEMM sums (Q before RoPE) of the pipelined,
 // split-role and small-batch kernels' K loops in args.dbg [M, H*128]; the
@@ -84,6 +88,8 @@ hipError_t launch_indexer_q_small_dump(const IndexerQArgs& args, hipStream_t str
 // (s_memtime start, end; s_memrealtime start, end; zeros for a workgroup with
 // no tiles); args.chunks set
 hipError_t launch_indexer_q_split_clock(const IndexerQArgs& args, hipStream_t stream);
+// the same stamps from the build reading args.cos_sin_lanes (indexer_q_split_lanes_clock.hip)
+hipError_t launch_indexer_q_split_lanes_clock(const IndexerQArgs& args, hipStream_t stream);
 
 // the small-batch FP4-output kernel (indexer_q_small.hip): K = 1536, 1 to 256
 // tokens, weight scales 4-byte aligned
@@ -130,5 +136,8 @@ int cu_count();
 
 hipError_t launch_rope_table(double theta, int64_t max_pos, int32_t rope_dim,
                              float* cos_sin, hipStream_t stream);
+// the lane-ordered copy of a [max_pos, 64] table: ceil(max_pos / 32) * 2048 floats
+// (layout in rope_table.hip)
+hipError_t launch_rope_table_lanes(const float* cos_sin, int64_t max_pos, float* out, hipStream_t stream);
 
 }  // namespace iqp

@@ -20,6 +20,9 @@
  *   5. fp8_quant_weight_128x128_ue8m0   the weights' E4M3 codes and per-tile
  *      scales that calls 2 and 4 take (weight preparation, off the
  *      per-token path).
+ *   6. iqp_rope_table_lanes   a RoPE table rearranged for the prefill kernel's
+ *      16-byte loads (built once per table); indexer_q_gemm_rope_fp4_lanes
+ *      is call 2 reading it.
  *
  * Conventions shared by every entry point:
  *
@@ -58,7 +61,7 @@ extern "C" {
 #define IQP_ERR_UNSUPPORTED 2  /* well formed but outside the contract (K % 128, alignment, head shape, device): use another path */
 #define IQP_ERR_HIP         3  /* a HIP runtime call or kernel launch failed */
 
-#define IQP_ABI_VERSION     1
+#define IQP_ABI_VERSION     2
 
 /* Convention flags of indexer_q_gemm_rope_fp4_ex, indexer_q_prep_bf16_ex and
  * indexer_q_rope_hadamard_fp4 (0: the defaults of indexer_q_gemm_rope_fp4).
@@ -197,6 +200,38 @@ int indexer_q_gemm_rope_fp4_ex(const void* a, int64_t lda,
                                int32_t flags, void* stream);
 
 /*
+ * indexer_q_gemm_rope_fp4_lanes — indexer_q_gemm_rope_fp4 (default
+ * conventions) that takes, beside the table, its lane-ordered copy from
+ * iqp_rope_table_lanes (built once per table, like the weights).
+ *
+ * The same pages and the same computation: RoPE on the indexer Q with a
+ * cos/sin table (tokenspeed PR "perf(deepseek-v4): accelerate indexer Q and
+ * packed FP8 quantization", Summary; TensorRT-LLM PR "Fuse DeepSeek-V4
+ * Indexer Q projection with CuTe DSL", sequence diagram). The output is
+ * byte for byte that of indexer_q_gemm_rope_fp4 with the same arguments:
+ * where that call runs the split-role K = 1536 kernel (1024 tokens and
+ * more) the rows are read from cos_sin_lanes, elsewhere from cos_sin. The
+ * copy pays where a 32-token sub-tile's positions run consecutively (prefill;
+ * 16-byte loads then read whole 1 KiB segments instead of gathering 32 rows);
+ * for scattered positions it is somewhat slower than the table itself.
+ *
+ *   cos_sin_lanes  float32, ceil(max_pos / 32) * 2048 elements, 16-byte
+ *                  aligned, filled by iqp_rope_table_lanes from this cos_sin
+ *                  and max_pos (any other content gives undefined output);
+ *                  NULL: IQP_ERR_INVALID.
+ * Every other argument, layout and error is that of indexer_q_gemm_rope_fp4.
+ */
+int indexer_q_gemm_rope_fp4_lanes(const void* a, int64_t lda,
+                                  const int32_t* a_scales, int64_t as_stride_m, int64_t as_stride_w,
+                                  const void* w, int64_t ldw,
+                                  const uint8_t* w_scales,
+                                  int64_t M, int64_t K, int32_t H, int32_t D, int32_t rope_dim,
+                                  const int64_t* positions,
+                                  const float* cos_sin, const float* cos_sin_lanes, int64_t max_pos,
+                                  uint8_t* q_fp4, uint8_t* q_scales,
+                                  void* stream);
+
+/*
  * indexer_q_prep_bf16 — the whole indexer-Q preparation in one launch for
  * decode-sized batches: bf16 activations in, packed FP4 Q and scales out.
  *
@@ -323,6 +358,26 @@ int iqp_rope_cos_sin_table(double theta, int64_t max_pos, int32_t rope_dim,
                            float* cos_sin, void* stream);
 
 /*
+ * iqp_rope_table_lanes — the lane-ordered copy of a RoPE table that
+ * indexer_q_gemm_rope_fp4_lanes reads (the same values, rearranged; built
+ * once per table). Element k = 2048 b + 256 L + 4 (2 r + h) + e holds
+ *   cos_sin[32 b + r, 32 (L % 2) + 8 (L / 2) + 4 h + e]
+ * for 0 <= L < 8, 0 <= r < 32, h < 2, e < 4 where 32 b + r < max_pos, and 0.0
+ * past max_pos: block b holds positions 32 b .. 32 b + 31, each 16-byte
+ * piece the load one kernel lane makes. (tokenspeed PR "perf(deepseek-v4):
+ * accelerate indexer Q and packed FP8 quantization", Summary: RoPE on the
+ * indexer Q; the layout is this library's.)
+ *
+ *   cos_sin  float32 [max_pos, rope_dim], 16-byte aligned; rope_dim must be
+ *            64 (else IQP_ERR_UNSUPPORTED).
+ *   out      float32, ceil(max_pos / 32) * 2048 elements, 16-byte aligned;
+ *            must not overlap cos_sin.
+ *   max_pos >= 0 (0: no-op).
+ */
+int iqp_rope_table_lanes(const float* cos_sin, int64_t max_pos, int32_t rope_dim,
+                         float* out, void* stream);
+
+/*
  * iqp_debug_indexer_q_f32 — diagnostic twin of indexer_q_gemm_rope_fp4 for
  * parity testing of its stages (TensorRT-LLM PR "Fuse DeepSeek-V4 Indexer Q
  * projection with CuTe DSL", sequence diagram: the GEMM result feeds the
@@ -369,6 +424,10 @@ int iqp_debug_indexer_q_prep_bf16_f32(const void* x, int64_t ldx, const void* w,
  * clock). Supported where the call runs the split-role kernel (K = 1536,
  * 1024 tokens or more); elsewhere IQP_ERR_UNSUPPORTED with nothing enqueued.
  *
+ *   cos_sin_lanes   NULL (the build that reads cos_sin), or the table's
+ *                   lane-ordered copy as indexer_q_gemm_rope_fp4_lanes takes
+ *                   it (the build that reads that; 16-byte aligned).
+ *
  *   stamps          uint64 [4 * workgroups], 16-byte aligned: for workgroup
  *                   g, stamps[4g], [4g+1] = the shader clock counter
  *                   (s_memtime) at its start and end, [4g+2], [4g+3] = the
@@ -389,7 +448,7 @@ int iqp_debug_indexer_q_clock(const void* a, int64_t lda,
                               const uint8_t* w_scales,
                               int64_t M, int64_t K, int32_t H, int32_t D, int32_t rope_dim,
                               const int64_t* positions,
-                              const float* cos_sin, int64_t max_pos,
+                              const float* cos_sin, const float* cos_sin_lanes, int64_t max_pos,
                               uint8_t* q_fp4, uint8_t* q_scales,
                               uint64_t* stamps, int64_t stamp_capacity, int64_t* n_workgroups,
                               void* stream);

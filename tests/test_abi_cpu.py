@@ -27,7 +27,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     assert {"fp8_quant_1x128_ue8m0", "indexer_q_gemm_rope_fp4", "indexer_q_rope_hadamard_fp4",
             "indexer_q_prep_bf16", "fp8_quant_weight_128x128_ue8m0", "iqp_status_string",
-            "iqp_abi_version"} <= set(names)
+            "iqp_abi_version", "iqp_rope_table_lanes", "indexer_q_gemm_rope_fp4_lanes"} <= set(names)
 
 
 def test_library_exports_every_declared_symbol(iqp):
@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(iqp):
 
 
 def test_version_and_status_strings(iqp):
-    assert iqp.abi_version() == 1
+    assert iqp.abi_version() == 2
     for st in range(4):
         assert iqp._lib.iqp_status_string(st)
     assert b"unknown" in iqp._lib.iqp_status_string(99)
@@ -130,6 +130,31 @@ def test_debug_and_table_argument_checks(iqp):
     assert lib.iqp_rope_cos_sin_table(-1.0, 10, 64, P(16), None) == iqp.IQP_ERR_INVALID
     assert lib.iqp_rope_cos_sin_table(10000.0, 10, 64, P(0), None) == iqp.IQP_ERR_INVALID
     assert lib.iqp_rope_cos_sin_table(10000.0, 0, 64, P(0), None) == iqp.IQP_OK
+
+
+def fused_lanes(iqp, M=4, K=256, H=2, D=128, rd=64, lda=256, cs=16, lanes=16, q=16):
+    return iqp._lib.indexer_q_gemm_rope_fp4_lanes(P(16), lda, P(16), 1, 1, P(16), 256, P(16), M, K, H, D, rd,
+                                                  P(16), P(cs), P(lanes), 10, P(q), P(16), None)
+
+
+def test_lane_table_argument_checks(iqp):
+    lib, inv, uns = iqp._lib, iqp.IQP_ERR_INVALID, iqp.IQP_ERR_UNSUPPORTED
+    assert lib.iqp_rope_table_lanes(P(16), -1, 64, P(16), None) == inv
+    assert lib.iqp_rope_table_lanes(P(16), 10, -1, P(16), None) == inv
+    assert lib.iqp_rope_table_lanes(P(0), 10, 64, P(16), None) == inv
+    assert lib.iqp_rope_table_lanes(P(16), 10, 64, P(0), None) == inv
+    assert lib.iqp_rope_table_lanes(P(16), 10, 32, P(16), None) == uns   # the copy is laid out for 64 columns
+    assert lib.iqp_rope_table_lanes(P(8), 10, 64, P(16), None) == uns
+    assert lib.iqp_rope_table_lanes(P(16), 10, 64, P(24), None) == uns
+    assert lib.iqp_rope_table_lanes(P(0), 0, 64, P(0), None) == iqp.IQP_OK   # empty table: no-op
+    assert fused_lanes(iqp, lanes=0) == inv
+    assert fused_lanes(iqp, lanes=8) == uns
+    assert fused_lanes(iqp, M=-3) == inv                       # the base call's checks still apply
+    assert fused_lanes(iqp, cs=0) == inv
+    assert fused_lanes(iqp, lda=128) == inv
+    assert fused_lanes(iqp, D=64) == uns
+    assert fused_lanes(iqp, q=20) == uns
+    assert fused_lanes(iqp, M=0, lanes=0) == iqp.IQP_OK        # M = 0: no-op
 
 
 def epilogue(iqp, q=16, ldq=256, M=4, H=2, D=128, rd=64, pos=16, cs=16, mp=10, out=16, sc=16, flags=0):
@@ -245,10 +270,10 @@ def test_binding_rejects_short_activation_scale_rows(iqp):
         iqp.debug_indexer_q_f32(a, torch.zeros((M, 2), dtype=torch.int32), w, ws, pos, cs, stage=0, n_heads=H)
 
 
-def clock(iqp, M=2048, K=1536, H=64, stamps=16, cap=1024, nwg=True, q=16, qs=16):
+def clock(iqp, M=2048, K=1536, H=64, stamps=16, cap=1024, nwg=True, q=16, qs=16, lanes=0):
     n = ctypes.c_int64(-1)
     st = iqp._lib.iqp_debug_indexer_q_clock(P(16), K, P(16), 3, 1, P(16), K, P(16), M, K, H, 128, 64,
-                                            P(16), P(16), 10, P(q), P(qs), P(stamps), cap,
+                                            P(16), P(16), P(lanes), 10, P(q), P(qs), P(stamps), cap,
                                             ctypes.byref(n) if nwg else None, None)
     return st, n.value
 
@@ -261,6 +286,7 @@ def test_clock_and_debug_argument_checks(iqp):
     assert clock(iqp, stamps=0) == (iqp.IQP_ERR_INVALID, 0)
     assert clock(iqp, stamps=24) == (iqp.IQP_ERR_UNSUPPORTED, 0)   # stamps not 16-byte aligned
     assert clock(iqp, M=0) == (iqp.IQP_ERR_UNSUPPORTED, 0)
+    assert clock(iqp, lanes=8) == (iqp.IQP_ERR_UNSUPPORTED, 0)     # the lane-ordered copy not 16-byte aligned
     lib = iqp._lib
     assert lib.iqp_device_clock_rates(None, None) == iqp.IQP_ERR_INVALID
     # the debug GEMM stage 3 and the one-launch twin reject before any device call
