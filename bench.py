@@ -119,7 +119,7 @@ KERNEL_SOURCES = {
     "epilogue": ("epilogue_bf16.hip", "iq_common.h"),
 }
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "indexer_q_chain_m4632_rocprofv3.md")
-MFMA_PROFILE = os.path.join(ROOT, "profiles", "indexer_q_split_mfma_counters_m4632.md")
+MFMA_PROFILE = os.path.join(ROOT, "profiles", "indexer_q_split_lanes_mfma_counters_m4632.md")
 
 
 def source_digest(kernel):
