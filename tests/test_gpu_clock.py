@@ -1,6 +1,7 @@
-"""GPU: the clock-stamp build of the split-role fused kernel (the figure
-bench.py reads its shader clock from) computes the same bytes as the
-production call, and its stamps describe a plausible clock."""
+"""GPU: the clock-stamp builds of the split-role fused kernel (bench.py reads
+its shader clock from the one reading the RoPE table's lane-ordered copy)
+compute the same bytes as the production call, and their stamps describe a
+plausible clock."""
 import pytest
 import torch
 
@@ -17,12 +18,16 @@ def setup(gpu_lib):
     return w.cuda(), wsb.cuda(), inp["x"].cuda(), inp["positions"].cuda(), cs
 
 
+@pytest.mark.parametrize("lanes", [False, True], ids=["table", "lane_copy"])
 @pytest.mark.parametrize("M", [1024, 1157, 4632])
-def test_clock_build_gives_the_production_bytes(gpu_lib, setup, M):
+def test_clock_build_gives_the_production_bytes(gpu_lib, setup, M, lanes):
+    """Both clock-stamp builds: the one reading the table, and the one reading
+    its lane-ordered copy (the kernel bench.py times)."""
     w, wsb, x, pos, cs = setup
+    kw = dict(cos_sin_lanes=gpu_lib.rope_table_lanes(cs)) if lanes else {}
     a, a_s = gpu_lib.fp8_quant_1x128_ue8m0(x[:M])
-    q, qs = gpu_lib.indexer_q_gemm_rope_fp4(a, a_s, w, wsb, pos[:M], cs)
-    q2, qs2, st = gpu_lib.debug_indexer_q_clock(a, a_s, w, wsb, pos[:M], cs)
+    q, qs = gpu_lib.indexer_q_gemm_rope_fp4(a, a_s, w, wsb, pos[:M], cs, **kw)
+    q2, qs2, st = gpu_lib.debug_indexer_q_clock(a, a_s, w, wsb, pos[:M], cs, **kw)
     torch.cuda.synchronize()
     assert torch.equal(q, q2) and torch.equal(qs, qs2)
     st = st.cpu()

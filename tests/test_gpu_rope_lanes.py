@@ -141,3 +141,20 @@ def test_lane_table_binding_checks(gpu_lib):
     with pytest.raises(ValueError):
         gpu_lib.indexer_q_gemm_rope_fp4(a, a_s, codes.cuda(), sb.cuda(), pos, cs, n_heads=2,
                                         cos_sin_lanes=gpu_lib.rope_table_lanes(cs), scale_rule="ocp_floor")
+
+
+@pytest.mark.parametrize("M", [8, 1200])
+def test_prep_with_lane_copy_bytes_equal(gpu_lib, M):
+    """indexer_q_prep with the copy: the one-launch call (8 tokens, which reads
+    the table) and the two-call path (1200 tokens, which reads the copy) give
+    the bytes of the same call without it."""
+    codes, sb = S.weights()
+    g = S.rng("indexer_q_m128", 3400 + M)
+    x = S.activations_outlier(g, M, 1536).cuda()
+    pos = _positions("offset", M, 4096, M).cuda()
+    cs = gpu_lib.rope_cos_sin_table(S.ROPE_THETA, 4096, 64)
+    lanes = gpu_lib.rope_table_lanes(cs)
+    q0, s0 = gpu_lib.indexer_q_prep(x, codes.cuda(), sb.cuda(), pos, cs)
+    q1, s1 = gpu_lib.indexer_q_prep(x, codes.cuda(), sb.cuda(), pos, cs, cos_sin_lanes=lanes)
+    torch.cuda.synchronize()
+    assert torch.equal(q0, q1) and torch.equal(s0, s1)
