@@ -464,9 +464,10 @@ def weight_prep_roofline(iqp, dev, reps):
 
 def decode_mix(iqp, S, dev, w, wsb, reps):
     """256 independent calls, M from {1, 2, 4, 8, 16, 32, 64}: each the
-    indexer-Q preparation of X [M, 1536] (one launch up to
-    ONE_LAUNCH_MAX_TOKENS tokens, two calls above) and a standalone
-    quantization of X' [M, 7168]. Sustained calls/s from one captured graph of
+    indexer-Q preparation of X [M, 1536] and the quantization of X' [M, 7168]
+    (up to ONE_LAUNCH_WITH_QUANT_MAX_TOKENS tokens, i.e. every call of the
+    mix, one launch for both, indexer_q_prep_bf16_with_quant; above, three:
+    the two-call preparation and a standalone quantization). Sustained calls/s from one captured graph of
     the whole mix, hot (one weight copy) and cold (call i reads weight copy
     i % 24: 302 MB, beyond the Infinity Cache); per-call latency = the mean
     call time of its M in a graph of 20 such calls (hot) or of 24 calls over
@@ -495,12 +496,12 @@ def decode_mix(iqp, S, dev, w, wsb, reps):
         iqp.fp8_quant_1x128_ue8m0(c["xw"], q=c["aw"], scales=c["asw"])
 
     def one(c, wt):
+        # the Q preparation and the quantization of X' in one launch
         iqp.indexer_q_prep_bf16(c["x"], wt[0], wt[1], c["pos"], cs, n_heads=N_HEADS, q_fp4=c["q"],
-                                q_scales=c["qs"])
-        iqp.fp8_quant_1x128_ue8m0(c["xw"], q=c["aw"], scales=c["asw"])
+                                q_scales=c["qs"], quant_beside=c["xw"], quant_beside_out=(c["aw"], c["asw"]))
 
     def routed(c, wt):
-        (one if c["M"] <= iqp.ONE_LAUNCH_MAX_TOKENS else two)(c, wt)
+        (one if c["M"] <= iqp.ONE_LAUNCH_WITH_QUANT_MAX_TOKENS else two)(c, wt)
 
     hot = (w, wsb)
     n_w = 24
@@ -529,9 +530,9 @@ def decode_mix(iqp, S, dev, w, wsb, reps):
     mix_k_s = float(sum(lat_k[c["M"]] for c in calls)) * 1e-6
     return {
         "workload": "decode mix: 256 independent calls, M uniform over {1,2,4,8,16,32,64}; each call X bf16 "
-                    "[M,1536] -> FP8 quant -> GEMM + RoPE + Hadamard + FP4 (64 heads), one launch up to "
-                    f"{iqp.ONE_LAUNCH_MAX_TOKENS} tokens and two calls above, plus a standalone FP8 quant of "
-                    "X' [M,7168]; positions U[0,131072)",
+                    "[M,1536] -> FP8 quant -> GEMM + RoPE + Hadamard + FP4 (64 heads) and an FP8 quant of X' "
+                    f"[M,7168]: one launch for both up to {iqp.ONE_LAUNCH_WITH_QUANT_MAX_TOKENS} tokens, three "
+                    "launches above; positions U[0,131072)",
         "calls_per_s": len(calls) / t_hot, "calls_per_s_cold": len(calls) / t_cold,
         "latency_us_hot": {"p50": float(np.percentile(per_hot, 50)), "p99": float(np.percentile(per_hot, 99))},
         "latency_us_cold": {"p50": float(np.percentile(per_cold, 50)), "p99": float(np.percentile(per_cold, 99))},

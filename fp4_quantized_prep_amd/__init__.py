@@ -24,12 +24,19 @@ __all__ = [
     "indexer_q_rope_hadamard_fp4", "indexer_q_prep_bf16", "indexer_q_prep", "fp8_quant_weight_128x128_ue8m0", "abi_version", "library_path",
     "rope_table_lanes", "rope_table_lanes_size",
     "IQP_OK", "IQP_ERR_INVALID", "IQP_ERR_UNSUPPORTED", "IQP_ERR_HIP", "ONE_LAUNCH_MAX_TOKENS",
+    "ONE_LAUNCH_WITH_QUANT_MAX_TOKENS",
     "IQP_ROPE_INTERLEAVED", "IQP_FP4_SCALE_OCP_FLOOR", "IQP_W_SCALES_PER_ROW",
 ]
 
 #: Up to this many tokens indexer_q_prep takes the one-launch path (measured on
 #: MI355X: faster there; from 32 tokens the two calls are as fast or faster).
 ONE_LAUNCH_MAX_TOKENS = 16
+
+#: Up to this many tokens a decode step that also quantizes an independent
+#: [M, 7168] activation is faster as one launch (indexer_q_prep_bf16 with
+#: quant_beside) than as three (quantize, fused call, quantize): measured on
+#: MI355X, 9.6 vs 11.2 us at 32 tokens, 11.8 vs 12.4 at 128, 17.9 vs 17.2 at 192.
+ONE_LAUNCH_WITH_QUANT_MAX_TOKENS = 128
 
 IQP_ROPE_INTERLEAVED = 0x1
 IQP_FP4_SCALE_OCP_FLOOR = 0x2
@@ -66,6 +73,9 @@ def _load():
     lib.indexer_q_prep_bf16.restype = ctypes.c_int
     lib.indexer_q_prep_bf16_ex.argtypes = lib.indexer_q_prep_bf16.argtypes[:-1] + [c_i32, c_p]
     lib.indexer_q_prep_bf16_ex.restype = ctypes.c_int
+    lib.indexer_q_prep_bf16_with_quant.argtypes = lib.indexer_q_prep_bf16.argtypes[:-1] + \
+        [c_p, c_i64, c_i64, c_i64, c_p, c_i64, c_p, c_i64, c_i64, c_p]
+    lib.indexer_q_prep_bf16_with_quant.restype = ctypes.c_int
     lib.fp8_quant_weight_128x128_ue8m0.argtypes = [c_p, c_i64, c_i64, c_i64, c_p, c_i64, c_p, c_i64, c_p]
     lib.fp8_quant_weight_128x128_ue8m0.restype = ctypes.c_int
     lib.indexer_q_rope_hadamard_fp4.argtypes = [c_p, c_i64, c_i64, c_i32, c_i32, c_i32, c_p, c_p, c_i64,
@@ -157,8 +167,18 @@ def fp8_quant_1x128_ue8m0(x: torch.Tensor, scale_layout: str = "k", q: torch.Ten
     storage is [ceil(K/512), M rounded up to 4] and the returned view has
     strides (1, M_pad). Pre-allocated ``q`` / ``scales`` may be passed in.
     """
-    if x.dim() != 2:
-        raise ValueError("x must be 2-D")
+    q, scales = _quant_outputs(x, scale_layout, q, scales)
+    M, K = x.shape
+    st = _lib.fp8_quant_1x128_ue8m0(_ptr(x), M, K, x.stride(0), _ptr(q), q.stride(0), _ptr(scales),
+                                    scales.stride(0), scales.stride(1), _stream(x, stream))
+    _check(st, "fp8_quant_1x128_ue8m0")
+    return q, scales
+
+
+def _quant_outputs(x, scale_layout, q, scales):
+    """Checks of a quantization's input and outputs (allocated when None)."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError("x must be a 2-D tensor")
     dev = x.device
     _require(x, "x", torch.bfloat16, dev, 2)
     if x.stride(1) != 1:
@@ -182,9 +202,6 @@ def fp8_quant_1x128_ue8m0(x: torch.Tensor, scale_layout: str = "k", q: torch.Ten
     _require(scales, "scales", torch.int32, dev, 2)
     if tuple(scales.shape) != (M, nw):
         raise ValueError(f"scales must be [{M}, {nw}] (one packed word per 512 columns), got {tuple(scales.shape)}")
-    st = _lib.fp8_quant_1x128_ue8m0(_ptr(x), M, K, x.stride(0), _ptr(q), q.stride(0), _ptr(scales),
-                                    scales.stride(0), scales.stride(1), _stream(x, stream))
-    _check(st, "fp8_quant_1x128_ue8m0")
     return q, scales
 
 
@@ -412,12 +429,20 @@ def rope_table_lanes(cos_sin, out=None, stream=None):
 @_on_stream
 def indexer_q_prep_bf16(x, w, w_scales, positions, cos_sin, n_heads: int = 64, head_dim: int = 128,
                         rope_dim: int = 64, q_fp4=None, q_scales=None, rope_layout: str = "half_split",
-                        scale_rule: str = "ceil", w_scale_layout: str = "tile_128x128", stream=None):
+                        scale_rule: str = "ceil", w_scale_layout: str = "tile_128x128", quant_beside=None,
+                        quant_beside_out=None, quant_beside_layout: str = "k", stream=None):
     """The whole preparation in one launch for up to 256 tokens (K = 1536):
     bf16 x [M, K] -> FP8 quantization (in the kernel, never stored) -> fused
     projection / RoPE / Hadamard / FP4. Returns ``(q_fp4, q_scales)``. The
     convention arguments are those of :func:`indexer_q_gemm_rope_fp4`
-    (indexer_q_prep_bf16_ex)."""
+    (indexer_q_prep_bf16_ex).
+
+    quant_beside: an independent bf16 [M2, K2] matrix (M2 <= 256) quantized
+    as :func:`fp8_quant_1x128_ue8m0` would, in the same launch
+    (indexer_q_prep_bf16_with_quant; default conventions only); the call then
+    returns ``(q_fp4, q_scales, q2, scales2)``. quant_beside_out: preallocated
+    ``(q2, scales2)``; quant_beside_layout: their words' layout ("k" or "mn")
+    when allocated here."""
     if w_scale_layout not in ("tile_128x128", "row_1x128"):
         raise ValueError("w_scale_layout must be 'tile_128x128' or 'row_1x128'")
     rows = w_scale_layout == "row_1x128"
@@ -435,6 +460,19 @@ def indexer_q_prep_bf16(x, w, w_scales, positions, cos_sin, n_heads: int = 64, h
     if tuple(q_fp4.shape) != (M, n_heads, head_dim // 2) or tuple(q_scales.shape) != (M, n_heads, head_dim // 32):
         raise ValueError("q_fp4 / q_scales have the wrong shape")
     args += [_ptr(q_fp4), _ptr(q_scales)]
+    if quant_beside is not None:
+        if flags != 0:
+            raise ValueError("quant_beside serves the default conventions only")
+        q2, s2 = quant_beside_out if quant_beside_out is not None else (None, None)
+        q2, s2 = _quant_outputs(quant_beside, quant_beside_layout, q2, s2)
+        if quant_beside.device != dev:
+            raise ValueError("quant_beside must be on the device of x")
+        M2, K2 = quant_beside.shape
+        st = _lib.indexer_q_prep_bf16_with_quant(*args, _ptr(quant_beside), M2, K2, quant_beside.stride(0), _ptr(q2),
+                                                 q2.stride(0), _ptr(s2), s2.stride(0), s2.stride(1),
+                                                 _stream(x, stream))
+        _check(st, "indexer_q_prep_bf16_with_quant")
+        return q_fp4, q_scales, q2, s2
     if flags == 0:
         st = _lib.indexer_q_prep_bf16(*args, _stream(x, stream))
         _check(st, "indexer_q_prep_bf16")

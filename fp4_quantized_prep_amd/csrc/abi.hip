@@ -220,6 +220,52 @@ int indexer_q_prep_bf16_ex(const void* x, int64_t ldx, const void* w, int64_t ld
   return from_hip(iqp::launch_indexer_q_small_bf16_variant(p, flags, static_cast<hipStream_t>(stream)));
 }
 
+int indexer_q_prep_bf16_with_quant(const void* x, int64_t ldx, const void* w, int64_t ldw, const uint8_t* w_scales,
+                                   int64_t M, int64_t K, int32_t H, int32_t D, int32_t rope_dim,
+                                   const int64_t* positions, const float* cos_sin, int64_t max_pos,
+                                   uint8_t* q_fp4, uint8_t* q_scales, const void* x2, int64_t M2, int64_t K2,
+                                   int64_t ldx2, void* q2, int64_t ldq2, int32_t* scales2, int64_t s_stride_m2,
+                                   int64_t s_stride_w2, void* stream) {
+  // the second matrix: fp8_quant_1x128_ue8m0's checks, at decode sizes
+  if (M2 < 0 || K2 < 0) return IQP_ERR_INVALID;
+  const bool side = M2 > 0 && K2 > 0;
+  if (side) {
+    if (!x2 || !q2 || !scales2) return IQP_ERR_INVALID;
+    if (ldx2 < K2 || ldq2 < K2) return IQP_ERR_INVALID;
+    if (K2 % 128) return IQP_ERR_UNSUPPORTED;
+    if (check_scale_strides(M2, (K2 / 128 + 3) / 4, s_stride_m2, s_stride_w2) != IQP_OK) return IQP_ERR_INVALID;
+    if (!aligned(x2, 16) || ldx2 % 8 || !aligned(q2, 8) || ldq2 % 8 || !aligned(scales2, 4))
+      return IQP_ERR_UNSUPPORTED;
+    if (M2 > 256 || K2 / 128 > 0x7FFFFFFF) return IQP_ERR_UNSUPPORTED;
+  }
+  iqp::IndexerQArgs p{};
+  const int st = prep_bf16_args(x, ldx, w, ldw, w_scales, M, K, H, D, rope_dim, positions, cos_sin, max_pos,
+                                q_fp4, q_scales, p);
+  if (st != IQP_OK) return st;
+  if (M == 0) {   // no tokens for the projection: the quantization alone
+    if (!side) return IQP_OK;
+    const int ds = device_status();
+    if (ds != IQP_OK) return ds;
+    return from_hip(iqp::launch_fp8_quant(static_cast<const uint16_t*>(x2), M2, K2, ldx2, static_cast<uint8_t*>(q2),
+                                          ldq2, scales2, s_stride_m2, s_stride_w2, static_cast<hipStream_t>(stream)));
+  }
+  p.q_fp4 = q_fp4;
+  p.q_scales = q_scales;
+  if (side) {
+    p.side_x = static_cast<const uint16_t*>(x2);
+    p.side_ldx = ldx2;
+    p.side_q = static_cast<uint8_t*>(q2);
+    p.side_ldq = ldq2;
+    p.side_scales = scales2;
+    p.side_sm = s_stride_m2;
+    p.side_sw = s_stride_w2;
+    p.side_nkb = (int32_t)(K2 / 128);
+    p.side_nw = (p.side_nkb + 3) / 4;
+    p.side_words = M2 * p.side_nw;
+  }
+  return from_hip(iqp::launch_indexer_q_small_bf16(p, static_cast<hipStream_t>(stream)));
+}
+
 int iqp_debug_indexer_q_prep_bf16_f32(const void* x, int64_t ldx, const void* w, int64_t ldw,
                                       const uint8_t* w_scales, int64_t M, int64_t K, int32_t H, int32_t D,
                                       int32_t rope_dim, const int64_t* positions, const float* cos_sin,

@@ -70,6 +70,66 @@ __device__ __forceinline__ v4u codes16(v4u a, v4u b, int e) {
   return v4u{cvt4(a[0], a[1], mul), cvt4(a[2], a[3], mul), cvt4(b[0], b[1], mul), cvt4(b[2], b[3], mul)};
 }
 
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+
+// maximum over each row of 16 lanes (a block in the word layout below)
+__device__ __forceinline__ uint32_t lanes16_max(uint32_t v) {
+  v = lanes8_max(v);
+  return max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, DPP_ROW_MIRROR, 0xF, 0xF, false));
+}
+
+// One wave's share of the packed quantization of a row-major [M, K] bf16
+// matrix: packed words first and first + 1 (row-major over [M, nw], nw =
+// ceil(K / 512), `words` = M nw in all). In load k lane l reads 16 bytes (8
+// bf16) of word first + k at byte 16 l, so every load covers 1 KiB
+// contiguously and 16 lanes hold one 128-element block; the block amax is a
+// DPP maximum over that row of lanes; v_cvt_pk_fp8_f32 rounds x 2^-e to
+// E4M3; lanes store 8 bytes each; the word's four block bytes (zero past
+// the last block) are gathered by readlane and stored by lane 0. NT_STORE:
+// non-temporal code stores. Used by the standalone quantizer and, beside
+// the one-launch indexer-Q kernel, for an independent matrix.
+template <bool NT_STORE>
+__device__ __forceinline__ void quant_word_pair(const uint16_t* __restrict__ x, int64_t ldx, uint8_t* __restrict__ q,
+                                                int64_t ldq, int32_t* __restrict__ scales, int64_t sm, int64_t sw,
+                                                int32_t nw, int32_t nkb, int64_t words, int64_t first, int lane) {
+  const int blk = lane >> 4;  // block of this lane within a word
+  v4u d[2];
+  int64_t row[2];
+  int w[2];
+  bool valid[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int64_t word = first + k;
+    row[k] = word / nw;
+    w[k] = (int)(word - row[k] * nw);
+    valid[k] = word < words && 4 * w[k] + blk < nkb;
+    d[k] = v4u{0u, 0u, 0u, 0u};
+    if (valid[k])
+      d[k] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(x + row[k] * ldx + (int64_t)w[k] * 512 + lane * 8));
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const uint32_t m = max(max(mag2(d[k][0]), mag2(d[k][1])), max(mag2(d[k][2]), mag2(d[k][3])));
+    const int e = block_exponent(lanes16_max(m));
+    const float mul = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, a normal float
+    const v2u o = v2u{cvt4(d[k][0], d[k][1], mul), cvt4(d[k][2], d[k][3], mul)};
+    if (valid[k]) {
+      v2u* dst = reinterpret_cast<v2u*>(q + row[k] * ldq + (int64_t)w[k] * 512 + lane * 8);
+      if constexpr (NT_STORE)
+        __builtin_nontemporal_store(o, dst);
+      else
+        *dst = o;
+    }
+    // the word's four block bytes, from the first lane of each row
+    const uint32_t byte = valid[k] ? (uint32_t)(e + 127) : 0u;
+    const uint32_t wv = (uint32_t)__builtin_amdgcn_readlane((int)byte, 0) |
+                        ((uint32_t)__builtin_amdgcn_readlane((int)byte, 16) << 8) |
+                        ((uint32_t)__builtin_amdgcn_readlane((int)byte, 32) << 16) |
+                        ((uint32_t)__builtin_amdgcn_readlane((int)byte, 48) << 24);
+    if (lane == 0 && first + k < words) scales[row[k] * sm + (int64_t)w[k] * sw] = (int32_t)wv;
+  }
+}
+
 }  // namespace fp8q
 }  // namespace
 }  // namespace iqp

@@ -110,8 +110,23 @@ template <bool XIN, bool DUMP = false>
 __global__ __launch_bounds__(NTHREADS, 1)
 void IQP_SMALL_KERNEL(IndexerQArgs pa) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
-  const int head = blockIdx.x;
   const int tid = threadIdx.x;
+  if constexpr (XIN && !DUMP) {
+    // grid rows past the heads' token tiles: the independent quantization run
+    // beside this kernel, two packed words per wave as the standalone
+    // quantizer's workgroups take them (its codes stay in cache: decode-sized)
+    const int main_rows = (int)((pa.M + TILE - 1) / TILE);
+    if ((int)blockIdx.y >= main_rows) {
+      const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+      const int64_t g = (int64_t)(blockIdx.y - main_rows) * gridDim.x + blockIdx.x;
+      const int64_t first = 2 * (g * NWAVES + w);
+      if (first < pa.side_words)
+        fp8q::quant_word_pair<false>(pa.side_x, pa.side_ldx, pa.side_q, pa.side_ldq, pa.side_scales, pa.side_sm,
+                                     pa.side_sw, pa.side_nw, pa.side_nkb, pa.side_words, first, tid & 63);
+      return;
+    }
+  }
+  const int head = blockIdx.x;
   const int lane = tid & 63, half = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // the column tile's tokens: the batch seen from token t0 on
@@ -462,7 +477,12 @@ bool indexer_q_small_bf16_supported(const IndexerQArgs& a) {
 }
 
 hipError_t launch_indexer_q_small_bf16(const IndexerQArgs& a, hipStream_t stream) {
-  const dim3 grid((unsigned)a.H, (unsigned)((a.M + small::TILE - 1) / small::TILE)), block(small::NTHREADS);
+  // extra grid rows for the quantization beside it: two words per wave
+  const int64_t side_wgs = (a.side_words + 2 * small::NWAVES - 1) / (2 * small::NWAVES);
+  const int64_t side_rows = (side_wgs + a.H - 1) / a.H;
+  const int64_t rows = (a.M + small::TILE - 1) / small::TILE + side_rows;
+  if (rows > 65535) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)a.H, (unsigned)rows), block(small::NTHREADS);
   hipLaunchKernelGGL(small::IQP_SMALL_KERNEL<true>, grid, block, 0, stream, a);
   return hipGetLastError();
 }

@@ -29,6 +29,18 @@ struct IndexerQArgs {
   const uint16_t* x;             // bf16 activations [M, K], row stride ldx elements (one-launch small path)
   int64_t ldx;
   int32_t chunks;                // token chunks per head pair (set by the launcher)
+  // one-launch kernel: the packed FP8 quantization of an independent bf16
+  // matrix [side_words / side_nw rows, K] run by extra workgroups of the
+  // same launch (none when side_words == 0); layout and strides as in
+  // launch_fp8_quant
+  const uint16_t* side_x;
+  int64_t side_ldx;
+  uint8_t* side_q;
+  int64_t side_ldq;
+  int32_t* side_scales;
+  int64_t side_sm, side_sw;
+  int32_t side_nw, side_nkb;
+  int64_t side_words;
 };
 
 hipError_t launch_fp8_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,

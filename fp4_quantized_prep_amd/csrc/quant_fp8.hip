@@ -34,17 +34,9 @@ namespace iqp {
 namespace {
 
 constexpr int QWAVES = 4;  // waves per workgroup, two scale words each
-using namespace fp8q;
-typedef unsigned v2u __attribute__((ext_vector_type(2)));
-
-// maximum over each row of 16 lanes (a block)
-__device__ __forceinline__ uint32_t lanes16_max(uint32_t v) {
-  v = lanes8_max(v);
-  return max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, DPP_ROW_MIRROR, 0xF, 0xF, false));
-}
 
 // Words 2 i and 2 i + 1 (row-major over [M, nw]) of the whole tensor go to
-// wave i.
+// wave i (the arithmetic: fp8q::quant_word_pair).
 template <bool NT_STORE>
 __global__ __launch_bounds__(QWAVES * 64)
 void fp8_quant_1x128_kernel(const uint16_t* __restrict__ x, int64_t ldx,
@@ -52,46 +44,10 @@ void fp8_quant_1x128_kernel(const uint16_t* __restrict__ x, int64_t ldx,
                             int32_t* __restrict__ scales, int64_t sm, int64_t sw,
                             int32_t nw, int32_t nkb, int64_t words) {
   const int lane = threadIdx.x & 63;
-  const int blk = lane >> 4;  // block of this lane within a word
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t first = 2 * ((int64_t)blockIdx.x * QWAVES + wave);
   if (first >= words) return;   // uniform across the wave
-
-  v4u d[2];
-  int64_t row[2];
-  int w[2];
-  bool valid[2];
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int64_t word = first + k;
-    row[k] = word / nw;
-    w[k] = (int)(word - row[k] * nw);
-    valid[k] = word < words && 4 * w[k] + blk < nkb;
-    d[k] = v4u{0u, 0u, 0u, 0u};
-    if (valid[k])
-      d[k] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(x + row[k] * ldx + (int64_t)w[k] * 512 + lane * 8));
-  }
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const uint32_t m = max(max(mag2(d[k][0]), mag2(d[k][1])), max(mag2(d[k][2]), mag2(d[k][3])));
-    const int e = block_exponent(lanes16_max(m));
-    const float mul = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, a normal float
-    const v2u o = v2u{cvt4(d[k][0], d[k][1], mul), cvt4(d[k][2], d[k][3], mul)};
-    if (valid[k]) {
-      v2u* dst = reinterpret_cast<v2u*>(q + row[k] * ldq + (int64_t)w[k] * 512 + lane * 8);
-      if constexpr (NT_STORE)
-        __builtin_nontemporal_store(o, dst);
-      else
-        *dst = o;
-    }
-    // the word's four block bytes, from the first lane of each row
-    const uint32_t byte = valid[k] ? (uint32_t)(e + 127) : 0u;
-    const uint32_t wv = (uint32_t)__builtin_amdgcn_readlane((int)byte, 0) |
-                        ((uint32_t)__builtin_amdgcn_readlane((int)byte, 16) << 8) |
-                        ((uint32_t)__builtin_amdgcn_readlane((int)byte, 32) << 16) |
-                        ((uint32_t)__builtin_amdgcn_readlane((int)byte, 48) << 24);
-    if (lane == 0 && first + k < words) scales[row[k] * sm + (int64_t)w[k] * sw] = (int32_t)wv;
-  }
+  fp8q::quant_word_pair<NT_STORE>(x, ldx, q, ldq, scales, sm, sw, nw, nkb, words, first, lane);
 }
 
 }  // namespace

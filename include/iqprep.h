@@ -16,7 +16,9 @@
  *   3. indexer_q_rope_hadamard_fp4   the same RoPE / Hadamard / FP4 epilogue as
  *      a standalone launch over a bf16 Q (the unfused chain's second half).
  *   4. indexer_q_prep_bf16   calls 1 and 2 as one launch for decode-sized
- *      batches (up to 256 tokens); indexer_q_prep_bf16_ex takes the flags.
+ *      batches (up to 256 tokens); indexer_q_prep_bf16_ex takes the flags;
+ *      indexer_q_prep_bf16_with_quant also runs call 1 on an independent
+ *      matrix in the same launch.
  *   5. fp8_quant_weight_128x128_ue8m0   the weights' E4M3 codes and per-tile
  *      scales that calls 2 and 4 take (weight preparation, off the
  *      per-token path).
@@ -273,6 +275,35 @@ int indexer_q_prep_bf16_ex(const void* x, int64_t ldx, const void* w, int64_t ld
                            int64_t M, int64_t K, int32_t H, int32_t D, int32_t rope_dim,
                            const int64_t* positions, const float* cos_sin, int64_t max_pos,
                            uint8_t* q_fp4, uint8_t* q_scales, int32_t flags, void* stream);
+
+/*
+ * indexer_q_prep_bf16_with_quant — indexer_q_prep_bf16 (default conventions)
+ * and fp8_quant_1x128_ue8m0 of an independent bf16 matrix x2 in ONE launch:
+ * extra workgroups of the one-launch kernel quantize x2 (a decode step's
+ * other activation, e.g. the [M, 7168] input of a wider projection) while
+ * the others prepare Q, saving a launch per step (tokenspeed PR
+ * "perf(deepseek-v4): accelerate indexer Q and packed FP8 quantization",
+ * Performance: the packed quantizer and the Q preparation timed as a decode
+ * CUDA Graph replay per step; Summary for both operations).
+ *
+ * The first 15 arguments, their layouts and errors are indexer_q_prep_bf16's;
+ * x2, M2, K2, ldx2, q2, ldq2, scales2, s_stride_m2, s_stride_w2 are
+ * fp8_quant_1x128_ue8m0's (x, M, K, ldx, q, ldq, scales, s_stride_m,
+ * s_stride_w), with the same checks and M2 at most 256 (else
+ * IQP_ERR_UNSUPPORTED). Both outputs are byte for byte those of the two
+ * separate calls. M2 == 0 or K2 == 0: the first call alone; M == 0: the
+ * quantization alone (its own launch). The x2 / q2 / scales2 regions must
+ * not overlap the other call's buffers.
+ */
+int indexer_q_prep_bf16_with_quant(const void* x, int64_t ldx, const void* w, int64_t ldw,
+                                   const uint8_t* w_scales,
+                                   int64_t M, int64_t K, int32_t H, int32_t D, int32_t rope_dim,
+                                   const int64_t* positions, const float* cos_sin, int64_t max_pos,
+                                   uint8_t* q_fp4, uint8_t* q_scales,
+                                   const void* x2, int64_t M2, int64_t K2, int64_t ldx2,
+                                   void* q2, int64_t ldq2, int32_t* scales2,
+                                   int64_t s_stride_m2, int64_t s_stride_w2,
+                                   void* stream);
 
 /*
  * indexer_q_rope_hadamard_fp4 — the epilogue of indexer_q_gemm_rope_fp4 as a

@@ -121,6 +121,28 @@ def test_one_launch_ex_argument_checks(iqp):
     assert lib.indexer_q_prep_bf16_ex(*wide, 1, None) == iqp.IQP_ERR_UNSUPPORTED  # K must be 1536
 
 
+def test_one_launch_with_quant_argument_checks(iqp):
+    lib, inv, uns = iqp._lib, iqp.IQP_ERR_INVALID, iqp.IQP_ERR_UNSUPPORTED
+    base = [P(16), 1536, P(16), 1536, P(16), 4, 1536, 2, 128, 64, P(16), P(16), 10, P(16), P(16)]
+
+    def call(M=4, x2=16, M2=3, K2=7168, ldx2=7168, q2=16, ldq2=7168, s2=16, sm=14, sw=1):
+        args = list(base)
+        args[5] = M
+        return lib.indexer_q_prep_bf16_with_quant(*args, P(x2), M2, K2, ldx2, P(q2), ldq2, P(s2), sm, sw, None)
+    assert call(M2=-1) == inv
+    assert call(x2=0) == inv
+    assert call(q2=0) == inv
+    assert call(s2=0) == inv
+    assert call(ldx2=4096) == inv
+    assert call(K2=100, ldx2=128, ldq2=128) == uns          # K not a multiple of 128
+    assert call(sm=2, sw=2) == inv                          # neither scale-word layout
+    assert call(x2=8) == uns                                # not 16-byte aligned
+    assert call(M2=257, sm=14) == uns                       # beyond decode sizes
+    assert call(M=257) == uns                               # the one-launch call's own limit
+    assert call(M=0, M2=0) == iqp.IQP_OK                    # nothing to do
+    assert call(M2=0, x2=0, q2=0, s2=0, M=0) == iqp.IQP_OK
+
+
 def test_debug_and_table_argument_checks(iqp):
     lib = iqp._lib
     args = [P(16), 256, P(16), 1, 1, P(16), 256, P(16), 4, 256, 2, 128, 64, P(16), P(16), 10]

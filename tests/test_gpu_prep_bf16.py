@@ -196,3 +196,28 @@ def test_routing_helper_passes_the_flags(gpu_lib, weights, table, M):
     torch.cuda.synchronize()
     assert torch.equal(q1, q2) and torch.equal(s1, s2)
     assert not torch.equal(q1, q0)
+
+
+@pytest.mark.parametrize("M,M2,K2,layout", [(1, 1, 7168, "k"), (5, 7, 640, "k"), (16, 64, 7168, "mn"),
+                                            (100, 3, 7168, "k"), (256, 256, 7168, "k"), (0, 9, 7168, "k")])
+def test_one_launch_with_quant_beside_matches_separate_calls(gpu_lib, weights, table, M, M2, K2, layout):
+    """indexer_q_prep_bf16_with_quant: the Q preparation and the quantization
+    of an independent matrix in one launch give byte for byte the outputs of
+    the two separate calls (a ragged last word at K2 = 640, MN-major words,
+    no tokens for the projection)."""
+    codes, sb, wd, wsd = weights
+    inp = S.indexer_q_inputs("indexer_q_m128", M=max(M, 1))
+    x = inp["x"][:M].cuda()
+    pos = inp["positions"][:M].cuda()
+    g = S.rng("decode_mix", 4000 + M2 + K2)
+    x2 = S.activations_outlier(g, M2, K2).cuda()
+    print(f"[prep_bf16 + quant] M={M} M2={M2} K2={K2} {layout}", flush=True)
+    q, s, q2, s2 = gpu_lib.indexer_q_prep_bf16(x, wd, wsd, pos, table[4096], quant_beside=x2,
+                                                quant_beside_layout=layout)
+    r2, rs2 = gpu_lib.fp8_quant_1x128_ue8m0(x2, scale_layout=layout)
+    if M:
+        r, rs = gpu_lib.indexer_q_prep_bf16(x, wd, wsd, pos, table[4096])
+    torch.cuda.synchronize()
+    assert torch.equal(q2, r2) and torch.equal(s2, rs2), "the quantization beside differs"
+    if M:
+        assert torch.equal(q, r) and torch.equal(s, rs), "the Q preparation differs"
