@@ -467,8 +467,8 @@ def decode_mix(iqp, S, dev, w, wsb, reps):
     indexer-Q preparation of X [M, 1536] and the quantization of X' [M, 7168]
     (up to ONE_LAUNCH_WITH_QUANT_MAX_TOKENS tokens, i.e. every call of the
     mix, one launch for both, indexer_q_prep_bf16_with_quant; above, three:
-    the two-call preparation and a standalone quantization). Sustained calls/s from one captured graph of
-    the whole mix, hot (one weight copy) and cold (call i reads weight copy
+    the two-call preparation and a standalone quantization). Sustained
+    calls/s from one captured graph of the whole mix, hot (one weight copy) and cold (call i reads weight copy
     i % 24: 302 MB, beyond the Infinity Cache); per-call latency = the mean
     call time of its M in a graph of 20 such calls (hot) or of 24 calls over
     the 24 copies (cold), with p50 / p99 over the mix's calls."""
@@ -489,7 +489,7 @@ def decode_mix(iqp, S, dev, w, wsb, reps):
             "qs": torch.empty((m, N_HEADS, HEAD_DIM // 32), dtype=torch.uint8, device=dev),
         })
 
-    def two(c, wt):
+    def three(c, wt):
         iqp.fp8_quant_1x128_ue8m0(c["x"], q=c["a"], scales=c["as"])
         iqp.indexer_q_gemm_rope_fp4(c["a"], c["as"], wt[0], wt[1], c["pos"], cs, n_heads=N_HEADS,
                                     q_fp4=c["q"], q_scales=c["qs"])
@@ -501,7 +501,7 @@ def decode_mix(iqp, S, dev, w, wsb, reps):
                                 q_scales=c["qs"], quant_beside=c["xw"], quant_beside_out=(c["aw"], c["asw"]))
 
     def routed(c, wt):
-        (one if c["M"] <= iqp.ONE_LAUNCH_WITH_QUANT_MAX_TOKENS else two)(c, wt)
+        (one if c["M"] <= iqp.ONE_LAUNCH_WITH_QUANT_MAX_TOKENS else three)(c, wt)
 
     hot = (w, wsb)
     n_w = 24
@@ -511,7 +511,7 @@ def decode_mix(iqp, S, dev, w, wsb, reps):
     t_cold = med(replay_times(capture(lambda _: [routed(c, cold[i % n_w]) for i, c in enumerate(calls)], 1),
                               1, reps))
     t_one = med(replay_times(capture(lambda _: [one(c, hot) for c in calls], 1), 1, reps))
-    t_two = med(replay_times(capture(lambda _: [two(c, hot) for c in calls], 1), 1, reps))
+    t_three = med(replay_times(capture(lambda _: [three(c, hot) for c in calls], 1), 1, reps))
     lat_hot, lat_cold, lat_k = {}, {}, {}
     for m in sorted({c["M"] for c in calls}):
         c = next(c for c in calls if c["M"] == m)
@@ -538,7 +538,7 @@ def decode_mix(iqp, S, dev, w, wsb, reps):
         "latency_us_cold": {"p50": float(np.percentile(per_cold, 50)), "p99": float(np.percentile(per_cold, 99))},
         "per_M_call_us_hot": {str(k): v for k, v in lat_hot.items()},
         "per_M_call_us_cold": {str(k): v for k, v in lat_cold.items()},
-        "one_launch_path_calls_per_s": len(calls) / t_one, "two_call_path_calls_per_s": len(calls) / t_two,
+        "one_launch_path_calls_per_s": len(calls) / t_one, "three_launch_path_calls_per_s": len(calls) / t_three,
         "one_launch_kernel_roofline": {
             "kernel": "indexer_q_small_kernel<bf16 in> (FP8 quant + GEMM + RoPE + Hadamard + FP4, M <= 256)",
             "bound": "hbm", "achieved": mix_bytes / mix_k_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
