@@ -22,7 +22,7 @@ __all__ = [
     "IqpError", "fp8_quant_1x128_ue8m0", "indexer_q_gemm_rope_fp4", "rope_cos_sin_table",
     "debug_indexer_q_f32", "debug_indexer_q_prep_bf16_f32", "debug_indexer_q_clock", "device_clock_rates",
     "indexer_q_rope_hadamard_fp4", "indexer_q_prep_bf16", "indexer_q_prep", "fp8_quant_weight_128x128_ue8m0", "abi_version", "library_path",
-    "rope_table_lanes", "rope_table_lanes_size",
+    "rope_table_lanes", "rope_table_lanes_size", "indexer_q_workspace_bytes", "indexer_q_workspace",
     "IQP_OK", "IQP_ERR_INVALID", "IQP_ERR_UNSUPPORTED", "IQP_ERR_HIP", "ONE_LAUNCH_MAX_TOKENS",
     "ONE_LAUNCH_WITH_QUANT_MAX_TOKENS",
     "IQP_ROPE_INTERLEAVED", "IQP_FP4_SCALE_OCP_FLOOR", "IQP_W_SCALES_PER_ROW",
@@ -76,6 +76,11 @@ def _load():
     lib.indexer_q_prep_bf16_with_quant.argtypes = lib.indexer_q_prep_bf16.argtypes[:-1] + \
         [c_p, c_i64, c_i64, c_i64, c_p, c_i64, c_p, c_i64, c_i64, c_p]
     lib.indexer_q_prep_bf16_with_quant.restype = ctypes.c_int
+    lib.indexer_q_prep_bf16_with_quant_ws.argtypes = lib.indexer_q_prep_bf16_with_quant.argtypes[:-1] + \
+        [c_p, c_i64, c_p]
+    lib.indexer_q_prep_bf16_with_quant_ws.restype = ctypes.c_int
+    lib.indexer_q_workspace_bytes.argtypes = [c_i32]
+    lib.indexer_q_workspace_bytes.restype = c_i64
     lib.fp8_quant_weight_128x128_ue8m0.argtypes = [c_p, c_i64, c_i64, c_i64, c_p, c_i64, c_p, c_i64, c_p]
     lib.fp8_quant_weight_128x128_ue8m0.restype = ctypes.c_int
     lib.indexer_q_rope_hadamard_fp4.argtypes = [c_p, c_i64, c_i64, c_i32, c_i32, c_i32, c_p, c_p, c_i64,
@@ -430,7 +435,7 @@ def rope_table_lanes(cos_sin, out=None, stream=None):
 def indexer_q_prep_bf16(x, w, w_scales, positions, cos_sin, n_heads: int = 64, head_dim: int = 128,
                         rope_dim: int = 64, q_fp4=None, q_scales=None, rope_layout: str = "half_split",
                         scale_rule: str = "ceil", w_scale_layout: str = "tile_128x128", quant_beside=None,
-                        quant_beside_out=None, quant_beside_layout: str = "k", stream=None):
+                        quant_beside_out=None, quant_beside_layout: str = "k", workspace=None, stream=None):
     """The whole preparation in one launch for up to 256 tokens (K = 1536):
     bf16 x [M, K] -> FP8 quantization (in the kernel, never stored) -> fused
     projection / RoPE / Hadamard / FP4. Returns ``(q_fp4, q_scales)``. The
@@ -442,7 +447,13 @@ def indexer_q_prep_bf16(x, w, w_scales, positions, cos_sin, n_heads: int = 64, h
     (indexer_q_prep_bf16_with_quant; default conventions only); the call then
     returns ``(q_fp4, q_scales, q2, scales2)``. quant_beside_out: preallocated
     ``(q2, scales2)``; quant_beside_layout: their words' layout ("k" or "mn")
-    when allocated here."""
+    when allocated here.
+
+    workspace: a uint8 device tensor from :func:`indexer_q_workspace` (zero
+    before its first use; every call leaves it so): up to 64 tokens the
+    kernel then splits each head's K range over 2 or 4 workgroups
+    (indexer_q_prep_bf16_with_quant_ws; default conventions only). Calls
+    sharing a workspace must not run concurrently."""
     if w_scale_layout not in ("tile_128x128", "row_1x128"):
         raise ValueError("w_scale_layout must be 'tile_128x128' or 'row_1x128'")
     rows = w_scale_layout == "row_1x128"
@@ -460,19 +471,34 @@ def indexer_q_prep_bf16(x, w, w_scales, positions, cos_sin, n_heads: int = 64, h
     if tuple(q_fp4.shape) != (M, n_heads, head_dim // 2) or tuple(q_scales.shape) != (M, n_heads, head_dim // 32):
         raise ValueError("q_fp4 / q_scales have the wrong shape")
     args += [_ptr(q_fp4), _ptr(q_scales)]
-    if quant_beside is not None:
+    if workspace is not None:
+        if flags != 0:
+            raise ValueError("workspace serves the default conventions only")
+        _require(workspace, "workspace", torch.uint8, dev, 1)
+        if not workspace.is_contiguous() or workspace.numel() < indexer_q_workspace_bytes(n_heads):
+            raise ValueError(f"workspace must be a contiguous uint8 tensor of at least "
+                             f"{indexer_q_workspace_bytes(n_heads)} bytes (indexer_q_workspace)")
+    if quant_beside is not None or workspace is not None:
         if flags != 0:
             raise ValueError("quant_beside serves the default conventions only")
-        q2, s2 = quant_beside_out if quant_beside_out is not None else (None, None)
-        q2, s2 = _quant_outputs(quant_beside, quant_beside_layout, q2, s2)
-        if quant_beside.device != dev:
-            raise ValueError("quant_beside must be on the device of x")
-        M2, K2 = quant_beside.shape
-        st = _lib.indexer_q_prep_bf16_with_quant(*args, _ptr(quant_beside), M2, K2, quant_beside.stride(0), _ptr(q2),
-                                                 q2.stride(0), _ptr(s2), s2.stride(0), s2.stride(1),
-                                                 _stream(x, stream))
-        _check(st, "indexer_q_prep_bf16_with_quant")
-        return q_fp4, q_scales, q2, s2
+        if quant_beside is not None:
+            q2, s2 = quant_beside_out if quant_beside_out is not None else (None, None)
+            q2, s2 = _quant_outputs(quant_beside, quant_beside_layout, q2, s2)
+            if quant_beside.device != dev:
+                raise ValueError("quant_beside must be on the device of x")
+            M2, K2 = quant_beside.shape
+            side = [_ptr(quant_beside), M2, K2, quant_beside.stride(0), _ptr(q2), q2.stride(0), _ptr(s2),
+                    s2.stride(0), s2.stride(1)]
+        else:
+            side = [None, 0, 0, 0, None, 0, None, 0, 0]
+        if workspace is not None:
+            st = _lib.indexer_q_prep_bf16_with_quant_ws(*args, *side, _ptr(workspace), workspace.numel(),
+                                                        _stream(x, stream))
+            _check(st, "indexer_q_prep_bf16_with_quant_ws")
+        else:
+            st = _lib.indexer_q_prep_bf16_with_quant(*args, *side, _stream(x, stream))
+            _check(st, "indexer_q_prep_bf16_with_quant")
+        return (q_fp4, q_scales, q2, s2) if quant_beside is not None else (q_fp4, q_scales)
     if flags == 0:
         st = _lib.indexer_q_prep_bf16(*args, _stream(x, stream))
         _check(st, "indexer_q_prep_bf16")
@@ -480,6 +506,16 @@ def indexer_q_prep_bf16(x, w, w_scales, positions, cos_sin, n_heads: int = 64, h
         st = _lib.indexer_q_prep_bf16_ex(*args, flags, _stream(x, stream))
         _check(st, "indexer_q_prep_bf16_ex")
     return q_fp4, q_scales
+
+
+def indexer_q_workspace_bytes(n_heads: int = 64) -> int:
+    """Bytes of the split-K workspace for n_heads heads (indexer_q_workspace_bytes)."""
+    return int(_lib.indexer_q_workspace_bytes(n_heads))
+
+
+def indexer_q_workspace(n_heads: int = 64, device=None):
+    """A zeroed workspace for :func:`indexer_q_prep_bf16` (``workspace=``)."""
+    return torch.zeros(indexer_q_workspace_bytes(n_heads), dtype=torch.uint8, device=device)
 
 
 def _prep_bf16_common(x, w, w_scales, positions, cos_sin, n_heads, head_dim, rope_dim, w_scale_rows):

@@ -220,12 +220,17 @@ int indexer_q_prep_bf16_ex(const void* x, int64_t ldx, const void* w, int64_t ld
   return from_hip(iqp::launch_indexer_q_small_bf16_variant(p, flags, static_cast<hipStream_t>(stream)));
 }
 
-int indexer_q_prep_bf16_with_quant(const void* x, int64_t ldx, const void* w, int64_t ldw, const uint8_t* w_scales,
-                                   int64_t M, int64_t K, int32_t H, int32_t D, int32_t rope_dim,
-                                   const int64_t* positions, const float* cos_sin, int64_t max_pos,
-                                   uint8_t* q_fp4, uint8_t* q_scales, const void* x2, int64_t M2, int64_t K2,
-                                   int64_t ldx2, void* q2, int64_t ldq2, int32_t* scales2, int64_t s_stride_m2,
-                                   int64_t s_stride_w2, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// indexer_q_prep_bf16_with_quant, with the small-batch kernel split over K
+// where the workspace ws is given (null: not split)
+int prep_with_quant(const void* x, int64_t ldx, const void* w, int64_t ldw, const uint8_t* w_scales, int64_t M,
+                    int64_t K, int32_t H, int32_t D, int32_t rope_dim, const int64_t* positions,
+                    const float* cos_sin, int64_t max_pos, uint8_t* q_fp4, uint8_t* q_scales, const void* x2,
+                    int64_t M2, int64_t K2, int64_t ldx2, void* q2, int64_t ldq2, int32_t* scales2,
+                    int64_t s_stride_m2, int64_t s_stride_w2, uint8_t* ws, void* stream) {
   // the second matrix: fp8_quant_1x128_ue8m0's checks, at decode sizes
   if (M2 < 0 || K2 < 0) return IQP_ERR_INVALID;
   const bool side = M2 > 0 && K2 > 0;
@@ -251,6 +256,7 @@ int indexer_q_prep_bf16_with_quant(const void* x, int64_t ldx, const void* w, in
   }
   p.q_fp4 = q_fp4;
   p.q_scales = q_scales;
+  p.splitk_ws = ws;
   if (side) {
     p.side_x = static_cast<const uint16_t*>(x2);
     p.side_ldx = ldx2;
@@ -264,6 +270,36 @@ int indexer_q_prep_bf16_with_quant(const void* x, int64_t ldx, const void* w, in
     p.side_words = M2 * p.side_nw;
   }
   return from_hip(iqp::launch_indexer_q_small_bf16(p, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int indexer_q_prep_bf16_with_quant(const void* x, int64_t ldx, const void* w, int64_t ldw, const uint8_t* w_scales,
+                                   int64_t M, int64_t K, int32_t H, int32_t D, int32_t rope_dim,
+                                   const int64_t* positions, const float* cos_sin, int64_t max_pos,
+                                   uint8_t* q_fp4, uint8_t* q_scales, const void* x2, int64_t M2, int64_t K2,
+                                   int64_t ldx2, void* q2, int64_t ldq2, int32_t* scales2, int64_t s_stride_m2,
+                                   int64_t s_stride_w2, void* stream) {
+  return prep_with_quant(x, ldx, w, ldw, w_scales, M, K, H, D, rope_dim, positions, cos_sin, max_pos, q_fp4,
+                         q_scales, x2, M2, K2, ldx2, q2, ldq2, scales2, s_stride_m2, s_stride_w2, nullptr, stream);
+}
+
+int64_t indexer_q_workspace_bytes(int32_t H) { return H > 0 ? iqp::splitk_workspace_bytes(H) : 0; }
+
+int indexer_q_prep_bf16_with_quant_ws(const void* x, int64_t ldx, const void* w, int64_t ldw,
+                                      const uint8_t* w_scales, int64_t M, int64_t K, int32_t H, int32_t D,
+                                      int32_t rope_dim, const int64_t* positions, const float* cos_sin,
+                                      int64_t max_pos, uint8_t* q_fp4, uint8_t* q_scales, const void* x2,
+                                      int64_t M2, int64_t K2, int64_t ldx2, void* q2, int64_t ldq2,
+                                      int32_t* scales2, int64_t s_stride_m2, int64_t s_stride_w2,
+                                      void* workspace, int64_t workspace_bytes, void* stream) {
+  if (!workspace || (H > 0 && workspace_bytes < iqp::splitk_workspace_bytes(H))) return IQP_ERR_INVALID;
+  if (!aligned(workspace, 256)) return IQP_ERR_UNSUPPORTED;
+  return prep_with_quant(x, ldx, w, ldw, w_scales, M, K, H, D, rope_dim, positions, cos_sin, max_pos, q_fp4,
+                         q_scales, x2, M2, K2, ldx2, q2, ldq2, scales2, s_stride_m2, s_stride_w2,
+                         static_cast<uint8_t*>(workspace), stream);
 }
 
 int iqp_debug_indexer_q_prep_bf16_f32(const void* x, int64_t ldx, const void* w, int64_t ldw,

@@ -38,6 +38,18 @@
 // their results are never stored; an MFMA column depends on its own token's
 // row only, so whatever those rows hold stays in columns that are dropped.
 //
+// Split-K build of the one-launch variant below (S > 1; 17 to 64 tokens,
+// given a workspace): with one or two tiles the grid above fills 64 or 128
+// CUs, and each of them quantizes the tile's whole 32 x 1536 activations
+// before its K loop can start. Here S workgroups share a head and tile, each
+// taking 12 / S consecutive K blocks (it quantizes only those, and has all of
+// its weight blocks in flight at once, no ring refills). Each stores its float32 sums (4 KiB a wave, in the
+// accumulators' register order) to the workspace, then takes a ticket from
+// the head and tile's counter; the one that draws the last ticket adds the S
+// partial sums in split order (so the result does not depend on which one
+// that is), resets the counter and runs the epilogue; the others exit. No
+// workgroup waits for another.
+//
 // One-launch variant (XIN): the workgroup takes bf16 activations and
 // quantizes its own rows (the packed-UE8M0 FP8 1x128 rule, with the
 // standalone quantizer's arithmetic) straight into the LDS layout above,
@@ -102,20 +114,32 @@ __device__ __forceinline__ void static_for(F&& f) {
 // LDS byte of 16-byte chunk c (0..95) of activation row r
 __device__ __forceinline__ uint32_t a_slot(int r, int c) { return (uint32_t)(r * KROW + 16 * (c ^ (r & 15))); }
 
-constexpr int XSTEPS = TILE * NKB / 32;      // one-launch variant: 32 blocks per step, up to 12 steps
+// byte i (0 .. 11) of the 12 held in w[0..2]; i is uniform, so the selects
+// are scalar where w is
+__device__ __forceinline__ uint32_t byte12(const uint32_t (&w)[3], int i) {
+  const uint32_t x = i < 4 ? w[0] : (i < 8 ? w[1] : w[2]);
+  return x >> (8 * (i & 3));
+}
 
 // DUMP (diagnostic build, default configuration only): the float32 GEMM
 // sums (Q before RoPE) go to pa.dbg [M, H*128] in place of the epilogue.
-template <bool XIN, bool DUMP = false>
+// S: workgroups per head and tile, each over NKB / S K blocks (split-K
+// build, default configuration only; grid rows are tile-major, split-minor).
+template <bool XIN, bool DUMP = false, int S = 1>
 __global__ __launch_bounds__(NTHREADS, 1)
 void IQP_SMALL_KERNEL(IndexerQArgs pa) {
+  constexpr int KBS = NKB / S;                  // K blocks of this workgroup
+  constexpr int XSTEPS = TILE * KBS / 32;       // one-launch variant: 32 blocks per step
+  static_assert(NKB % S == 0 && (S == 1 || KBS <= NST - 1), "a split's blocks fit the ring, its last stage spare");
+  static_assert(S == 1 || (XIN && IQP_SMALL_VARIANT == 0), "the split-K build is the default one-launch kernel's");
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
   const int tid = threadIdx.x;
+  const int ntiles = (int)((pa.M + TILE - 1) / TILE);
   if constexpr (XIN && !DUMP) {
     // grid rows past the heads' token tiles: the independent quantization run
     // beside this kernel, two packed words per wave as the standalone
     // quantizer's workgroups take them (its codes stay in cache: decode-sized)
-    const int main_rows = (int)((pa.M + TILE - 1) / TILE);
+    const int main_rows = ntiles * S;
     if ((int)blockIdx.y >= main_rows) {
       const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
       const int64_t g = (int64_t)(blockIdx.y - main_rows) * gridDim.x + blockIdx.x;
@@ -129,11 +153,15 @@ void IQP_SMALL_KERNEL(IndexerQArgs pa) {
   const int head = blockIdx.x;
   const int lane = tid & 63, half = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // the column tile's tokens: the batch seen from token t0 on
-  const int64_t t0 = TILE * (int64_t)blockIdx.y;
+  const int tile = (int)blockIdx.y / S;
+  const int split = (int)blockIdx.y - S * tile;
+  const int kb0 = S == 1 ? 0 : KBS * split;   // the first K block of this workgroup
+  // the column tile's tokens: the batch seen from token t0 on (and, split,
+  // from K block kb0 on)
+  const int64_t t0 = TILE * (int64_t)tile;
   IndexerQArgs p = pa;
   if constexpr (XIN) {
-    p.x += t0 * p.ldx;
+    p.x += t0 * p.ldx + KB * kb0;
   } else {
     p.a += t0 * p.lda;
     p.a_scale_bytes += 4 * t0 * p.as_sm;
@@ -145,18 +173,19 @@ void IQP_SMALL_KERNEL(IndexerQArgs pa) {
   const int M = (int)p.M;   // 1 .. 32
 
   // 1x. (one-launch variant) the tile's bf16 rows into registers: block
-  //     b = 12 r + j (row r, K block j) is step b / 32, wave b / 8 % 4, lanes
-  //     8 (b % 8) .. +7 of it, 16 values a lane; steps past the tile's 12 M
-  //     blocks are not loaded, lanes past them reload the last block.
+  //     b = KBS r + j (row r, K block j of the workgroup's KBS) is step
+  //     b / 32, wave b / 8 % 4, lanes 8 (b % 8) .. +7 of it, 16 values a
+  //     lane; steps past the tile's KBS M blocks are not loaded, lanes past
+  //     them reload the last block.
   fp8q::v4u xa[XSTEPS], xb[XSTEPS];
-  const int nblk = NKB * M;
+  const int nblk = KBS * M;
   const int nsteps = (nblk + 31) / 32;
   if constexpr (XIN) {
 #pragma unroll
     for (int s = 0; s < XSTEPS; ++s) {
       if (s < nsteps) {
         const int b = min(32 * s + 8 * wave + (lane >> 3), nblk - 1);
-        const int r = b / NKB, j = b - NKB * r;
+        const int r = b / KBS, j = b - KBS * r;
         const fp8q::v4u* src = reinterpret_cast<const fp8q::v4u*>(p.x + (int64_t)r * p.ldx + KB * j + 16 * (lane & 7));
         xa[s] = src[0];
         xb[s] = src[1];
@@ -214,7 +243,9 @@ void IQP_SMALL_KERNEL(IndexerQArgs pa) {
   //    8 c + l / 8 (of the wave's 32) into stage j % NST, LDS row 8 c + l / 8
   //    slot l % 8, which holds the row's 16-byte chunk (l % 8) ^ (row / 2 % 8);
   //    the column 128 j is the instruction offset (added to the LDS address too).
-  const rsrc_t rw = make_rsrc(p.w + (int64_t)head * HEAD_DIM * p.ldw, (uint64_t)HEAD_DIM * p.ldw);
+  //    Split build: blocks kb0 .. kb0 + KBS - 1, all issued at once.
+  const rsrc_t rw = make_rsrc(p.w + (int64_t)head * HEAD_DIM * p.ldw + KB * kb0,
+                              (uint64_t)HEAD_DIM * p.ldw - KB * kb0);
   uint32_t wv[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
@@ -240,12 +271,13 @@ void IQP_SMALL_KERNEL(IndexerQArgs pa) {
   } else {
     // the ring's first NST - 1 blocks; the last stage of wave 0's ring holds
     // the scale-byte exchange (byte 12 r + j: row r, block j) until its block
-    // is issued
-    static_for<0, NST - 1>([&](auto jc) __attribute__((always_inline)) { copies(jc); });
+    // is issued (split build: all KBS blocks, the last stage stays spare)
+    constexpr int FIRST = S > 1 ? KBS : NST - 1;
+    static_for<0, FIRST>([&](auto jc) __attribute__((always_inline)) { copies(jc); });
     __builtin_amdgcn_sched_barrier(0);
     uint8_t* const xch = lds + W_OFF + (NST - 1) * WSTAGE;
     {
-      constexpr int WAIT = waitcnt_vm(4 * (NST - 1));   // the rows and the position have landed
+      constexpr int WAIT = waitcnt_vm(4 * FIRST);   // the rows and the position have landed
       __builtin_amdgcn_s_waitcnt(WAIT);
     }
 #pragma unroll
@@ -255,9 +287,9 @@ void IQP_SMALL_KERNEL(IndexerQArgs pa) {
         const int e = fp8q::block_exponent(fp8q::lanes8_max(fp8q::mag16(xa[s], xb[s])));
         const fp8q::v4u codes = fp8q::codes16(xa[s], xb[s], e);
         if (b < nblk) {
-          const int r = b / NKB, j = b - NKB * r;
+          const int r = b / KBS, j = b - KBS * r;
           *reinterpret_cast<fp8q::v4u*>(lds + a_slot(r, 8 * j + (lane & 7))) = codes;
-          if ((lane & 7) == 0) xch[b] = (uint8_t)(e + 127);
+          if ((lane & 7) == 0) xch[NKB * r + j] = (uint8_t)(e + 127);
         }
       }
     }
@@ -268,24 +300,27 @@ void IQP_SMALL_KERNEL(IndexerQArgs pa) {
 #pragma unroll
     for (int k = 0; k < 3; ++k) asw[k] = xw[k];
     __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);
-    block_barrier();   // every wave has its words: the stage may be refilled
-    copies(std::integral_constant<int, NST - 1>{});
+    if constexpr (S == 1) {
+      block_barrier();   // every wave has its words: the stage may be refilled
+      copies(std::integral_constant<int, NST - 1>{});
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 
   // 4. the K loop: block j's weights are in stage j % NST once only the
   //    copies of the blocks after it may be outstanding (and the 4 RoPE row
   //    loads issued after block NST's copies); the stage is refilled with
-  //    block j + NST once its fragments are read
+  //    block j + NST once its fragments are read (split build: the KBS
+  //    blocks of the workgroup, none refilled)
   v4f rc[2], rs[2];
   v16f acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
   const int arow = lane & 31;
   const int wswz = (arow >> 1) & 7;
-  static_for<0, NKB>([&](auto jc) __attribute__((always_inline)) {
+  static_for<0, KBS>([&](auto jc) __attribute__((always_inline)) {
     constexpr int j = decltype(jc)::value;
-    constexpr int last = j + NST - 1 < NKB - 1 ? j + NST - 1 : NKB - 1;
+    constexpr int last = j + NST - 1 < KBS - 1 ? j + NST - 1 : KBS - 1;
     constexpr int WAIT = waitcnt_vm(4 * (last - j) + (j >= 1 && j <= NST ? 4 : 0));
     __builtin_amdgcn_s_waitcnt(WAIT);
     const uint8_t* st = ring + (j % NST) * WSTAGE + KB * arow;
@@ -298,7 +333,7 @@ void IQP_SMALL_KERNEL(IndexerQArgs pa) {
       afr[kh] = make_v8i(*reinterpret_cast<const v4u*>(lds + a_slot(arow, 8 * j + c0)),
                          *reinterpret_cast<const v4u*>(lds + a_slot(arow, 8 * j + c0 + 1)));
     }
-    if constexpr (j + NST < NKB) {
+    if constexpr (j + NST < KBS) {
       __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);   // the stage's fragments are in registers
       copies(std::integral_constant<int, j + NST>{});
     }
@@ -314,13 +349,62 @@ void IQP_SMALL_KERNEL(IndexerQArgs pa) {
         rs[h] = *reinterpret_cast<const v4f*>(row + 32 + (VAR_IL ? 16 : 4) * h);
       }
     }
-    const int ws = (int)(wsw[j >> 2] >> (8 * (j & 3)));
-    const int as = (int)(asw[j >> 2] >> (8 * (j & 3)));
+    // the weight bytes are the head's 12 (from the workgroup's first K
+    // block); the activation bytes the token's 12 (split build: its KBS)
+    const int ws = (int)byte12(wsw, kb0 + j);
+    const int as = (int)byte12(asw, j);
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
       acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wfr[kh], afr[kh], acc, 0, 0, 0, ws, 0, as);
     __builtin_amdgcn_sched_barrier(0);
   });
+
+  // 4s. split build: the sums to the workspace (split s, head and tile u:
+  //     4 KiB a wave, register group g of lane l at byte 16 (64 g + l), so
+  //     that each store writes 1 KiB), a ticket from u's counter, and only
+  //     the last of u's workgroups goes on, with the S sums added in split
+  //     order. The sums are stored and loaded device-coherent (the sc1 cache
+  //     policy of relaxed device-scope atomics), and each workgroup's stores
+  //     have completed before its ticket is taken; the counter is a
+  //     device-scope atomic. No fence is needed beyond that, so no cache is
+  //     written back or invalidated.
+  if constexpr (S > 1) {
+    constexpr int CPOL_DEVICE = 0x10;   // sc1
+    const int64_t nunits = (int64_t)pa.H * ntiles;
+    const int64_t unit = (int64_t)head * ntiles + tile;
+    int32_t* const cnt = reinterpret_cast<int32_t*>(pa.splitk_ws) + unit;
+    const rsrc_t rp = make_rsrc(pa.splitk_ws + splitk_counter_bytes(pa.H), (uint64_t)65536 * pa.H);
+    const uint32_t off0 = (uint32_t)((unit * NWAVES + wave) * 4096 + 16 * lane);
+    const uint32_t split_stride = (uint32_t)(nunits * NWAVES * 4096);
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      __builtin_amdgcn_raw_buffer_store_b128(
+          v4u{__float_as_uint(acc[4 * g]), __float_as_uint(acc[4 * g + 1]), __float_as_uint(acc[4 * g + 2]),
+              __float_as_uint(acc[4 * g + 3])},
+          rp, off0 + split * split_stride + 1024 * g, 0, CPOL_DEVICE);
+    __builtin_amdgcn_s_waitcnt(WAITCNT_VM0);   // this wave's sums have been written
+    __syncthreads();
+    // wave 0's spare ring stage (the scale exchange before it ended with the K loop)
+    int32_t* const flag = reinterpret_cast<int32_t*>(lds + W_OFF + NST * WSTAGE - 4);
+    if (tid == 0) {
+      const int32_t ticket = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const bool last_one = ticket == S - 1;
+      if (last_one) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // for the next call
+      *flag = last_one ? 1 : 0;
+    }
+    __syncthreads();
+    if (*flag == 0) return;   // uniform over the workgroup
+#pragma unroll
+    for (int s2 = 0; s2 < S; ++s2) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const v4u x = __builtin_amdgcn_raw_buffer_load_b128(rp, off0 + s2 * split_stride + 1024 * g, 0, CPOL_DEVICE);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          acc[4 * g + q] = s2 == 0 ? __uint_as_float(x[q]) : acc[4 * g + q] + __uint_as_float(x[q]);
+      }
+    }
+  }
 
   // 5. the four 32-row slices meet in LDS (over the activation rows, once
   //    every wave is done reading them) as token rows: accumulator group g
@@ -463,6 +547,18 @@ bool indexer_q_small_supported(const IndexerQArgs& a) {
          a.ldw <= (1 << 22) && (reinterpret_cast<uintptr_t>(a.w_scales) & 3) == 0;
 }
 
+// workgroups per head and tile of the one-launch kernel: with a workspace,
+// 3 from 17 to 32 tokens and 2 from 33 to 64 (at most 4 partial-sum sets a
+// head, the workspace's), else 1. Measured on MI355X with an [M, 7168]
+// quantization beside it: 16 tokens 7.6 us either way, 24 tokens 7.9 against
+// 8.6, 32 tokens 8.2 against 9.5, 48 tokens 8.7 against 9.6, 64 tokens 9.6
+// against 9.8; below 16 tokens the split is slower (8 tokens 7.3 against 6.7)
+static int splitk_splits(const IndexerQArgs& a) {
+  if (a.splitk_ws == nullptr || a.M < SPLITK_MIN_TOKENS || a.M > SPLITK_MAX_TOKENS) return 1;
+  return a.M <= small::TILE ? 3 : 2;
+}
+
+
 hipError_t launch_indexer_q_small(const IndexerQArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)a.H, (unsigned)((a.M + small::TILE - 1) / small::TILE)), block(small::NTHREADS);
   hipLaunchKernelGGL(small::IQP_SMALL_KERNEL<false>, grid, block, 0, stream, a);
@@ -480,10 +576,16 @@ hipError_t launch_indexer_q_small_bf16(const IndexerQArgs& a, hipStream_t stream
   // extra grid rows for the quantization beside it: two words per wave
   const int64_t side_wgs = (a.side_words + 2 * small::NWAVES - 1) / (2 * small::NWAVES);
   const int64_t side_rows = (side_wgs + a.H - 1) / a.H;
-  const int64_t rows = (a.M + small::TILE - 1) / small::TILE + side_rows;
+  const int S = splitk_splits(a);
+  const int64_t rows = S * ((a.M + small::TILE - 1) / small::TILE) + side_rows;
   if (rows > 65535) return hipErrorInvalidValue;
   const dim3 grid((unsigned)a.H, (unsigned)rows), block(small::NTHREADS);
-  hipLaunchKernelGGL(small::IQP_SMALL_KERNEL<true>, grid, block, 0, stream, a);
+  if (S == 3)
+    hipLaunchKernelGGL((small::IQP_SMALL_KERNEL<true, false, 3>), grid, block, 0, stream, a);
+  else if (S == 2)
+    hipLaunchKernelGGL((small::IQP_SMALL_KERNEL<true, false, 2>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((small::IQP_SMALL_KERNEL<true, false, 1>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

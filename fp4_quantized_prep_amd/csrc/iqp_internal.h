@@ -41,7 +41,19 @@ struct IndexerQArgs {
   int64_t side_sm, side_sw;
   int32_t side_nw, side_nkb;
   int64_t side_words;
+  // small-batch kernel, split over K (null: not split): the workspace of
+  // splitk_workspace_bytes(H) bytes, zero before its first use and left zero
+  // by every call (the counters); calls sharing one must not overlap
+  uint8_t* splitk_ws;
 };
+
+// the one-launch kernel's split-K workspace: one counter per head and
+// 32-token tile, then each split's float32 partial sums of every head and
+// tile (at most 4 sets of 16 KiB a head: 3 splits x 1 tile, 2 x 2)
+constexpr int64_t SPLITK_MIN_TOKENS = 17;
+constexpr int64_t SPLITK_MAX_TOKENS = 64;
+__host__ __device__ constexpr int64_t splitk_counter_bytes(int64_t H) { return (8 * H + 255) / 256 * 256; }
+__host__ __device__ constexpr int64_t splitk_workspace_bytes(int64_t H) { return splitk_counter_bytes(H) + 65536 * H; }
 
 hipError_t launch_fp8_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                             uint8_t* q, int64_t ldq, int32_t* scales,
@@ -118,6 +130,8 @@ hipError_t launch_indexer_q_small_v6(const IndexerQArgs& args, hipStream_t strea
 hipError_t launch_indexer_q_small_v7(const IndexerQArgs& args, hipStream_t stream);
 // the same kernel quantizing bf16 activations (args.x, args.ldx) itself: one
 // launch from X to FP4 Q; K = 1536, 1 to 256 tokens
+// (with args.splitk_ws set and SPLITK_MIN_TOKENS to SPLITK_MAX_TOKENS
+// tokens, its split-K build)
 bool indexer_q_small_bf16_supported(const IndexerQArgs& args);
 hipError_t launch_indexer_q_small_bf16(const IndexerQArgs& args, hipStream_t stream);
 // the same with convention variant v = 1..7 compiled in (indexer_q_small_v<v>.hip),

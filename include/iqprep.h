@@ -18,7 +18,9 @@
  *   4. indexer_q_prep_bf16   calls 1 and 2 as one launch for decode-sized
  *      batches (up to 256 tokens); indexer_q_prep_bf16_ex takes the flags;
  *      indexer_q_prep_bf16_with_quant also runs call 1 on an independent
- *      matrix in the same launch.
+ *      matrix in the same launch; indexer_q_prep_bf16_with_quant_ws is that
+ *      call with a caller-owned workspace, which lets it split each head's
+ *      K range over several workgroups at 17 to 64 tokens.
  *   5. fp8_quant_weight_128x128_ue8m0   the weights' E4M3 codes and per-tile
  *      scales that calls 2 and 4 take (weight preparation, off the
  *      per-token path).
@@ -63,7 +65,7 @@ extern "C" {
 #define IQP_ERR_UNSUPPORTED 2  /* well formed but outside the contract (K % 128, alignment, head shape, device): use another path */
 #define IQP_ERR_HIP         3  /* a HIP runtime call or kernel launch failed */
 
-#define IQP_ABI_VERSION     2
+#define IQP_ABI_VERSION     3
 
 /* Convention flags of indexer_q_gemm_rope_fp4_ex, indexer_q_prep_bf16_ex and
  * indexer_q_rope_hadamard_fp4 (0: the defaults of indexer_q_gemm_rope_fp4).
@@ -304,6 +306,51 @@ int indexer_q_prep_bf16_with_quant(const void* x, int64_t ldx, const void* w, in
                                    void* q2, int64_t ldq2, int32_t* scales2,
                                    int64_t s_stride_m2, int64_t s_stride_w2,
                                    void* stream);
+
+/*
+ * indexer_q_workspace_bytes — bytes of the workspace that
+ * indexer_q_prep_bf16_with_quant_ws needs for H heads: 256 bytes of counters
+ * per 32 heads (rounded up), then 64 KiB per head of float32 partial sums.
+ * 4,194,816 bytes at H = 64. H <= 0: 0.
+ */
+int64_t indexer_q_workspace_bytes(int32_t H);
+
+/*
+ * indexer_q_prep_bf16_with_quant_ws — indexer_q_prep_bf16_with_quant with a
+ * workspace (the same arguments, then workspace, workspace_bytes). From 17
+ * to 64 tokens the one-launch kernel then splits each head's K range (12
+ * blocks of 128) over 3 workgroups (17 to 32 tokens) or 2 (33 to 64): each
+ * quantizes only its blocks of X and streams only its blocks of W, stores
+ * its float32 partial sums in the workspace and takes a ticket from the head
+ * and tile's counter there; the workgroup that draws the last ticket adds the
+ * partial sums in split order, resets the counter and runs the RoPE /
+ * Hadamard / FP4 epilogue. Outside that range the workspace is not touched.
+ * The GEMM is the same block-scaled FP8 contraction as in the unsplit kernel
+ * (TensorRT-LLM PR "Fuse DeepSeek-V4 Indexer Q projection with CuTe DSL",
+ * sequence diagram); only the order in which the float32 partial sums are
+ * added differs, and it is fixed, so results are deterministic. Measured on
+ * MI355X with an [M, 7168] quantization beside it: 7.9 us against 8.6 at 24
+ * tokens, 8.2 against 9.5 at 32, 8.7 against 9.6 at 48.
+ *
+ * workspace: device memory of at least indexer_q_workspace_bytes(H) bytes,
+ * 256-byte aligned, owned by the caller, filled with zeros before its first
+ * use (each call leaves its counters at zero again; the partial sums need no
+ * clearing). Calls that share a workspace must not run concurrently (one
+ * workspace per stream, or order the calls): their counters would mix.
+ *
+ * Errors: null workspace or workspace_bytes too small: IQP_ERR_INVALID;
+ * workspace not 256-byte aligned: IQP_ERR_UNSUPPORTED; everything else as in
+ * indexer_q_prep_bf16_with_quant.
+ */
+int indexer_q_prep_bf16_with_quant_ws(const void* x, int64_t ldx, const void* w, int64_t ldw,
+                                      const uint8_t* w_scales,
+                                      int64_t M, int64_t K, int32_t H, int32_t D, int32_t rope_dim,
+                                      const int64_t* positions, const float* cos_sin, int64_t max_pos,
+                                      uint8_t* q_fp4, uint8_t* q_scales,
+                                      const void* x2, int64_t M2, int64_t K2, int64_t ldx2,
+                                      void* q2, int64_t ldq2, int32_t* scales2,
+                                      int64_t s_stride_m2, int64_t s_stride_w2,
+                                      void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
  * indexer_q_rope_hadamard_fp4 — the epilogue of indexer_q_gemm_rope_fp4 as a

@@ -27,7 +27,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     assert {"fp8_quant_1x128_ue8m0", "indexer_q_gemm_rope_fp4", "indexer_q_rope_hadamard_fp4",
             "indexer_q_prep_bf16", "fp8_quant_weight_128x128_ue8m0", "iqp_status_string",
-            "iqp_abi_version", "iqp_rope_table_lanes", "indexer_q_gemm_rope_fp4_lanes"} <= set(names)
+            "iqp_abi_version", "iqp_rope_table_lanes", "indexer_q_gemm_rope_fp4_lanes",
+            "indexer_q_workspace_bytes", "indexer_q_prep_bf16_with_quant_ws"} <= set(names)
 
 
 def test_library_exports_every_declared_symbol(iqp):
@@ -37,7 +38,7 @@ def test_library_exports_every_declared_symbol(iqp):
 
 
 def test_version_and_status_strings(iqp):
-    assert iqp.abi_version() == 2
+    assert iqp.abi_version() == 3
     for st in range(4):
         assert iqp._lib.iqp_status_string(st)
     assert b"unknown" in iqp._lib.iqp_status_string(99)
@@ -141,6 +142,29 @@ def test_one_launch_with_quant_argument_checks(iqp):
     assert call(M=257) == uns                               # the one-launch call's own limit
     assert call(M=0, M2=0) == iqp.IQP_OK                    # nothing to do
     assert call(M2=0, x2=0, q2=0, s2=0, M=0) == iqp.IQP_OK
+
+
+def test_workspace_size_and_argument_checks(iqp):
+    lib, inv, uns = iqp._lib, iqp.IQP_ERR_INVALID, iqp.IQP_ERR_UNSUPPORTED
+    # 8 bytes of counters a head rounded up to 256, then 64 KiB of partial sums a head
+    assert iqp.indexer_q_workspace_bytes(64) == 512 + 64 * 65536 == 4194816
+    assert iqp.indexer_q_workspace_bytes(1) == 256 + 65536
+    assert iqp.indexer_q_workspace_bytes(33) == 512 + 33 * 65536
+    assert lib.indexer_q_workspace_bytes(0) == 0 and lib.indexer_q_workspace_bytes(-3) == 0
+    base = [P(16), 1536, P(16), 1536, P(16), 20, 1536, 2, 128, 64, P(16), P(16), 10, P(16), P(16)]
+    need = iqp.indexer_q_workspace_bytes(2)
+
+    def call(M=20, M2=3, ws=4096, nbytes=need):
+        args = list(base)
+        args[5] = M
+        return lib.indexer_q_prep_bf16_with_quant_ws(*args, P(16), M2, 7168, 7168, P(16), 7168, P(16), 14, 1,
+                                                     P(ws), nbytes, None)
+    assert call(ws=0) == inv                                # no workspace
+    assert call(nbytes=need - 1) == inv                     # too small for H = 2
+    assert call(ws=4096 + 16) == uns                        # not 256-byte aligned
+    assert call(M=257) == uns                               # the one-launch call's own limit
+    assert call(M2=-1) == inv                               # the second matrix's checks
+    assert call(M=0, M2=0) == iqp.IQP_OK                    # nothing to do
 
 
 def test_debug_and_table_argument_checks(iqp):
