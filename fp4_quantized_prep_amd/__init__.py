@@ -25,7 +25,7 @@ __all__ = [
     "rope_table_lanes", "rope_table_lanes_size", "indexer_q_workspace_bytes", "indexer_q_workspace",
     "IQP_OK", "IQP_ERR_INVALID", "IQP_ERR_UNSUPPORTED", "IQP_ERR_HIP", "ONE_LAUNCH_MAX_TOKENS",
     "ONE_LAUNCH_WITH_QUANT_MAX_TOKENS",
-    "IQP_ROPE_INTERLEAVED", "IQP_FP4_SCALE_OCP_FLOOR", "IQP_W_SCALES_PER_ROW",
+    "IQP_ROPE_INTERLEAVED", "IQP_FP4_SCALE_OCP_FLOOR", "IQP_W_SCALES_PER_ROW", "IQP_NOALLOC_MAX_HEADS",
 ]
 
 #: Up to this many tokens indexer_q_prep takes the one-launch path (measured on
@@ -37,6 +37,9 @@ ONE_LAUNCH_MAX_TOKENS = 16
 #: quant_beside) than as three (quantize, fused call, quantize): measured on
 #: MI355X, 9.6 vs 11.2 us at 32 tokens, 11.8 vs 12.4 at 128, 17.9 vs 17.2 at 192.
 ONE_LAUNCH_WITH_QUANT_MAX_TOKENS = 128
+
+#: Heads the allocation-free call's scratch holds (IQP_NOALLOC_MAX_HEADS).
+IQP_NOALLOC_MAX_HEADS = 64
 
 IQP_ROPE_INTERLEAVED = 0x1
 IQP_FP4_SCALE_OCP_FLOOR = 0x2
@@ -79,6 +82,8 @@ def _load():
     lib.indexer_q_prep_bf16_with_quant_ws.argtypes = lib.indexer_q_prep_bf16_with_quant.argtypes[:-1] + \
         [c_p, c_i64, c_p]
     lib.indexer_q_prep_bf16_with_quant_ws.restype = ctypes.c_int
+    lib.indexer_q_prep_bf16_with_quant_noalloc.argtypes = lib.indexer_q_prep_bf16_with_quant.argtypes
+    lib.indexer_q_prep_bf16_with_quant_noalloc.restype = ctypes.c_int
     lib.indexer_q_workspace_bytes.argtypes = [c_i32]
     lib.indexer_q_workspace_bytes.restype = c_i64
     lib.fp8_quant_weight_128x128_ue8m0.argtypes = [c_p, c_i64, c_i64, c_i64, c_p, c_i64, c_p, c_i64, c_p]
@@ -435,7 +440,8 @@ def rope_table_lanes(cos_sin, out=None, stream=None):
 def indexer_q_prep_bf16(x, w, w_scales, positions, cos_sin, n_heads: int = 64, head_dim: int = 128,
                         rope_dim: int = 64, q_fp4=None, q_scales=None, rope_layout: str = "half_split",
                         scale_rule: str = "ceil", w_scale_layout: str = "tile_128x128", quant_beside=None,
-                        quant_beside_out=None, quant_beside_layout: str = "k", workspace=None, stream=None):
+                        quant_beside_out=None, quant_beside_layout: str = "k", workspace=None,
+                        no_alloc: bool = False, stream=None):
     """The whole preparation in one launch for up to 256 tokens (K = 1536):
     bf16 x [M, K] -> FP8 quantization (in the kernel, never stored) -> fused
     projection / RoPE / Hadamard / FP4. Returns ``(q_fp4, q_scales)``. The
@@ -453,7 +459,12 @@ def indexer_q_prep_bf16(x, w, w_scales, positions, cos_sin, n_heads: int = 64, h
     before its first use; every call leaves it so): up to 64 tokens the
     kernel then splits each head's K range over 2 or 4 workgroups
     (indexer_q_prep_bf16_with_quant_ws; default conventions only). Calls
-    sharing a workspace must not run concurrently."""
+    sharing a workspace must not run concurrently.
+
+    no_alloc: the same split with the library's own per-GPU scratch instead
+    of a workspace (indexer_q_prep_bf16_with_quant_noalloc: the C call
+    allocates nothing; up to IQP_NOALLOC_MAX_HEADS heads). Such calls must not
+    overlap on one GPU. (Outputs not given are still allocated here.)"""
     if w_scale_layout not in ("tile_128x128", "row_1x128"):
         raise ValueError("w_scale_layout must be 'tile_128x128' or 'row_1x128'")
     rows = w_scale_layout == "row_1x128"
@@ -471,14 +482,17 @@ def indexer_q_prep_bf16(x, w, w_scales, positions, cos_sin, n_heads: int = 64, h
     if tuple(q_fp4.shape) != (M, n_heads, head_dim // 2) or tuple(q_scales.shape) != (M, n_heads, head_dim // 32):
         raise ValueError("q_fp4 / q_scales have the wrong shape")
     args += [_ptr(q_fp4), _ptr(q_scales)]
-    if workspace is not None:
+    if no_alloc and workspace is not None:
+        raise ValueError("no_alloc uses the library's scratch: pass no workspace")
+    if workspace is not None or no_alloc:
         if flags != 0:
-            raise ValueError("workspace serves the default conventions only")
+            raise ValueError("workspace / no_alloc serve the default conventions only")
+    if workspace is not None:
         _require(workspace, "workspace", torch.uint8, dev, 1)
         if not workspace.is_contiguous() or workspace.numel() < indexer_q_workspace_bytes(n_heads):
             raise ValueError(f"workspace must be a contiguous uint8 tensor of at least "
                              f"{indexer_q_workspace_bytes(n_heads)} bytes (indexer_q_workspace)")
-    if quant_beside is not None or workspace is not None:
+    if quant_beside is not None or workspace is not None or no_alloc:
         if flags != 0:
             raise ValueError("quant_beside serves the default conventions only")
         if quant_beside is not None:
@@ -495,6 +509,9 @@ def indexer_q_prep_bf16(x, w, w_scales, positions, cos_sin, n_heads: int = 64, h
             st = _lib.indexer_q_prep_bf16_with_quant_ws(*args, *side, _ptr(workspace), workspace.numel(),
                                                         _stream(x, stream))
             _check(st, "indexer_q_prep_bf16_with_quant_ws")
+        elif no_alloc:
+            st = _lib.indexer_q_prep_bf16_with_quant_noalloc(*args, *side, _stream(x, stream))
+            _check(st, "indexer_q_prep_bf16_with_quant_noalloc")
         else:
             st = _lib.indexer_q_prep_bf16_with_quant(*args, *side, _stream(x, stream))
             _check(st, "indexer_q_prep_bf16_with_quant")

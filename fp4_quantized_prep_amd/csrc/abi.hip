@@ -5,9 +5,17 @@
 // the current device is gfx950, and enqueues its kernel on the caller's stream.
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 #include "iqp_internal.h"
 #include "iqprep.h"
+
+// The allocation-free entry point's scratch: the split-K workspace for up to
+// IQP_NOALLOC_MAX_HEADS heads, in static device storage (zero when the
+// library's code is loaded on a device; every call leaves its counters at zero
+// again). Each GPU holds its own copy until the process ends. Host code uses
+// only the per-device address that hipGetSymbolAddress returns for it.
+static __device__ __align__(256) uint8_t scratch[iqp::splitk_workspace_bytes(IQP_NOALLOC_MAX_HEADS)];
 
 namespace {
 
@@ -33,6 +41,28 @@ int device_status() {
 }
 
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// the current device's address of scratch, looked up once per device (with
+// that device current) and kept
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_address(uint8_t** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return IQP_ERR_HIP;
+  if (dev >= kMaxDevices) return IQP_ERR_UNSUPPORTED;
+  void* ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch[dev].load(std::memory_order_acquire);
+    if (ptr == nullptr) {
+      if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return IQP_ERR_HIP;
+      g_scratch[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = static_cast<uint8_t*>(ptr);
+  return IQP_OK;
+}
 
 // Packed scale words: [M, nw] logically; K-major or MN-major strides only.
 int check_scale_strides(int64_t M, int64_t nw, int64_t sm, int64_t sw) {
@@ -225,12 +255,13 @@ int indexer_q_prep_bf16_ex(const void* x, int64_t ldx, const void* w, int64_t ld
 namespace {
 
 // indexer_q_prep_bf16_with_quant, with the small-batch kernel split over K
-// where the workspace ws is given (null: not split)
+// where a workspace is given: ws, or (use_scratch) this device's scratch,
+// looked up after every check has passed (null and false: not split)
 int prep_with_quant(const void* x, int64_t ldx, const void* w, int64_t ldw, const uint8_t* w_scales, int64_t M,
                     int64_t K, int32_t H, int32_t D, int32_t rope_dim, const int64_t* positions,
                     const float* cos_sin, int64_t max_pos, uint8_t* q_fp4, uint8_t* q_scales, const void* x2,
                     int64_t M2, int64_t K2, int64_t ldx2, void* q2, int64_t ldq2, int32_t* scales2,
-                    int64_t s_stride_m2, int64_t s_stride_w2, uint8_t* ws, void* stream) {
+                    int64_t s_stride_m2, int64_t s_stride_w2, uint8_t* ws, bool use_scratch, void* stream) {
   // the second matrix: fp8_quant_1x128_ue8m0's checks, at decode sizes
   if (M2 < 0 || K2 < 0) return IQP_ERR_INVALID;
   const bool side = M2 > 0 && K2 > 0;
@@ -256,6 +287,10 @@ int prep_with_quant(const void* x, int64_t ldx, const void* w, int64_t ldw, cons
   }
   p.q_fp4 = q_fp4;
   p.q_scales = q_scales;
+  if (use_scratch) {
+    const int ss = scratch_address(&ws);
+    if (ss != IQP_OK) return ss;
+  }
   p.splitk_ws = ws;
   if (side) {
     p.side_x = static_cast<const uint16_t*>(x2);
@@ -283,7 +318,8 @@ int indexer_q_prep_bf16_with_quant(const void* x, int64_t ldx, const void* w, in
                                    int64_t ldx2, void* q2, int64_t ldq2, int32_t* scales2, int64_t s_stride_m2,
                                    int64_t s_stride_w2, void* stream) {
   return prep_with_quant(x, ldx, w, ldw, w_scales, M, K, H, D, rope_dim, positions, cos_sin, max_pos, q_fp4,
-                         q_scales, x2, M2, K2, ldx2, q2, ldq2, scales2, s_stride_m2, s_stride_w2, nullptr, stream);
+                         q_scales, x2, M2, K2, ldx2, q2, ldq2, scales2, s_stride_m2, s_stride_w2, nullptr, false,
+                         stream);
 }
 
 int64_t indexer_q_workspace_bytes(int32_t H) { return H > 0 ? iqp::splitk_workspace_bytes(H) : 0; }
@@ -299,7 +335,20 @@ int indexer_q_prep_bf16_with_quant_ws(const void* x, int64_t ldx, const void* w,
   if (!aligned(workspace, 256)) return IQP_ERR_UNSUPPORTED;
   return prep_with_quant(x, ldx, w, ldw, w_scales, M, K, H, D, rope_dim, positions, cos_sin, max_pos, q_fp4,
                          q_scales, x2, M2, K2, ldx2, q2, ldq2, scales2, s_stride_m2, s_stride_w2,
-                         static_cast<uint8_t*>(workspace), stream);
+                         static_cast<uint8_t*>(workspace), false, stream);
+}
+
+int indexer_q_prep_bf16_with_quant_noalloc(const void* x, int64_t ldx, const void* w, int64_t ldw,
+                                           const uint8_t* w_scales, int64_t M, int64_t K, int32_t H, int32_t D,
+                                           int32_t rope_dim, const int64_t* positions, const float* cos_sin,
+                                           int64_t max_pos, uint8_t* q_fp4, uint8_t* q_scales, const void* x2,
+                                           int64_t M2, int64_t K2, int64_t ldx2, void* q2, int64_t ldq2,
+                                           int32_t* scales2, int64_t s_stride_m2, int64_t s_stride_w2,
+                                           void* stream) {
+  if (H > IQP_NOALLOC_MAX_HEADS) return IQP_ERR_UNSUPPORTED;   // more than the scratch holds
+  return prep_with_quant(x, ldx, w, ldw, w_scales, M, K, H, D, rope_dim, positions, cos_sin, max_pos, q_fp4,
+                         q_scales, x2, M2, K2, ldx2, q2, ldq2, scales2, s_stride_m2, s_stride_w2, nullptr, true,
+                         stream);
 }
 
 int iqp_debug_indexer_q_prep_bf16_f32(const void* x, int64_t ldx, const void* w, int64_t ldw,

@@ -20,7 +20,9 @@
  *      indexer_q_prep_bf16_with_quant also runs call 1 on an independent
  *      matrix in the same launch; indexer_q_prep_bf16_with_quant_ws is that
  *      call with a caller-owned workspace, which lets it split each head's
- *      K range over several workgroups at 17 to 64 tokens.
+ *      K range over several workgroups at 17 to 64 tokens, and
+ *      indexer_q_prep_bf16_with_quant_noalloc the same with the library's own
+ *      scratch, for callers that cannot allocate.
  *   5. fp8_quant_weight_128x128_ue8m0   the weights' E4M3 codes and per-tile
  *      scales that calls 2 and 4 take (weight preparation, off the
  *      per-token path).
@@ -45,7 +47,9 @@
  *     silently.
  *   - M == 0 is a successful no-op.
  *   - Entry points are reentrant and thread-safe; the only global state is a
- *     per-device cache of the device architecture, filled on first use.
+ *     per-device cache of the device architecture, filled on first use, and
+ *     the per-device scratch of indexer_q_prep_bf16_with_quant_noalloc (whose
+ *     calls must not overlap on one GPU).
  *
  * Number formats: E4M3 is the OCP OFP8 "fn" variant (bias 7, max 448, no
  * infinities); E2M1 is OCP MX FP4 (magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6);
@@ -351,6 +355,37 @@ int indexer_q_prep_bf16_with_quant_ws(const void* x, int64_t ldx, const void* w,
                                       void* q2, int64_t ldq2, int32_t* scales2,
                                       int64_t s_stride_m2, int64_t s_stride_w2,
                                       void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * indexer_q_prep_bf16_with_quant_noalloc — indexer_q_prep_bf16_with_quant_ws
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * arguments without the workspace, which is instead the library's own
+ * scratch, a static device array of indexer_q_workspace_bytes(
+ * IQP_NOALLOC_MAX_HEADS) = 4,194,816 bytes that each GPU the library runs on
+ * holds until the process ends (it is zero when the library is loaded, and
+ * every call leaves its counters at zero). The call allocates nothing.
+ *
+ * Every call on one GPU shares that GPU's scratch: calls that overlap on one
+ * GPU (on different streams, or from several threads) race and must not be
+ * made; order them on one stream. Results are byte for byte those of
+ * indexer_q_prep_bf16_with_quant_ws.
+ *
+ * Errors: H > IQP_NOALLOC_MAX_HEADS: IQP_ERR_UNSUPPORTED (the scratch is too
+ * small; use indexer_q_prep_bf16_with_quant_ws); otherwise as in
+ * indexer_q_prep_bf16_with_quant (the scratch's address is looked up once per
+ * device, at the first call that gets past the checks; IQP_ERR_HIP if that
+ * fails).
+ */
+#define IQP_NOALLOC_MAX_HEADS 64
+int indexer_q_prep_bf16_with_quant_noalloc(const void* x, int64_t ldx, const void* w, int64_t ldw,
+                                           const uint8_t* w_scales,
+                                           int64_t M, int64_t K, int32_t H, int32_t D, int32_t rope_dim,
+                                           const int64_t* positions, const float* cos_sin, int64_t max_pos,
+                                           uint8_t* q_fp4, uint8_t* q_scales,
+                                           const void* x2, int64_t M2, int64_t K2, int64_t ldx2,
+                                           void* q2, int64_t ldq2, int32_t* scales2,
+                                           int64_t s_stride_m2, int64_t s_stride_w2, void* stream);
 
 /*
  * indexer_q_rope_hadamard_fp4 — the epilogue of indexer_q_gemm_rope_fp4 as a

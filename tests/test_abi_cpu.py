@@ -28,7 +28,8 @@ def test_header_declares_the_boundary():
     assert {"fp8_quant_1x128_ue8m0", "indexer_q_gemm_rope_fp4", "indexer_q_rope_hadamard_fp4",
             "indexer_q_prep_bf16", "fp8_quant_weight_128x128_ue8m0", "iqp_status_string",
             "iqp_abi_version", "iqp_rope_table_lanes", "indexer_q_gemm_rope_fp4_lanes",
-            "indexer_q_workspace_bytes", "indexer_q_prep_bf16_with_quant_ws"} <= set(names)
+            "indexer_q_workspace_bytes", "indexer_q_prep_bf16_with_quant_ws",
+            "indexer_q_prep_bf16_with_quant_noalloc"} <= set(names)
 
 
 def test_library_exports_every_declared_symbol(iqp):
@@ -165,6 +166,23 @@ def test_workspace_size_and_argument_checks(iqp):
     assert call(M=257) == uns                               # the one-launch call's own limit
     assert call(M2=-1) == inv                               # the second matrix's checks
     assert call(M=0, M2=0) == iqp.IQP_OK                    # nothing to do
+
+
+def test_no_alloc_argument_checks(iqp):
+    lib, inv, uns = iqp._lib, iqp.IQP_ERR_INVALID, iqp.IQP_ERR_UNSUPPORTED
+    base = [P(16), 1536, P(16), 1536, P(16), 20, 1536, 2, 128, 64, P(16), P(16), 10, P(16), P(16)]
+
+    def call(M=20, H=2, x2=16, M2=3):
+        args = list(base)
+        args[5], args[7] = M, H
+        return lib.indexer_q_prep_bf16_with_quant_noalloc(*args, P(x2), M2, 7168, 7168, P(16), 7168, P(16), 14, 1,
+                                                          None)
+    assert iqp.IQP_NOALLOC_MAX_HEADS == 64
+    assert call(H=65) == uns                                # beyond what the scratch holds
+    assert call(x2=0) == inv                                # the second matrix's checks
+    assert call(M=257) == uns                               # the one-launch call's own limit
+    assert call(M=-1) == inv
+    assert call(M=0, M2=0) == iqp.IQP_OK                    # nothing to do, no device touched
 
 
 def test_debug_and_table_argument_checks(iqp):
