@@ -466,7 +466,9 @@ def decode_mix(iqp, S, dev, w, wsb, reps):
     """256 independent calls, M from {1, 2, 4, 8, 16, 32, 64}: each the
     indexer-Q preparation of X [M, 1536] and the quantization of X' [M, 7168]
     (up to ONE_LAUNCH_WITH_QUANT_MAX_TOKENS tokens, i.e. every call of the
-    mix, one launch for both, indexer_q_prep_bf16_with_quant; above, three:
+    mix, one launch for both, indexer_q_prep_bf16_with_quant_ws with one
+    workspace, whose kernel splits each head's K range from 17 to 64 tokens;
+    above, three:
     the two-call preparation and a standalone quantization). Sustained
     calls/s from one captured graph of the whole mix, hot (one weight copy) and cold (call i reads weight copy
     i % 24: 302 MB, beyond the Infinity Cache); per-call latency = the mean
@@ -476,6 +478,7 @@ def decode_mix(iqp, S, dev, w, wsb, reps):
     import torch
     max_pos = 131072
     cs = iqp.rope_cos_sin_table(S.ROPE_THETA, max_pos, 64, device=dev)
+    ws = iqp.indexer_q_workspace(N_HEADS, device=dev)   # shared by every call: they run in stream order
     calls = []
     for c in S.decode_calls(256):
         m = c["x"].shape[0]
@@ -498,7 +501,8 @@ def decode_mix(iqp, S, dev, w, wsb, reps):
     def one(c, wt):
         # the Q preparation and the quantization of X' in one launch
         iqp.indexer_q_prep_bf16(c["x"], wt[0], wt[1], c["pos"], cs, n_heads=N_HEADS, q_fp4=c["q"],
-                                q_scales=c["qs"], quant_beside=c["xw"], quant_beside_out=(c["aw"], c["asw"]))
+                                q_scales=c["qs"], quant_beside=c["xw"], quant_beside_out=(c["aw"], c["asw"]),
+                                workspace=ws)
 
     def routed(c, wt):
         (one if c["M"] <= iqp.ONE_LAUNCH_WITH_QUANT_MAX_TOKENS else three)(c, wt)
@@ -519,7 +523,7 @@ def decode_mix(iqp, S, dev, w, wsb, reps):
         lat_cold[m] = med(replay_times(capture(lambda _: [routed(c, cold[j]) for j in range(n_w)], 1), n_w, 5)) * 1e6
         if m <= 256:
             lat_k[m] = med(replay_times(capture(lambda _: [iqp.indexer_q_prep_bf16(
-                c["x"], w, wsb, c["pos"], cs, n_heads=N_HEADS, q_fp4=c["q"], q_scales=c["qs"])
+                c["x"], w, wsb, c["pos"], cs, n_heads=N_HEADS, q_fp4=c["q"], q_scales=c["qs"], workspace=ws)
                 for _ in range(20)], 1), 20, 5)) * 1e6
         print(f"[bench] decode M={m}: {lat_hot[m]:.2f} us hot, {lat_cold[m]:.2f} us cold per call",
               file=sys.stderr, flush=True)
@@ -531,8 +535,8 @@ def decode_mix(iqp, S, dev, w, wsb, reps):
     return {
         "workload": "decode mix: 256 independent calls, M uniform over {1,2,4,8,16,32,64}; each call X bf16 "
                     "[M,1536] -> FP8 quant -> GEMM + RoPE + Hadamard + FP4 (64 heads) and an FP8 quant of X' "
-                    f"[M,7168]: one launch for both up to {iqp.ONE_LAUNCH_WITH_QUANT_MAX_TOKENS} tokens, three "
-                    "launches above; positions U[0,131072)",
+                    f"[M,7168]: one launch for both up to {iqp.ONE_LAUNCH_WITH_QUANT_MAX_TOKENS} tokens (split over "
+                    "K from 17 to 64 tokens, with a workspace), three launches above; positions U[0,131072)",
         "calls_per_s": len(calls) / t_hot, "calls_per_s_cold": len(calls) / t_cold,
         "latency_us_hot": {"p50": float(np.percentile(per_hot, 50)), "p99": float(np.percentile(per_hot, 99))},
         "latency_us_cold": {"p50": float(np.percentile(per_cold, 50)), "p99": float(np.percentile(per_cold, 99))},
@@ -540,7 +544,8 @@ def decode_mix(iqp, S, dev, w, wsb, reps):
         "per_M_call_us_cold": {str(k): v for k, v in lat_cold.items()},
         "one_launch_path_calls_per_s": len(calls) / t_one, "three_launch_path_calls_per_s": len(calls) / t_three,
         "one_launch_kernel_roofline": {
-            "kernel": "indexer_q_small_kernel<bf16 in> (FP8 quant + GEMM + RoPE + Hadamard + FP4, M <= 256)",
+            "kernel": "indexer_q_small_kernel<bf16 in> (FP8 quant + GEMM + RoPE + Hadamard + FP4, M <= 256; "
+                      "split over K from 17 to 64 tokens)",
             "bound": "hbm", "achieved": mix_bytes / mix_k_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": mix_bytes / mix_k_s / 1e9 / PEAK_HBM_GBS,
             "algorithmic_bytes_per_launch": mix_bytes / len(calls),
