@@ -255,13 +255,14 @@ int indexer_q_prep_bf16_ex(const void* x, int64_t ldx, const void* w, int64_t ld
 namespace {
 
 // indexer_q_prep_bf16_with_quant, with the small-batch kernel split over K
-// where a workspace is given: ws, or (use_scratch) this device's scratch,
-// looked up after every check has passed (null and false: not split)
+// where a workspace is given: ws of ws_bytes, or (use_scratch) this device's
+// scratch, looked up after every check has passed (null and false: not split)
 int prep_with_quant(const void* x, int64_t ldx, const void* w, int64_t ldw, const uint8_t* w_scales, int64_t M,
                     int64_t K, int32_t H, int32_t D, int32_t rope_dim, const int64_t* positions,
                     const float* cos_sin, int64_t max_pos, uint8_t* q_fp4, uint8_t* q_scales, const void* x2,
                     int64_t M2, int64_t K2, int64_t ldx2, void* q2, int64_t ldq2, int32_t* scales2,
-                    int64_t s_stride_m2, int64_t s_stride_w2, uint8_t* ws, bool use_scratch, void* stream) {
+                    int64_t s_stride_m2, int64_t s_stride_w2, uint8_t* ws, int64_t ws_bytes, bool use_scratch,
+                    void* stream) {
   // the second matrix: fp8_quant_1x128_ue8m0's checks, at decode sizes
   if (M2 < 0 || K2 < 0) return IQP_ERR_INVALID;
   const bool side = M2 > 0 && K2 > 0;
@@ -290,8 +291,10 @@ int prep_with_quant(const void* x, int64_t ldx, const void* w, int64_t ldw, cons
   if (use_scratch) {
     const int ss = scratch_address(&ws);
     if (ss != IQP_OK) return ss;
+    ws_bytes = (int64_t)sizeof(scratch);
   }
   p.splitk_ws = ws;
+  p.splitk_ws_bytes = ws_bytes;
   if (side) {
     p.side_x = static_cast<const uint16_t*>(x2);
     p.side_ldx = ldx2;
@@ -318,7 +321,7 @@ int indexer_q_prep_bf16_with_quant(const void* x, int64_t ldx, const void* w, in
                                    int64_t ldx2, void* q2, int64_t ldq2, int32_t* scales2, int64_t s_stride_m2,
                                    int64_t s_stride_w2, void* stream) {
   return prep_with_quant(x, ldx, w, ldw, w_scales, M, K, H, D, rope_dim, positions, cos_sin, max_pos, q_fp4,
-                         q_scales, x2, M2, K2, ldx2, q2, ldq2, scales2, s_stride_m2, s_stride_w2, nullptr, false,
+                         q_scales, x2, M2, K2, ldx2, q2, ldq2, scales2, s_stride_m2, s_stride_w2, nullptr, 0, false,
                          stream);
 }
 
@@ -335,7 +338,7 @@ int indexer_q_prep_bf16_with_quant_ws(const void* x, int64_t ldx, const void* w,
   if (!aligned(workspace, 256)) return IQP_ERR_UNSUPPORTED;
   return prep_with_quant(x, ldx, w, ldw, w_scales, M, K, H, D, rope_dim, positions, cos_sin, max_pos, q_fp4,
                          q_scales, x2, M2, K2, ldx2, q2, ldq2, scales2, s_stride_m2, s_stride_w2,
-                         static_cast<uint8_t*>(workspace), false, stream);
+                         static_cast<uint8_t*>(workspace), workspace_bytes, false, stream);
 }
 
 int indexer_q_prep_bf16_with_quant_noalloc(const void* x, int64_t ldx, const void* w, int64_t ldw,
@@ -347,7 +350,7 @@ int indexer_q_prep_bf16_with_quant_noalloc(const void* x, int64_t ldx, const voi
                                            void* stream) {
   if (H > IQP_NOALLOC_MAX_HEADS) return IQP_ERR_UNSUPPORTED;   // more than the scratch holds
   return prep_with_quant(x, ldx, w, ldw, w_scales, M, K, H, D, rope_dim, positions, cos_sin, max_pos, q_fp4,
-                         q_scales, x2, M2, K2, ldx2, q2, ldq2, scales2, s_stride_m2, s_stride_w2, nullptr, true,
+                         q_scales, x2, M2, K2, ldx2, q2, ldq2, scales2, s_stride_m2, s_stride_w2, nullptr, 0, true,
                          stream);
 }
 

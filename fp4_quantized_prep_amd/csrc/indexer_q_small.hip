@@ -373,7 +373,7 @@ void IQP_SMALL_KERNEL(IndexerQArgs pa) {
     const int64_t nunits = (int64_t)pa.H * ntiles;
     const int64_t unit = (int64_t)head * ntiles + tile;
     int32_t* const cnt = reinterpret_cast<int32_t*>(pa.splitk_ws) + unit;
-    const rsrc_t rp = make_rsrc(pa.splitk_ws + splitk_counter_bytes(pa.H), (uint64_t)65536 * pa.H);
+    const rsrc_t rp = make_rsrc(pa.splitk_ws + splitk_counter_region(pa.splitk_ws_bytes), (uint64_t)65536 * pa.H);
     const uint32_t off0 = (uint32_t)((unit * NWAVES + wave) * 4096 + 16 * lane);
     const uint32_t split_stride = (uint32_t)(nunits * NWAVES * 4096);
 #pragma unroll

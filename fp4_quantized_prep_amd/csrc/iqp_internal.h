@@ -41,19 +41,27 @@ struct IndexerQArgs {
   int64_t side_sm, side_sw;
   int32_t side_nw, side_nkb;
   int64_t side_words;
-  // small-batch kernel, split over K (null: not split): the workspace of
-  // splitk_workspace_bytes(H) bytes, zero before its first use and left zero
-  // by every call (the counters); calls sharing one must not overlap
+  // small-batch kernel, split over K (null: not split): the workspace, of
+  // splitk_ws_bytes >= splitk_workspace_bytes(H) bytes, zero before its first
+  // use and left zero by every call (the counters); calls sharing one must
+  // not overlap
   uint8_t* splitk_ws;
+  int64_t splitk_ws_bytes;
 };
 
-// the one-launch kernel's split-K workspace: one counter per head and
-// 32-token tile, then each split's float32 partial sums of every head and
-// tile (at most 4 sets of 16 KiB a head: 3 splits x 1 tile, 2 x 2)
+// the one-launch kernel's split-K workspace: the counters (one per head and
+// 32-token tile), then each split's float32 partial sums of every head and
+// tile (at most 4 sets of 16 KiB a head: 3 splits x 1 tile, 2 x 2). The
+// counter region is sized by the workspace, for the most heads it can hold
+// (8 bytes a head, in 256-byte units), so that calls with different head
+// counts find their counters in one region and may share a workspace.
 constexpr int64_t SPLITK_MIN_TOKENS = 17;
 constexpr int64_t SPLITK_MAX_TOKENS = 64;
 __host__ __device__ constexpr int64_t splitk_counter_bytes(int64_t H) { return (8 * H + 255) / 256 * 256; }
 __host__ __device__ constexpr int64_t splitk_workspace_bytes(int64_t H) { return splitk_counter_bytes(H) + 65536 * H; }
+__host__ __device__ constexpr int64_t splitk_counter_region(int64_t ws_bytes) {
+  return splitk_counter_bytes(ws_bytes / (65536 + 8));
+}
 
 hipError_t launch_fp8_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                             uint8_t* q, int64_t ldq, int32_t* scales,

@@ -315,7 +315,9 @@ int indexer_q_prep_bf16_with_quant(const void* x, int64_t ldx, const void* w, in
  * indexer_q_workspace_bytes — bytes of the workspace that
  * indexer_q_prep_bf16_with_quant_ws needs for H heads: 256 bytes of counters
  * per 32 heads (rounded up), then 64 KiB per head of float32 partial sums.
- * 4,194,816 bytes at H = 64. H <= 0: 0.
+ * 4,194,816 bytes at H = 64. H <= 0: 0. (A workspace of B bytes keeps its
+ * counters for the most heads it can hold, B / 65544, so one workspace
+ * serves calls with any head count it is large enough for.)
  */
 int64_t indexer_q_workspace_bytes(int32_t H);
 

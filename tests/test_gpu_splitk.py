@@ -155,6 +155,25 @@ def test_split_other_head_counts(gpu_lib, H):
         assert rep["ok"], (H, M, rep)
 
 
+def test_one_workspace_serves_several_head_counts(gpu_lib, setup):
+    """A workspace sized for 64 heads keeps its counters where a call with 3
+    heads looks for them too, so calls with either head count can take turns
+    on it (the counter region is sized by the workspace, not by the call)."""
+    codes64, sb64, wd, wsd, cs, ws = setup
+    c3, s3 = weights_for_heads(3)
+    c3d, s3d = c3.cuda(), s3.cuda()
+    for H, M in ((3, 24), (64, 40), (3, 50), (64, 20), (3, 30), (64, 64)):
+        print(f"[splitk] shared workspace H={H} M={M}", flush=True)
+        x, pos, _ = inputs(M, 500 + 10 * H + M)
+        codes, sb, w_, s_ = (c3, s3, c3d, s3d) if H == 3 else (codes64, sb64, wd, wsd)
+        q, qs = gpu_lib.indexer_q_prep_bf16(x.cuda(), w_, s_, pos.cuda(), cs, n_heads=H, workspace=ws)
+        torch.cuda.synchronize()
+        assert int(ws[:512].view(torch.int32).abs().sum()) == 0
+        ref = oracle_chain_from_x(x, codes, sb, pos, H)
+        rep = C.check_fp4(q.cpu().numpy(), qs.cpu().numpy(), ref["z"], ref["q_fp4"], ref["q_scales"])
+        assert rep["ok"], (H, M, rep)
+
+
 def test_workspace_binding_checks(gpu_lib, setup):
     codes, sb, wd, wsd, cs, ws = setup
     x, pos, _ = inputs(20, 400)
