@@ -467,7 +467,7 @@ def decode_mix(iqp, S, dev, w, wsb, reps):
     indexer-Q preparation of X [M, 1536] and the quantization of X' [M, 7168]
     (up to ONE_LAUNCH_WITH_QUANT_MAX_TOKENS tokens, i.e. every call of the
     mix, one launch for both, indexer_q_prep_bf16_with_quant_ws with one
-    workspace, whose kernel splits each head's K range from 17 to 64 tokens;
+    workspace, whose kernel splits each head's K range from 12 to 64 tokens;
     above, three:
     the two-call preparation and a standalone quantization). Sustained
     calls/s from one captured graph of the whole mix, hot (one weight copy) and cold (call i reads weight copy
@@ -536,7 +536,7 @@ def decode_mix(iqp, S, dev, w, wsb, reps):
         "workload": "decode mix: 256 independent calls, M uniform over {1,2,4,8,16,32,64}; each call X bf16 "
                     "[M,1536] -> FP8 quant -> GEMM + RoPE + Hadamard + FP4 (64 heads) and an FP8 quant of X' "
                     f"[M,7168]: one launch for both up to {iqp.ONE_LAUNCH_WITH_QUANT_MAX_TOKENS} tokens (split over "
-                    "K from 17 to 64 tokens, with a workspace), three launches above; positions U[0,131072)",
+                    "K from 12 to 64 tokens, with a workspace), three launches above; positions U[0,131072)",
         "calls_per_s": len(calls) / t_hot, "calls_per_s_cold": len(calls) / t_cold,
         "latency_us_hot": {"p50": float(np.percentile(per_hot, 50)), "p99": float(np.percentile(per_hot, 99))},
         "latency_us_cold": {"p50": float(np.percentile(per_cold, 50)), "p99": float(np.percentile(per_cold, 99))},
@@ -545,7 +545,7 @@ def decode_mix(iqp, S, dev, w, wsb, reps):
         "one_launch_path_calls_per_s": len(calls) / t_one, "three_launch_path_calls_per_s": len(calls) / t_three,
         "one_launch_kernel_roofline": {
             "kernel": "indexer_q_small_kernel<bf16 in> (FP8 quant + GEMM + RoPE + Hadamard + FP4, M <= 256; "
-                      "split over K from 17 to 64 tokens)",
+                      "split over K from 12 to 64 tokens)",
             "bound": "hbm", "achieved": mix_bytes / mix_k_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": mix_bytes / mix_k_s / 1e9 / PEAK_HBM_GBS,
             "algorithmic_bytes_per_launch": mix_bytes / len(calls),

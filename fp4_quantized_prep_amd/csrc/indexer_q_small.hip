@@ -38,7 +38,7 @@
 // their results are never stored; an MFMA column depends on its own token's
 // row only, so whatever those rows hold stays in columns that are dropped.
 //
-// Split-K build of the one-launch variant below (S > 1; 17 to 64 tokens,
+// Split-K build of the one-launch variant below (S > 1; 12 to 64 tokens,
 // given a workspace): with one or two tiles the grid above fills 64 or 128
 // CUs, and each of them quantizes the tile's whole 32 x 1536 activations
 // before its K loop can start. Here S workgroups share a head and tile, each
@@ -548,11 +548,15 @@ bool indexer_q_small_supported(const IndexerQArgs& a) {
 }
 
 // workgroups per head and tile of the one-launch kernel: with a workspace,
-// 3 from 17 to 32 tokens and 2 from 33 to 64 (at most 4 partial-sum sets a
+// 3 from 12 to 32 tokens and 2 from 33 to 64 (at most 4 partial-sum sets a
 // head, the workspace's), else 1. Measured on MI355X with an [M, 7168]
-// quantization beside it: 16 tokens 7.6 us either way, 24 tokens 7.9 against
-// 8.6, 32 tokens 8.2 against 9.5, 48 tokens 8.7 against 9.6, 64 tokens 9.6
-// against 9.8; below 16 tokens the split is slower (8 tokens 7.3 against 6.7)
+// quantization beside it, split against unsplit, weights hot in the
+// Infinity Cache / cold in HBM: 8 tokens 7.3 / 8.7 against 6.7 / 8.9, 12
+// tokens 7.5 / 8.7 against 7.3 / 9.5, 16 tokens 7.6 / 8.7 against 7.6 / 9.9,
+// 24 tokens 7.9 / 8.8 against 8.6 / 10.8, 32 tokens 8.2 / 9.1 against
+// 9.5 / 11.6, 48 tokens 8.7 against 9.6, 64 tokens 9.6 against 9.8 (hot);
+// with one token the split's extra round trip costs 1.1 / 0.3 us. Hot
+// weights would start the split at 17 tokens, cold ones at 8.
 static int splitk_splits(const IndexerQArgs& a) {
   if (a.splitk_ws == nullptr || a.M < SPLITK_MIN_TOKENS || a.M > SPLITK_MAX_TOKENS) return 1;
   return a.M <= small::TILE ? 3 : 2;

@@ -55,7 +55,7 @@ struct IndexerQArgs {
 // counter region is sized by the workspace, for the most heads it can hold
 // (8 bytes a head, in 256-byte units), so that calls with different head
 // counts find their counters in one region and may share a workspace.
-constexpr int64_t SPLITK_MIN_TOKENS = 17;
+constexpr int64_t SPLITK_MIN_TOKENS = 12;
 constexpr int64_t SPLITK_MAX_TOKENS = 64;
 __host__ __device__ constexpr int64_t splitk_counter_bytes(int64_t H) { return (8 * H + 255) / 256 * 256; }
 __host__ __device__ constexpr int64_t splitk_workspace_bytes(int64_t H) { return splitk_counter_bytes(H) + 65536 * H; }

@@ -20,7 +20,7 @@
  *      indexer_q_prep_bf16_with_quant also runs call 1 on an independent
  *      matrix in the same launch; indexer_q_prep_bf16_with_quant_ws is that
  *      call with a caller-owned workspace, which lets it split each head's
- *      K range over several workgroups at 17 to 64 tokens, and
+ *      K range over several workgroups at 12 to 64 tokens, and
  *      indexer_q_prep_bf16_with_quant_noalloc the same with the library's own
  *      scratch, for callers that cannot allocate.
  *   5. fp8_quant_weight_128x128_ue8m0   the weights' E4M3 codes and per-tile
@@ -323,9 +323,9 @@ int64_t indexer_q_workspace_bytes(int32_t H);
 
 /*
  * indexer_q_prep_bf16_with_quant_ws — indexer_q_prep_bf16_with_quant with a
- * workspace (the same arguments, then workspace, workspace_bytes). From 17
+ * workspace (the same arguments, then workspace, workspace_bytes). From 12
  * to 64 tokens the one-launch kernel then splits each head's K range (12
- * blocks of 128) over 3 workgroups (17 to 32 tokens) or 2 (33 to 64): each
+ * blocks of 128) over 3 workgroups (12 to 32 tokens) or 2 (33 to 64): each
  * quantizes only its blocks of X and streams only its blocks of W, stores
  * its float32 partial sums in the workspace and takes a ticket from the head
  * and tile's counter there; the workgroup that draws the last ticket adds the
@@ -335,8 +335,10 @@ int64_t indexer_q_workspace_bytes(int32_t H);
  * (TensorRT-LLM PR "Fuse DeepSeek-V4 Indexer Q projection with CuTe DSL",
  * sequence diagram); only the order in which the float32 partial sums are
  * added differs, and it is fixed, so results are deterministic. Measured on
- * MI355X with an [M, 7168] quantization beside it: 7.9 us against 8.6 at 24
- * tokens, 8.2 against 9.5 at 32, 8.7 against 9.6 at 48.
+ * MI355X with an [M, 7168] quantization beside it, weights in the Infinity
+ * Cache: 7.9 us against 8.6 at 24 tokens, 8.2 against 9.5 at 32, 8.7
+ * against 9.6 at 48; weights in HBM: 8.7 against 9.9 at 16 tokens, 9.1
+ * against 11.6 at 32.
  *
  * workspace: device memory of at least indexer_q_workspace_bytes(H) bytes,
  * 256-byte aligned, owned by the caller, filled with zeros before its first
