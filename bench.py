@@ -468,10 +468,11 @@ def decode_mix(iqp, S, dev, w, wsb, reps):
     (up to ONE_LAUNCH_WITH_QUANT_MAX_TOKENS tokens, i.e. every call of the
     mix, one launch for both, indexer_q_prep_bf16_with_quant_ws with one
     workspace, whose kernel splits each head's K range from 12 to 64 tokens;
-    above, three:
-    the two-call preparation and a standalone quantization). Sustained
-    calls/s from one captured graph of the whole mix, hot (one weight copy) and cold (call i reads weight copy
-    i % 24: 302 MB, beyond the Infinity Cache); per-call latency = the mean
+    above, three: the two-call preparation and a standalone quantization).
+    Sustained calls/s from one captured graph of the whole mix, hot (one
+    weight copy) and cold (call i reads weight copy i % 24: 302 MB, beyond the
+    Infinity Cache), and launched back to back from Python (hot, host launch
+    cost included); per-call latency = the mean
     call time of its M in a graph of 20 such calls (hot) or of 24 calls over
     the 24 copies (cold), with p50 / p99 over the mix's calls."""
     import numpy as np
@@ -515,6 +516,19 @@ def decode_mix(iqp, S, dev, w, wsb, reps):
     t_cold = med(replay_times(capture(lambda _: [routed(c, cold[i % n_w]) for i, c in enumerate(calls)], 1),
                               1, reps))
     t_one = med(replay_times(capture(lambda _: [one(c, hot) for c in calls], 1), 1, reps))
+    # the same mix launched back to back from Python (hot weights): host launch
+    # cost included, wall clock between two synchronizations, median of reps
+    eager = []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for c in calls:
+            routed(c, hot)
+        torch.cuda.synchronize()
+        eager.append(time.perf_counter() - t0)
+    t_eager = med(eager)
+    print(f"[bench] decode mix: {len(calls) / t_hot:.0f} calls/s hot, {len(calls) / t_cold:.0f} cold (graph "
+          f"replay), {len(calls) / t_eager:.0f} launched back to back", file=sys.stderr, flush=True)
     t_three = med(replay_times(capture(lambda _: [three(c, hot) for c in calls], 1), 1, reps))
     lat_hot, lat_cold, lat_k = {}, {}, {}
     for m in sorted({c["M"] for c in calls}):
@@ -538,6 +552,7 @@ def decode_mix(iqp, S, dev, w, wsb, reps):
                     f"[M,7168]: one launch for both up to {iqp.ONE_LAUNCH_WITH_QUANT_MAX_TOKENS} tokens (split over "
                     "K from 12 to 64 tokens, with a workspace), three launches above; positions U[0,131072)",
         "calls_per_s": len(calls) / t_hot, "calls_per_s_cold": len(calls) / t_cold,
+        "calls_per_s_eager": len(calls) / t_eager,
         "latency_us_hot": {"p50": float(np.percentile(per_hot, 50)), "p99": float(np.percentile(per_hot, 99))},
         "latency_us_cold": {"p50": float(np.percentile(per_cold, 50)), "p99": float(np.percentile(per_cold, 99))},
         "per_M_call_us_hot": {str(k): v for k, v in lat_hot.items()},
