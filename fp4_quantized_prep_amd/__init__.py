@@ -24,7 +24,7 @@ __all__ = [
     "indexer_q_rope_hadamard_fp4", "indexer_q_prep_bf16", "indexer_q_prep", "fp8_quant_weight_128x128_ue8m0", "abi_version", "library_path",
     "rope_table_lanes", "rope_table_lanes_size", "indexer_q_workspace_bytes", "indexer_q_workspace",
     "IQP_OK", "IQP_ERR_INVALID", "IQP_ERR_UNSUPPORTED", "IQP_ERR_HIP", "ONE_LAUNCH_MAX_TOKENS",
-    "ONE_LAUNCH_WITH_QUANT_MAX_TOKENS",
+    "ONE_LAUNCH_WITH_QUANT_MAX_TOKENS", "ONE_LAUNCH_WITH_WORKSPACE_MAX_TOKENS",
     "IQP_ROPE_INTERLEAVED", "IQP_FP4_SCALE_OCP_FLOOR", "IQP_W_SCALES_PER_ROW", "IQP_NOALLOC_MAX_HEADS",
 ]
 
@@ -37,6 +37,12 @@ ONE_LAUNCH_MAX_TOKENS = 16
 #: quant_beside) than as three (quantize, fused call, quantize): measured on
 #: MI355X, 9.6 vs 11.2 us at 32 tokens, 11.8 vs 12.4 at 128, 17.9 vs 17.2 at 192.
 ONE_LAUNCH_WITH_QUANT_MAX_TOKENS = 128
+
+#: With a split-K workspace indexer_q_prep takes the one-launch path up to this
+#: many tokens (measured on MI355X, Q preparation alone, weights hot / cold in
+#: HBM: 32 tokens 8.3 / 9.1 us against 8.9 / 11.7 for the two calls, 64 tokens
+#: 9.2 / 10.4 against 9.0 / 11.5).
+ONE_LAUNCH_WITH_WORKSPACE_MAX_TOKENS = 64
 
 #: Heads the allocation-free call's scratch holds (IQP_NOALLOC_MAX_HEADS).
 IQP_NOALLOC_MAX_HEADS = 64
@@ -625,16 +631,25 @@ def device_clock_rates():
 @_on_stream
 def indexer_q_prep(x, w, w_scales, positions, cos_sin, n_heads: int = 64, rope_layout: str = "half_split",
                    scale_rule: str = "ceil", w_scale_layout: str = "tile_128x128", cos_sin_lanes=None,
-                   stream=None):
+                   workspace=None, stream=None):
     """The whole indexer-Q preparation for a bf16 [M, K] activation batch:
-    up to ONE_LAUNCH_MAX_TOKENS tokens at K = 1536 the one-launch call, else
-    FP8 quantization then the fused projection / RoPE / Hadamard / FP4 call,
-    both on one stream. Returns ``(q_fp4, q_scales)``; the paths give the same
-    bytes. The convention arguments and ``cos_sin_lanes`` are those of
-    :func:`indexer_q_gemm_rope_fp4` (the one-launch call reads the table)."""
+    up to ONE_LAUNCH_MAX_TOKENS tokens at K = 1536 the one-launch call (up to
+    ONE_LAUNCH_WITH_WORKSPACE_MAX_TOKENS given a ``workspace`` from
+    :func:`indexer_q_workspace` and the default conventions: the call then
+    splits each head's K range from 12 tokens), else FP8 quantization then the
+    fused projection / RoPE / Hadamard / FP4 call, both on one stream. Returns
+    ``(q_fp4, q_scales)``; the paths pass the same acceptance rule (without a
+    workspace they give the same bytes). The convention arguments and
+    ``cos_sin_lanes`` are those of :func:`indexer_q_gemm_rope_fp4` (the
+    one-launch call reads the table)."""
     conv = dict(rope_layout=rope_layout, scale_rule=scale_rule, w_scale_layout=w_scale_layout)
-    if (1 <= x.shape[0] <= ONE_LAUNCH_MAX_TOKENS and x.dim() == 2 and x.shape[1] == 1536
+    default = rope_layout == "half_split" and scale_rule == "ceil" and w_scale_layout == "tile_128x128"
+    limit = ONE_LAUNCH_WITH_WORKSPACE_MAX_TOKENS if (workspace is not None and default) else ONE_LAUNCH_MAX_TOKENS
+    if (1 <= x.shape[0] <= limit and x.dim() == 2 and x.shape[1] == 1536
             and x.data_ptr() % 16 == 0 and x.stride(0) % 8 == 0 and w_scales.data_ptr() % 4 == 0):
+        if workspace is not None and default:
+            return indexer_q_prep_bf16(x, w, w_scales, positions, cos_sin, n_heads=n_heads, workspace=workspace,
+                                       stream=stream)
         return indexer_q_prep_bf16(x, w, w_scales, positions, cos_sin, n_heads=n_heads, stream=stream, **conv)
     a, a_scales = fp8_quant_1x128_ue8m0(x, stream=stream)
     return indexer_q_gemm_rope_fp4(a, a_scales, w, w_scales, positions, cos_sin, n_heads=n_heads,

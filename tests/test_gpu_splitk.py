@@ -174,6 +174,26 @@ def test_one_workspace_serves_several_head_counts(gpu_lib, setup):
         assert rep["ok"], (H, M, rep)
 
 
+@pytest.mark.parametrize("M", [40, 64, 65])
+def test_routing_helper_with_a_workspace(gpu_lib, setup, M):
+    """indexer_q_prep given a workspace: the split one-launch call up to 64
+    tokens (its bytes), the two calls above; the oracle's rule either way."""
+    codes, sb, wd, wsd, cs, ws = setup
+    x, pos, _ = inputs(M, 600 + M)
+    xd, pd = x.cuda(), pos.cuda()
+    q1, s1 = gpu_lib.indexer_q_prep(xd, wd, wsd, pd, cs, workspace=ws)
+    if M <= gpu_lib.ONE_LAUNCH_WITH_WORKSPACE_MAX_TOKENS:
+        q2, s2 = gpu_lib.indexer_q_prep_bf16(xd, wd, wsd, pd, cs, workspace=ws)
+    else:
+        a, a_s = gpu_lib.fp8_quant_1x128_ue8m0(xd)
+        q2, s2 = gpu_lib.indexer_q_gemm_rope_fp4(a, a_s, wd, wsd, pd, cs)
+    torch.cuda.synchronize()
+    assert torch.equal(q1, q2) and torch.equal(s1, s2)
+    ref = oracle_chain_from_x(x, codes, sb, pos, 64)
+    rep = C.check_fp4(q1.cpu().numpy(), s1.cpu().numpy(), ref["z"], ref["q_fp4"], ref["q_scales"])
+    assert rep["ok"], rep
+
+
 def test_workspace_binding_checks(gpu_lib, setup):
     codes, sb, wd, wsd, cs, ws = setup
     x, pos, _ = inputs(20, 400)
