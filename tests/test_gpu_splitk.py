@@ -174,6 +174,22 @@ def test_one_workspace_serves_several_head_counts(gpu_lib, setup):
         assert rep["ok"], (H, M, rep)
 
 
+def test_split_strided_rows(gpu_lib, setup):
+    """Rows of X 2048 elements apart (a view of a wider buffer), at both split
+    counts: the same bytes as the contiguous call."""
+    codes, sb, wd, wsd, cs, ws = setup
+    for M in (12, 40):
+        x, pos, _ = inputs(M, 700 + M)
+        wide = torch.zeros((M, 2048), dtype=torch.bfloat16, device="cuda")
+        wide[:, :1536] = x.cuda()
+        xv = wide[:, :1536]
+        assert xv.stride(0) == 2048
+        q1, s1 = gpu_lib.indexer_q_prep_bf16(xv, wd, wsd, pos.cuda(), cs, workspace=ws)
+        q2, s2 = gpu_lib.indexer_q_prep_bf16(x.cuda(), wd, wsd, pos.cuda(), cs, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(q1, q2) and torch.equal(s1, s2), M
+
+
 @pytest.mark.parametrize("M", [40, 64, 65])
 def test_routing_helper_with_a_workspace(gpu_lib, setup, M):
     """indexer_q_prep given a workspace: the split one-launch call up to 64
