@@ -624,6 +624,91 @@ __device__ __forceinline__ void epilogue_alone(Epi& es, v16f (&accp)[MAX_TM][4],
 #undef IQP_EPI_H
 }
 
+// Split build, the chunk's last tile: no K loop runs under its epilogue, and
+// the other group's waves are idle, so the wave that computed the tile runs
+// the first sub-tile's epilogue and hands the second sub-tile's sums to the
+// other group's wave on its SIMD (same head and tokens) through LDS, 16 KiB a
+// wave: group-major 16-byte pieces, piece q = 4 tn + g of lane l at 1 KiB q +
+// 16 l. The areas are weight stage 0 (waves 0, 1) and activation stages 0
+// and 2 (waves 2, 3): the copies into them were those of blocks 11 and 12,
+// landed by the tile's last barrier, and no later copy goes there (the
+// chunk's last copies, zero-byte reads past it, fill weight stages 1 and 2
+// and activation stage 1, and may still be in flight). One barrier, which
+// both groups take, separates the writes from the reads.
+__device__ __forceinline__ uint8_t* handoff_at(const Ctx& c) {
+  const int off = c.wave < 2 ? W_OFF + 16384 * c.wave : A_OFF + 2 * A_BYTES * (c.wave - 2);
+  return c.lds + off + 16 * fresh(c.lane);
+}
+static_assert(NST == 3 && W_BYTES >= 2 * 16384 && A_BYTES == 16384, "the hand-over areas");
+
+template <int NTMP>
+__device__ __forceinline__ void epilogue_owner(Epi& es, v16f (&accp)[MAX_TM][4], const Ctx& c) {
+  static_assert(SPLIT && NTMP == 2, "the split build's two sub-tiles");
+  {
+    uint8_t* const b = handoff_at(c);
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<v4f*>(b + 1024 * (4 * tn + g)) =
+            v4f{accp[1][tn][4 * g], accp[1][tn][4 * g + 1], accp[1][tn][4 * g + 2], accp[1][tn][4 * g + 3]};
+  }
+  __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);
+  block_barrier();   // the second sub-tile's sums are in LDS
+  es.rope = rope_rows(es.npos0, c);
+  auto run = [&](auto hc) __attribute__((always_inline)) {
+    constexpr int H = decltype(hc)::value;
+    constexpr int n = phase_items(H % 12);
+#pragma unroll
+    for (int i = 0; i < n; ++i) epi_item<H, NTMP, true>(es, accp, i, c);
+  };
+#define IQP_EPI_H(H) run(std::integral_constant<int, H>{});
+  IQP_EPI_H(0) IQP_EPI_H(1) IQP_EPI_H(2) IQP_EPI_H(3) IQP_EPI_H(4) IQP_EPI_H(5)
+  IQP_EPI_H(6) IQP_EPI_H(7) IQP_EPI_H(8) IQP_EPI_H(9) IQP_EPI_H(10) IQP_EPI_H(11)
+#undef IQP_EPI_H
+}
+
+// the other group's wave: the second sub-tile of the chunk's last tile (tile
+// `last`, whose positions are still in LDS), from the sums handed over
+template <int NTMP>
+__device__ __forceinline__ void epilogue_helper(Epi& es, v16f (&accp)[MAX_TM][4], const Ctx& c, int64_t last) {
+  static_assert(SPLIT && NTMP == 2, "the split build's two sub-tiles");
+  const int64_t tbase = TOKS * last;
+  es.tlane = (int)(tbase + 32 * c.th + (fresh(c.lane) & 31));
+  {
+    const int64_t* pl = reinterpret_cast<const int64_t*>(c.lds + P_OFF + P_BYTES * (int)(last & 1)) + 32 * c.th +
+                        (fresh(c.lane) & 31);
+    const int64_t v = pl[TM_STRIDE];
+    es.pos1 = (int32_t)(v < 0 ? 0 : (v >= c.p.max_pos ? c.p.max_pos - 1 : v));
+  }
+  // its RoPE rows into the first sub-tile's accumulators 0 and 1, where the
+  // second sub-tile's RoPE reads them
+  rope_into_acc(rope_rows(es.pos1, c), accp);
+  block_barrier();   // the owner's sums are in LDS
+  {
+    const uint8_t* const b = handoff_at(c);
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const v4f x = *reinterpret_cast<const v4f*>(b + 1024 * (4 * tn + g));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) accp[1][tn][4 * g + q] = x[q];
+      }
+  }
+  asm volatile("" : "+a"(accp[0][0]), "+a"(accp[0][1]));
+  auto run = [&](auto hc) __attribute__((always_inline)) {
+    constexpr int H = decltype(hc)::value;
+    constexpr int n = phase_items(H % 12);
+#pragma unroll
+    for (int i = 0; i < n; ++i) epi_item<H, NTMP, true>(es, accp, i, c);
+  };
+#define IQP_EPI_H(H) run(std::integral_constant<int, H>{});
+  IQP_EPI_H(12) IQP_EPI_H(13) IQP_EPI_H(14) IQP_EPI_H(15) IQP_EPI_H(16) IQP_EPI_H(17)
+  IQP_EPI_H(18) IQP_EPI_H(19) IQP_EPI_H(20) IQP_EPI_H(21) IQP_EPI_H(22) IQP_EPI_H(23)
+#undef IQP_EPI_H
+}
+
 // ---------------------------------------------------------------------------
 // One half-step: slot s issues MFMA s of 4 NTM on the operands F, then its
 // share of the LDS reads filling N (the next half-step's operands), of the
@@ -999,9 +1084,12 @@ void IQP_PIPE_KERNEL(IndexerQArgs p) {
         k_loop<ROLE_EPI, MAX_TM, DUMP ? 0 : MAX_TM>(c, acc, f0, f1, as0, as1, es, acc);
         advance();
       } else if constexpr (!DUMP) {
-        es.rope = rope_rows(es.npos0, c);
-        epilogue_alone<MAX_TM>(es, acc, c);
+        epilogue_owner<MAX_TM>(es, acc, c);
       }
+    }
+    // the group that did not compute the chunk's last tile takes its second sub-tile
+    if constexpr (!DUMP) {
+      if (group != (int)((t_end - 1 - t_begin) & 1)) epilogue_helper<MAX_TM>(es, acc, c, t_end - 1);
     }
   }
   __builtin_amdgcn_s_waitcnt(WAITCNT_VM0);   // no LDS copy may outlive the workgroup
