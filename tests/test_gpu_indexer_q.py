@@ -307,15 +307,35 @@ def test_fused_chain_variants_other_k_and_heads(gpu_lib, table, layout, rule):
     assert rep["ok"], rep
 
 
-def test_fused_chain_variant_m4632_sampled(gpu_lib, weights, table):
+@pytest.mark.parametrize("layout", ["interleaved", "half_split"])
+def test_fused_chain_variant_m4632_sampled(gpu_lib, weights, table, layout):
+    """4632 tokens with the floor rule: interleaved pairs run the one-role
+    pipelined build, half-split pairs its split-role build."""
     codes, sb, wd, wsd = weights
     inp = S.indexer_q_inputs("indexer_q_m4632")
     x, pos = inp["x"], inp["positions"]
-    q, s = device_chain_variant(gpu_lib, x, wd, wsd, pos, table[4632], 64, "interleaved", "ocp_floor")
+    print(f"[variant] M=4632 {layout} ocp_floor", flush=True)
+    q, s = device_chain_variant(gpu_lib, x, wd, wsd, pos, table[4632], 64, layout, "ocp_floor")
     rows = np.unique(np.concatenate([np.arange(8), np.random.default_rng(4634).integers(0, 4632, 120),
                                      np.arange(4632 - 8, 4632)]))
-    ref = oracle_chain_from_x(x[rows], codes, sb, pos[rows], 64, "interleaved", "ocp_floor")
+    ref = oracle_chain_from_x(x[rows], codes, sb, pos[rows], 64, layout, "ocp_floor")
     rep = C.check_fp4(q[rows], s[rows], ref["z"], ref["q_fp4"], ref["q_scales"], scale_rule="ocp_floor")
+    assert rep["ok"], rep
+
+
+@pytest.mark.parametrize("M", [1024, 2048])
+def test_fused_floor_rule_split_build_every_token(gpu_lib, weights, table, M):
+    """The floor-rule call from 1024 tokens runs the split-role build
+    (indexer_q_split_v2.hip): every token against the oracle, at the
+    threshold and at 16 tiles a head pair."""
+    codes, sb, wd, wsd = weights
+    inp = S.indexer_q_inputs("indexer_q_m4632")
+    x, pos = inp["x"][:M], inp["positions"][:M]
+    print(f"[variant] M={M} half_split ocp_floor (split-role build)", flush=True)
+    q, s = device_chain_variant(gpu_lib, x, wd, wsd, pos, table[4632], 64, "half_split", "ocp_floor")
+    ref = oracle_chain_from_x(x, codes, sb, pos, 64, "half_split", "ocp_floor")
+    rep = C.check_fp4(q, s, ref["z"], ref["q_fp4"], ref["q_scales"], scale_rule="ocp_floor")
+    print(rep)
     assert rep["ok"], rep
 
 
