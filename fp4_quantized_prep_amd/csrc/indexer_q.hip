@@ -591,9 +591,14 @@ hipError_t launch_indexer_q_variant(const IndexerQArgs& a_in, int variant, hipSt
       (variant <= 3 || (reinterpret_cast<uintptr_t>(a_in.w_scales) & 3) == 0)) {
     IndexerQArgs a;
     if (!pipe_args(a_in, a)) return hipErrorInvalidValue;
-    // the floor-rule variant has a split-role build (the only one that fits it)
-    if (variant == 2 && a.M >= SPLIT_MIN_TOKENS && indexer_q_split_supported(a))
-      return launch_indexer_q_split_v2(a, stream);
+    // the variants without per-row weight scales have split-role builds
+    if (variant <= 3 && a.M >= SPLIT_MIN_TOKENS && indexer_q_split_supported(a)) {
+      switch (variant) {
+        case 1: return launch_indexer_q_split_v1(a, stream);
+        case 2: return launch_indexer_q_split_v2(a, stream);
+        default: return launch_indexer_q_split_v3(a, stream);
+      }
+    }
     switch (variant) {
       case 1: return launch_indexer_q_pipe_v1(a, stream);
       case 2: return launch_indexer_q_pipe_v2(a, stream);

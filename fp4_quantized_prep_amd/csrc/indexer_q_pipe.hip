@@ -140,8 +140,8 @@ constexpr int WAITCNT_VM13 = (13 & 15) | (7 << 4) | (15 << 8) | ((13 >> 4) << 14
 // ROPE1_BLOCK (its first sub-tile's RoPE is done by then), ahead of that
 // half-step's copies, whose barrier then leaves ROPE_LOADS more outstanding.
 constexpr int ROPE1_BLOCK = 2;
-constexpr int ROPE_LOADS = 8;                       // load_rope: 8 loads of 16 bytes
-static_assert(!(SPLIT && VAR_IL), "the split build's wait counts assume the half-split RoPE rows");
+// load_rope: 8 loads of 16 bytes; interleaved pairs, 16 of 8 bytes
+constexpr int ROPE_LOADS = VAR_IL ? 16 : 8;
 // s_waitcnt vmcnt(n), n < 64
 constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
@@ -404,8 +404,9 @@ __device__ __forceinline__ void epi_item(Epi& es, v16f (&accp)[MAX_TM][4], int i
     } else if (i < 16) {           // interleaved pair 16 tn + 4 g + 2 half + k: registers 4g + 2k, 4g + 2k + 1
       const int tn = i >> 3, g = (i >> 1) & 3, k = i & 1, r = 4 * g + 2 * k;
       const float x = accp[tm][tn][r], y = accp[tm][tn][r + 1];
-      const float cc = es.rope.c[2 * tn + (g >> 1)][2 * (g & 1) + k];
-      const float ss = es.rope.s[2 * tn + (g >> 1)][2 * (g & 1) + k];
+      const int cj = 2 * tn + (g >> 1), ce = 2 * (g & 1) + k;   // entry ce of group cj
+      const float cc = (SPLIT && tm == 1) ? accp[0][0][4 * cj + ce] : es.rope.c[cj][ce];
+      const float ss = (SPLIT && tm == 1) ? accp[0][1][4 * cj + ce] : es.rope.s[cj][ce];
       es.v[tn][r] = x * cc - y * ss;
       es.v[tn][r + 1] = y * cc + x * ss;
     } else {

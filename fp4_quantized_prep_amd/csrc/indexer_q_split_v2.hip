@@ -1,8 +1,6 @@
 // Split-role build of the pipelined fused kernel (indexer_q_split.hip) with a
 // convention variant: FP4 block scales by the OCP MX rule (codes saturate at
-// 6). The other variants stay on the one-role schedule: interleaved RoPE
-// pairs do not fit the split build's RoPE row wait counts, and per-row weight
-// scales do not fit its registers.
+// 6).
 #define IQP_PIPE_VARIANT 2
 #define IQP_PIPE_SPLIT 1
 #define IQP_PIPE_LAUNCH launch_indexer_q_split_v2

@@ -107,9 +107,12 @@ bool indexer_q_split_supported(const IndexerQArgs& args);
 hipError_t launch_indexer_q_split(const IndexerQArgs& args, hipStream_t stream);
 // the same kernel reading the RoPE rows from args.cos_sin_lanes (indexer_q_split_lanes.hip)
 hipError_t launch_indexer_q_split_lanes(const IndexerQArgs& args, hipStream_t stream);
-// the split-role kernel with convention variant 2 (OCP floor-rule FP4 scales)
-// compiled in (indexer_q_split_v2.hip); where indexer_q_split_supported holds
+// the split-role kernel with convention variant v = 1..3 compiled in
+// (indexer_q_split_v<v>.hip; per-row weight scales do not fit its registers);
+// where indexer_q_split_supported holds
+hipError_t launch_indexer_q_split_v1(const IndexerQArgs& args, hipStream_t stream);
 hipError_t launch_indexer_q_split_v2(const IndexerQArgs& args, hipStream_t stream);
+hipError_t launch_indexer_q_split_v3(const IndexerQArgs& args, hipStream_t stream);
 
 // diagnostic builds: the float32 GEMM sums (Q before RoPE) of the pipelined,
 // split-role and small-batch kernels' K loops in args.dbg [M, H*128]; the

@@ -195,9 +195,9 @@ int indexer_q_gemm_rope_fp4(const void* a, int64_t lda,
  * K = 1536 production kernels (small-batch up to 256 tokens, pipelined
  * above) the flags run that kernel's variant build (per-row weight scales
  * in the pipelined one need w_scales 4-byte aligned; from 1024 tokens
- * IQP_FP4_SCALE_OCP_FLOOR alone runs the split-role build, the other flags
- * the one-role one); otherwise the general tiled kernel runs (slower than
- * the K = 1536 production kernels).
+ * flags without IQP_W_SCALES_PER_ROW run the split-role build, with it the
+ * one-role one); otherwise the general tiled kernel runs (slower than the
+ * K = 1536 production kernels).
  */
 int indexer_q_gemm_rope_fp4_ex(const void* a, int64_t lda,
                                const int32_t* a_scales, int64_t as_stride_m, int64_t as_stride_w,

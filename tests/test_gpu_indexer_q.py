@@ -309,8 +309,7 @@ def test_fused_chain_variants_other_k_and_heads(gpu_lib, table, layout, rule):
 
 @pytest.mark.parametrize("layout", ["interleaved", "half_split"])
 def test_fused_chain_variant_m4632_sampled(gpu_lib, weights, table, layout):
-    """4632 tokens with the floor rule: interleaved pairs run the one-role
-    pipelined build, half-split pairs its split-role build."""
+    """4632 tokens with the floor rule (the split-role variant builds)."""
     codes, sb, wd, wsd = weights
     inp = S.indexer_q_inputs("indexer_q_m4632")
     x, pos = inp["x"], inp["positions"]
@@ -323,18 +322,21 @@ def test_fused_chain_variant_m4632_sampled(gpu_lib, weights, table, layout):
     assert rep["ok"], rep
 
 
+@pytest.mark.parametrize("layout,rule", FUSED_VARIANTS)
 @pytest.mark.parametrize("M", [1024, 2048])
-def test_fused_floor_rule_split_build_every_token(gpu_lib, weights, table, M):
-    """The floor-rule call from 1024 tokens runs the split-role build
-    (indexer_q_split_v2.hip): every token against the oracle, at the
-    threshold and at 16 tiles a head pair."""
+def test_fused_variant_split_build_every_token(gpu_lib, weights, table, layout, rule, M):
+    """From 1024 tokens the flags call runs the split-role variant builds
+    (indexer_q_split_v1..3.hip): every token against the oracle, at the
+    threshold and at 16 tiles a head pair; scattered positions, so that
+    each lane's RoPE rows come from all over the table."""
     codes, sb, wd, wsd = weights
     inp = S.indexer_q_inputs("indexer_q_m4632")
-    x, pos = inp["x"][:M], inp["positions"][:M]
-    print(f"[variant] M={M} half_split ocp_floor (split-role build)", flush=True)
-    q, s = device_chain_variant(gpu_lib, x, wd, wsd, pos, table[4632], 64, "half_split", "ocp_floor")
-    ref = oracle_chain_from_x(x, codes, sb, pos, 64, "half_split", "ocp_floor")
-    rep = C.check_fp4(q, s, ref["z"], ref["q_fp4"], ref["q_scales"], scale_rule="ocp_floor")
+    x = inp["x"][:M]
+    pos = S.positions_uniform(S.rng("indexer_q_m4632", 77 + M), M, 32768)
+    print(f"[variant] M={M} {layout} {rule} (split-role build)", flush=True)
+    q, s = device_chain_variant(gpu_lib, x, wd, wsd, pos, table[32768], 64, layout, rule)
+    ref = oracle_chain_from_x(x, codes, sb, pos, 64, layout, rule)
+    rep = C.check_fp4(q, s, ref["z"], ref["q_fp4"], ref["q_scales"], scale_rule=rule)
     print(rep)
     assert rep["ok"], rep
 
