@@ -411,11 +411,13 @@ def row_scale_weights(H, K, seed):
 
 
 @pytest.mark.parametrize("M,H,K", [(1, 64, 1536), (5, 64, 1536), (128, 64, 1536), (256, 64, 1536),
-                                   (300, 64, 1536), (1157, 64, 1536), (300, 3, 1536), (70, 3, 1024)])
+                                   (300, 64, 1536), (1157, 64, 1536), (2048, 64, 1536), (300, 3, 1536),
+                                   (1100, 3, 1536), (70, 3, 1024)])
 def test_fused_chain_row_weight_scales(gpu_lib, table, M, H, K):
     """At K = 1536 the small-batch kernel's per-row build runs up to 256
-    tokens and the pipelined kernel's above (1157: uneven tile chunks; 3
-    heads: a pair without its second head); the general kernel at K = 1024."""
+    tokens and the pipelined kernel's one-role build above, also where other
+    calls take the split-role builds (1157: uneven tile chunks; 3 heads: a
+    pair without its second head); the general kernel at K = 1024."""
     codes, wsr = row_scale_weights(H, K, 103)
     if K == 1536:
         inp = S.indexer_q_inputs("indexer_q_m128", M=M)
@@ -458,7 +460,7 @@ def test_row_weight_scales_equal_to_tile_scales_give_the_same_bytes(gpu_lib, tab
         assert torch.equal(q0.cpu(), q1.cpu()) and torch.equal(s0.cpu(), s1.cpu()), (layout, rule)
 
 
-@pytest.mark.parametrize("M", [70, 300])
+@pytest.mark.parametrize("M", [70, 300, 1100])
 def test_row_weight_scales_with_variants(gpu_lib, table, M):
     H, K = 3, 1536
     codes, wsr = row_scale_weights(H, K, 105)
