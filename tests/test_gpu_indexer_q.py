@@ -307,6 +307,22 @@ def test_fused_chain_variants_other_k_and_heads(gpu_lib, table, layout, rule):
     assert rep["ok"], rep
 
 
+@pytest.mark.parametrize("layout,rule", FUSED_VARIANTS)
+def test_fused_variant_split_build_three_heads(gpu_lib, table, layout, rule):
+    """The split-role variant builds with 3 heads (the second pair without
+    its second head) and 1100 tokens (uneven tile chunks), every token."""
+    H, M, K = 3, 1100, 1536
+    codes, sb = S.weights(N=H * 128, K=K, seed=106)
+    g = S.rng("indexer_q_m4632", 962)
+    x = S.activations_outlier(g, M, K)
+    pos = S.positions_uniform(g, M, 32768)
+    print(f"[variant] M={M} H={H} {layout} {rule} (split-role build)", flush=True)
+    q, s = device_chain_variant(gpu_lib, x, codes.cuda(), sb.cuda(), pos, table[32768], H, layout, rule)
+    ref = oracle_chain_from_x(x, codes, sb, pos, H, layout, rule)
+    rep = C.check_fp4(q, s, ref["z"], ref["q_fp4"], ref["q_scales"], scale_rule=rule)
+    assert rep["ok"], rep
+
+
 @pytest.mark.parametrize("layout", ["interleaved", "half_split"])
 def test_fused_chain_variant_m4632_sampled(gpu_lib, weights, table, layout):
     """4632 tokens with the floor rule (the split-role variant builds)."""
