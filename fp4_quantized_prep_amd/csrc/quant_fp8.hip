@@ -26,18 +26,24 @@
 // lane held 16 consecutive values (two 16-byte loads 32 bytes apart: every
 // line fetched by two instructions) and 19.4 us for a copy with no
 // arithmetic in that older pattern; four words per wave instead of two ran
-// slower.
+// slower. Workgroups of 8 waves instead of 4 took it to 17.8 us (and
+// [32768, 7168] from 115.7 to 112.1 us) but slowed the small cached
+// quantization of [4632, 1536] (5.9 against 5.6 us), so the launcher picks
+// the shape with the store policy.
 #include "fp8_block.h"
 #include "iqp_internal.h"
 
 namespace iqp {
 namespace {
 
-constexpr int QWAVES = 4;  // waves per workgroup, two scale words each
+// waves per workgroup (two scale words each): outputs streamed past the
+// caches, and outputs kept in them
+constexpr int QWAVES_STREAM = 8;
+constexpr int QWAVES_CACHED = 4;
 
 // Words 2 i and 2 i + 1 (row-major over [M, nw]) of the whole tensor go to
 // wave i (the arithmetic: fp8q::quant_word_pair).
-template <bool NT_STORE>
+template <bool NT_STORE, int QWAVES>
 __global__ __launch_bounds__(QWAVES * 64)
 void fp8_quant_1x128_kernel(const uint16_t* __restrict__ x, int64_t ldx,
                             uint8_t* __restrict__ q, int64_t ldq,
@@ -58,9 +64,6 @@ hipError_t launch_fp8_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx
   const int32_t nkb = (int32_t)(K / 128);
   const int32_t nw = (nkb + 3) / 4;
   const int64_t words = M * nw;
-  const int64_t per_block = (int64_t)QWAVES * 2;
-  const int64_t blocks = (words + per_block - 1) / per_block;
-  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   // Up to 16 MiB of codes are stored through the caches, so that the
   // projection that reads them next finds them there; larger outputs are
   // streamed past them. Measured on MI355X: the 4632-token chain (7 MB of
@@ -68,8 +71,12 @@ hipError_t launch_fp8_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx
   // kernel alone: 62.4 us), while streaming keeps the standalone [4632,
   // 7168] quantization at 18.6 us against 19.0 us cached.
   const bool nt = M * ldq > ((int64_t)16 << 20);
-  hipLaunchKernelGGL(nt ? fp8_quant_1x128_kernel<true> : fp8_quant_1x128_kernel<false>, dim3((unsigned)blocks),
-                     dim3(QWAVES * 64), 0, stream,
+  const int qwaves = nt ? QWAVES_STREAM : QWAVES_CACHED;
+  const int64_t per_block = (int64_t)qwaves * 2;
+  const int64_t blocks = (words + per_block - 1) / per_block;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  auto kern = nt ? fp8_quant_1x128_kernel<true, QWAVES_STREAM> : fp8_quant_1x128_kernel<false, QWAVES_CACHED>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(qwaves * 64), 0, stream,
                      x, ldx, q, ldq, scales, s_stride_m, s_stride_w, nw, nkb, words);
   return hipGetLastError();
 }
