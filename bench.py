@@ -327,8 +327,6 @@ def fused_roofline(M, t_fused, samples, clock, name):
 def fused_kernel_name(M):
     if M <= 256:
         return "indexer_q_small_kernel (small-batch fused kernel)"
-    if M < 1024:
-        return "indexer_q_pipe_kernel (pipelined fused kernel)"
     return ("indexer_q_split_lanes_kernel (split-role fused kernel: GEMM + RoPE + Hadamard + FP4, RoPE rows "
             "from the table's lane-ordered copy)")
 

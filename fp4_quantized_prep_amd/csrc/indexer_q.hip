@@ -519,8 +519,11 @@ hipError_t launch_kernel(const IndexerQArgs& a_in, int stage, hipStream_t stream
 }  // namespace
 
 // token count from which the fused FP4 call runs the split-role build of the
-// pipelined kernel (measured: below it the one-role build is as fast or faster)
-constexpr int64_t SPLIT_MIN_TOKENS = 1024;
+// pipelined kernel: right above the small-batch kernel's range (measured,
+// byte-identical: 3-10 % faster than the one-role build from 384 to 1023
+// tokens, which keeps the per-row weight-scale builds and tables beyond
+// 2^31 positions)
+constexpr int64_t SPLIT_MIN_TOKENS = 257;
 
 // the pipelined kernel's launch arguments: one workgroup per CU, each head
 // pair gets CUs / pairs chunks of whole 128-token tiles

@@ -194,9 +194,9 @@ int indexer_q_gemm_rope_fp4(const void* a, int64_t lda,
  * Other bits: IQP_ERR_INVALID. Where the base call would run one of the
  * K = 1536 production kernels (small-batch up to 256 tokens, pipelined
  * above) the flags run that kernel's variant build (per-row weight scales
- * in the pipelined one need w_scales 4-byte aligned; from 1024 tokens
- * flags without IQP_W_SCALES_PER_ROW run the split-role build, with it the
- * one-role one); otherwise the general tiled kernel runs (slower than the
+ * in the pipelined one need w_scales 4-byte aligned; flags without
+ * IQP_W_SCALES_PER_ROW run its split-role build, with it the one-role one);
+ * otherwise the general tiled kernel runs (slower than the
  * K = 1536 production kernels).
  */
 int indexer_q_gemm_rope_fp4_ex(const void* a, int64_t lda,
@@ -219,7 +219,7 @@ int indexer_q_gemm_rope_fp4_ex(const void* a, int64_t lda,
  * packed FP8 quantization", Summary; TensorRT-LLM PR "Fuse DeepSeek-V4
  * Indexer Q projection with CuTe DSL", sequence diagram). The output is
  * byte for byte that of indexer_q_gemm_rope_fp4 with the same arguments:
- * where that call runs the split-role K = 1536 kernel (1024 tokens and
+ * where that call runs the split-role K = 1536 kernel (257 tokens and
  * more) the rows are read from cos_sin_lanes, elsewhere from cos_sin. The
  * copy pays where a 32-token sub-tile's positions run consecutively (prefill;
  * 16-byte loads then read whole 1 KiB segments instead of gathering 32 rows);
@@ -541,7 +541,7 @@ int iqp_debug_indexer_q_prep_bf16_f32(const void* x, int64_t ldx, const void* w,
  * ran at (tokenspeed PR "perf(deepseek-v4): accelerate indexer Q and packed
  * FP8 quantization", Performance: the pages quote kernel times with no
  * clock). Supported where the call runs the split-role kernel (K = 1536,
- * 1024 tokens or more); elsewhere IQP_ERR_UNSUPPORTED with nothing enqueued.
+ * 257 tokens or more); elsewhere IQP_ERR_UNSUPPORTED with nothing enqueued.
  *
  *   cos_sin_lanes   NULL (the build that reads cos_sin), or the table's
  *                   lane-ordered copy as indexer_q_gemm_rope_fp4_lanes takes

@@ -45,9 +45,9 @@ def test_clock_build_gives_the_production_bytes(gpu_lib, setup, M, lanes):
 
 def test_clock_build_limits(gpu_lib, setup):
     w, wsb, x, pos, cs = setup
-    a, a_s = gpu_lib.fp8_quant_1x128_ue8m0(x[:300])
-    with pytest.raises(gpu_lib.IqpError) as e:   # 300 tokens: the pipelined kernel runs
-        gpu_lib.debug_indexer_q_clock(a, a_s, w, wsb, pos[:300], cs)
+    a, a_s = gpu_lib.fp8_quant_1x128_ue8m0(x[:200])
+    with pytest.raises(gpu_lib.IqpError) as e:   # 200 tokens: the small-batch kernel runs
+        gpu_lib.debug_indexer_q_clock(a, a_s, w, wsb, pos[:200], cs)
     assert e.value.status == gpu_lib.IQP_ERR_UNSUPPORTED
     a, a_s = gpu_lib.fp8_quant_1x128_ue8m0(x[:2048])
     with pytest.raises(gpu_lib.IqpError) as e:   # too few stamp slots: nothing launched

@@ -152,12 +152,15 @@ def test_fused_chain_uneven_tile_chunks(gpu_lib, weights, table, M):
     assert rep["ok"], rep
 
 
-@pytest.mark.parametrize("M,H,max_pos", [(1023, 64, 4096), (1024, 64, 4096), (1300, 3, 131072),
-                                         (1100, 1, 4096), (2100, 8, 131072), (1500, 64, 131072)])
+@pytest.mark.parametrize("M,H,max_pos", [(256, 64, 4096), (257, 64, 4096), (383, 3, 4096), (1023, 64, 4096),
+                                         (1024, 64, 4096), (1300, 3, 131072), (1100, 1, 4096),
+                                         (2100, 8, 131072), (1500, 64, 131072)])
 def test_fused_chain_split_build(gpu_lib, table, M, H, max_pos):
-    """Token counts on both sides of the switch to the split-role build of the
-    pipelined kernel (1024 tokens), odd and single head counts (a head pair
-    with no second head), positions up to 131071; every token checked."""
+    """Token counts on both sides of the switch from the small-batch kernel
+    to the split-role build of the pipelined kernel (257 tokens: one tile a
+    workgroup, a partial second tile), odd and single head counts (a head
+    pair with no second head), positions up to 131071; every token
+    checked."""
     codes, sb = weights_for_heads(H)
     g = S.rng("indexer_q_m128", 1200 + M)
     x = S.activations_outlier(g, M, 1536)
@@ -341,9 +344,9 @@ def test_fused_chain_variant_m4632_sampled(gpu_lib, weights, table, layout):
 @pytest.mark.parametrize("layout,rule", FUSED_VARIANTS)
 @pytest.mark.parametrize("M", [1024, 2048])
 def test_fused_variant_split_build_every_token(gpu_lib, weights, table, layout, rule, M):
-    """From 1024 tokens the flags call runs the split-role variant builds
-    (indexer_q_split_v1..3.hip): every token against the oracle, at the
-    threshold and at 16 tiles a head pair; scattered positions, so that
+    """Above 256 tokens the flags call runs the split-role variant builds
+    (indexer_q_split_v1..3.hip): every token against the oracle, at 8 and
+    16 tiles a head pair; scattered positions, so that
     each lane's RoPE rows come from all over the table."""
     codes, sb, wd, wsd = weights
     inp = S.indexer_q_inputs("indexer_q_m4632")

@@ -8,9 +8,9 @@ one-launch kernel's twin), and Q is compared element by element with the
 oracle's exact GEMM (TensorRT-LLM PR page, sequence diagram: the GEMM result
 feeds the RoPE / FP4 epilogue) under the matrix-core error bound.
 
-Token counts: 1 to 256 (small-batch kernel), 300 and 1023 (pipelined), 1024,
-1157 and 4632 (split-role; 4632 checked on sampled tokens), with an odd head
-count on each of the large kernels."""
+Token counts: 1 to 256 (small-batch kernel), 300, 1023, 1024, 1157 and 4632
+(the split-role build of the pipelined kernel, from 257 tokens; 4632 checked
+on sampled tokens), with an odd head count on each of the large kernels."""
 import numpy as np
 import pytest
 import torch

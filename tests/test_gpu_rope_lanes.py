@@ -6,7 +6,7 @@ against that rearrangement written out here from its definition in
 include/iqprep.h. The fused call must give the bytes of the call that reads
 the table itself, whatever the positions: consecutive (aligned to the
 32-position blocks or not), packed sequences restarting at 0, scattered, and
-a token count below the split-role kernel's (where the table is read). One
+a token count of the small-batch kernel (where the table is read). One
 ragged prefill is also checked against the oracle, every token."""
 import numpy as np
 import pytest
@@ -74,7 +74,8 @@ CASES = [
     (3000, 64, 32768, "packed"),
     (2048, 64, 32768, "scattered"),
     (1300, 3, 4096, "offset"),
-    (500, 64, 4096, "consecutive"),      # below the split-role kernel's token count
+    (500, 64, 4096, "consecutive"),
+    (200, 64, 4096, "consecutive"),      # the small-batch kernel: the table is read
 ]
 
 
